@@ -1,0 +1,199 @@
+"""Python binding of libgdn.so, the MI355X (gfx950) Gated DeltaNet decode step.
+
+Argument marshalling only: every function here checks dtypes, devices and
+layouts of torch tensors, turns them into device pointers and calls the C ABI
+declared in ``include/gdn.h`` on the current torch stream (or the stream
+given).  All arithmetic runs in the HIP kernels.  There is no fallback: if
+libgdn.so is missing or a call fails, this raises.
+
+Build the library with ``python -m gated_deltanet_recurrent_decode_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["GdnError", "lib", "gdn_decode_step", "conv_decode", "slot_commit", "traffic_probe",
+           "status_string", "LIB_PATH", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+EXPORTS = ("gdn_decode_step", "conv_decode", "slot_commit", "gdn_status_string", "gdn_traffic_probe")
+
+GDN_OK = 0
+
+
+class GdnError(RuntimeError):
+    """A non-OK status from libgdn."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {status_string(status)}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "H_k", "H_v", "d_k", "d_v", "W", "N")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run: python -m gated_deltanet_recurrent_decode_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.gdn_decode_step.restype = i32
+    L.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
+    L.conv_decode.restype = i32
+    L.conv_decode.argtypes = [i32, i32, i32, i32, P, i64, P, P, P, P, P, P, i64, i32, P]
+    L.slot_commit.restype = i32
+    L.slot_commit.argtypes = [P, P, i32, P]
+    L.gdn_status_string.restype = ctypes.c_char_p
+    L.gdn_status_string.argtypes = [i32]
+    L.gdn_traffic_probe.restype = i32
+    L.gdn_traffic_probe.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != GDN_OK:
+        raise GdnError(fn, status)
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype, *, allow_none=False):
+    torch = _torch()
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    return t
+
+
+def _contig(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ entry points
+
+def gdn_decode_step(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, *,
+                    H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """One fused decode step (see ``gdn_decode_step`` in include/gdn.h).
+
+    x [B][T][C] bf16 (rows may be strided; the inner two dims contiguous),
+    conv_w [C][4] bf16, conv_b [C] bf16 or None, conv_state [N][3][C] bf16,
+    state [N][H_v][d_k][d_v] fp32, g/beta [B][T][H_v] fp32, read_slot/write_slot
+    [B] int32 (write_slot None => in place), out [B][T][H_v][d_v] bf16."""
+    torch = _torch()
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _dev(x, "x", bf)
+    for t, n, dt in ((conv_w, "conv_w", bf), (conv_state, "conv_state", bf), (state, "state", f32),
+                     (g, "g", f32), (beta, "beta", f32), (read_slot, "read_slot", i32), (out, "out", bf)):
+        _contig(_dev(t, n, dt), n)
+    _contig(_dev(conv_b, "conv_b", bf, allow_none=True), "conv_b")
+    _contig(_dev(write_slot, "write_slot", i32, allow_none=True), "write_slot")
+    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError("x: expected [B][T][C] with contiguous tokens and channels")
+    if state.dim() != 4 or conv_state.dim() != 3 or conv_w.dim() != 2:
+        raise ValueError("state must be [N][H_v][d_k][d_v], conv_state [N][W-1][C], conv_w [C][W]")
+    B, T, C = x.shape
+    N, H_v, d_k, d_v = state.shape
+    W = conv_w.shape[1]
+    if conv_state.shape != (N, W - 1, C) or conv_w.shape[0] != C:
+        raise ValueError("conv_state / conv_w do not match x and state")
+    if g.shape != (B, T, H_v) or beta.shape != (B, T, H_v) or out.shape != (B, T, H_v, d_v):
+        raise ValueError("g, beta, out do not match [B][T][H_v](, d_v)")
+    if read_slot.shape != (B,) or (write_slot is not None and write_slot.shape != (B,)):
+        raise ValueError("slot arrays must be [B]")
+    if conv_b is not None and conv_b.shape != (C,):
+        raise ValueError("conv_b must be [C]")
+    d = Dims(B, T, H_k, H_v, d_k, d_v, W, N)
+    x_row_stride = x.stride(0) if B > 0 else T * C
+    _check("gdn_decode_step", lib().gdn_decode_step(
+        ctypes.byref(d), _ptr(x), x_row_stride, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+        _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(out), float(q_scale), float(l2_eps),
+        _stream(stream)))
+
+
+def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,
+                stream=None) -> None:
+    """Pooled conv decode for one token a row (see ``conv_decode`` in include/gdn.h).
+
+    x [B][>=C] bf16 (row-strided), conv_w [C][4], conv_b [C] or None, conv_state [N][3][C],
+    read_slot/write_slot [B] int32 (write_slot None => in place), out [B][>=C] bf16 (row-strided)."""
+    torch = _torch()
+    bf, i32 = torch.bfloat16, torch.int32
+    _dev(x, "x", bf)
+    _dev(out, "out", bf)
+    for t, n, dt in ((conv_w, "conv_w", bf), (conv_state, "conv_state", bf), (read_slot, "read_slot", i32)):
+        _contig(_dev(t, n, dt), n)
+    _contig(_dev(conv_b, "conv_b", bf, allow_none=True), "conv_b")
+    _contig(_dev(write_slot, "write_slot", i32, allow_none=True), "write_slot")
+    N, Wm1, C = conv_state.shape
+    B = read_slot.shape[0]
+    if x.dim() != 2 or out.dim() != 2 or x.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("x and out must be [B][C] with contiguous channels")
+    if x.shape[0] != B or out.shape[0] != B or x.shape[1] < C or out.shape[1] < C:
+        raise ValueError("x / out do not match [B][C]")
+    _check("conv_decode", lib().conv_decode(
+        B, C, Wm1 + 1, N, _ptr(x), x.stride(0) if B > 0 else C, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+        _ptr(read_slot), _ptr(write_slot), _ptr(out), out.stride(0) if B > 0 else C, int(bool(activation)),
+        _stream(stream)))
+
+
+def slot_commit(read_slot, write_slot, *, stream=None) -> None:
+    """Swap each row's read and write slot on the device (see ``slot_commit`` in include/gdn.h)."""
+    torch = _torch()
+    _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
+    _contig(_dev(write_slot, "write_slot", torch.int32), "write_slot")
+    if read_slot.shape != write_slot.shape or read_slot.dim() != 1:
+        raise ValueError("slot arrays must both be [B]")
+    _check("slot_commit", lib().slot_commit(_ptr(read_slot), _ptr(write_slot), read_slot.shape[0],
+                                            _stream(stream)))
+
+
+def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, stream=None) -> None:
+    """The step's state traffic with no arithmetic (see ``gdn_traffic_probe`` in include/gdn.h).
+
+    mode 0 read only, 1 write only, 2 copy (twin), 3 read + write back (in place)."""
+    torch = _torch()
+    _contig(_dev(state, "state", torch.float32), "state")
+    _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
+    _contig(_dev(write_slot, "write_slot", torch.int32, allow_none=True), "write_slot")
+    _contig(_dev(sink, "sink", torch.float32), "sink")
+    N, H, d_k, d_v = state.shape
+    _check("gdn_traffic_probe", lib().gdn_traffic_probe(
+        int(mode), read_slot.shape[0], H, d_k, d_v, N, _ptr(state), _ptr(read_slot), _ptr(write_slot),
+        _ptr(sink), _stream(stream)))

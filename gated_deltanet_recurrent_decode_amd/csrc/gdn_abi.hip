@@ -1,0 +1,161 @@
+// gdn_abi.hip -- the extern "C" boundary of libgdn.so: host-side validation,
+// then one launch on the caller's stream.  Nothing here allocates, synchronises
+// or reads device memory, so every entry point can be captured into a graph.
+// The contracts are stated in include/gdn.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+} // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "inconsistent or out-of-range sizes or strides";
+    case GDN_ERR_UNSUPPORTED: return "sizes or alignment outside what the kernels are built for";
+    case GDN_ERR_REFUSED: return "refused: a twin-slot write takes one token a row (multi-token walks stay in place)";
+    case GDN_ERR_HIP: return "the HIP launch failed";
+    }
+    return "unknown gdn_status";
+}
+
+gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                           const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                           float *state, const float *g, const float *beta,
+                           const int32_t *read_slot, const int32_t *write_slot, gdn_bf16 *out,
+                           float q_scale, float l2_eps, hipStream_t stream)
+{
+    if (!dims || !x || !conv_w || !conv_state || !state || !g || !beta || !read_slot || !out)
+        return GDN_ERR_NULL;
+    const gdn_dims d = *dims;
+    if (d.B < 0 || d.T < 1 || d.H_k < 1 || d.H_v < 1 || d.N < 1 || d.H_v % d.H_k != 0)
+        return GDN_ERR_SHAPE;
+    if (!head_dim_ok(d.d_k) || !head_dim_ok(d.d_v) || d.W != 4)
+        return GDN_ERR_UNSUPPORTED;
+    const int64_t C = 2LL * d.H_k * d.d_k + (int64_t)d.H_v * d.d_v;
+    if (C > INT32_MAX || x_row_stride < (int64_t)d.T * C)
+        return GDN_ERR_SHAPE;
+    if ((int64_t)d.B * d.H_v * 4 > INT32_MAX) // workgroups in the grid
+        return GDN_ERR_SHAPE;
+    if (!(l2_eps >= 0.0f) || !isfinite(l2_eps) || !isfinite(q_scale))
+        return GDN_ERR_SHAPE;
+    const int G = d.H_v / d.H_k;
+    if (write_slot && d.T > 1)
+        return GDN_ERR_REFUSED;
+    if (!write_slot && G != 1 && G != 2 && G != 4)
+        return GDN_ERR_UNSUPPORTED;
+    if (!aligned(state, 16) || !aligned(out, 8) || !aligned(conv_w, 8))
+        return GDN_ERR_UNSUPPORTED;
+    if (d.B == 0)
+        return GDN_OK;
+
+    gdn::StepParams p{};
+    p.x = x;
+    p.x_row_stride = x_row_stride;
+    p.conv_w = conv_w;
+    p.conv_b = conv_b;
+    p.conv_state = conv_state;
+    p.state = state;
+    p.g = g;
+    p.beta = beta;
+    p.read_slot = read_slot;
+    p.write_slot = write_slot;
+    p.out = out;
+    p.q_scale = q_scale;
+    p.l2_eps = l2_eps;
+    p.B = d.B;
+    p.T = d.T;
+    p.H_k = d.H_k;
+    p.H_v = d.H_v;
+    p.N = d.N;
+    p.C = (int)C;
+    p.G = G;
+    p.twin = write_slot ? 1 : 0;
+    return from_hip(gdn::launch_gdn_step(p, d.d_k, d.d_v, stream));
+}
+
+gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,
+                       int64_t x_row_stride, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
+                       gdn_bf16 *conv_state, const int32_t *read_slot, const int32_t *write_slot,
+                       gdn_bf16 *out, int64_t out_row_stride, int32_t activation,
+                       hipStream_t stream)
+{
+    if (!x || !conv_w || !conv_state || !read_slot || !out)
+        return GDN_ERR_NULL;
+    if (B < 0 || C < 1 || N < 1 || x_row_stride < C || out_row_stride < C || B > 65535)
+        return GDN_ERR_SHAPE;
+    if (activation != 0 && activation != 1)
+        return GDN_ERR_SHAPE;
+    if (W != 4)
+        return GDN_ERR_UNSUPPORTED;
+    if (B == 0)
+        return GDN_OK;
+    gdn::ConvParams p{};
+    p.x = x;
+    p.x_row_stride = x_row_stride;
+    p.conv_w = conv_w;
+    p.conv_b = conv_b;
+    p.conv_state = conv_state;
+    p.read_slot = read_slot;
+    p.write_slot = write_slot;
+    p.out = out;
+    p.out_row_stride = out_row_stride;
+    p.B = B;
+    p.C = C;
+    p.N = N;
+    p.activation = activation;
+    return from_hip(gdn::launch_conv_decode(p, stream));
+}
+
+gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipStream_t stream)
+{
+    if (!read_slot || !write_slot)
+        return GDN_ERR_NULL;
+    if (B < 0)
+        return GDN_ERR_SHAPE;
+    return from_hip(gdn::launch_slot_commit(read_slot, write_slot, B, stream));
+}
+
+gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                             float *state, const int32_t *read_slot, const int32_t *write_slot,
+                             float *sink, hipStream_t stream)
+{
+    if (!state || !read_slot || !sink || ((mode == 1 || mode == 2) && !write_slot))
+        return GDN_ERR_NULL;
+    if (mode < 0 || mode > 3 || B < 0 || H < 1 || N < 1 || (int64_t)B * H > INT32_MAX)
+        return GDN_ERR_SHAPE;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v))
+        return GDN_ERR_UNSUPPORTED;
+    if (!aligned(state, 16))
+        return GDN_ERR_UNSUPPORTED;
+    if (B == 0)
+        return GDN_OK;
+    gdn::ProbeParams p{};
+    p.state = state;
+    p.read_slot = read_slot;
+    p.write_slot = write_slot;
+    p.sink = sink;
+    p.one = 1.0f;
+    p.B = B;
+    p.H = H;
+    p.N = N;
+    p.mode = mode;
+    return from_hip(gdn::launch_traffic_probe(p, d_k, d_v, stream));
+}
+
+} // extern "C"

@@ -1,0 +1,57 @@
+// gdn_internal.h -- kernel parameter blocks and launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Everything the fused step kernel reads; passed by value as the kernel argument.
+struct StepParams {
+    const uint16_t *x;       // [B][T][C] bf16, rows x_row_stride apart
+    int64_t x_row_stride;
+    const uint16_t *conv_w;  // [C][4] bf16
+    const uint16_t *conv_b;  // [C] bf16 or null
+    uint16_t *conv_state;    // [N][3][C] bf16
+    float *state;            // [N][H_v][d_k][d_v] fp32
+    const float *g;          // [B][T][H_v]
+    const float *beta;       // [B][T][H_v]
+    const int32_t *read_slot;
+    const int32_t *write_slot; // null in place
+    uint16_t *out;           // [B][T][H_v][d_v] bf16
+    float q_scale;
+    float l2_eps;
+    int B, T, H_k, H_v, N, C, G;
+    int n_slices; // d_v column slices per head (set by the launcher)
+    int twin;     // 1: write to write_slot; 0: in place
+};
+
+struct ConvParams {
+    const uint16_t *x;
+    int64_t x_row_stride;
+    const uint16_t *conv_w;
+    const uint16_t *conv_b;
+    uint16_t *conv_state;
+    const int32_t *read_slot;
+    const int32_t *write_slot;
+    uint16_t *out;
+    int64_t out_row_stride;
+    int B, C, N;
+    int activation;
+};
+
+struct ProbeParams {
+    float *state;
+    const int32_t *read_slot;
+    const int32_t *write_slot;
+    float *sink;
+    float one; // 1.0f, opaque to the compiler so stores of loaded values stay
+    int B, H, N, mode;
+};
+
+hipError_t launch_gdn_step(const StepParams &p, int d_k, int d_v, hipStream_t stream);
+hipError_t launch_conv_decode(const ConvParams &p, hipStream_t stream);
+hipError_t launch_slot_commit(int32_t *read_slot, int32_t *write_slot, int B, hipStream_t stream);
+hipError_t launch_traffic_probe(const ProbeParams &p, int d_k, int d_v, hipStream_t stream);
+
+} // namespace gdn

@@ -1,0 +1,370 @@
+// gdn_step.hip -- the fused Gated DeltaNet decode step for gfx950.
+//
+// One workgroup owns a tile (row r, key head hk, HPW value heads of that key
+// head, DVS of the d_v state columns).  Per tile it:
+//   1. issues the loads of its fp32 state slices (d_k x DVS per head, 16-byte
+//      loads, each wave instruction covering whole 128-byte lines), so HBM
+//      streams while the rest of the prologue runs;
+//   2. runs the conv decode + SiLU of the channels it needs (q and k of hk, v
+//      of its heads' columns) into LDS, and writes the advanced conv window of
+//      the channels it owns to the write slot;
+//   3. L2-normalises q and k (wave butterflies over LDS, done redundantly by
+//      every wave so no extra barrier is needed);
+//   4. per head: one pass over the register-resident state gives both
+//      a = S^T k^ and b = S^T q^ (in-thread over its rows, butterfly across
+//      the row groups of a wave, LDS across waves, all in a fixed order);
+//      u = beta (v - alpha a); S' = alpha S + k^ u^T; o = alpha b + u (k^.q^),
+//      which equals S'^T q^;
+//   5. stores S' to the write slot (the read slot in place) and o as bf16.
+// The delta rule is Gated DeltaNet's (decay, predict with the decayed state,
+// correct, read out); the slot handling follows mstar PR #1139, "What
+// changed" (twin slots, keep_in_place) and "Tests" (padding on slot 0).
+//
+// No MFMA: per state element the step does a handful of FMAs against 8 bytes
+// of HBM traffic, far under the fp32 ridge point, so the kernel is written for
+// bandwidth: wide coalesced loads, every tile loaded once, no re-reads.
+
+#include "device_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// Thread layout of one head slice (d_k rows x DVS columns): eight row groups
+// always, CG = DVS/4 float4 column groups, so NTH = 8 * CG threads.  Thread
+// (rg, cg) holds rows rg, rg+8, ..., columns 4cg..4cg+3.  Fixing the row
+// groups at eight makes the order of every sum over d_k the same for every
+// column split and head grouping: in-thread over m, then the pairwise tree
+// ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over row groups -- so twin and
+// in-place launches, and padded and unpadded buckets, give identical bits.
+template <int DK, int DVS, int HPW>
+struct StepCfg {
+    static constexpr int RG = 8;                   // row groups
+    static constexpr int CG = DVS / 4;             // float4 column groups in a head slice
+    static constexpr int NTH = RG * CG;            // threads per head slice
+    static constexpr int RPT = DK / RG;            // state rows held by each thread
+    static constexpr int NWH = NTH / 64;           // waves per head slice
+    static constexpr int NT = NTH * HPW;           // threads per workgroup
+    static constexpr int NCH = 2 * DK + HPW * DVS; // conv channels the workgroup needs
+    static constexpr int NCP = (NCH + NT - 1) / NT; // conv channels per thread
+    static_assert(CG >= 8 && CG <= 64 && 64 % CG == 0, "a wave must hold whole row groups");
+    static_assert(DK % RG == 0, "rows must tile the row groups");
+    static_assert(NWH == 1 || NWH == 2 || NWH == 4, "pairwise tree over at most four waves");
+    static_assert(NT <= 1024, "workgroup too large");
+};
+
+// Raw buffer resource over one head's d_k x d_v fp32 tile: every state access
+// is a 32-bit per-lane offset plus a uniform row offset, so the sixteen loads
+// of a thread share one address register, and nothing outside the tile can
+// be touched (out-of-range lanes read 0 and drop their stores).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(float *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+template <int DK, int DV, int DVS, int HPW, bool MT>
+__global__ __launch_bounds__(2 * DVS * HPW) void gdn_step_kernel(StepParams p)
+{
+    using Cfg = StepCfg<DK, DVS, HPW>;
+    static_assert(Cfg::NT == 2 * DVS * HPW, "launch bound must match the layout");
+    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH;
+    constexpr int NCH = Cfg::NCH, NCP = Cfg::NCP;
+
+    __shared__ float y_lds[NCP * NT];
+    __shared__ float4 red_lds[HPW][NWH][2][CG];
+
+    const int tid = threadIdx.x;
+    const int hloc = tid / NTH;      // head of the group this thread updates
+    const int ht = tid - hloc * NTH; // thread index inside its head slice
+    const int cg = ht % CG;
+    const int rg = ht / CG;
+    const int wv = ht >> 6;
+    const int lane = tid & 63;
+
+    // tile -> (row, key head, head group, column slice)
+    int tile = blockIdx.x;
+    const int cs = tile % p.n_slices;
+    tile /= p.n_slices;
+    const int ngrp = p.G / HPW;
+    const int grp = tile % ngrp;
+    tile /= ngrp;
+    const int hk = tile % p.H_k;
+    const int r = tile / p.H_k;
+    const int hv0 = hk * p.G + grp * HPW;
+    const int col0 = cs * DVS;
+    const int T = MT ? p.T : 1;
+
+    const int rs = p.read_slot[r];
+    const int ws = p.twin ? p.write_slot[r] : rs;
+    const bool bad = rs < 0 || rs >= p.N || ws < 0 || ws >= p.N || (p.twin && ws == rs);
+    if (rs == 0 || bad) {
+        // padding row (or a row with an unusable slot): touch no slot; out gets
+        // +0.0 for padding and NaN for the unusable slot.
+        const uint16_t fill = rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
+        for (int e = tid; e < T * HPW * DVS; e += NT) {
+            const int t = e / (HPW * DVS);
+            const int h = (e / DVS) % HPW;
+            const int j = e % DVS;
+            p.out[(((size_t)r * T + t) * p.H_v + hv0 + h) * DV + col0 + j] = fill;
+        }
+        return;
+    }
+
+    // ---- conv inputs of token 0 first: they are few and on the critical path,
+    // and loads complete in order, so issuing them before the state tile lets
+    // the conv run while the tile is still streaming in.
+    const bool own_qk = (grp == 0 && cs == 0);
+    const int C = p.C;
+    const uint16_t *xrow = p.x + (size_t)r * p.x_row_stride;
+    const uint16_t *cs_rd = p.conv_state + (size_t)rs * 3 * C;
+    uint16_t *cs_wr = p.conv_state + (size_t)ws * 3 * C;
+    // Branch-free: a lane past the last channel loads channel 0's inputs and
+    // discards them, so the loads of every lane stay in one straight run and
+    // nothing waits on them before the state loads are issued.
+    const int hv = hv0 + hloc;
+    // gates of token 0, also ahead of the state tile
+    float g_t = p.g[(size_t)r * T * p.H_v + hv];
+    float b_t = p.beta[(size_t)r * T * p.H_v + hv];
+    const uint16_t *bias_src = p.conv_b ? p.conv_b : p.conv_w; // conv_w: in-bounds stand-in, unused
+    int ch[NCP];
+    bool own[NCP];
+    uint2 wq[NCP];
+    uint16_t r0[NCP], r1[NCP], r2[NCP], xb[NCP], bb[NCP];
+#pragma unroll
+    for (int k = 0; k < NCP; ++k) {
+        const int e = tid + k * NT;
+        const bool valid = (NCH % NT == 0) || (e < NCH);
+        const int ee = valid ? e : 0;
+        const bool isq = ee < DK;
+        const bool isk = !isq && ee < 2 * DK;
+        const int ve = ee >= 2 * DK ? ee - 2 * DK : 0;
+        const int h = ve / DVS;
+        const int c = isq ? hk * DK + ee
+                    : isk ? p.H_k * DK + hk * DK + (ee - DK)
+                          : 2 * p.H_k * DK + (hv0 + h) * DV + col0 + (ve - h * DVS);
+        ch[k] = valid ? c : -1;
+        own[k] = valid && ((isq || isk) ? own_qk : true);
+        wq[k] = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)c * 4);
+        r0[k] = cs_rd[c];
+        r1[k] = cs_rd[C + c];
+        r2[k] = cs_rd[2 * C + c];
+        xb[k] = xrow[c];
+        bb[k] = bias_src[c];
+    }
+
+    // ---- state slice -> registers
+    constexpr uint32_t TILE = (uint32_t)DK * DV;
+    const __amdgpu_buffer_rsrc_t rd_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u);
+    const uint32_t voff = (uint32_t)((rg * DV + col0 + 4 * cg) * 4);
+    float4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd_tile, voff, m * RG * DV * 4, 0));
+
+    float w0[NCP], w1[NCP], w2[NCP];
+#pragma unroll
+    for (int k = 0; k < NCP; ++k) {
+        w0[k] = bf16_to_f32(r0[k]);
+        w1[k] = bf16_to_f32(r1[k]);
+        w2[k] = bf16_to_f32(r2[k]);
+    }
+
+    for (int t = 0; t < T; ++t) {
+        if (MT && t > 0) {
+            lds_barrier(); // the previous token's readers of y_lds / red_lds are done
+#pragma unroll
+            for (int k = 0; k < NCP; ++k)
+                xb[k] = xrow[(size_t)t * C + (ch[k] >= 0 ? ch[k] : 0)];
+            g_t = p.g[((size_t)r * T + t) * p.H_v + hv];
+            b_t = p.beta[((size_t)r * T + t) * p.H_v + hv];
+        }
+
+        // ---- conv decode + SiLU of this workgroup's channels -> LDS; the
+        // window advances in registers
+#pragma unroll
+        for (int k = 0; k < NCP; ++k) {
+            // lanes past the last channel compute on stand-in inputs and write
+            // the padding of y_lds, so this loop has no branch
+            const float xv = bf16_to_f32(xb[k]);
+            float acc = __uint_as_float(wq[k].x << 16) * w0[k];
+            acc = fmaf(__uint_as_float(wq[k].x & 0xffff0000u), w1[k], acc);
+            acc = fmaf(__uint_as_float(wq[k].y << 16), w2[k], acc);
+            acc = fmaf(__uint_as_float(wq[k].y & 0xffff0000u), xv, acc);
+            if (p.conv_b)
+                acc += bf16_to_f32(bb[k]);
+            y_lds[tid + k * NT] = silu(acc);
+            w0[k] = w1[k];
+            w1[k] = w2[k];
+            w2[k] = xv;
+        }
+        lds_barrier();
+
+        // ---- L2 norms of q and k (every wave computes the same sums)
+        float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int i = lane; i < DK; i += 64) {
+            const float qv = y_lds[i], kv = y_lds[DK + i];
+            sq = fmaf(qv, qv, sq);
+            sk = fmaf(kv, kv, sk);
+            sqk = fmaf(qv, kv, sqk);
+        }
+        sq = xor_sum<1>(sq);
+        sk = xor_sum<1>(sk);
+        sqk = xor_sum<1>(sqk);
+        const float rq = 1.0f / sqrtf(sq + p.l2_eps);
+        const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+        const float qs = rq * p.q_scale;
+        const float kq = sqk * rk * qs; // k^ . q^
+
+        // ---- projections of the state onto k^ and q^
+        const size_t gi = ((size_t)r * T + t) * p.H_v + hv;
+        const float alpha = expf(g_t);
+        const float bt = b_t;
+        float4 pa = f4_zero(), pb = f4_zero();
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float kh = y_lds[DK + i] * rk;
+            const float qh = y_lds[i] * qs;
+            pa.x = fmaf(s[m].x, kh, pa.x);
+            pa.y = fmaf(s[m].y, kh, pa.y);
+            pa.z = fmaf(s[m].z, kh, pa.z);
+            pa.w = fmaf(s[m].w, kh, pa.w);
+            pb.x = fmaf(s[m].x, qh, pb.x);
+            pb.y = fmaf(s[m].y, qh, pb.y);
+            pb.z = fmaf(s[m].z, qh, pb.z);
+            pb.w = fmaf(s[m].w, qh, pb.w);
+        }
+        pa.x = xor_sum<CG>(pa.x);
+        pa.y = xor_sum<CG>(pa.y);
+        pa.z = xor_sum<CG>(pa.z);
+        pa.w = xor_sum<CG>(pa.w);
+        pb.x = xor_sum<CG>(pb.x);
+        pb.y = xor_sum<CG>(pb.y);
+        pb.z = xor_sum<CG>(pb.z);
+        pb.w = xor_sum<CG>(pb.w);
+        if (lane < CG) {
+            red_lds[hloc][wv][0][cg] = pa;
+            red_lds[hloc][wv][1][cg] = pb;
+        }
+        lds_barrier();
+        // the higher row-group bits live in the wave index: finish the same
+        // pairwise tree across the waves of this head slice
+        float4 av[NWH], bv[NWH];
+#pragma unroll
+        for (int w = 0; w < NWH; ++w) {
+            av[w] = red_lds[hloc][w][0][cg];
+            bv[w] = red_lds[hloc][w][1][cg];
+        }
+#pragma unroll
+        for (int st = 1; st < NWH; st *= 2) {
+#pragma unroll
+            for (int w = 0; w + st < NWH; w += 2 * st) {
+                av[w].x += av[w + st].x; av[w].y += av[w + st].y; av[w].z += av[w + st].z; av[w].w += av[w + st].w;
+                bv[w].x += bv[w + st].x; bv[w].y += bv[w + st].y; bv[w].z += bv[w + st].z; bv[w].w += bv[w + st].w;
+            }
+        }
+        const float4 a = av[0], b = bv[0];
+
+        // ---- delta update in registers, and the read-out
+        const float *vv = &y_lds[2 * DK + hloc * DVS + 4 * cg];
+        float4 u;
+        u.x = bt * (vv[0] - alpha * a.x);
+        u.y = bt * (vv[1] - alpha * a.y);
+        u.z = bt * (vv[2] - alpha * a.z);
+        u.w = bt * (vv[3] - alpha * a.w);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const float kh = y_lds[DK + rg + RG * m] * rk;
+            s[m].x = fmaf(kh, u.x, alpha * s[m].x);
+            s[m].y = fmaf(kh, u.y, alpha * s[m].y);
+            s[m].z = fmaf(kh, u.z, alpha * s[m].z);
+            s[m].w = fmaf(kh, u.w, alpha * s[m].w);
+        }
+        if (rg == 0) {
+            const float o0 = fmaf(u.x, kq, alpha * b.x);
+            const float o1 = fmaf(u.y, kq, alpha * b.y);
+            const float o2 = fmaf(u.z, kq, alpha * b.z);
+            const float o3 = fmaf(u.w, kq, alpha * b.w);
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+            pk.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+            *reinterpret_cast<uint2 *>(p.out + (gi * DV + col0 + 4 * cg)) = pk;
+        }
+    }
+
+    // ---- advanced conv windows of the channels this workgroup owns (bf16
+    // values throughout, so the narrowing is exact)
+#pragma unroll
+    for (int k = 0; k < NCP; ++k) {
+        if (ch[k] >= 0 && own[k]) {
+            cs_wr[ch[k]] = f32_to_bf16_exact(w0[k]);
+            cs_wr[C + ch[k]] = f32_to_bf16_exact(w1[k]);
+            cs_wr[2 * C + ch[k]] = f32_to_bf16_exact(w2[k]);
+        }
+    }
+
+    // ---- new state -> write slot (the read slot in place)
+    const __amdgpu_buffer_rsrc_t wr_tile = tile_rsrc(p.state + ((size_t)ws * p.H_v + hv) * TILE, TILE * 4u);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), wr_tile, voff, m * RG * DV * 4, 0);
+}
+
+template <int DK, int DV, int DVS, int HPW, bool MT>
+static hipError_t launch_step(const StepParams &p, hipStream_t stream)
+{
+    const long long tiles = (long long)p.B * p.H_k * (p.G / HPW) * (DV / DVS);
+    if (tiles <= 0)
+        return hipSuccess;
+    StepParams q = p;
+    q.n_slices = DV / DVS;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, DVS, HPW, MT>),
+                           dim3((unsigned)tiles), dim3(StepCfg<DK, DVS, HPW>::NT), args, 0, stream);
+}
+
+// Column slices per head for a twin step: split d_v when the rows alone give
+// too few workgroups to cover the 256 compute units (slices stay >= 32 columns).
+static int pick_slices(const StepParams &p, int dv)
+{
+    const long long heads = (long long)p.B * p.H_v;
+    if (heads >= 512)
+        return 1;
+    if (heads >= 128 || dv < 128)
+        return 2;
+    return 4;
+}
+
+template <int DK, int DV>
+static hipError_t dispatch_dims(const StepParams &p, hipStream_t stream)
+{
+    if (!p.twin) {
+        // in place: one workgroup owns every channel of its key head (all G
+        // value heads, all columns), so no other workgroup reads a conv window
+        // it overwrites
+        switch (p.G) {
+        case 1: return launch_step<DK, DV, DV, 1, true>(p, stream);
+        case 2: return launch_step<DK, DV, DV, 2, true>(p, stream);
+        case 4: return launch_step<DK, DV, DV, 4, true>(p, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (pick_slices(p, DV)) {
+    case 1: return launch_step<DK, DV, DV, 1, false>(p, stream);
+    case 2: return launch_step<DK, DV, DV / 2, 1, false>(p, stream);
+    default: return launch_step<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32), 1, false>(p, stream);
+    }
+}
+
+hipError_t launch_gdn_step(const StepParams &p, int d_k, int d_v, hipStream_t stream)
+{
+    if (d_k == 128 && d_v == 128) return dispatch_dims<128, 128>(p, stream);
+    if (d_k == 64 && d_v == 64) return dispatch_dims<64, 64>(p, stream);
+    if (d_k == 128 && d_v == 64) return dispatch_dims<128, 64>(p, stream);
+    if (d_k == 64 && d_v == 128) return dispatch_dims<64, 128>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+} // namespace gdn

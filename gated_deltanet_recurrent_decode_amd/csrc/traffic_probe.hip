@@ -1,0 +1,79 @@
+// traffic_probe.hip -- the decode step's state traffic with no arithmetic (gfx950).
+//
+// Calibration in the manner of mstar PR #1139, "Numbers": a kernel with the
+// GDN step's reads and writes and no math, plus its read-only and write-only
+// halves, gives the practical bandwidth ceiling of this access pattern.  The
+// grid, thread layout and slot addressing are those of the fused step with
+// one head per workgroup and whole d_v rows.
+
+#include "device_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+template <int DK, int DV, int NTH>
+__global__ __launch_bounds__(NTH) void traffic_probe_kernel(ProbeParams p)
+{
+    constexpr int CG = DV / 4, RG = NTH / CG, RPT = DK / RG;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const int h = blockIdx.x % p.H;
+    const int r = blockIdx.x / p.H;
+    const int rs = p.read_slot[r];
+    const int ws = (p.mode == 0 || p.mode == 3) ? rs : p.write_slot[r];
+    if (rs <= 0 || rs >= p.N || ws <= 0 || ws >= p.N)
+        return;
+    constexpr size_t TILE = (size_t)DK * DV;
+    const size_t off = 4 * cg;
+    const float *src = p.state + ((size_t)rs * p.H + h) * TILE + off;
+    float *dst = p.state + ((size_t)ws * p.H + h) * TILE + off;
+    float4 s[RPT];
+    if (p.mode != 1) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            s[m] = *reinterpret_cast<const float4 *>(src + (size_t)(rg + RG * m) * DV);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            s[m] = make_float4(p.one, p.one, p.one, p.one);
+    }
+    if (p.mode == 0) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            acc += s[m].x + s[m].y + s[m].z + s[m].w;
+        if (acc == -3.0e38f) // never true for finite state; keeps the loads alive
+            p.sink[0] = acc;
+        return;
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        float4 v = s[m];
+        v.x *= p.one; v.y *= p.one; v.z *= p.one; v.w *= p.one;
+        *reinterpret_cast<float4 *>(dst + (size_t)(rg + RG * m) * DV) = v;
+    }
+}
+
+template <int DK, int DV>
+static hipError_t launch_probe(const ProbeParams &p, hipStream_t stream)
+{
+    constexpr int NTH = (DK * DV >= 128 * 128) ? 256 : 128;
+    const long long tiles = (long long)p.B * p.H;
+    if (tiles <= 0)
+        return hipSuccess;
+    ProbeParams q = p;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&traffic_probe_kernel<DK, DV, NTH>), dim3((unsigned)tiles),
+                           dim3(NTH), args, 0, stream);
+}
+
+hipError_t launch_traffic_probe(const ProbeParams &p, int d_k, int d_v, hipStream_t stream)
+{
+    if (d_k == 128 && d_v == 128) return launch_probe<128, 128>(p, stream);
+    if (d_k == 64 && d_v == 64) return launch_probe<64, 64>(p, stream);
+    if (d_k == 128 && d_v == 64) return launch_probe<128, 64>(p, stream);
+    if (d_k == 64 && d_v == 128) return launch_probe<64, 128>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+} // namespace gdn

@@ -1,0 +1,171 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the pooled Gated DeltaNet decode step for
+ * MI355X (gfx950), its conv decode, and slot commit.
+ *
+ * Sources (the mstar pull-request pages):
+ *   PR #1139, "Why" and "Numbers": the GDN rule of a Qwen3.5 decode step is
+ *     state traffic -- the recurrent state is read from the pool and written
+ *     back once per step, and writing a second slot instead of the one just
+ *     read is cheaper.
+ *   PR #1139, "What changed": a request holds two slots (twin_slots); a decode
+ *     step reads one and writes the other, commit swaps them; prefill, split
+ *     walks and the mixed step's decode half update in place (keep_in_place);
+ *     both give the same values.  causal_conv1d_decode advances the conv
+ *     window by one token a row and honours a separate write slot.
+ *   PR #1139, "Tests", and PR #965, "What changed": padding rows address the
+ *     null slot 0 and leave every real row's result unchanged.
+ *   PR #965 review notes: a captured step must not allocate.
+ *   The update rule is Gated DeltaNet's (Yang et al., ICLR 2025); the pages
+ *   name it but never print it.
+ *
+ * Conventions for every entry point:
+ *   - Every array pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees, synchronises the host or reads device
+ *     memory from the host, so every call is stream-ordered on `stream` and
+ *     can be captured into a HIP graph.
+ *   - bf16 values travel as their 16-bit patterns (gdn_bf16).
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-OK status means nothing was enqueued (GDN_ERR_HIP: the launch
+ *     itself failed).
+ *   - Preconditions NOT checked on the host (they live in device memory):
+ *     slot values lie in [0, N); no two real rows share a slot; for a twin
+ *     write a real row's write slot differs from its read slot and from every
+ *     other row's slots.  The kernels bounds-check every slot they read: a
+ *     row with a slot outside [0, N), or a twin row whose write slot equals
+ *     its read slot, touches no pool memory and gets NaN in every output
+ *     element instead.
+ *   - Calls that overlap on the same pool slots race (as any two kernels
+ *     writing the same memory would).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t gdn_bf16; /* bfloat16 bit pattern */
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes or strides */
+    GDN_ERR_UNSUPPORTED = 3, /* sizes outside what the kernels are built for */
+    GDN_ERR_REFUSED = 4,     /* a twin-slot write with more than one token a row */
+    GDN_ERR_HIP = 5          /* the HIP launch returned an error */
+} gdn_status;
+
+/* Sizes of one decode step.
+ *   B    rows (requests) in the step; 0 is allowed and enqueues nothing
+ *   T    tokens per row, processed in order (T > 1 only in place)
+ *   H_k  key heads;  H_v value heads, a multiple of H_k; value head hv reads
+ *        key head hv / (H_v / H_k)
+ *   d_k, d_v  head dims, each 64 or 128
+ *   W    conv width (4)
+ *   N    slots in the pool, including the null slot 0
+ * The conv runs over C = 2*H_k*d_k + H_v*d_v channels ordered q | k | v,
+ * head-major. */
+typedef struct gdn_dims {
+    int32_t B, T, H_k, H_v, d_k, d_v, W, N;
+} gdn_dims;
+
+/*
+ * gdn_decode_step -- one fused GDN decode step over B rows of a slot pool
+ * (PR #1139, "What changed": twin slots and keep_in_place; "Tests": padding
+ * on the null slot; Gated DeltaNet's rule for the update).
+ *
+ * For each row r with rs = read_slot[r] and ws = write_slot[r] (ws = rs when
+ * write_slot is NULL, the in-place mode), for t = 0..T-1, all in fp32:
+ *   conv:   for each channel c, win = [conv_state[rs][0..W-2][c], x[r][t][c]],
+ *           y[c] = silu(sum_w conv_w[c][w] * win[w] (+ conv_b[c])); the
+ *           window advances by one token
+ *   split:  q = y[hk*d_k ..], k = y[H_k*d_k + hk*d_k ..],
+ *           v = y[2*H_k*d_k + hv*d_v ..], hk = hv / (H_v/H_k)
+ *   norm:   q^ = q / sqrt(sum q^2 + l2_eps) * q_scale, k^ = k / sqrt(sum k^2 + l2_eps)
+ *   rule:   alpha = exp(g[r][t][hv]), b = beta[r][t][hv]
+ *           S <- alpha * S;  S <- S + b * k^ (v - S^T k^)^T;  o = S^T q^
+ *   out[r][t][hv][:] = o rounded to bf16 (nearest even)
+ * then S goes to state[ws] and the advanced window to conv_state[ws].
+ * A row with rs == 0 is padding: its out is +0.0 and it reads and writes no
+ * slot, so slot 0 stays as it is.
+ *
+ * Layouts (all contiguous unless a stride is given):
+ *   x          [B][T][C] bf16; rows x_row_stride elements apart (>= T*C)
+ *   conv_w     [C][W] bf16;  conv_b [C] bf16 or NULL
+ *   conv_state [N][W-1][C] bf16 (oldest input first)
+ *   state      [N][H_v][d_k][d_v] fp32, S[i][j] with i over keys
+ *   g, beta    [B][T][H_v] fp32 (log decay, and the delta-rule strength)
+ *   read_slot, write_slot  [B] int32; write_slot NULL => in place
+ *   out        [B][T][H_v][d_v] bf16
+ * Twin mode reads only read slots and writes only write slots and out; in
+ * place reads and writes the read slots.  T > 1 with a twin write returns
+ * GDN_ERR_REFUSED (multi-token walks stay in place).  In place needs
+ * H_v/H_k in {1, 2, 4}.  Alignment: state 16 bytes, out and conv_w 8 bytes
+ * (GDN_ERR_UNSUPPORTED otherwise).
+ */
+gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                           const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                           float *state, const float *g, const float *beta,
+                           const int32_t *read_slot, const int32_t *write_slot, gdn_bf16 *out,
+                           float q_scale, float l2_eps, hipStream_t stream);
+
+/*
+ * conv_decode -- the pooled conv update for one token a row, standalone
+ * (PR #1139, "What changed": causal_conv1d_decode, with null slots, strided
+ * rows, optional bias and activation, and a write slot that leaves the read
+ * slot alone).
+ *
+ * For each row r with rs = read_slot[r], ws = write_slot ? write_slot[r] : rs,
+ * and each channel c < C:
+ *   win = [conv_state[rs][0..W-2][c], x[r][c]]
+ *   y   = sum_w conv_w[c][w] * win[w] (+ conv_b[c]), in fp32
+ *   out[r][c] = bf16(activation ? silu(y) : y)
+ *   conv_state[ws][..][c] = win[1..W-1]   (a bit-exact shift of bf16 values)
+ * A row with rs == 0 gets +0.0 outputs and touches no slot.
+ *   x   [B][C] bf16, rows x_row_stride elements apart (>= C)
+ *   out [B][C] bf16, rows out_row_stride elements apart (>= C)
+ *   activation: 0 none, 1 SiLU.  W must be 4.
+ */
+gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,
+                       int64_t x_row_stride, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
+                       gdn_bf16 *conv_state, const int32_t *read_slot, const int32_t *write_slot,
+                       gdn_bf16 *out, int64_t out_row_stride, int32_t activation,
+                       hipStream_t stream);
+
+/*
+ * slot_commit -- commit of a twin-slot step (PR #1139, "What changed"): each
+ * row's read and write slot trade places on the device, stream-ordered after
+ * the step, so the next step reads what this one wrote.  Rows whose two
+ * slots are equal (in place, padding on slot 0) are unchanged.
+ *   read_slot, write_slot [B] int32.  B = 0 enqueues nothing.
+ */
+gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipStream_t stream);
+
+/* Static text for a status code (host only). */
+const char *gdn_status_string(gdn_status status);
+
+/*
+ * gdn_traffic_probe -- calibration: the state traffic of gdn_decode_step at
+ * the same shapes, grid and access pattern, with no arithmetic (the method
+ * of PR #1139, "Numbers": a kernel with the step's reads and writes and no
+ * math, and its read-only and write-only halves).
+ *   mode 0  read only: reads every real row's read-slot tiles
+ *   mode 1  write only: writes every real row's write-slot tiles
+ *   mode 2  copy: reads the read slot, writes the write slot (twin traffic)
+ *   mode 3  in place: reads the read slot and writes it back
+ * state is [N][H][d_k][d_v] fp32; rows with read slot 0 are skipped.
+ * sink [1] fp32 receives nothing in practice; it only keeps the read-only
+ * mode's loads alive.  d_k, d_v in {64, 128}.
+ */
+gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                             float *state, const int32_t *read_slot, const int32_t *write_slot,
+                             float *sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,111 @@
+"""The C ABI of libgdn.so on the CPU: it loads, exports every function that
+include/gdn.h declares, and its host-side validation refuses bad arguments with
+the documented status before anything is launched (no GPU needed: every call
+here fails validation, so no kernel is enqueued).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_recurrent_decode_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL, SHAPE, UNSUPPORTED, REFUSED, HIP = range(6)
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in nm.stdout.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+
+
+def test_status_strings():
+    for s in range(6):
+        assert gdn.status_string(s)
+    assert gdn.status_string(0) == "ok"
+    assert "unknown" in gdn.status_string(99)
+
+
+def _dims(**kw):
+    base = dict(B=4, T=1, H_k=4, H_v=4, d_k=64, d_v=64, W=4, N=9)
+    base.update(kw)
+    return gdn.Dims(*[base[k] for k in ("B", "T", "H_k", "H_v", "d_k", "d_v", "W", "N")])
+
+
+def _step(d, *, x=FAKE, stride=None, conv_w=FAKE, state=FAKE, out=FAKE, write_slot=FAKE, eps=1e-6, qs=1.0,
+          dims_ptr=True):
+    C = 2 * d.H_k * d.d_k + d.H_v * d.d_v
+    st = d.T * C if stride is None else stride
+    return gdn.lib().gdn_decode_step(ctypes.byref(d) if dims_ptr else None, x, st, conv_w, None, FAKE, state,
+                                     FAKE, FAKE, FAKE, write_slot, out, qs, eps, None)
+
+
+def test_step_validation():
+    assert _step(_dims(), dims_ptr=False) == NULL
+    assert _step(_dims(), x=None) == NULL
+    assert _step(_dims(), out=None) == NULL
+    assert _step(_dims(B=-1)) == SHAPE
+    assert _step(_dims(T=0)) == SHAPE
+    assert _step(_dims(H_k=3, H_v=4)) == SHAPE
+    assert _step(_dims(N=0)) == SHAPE
+    assert _step(_dims(d_k=96)) == UNSUPPORTED
+    assert _step(_dims(d_v=256)) == UNSUPPORTED
+    assert _step(_dims(W=3)) == UNSUPPORTED
+    d = _dims()
+    assert _step(d, stride=2 * 4 * 64 + 4 * 64 - 1) == SHAPE
+    assert _step(_dims(), eps=-1.0) == SHAPE
+    assert _step(_dims(), qs=float("nan")) == SHAPE
+    # twin writes take one token a row; multi-token walks stay in place
+    assert _step(_dims(T=4)) == REFUSED
+    # in place needs H_v / H_k in {1, 2, 4}
+    assert _step(_dims(H_k=1, H_v=8), write_slot=None) == UNSUPPORTED
+    # alignment
+    assert _step(_dims(), state=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert _step(_dims(), out=ctypes.c_void_p(0x10002)) == UNSUPPORTED
+    assert _step(_dims(), conv_w=ctypes.c_void_p(0x10004)) == UNSUPPORTED
+
+
+def test_conv_decode_validation():
+    f = gdn.lib().conv_decode
+    assert f(4, 16, 4, 9, None, 16, FAKE, None, FAKE, FAKE, None, FAKE, 16, 1, None) == NULL
+    assert f(-1, 16, 4, 9, FAKE, 16, FAKE, None, FAKE, FAKE, None, FAKE, 16, 1, None) == SHAPE
+    assert f(4, 16, 4, 9, FAKE, 15, FAKE, None, FAKE, FAKE, None, FAKE, 16, 1, None) == SHAPE
+    assert f(4, 16, 4, 9, FAKE, 16, FAKE, None, FAKE, FAKE, None, FAKE, 15, 1, None) == SHAPE
+    assert f(4, 16, 4, 9, FAKE, 16, FAKE, None, FAKE, FAKE, None, FAKE, 16, 2, None) == SHAPE
+    assert f(4, 16, 3, 9, FAKE, 16, FAKE, None, FAKE, FAKE, None, FAKE, 16, 1, None) == UNSUPPORTED
+
+
+def test_slot_commit_and_probe_validation():
+    L = gdn.lib()
+    assert L.slot_commit(None, FAKE, 4, None) == NULL
+    assert L.slot_commit(FAKE, FAKE, -1, None) == SHAPE
+    assert L.gdn_traffic_probe(2, 4, 4, 64, 64, 9, FAKE, FAKE, None, FAKE, None) == NULL
+    assert L.gdn_traffic_probe(7, 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(0, 4, 4, 96, 64, 9, FAKE, FAKE, None, FAKE, None) == UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdn, "_lib", None)
+    with pytest.raises(ImportError):
+        gdn.lib()

@@ -1,0 +1,389 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, at small shapes that span several tiles and ragged rows and
+at the full workload sizes, plus the relational invariants the mstar pages
+test for this path (PR #1139 "Tests": twin == in place, a twin step touches no
+other slot, conv decode with null slots / strided rows / write slots; PR #965
+"What changed": padding width changes no real row).
+
+Tolerances are the ones in tests/helpers.py.
+"""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import oracle
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_recurrent_decode_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+def _check_step(gdn, case, *, twin=True, q_scale=1.0, layer=0, step_i=0, poison=True):
+    """One step on GPU and oracle; compare out, every written slot, and that
+    nothing else in the pool changed."""
+    t = H.torch()
+    s = case.shape
+    pool = case.pools[layer]
+    step = case.steps[step_i][layer]
+    hp = H.HostPool(pool)
+    dp = H.DevPool(pool)
+    real = pool.read_slot != 0
+    if twin and poison:
+        # NaN-poison the write slots: every element must be written by the step
+        wr_real = t.from_numpy(pool.write_slot[real].astype(np.int64)).cuda()
+        dp.state[wr_real] = float("nan")
+    before_state = dp.state.clone()
+    before_conv = dp.conv_state.clone()
+    out = H.gpu_step(gdn, dp, step, s, twin=twin, q_scale=q_scale)
+    ref = H.oracle_step(oracle, hp, step, s, twin=twin, q_scale=q_scale)
+    t.cuda.synchronize()
+    H.assert_out_close(out, ref)
+    written = sorted({int(x) for x in (pool.write_slot if twin else pool.read_slot)[real]})
+    idx = t.tensor(written, dtype=t.int64, device="cuda")
+    H.assert_state_close(dp.state[idx].cpu().numpy(), hp.state[written])
+    np.testing.assert_array_equal(H.bf16_host(dp.conv_state[idx]), hp.conv_state[written])
+    # nothing but the written slots changed (bitwise, NaN-aware)
+    mask = t.ones(s.N, dtype=t.bool, device="cuda")
+    mask[idx] = False
+    assert t.equal(dp.state[mask].view(t.int32), before_state[mask].view(t.int32)), "a slot outside the write set changed"
+    assert t.equal(dp.conv_state[mask].view(t.int16), before_conv[mask].view(t.int16))
+    return dp, out
+
+
+# ------------------------------------------------------------------ small shapes
+
+SMALL = [
+    # B, T, H_k, H_v, d, d_v, twin, real_rows
+    (4, 1, 4, 4, 64, 64, True, None),      # the tiny workload's shapes
+    (5, 1, 2, 2, 128, 128, True, None),    # ragged rows, column-split tiles (4 slices)
+    (3, 1, 2, 4, 128, 128, True, None),    # GQA, G = 2
+    (2, 1, 1, 4, 64, 64, True, None),      # GQA, G = 4
+    (7, 1, 2, 2, 128, 64, True, None),     # d_k != d_v
+    (6, 1, 2, 2, 64, 128, True, 4),        # padding rows on slot 0
+    (40, 1, 4, 4, 128, 128, True, None),   # 160 heads: 2 slices
+    (150, 1, 2, 4, 64, 64, True, None),    # 600 heads: whole tiles
+    (5, 1, 2, 2, 128, 128, False, None),   # in place
+    (3, 3, 2, 4, 128, 128, False, None),   # in place, 3 tokens, G = 2
+    (4, 2, 1, 4, 64, 64, False, 3),        # in place, G = 4, padding
+    (9, 4, 2, 2, 64, 128, False, None),    # in place, 4 tokens
+]
+
+
+@pytest.mark.parametrize("B,T,hk,hv,d,dv,twin,real", SMALL,
+                         ids=[f"B{c[0]}-T{c[1]}-{c[2]}x{c[3]}-d{c[4]}x{c[5]}-{'twin' if c[6] else 'inplace'}"
+                              f"{'' if c[7] is None else '-pad'}" for c in SMALL])
+def test_small_shapes_match_oracle(gdn, torch, B, T, hk, hv, d, dv, twin, real):
+    case = gi.small(B=B, T=T, H_k=hk, H_v=hv, d=d, d_v=dv, twin=twin, real_rows=real, seed=B * 7 + T)
+    _check_step(gdn, case, twin=twin)
+
+
+def test_q_scale(gdn, torch):
+    case = gi.small(B=3, T=1, H_k=2, H_v=2, d=128, seed=5)
+    _check_step(gdn, case, q_scale=128 ** -0.5)
+
+
+def test_conv_bias(gdn, torch):
+    t = torch
+    case = gi.small(B=3, T=1, H_k=2, H_v=2, d=64, seed=6)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    bias = gi.bf16_bits(np.random.Generator(np.random.PCG64(9)).standard_normal(s.C).astype(np.float32))
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    out = H.gpu_step(gdn, dp, step, s, conv_b=H.bf16_dev(bias))
+    ref = oracle.gdn_decode_step(step.x, hp.conv_w, bias, hp.conv_state, hp.state, step.g, step.beta, hp.rd, hp.wr,
+                                 H_k=s.H_k)
+    t.cuda.synchronize()
+    H.assert_out_close(out, ref)
+    wr = [int(x) for x in pool.write_slot]
+    H.assert_state_close(dp.state[wr].cpu().numpy(), hp.state[wr])
+
+
+# ------------------------------------------------------------------ workload: tiny, 8 chained steps
+
+def test_tiny_eight_chained_steps_with_commit(gdn, torch):
+    t = torch
+    case = gi.tiny()
+    s, pool = case.shape, case.pools[0]
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    for k in range(8):
+        step = case.steps[k][0]
+        out = H.gpu_step(gdn, dp, step, s)
+        ref = H.oracle_step(oracle, hp, step, s)
+        gdn.slot_commit(dp.rd, dp.wr)
+        oracle.slot_commit(hp.rd, hp.wr)
+        t.cuda.synchronize()
+        H.assert_out_close(out, ref, f"out step {k}")
+        H.assert_state_close(dp.state.cpu().numpy(), hp.state, f"pool after step {k}")
+        np.testing.assert_array_equal(H.bf16_host(dp.conv_state), hp.conv_state)
+        np.testing.assert_array_equal(dp.rd.cpu().numpy(), hp.rd)
+        np.testing.assert_array_equal(dp.wr.cpu().numpy(), hp.wr)
+
+
+# ------------------------------------------------------------------ workload: 0.8B layer, 64 rows
+
+def test_08b_layer_64_rows_twin(gdn, torch):
+    case = gi.qwen08b()
+    _check_step(gdn, case)
+
+
+# ------------------------------------------------------------------ workload: row sweep, twin and in place
+
+@pytest.mark.parametrize("B", gi.SWEEP_ROWS)
+def test_sweep_twin_and_in_place(gdn, torch, B):
+    t = torch
+    case = gi.qwen08b(B=B)
+    dp_t, out_t = _check_step(gdn, case, twin=True, poison=False)
+    dp_i, out_i = _check_step(gdn, case, twin=False)
+    # same values from both write modes, bit for bit (PR #1139: same kernel, same values)
+    assert t.equal(out_t.view(t.int16), out_i.view(t.int16))
+    pool = case.pools[0]
+    wr = t.from_numpy(pool.write_slot.astype(np.int64)).cuda()
+    rd = t.from_numpy(pool.read_slot.astype(np.int64)).cuda()
+    assert t.equal(dp_t.state[wr].view(t.int32), dp_i.state[rd].view(t.int32))
+    assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
+
+
+# ------------------------------------------------------------------ workload: 9B-like, 24 layers
+
+def test_9b_24_layers_back_to_back_sampled_rows(gdn, torch):
+    t = torch
+    case = gi.qwen9b()
+    s = case.shape
+    dps = [H.DevPool(p) for p in case.pools]
+    outs = [H.gpu_step(gdn, dps[L], case.steps[0][L], s) for L in range(24)]
+    t.cuda.synchronize()
+    rows = [0, 17, 40, 63]
+    for L in range(24):
+        pool = case.pools[L]
+        hp = H.HostPool(pool)
+        ref = H.oracle_step(oracle, hp, case.steps[0][L], s, rows=rows)
+        H.assert_out_close(outs[L][rows], ref, f"layer {L} out")
+        wr = [int(pool.write_slot[r]) for r in rows]
+        H.assert_state_close(dps[L].state[wr].cpu().numpy(), hp.state[wr], f"layer {L} state")
+        np.testing.assert_array_equal(H.bf16_host(dps[L].conv_state[wr]), hp.conv_state[wr])
+
+
+# ------------------------------------------------------------------ workload: padded bucket
+
+def test_padded_bucket_twin_real_rows_identical_to_unpadded(gdn, torch):
+    t = torch
+    case = gi.padded()
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp, out = _check_step(gdn, case)
+    assert t.count_nonzero(out[gi.PADDED_REAL:].view(t.int16)) == 0, "padding rows must read out +0.0"
+    assert t.count_nonzero(dp.state[0].view(t.int32)) == 0 and t.count_nonzero(dp.conv_state[0].view(t.int16)) == 0
+    # the same 46 rows without the padding: bit-identical outputs and state
+    n = gi.PADDED_REAL
+    dp2 = H.DevPool(pool)
+    dp2.rd, dp2.wr = dp2.rd[:n].contiguous(), dp2.wr[:n].contiguous()
+    sub = gi.StepInputs(np.ascontiguousarray(step.x[:n]), np.ascontiguousarray(step.g[:n]),
+                        np.ascontiguousarray(step.beta[:n]))
+    out2 = H.gpu_step(gdn, dp2, sub, s)
+    t.cuda.synchronize()
+    assert t.equal(out[:n].view(t.int16), out2.view(t.int16))
+    wr = t.from_numpy(pool.write_slot[:n].astype(np.int64)).cuda()
+    assert t.equal(dp.state[wr].view(t.int32), dp2.state[wr].view(t.int32))
+    assert t.equal(dp.conv_state[wr].view(t.int16), dp2.conv_state[wr].view(t.int16))
+
+
+def test_padded_bucket_in_place_four_tokens(gdn, torch):
+    t = torch
+    case = gi.padded(T=4, twin=False)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp, out4 = _check_step(gdn, case, twin=False)
+    # four single-token in-place calls give the same bits as one four-token call
+    dp1 = H.DevPool(pool)
+    for k in range(4):
+        sub = gi.StepInputs(np.ascontiguousarray(step.x[:, k:k + 1]), np.ascontiguousarray(step.g[:, k:k + 1]),
+                            np.ascontiguousarray(step.beta[:, k:k + 1]))
+        o = H.gpu_step(gdn, dp1, sub, s, twin=False)
+        assert t.equal(o[:, 0].view(t.int16), out4[:, k].view(t.int16)), f"token {k}"
+    assert t.equal(dp1.state.view(t.int32), dp.state.view(t.int32))
+    assert t.equal(dp1.conv_state.view(t.int16), dp.conv_state.view(t.int16))
+
+
+# ------------------------------------------------------------------ standalone conv decode
+
+@pytest.mark.parametrize("bias,act,twin", [(False, True, True), (True, True, True), (False, False, True),
+                                           (True, False, False)])
+def test_conv_decode_matches_oracle(gdn, torch, bias, act, twin):
+    t = torch
+    rng = np.random.Generator(np.random.PCG64(11))
+    B, C, N = 7, 6144 + 40, 17
+    w = gi.bf16_bits(rng.uniform(-0.5, 0.5, (C, 4)).astype(np.float32))
+    b = gi.bf16_bits(rng.standard_normal(C).astype(np.float32)) if bias else None
+    cs = np.zeros((N, 3, C), np.uint16)
+    cs[1:] = gi.bf16_bits(rng.standard_normal((N - 1, 3, C)).astype(np.float32))
+    # strided rows: x and out rows padded past C
+    xs = gi.bf16_bits(rng.standard_normal((B, C + 24)).astype(np.float32))
+    rd = np.array([3, 0, 5, 7, 9, 0, 1], np.int32)
+    wr = np.array([4, 0, 6, 8, 10, 0, 2], np.int32) if twin else rd.copy()
+    cs_dev = H.bf16_dev(cs)
+    out = t.zeros((B, C + 8), dtype=t.bfloat16, device="cuda")
+    before = cs_dev.clone()
+    gdn.conv_decode(H.bf16_dev(xs)[:, :], H.bf16_dev(w), None if b is None else H.bf16_dev(b), cs_dev,
+                    t.from_numpy(rd).cuda(), t.from_numpy(wr).cuda() if twin else None, out, activation=act)
+    cs_ref = cs.copy()
+    ref = oracle.conv_decode(np.ascontiguousarray(xs), w, b, cs_ref, rd, wr if twin else None, act=act)
+    t.cuda.synchronize()
+    got = H.bf16_host_f64(out[:, :C])
+    # output: fp32 arithmetic rounded once to bf16 -> within one bf16 ulp of the fp64 value
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(got - ref) <= ulp + 1e-30), np.max(np.abs(got - ref) / ulp)
+    np.testing.assert_array_equal(H.bf16_host(cs_dev), cs_ref)
+    # padding rows zero; the read slot stays as it was in twin mode
+    assert np.all(got[[1, 5]] == 0)
+    if twin:
+        for r in rd[rd != 0]:
+            assert t.equal(cs_dev[int(r)].view(t.int16), before[int(r)].view(t.int16))
+
+
+# ------------------------------------------------------------------ slot commit
+
+def test_slot_commit(gdn, torch):
+    t = torch
+    rd0 = np.array([1, 0, 5, 7, 9], np.int32)
+    wr0 = np.array([2, 0, 6, 7, 10], np.int32)
+    rd, wr = t.from_numpy(rd0).cuda(), t.from_numpy(wr0).cuda()
+    gdn.slot_commit(rd, wr)
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(rd.cpu().numpy(), wr0)
+    np.testing.assert_array_equal(wr.cpu().numpy(), rd0)
+    gdn.slot_commit(rd, wr)
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(rd.cpu().numpy(), rd0)
+    np.testing.assert_array_equal(wr.cpu().numpy(), wr0)
+    # more rows than one launch's threads: the grid-stride loop covers them all
+    ar = t.arange(1, 300001, dtype=t.int32, device="cuda")
+    big, big2 = ar.clone(), ar + 7
+    gdn.slot_commit(big, big2)
+    t.cuda.synchronize()
+    assert t.equal(big, ar + 7)
+    assert t.equal(big2, ar)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_step_is_a_no_op(gdn, torch):
+    t = torch
+    case = gi.small(B=2, T=1, H_k=2, H_v=2, d=64)
+    s, pool = case.shape, case.pools[0]
+    dp = H.DevPool(pool)
+    before = dp.state.clone()
+    out = t.empty((0, 1, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    gdn.gdn_decode_step(t.empty((0, 1, s.C), dtype=t.bfloat16, device="cuda"), dp.conv_w, None, dp.conv_state,
+                        dp.state, t.empty((0, 1, s.H_v), device="cuda"), t.empty((0, 1, s.H_v), device="cuda"),
+                        dp.rd[:0], dp.wr[:0], out, H_k=s.H_k)
+    gdn.slot_commit(dp.rd[:0], dp.wr[:0])
+    t.cuda.synchronize()
+    assert t.equal(before, dp.state)
+
+
+def test_unusable_slots_give_nan_and_touch_nothing(gdn, torch):
+    t = torch
+    case = gi.small(B=3, T=1, H_k=2, H_v=2, d=64, N=9)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp = H.DevPool(pool)
+    rd = pool.read_slot.copy()
+    wr = pool.write_slot.copy()
+    rd[1] = s.N + 5      # out of range
+    wr[2] = rd[2]        # twin row writing over its own read slot
+    dp.rd, dp.wr = t.from_numpy(rd).cuda(), t.from_numpy(wr).cuda()
+    before_s, before_c = dp.state.clone(), dp.conv_state.clone()
+    out = H.gpu_step(gdn, dp, step, s)
+    t.cuda.synchronize()
+    o = H.bf16_host_f64(out)
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and not np.isnan(o[0]).any()
+    mask = t.ones(s.N, dtype=t.bool, device="cuda")
+    mask[int(wr[0])] = False
+    assert t.equal(dp.state[mask], before_s[mask])
+    assert t.equal(dp.conv_state[mask].view(t.int16), before_c[mask].view(t.int16))
+
+
+def test_refusals_through_the_binding(gdn, torch):
+    t = torch
+    case = gi.small(B=2, T=2, H_k=2, H_v=2, d=64)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp = H.DevPool(pool)
+    with pytest.raises(gdn.GdnError) as e:
+        H.gpu_step(gdn, dp, step, s, twin=True)
+    assert e.value.status == 4
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_replay_of_step_and_commit_matches_eager(gdn, torch):
+    """Step + commit captured once and replayed several times, with eager work
+    between replays, gives the bits of the same steps run eagerly."""
+    t = torch
+    case = gi.small(B=16, T=1, H_k=4, H_v=4, d=128, steps=1, seed=21)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp_e, dp_g = H.DevPool(pool), H.DevPool(pool)
+    x, g, beta = H.bf16_dev(step.x), t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda()
+    out_e = t.empty((s.B, 1, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    out_g = t.empty_like(out_e)
+
+    def run(dp, out):
+        gdn.gdn_decode_step(x, dp.conv_w, None, dp.conv_state, dp.state, g, beta, dp.rd, dp.wr, out, H_k=s.H_k)
+        gdn.slot_commit(dp.rd, dp.wr)
+
+    stream = t.cuda.Stream()
+    graph = t.cuda.CUDAGraph()
+    # capture on a copy of the pool that is then reset, so the first replay starts from the initial state
+    with t.cuda.stream(stream):
+        run(dp_g, out_g)  # warm-up outside capture
+    t.cuda.synchronize()
+    dp_g.state.copy_(t.from_numpy(pool.state).cuda())
+    dp_g.conv_state.copy_(H.bf16_dev(pool.conv_state))
+    dp_g.rd.copy_(t.from_numpy(pool.read_slot).cuda())
+    dp_g.wr.copy_(t.from_numpy(pool.write_slot).cuda())
+    t.cuda.synchronize()
+    with t.cuda.graph(graph, stream=stream):
+        run(dp_g, out_g)
+    t.cuda.synchronize()
+    # capture does not execute: the pool must still be the initial one
+    assert t.equal(dp_g.state, t.from_numpy(pool.state).cuda())
+    for k in range(4):
+        run(dp_e, out_e)
+        graph.replay()
+        t.cuda.synchronize()
+        _ = (dp_e.state.sum() + 1).item()  # eager work between replays
+        assert t.equal(out_g.view(t.int16), out_e.view(t.int16)), f"replay {k}"
+        assert t.equal(dp_g.state.view(t.int32), dp_e.state.view(t.int32)), f"replay {k}"
+        assert t.equal(dp_g.rd, dp_e.rd) and t.equal(dp_g.wr, dp_e.wr)
+
+
+# ------------------------------------------------------------------ calibration probe
+
+def test_traffic_probe_moves_the_tiles(gdn, torch):
+    t = torch
+    case = gi.small(B=4, T=1, H_k=2, H_v=2, d=128, N=11)
+    pool = case.pools[0]
+    dp = H.DevPool(pool)
+    sink = t.zeros(1, device="cuda")
+    rd = [int(x) for x in pool.read_slot]
+    wr = [int(x) for x in pool.write_slot]
+    gdn.traffic_probe(2, dp.state, dp.rd, dp.wr, sink)           # copy
+    t.cuda.synchronize()
+    assert t.equal(dp.state[wr], dp.state[rd])
+    gdn.traffic_probe(1, dp.state, dp.rd, dp.wr, sink)           # write only
+    t.cuda.synchronize()
+    assert bool((dp.state[wr] == 1.0).all())
+    before = dp.state.clone()
+    gdn.traffic_probe(3, dp.state, dp.rd, None, sink)            # in place, values unchanged
+    gdn.traffic_probe(0, dp.state, dp.rd, None, sink)            # read only
+    t.cuda.synchronize()
+    assert t.equal(before, dp.state)
+    assert float(sink[0]) == 0.0
