@@ -45,6 +45,12 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run: python -m gated_deltanet_recurrent_decode_amd.build")
+    try:
+        # load torch's HIP runtime first, so libgdn binds to the same runtime
+        # instance that owns the caller's streams and memory
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     L.gdn_decode_step.restype = i32

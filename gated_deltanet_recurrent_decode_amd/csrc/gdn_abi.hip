@@ -40,9 +40,13 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
                            const int32_t *read_slot, const int32_t *write_slot, gdn_bf16 *out,
                            float q_scale, float l2_eps, hipStream_t stream)
 {
-    if (!dims || !x || !conv_w || !conv_state || !state || !g || !beta || !read_slot || !out)
+    if (!dims)
         return GDN_ERR_NULL;
     const gdn_dims d = *dims;
+    if (d.B == 0) // nothing to do; per-row arrays may be NULL
+        return GDN_OK;
+    if (!x || !conv_w || !conv_state || !state || !g || !beta || !read_slot || !out)
+        return GDN_ERR_NULL;
     if (d.B < 0 || d.T < 1 || d.H_k < 1 || d.H_v < 1 || d.N < 1 || d.H_v % d.H_k != 0)
         return GDN_ERR_SHAPE;
     if (!head_dim_ok(d.d_k) || !head_dim_ok(d.d_v) || d.W != 4)
@@ -59,10 +63,10 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
         return GDN_ERR_REFUSED;
     if (!write_slot && G != 1 && G != 2 && G != 4)
         return GDN_ERR_UNSUPPORTED;
-    if (!aligned(state, 16) || !aligned(out, 8) || !aligned(conv_w, 8))
+    // the step reads and writes four channels at a time and whole fp32 rows
+    if (!aligned(state, 16) || !aligned(out, 8) || !aligned(conv_w, 16) || !aligned(conv_state, 8) ||
+        !aligned(x, 8) || x_row_stride % 4 != 0 || (conv_b && !aligned(conv_b, 8)))
         return GDN_ERR_UNSUPPORTED;
-    if (d.B == 0)
-        return GDN_OK;
 
     gdn::StepParams p{};
     p.x = x;
@@ -95,6 +99,8 @@ gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf1
                        gdn_bf16 *out, int64_t out_row_stride, int32_t activation,
                        hipStream_t stream)
 {
+    if (B == 0)
+        return GDN_OK;
     if (!x || !conv_w || !conv_state || !read_slot || !out)
         return GDN_ERR_NULL;
     if (B < 0 || C < 1 || N < 1 || x_row_stride < C || out_row_stride < C || B > 65535)
@@ -124,6 +130,8 @@ gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf1
 
 gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipStream_t stream)
 {
+    if (B == 0)
+        return GDN_OK;
     if (!read_slot || !write_slot)
         return GDN_ERR_NULL;
     if (B < 0)

@@ -45,7 +45,6 @@ struct StepCfg {
     static constexpr int NWH = NTH / 64;           // waves per head slice
     static constexpr int NT = NTH * HPW;           // threads per workgroup
     static constexpr int NCH = 2 * DK + HPW * DVS; // conv channels the workgroup needs
-    static constexpr int NCP = (NCH + NT - 1) / NT; // conv channels per thread
     static_assert(CG >= 8 && CG <= 64 && 64 % CG == 0, "a wave must hold whole row groups");
     static_assert(DK % RG == 0, "rows must tile the row groups");
     static_assert(NWH == 1 || NWH == 2 || NWH == 4, "pairwise tree over at most four waves");
@@ -62,20 +61,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(float *base, uint32_
 }
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// One channel of the width-4 conv with SiLU, from bf16 values already moved
+// into the high half of a 32-bit word (so they read as fp32): taps 0-1 in
+// w01, taps 2-3 in w23 (tap 3 multiplies the current token), the three
+// window values oldest first, the token, and the bias (added when present).
+__device__ __forceinline__ float conv_tap4(uint32_t w01, uint32_t w23, uint32_t a0, uint32_t a1, uint32_t a2,
+                                           uint32_t xv, uint32_t bias, bool has_bias)
+{
+    float acc = __uint_as_float(w01 << 16) * __uint_as_float(a0);
+    acc = fmaf(__uint_as_float(w01 & 0xffff0000u), __uint_as_float(a1), acc);
+    acc = fmaf(__uint_as_float(w23 << 16), __uint_as_float(a2), acc);
+    acc = fmaf(__uint_as_float(w23 & 0xffff0000u), __uint_as_float(xv), acc);
+    if (has_bias)
+        acc += __uint_as_float(bias);
+    return silu(acc);
+}
+
+// Cache-policy bits of the buffer accesses (gfx950): 2 = nt (streaming).  The
+// new state is written once and not read again within a step, so its stores
+// stream past the caches; on MI355X this is what lets the write stream overlap
+// the read stream of other tiles at full bandwidth (plain stores allocate in
+// the caches and their evictions compete with the reads).
+constexpr int kLoadPolicy = 0;
+// Four waves per SIMD for the whole-tile single-token kernel: a 64-row step
+// (1024 head tiles of 256 threads) is then resident on the 256 compute units
+// all at once.  The multi-token kernels carry more live state and are left
+// to the compiler (forcing four waves there spills to scratch).
+constexpr int kWavesPerEU = 4;
+constexpr int kStorePolicy = 2;
 
 template <int DK, int DV, int DVS, int HPW, bool MT>
-__global__ __launch_bounds__(2 * DVS * HPW) void gdn_step_kernel(StepParams p)
+__global__ __launch_bounds__(2 * DVS * HPW) __attribute__((amdgpu_waves_per_eu((!MT && DVS == DV) ? kWavesPerEU : 1)))
+void gdn_step_kernel(StepParams p)
 {
     using Cfg = StepCfg<DK, DVS, HPW>;
     static_assert(Cfg::NT == 2 * DVS * HPW, "launch bound must match the layout");
     constexpr int NT = Cfg::NT, NTH = Cfg::NTH, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH;
-    constexpr int NCH = Cfg::NCH, NCP = Cfg::NCP;
+    constexpr int NCH = Cfg::NCH;
 
-    __shared__ float y_lds[NCP * NT];
+    __shared__ float y_lds[NCH + 4]; // + a padding slot for spare conv lanes
     __shared__ float4 red_lds[HPW][NWH][2][CG];
 
     const int tid = threadIdx.x;
-    const int hloc = tid / NTH;      // head of the group this thread updates
+    // head of the group this thread updates; NTH is a multiple of the wave size,
+    // so this is wave-uniform -- say so, or every buffer access that depends on
+    // it would be compiled as a loop over lanes
+    const int hloc = __builtin_amdgcn_readfirstlane(tid / NTH);
     const int ht = tid - hloc * NTH; // thread index inside its head slice
     const int cg = ht % CG;
     const int rg = ht / CG;
@@ -113,45 +146,58 @@ __global__ __launch_bounds__(2 * DVS * HPW) void gdn_step_kernel(StepParams p)
 
     // ---- conv inputs of token 0 first: they are few and on the critical path,
     // and loads complete in order, so issuing them before the state tile lets
-    // the conv run while the tile is still streaming in.
+    // the conv run while the tile is still streaming in.  Each conv lane takes
+    // four consecutive channels: 8-byte loads of its window rows, x and bias,
+    // 16-byte loads of its weights, all raw bf16 bits.  NCL lanes do the conv,
+    // whole waves except the last, whose spare lanes read lane 0's channels and
+    // write their result to a padding slot of y_lds.
+    constexpr int NCL = NCH / 4;               // conv lanes (channel quads)
+    constexpr int NCW = (NCL + 63) / 64;       // waves' worth of conv lanes
+    constexpr int NCQ = (NCL + NT - 1) / NT;   // quads per thread
     const bool own_qk = (grp == 0 && cs == 0);
     const int C = p.C;
-    const uint16_t *xrow = p.x + (size_t)r * p.x_row_stride;
-    const uint16_t *cs_rd = p.conv_state + (size_t)rs * 3 * C;
-    uint16_t *cs_wr = p.conv_state + (size_t)ws * 3 * C;
-    // Branch-free: a lane past the last channel loads channel 0's inputs and
-    // discards them, so the loads of every lane stay in one straight run and
-    // nothing waits on them before the state loads are issued.
     const int hv = hv0 + hloc;
     // gates of token 0, also ahead of the state tile
     float g_t = p.g[(size_t)r * T * p.H_v + hv];
     float b_t = p.beta[(size_t)r * T * p.H_v + hv];
+    const uint16_t *xrow = p.x + (size_t)r * p.x_row_stride;
+    const uint16_t *cs_rd = p.conv_state + (size_t)rs * 3 * C;
+    uint16_t *cs_wr = p.conv_state + (size_t)ws * 3 * C;
     const uint16_t *bias_src = p.conv_b ? p.conv_b : p.conv_w; // conv_w: in-bounds stand-in, unused
-    int ch[NCP];
-    bool own[NCP];
-    uint2 wq[NCP];
-    uint16_t r0[NCP], r1[NCP], r2[NCP], xb[NCP], bb[NCP];
+    bool conv_wave[NCQ], conv_lane[NCQ], own[NCQ];
+    int c[NCQ], e4[NCQ];
+    uint4 wlo[NCQ], whi[NCQ];
+    uint2 wn0[NCQ], wn1[NCQ], wn2[NCQ], xq[NCQ], bq[NCQ];
 #pragma unroll
-    for (int k = 0; k < NCP; ++k) {
-        const int e = tid + k * NT;
-        const bool valid = (NCH % NT == 0) || (e < NCH);
-        const int ee = valid ? e : 0;
-        const bool isq = ee < DK;
-        const bool isk = !isq && ee < 2 * DK;
-        const int ve = ee >= 2 * DK ? ee - 2 * DK : 0;
+    for (int k = 0; k < NCQ; ++k) {
+        const int li = tid + k * NT;
+        conv_wave[k] = (li >> 6) < NCW; // wave-uniform (NT is a multiple of 64)
+        conv_lane[k] = li < NCL;
+        e4[k] = conv_lane[k] ? 4 * li : 0; // first channel of the quad
+        const int e = e4[k];
+        const bool isq = e < DK;
+        const bool isk = !isq && e < 2 * DK;
+        const int ve = e >= 2 * DK ? e - 2 * DK : 0;
         const int h = ve / DVS;
-        const int c = isq ? hk * DK + ee
-                    : isk ? p.H_k * DK + hk * DK + (ee - DK)
-                          : 2 * p.H_k * DK + (hv0 + h) * DV + col0 + (ve - h * DVS);
-        ch[k] = valid ? c : -1;
-        own[k] = valid && ((isq || isk) ? own_qk : true);
-        wq[k] = *reinterpret_cast<const uint2 *>(p.conv_w + (size_t)c * 4);
-        r0[k] = cs_rd[c];
-        r1[k] = cs_rd[C + c];
-        r2[k] = cs_rd[2 * C + c];
-        xb[k] = xrow[c];
-        bb[k] = bias_src[c];
+        c[k] = isq ? hk * DK + e
+               : isk ? p.H_k * DK + hk * DK + (e - DK)
+                     : 2 * p.H_k * DK + (hv0 + h) * DV + col0 + (ve - h * DVS);
+        own[k] = conv_lane[k] && ((isq || isk) ? own_qk : true);
+        wlo[k] = whi[k] = make_uint4(0, 0, 0, 0);
+        wn0[k] = wn1[k] = wn2[k] = xq[k] = bq[k] = make_uint2(0, 0);
+        if (conv_wave[k]) {
+            const int ck = c[k];
+            wlo[k] = *reinterpret_cast<const uint4 *>(p.conv_w + (size_t)ck * 4);
+            whi[k] = *reinterpret_cast<const uint4 *>(p.conv_w + (size_t)ck * 4 + 8);
+            wn0[k] = *reinterpret_cast<const uint2 *>(cs_rd + ck);
+            wn1[k] = *reinterpret_cast<const uint2 *>(cs_rd + C + ck);
+            wn2[k] = *reinterpret_cast<const uint2 *>(cs_rd + 2 * C + ck);
+            xq[k] = *reinterpret_cast<const uint2 *>(xrow + ck);
+            bq[k] = *reinterpret_cast<const uint2 *>(bias_src + ck);
+        }
     }
+    // conv inputs stay ahead of the tile loads
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- state slice -> registers
     constexpr uint32_t TILE = (uint32_t)DK * DV;
@@ -160,43 +206,43 @@ __global__ __launch_bounds__(2 * DVS * HPW) void gdn_step_kernel(StepParams p)
     float4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        s[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd_tile, voff, m * RG * DV * 4, 0));
+        s[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd_tile, voff, m * RG * DV * 4, kLoadPolicy));
+    // Every load of the step is now in flight.  Keep the scheduler from sinking
+    // any of them below the first wait: under a saturated memory system a load
+    // issued after the flood of tile loads queues behind all of them.
+    __builtin_amdgcn_sched_barrier(0);
 
-    float w0[NCP], w1[NCP], w2[NCP];
-#pragma unroll
-    for (int k = 0; k < NCP; ++k) {
-        w0[k] = bf16_to_f32(r0[k]);
-        w1[k] = bf16_to_f32(r1[k]);
-        w2[k] = bf16_to_f32(r2[k]);
-    }
-
+    const bool has_bias = p.conv_b != nullptr;
     for (int t = 0; t < T; ++t) {
         if (MT && t > 0) {
             lds_barrier(); // the previous token's readers of y_lds / red_lds are done
 #pragma unroll
-            for (int k = 0; k < NCP; ++k)
-                xb[k] = xrow[(size_t)t * C + (ch[k] >= 0 ? ch[k] : 0)];
+            for (int k = 0; k < NCQ; ++k)
+                if (conv_wave[k])
+                    xq[k] = *reinterpret_cast<const uint2 *>(xrow + (size_t)t * C + c[k]);
             g_t = p.g[((size_t)r * T + t) * p.H_v + hv];
             b_t = p.beta[((size_t)r * T + t) * p.H_v + hv];
         }
 
         // ---- conv decode + SiLU of this workgroup's channels -> LDS; the
-        // window advances in registers
+        // window (raw bf16 bits) advances in registers
 #pragma unroll
-        for (int k = 0; k < NCP; ++k) {
-            // lanes past the last channel compute on stand-in inputs and write
-            // the padding of y_lds, so this loop has no branch
-            const float xv = bf16_to_f32(xb[k]);
-            float acc = __uint_as_float(wq[k].x << 16) * w0[k];
-            acc = fmaf(__uint_as_float(wq[k].x & 0xffff0000u), w1[k], acc);
-            acc = fmaf(__uint_as_float(wq[k].y << 16), w2[k], acc);
-            acc = fmaf(__uint_as_float(wq[k].y & 0xffff0000u), xv, acc);
-            if (p.conv_b)
-                acc += bf16_to_f32(bb[k]);
-            y_lds[tid + k * NT] = silu(acc);
-            w0[k] = w1[k];
-            w1[k] = w2[k];
-            w2[k] = xv;
+        for (int k = 0; k < NCQ; ++k) {
+            if (!conv_wave[k])
+                continue;
+            const uint4 wl = wlo[k], wh = whi[k];
+            const uint2 a0 = wn0[k], a1 = wn1[k], a2 = wn2[k], xx = xq[k], bb = bq[k];
+            float4 y;
+            y.x = conv_tap4(wl.x, wl.y, a0.x << 16, a1.x << 16, a2.x << 16, xx.x << 16, bb.x << 16, has_bias);
+            y.y = conv_tap4(wl.z, wl.w, a0.x & 0xffff0000u, a1.x & 0xffff0000u, a2.x & 0xffff0000u,
+                            xx.x & 0xffff0000u, bb.x & 0xffff0000u, has_bias);
+            y.z = conv_tap4(wh.x, wh.y, a0.y << 16, a1.y << 16, a2.y << 16, xx.y << 16, bb.y << 16, has_bias);
+            y.w = conv_tap4(wh.z, wh.w, a0.y & 0xffff0000u, a1.y & 0xffff0000u, a2.y & 0xffff0000u,
+                            xx.y & 0xffff0000u, bb.y & 0xffff0000u, has_bias);
+            *reinterpret_cast<float4 *>(&y_lds[conv_lane[k] ? e4[k] : NCH]) = y;
+            wn0[k] = a1;
+            wn1[k] = a2;
+            wn2[k] = xx;
         }
         lds_barrier();
 
@@ -287,21 +333,21 @@ __global__ __launch_bounds__(2 * DVS * HPW) void gdn_step_kernel(StepParams p)
             const float o1 = fmaf(u.y, kq, alpha * b.y);
             const float o2 = fmaf(u.z, kq, alpha * b.z);
             const float o3 = fmaf(u.w, kq, alpha * b.w);
-            uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
-            pk.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
-            *reinterpret_cast<uint2 *>(p.out + (gi * DV + col0 + 4 * cg)) = pk;
+            const u32x2 pk = {(uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16),
+                              (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16)};
+            __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(p.out + (gi * DV + col0 + 4 * cg)));
         }
     }
 
-    // ---- advanced conv windows of the channels this workgroup owns (bf16
-    // values throughout, so the narrowing is exact)
+    // ---- advanced conv windows of the channels this workgroup owns: a shift
+    // of bf16 values, stored as the bits they were read as
 #pragma unroll
-    for (int k = 0; k < NCP; ++k) {
-        if (ch[k] >= 0 && own[k]) {
-            cs_wr[ch[k]] = f32_to_bf16_exact(w0[k]);
-            cs_wr[C + ch[k]] = f32_to_bf16_exact(w1[k]);
-            cs_wr[2 * C + ch[k]] = f32_to_bf16_exact(w2[k]);
+    for (int k = 0; k < NCQ; ++k) {
+        if (own[k]) {
+            uint16_t *dst = cs_wr + c[k];
+            __builtin_nontemporal_store(u32x2{wn0[k].x, wn0[k].y}, reinterpret_cast<u32x2 *>(dst));
+            __builtin_nontemporal_store(u32x2{wn1[k].x, wn1[k].y}, reinterpret_cast<u32x2 *>(dst + C));
+            __builtin_nontemporal_store(u32x2{wn2[k].x, wn2[k].y}, reinterpret_cast<u32x2 *>(dst + 2 * C));
         }
     }
 
@@ -309,7 +355,8 @@ __global__ __launch_bounds__(2 * DVS * HPW) void gdn_step_kernel(StepParams p)
     const __amdgpu_buffer_rsrc_t wr_tile = tile_rsrc(p.state + ((size_t)ws * p.H_v + hv) * TILE, TILE * 4u);
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), wr_tile, voff, m * RG * DV * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), wr_tile, voff, m * RG * DV * 4,
+                                               kStorePolicy);
 }
 
 template <int DK, int DV, int DVS, int HPW, bool MT>

@@ -11,6 +11,8 @@
 
 namespace gdn {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int DK, int DV, int NTH>
 __global__ __launch_bounds__(NTH) void traffic_probe_kernel(ProbeParams p)
 {
@@ -48,9 +50,9 @@ __global__ __launch_bounds__(NTH) void traffic_probe_kernel(ProbeParams p)
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        float4 v = s[m];
-        v.x *= p.one; v.y *= p.one; v.z *= p.one; v.w *= p.one;
-        *reinterpret_cast<float4 *>(dst + (size_t)(rg + RG * m) * DV) = v;
+        // streaming stores, as the decode step writes its state
+        f32x4 v = {s[m].x * p.one, s[m].y * p.one, s[m].z * p.one, s[m].w * p.one};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst + (size_t)(rg + RG * m) * DV));
     }
 }
 

@@ -59,7 +59,8 @@ typedef enum gdn_status {
 } gdn_status;
 
 /* Sizes of one decode step.
- *   B    rows (requests) in the step; 0 is allowed and enqueues nothing
+ *   B    rows (requests) in the step; 0 is allowed, enqueues nothing and
+ *        returns GDN_OK before any other check (the arrays may then be NULL)
  *   T    tokens per row, processed in order (T > 1 only in place)
  *   H_k  key heads;  H_v value heads, a multiple of H_k; value head hv reads
  *        key head hv / (H_v / H_k)
@@ -103,8 +104,9 @@ typedef struct gdn_dims {
  * Twin mode reads only read slots and writes only write slots and out; in
  * place reads and writes the read slots.  T > 1 with a twin write returns
  * GDN_ERR_REFUSED (multi-token walks stay in place).  In place needs
- * H_v/H_k in {1, 2, 4}.  Alignment: state 16 bytes, out and conv_w 8 bytes
- * (GDN_ERR_UNSUPPORTED otherwise).
+ * H_v/H_k in {1, 2, 4}.  Alignment (GDN_ERR_UNSUPPORTED otherwise): state
+ * and conv_w 16 bytes; x, conv_b, conv_state and out 8 bytes; x_row_stride a
+ * multiple of 4 elements.
  */
 gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
                            const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
@@ -127,7 +129,7 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
  * A row with rs == 0 gets +0.0 outputs and touches no slot.
  *   x   [B][C] bf16, rows x_row_stride elements apart (>= C)
  *   out [B][C] bf16, rows out_row_stride elements apart (>= C)
- *   activation: 0 none, 1 SiLU.  W must be 4.
+ *   activation: 0 none, 1 SiLU.  W must be 4.  B = 0 returns GDN_OK at once.
  */
 gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,
                        int64_t x_row_stride, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
@@ -140,7 +142,7 @@ gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf1
  * row's read and write slot trade places on the device, stream-ordered after
  * the step, so the next step reads what this one wrote.  Rows whose two
  * slots are equal (in place, padding on slot 0) are unchanged.
- *   read_slot, write_slot [B] int32.  B = 0 enqueues nothing.
+ *   read_slot, write_slot [B] int32.  B = 0 returns GDN_OK at once.
  */
 gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipStream_t stream);
 
