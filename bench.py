@@ -1,24 +1,29 @@
 """Benchmark of the pooled GDN decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows B] [--mode twin|inplace]
-                    [--hot] [--graph] [--no-cpu] [--no-calib]
+                    [--commit fused|separate] [--hot] [--graph] [--no-cpu] [--no-calib]
 
 Workload: one 0.8B-like GDN layer -- B = 64 rows, 16 key and 16 value heads,
 d_k = d_v = 128 fp32 state (1 MiB a row), conv width 4 over 6144 channels with
-bf16 conv windows, a pool of 257 slot pairs (N = 513), twin-slot writes.
-A step is the whole path: the fused decode step (conv + SiLU, L2 norm, gates,
-delta rule, read-out, twin write) and the slot commit, on synthetic seeded
-inputs already resident in HBM.
+bf16 conv windows and activations, a pool of 257 slot pairs (N = 513),
+twin-slot writes.  A step is the whole path: conv + SiLU, L2 norm, gates,
+delta rule, read-out, the twin write, and the slot commit.  With --commit fused
+(default) the commit is folded into the step kernel, which writes the swapped
+slot pair into a second pair of slot arrays (the two pairs alternate); with
+--commit separate it is its own kernel after the step.  Inputs are synthetic,
+seeded, and resident in HBM before the timed region.
 
 Cold cache: MI355X's 256 MB Infinity Cache could hold one 64-row working set
-(128 MiB), so consecutive steps rotate over four disjoint 64-row sets that use
-all 256 slot pairs; a set's slots were last touched 384 MiB of traffic earlier.
---hot runs the same rows every step (reported as such).
+(128 MiB), so consecutive steps rotate over disjoint row sets: four 64-row sets
+over all 256 slot pairs for twin writes (512 MiB touched), eight over 512 slots
+in place.  --hot runs the same rows every step (reported as such).
 
-Prints ONE JSON line on stdout.  value = rows/s over the timed steps
-(step = decode kernel + commit kernel); roofline = the decode kernel's
-algorithmic bytes / its mean duration (HIP events around every launch in the
-timed region, on the launch stream) against 8 TB/s.
+Timing: each timed loop is queued behind a GPU sleep long enough for the host
+to enqueue the whole loop, so the GPU runs the steps back to back and the
+Python launch cost never shows up as GPU idle time.  value = rows/s from the
+loop without per-kernel events; roofline = the step kernel's algorithmic bytes
+over its mean duration, from fence-free HIP events around every launch of a
+second identical loop.  Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -35,20 +40,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 
 
 def algorithmic_bytes(B_real: int, B_pad: int, T: int, H_v: int, d_k: int, d_v: int, C: int, W: int,
                       twin: bool) -> int:
     """Bytes one decode launch must move.  Per real row: the state tile read and
     written (fp32), the conv window read and written (bf16), T tokens of x (bf16),
-    the read-out (bf16), g and beta (fp32) and the two slot indices.  Per padding
-    row: its slot indices and its zero read-out.  Once per launch: conv weights."""
+    the read-out (bf16), g and beta (fp32) and the slot indices (two, and two
+    more written by a fused commit).  Per padding row: its slot indices and its
+    zero read-out.  Once per launch: the conv weights."""
     state = 2 * H_v * d_k * d_v * 4
     conv = 2 * (W - 1) * C * 2
     x = T * C * 2
     out = T * H_v * d_v * 2
     gates = 2 * T * H_v * 4
-    slots = 8 if twin else 4
+    slots = 16 if twin else 4
     per_real = state + conv + x + out + gates + slots
     per_pad = slots + out
     return B_real * per_real + B_pad * per_pad + C * W * 2
@@ -128,8 +135,175 @@ def cpu_baseline(seconds: float = 10.0) -> dict:
         i += 1
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} rows of the 64-row workload (8-row slices, one step each), fp64 C loops, "
-                      f"one thread, {dt:.1f} s", "us_per_64_row_step": 64 / (rows / dt) * 1e6}
+            "sample": f"{rows} rows of the 64-row workload in 8-row calls (one decode step each), "
+                      f"fp64 C loops on one host thread, {dt:.1f} s",
+            "us_per_64_row_step": 64 / (rows / dt) * 1e6}
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+
+        import gated_deltanet_recurrent_decode_amd as gdn
+        import gdn_inputs as gi
+
+        self.torch, self.gdn = torch, gdn
+        gdn.lib()
+        torch.cuda.set_device(0)
+        self.args = args
+        self.twin = args.mode == "twin"
+        self.fused = self.twin and args.commit == "fused"
+        B = self.B = args.rows
+        # the pool (257 slot pairs) and inputs for all 256 pair-rows
+        case = gi.qwen08b(B=256)
+        s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+        self.shape = s
+        self.state = torch.from_numpy(pool.state).cuda()
+        self.conv_state = _bf(torch, pool.conv_state)
+        self.conv_w = _bf(torch, pool.conv_w)
+        if self.twin:
+            nsets = 1 if args.hot else max(1, min(4, 256 // B))
+            slot_rows = [(pool.read_slot[k * B:(k + 1) * B], pool.write_slot[k * B:(k + 1) * B]) for k in range(nsets)]
+        else:
+            nsets = 1 if args.hot else max(1, min(8, 512 // B))
+            perm = np.random.Generator(np.random.PCG64(1)).permutation(512).astype(np.int32) + 1
+            slot_rows = [(perm[k * B:(k + 1) * B], None) for k in range(nsets)]
+        self.nsets = nsets
+        self.sets = []
+        for k, (rd, wr) in enumerate(slot_rows):
+            rows = np.arange(k * B, (k + 1) * B) % 256
+            st = dict(x=_bf(torch, step.x[rows]), g=torch.from_numpy(np.ascontiguousarray(step.g[rows])).cuda(),
+                      beta=torch.from_numpy(np.ascontiguousarray(step.beta[rows])).cuda(),
+                      rd=torch.from_numpy(np.ascontiguousarray(rd)).cuda(),
+                      wr=None if wr is None else torch.from_numpy(np.ascontiguousarray(wr)).cuda(),
+                      out=torch.empty((B, 1, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda"))
+            # the second pair of slot arrays the fused commit alternates with
+            st["pairs"] = [(st["rd"], st["wr"]), (torch.empty_like(st["rd"]), None if wr is None else
+                                                  torch.empty_like(st["wr"]))]
+            st["parity"] = 0
+            self.sets.append(st)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+        self.timer = HipTimer()
+        self.bytes = algorithmic_bytes(B, 0, 1, s.H_v, s.d_k, s.d_v, s.C, s.W, self.twin)
+        self.cycles_per_ms = None
+
+    def launch(self, st):
+        g, s = self.gdn, self.shape
+        if self.fused:
+            (rd, wr), (nrd, nwr) = st["pairs"][st["parity"]], st["pairs"][1 - st["parity"]]
+            g.gdn_decode_step_commit(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
+                                     rd, wr, nrd, nwr, st["out"], H_k=s.H_k)
+            st["parity"] ^= 1
+        else:
+            g.gdn_decode_step(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
+                              st["rd"], st["wr"] if self.twin else None, st["out"], H_k=s.H_k)
+
+    def commit(self, st):
+        if self.twin and not self.fused:
+            self.gdn.slot_commit(st["rd"], st["wr"])
+
+    def step(self, i):
+        st = self.sets[i % self.nsets]
+        self.launch(st)
+        self.commit(st)
+
+    def _sleep_for(self, ms: float):
+        """Queue a GPU spin of about `ms` milliseconds on the current stream."""
+        torch = self.torch
+        if self.cycles_per_ms is None:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            torch.cuda._sleep(2_000_000)
+            b.record()
+            torch.cuda.synchronize()
+            self.cycles_per_ms = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+        torch.cuda._sleep(int(ms * self.cycles_per_ms))
+
+    def timed(self, K: int, per_kernel_events: bool, graph=None):
+        """K steps queued behind a sleep; returns (ms per step, kernel durations in us or None)."""
+        torch, timer = self.torch, self.timer
+        sh = self.stream.cuda_stream
+        kev = [(timer.event(), timer.event()) for _ in range(K)] if per_kernel_events else None
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # enough sleep for the host to queue the whole loop (about 60 us a step from Python)
+        self._sleep_for(max(5.0, K * (0.12 if per_kernel_events else 0.08)))
+        t_host = time.perf_counter()
+        start.record()
+        if graph is not None:
+            for _ in range(K // graph[1]):
+                graph[0].replay()
+        else:
+            for i in range(K):
+                st = self.sets[i % self.nsets]
+                if kev is not None:
+                    timer.record(kev[i][0], sh)
+                self.launch(st)
+                if kev is not None:
+                    timer.record(kev[i][1], sh)
+                self.commit(st)
+        end.record()
+        host_ms = (time.perf_counter() - t_host) * 1e3
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        kus = None
+        if kev is not None:
+            kus = np.array([timer.elapsed_ms(a, b) for a, b in kev]) * 1e3
+            for a, b in kev:
+                timer.destroy(a)
+                timer.destroy(b)
+        return total_ms / K, kus, host_ms
+
+    def capture(self):
+        """One graph holding two steps of every row set (both parities of the
+        fused commit); returns (graph, steps per replay)."""
+        torch = self.torch
+        n = 2 * self.nsets
+        side = torch.cuda.Stream()
+        side.wait_stream(self.stream)
+        with torch.cuda.stream(side):
+            for i in range(n):
+                self.step(i)
+        self.stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                self.step(i)
+        torch.cuda.synchronize()
+        return g, n
+
+    def calibration(self, reps: int = 64) -> dict:
+        """The step's state traffic with no arithmetic, same grid and slots."""
+        torch, timer, gdn = self.torch, self.timer, self.gdn
+        sh = self.stream.cuda_stream
+        sink = torch.zeros(1, device="cuda")
+        s = self.shape
+        cal = {}
+        modes = ((0, "read_only"), (1, "write_only"), (2, "copy_twin"), (3, "read_write_in_place"))
+        for mode, name in modes:
+            if mode in (1, 2) and not self.twin:
+                continue
+            for i in range(8):
+                st = self.sets[i % self.nsets]
+                gdn.traffic_probe(mode, self.state, st["rd"], st["wr"], sink)
+            torch.cuda.synchronize()
+            evs = [(timer.event(), timer.event()) for _ in range(reps)]
+            self._sleep_for(5.0 + reps * 0.12)
+            for i in range(reps):
+                st = self.sets[i % self.nsets]
+                timer.record(evs[i][0], sh)
+                gdn.traffic_probe(mode, self.state, st["rd"], st["wr"], sink)
+                timer.record(evs[i][1], sh)
+            torch.cuda.synchronize()
+            us = np.array([timer.elapsed_ms(a, b) for a, b in evs]) * 1e3
+            for a, b in evs:
+                timer.destroy(a)
+                timer.destroy(b)
+            nbytes = (1 if mode in (0, 1) else 2) * self.B * s.H_v * s.d_k * s.d_v * 4
+            cal[name] = {"us_mean": float(us.mean()), "GBps": nbytes / (us.mean() * 1e-6) / 1e9}
+        return cal
 
 
 def main() -> int:
@@ -139,8 +313,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", type=int, default=64)
     ap.add_argument("--mode", choices=("twin", "inplace"), default="twin")
+    ap.add_argument("--commit", choices=("fused", "separate"), default="fused")
     ap.add_argument("--hot", action="store_true", help="same rows every step (cache-warm)")
-    ap.add_argument("--graph", action="store_true", help="replay steps from a captured HIP graph")
+    ap.add_argument("--graph", action="store_true", help="time steps replayed from a captured HIP graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-calib", action="store_true", help="skip the traffic calibration probes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -148,100 +323,33 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the decode step "
-              "shards by rows or heads with no exchange inside the step, and no multi-GPU path is built.",
+              "shards by rows or by heads with no exchange inside the step, and no multi-GPU path is built.",
               file=sys.stderr)
         return 2
 
-    import torch
-
-    import gated_deltanet_recurrent_decode_amd as gdn
-    import gdn_inputs as gi
-
-    gdn.lib()
-    torch.cuda.set_device(0)
-    twin = args.mode == "twin"
-    B = args.rows
-    nsets = 1 if args.hot else max(1, min(4, 256 // B))
-    # one pool of 257 slot pairs; the row sets take disjoint pairs
-    case = gi.qwen08b(B=B * nsets, twin=twin)
-    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
-    state = torch.from_numpy(pool.state).cuda()
-    conv_state = _bf(torch, pool.conv_state)
-    conv_w = _bf(torch, pool.conv_w)
-    sets = []
-    for k in range(nsets):
-        sl = slice(k * B, (k + 1) * B)
-        sets.append(dict(
-            x=_bf(torch, step.x[sl]), g=torch.from_numpy(np.ascontiguousarray(step.g[sl])).cuda(),
-            beta=torch.from_numpy(np.ascontiguousarray(step.beta[sl])).cuda(),
-            rd=torch.from_numpy(np.ascontiguousarray(pool.read_slot[sl])).cuda(),
-            wr=torch.from_numpy(np.ascontiguousarray(pool.write_slot[sl])).cuda(),
-            out=torch.empty((B, 1, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda")))
-    del case, pool, step
-    torch.cuda.synchronize()
-
-    def one_step(st):
-        gdn.gdn_decode_step(st["x"], conv_w, None, conv_state, state, st["g"], st["beta"], st["rd"],
-                            st["wr"] if twin else None, st["out"], H_k=s.H_k)
-        if twin:
-            gdn.slot_commit(st["rd"], st["wr"])
-
-    stream = torch.cuda.current_stream()
-    graph = None
-    if args.graph:
-        # one graph holding one step of every set, replayed as a unit
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for st in sets:
-                one_step(st)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for st in sets:
-                one_step(st)
-        torch.cuda.synchronize()
-
+    b = Bench(args)
+    s = b.shape
     for i in range(args.warmup):
-        if graph is not None:
-            graph.replay()
-        else:
-            one_step(sets[i % nsets])
-    torch.cuda.synchronize()
+        b.step(i)
+    b.torch.cuda.synchronize()
 
     K = args.steps
-    if graph is not None:
-        K = max(nsets, (K // nsets) * nsets)
-    timer = HipTimer()
-    sh = stream.cuda_stream
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    kev = [(timer.event(), timer.event()) for _ in range(K)] if graph is None else []
-    torch.cuda.synchronize()
-    start.record(stream)
-    if graph is not None:
-        for _ in range(K // nsets):
-            graph.replay()
-    else:
-        for i in range(K):
-            st = sets[i % nsets]
-            e0, e1 = kev[i]
-            timer.record(e0, sh)
-            gdn.gdn_decode_step(st["x"], conv_w, None, conv_state, state, st["g"], st["beta"], st["rd"],
-                                st["wr"] if twin else None, st["out"], H_k=s.H_k)
-            timer.record(e1, sh)
-            if twin:
-                gdn.slot_commit(st["rd"], st["wr"])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
-    rows_per_s = B / (ms_per_step * 1e-3)
+    graph = None
+    if args.graph:
+        graph = b.capture()
+        K = max(graph[1], (K // graph[1]) * graph[1])
+        for _ in range(2):
+            graph[0].replay()
+        b.torch.cuda.synchronize()
+    ms_per_step, _, host_ms = b.timed(K, per_kernel_events=False, graph=graph)
+    _, kus, _ = b.timed(K, per_kernel_events=True)
 
-    step_bytes = algorithmic_bytes(B, 0, 1, s.H_v, s.d_k, s.d_v, s.C, s.W, twin)
+    rows_per_s = b.B / (ms_per_step * 1e-3)
+    twin = b.twin
+    commit = ("folded into the step kernel (next slot pair written by the step)" if b.fused else
+              "separate slot_commit kernel" if twin else "none (in place)")
     result = {
-        "metric": "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows",
+        "metric": METRIC,
         "value": rows_per_s,
         "unit": "rows/s",
         "n_gpus": 1,
@@ -254,54 +362,32 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"0.8B-like GDN layer decode step: {B} rows x 16+16 heads x 128x128 fp32 state, "
+        "config": {"workload": f"0.8B-like GDN layer decode step: {b.B} rows x 16+16 heads x 128x128 fp32 state, "
                                f"conv width 4 over 6144 channels, bf16 conv windows and activations, "
-                               f"257 slot pairs, {'twin-slot write + commit' if twin else 'in-place write'}, "
-                               f"{'same rows every step (cache-warm)' if args.hot else f'{nsets} disjoint row sets rotated (cold cache)'}"
-                               f"{', HIP graph replay' if graph is not None else ''}",
-                   "B": B, "T": 1, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": s.N,
-                   "write": args.mode, "row_sets": nsets, "graph": graph is not None},
-        "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                               f"257 slot pairs, {'twin-slot write' if twin else 'in-place write'}, commit "
+                               f"{commit}, "
+                               + ("same rows every step (cache-warm)" if args.hot else
+                                  f"{b.nsets} disjoint row sets rotated (cold cache)")
+                               + (", HIP graph replay" if graph is not None else ", stream launches"),
+                   "B": b.B, "T": 1, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": s.N,
+                   "write": args.mode, "commit": "fused" if b.fused else ("separate" if twin else "none"),
+                   "row_sets": b.nsets, "graph": graph is not None},
+        "step_GBps": b.bytes / (ms_per_step * 1e-3) / 1e9,
+        "host_enqueue_ms": host_ms,
     }
-    if kev:
-        kms = np.array([timer.elapsed_ms(a, b) for a, b in kev])
-        for a, b in kev:
-            timer.destroy(a)
-            timer.destroy(b)
-        k_us = float(kms.mean() * 1e3)
-        achieved = step_bytes / (k_us * 1e-6) / 1e9
-        result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                              "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
-                              "kernel": "gdn_step_kernel", "kernel_us_mean": k_us,
-                              "kernel_us_p10": float(np.percentile(kms, 10) * 1e3),
-                              "kernel_us_p50": float(np.percentile(kms, 50) * 1e3),
-                              "kernel_us_p90": float(np.percentile(kms, 90) * 1e3),
-                              "bytes_per_launch": step_bytes}
-
+    k_us = float(kus.mean())
+    achieved = b.bytes / (k_us * 1e-6) / 1e9
+    result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                          "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                          "kernel": "gdn_step_kernel", "kernel_us_mean": k_us,
+                          "kernel_us_p10": float(np.percentile(kus, 10)),
+                          "kernel_us_p50": float(np.percentile(kus, 50)),
+                          "kernel_us_p90": float(np.percentile(kus, 90)),
+                          "bytes_per_launch": b.bytes}
     if not args.no_calib:
-        sink = torch.zeros(1, device="cuda")
-        cal = {}
-        for mode, name in ((0, "read_only"), (1, "write_only"), (2, "copy_twin"), (3, "read_write_in_place")):
-            ts = []
-            for i in range(max(8, args.warmup // 2) + 64):
-                st = sets[i % nsets]
-                e0, e1 = timer.event(), timer.event()
-                timer.record(e0, sh)
-                gdn.traffic_probe(mode, state, st["rd"], st["wr"], sink)
-                timer.record(e1, sh)
-                ts.append((e0, e1))
-            torch.cuda.synchronize()
-            us = np.array([timer.elapsed_ms(a, b) for a, b in ts[-64:]]) * 1e3
-            for a, b in ts:
-                timer.destroy(a)
-                timer.destroy(b)
-            nbytes = (1 if mode in (0, 1) else 2) * B * s.H_v * s.d_k * s.d_v * 4
-            cal[name] = {"us_mean": float(us.mean()), "GBps": nbytes / (us.mean() * 1e-6) / 1e9}
-        result["calibration"] = cal
-
+        result["calibration"] = b.calibration()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
-
     print(json.dumps(result), flush=True)
     return 0
 

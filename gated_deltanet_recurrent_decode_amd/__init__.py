@@ -13,12 +13,13 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["GdnError", "lib", "gdn_decode_step", "conv_decode", "slot_commit", "traffic_probe",
-           "status_string", "LIB_PATH", "EXPORTS"]
+__all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit",
+           "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-EXPORTS = ("gdn_decode_step", "conv_decode", "slot_commit", "gdn_status_string", "gdn_traffic_probe")
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit", "gdn_status_string",
+           "gdn_traffic_probe")
 
 GDN_OK = 0
 
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
     P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     L.gdn_decode_step.restype = i32
     L.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
+    L.gdn_decode_step_commit.restype = i32
+    L.gdn_decode_step_commit.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.conv_decode.restype = i32
     L.conv_decode.argtypes = [i32, i32, i32, i32, P, i64, P, P, P, P, P, P, i64, i32, P]
     L.slot_commit.restype = i32
@@ -114,14 +117,7 @@ def _stream(stream):
 
 # ------------------------------------------------------------------ entry points
 
-def gdn_decode_step(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, *,
-                    H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
-    """One fused decode step (see ``gdn_decode_step`` in include/gdn.h).
-
-    x [B][T][C] bf16 (rows may be strided; the inner two dims contiguous),
-    conv_w [C][4] bf16, conv_b [C] bf16 or None, conv_state [N][3][C] bf16,
-    state [N][H_v][d_k][d_v] fp32, g/beta [B][T][H_v] fp32, read_slot/write_slot
-    [B] int32 (write_slot None => in place), out [B][T][H_v][d_v] bf16."""
+def _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k):
     torch = _torch()
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     _dev(x, "x", bf)
@@ -147,10 +143,41 @@ def gdn_decode_step(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, wr
         raise ValueError("conv_b must be [C]")
     d = Dims(B, T, H_k, H_v, d_k, d_v, W, N)
     x_row_stride = x.stride(0) if B > 0 else T * C
+    return d, x_row_stride
+
+
+def gdn_decode_step(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, *,
+                    H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """One fused decode step (see ``gdn_decode_step`` in include/gdn.h).
+
+    x [B][T][C] bf16 (rows may be strided; the inner two dims contiguous),
+    conv_w [C][4] bf16, conv_b [C] bf16 or None, conv_state [N][3][C] bf16,
+    state [N][H_v][d_k][d_v] fp32, g/beta [B][T][H_v] fp32, read_slot/write_slot
+    [B] int32 (write_slot None => in place), out [B][T][H_v][d_v] bf16."""
+    d, xs = _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k)
     _check("gdn_decode_step", lib().gdn_decode_step(
-        ctypes.byref(d), _ptr(x), x_row_stride, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+        ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
         _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(out), float(q_scale), float(l2_eps),
         _stream(stream)))
+
+
+def gdn_decode_step_commit(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, next_read_slot,
+                           next_write_slot, out, *, H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6,
+                           stream=None) -> None:
+    """A twin-slot decode step with the commit folded in (see ``gdn_decode_step_commit``
+    in include/gdn.h): also writes next_read_slot = write_slot, next_write_slot = read_slot."""
+    torch = _torch()
+    if write_slot is None:
+        raise ValueError("gdn_decode_step_commit writes twin slots: write_slot is required")
+    for t, n in ((next_read_slot, "next_read_slot"), (next_write_slot, "next_write_slot")):
+        _contig(_dev(t, n, torch.int32), n)
+        if t.shape != read_slot.shape:
+            raise ValueError(f"{n} must be [B]")
+    d, xs = _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k)
+    _check("gdn_decode_step_commit", lib().gdn_decode_step_commit(
+        ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+        _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(next_read_slot), _ptr(next_write_slot),
+        _ptr(out), float(q_scale), float(l2_eps), _stream(stream)))
 
 
 def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,

@@ -19,9 +19,7 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 } // namespace
 
-extern "C" {
-
-const char *gdn_status_string(gdn_status status)
+extern "C" const char *gdn_status_string(gdn_status status)
 {
     switch (status) {
     case GDN_OK: return "ok";
@@ -34,11 +32,12 @@ const char *gdn_status_string(gdn_status status)
     return "unknown gdn_status";
 }
 
-gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
-                           const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
-                           float *state, const float *g, const float *beta,
-                           const int32_t *read_slot, const int32_t *write_slot, gdn_bf16 *out,
-                           float q_scale, float l2_eps, hipStream_t stream)
+namespace {
+
+gdn_status step_impl(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const gdn_bf16 *conv_w,
+                     const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
+                     const int32_t *read_slot, const int32_t *write_slot, int32_t *next_read_slot,
+                     int32_t *next_write_slot, gdn_bf16 *out, float q_scale, float l2_eps, hipStream_t stream)
 {
     if (!dims)
         return GDN_ERR_NULL;
@@ -79,6 +78,8 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
     p.beta = beta;
     p.read_slot = read_slot;
     p.write_slot = write_slot;
+    p.next_read_slot = next_read_slot;
+    p.next_write_slot = next_write_slot;
     p.out = out;
     p.q_scale = q_scale;
     p.l2_eps = l2_eps;
@@ -91,6 +92,42 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
     p.G = G;
     p.twin = write_slot ? 1 : 0;
     return from_hip(gdn::launch_gdn_step(p, d.d_k, d.d_v, stream));
+}
+
+} // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                           const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                           float *state, const float *g, const float *beta,
+                           const int32_t *read_slot, const int32_t *write_slot, gdn_bf16 *out,
+                           float q_scale, float l2_eps, hipStream_t stream)
+{
+    return step_impl(dims, x, x_row_stride, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot,
+                     nullptr, nullptr, out, q_scale, l2_eps, stream);
+}
+
+gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                  const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                                  float *state, const float *g, const float *beta, const int32_t *read_slot,
+                                  const int32_t *write_slot, int32_t *next_read_slot, int32_t *next_write_slot,
+                                  gdn_bf16 *out, float q_scale, float l2_eps, hipStream_t stream)
+{
+    if (dims && dims->B != 0) {
+        if (!write_slot || !next_read_slot || !next_write_slot)
+            return GDN_ERR_NULL;
+        const int32_t *ins[2] = {read_slot, write_slot};
+        const int32_t *outs[2] = {next_read_slot, next_write_slot};
+        if (next_read_slot == next_write_slot)
+            return GDN_ERR_SHAPE;
+        for (const int32_t *a : ins)
+            for (const int32_t *b : outs)
+                if (a == b)
+                    return GDN_ERR_SHAPE;
+    }
+    return step_impl(dims, x, x_row_stride, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot,
+                     next_read_slot, next_write_slot, out, q_scale, l2_eps, stream);
 }
 
 gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,

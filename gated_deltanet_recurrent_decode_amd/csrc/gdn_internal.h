@@ -22,6 +22,8 @@ struct StepParams {
     float q_scale;
     float l2_eps;
     int B, T, H_k, H_v, N, C, G;
+    int32_t *next_read_slot;  // fused commit: receives write_slot[r] (null: no commit)
+    int32_t *next_write_slot; // fused commit: receives read_slot[r]
     int n_slices; // d_v column slices per head (set by the launcher)
     int twin;     // 1: write to write_slot; 0: in place
 };

@@ -131,6 +131,13 @@ void gdn_step_kernel(StepParams p)
     const int rs = p.read_slot[r];
     const int ws = p.twin ? p.write_slot[r] : rs;
     const bool bad = rs < 0 || rs >= p.N || ws < 0 || ws >= p.N || (p.twin && ws == rs);
+    // fused commit: one workgroup per row writes the swapped pair into the
+    // next step's slot arrays (distinct from the ones every workgroup of this
+    // step reads, so there is no race)
+    if (p.next_read_slot && hk == 0 && grp == 0 && cs == 0 && tid == 0) {
+        p.next_read_slot[r] = ws;
+        p.next_write_slot[r] = rs;
+    }
     if (rs == 0 || bad) {
         // padding row (or a row with an unusable slot): touch no slot; out gets
         // +0.0 for padding and NaN for the unusable slot.

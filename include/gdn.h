@@ -115,6 +115,26 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
                            float q_scale, float l2_eps, hipStream_t stream);
 
 /*
+ * gdn_decode_step_commit -- gdn_decode_step (twin-slot write) with the
+ * commit folded in (PR #1139, "What changed": commit swaps the two slots of
+ * a request; "Numbers": a small kernel in a captured graph costs about as
+ * much as its launch, so the step does it instead of a second kernel).
+ * Everything gdn_decode_step does, plus, for every row r (padding rows
+ * included):
+ *   next_read_slot[r] = write_slot[r];  next_write_slot[r] = read_slot[r]
+ * so the next step reads what this one wrote.  The next-step arrays must not
+ * overlap read_slot or write_slot (the step reads those while it writes the
+ * next ones); a caller alternates between two pairs of slot arrays.
+ * write_slot, next_read_slot and next_write_slot are required (NULL gives
+ * GDN_ERR_NULL); passing the same array twice gives GDN_ERR_SHAPE.
+ */
+gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                  const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                                  float *state, const float *g, const float *beta, const int32_t *read_slot,
+                                  const int32_t *write_slot, int32_t *next_read_slot, int32_t *next_write_slot,
+                                  gdn_bf16 *out, float q_scale, float l2_eps, hipStream_t stream);
+
+/*
  * conv_decode -- the pooled conv update for one token a row, standalone
  * (PR #1139, "What changed": causal_conv1d_decode, with null slots, strided
  * rows, optional bias and activation, and a write slot that leaves the read

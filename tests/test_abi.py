@@ -85,6 +85,26 @@ def test_step_validation():
     assert _step(_dims(), conv_w=ctypes.c_void_p(0x10004)) == UNSUPPORTED
 
 
+def test_step_commit_validation():
+    f = gdn.lib().gdn_decode_step_commit
+    d = _dims()
+    C = 2 * 4 * 64 + 4 * 64
+    other = ctypes.c_void_p(0x20000)
+    other2 = ctypes.c_void_p(0x30000)
+
+    def call(rd=FAKE, wr=FAKE, nrd=other, nwr=other2):
+        return f(ctypes.byref(d), FAKE, C, FAKE, None, FAKE, FAKE, FAKE, FAKE, rd, wr, nrd, nwr, FAKE, 1.0, 1e-6,
+                 None)
+    assert call(wr=None) == NULL
+    assert call(nrd=None) == NULL
+    assert call(nwr=None) == NULL
+    assert call(rd=ctypes.c_void_p(0x40000), wr=ctypes.c_void_p(0x50000), nrd=ctypes.c_void_p(0x40000)) == SHAPE
+    assert call(nrd=other, nwr=other) == SHAPE
+    empty = gdn.Dims(0, 1, 4, 4, 64, 64, 4, 9)
+    assert f(ctypes.byref(empty), None, 0, None, None, None, None, None, None, None, None, None, None, None, 1.0,
+             1e-6, None) == OK
+
+
 def test_conv_decode_validation():
     f = gdn.lib().conv_decode
     assert f(4, 16, 4, 9, None, 16, FAKE, None, FAKE, FAKE, None, FAKE, 16, 1, None) == NULL

@@ -214,6 +214,55 @@ def test_padded_bucket_in_place_four_tokens(gdn, torch):
     assert t.equal(dp1.conv_state.view(t.int16), dp.conv_state.view(t.int16))
 
 
+# ------------------------------------------------------------------ fused commit
+
+def test_step_commit_equals_step_then_commit(gdn, torch):
+    t = torch
+    case = gi.small(B=12, T=1, H_k=4, H_v=8, d=128, real_rows=10, N=25, seed=31)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp1, dp2 = H.DevPool(pool), H.DevPool(pool)
+    out1 = H.gpu_step(gdn, dp1, step, s)
+    gdn.slot_commit(dp1.rd, dp1.wr)
+    out2 = t.empty_like(out1)
+    nrd = t.full_like(dp2.rd, -7)
+    nwr = t.full_like(dp2.wr, -7)
+    gdn.gdn_decode_step_commit(H.bf16_dev(step.x), dp2.conv_w, None, dp2.conv_state, dp2.state,
+                               t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda(), dp2.rd, dp2.wr, nrd, nwr,
+                               out2, H_k=s.H_k)
+    t.cuda.synchronize()
+    assert t.equal(out1.view(t.int16), out2.view(t.int16))
+    assert t.equal(dp1.state.view(t.int32), dp2.state.view(t.int32))
+    assert t.equal(dp1.conv_state.view(t.int16), dp2.conv_state.view(t.int16))
+    assert t.equal(nrd, dp1.rd) and t.equal(nwr, dp1.wr)
+    # the arrays the step read are left as they were
+    assert t.equal(dp2.rd, t.from_numpy(pool.read_slot).cuda()) and t.equal(dp2.wr, t.from_numpy(pool.write_slot).cuda())
+
+
+def test_tiny_chain_with_fused_commit_matches_oracle(gdn, torch):
+    """The tiny workload's 8 chained steps, with the commit folded into each step
+    through two alternating pairs of slot arrays."""
+    t = torch
+    case = gi.tiny()
+    s, pool = case.shape, case.pools[0]
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    pairs = [(dp.rd, dp.wr), (t.empty_like(dp.rd), t.empty_like(dp.wr))]
+    for k in range(8):
+        step = case.steps[k][0]
+        (rd, wr), (nrd, nwr) = pairs[k % 2], pairs[(k + 1) % 2]
+        out = t.empty((s.B, 1, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+        gdn.gdn_decode_step_commit(H.bf16_dev(step.x), dp.conv_w, None, dp.conv_state, dp.state,
+                                   t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda(), rd, wr, nrd, nwr, out,
+                                   H_k=s.H_k)
+        ref = H.oracle_step(oracle, hp, step, s)
+        oracle.slot_commit(hp.rd, hp.wr)
+        t.cuda.synchronize()
+        H.assert_out_close(out, ref, f"out step {k}")
+        H.assert_state_close(dp.state.cpu().numpy(), hp.state, f"pool after step {k}")
+        np.testing.assert_array_equal(H.bf16_host(dp.conv_state), hp.conv_state)
+        np.testing.assert_array_equal(nrd.cpu().numpy(), hp.rd)
+        np.testing.assert_array_equal(nwr.cpu().numpy(), hp.wr)
+
+
 # ------------------------------------------------------------------ standalone conv decode
 
 @pytest.mark.parametrize("bias,act,twin", [(False, True, True), (True, True, True), (False, False, True),
