@@ -42,6 +42,24 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0
 METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 
+# HBM bytes per launch of the step kernel on the default workload, from the two
+# rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
+# each scaled by what it reads for a copy of known size).  Only valid for the
+# kernel source the counters were taken on: reported as null otherwise.
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "b208127d24f217eb6df75f28a5df47dd0e87abc46cee0d236fdee174cc90c970",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_097_107}
+KERNEL_SOURCES = ("gdn_step.hip", "device_common.h", "gdn_internal.h")
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "gated_deltanet_recurrent_decode_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def algorithmic_bytes(B_real: int, B_pad: int, T: int, H_v: int, d_k: int, d_v: int, C: int, W: int,
                       twin: bool) -> int:
@@ -322,7 +340,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the decode step "
+        print(f"bench.py: the decode step runs on one GPU (asked for --gpus {args.gpus}); it "
               "shards by rows or by heads with no exchange inside the step, and no multi-GPU path is built.",
               file=sys.stderr)
         return 2
@@ -377,8 +395,14 @@ def main() -> int:
     }
     k_us = float(kus.mean())
     achieved = b.bytes / (k_us * 1e-6) / 1e9
+    traffic = None
+    workload_key = (b.B, args.mode, "fused" if b.fused else "separate", bool(args.hot))
+    if (kernel_sources_sha256() == MEASURED_TRAFFIC["kernel_sources_sha256"]
+            and workload_key == MEASURED_TRAFFIC["workload"]):
+        traffic = MEASURED_TRAFFIC["bytes_per_launch"]
     result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                          "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                          "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                          "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                           "kernel": "gdn_step_kernel", "kernel_us_mean": k_us,
                           "kernel_us_p10": float(np.percentile(kus, 10)),
                           "kernel_us_p50": float(np.percentile(kus, 50)),
