@@ -79,18 +79,20 @@ __device__ __forceinline__ float conv_tap4(uint32_t w01, uint32_t w23, uint32_t 
     return silu(acc);
 }
 
-// Cache-policy bits of the buffer accesses (gfx950): 2 = nt (streaming).  The
-// new state is written once and not read again within a step, so its stores
-// stream past the caches; on MI355X this is what lets the write stream overlap
-// the read stream of other tiles at full bandwidth (plain stores allocate in
-// the caches and their evictions compete with the reads).
-constexpr int kLoadPolicy = 0;
+// Cache-policy bits of the buffer accesses (gfx950): 2 = nt (streaming).  A
+// state tile is read once and written once per step and is not touched again
+// until the next step of the layer, long after the caches have turned over,
+// so both directions stream past the caches.  On MI355X this is what lets the
+// write stream overlap the read stream of other tiles: plain stores allocate
+// in the caches and their evictions compete with the reads, and streaming
+// reads leave the Infinity Cache to the small per-row inputs.
+constexpr int kLoadPolicy = 2;
+constexpr int kStorePolicy = 2;
 // Four waves per SIMD for the whole-tile single-token kernel: a 64-row step
 // (1024 head tiles of 256 threads) is then resident on the 256 compute units
 // all at once.  The multi-token kernels carry more live state and are left
 // to the compiler (forcing four waves there spills to scratch).
 constexpr int kWavesPerEU = 4;
-constexpr int kStorePolicy = 2;
 
 template <int DK, int DV, int DVS, int HPW, bool MT>
 __global__ __launch_bounds__(2 * DVS * HPW) __attribute__((amdgpu_waves_per_eu((!MT && DVS == DV) ? kWavesPerEU : 1)))
@@ -379,14 +381,15 @@ static hipError_t launch_step(const StepParams &p, hipStream_t stream)
                            dim3((unsigned)tiles), dim3(StepCfg<DK, DVS, HPW>::NT), args, 0, stream);
 }
 
-// Column slices per head for a twin step: split d_v when the rows alone give
-// too few workgroups to cover the 256 compute units (slices stay >= 32 columns).
+// Column slices per head for a twin step: split d_v only when the rows give
+// very few workgroups (with the state cold in HBM, whole tiles win from 16
+// rows of 16 heads up; slices stay >= 32 columns).
 static int pick_slices(const StepParams &p, int dv)
 {
     const long long heads = (long long)p.B * p.H_v;
-    if (heads >= 512)
+    if (heads >= 128)
         return 1;
-    if (heads >= 128 || dv < 128)
+    if (heads >= 32 || dv < 128)
         return 2;
     return 4;
 }

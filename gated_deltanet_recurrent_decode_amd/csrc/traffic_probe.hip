@@ -31,9 +31,12 @@ __global__ __launch_bounds__(NTH) void traffic_probe_kernel(ProbeParams p)
     float *dst = p.state + ((size_t)ws * p.H + h) * TILE + off;
     float4 s[RPT];
     if (p.mode != 1) {
+        // streaming loads, as the decode step reads its state
 #pragma unroll
-        for (int m = 0; m < RPT; ++m)
-            s[m] = *reinterpret_cast<const float4 *>(src + (size_t)(rg + RG * m) * DV);
+        for (int m = 0; m < RPT; ++m) {
+            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + (size_t)(rg + RG * m) * DV));
+            s[m] = make_float4(v.x, v.y, v.z, v.w);
+        }
     } else {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
