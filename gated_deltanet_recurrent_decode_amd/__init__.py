@@ -14,12 +14,12 @@ import ctypes
 import os
 
 __all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit",
-           "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
+           "slot_reset", "slot_copy", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit", "gdn_status_string",
-           "gdn_traffic_probe")
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit", "gdn_slot_reset",
+           "gdn_slot_copy", "gdn_status_string", "gdn_traffic_probe")
 
 GDN_OK = 0
 
@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
     L.slot_commit.argtypes = [P, P, i32, P]
     L.gdn_status_string.restype = ctypes.c_char_p
     L.gdn_status_string.argtypes = [i32]
+    L.gdn_slot_reset.restype = i32
+    L.gdn_slot_reset.argtypes = [ctypes.POINTER(Dims), P, P, P, i32, P]
+    L.gdn_slot_copy.restype = i32
+    L.gdn_slot_copy.argtypes = [ctypes.POINTER(Dims), P, P, P, P, i32, P]
     L.gdn_traffic_probe.restype = i32
     L.gdn_traffic_probe.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P]
     _lib = L
@@ -215,6 +219,37 @@ def slot_commit(read_slot, write_slot, *, stream=None) -> None:
         raise ValueError("slot arrays must both be [B]")
     _check("slot_commit", lib().slot_commit(_ptr(read_slot), _ptr(write_slot), read_slot.shape[0],
                                             _stream(stream)))
+
+
+def _pool_dims(state, conv_state, H_k):
+    torch = _torch()
+    _contig(_dev(state, "state", torch.float32), "state")
+    _contig(_dev(conv_state, "conv_state", torch.bfloat16), "conv_state")
+    if state.dim() != 4 or conv_state.dim() != 3 or state.shape[0] != conv_state.shape[0]:
+        raise ValueError("state must be [N][H_v][d_k][d_v] and conv_state [N][W-1][C] over the same slots")
+    N, H_v, d_k, d_v = state.shape
+    return Dims(0, 1, H_k, H_v, d_k, d_v, conv_state.shape[1] + 1, N)
+
+
+def slot_reset(state, conv_state, slots, *, H_k: int, stream=None) -> None:
+    """Zero the state and conv window of every listed slot (see ``gdn_slot_reset`` in include/gdn.h)."""
+    torch = _torch()
+    _contig(_dev(slots, "slots", torch.int32), "slots")
+    d = _pool_dims(state, conv_state, H_k)
+    _check("gdn_slot_reset", lib().gdn_slot_reset(ctypes.byref(d), _ptr(state), _ptr(conv_state), _ptr(slots),
+                                                  slots.numel(), _stream(stream)))
+
+
+def slot_copy(state, conv_state, src_slots, dst_slots, *, H_k: int, stream=None) -> None:
+    """Copy slot src[i] to slot dst[i], state and conv window (see ``gdn_slot_copy`` in include/gdn.h)."""
+    torch = _torch()
+    _contig(_dev(src_slots, "src_slots", torch.int32), "src_slots")
+    _contig(_dev(dst_slots, "dst_slots", torch.int32), "dst_slots")
+    if src_slots.shape != dst_slots.shape or src_slots.dim() != 1:
+        raise ValueError("src_slots and dst_slots must both be [n]")
+    d = _pool_dims(state, conv_state, H_k)
+    _check("gdn_slot_copy", lib().gdn_slot_copy(ctypes.byref(d), _ptr(state), _ptr(conv_state), _ptr(src_slots),
+                                                _ptr(dst_slots), src_slots.numel(), _stream(stream)))
 
 
 def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, stream=None) -> None:

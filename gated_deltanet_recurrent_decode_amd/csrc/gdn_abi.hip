@@ -176,6 +176,50 @@ gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipSt
     return from_hip(gdn::launch_slot_commit(read_slot, write_slot, B, stream));
 }
 
+static gdn_status slot_ops_impl(const gdn_dims *dims, float *state, gdn_bf16 *conv_state, const int32_t *src,
+                                const int32_t *dst, int32_t n, hipStream_t stream)
+{
+    if (!dims)
+        return GDN_ERR_NULL;
+    if (n == 0)
+        return GDN_OK;
+    const gdn_dims d = *dims;
+    if (!state || !conv_state || !dst)
+        return GDN_ERR_NULL;
+    if (n < 0 || n > 65535 || d.H_k < 1 || d.H_v < 1 || d.d_k < 1 || d.d_v < 1 || d.W < 2 || d.N < 1 ||
+        d.H_v % d.H_k != 0)
+        return GDN_ERR_SHAPE;
+    const int64_t C = 2LL * d.H_k * d.d_k + (int64_t)d.H_v * d.d_v;
+    const int64_t slot_state = (int64_t)d.H_v * d.d_k * d.d_v;
+    if (slot_state % 4 != 0 || C % 4 != 0 || !aligned(state, 16) || !aligned(conv_state, 8))
+        return GDN_ERR_UNSUPPORTED;
+    gdn::SlotOpsParams p{};
+    p.state = state;
+    p.conv_state = conv_state;
+    p.src = src;
+    p.dst = dst;
+    p.slot_state = (size_t)slot_state;
+    p.slot_conv = (size_t)((d.W - 1) * C);
+    p.N = d.N;
+    return from_hip(gdn::launch_slot_ops(p, n, stream));
+}
+
+gdn_status gdn_slot_reset(const gdn_dims *dims, float *state, gdn_bf16 *conv_state, const int32_t *slots,
+                          int32_t n, hipStream_t stream)
+{
+    if (n != 0 && !slots)
+        return GDN_ERR_NULL;
+    return slot_ops_impl(dims, state, conv_state, nullptr, slots, n, stream);
+}
+
+gdn_status gdn_slot_copy(const gdn_dims *dims, float *state, gdn_bf16 *conv_state, const int32_t *src_slots,
+                         const int32_t *dst_slots, int32_t n, hipStream_t stream)
+{
+    if (n != 0 && (!src_slots || !dst_slots))
+        return GDN_ERR_NULL;
+    return slot_ops_impl(dims, state, conv_state, src_slots, dst_slots, n, stream);
+}
+
 gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
                              float *state, const int32_t *read_slot, const int32_t *write_slot,
                              float *sink, hipStream_t stream)

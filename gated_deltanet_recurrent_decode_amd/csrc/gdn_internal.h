@@ -51,9 +51,21 @@ struct ProbeParams {
     int B, H, N, mode;
 };
 
+// Zero (src == null) or copy (src[i] -> dst[i]) whole slots of the pool.
+struct SlotOpsParams {
+    float *state;         // [N][slot_state] fp32
+    uint16_t *conv_state; // [N][slot_conv] bf16
+    const int32_t *src;   // [n] or null (reset)
+    const int32_t *dst;   // [n]
+    size_t slot_state;    // H_v * d_k * d_v
+    size_t slot_conv;     // (W - 1) * C
+    int N;
+};
+
 hipError_t launch_gdn_step(const StepParams &p, int d_k, int d_v, hipStream_t stream);
 hipError_t launch_conv_decode(const ConvParams &p, hipStream_t stream);
 hipError_t launch_slot_commit(int32_t *read_slot, int32_t *write_slot, int B, hipStream_t stream);
+hipError_t launch_slot_ops(const SlotOpsParams &p, int n, hipStream_t stream);
 hipError_t launch_traffic_probe(const ProbeParams &p, int d_k, int d_v, hipStream_t stream);
 
 } // namespace gdn

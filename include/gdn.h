@@ -166,6 +166,31 @@ gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf1
  */
 gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipStream_t stream);
 
+/*
+ * gdn_slot_reset -- zero slots of the pool (PR #1139, "Tests": rollback and
+ * release zero both slots of a request).  For each i < n with
+ * s = slots[i] in [1, N): state[s] (H_v*d_k*d_v fp32) and conv_state[s]
+ * ((W-1)*C bf16) become +0.0.  Slot 0 and indices outside [1, N) are skipped
+ * (the null slot is never written).  Uses dims' H_k, H_v, d_k, d_v, W and N
+ * (B and T are ignored).  n = 0 returns GDN_OK at once; 0 <= n <= 65535.
+ * Alignment: state 16 bytes, conv_state 8 bytes.
+ */
+gdn_status gdn_slot_reset(const gdn_dims *dims, float *state, gdn_bf16 *conv_state, const int32_t *slots,
+                          int32_t n, hipStream_t stream);
+
+/*
+ * gdn_slot_copy -- copy whole slots (PR #1139, "Tests": decode snapshots and
+ * forks must read the right slot; a prefix snapshot is the conv window and
+ * the state).  For each i < n with src = src_slots[i] in [0, N) and
+ * dst = dst_slots[i] in [1, N): state[dst] = state[src] and
+ * conv_state[dst] = conv_state[src], bit for bit.  Pairs with dst = 0 or an
+ * index out of range are skipped.  Preconditions (not checked): the
+ * destinations are distinct and none is also a source in the same call.
+ * Sizes and alignment as gdn_slot_reset.
+ */
+gdn_status gdn_slot_copy(const gdn_dims *dims, float *state, gdn_bf16 *conv_state, const int32_t *src_slots,
+                         const int32_t *dst_slots, int32_t n, hipStream_t stream);
+
 /* Static text for a status code (host only). */
 const char *gdn_status_string(gdn_status status);
 

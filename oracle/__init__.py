@@ -66,6 +66,12 @@ def _load():
     lib.oracle_gdn_decode_step.argtypes = [i32] * 8 + [P, i64, P, P, P, P, P, P, P, P, P, dbl, dbl]
     lib.oracle_slot_commit.restype = None
     lib.oracle_slot_commit.argtypes = [P, P, i32]
+    lib.oracle_gdn_decode_step_tokens.restype = i32
+    lib.oracle_gdn_decode_step_tokens.argtypes = [i32] * 8 + [P, i64, P, P, P, P, P, P, P, P, P, dbl, dbl]
+    lib.oracle_slot_reset.restype = None
+    lib.oracle_slot_reset.argtypes = [i32] * 6 + [P, P, P, i32]
+    lib.oracle_slot_copy.restype = None
+    lib.oracle_slot_copy.argtypes = [i32] * 6 + [P, P, P, P, i32]
     _lib = lib
     return lib
 
@@ -183,3 +189,52 @@ def slot_commit(read_slot: np.ndarray, write_slot: np.ndarray) -> None:
     _check(write_slot, np.int32, "write_slot")
     assert read_slot.shape == write_slot.shape
     _load().oracle_slot_commit(_ptr(read_slot), _ptr(write_slot), read_slot.shape[0])
+
+
+def _pool_dims(state, conv_state):
+    N, H_v, d_k, d_v = state.shape
+    N2, Wm1, C = conv_state.shape
+    assert N2 == N
+    return H_v, d_k, d_v, Wm1 + 1, C, N
+
+
+def slot_reset(state: np.ndarray, conv_state: np.ndarray, slots: np.ndarray) -> None:
+    """Zero the state and conv window of every listed slot (slot 0 and out-of-range slots skipped)."""
+    _check(state, np.float32, "state")
+    _check(conv_state, np.uint16, "conv_state")
+    _check(slots, np.int32, "slots")
+    _load().oracle_slot_reset(*_pool_dims(state, conv_state), _ptr(state), _ptr(conv_state), _ptr(slots), slots.size)
+
+
+def slot_copy(state: np.ndarray, conv_state: np.ndarray, src: np.ndarray, dst: np.ndarray) -> None:
+    """Copy slot src[i] (state and conv window) to slot dst[i]; dst 0 and out-of-range pairs skipped."""
+    _check(state, np.float32, "state")
+    _check(conv_state, np.uint16, "conv_state")
+    _check(src, np.int32, "src")
+    _check(dst, np.int32, "dst")
+    assert src.shape == dst.shape
+    _load().oracle_slot_copy(*_pool_dims(state, conv_state), _ptr(state), _ptr(conv_state), _ptr(src), _ptr(dst),
+                             src.size)
+
+
+def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, token_slots,
+                           *, H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6) -> np.ndarray:
+    """T tokens a row from the read slot; after token t the state and window go to
+    token_slots[r][t] (0: not kept).  Returns out [B][T][H_v][d_v] fp64."""
+    B, T, C = x.shape
+    N, H_v, d_k, d_v = state.shape
+    W = conv_state.shape[1] + 1
+    for a, dt, n in ((x, np.uint16, "x"), (conv_w, np.uint16, "conv_w"), (conv_state, np.uint16, "conv_state"),
+                     (state, np.float32, "state"), (g, np.float32, "g"), (beta, np.float32, "beta"),
+                     (read_slot, np.int32, "read_slot"), (token_slots, np.int32, "token_slots")):
+        _check(a, dt, n)
+    _check(conv_b, np.uint16, "conv_b")
+    assert token_slots.shape == (B, T)
+    out = np.empty((B, T, H_v, d_v), np.float64)
+    rc = _load().oracle_gdn_decode_step_tokens(B, T, H_k, H_v, d_k, d_v, W, N, _ptr(x), T * C, _ptr(conv_w),
+                                               _ptr(conv_b), _ptr(conv_state), _ptr(state), _ptr(g), _ptr(beta),
+                                               _ptr(read_slot), _ptr(token_slots), _ptr(out), float(q_scale),
+                                               float(l2_eps))
+    if rc != 0:
+        raise ValueError("oracle_gdn_decode_step_tokens: invalid slot or shape")
+    return out

@@ -190,6 +190,36 @@ void oracle_delta_rule(int dk, int dv, double *S, const double *q, const double 
     free(pred);
 }
 
+/* ---------- one token of one row, every value head ----------
+ *
+ * Conv decode + SiLU over all C channels (the window advances by one token),
+ * then for each value head hv: q and k of key head hv / (H_v / H_k), v of
+ * head hv (channel order q | k | v, head-major), L2-normalised q (times
+ * q_scale) and k, and the gated delta rule on that head's tile of S.
+ * g_t, beta_t: [H_v] gates of this token; o_t: [H_v][d_v].  y, qh, kh are
+ * work arrays of C, d_k and d_k doubles.
+ */
+static void oracle_row_token(int H_k, int H_v, int d_k, int d_v, int W, const uint16_t *x_t,
+                             const uint16_t *conv_w, const uint16_t *conv_b, double *win, double *S,
+                             const float *g_t, const float *beta_t, double *o_t, double q_scale, double l2_eps,
+                             double *y, double *qh, double *kh)
+{
+    const int G = H_v / H_k;
+    const int C = 2 * H_k * d_k + H_v * d_v;
+    const size_t tile = (size_t)d_k * d_v;
+    oracle_conv_token(C, W, conv_w, conv_b, win, x_t, 1, y);
+    for (int hv = 0; hv < H_v; ++hv) {
+        int hk = hv / G;
+        const double *q = y + (size_t)hk * d_k;
+        const double *k = y + (size_t)H_k * d_k + (size_t)hk * d_k;
+        const double *v = y + (size_t)2 * H_k * d_k + (size_t)hv * d_v;
+        oracle_l2norm(d_k, q, l2_eps, q_scale, qh);
+        oracle_l2norm(d_k, k, l2_eps, 1.0, kh);
+        oracle_delta_rule(d_k, d_v, S + (size_t)hv * tile, qh, kh, v, (double)g_t[hv], (double)beta_t[hv],
+                          o_t + (size_t)hv * d_v);
+    }
+}
+
 /* ---------- the whole decode step over a pooled state ----------
  *
  * Layouts (host arrays):
@@ -212,7 +242,6 @@ int oracle_gdn_decode_step(int B, int T, int H_k, int H_v, int d_k, int d_v, int
 {
     if (H_k <= 0 || H_v % H_k != 0 || W < 1 || T < 1)
         return -1;
-    const int G = H_v / H_k;
     const int C = 2 * H_k * d_k + H_v * d_v;
     const size_t tile = (size_t)d_k * d_v;
     const size_t slot_state = (size_t)H_v * tile;
@@ -243,19 +272,10 @@ int oracle_gdn_decode_step(int B, int T, int H_k, int H_v, int d_k, int d_v, int
             win[e] = bf16_bits_to_double(csrc[e]);
 
         for (int t = 0; t < T; ++t) {
-            const uint16_t *x_t = x + (size_t)r * x_row_stride + (size_t)t * C;
-            oracle_conv_token(C, W, conv_w, conv_b, win, x_t, 1, y);
-            for (int hv = 0; hv < H_v; ++hv) {
-                int hk = hv / G;
-                const double *q = y + (size_t)hk * d_k;
-                const double *k = y + (size_t)H_k * d_k + (size_t)hk * d_k;
-                const double *v = y + (size_t)2 * H_k * d_k + (size_t)hv * d_v;
-                oracle_l2norm(d_k, q, l2_eps, q_scale, qh);
-                oracle_l2norm(d_k, k, l2_eps, 1.0, kh);
-                size_t gi = ((size_t)r * T + t) * H_v + hv;
-                oracle_delta_rule(d_k, d_v, S + (size_t)hv * tile, qh, kh, v, (double)g[gi],
-                                  (double)beta[gi], out_r + ((size_t)t * H_v + hv) * d_v);
-            }
+            size_t rt = (size_t)r * T + t;
+            oracle_row_token(H_k, H_v, d_k, d_v, W, x + (size_t)r * x_row_stride + (size_t)t * C, conv_w, conv_b,
+                             win, S, g + rt * H_v, beta + rt * H_v, out_r + (size_t)t * H_v * d_v, q_scale, l2_eps,
+                             y, qh, kh);
         }
 
         float *dst = state + (size_t)ws * slot_state;
@@ -279,4 +299,108 @@ void oracle_slot_commit(int32_t *read_slot, int32_t *write_slot, int B)
         read_slot[r] = write_slot[r];
         write_slot[r] = t;
     }
+}
+
+/* ---------- slot lifecycle (PR #1139, "Tests": rollback and release zero both
+ * slots of a request; decode snapshots and forks read the right slot) ----------
+ *
+ * A slot's contents are its state [H_v][d_k][d_v] fp32 and its conv window
+ * [W-1][C] bf16.  Slot 0 is the null slot: it is never written.  A slot index
+ * outside [0, N) is skipped.
+ */
+void oracle_slot_reset(int H_v, int d_k, int d_v, int W, int C, int N, float *state, uint16_t *conv_state,
+                       const int32_t *slots, int n)
+{
+    const size_t slot_state = (size_t)H_v * d_k * d_v;
+    const size_t slot_conv = (size_t)(W - 1) * C;
+    for (int i = 0; i < n; ++i) {
+        int s = slots[i];
+        if (s <= 0 || s >= N)
+            continue;
+        for (size_t e = 0; e < slot_state; ++e)
+            state[(size_t)s * slot_state + e] = 0.0f;
+        for (size_t e = 0; e < slot_conv; ++e)
+            conv_state[(size_t)s * slot_conv + e] = 0;
+    }
+}
+
+/* dst[i] <- src[i] for every pair, contents taken as they were before the call
+ * (the destinations must be distinct and must not be any pair's source). */
+void oracle_slot_copy(int H_v, int d_k, int d_v, int W, int C, int N, float *state, uint16_t *conv_state,
+                      const int32_t *src, const int32_t *dst, int n)
+{
+    const size_t slot_state = (size_t)H_v * d_k * d_v;
+    const size_t slot_conv = (size_t)(W - 1) * C;
+    for (int i = 0; i < n; ++i) {
+        int a = src[i], b = dst[i];
+        if (a < 0 || a >= N || b <= 0 || b >= N)
+            continue;
+        memcpy(state + (size_t)b * slot_state, state + (size_t)a * slot_state, slot_state * sizeof(float));
+        memcpy(conv_state + (size_t)b * slot_conv, conv_state + (size_t)a * slot_conv, slot_conv * sizeof(uint16_t));
+    }
+}
+
+/* ---------- a state per token (PR #1139, "What changed": speculative
+ * decoding keeps a state per token in its slots) ----------
+ *
+ * Like oracle_gdn_decode_step in place over T tokens, except that after token
+ * t the state and the conv window are stored (fp32 / exact bf16) to slot
+ * token_slots[r*T + t] when that slot is not 0, and nothing is stored at the
+ * end.  The state stays fp64 between tokens; each stored copy is rounded to
+ * fp32.  A row with read slot 0 is padding (zero output, no slot touched).
+ * Returns 0, or -1 on an invalid slot.
+ */
+int oracle_gdn_decode_step_tokens(int B, int T, int H_k, int H_v, int d_k, int d_v, int W, int N,
+                                  const uint16_t *x, int64_t x_row_stride, const uint16_t *conv_w,
+                                  const uint16_t *conv_b, uint16_t *conv_state, float *state,
+                                  const float *g, const float *beta, const int32_t *read_slot,
+                                  const int32_t *token_slots, double *out, double q_scale, double l2_eps)
+{
+    if (H_k <= 0 || H_v % H_k != 0 || W < 2 || T < 1)
+        return -1;
+    const int C = 2 * H_k * d_k + H_v * d_v;
+    const size_t tile = (size_t)d_k * d_v;
+    const size_t slot_state = (size_t)H_v * tile;
+    const size_t slot_conv = (size_t)(W - 1) * C;
+    double *S = (double *)malloc(sizeof(double) * slot_state);
+    double *win = (double *)malloc(sizeof(double) * slot_conv);
+    double *y = (double *)malloc(sizeof(double) * (size_t)C);
+    double *qh = (double *)malloc(sizeof(double) * (size_t)d_k);
+    double *kh = (double *)malloc(sizeof(double) * (size_t)d_k);
+    int ok = 1;
+    for (int r = 0; r < B && ok; ++r) {
+        int rs = read_slot[r];
+        if (rs < 0 || rs >= N) { ok = 0; break; }
+        for (int t = 0; t < T; ++t) {
+            int ts = token_slots[(size_t)r * T + t];
+            if (ts < 0 || ts >= N) ok = 0;
+        }
+        if (!ok)
+            break;
+        double *out_r = out + (size_t)r * T * H_v * d_v;
+        const int padding = (rs == 0);
+        if (padding) {
+            memset(out_r, 0, sizeof(double) * (size_t)T * H_v * d_v);
+            continue;
+        }
+        for (size_t e = 0; e < slot_state; ++e)
+            S[e] = (double)state[(size_t)rs * slot_state + e];
+        for (size_t e = 0; e < slot_conv; ++e)
+            win[e] = bf16_bits_to_double(conv_state[(size_t)rs * slot_conv + e]);
+        for (int t = 0; t < T; ++t) {
+            size_t rt = (size_t)r * T + t;
+            oracle_row_token(H_k, H_v, d_k, d_v, W, x + (size_t)r * x_row_stride + (size_t)t * C, conv_w, conv_b,
+                             win, S, g + rt * H_v, beta + rt * H_v, out_r + (size_t)t * H_v * d_v, q_scale, l2_eps,
+                             y, qh, kh);
+            int ts = token_slots[(size_t)r * T + t];
+            if (ts != 0) {
+                for (size_t e = 0; e < slot_state; ++e)
+                    state[(size_t)ts * slot_state + e] = (float)S[e];
+                for (size_t e = 0; e < slot_conv; ++e)
+                    conv_state[(size_t)ts * slot_conv + e] = double_to_bf16_bits_exact(win[e], &ok);
+            }
+        }
+    }
+    free(S); free(win); free(y); free(qh); free(kh);
+    return ok ? 0 : -1;
 }

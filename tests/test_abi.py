@@ -105,6 +105,20 @@ def test_step_commit_validation():
              1e-6, None) == OK
 
 
+def test_slot_ops_validation():
+    L = gdn.lib()
+    d = _dims()
+    assert L.gdn_slot_reset(None, FAKE, FAKE, FAKE, 4, None) == NULL
+    assert L.gdn_slot_reset(ctypes.byref(d), FAKE, FAKE, None, 4, None) == NULL
+    assert L.gdn_slot_reset(ctypes.byref(d), FAKE, FAKE, FAKE, -1, None) == SHAPE
+    assert L.gdn_slot_reset(ctypes.byref(d), FAKE, FAKE, FAKE, 70000, None) == SHAPE
+    assert L.gdn_slot_reset(ctypes.byref(d), ctypes.c_void_p(0x10008), FAKE, FAKE, 4, None) == UNSUPPORTED
+    assert L.gdn_slot_reset(ctypes.byref(d), None, None, None, 0, None) == OK
+    assert L.gdn_slot_copy(ctypes.byref(d), FAKE, FAKE, None, FAKE, 4, None) == NULL
+    assert L.gdn_slot_copy(ctypes.byref(d), FAKE, FAKE, FAKE, None, 4, None) == NULL
+    assert L.gdn_slot_copy(ctypes.byref(_dims(H_k=3, H_v=4)), FAKE, FAKE, FAKE, FAKE, 4, None) == SHAPE
+
+
 def test_conv_decode_validation():
     f = gdn.lib().conv_decode
     assert f(4, 16, 4, 9, None, 16, FAKE, None, FAKE, FAKE, None, FAKE, 16, 1, None) == NULL

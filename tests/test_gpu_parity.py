@@ -299,6 +299,48 @@ def test_conv_decode_matches_oracle(gdn, torch, bias, act, twin):
             assert t.equal(cs_dev[int(r)].view(t.int16), before[int(r)].view(t.int16))
 
 
+# ------------------------------------------------------------------ slot lifecycle
+
+def test_slot_reset_and_copy_match_oracle(gdn, torch):
+    t = torch
+    case = gi.small(B=8, T=1, H_k=2, H_v=4, d=128, N=21, seed=41)
+    s, pool = case.shape, case.pools[0]
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    reset = np.array([3, 0, 17, 25, -2, 8], np.int32)         # 0, 25 and -2 are skipped
+    src = np.array([1, 2, 0, 9, 30], np.int32)
+    dst = np.array([11, 12, 13, 0, 14], np.int32)             # dst 0 and src 30 are skipped
+    gdn.slot_reset(dp.state, dp.conv_state, t.from_numpy(reset).cuda(), H_k=s.H_k)
+    oracle.slot_reset(hp.state, hp.conv_state, reset)
+    gdn.slot_copy(dp.state, dp.conv_state, t.from_numpy(src).cuda(), t.from_numpy(dst).cuda(), H_k=s.H_k)
+    oracle.slot_copy(hp.state, hp.conv_state, src, dst)
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(dp.state.cpu().numpy().view(np.uint32), hp.state.view(np.uint32))
+    np.testing.assert_array_equal(H.bf16_host(dp.conv_state), hp.conv_state)
+    assert t.count_nonzero(dp.state[0].view(t.int32)) == 0
+
+
+def test_forked_slot_steps_like_its_source(gdn, torch):
+    """A snapshot made with slot_copy steps bit-identically to the slot it was
+    copied from (PR #1139 "Tests": forks read the right slot)."""
+    t = torch
+    case = gi.qwen08b(B=4, seed=3)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp = H.DevPool(pool)
+    src = t.from_numpy(pool.read_slot.copy()).cuda()
+    free = [sl for sl in range(s.N - 1, 0, -1) if sl not in set(pool.read_slot.tolist())][:4]
+    forks = t.from_numpy(np.array(free, np.int32)).cuda()
+    gdn.slot_copy(dp.state, dp.conv_state, src, forks, H_k=s.H_k)
+    o1 = t.empty((4, 1, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    o2 = t.empty_like(o1)
+    x, g, beta = H.bf16_dev(step.x), t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda()
+    gdn.gdn_decode_step(x, dp.conv_w, None, dp.conv_state, dp.state, g, beta, src, None, o1, H_k=s.H_k)
+    gdn.gdn_decode_step(x, dp.conv_w, None, dp.conv_state, dp.state, g, beta, forks, None, o2, H_k=s.H_k)
+    t.cuda.synchronize()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16))
+    assert t.equal(dp.state[src.long()].view(t.int32), dp.state[forks.long()].view(t.int32))
+    assert t.equal(dp.conv_state[src.long()].view(t.int16), dp.conv_state[forks.long()].view(t.int16))
+
+
 # ------------------------------------------------------------------ slot commit
 
 def test_slot_commit(gdn, torch):

@@ -410,3 +410,64 @@ def test_invalid_slot_is_refused():
     with pytest.raises(ValueError):
         oracle.gdn_decode_step(step.x, pool.conv_w, None, pool.conv_state.copy(), pool.state.copy(),
                                step.g, step.beta, bad, pool.write_slot, H_k=1)
+
+
+# ------------------------------------------------------------------ slot lifecycle
+
+def test_slot_reset_zeroes_listed_slots_only():
+    case = gi.small(B=3, T=1, H_k=2, H_v=2, d=64, N=9)
+    pool = case.pools[0]
+    st, cs = pool.state.copy(), pool.conv_state.copy()
+    oracle.slot_reset(st, cs, np.array([3, 0, 7, 99, -1], np.int32))
+    for s_ in range(9):
+        if s_ in (3, 7):
+            assert not st[s_].any() and not cs[s_].any()
+        else:
+            np.testing.assert_array_equal(st[s_], pool.state[s_])
+            np.testing.assert_array_equal(cs[s_], pool.conv_state[s_])
+
+
+def test_slot_copy_then_step_equals_step_on_the_source():
+    """A fork made by copying a slot steps exactly like the slot it came from."""
+    case = gi.small(B=1, T=1, H_k=2, H_v=2, d=64, N=9)
+    pool, step = case.pools[0], case.steps[0][0]
+    st, cs = pool.state.copy(), pool.conv_state.copy()
+    src, dst = int(pool.read_slot[0]), 5 if int(pool.read_slot[0]) != 5 else 6
+    oracle.slot_copy(st, cs, np.array([src, 4], np.int32), np.array([dst, 0], np.int32))
+    np.testing.assert_array_equal(st[dst], pool.state[src])
+    np.testing.assert_array_equal(cs[dst], pool.conv_state[src])
+    np.testing.assert_array_equal(st[0], 0.0)  # the null slot is never written
+    o1 = oracle.gdn_decode_step(step.x, pool.conv_w, None, cs, st, step.g, step.beta,
+                                np.array([src], np.int32), None, H_k=2)
+    o2 = oracle.gdn_decode_step(step.x, pool.conv_w, None, cs, st, step.g, step.beta,
+                                np.array([dst], np.int32), None, H_k=2)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(st[src], st[dst])
+
+
+# ------------------------------------------------------------------ a state per token
+
+def test_per_token_states_equal_prefix_steps():
+    """The state kept after token t equals an in-place call over the first t+1
+    tokens (pins the per-token store: slot, token index, and that the kept
+    state is the one after that token, not before it)."""
+    case = gi.small(B=2, T=3, H_k=2, H_v=4, d=64, N=13, twin=False)
+    pool, step = case.pools[0], case.steps[0][0]
+    st, cs = pool.state.copy(), pool.conv_state.copy()
+    free = [s_ for s_ in range(1, 13) if s_ not in set(pool.read_slot.tolist())]
+    tok = np.array([[free[0], free[1], 0], [free[2], free[3], free[4]]], np.int32)  # row 0 keeps tokens 0, 1
+    out = oracle.gdn_decode_step_tokens(step.x, pool.conv_w, None, cs, st, step.g, step.beta, pool.read_slot, tok,
+                                        H_k=2)
+    for t in range(3):
+        st2, cs2 = pool.state.copy(), pool.conv_state.copy()
+        o2 = oracle.gdn_decode_step(np.ascontiguousarray(step.x[:, :t + 1]), pool.conv_w, None, cs2, st2,
+                                    np.ascontiguousarray(step.g[:, :t + 1]), np.ascontiguousarray(step.beta[:, :t + 1]),
+                                    pool.read_slot, None, H_k=2)
+        np.testing.assert_array_equal(out[:, :t + 1], o2)
+        for r in range(2):
+            if tok[r, t]:
+                np.testing.assert_array_equal(st[tok[r, t]], st2[pool.read_slot[r]])
+                np.testing.assert_array_equal(cs[tok[r, t]], cs2[pool.read_slot[r]])
+    # the read slots are not written
+    for r in range(2):
+        np.testing.assert_array_equal(st[pool.read_slot[r]], pool.state[pool.read_slot[r]])
