@@ -46,9 +46,9 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "b208127d24f217eb6df75f28a5df47dd0e87abc46cee0d236fdee174cc90c970",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_097_107}
-KERNEL_SOURCES = ("gdn_step.hip", "device_common.h", "gdn_internal.h")
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "514c5dd48bcb5d87efd6a66585f3fbbbec9a852182e8d6ef28d1f0356654f255",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_273_349}
+KERNEL_SOURCES = ("gdn_step_twin.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 
 def kernel_sources_sha256() -> str:
@@ -293,26 +293,44 @@ class Bench:
         return g, n
 
     def calibration(self, reps: int = 64) -> dict:
-        """The step's state traffic with no arithmetic, same grid and slots."""
+        """The step's state traffic with no arithmetic, same grid, slots and cache
+        policies (read only, write only, the twin copy, the in-place read and
+        write back), plus the twin copy's bytes as one contiguous copy -- the
+        plain-copy ceiling.  Twin visits swap the read and write slots of a row
+        set every time round, as the commit does, so nothing is re-read warm."""
         torch, timer, gdn = self.torch, self.timer, self.gdn
         sh = self.stream.cuda_stream
         sink = torch.zeros(1, device="cuda")
         s = self.shape
         cal = {}
-        modes = ((0, "read_only"), (1, "write_only"), (2, "copy_twin"), (3, "read_write_in_place"))
+        modes = ((0, "read_only"), (1, "write_only"), (2, "copy_twin"), (3, "read_write_in_place"),
+                 (4, "contiguous_copy"))
+
+        # the contiguous copy rotates over disjoint ranges of 2B slots as well
+        ranges = [(torch.tensor([1 + 2 * self.B * k], dtype=torch.int32, device="cuda"),
+                   torch.tensor([1 + 2 * self.B * k + self.B], dtype=torch.int32, device="cuda"))
+                  for k in range(self.nsets)]
+
+        def slots(mode, i):
+            st = self.sets[i % self.nsets]
+            rd, wr = (ranges[i % self.nsets] if mode == 4 else (st["rd"], st["wr"]))
+            if self.twin and (i // self.nsets) % 2:
+                return wr, rd
+            return rd, wr
+
         for mode, name in modes:
-            if mode in (1, 2) and not self.twin:
+            if mode in (1, 2, 4) and not self.twin:
+                continue
+            if mode == 3 and self.twin:
                 continue
             for i in range(8):
-                st = self.sets[i % self.nsets]
-                gdn.traffic_probe(mode, self.state, st["rd"], st["wr"], sink)
+                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.B)
             torch.cuda.synchronize()
             evs = [(timer.event(), timer.event()) for _ in range(reps)]
             self._sleep_for(5.0 + reps * 0.12)
             for i in range(reps):
-                st = self.sets[i % self.nsets]
                 timer.record(evs[i][0], sh)
-                gdn.traffic_probe(mode, self.state, st["rd"], st["wr"], sink)
+                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.B)
                 timer.record(evs[i][1], sh)
             torch.cuda.synchronize()
             us = np.array([timer.elapsed_ms(a, b) for a, b in evs]) * 1e3
@@ -403,7 +421,7 @@ def main() -> int:
     result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                           "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                           "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                          "kernel": "gdn_step_kernel", "kernel_us_mean": k_us,
+                          "kernel": "gdn_step_twin_kernel" if twin else "gdn_step_kernel", "kernel_us_mean": k_us,
                           "kernel_us_p10": float(np.percentile(kus, 10)),
                           "kernel_us_p50": float(np.percentile(kus, 50)),
                           "kernel_us_p90": float(np.percentile(kus, 90)),

@@ -252,10 +252,12 @@ def slot_copy(state, conv_state, src_slots, dst_slots, *, H_k: int, stream=None)
                                                 _ptr(dst_slots), src_slots.numel(), _stream(stream)))
 
 
-def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, stream=None) -> None:
+def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, rows: int | None = None, stream=None) -> None:
     """The step's state traffic with no arithmetic (see ``gdn_traffic_probe`` in include/gdn.h).
 
-    mode 0 read only, 1 write only, 2 copy (twin), 3 read + write back (in place)."""
+    mode 0 read only, 1 write only, 2 copy (twin), 3 read + write back (in place),
+    4 the bytes of mode 2 as one contiguous copy of `rows` slots (default: the
+    length of read_slot) from slot read_slot[0] on to slot write_slot[0] on."""
     torch = _torch()
     _contig(_dev(state, "state", torch.float32), "state")
     _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
@@ -263,5 +265,6 @@ def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, stream=None)
     _contig(_dev(sink, "sink", torch.float32), "sink")
     N, H, d_k, d_v = state.shape
     _check("gdn_traffic_probe", lib().gdn_traffic_probe(
-        int(mode), read_slot.shape[0], H, d_k, d_v, N, _ptr(state), _ptr(read_slot), _ptr(write_slot),
+        int(mode), read_slot.shape[0] if rows is None else int(rows), H, d_k, d_v, N, _ptr(state), _ptr(read_slot),
+        _ptr(write_slot),
         _ptr(sink), _stream(stream)))

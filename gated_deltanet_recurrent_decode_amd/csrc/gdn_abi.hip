@@ -91,7 +91,8 @@ gdn_status step_impl(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stri
     p.C = (int)C;
     p.G = G;
     p.twin = write_slot ? 1 : 0;
-    return from_hip(gdn::launch_gdn_step(p, d.d_k, d.d_v, stream));
+    return from_hip(p.twin ? gdn::launch_gdn_step_twin(p, d.d_k, d.d_v, stream)
+                           : gdn::launch_gdn_step(p, d.d_k, d.d_v, stream));
 }
 
 } // namespace
@@ -224,9 +225,12 @@ gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, in
                              float *state, const int32_t *read_slot, const int32_t *write_slot,
                              float *sink, hipStream_t stream)
 {
-    if (!state || !read_slot || !sink || ((mode == 1 || mode == 2) && !write_slot))
+    if (!state || !read_slot || !sink || ((mode == 1 || mode == 2 || mode == 4) && !write_slot))
         return GDN_ERR_NULL;
-    if (mode < 0 || mode > 3 || B < 0 || H < 1 || N < 1 || (int64_t)B * H > INT32_MAX)
+    if (mode < 0 || mode > 4 || B < 0 || H < 1 || N < 1 || (int64_t)B * H > INT32_MAX)
+        return GDN_ERR_SHAPE;
+    // mode 4 addresses B whole slots with 32-bit byte offsets
+    if (mode == 4 && (int64_t)B * H * d_k * d_v * 4 > INT32_MAX)
         return GDN_ERR_SHAPE;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v))
         return GDN_ERR_UNSUPPORTED;

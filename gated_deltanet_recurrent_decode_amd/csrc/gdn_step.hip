@@ -1,13 +1,14 @@
-// gdn_step.hip -- the fused Gated DeltaNet decode step for gfx950.
+// gdn_step.hip -- the fused Gated DeltaNet decode step for gfx950, in place
+// (keep_in_place), T tokens a row.
 //
-// One workgroup owns a tile (row r, key head hk, HPW value heads of that key
-// head, DVS of the d_v state columns).  Per tile it:
-//   1. issues the loads of its fp32 state slices (d_k x DVS per head, 16-byte
+// One workgroup owns a key head of a row with all G of its value heads, so no
+// other workgroup reads a conv window it overwrites.  Per workgroup it:
+//   1. issues the loads of its G fp32 state tiles (d_k x d_v each, 16-byte
 //      loads, each wave instruction covering whole 128-byte lines), so HBM
 //      streams while the rest of the prologue runs;
-//   2. runs the conv decode + SiLU of the channels it needs (q and k of hk, v
-//      of its heads' columns) into LDS, and writes the advanced conv window of
-//      the channels it owns to the write slot;
+//   2. per token: runs the conv decode + SiLU of its channels (q and k of the
+//      key head, v of its value heads) into LDS, the window advancing in
+//      registers;
 //   3. L2-normalises q and k (wave butterflies over LDS, done redundantly by
 //      every wave so no extra barrier is needed);
 //   4. per head: one pass over the register-resident state gives both
@@ -15,89 +16,27 @@
 //      the row groups of a wave, LDS across waves, all in a fixed order);
 //      u = beta (v - alpha a); S' = alpha S + k^ u^T; o = alpha b + u (k^.q^),
 //      which equals S'^T q^;
-//   5. stores S' to the write slot (the read slot in place) and o as bf16.
+//   5. after the last token, stores the state and the advanced window back to
+//      the read slot; o goes out as bf16 every token.
 // The delta rule is Gated DeltaNet's (decay, predict with the decayed state,
 // correct, read out); the slot handling follows mstar PR #1139, "What
-// changed" (twin slots, keep_in_place) and "Tests" (padding on slot 0).
+// changed" (keep_in_place for prefill, split walks and the mixed step's decode
+// half) and "Tests" (padding on slot 0).  Twin-slot steps run in
+// gdn_step_twin.hip with the same thread layout and summation order.
 //
 // No MFMA: per state element the step does a handful of FMAs against 8 bytes
 // of HBM traffic, far under the fp32 ridge point, so the kernel is written for
 // bandwidth: wide coalesced loads, every tile loaded once, no re-reads.
 
-#include "device_common.h"
 #include "gdn_internal.h"
+#include "step_common.h"
 
 namespace gdn {
 
-// Thread layout of one head slice (d_k rows x DVS columns): eight row groups
-// always, CG = DVS/4 float4 column groups, so NTH = 8 * CG threads.  Thread
-// (rg, cg) holds rows rg, rg+8, ..., columns 4cg..4cg+3.  Fixing the row
-// groups at eight makes the order of every sum over d_k the same for every
-// column split and head grouping: in-thread over m, then the pairwise tree
-// ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over row groups -- so twin and
-// in-place launches, and padded and unpadded buckets, give identical bits.
-template <int DK, int DVS, int HPW>
-struct StepCfg {
-    static constexpr int RG = 8;                   // row groups
-    static constexpr int CG = DVS / 4;             // float4 column groups in a head slice
-    static constexpr int NTH = RG * CG;            // threads per head slice
-    static constexpr int RPT = DK / RG;            // state rows held by each thread
-    static constexpr int NWH = NTH / 64;           // waves per head slice
-    static constexpr int NT = NTH * HPW;           // threads per workgroup
-    static constexpr int NCH = 2 * DK + HPW * DVS; // conv channels the workgroup needs
-    static_assert(CG >= 8 && CG <= 64 && 64 % CG == 0, "a wave must hold whole row groups");
-    static_assert(DK % RG == 0, "rows must tile the row groups");
-    static_assert(NWH == 1 || NWH == 2 || NWH == 4, "pairwise tree over at most four waves");
-    static_assert(NT <= 1024, "workgroup too large");
-};
-
-// Raw buffer resource over one head's d_k x d_v fp32 tile: every state access
-// is a 32-bit per-lane offset plus a uniform row offset, so the sixteen loads
-// of a thread share one address register, and nothing outside the tile can
-// be touched (out-of-range lanes read 0 and drop their stores).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(float *base, uint32_t bytes)
+template <int DK, int DV, int HPW>
+__global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-}
-
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-
-// One channel of the width-4 conv with SiLU, from bf16 values already moved
-// into the high half of a 32-bit word (so they read as fp32): taps 0-1 in
-// w01, taps 2-3 in w23 (tap 3 multiplies the current token), the three
-// window values oldest first, the token, and the bias (added when present).
-__device__ __forceinline__ float conv_tap4(uint32_t w01, uint32_t w23, uint32_t a0, uint32_t a1, uint32_t a2,
-                                           uint32_t xv, uint32_t bias, bool has_bias)
-{
-    float acc = __uint_as_float(w01 << 16) * __uint_as_float(a0);
-    acc = fmaf(__uint_as_float(w01 & 0xffff0000u), __uint_as_float(a1), acc);
-    acc = fmaf(__uint_as_float(w23 << 16), __uint_as_float(a2), acc);
-    acc = fmaf(__uint_as_float(w23 & 0xffff0000u), __uint_as_float(xv), acc);
-    if (has_bias)
-        acc += __uint_as_float(bias);
-    return silu(acc);
-}
-
-// Cache-policy bits of the buffer accesses (gfx950): 2 = nt (streaming).  A
-// state tile is read once and written once per step and is not touched again
-// until the next step of the layer, long after the caches have turned over,
-// so both directions stream past the caches.  On MI355X this is what lets the
-// write stream overlap the read stream of other tiles: plain stores allocate
-// in the caches and their evictions compete with the reads, and streaming
-// reads leave the Infinity Cache to the small per-row inputs.
-constexpr int kLoadPolicy = 2;
-constexpr int kStorePolicy = 2;
-// Four waves per SIMD for the whole-tile single-token kernel: a 64-row step
-// (1024 head tiles of 256 threads) is then resident on the 256 compute units
-// all at once.  The multi-token kernels carry more live state and are left
-// to the compiler (forcing four waves there spills to scratch).
-constexpr int kWavesPerEU = 4;
-
-template <int DK, int DV, int DVS, int HPW, bool MT>
-__global__ __launch_bounds__(2 * DVS * HPW) __attribute__((amdgpu_waves_per_eu((!MT && DVS == DV) ? kWavesPerEU : 1)))
-void gdn_step_kernel(StepParams p)
-{
+    constexpr int DVS = DV; // whole tiles
     using Cfg = StepCfg<DK, DVS, HPW>;
     static_assert(Cfg::NT == 2 * DVS * HPW, "launch bound must match the layout");
     constexpr int NT = Cfg::NT, NTH = Cfg::NTH, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH;
@@ -117,29 +56,15 @@ void gdn_step_kernel(StepParams p)
     const int wv = ht >> 6;
     const int lane = tid & 63;
 
-    // tile -> (row, key head, head group, column slice)
-    int tile = blockIdx.x;
-    const int cs = tile % p.n_slices;
-    tile /= p.n_slices;
-    const int ngrp = p.G / HPW;
-    const int grp = tile % ngrp;
-    tile /= ngrp;
-    const int hk = tile % p.H_k;
-    const int r = tile / p.H_k;
-    const int hv0 = hk * p.G + grp * HPW;
-    const int col0 = cs * DVS;
-    const int T = MT ? p.T : 1;
+    // workgroup -> (row, key head); its value heads are hk*G .. hk*G + G-1
+    const int hk = blockIdx.x % p.H_k;
+    const int r = blockIdx.x / p.H_k;
+    const int hv0 = hk * p.G;
+    constexpr int col0 = 0;
+    const int T = p.T;
 
     const int rs = p.read_slot[r];
-    const int ws = p.twin ? p.write_slot[r] : rs;
-    const bool bad = rs < 0 || rs >= p.N || ws < 0 || ws >= p.N || (p.twin && ws == rs);
-    // fused commit: one workgroup per row writes the swapped pair into the
-    // next step's slot arrays (distinct from the ones every workgroup of this
-    // step reads, so there is no race)
-    if (p.next_read_slot && hk == 0 && grp == 0 && cs == 0 && tid == 0) {
-        p.next_read_slot[r] = ws;
-        p.next_write_slot[r] = rs;
-    }
+    const bool bad = rs < 0 || rs >= p.N;
     if (rs == 0 || bad) {
         // padding row (or a row with an unusable slot): touch no slot; out gets
         // +0.0 for padding and NaN for the unusable slot.
@@ -163,7 +88,6 @@ void gdn_step_kernel(StepParams p)
     constexpr int NCL = NCH / 4;               // conv lanes (channel quads)
     constexpr int NCW = (NCL + 63) / 64;       // waves' worth of conv lanes
     constexpr int NCQ = (NCL + NT - 1) / NT;   // quads per thread
-    const bool own_qk = (grp == 0 && cs == 0);
     const int C = p.C;
     const int hv = hv0 + hloc;
     // gates of token 0, also ahead of the state tile
@@ -171,7 +95,7 @@ void gdn_step_kernel(StepParams p)
     float b_t = p.beta[(size_t)r * T * p.H_v + hv];
     const uint16_t *xrow = p.x + (size_t)r * p.x_row_stride;
     const uint16_t *cs_rd = p.conv_state + (size_t)rs * 3 * C;
-    uint16_t *cs_wr = p.conv_state + (size_t)ws * 3 * C;
+    uint16_t *cs_wr = p.conv_state + (size_t)rs * 3 * C;
     const uint16_t *bias_src = p.conv_b ? p.conv_b : p.conv_w; // conv_w: in-bounds stand-in, unused
     bool conv_wave[NCQ], conv_lane[NCQ], own[NCQ];
     int c[NCQ], e4[NCQ];
@@ -191,7 +115,7 @@ void gdn_step_kernel(StepParams p)
         c[k] = isq ? hk * DK + e
                : isk ? p.H_k * DK + hk * DK + (e - DK)
                      : 2 * p.H_k * DK + (hv0 + h) * DV + col0 + (ve - h * DVS);
-        own[k] = conv_lane[k] && ((isq || isk) ? own_qk : true);
+        own[k] = conv_lane[k]; // the workgroup owns every channel it reads
         wlo[k] = whi[k] = make_uint4(0, 0, 0, 0);
         wn0[k] = wn1[k] = wn2[k] = xq[k] = bq[k] = make_uint2(0, 0);
         if (conv_wave[k]) {
@@ -223,7 +147,7 @@ void gdn_step_kernel(StepParams p)
 
     const bool has_bias = p.conv_b != nullptr;
     for (int t = 0; t < T; ++t) {
-        if (MT && t > 0) {
+        if (t > 0) {
             lds_barrier(); // the previous token's readers of y_lds / red_lds are done
 #pragma unroll
             for (int k = 0; k < NCQ; ++k)
@@ -361,57 +285,34 @@ void gdn_step_kernel(StepParams p)
     }
 
     // ---- new state -> write slot (the read slot in place)
-    const __amdgpu_buffer_rsrc_t wr_tile = tile_rsrc(p.state + ((size_t)ws * p.H_v + hv) * TILE, TILE * 4u);
+    const __amdgpu_buffer_rsrc_t wr_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u);
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), wr_tile, voff, m * RG * DV * 4,
-                                               kStorePolicy);
+                                               kStorePolicyInPlace);
 }
 
-template <int DK, int DV, int DVS, int HPW, bool MT>
+template <int DK, int DV, int HPW>
 static hipError_t launch_step(const StepParams &p, hipStream_t stream)
 {
-    const long long tiles = (long long)p.B * p.H_k * (p.G / HPW) * (DV / DVS);
+    const long long tiles = (long long)p.B * p.H_k;
     if (tiles <= 0)
         return hipSuccess;
     StepParams q = p;
-    q.n_slices = DV / DVS;
+    q.n_slices = 1;
     void *args[] = {&q};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, DVS, HPW, MT>),
-                           dim3((unsigned)tiles), dim3(StepCfg<DK, DVS, HPW>::NT), args, 0, stream);
-}
-
-// Column slices per head for a twin step: split d_v only when the rows give
-// very few workgroups (with the state cold in HBM, whole tiles win from 16
-// rows of 16 heads up; slices stay >= 32 columns).
-static int pick_slices(const StepParams &p, int dv)
-{
-    const long long heads = (long long)p.B * p.H_v;
-    if (heads >= 128)
-        return 1;
-    if (heads >= 32 || dv < 128)
-        return 2;
-    return 4;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, HPW>), dim3((unsigned)tiles),
+                           dim3(StepCfg<DK, DV, HPW>::NT), args, 0, stream);
 }
 
 template <int DK, int DV>
 static hipError_t dispatch_dims(const StepParams &p, hipStream_t stream)
 {
-    if (!p.twin) {
-        // in place: one workgroup owns every channel of its key head (all G
-        // value heads, all columns), so no other workgroup reads a conv window
-        // it overwrites
-        switch (p.G) {
-        case 1: return launch_step<DK, DV, DV, 1, true>(p, stream);
-        case 2: return launch_step<DK, DV, DV, 2, true>(p, stream);
-        case 4: return launch_step<DK, DV, DV, 4, true>(p, stream);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    switch (pick_slices(p, DV)) {
-    case 1: return launch_step<DK, DV, DV, 1, false>(p, stream);
-    case 2: return launch_step<DK, DV, DV / 2, 1, false>(p, stream);
-    default: return launch_step<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32), 1, false>(p, stream);
+    switch (p.G) {
+    case 1: return launch_step<DK, DV, 1>(p, stream);
+    case 2: return launch_step<DK, DV, 2>(p, stream);
+    case 4: return launch_step<DK, DV, 4>(p, stream);
+    default: return hipErrorInvalidValue;
     }
 }
 

@@ -1,0 +1,365 @@
+// gdn_step_twin.hip -- the twin-slot, single-token decode step for gfx950.
+//
+// The same computation as the in-place step kernel (conv decode + SiLU, L2
+// norms, gated delta rule, read-out), with the same thread layout and the
+// same fixed summation order, so twin and in-place writes give identical
+// bits; it reads one slot of the request's pair and writes the other (mstar
+// PR #1139, "What changed").  One workgroup per head tile (row, value head,
+// column slice).  The code is straight-line: a padding row (read slot 0) or
+// a row with an unusable slot gets buffer resources of size 0, so its loads
+// return zeros without touching memory and its stores are dropped, and only
+// its read-out is written (zeros, or NaN for an unusable slot).  Without a
+// branch between the slot lookup and the loads, every load is issued after
+// a short chain of scalar waits, and each later wait covers exactly the loads
+// it needs (measured on MI355X: 0.5-1 us faster at 64 rows than the same
+// arithmetic with an early exit and pointer-based loads).
+
+#include "gdn_internal.h"
+#include "step_common.h"
+
+namespace gdn {
+
+// A byte offset past the end of every buffer resource used here: a load there
+// returns 0 and a store there is dropped, with no memory access.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bf16_rsrc(const uint16_t *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint2 load_b64(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Everything one head tile carries from its loads to its stores.
+template <int DK, int DVS>
+struct TwinTile {
+    using Cfg = StepCfg<DK, DVS, 1>;
+    static constexpr int NCL = Cfg::NCH / 4;                  // conv lanes (channel quads)
+    static constexpr int NCQ = (NCL + Cfg::NT - 1) / Cfg::NT; // quads per thread
+    int r, hv, hk, col0, rs, ws;
+    bool valid, real, own_qk;
+    uint16_t fill;
+    float g, beta;
+    int e4[NCQ], c[NCQ];
+    bool lane_ok[NCQ], own[NCQ];
+    uint4 wlo[NCQ], whi[NCQ];
+    uint2 wn0[NCQ], wn1[NCQ], wn2[NCQ], xq[NCQ], bq[NCQ];
+    float4 s[Cfg::RPT];
+};
+
+// Tile index -> (row, value head, column slice), its slots and gates.  Tiles
+// are ordered row-major, then value head, then column slice.
+template <int DK, int DVS>
+__device__ __forceinline__ void twin_locate(TwinTile<DK, DVS> &t, int tile, const StepParams &p)
+{
+    const int ntiles = p.B * p.H_v * p.n_slices;
+    t.valid = tile < ntiles;
+    const int tt = t.valid ? tile : 0;
+    const int cs = tt % p.n_slices;
+    const int rh = tt / p.n_slices;
+    t.hv = rh % p.H_v;
+    t.r = rh / p.H_v;
+    t.hk = t.hv / p.G;
+    t.col0 = cs * DVS;
+    t.own_qk = (t.hv % p.G == 0) && cs == 0; // the tile that writes back the key head's q/k windows
+    t.rs = p.read_slot[t.r];
+    t.ws = p.write_slot[t.r];
+    const bool bad = t.rs < 0 || t.rs >= p.N || t.ws < 0 || t.ws >= p.N || t.ws == t.rs;
+    t.real = t.valid && t.rs != 0 && !bad;
+    t.fill = t.rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
+    t.g = p.g[(size_t)t.r * p.H_v + t.hv];
+    t.beta = p.beta[(size_t)t.r * p.H_v + t.hv];
+}
+
+// The conv inputs of the tile's channels (q and k of its key head, v of its
+// columns): each conv lane takes four consecutive channels -- 16-byte weight
+// loads, 8-byte window, x and bias loads, raw bf16 bits.
+template <int DK, int DV, int DVS>
+__device__ __forceinline__ void twin_issue_small(TwinTile<DK, DVS> &t, const StepParams &p)
+{
+    using TT = TwinTile<DK, DVS>;
+    constexpr int NT = TT::Cfg::NT;
+    const int C = p.C;
+    const uint32_t cbytes = (uint32_t)C * 2u;
+    const __amdgpu_buffer_rsrc_t cw = bf16_rsrc(p.conv_w, cbytes * 4u);
+    const __amdgpu_buffer_rsrc_t win = bf16_rsrc(p.conv_state + (size_t)(t.real ? t.rs : 0) * 3 * C,
+                                                 t.real ? 3u * cbytes : 0u);
+    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x + (size_t)t.r * p.x_row_stride, t.real ? cbytes : 0u);
+    const __amdgpu_buffer_rsrc_t br = bf16_rsrc(p.conv_b ? p.conv_b : p.conv_w, p.conv_b ? cbytes : 0u);
+#pragma unroll
+    for (int q = 0; q < TT::NCQ; ++q) {
+        const int li = threadIdx.x + q * NT;
+        t.lane_ok[q] = li < TT::NCL;
+        const int e = t.lane_ok[q] ? 4 * li : 0;
+        t.e4[q] = e;
+        const bool isq = e < DK;
+        const bool isk = !isq && e < 2 * DK;
+        t.c[q] = isq ? t.hk * DK + e
+                 : isk ? p.H_k * DK + t.hk * DK + (e - DK)
+                       : 2 * p.H_k * DK + t.hv * DV + t.col0 + (e - 2 * DK);
+        t.own[q] = t.lane_ok[q] && ((isq || isk) ? t.own_qk : true);
+        const uint32_t o2 = t.lane_ok[q] ? (uint32_t)t.c[q] * 2u : kOOB;
+        const uint32_t o8 = t.lane_ok[q] ? (uint32_t)t.c[q] * 8u : kOOB;
+        t.wlo[q] = load_b128(cw, o8);
+        t.whi[q] = load_b128(cw, o8 + 16u);
+        t.wn0[q] = load_b64(win, o2);
+        t.wn1[q] = load_b64(win, o2 + cbytes);
+        t.wn2[q] = load_b64(win, o2 + 2u * cbytes);
+        t.xq[q] = load_b64(xr, o2);
+        t.bq[q] = load_b64(br, o2);
+    }
+}
+
+// The tile's fp32 state slice -> registers (16-byte streaming loads; each wave
+// instruction covers whole 128-byte lines).
+template <int DK, int DV, int DVS>
+__device__ __forceinline__ void twin_issue_state(TwinTile<DK, DVS> &t, const StepParams &p, uint32_t voff)
+{
+    using Cfg = typename TwinTile<DK, DVS>::Cfg;
+    constexpr uint32_t TILE = (uint32_t)DK * DV;
+    const __amdgpu_buffer_rsrc_t rd =
+        tile_rsrc(p.state + ((size_t)(t.real ? t.rs : 0) * p.H_v + t.hv) * TILE, t.real ? TILE * 4u : 0u);
+    const uint32_t vo = voff + (uint32_t)(t.col0 * 4);
+#pragma unroll
+    for (int m = 0; m < Cfg::RPT; ++m)
+        t.s[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, vo, m * Cfg::RG * DV * 4,
+                                                                                 kLoadPolicy));
+}
+
+// Conv + SiLU -> LDS, L2 norms, projections, the fixed-order reduction, the
+// delta update, the read-out, and the stores of o, the advanced conv windows
+// and the new state.
+template <int DK, int DV, int DVS>
+__device__ __forceinline__ void twin_process(TwinTile<DK, DVS> &t, const StepParams &p, int cg, int rg, int wv,
+                                             int lane, uint32_t voff, float *y_lds, float4 (*red_lds)[2][DVS / 4])
+{
+    using TT = TwinTile<DK, DVS>;
+    using Cfg = typename TT::Cfg;
+    constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH, NCH = Cfg::NCH;
+    constexpr int NCW = (TT::NCL + 63) / 64; // waves' worth of conv lanes
+    const bool has_bias = p.conv_b != nullptr;
+
+    // ---- conv decode + SiLU -> LDS; the window advances in registers
+#pragma unroll
+    for (int q = 0; q < TT::NCQ; ++q) {
+        if (((int)(threadIdx.x + q * Cfg::NT) >> 6) >= NCW) // wave-uniform; no memory access inside
+            continue;
+        const uint4 wl = t.wlo[q], wh = t.whi[q];
+        const uint2 a0 = t.wn0[q], a1 = t.wn1[q], a2 = t.wn2[q], xx = t.xq[q], bb = t.bq[q];
+        float4 y;
+        y.x = conv_tap4(wl.x, wl.y, a0.x << 16, a1.x << 16, a2.x << 16, xx.x << 16, bb.x << 16, has_bias);
+        y.y = conv_tap4(wl.z, wl.w, a0.x & 0xffff0000u, a1.x & 0xffff0000u, a2.x & 0xffff0000u,
+                        xx.x & 0xffff0000u, bb.x & 0xffff0000u, has_bias);
+        y.z = conv_tap4(wh.x, wh.y, a0.y << 16, a1.y << 16, a2.y << 16, xx.y << 16, bb.y << 16, has_bias);
+        y.w = conv_tap4(wh.z, wh.w, a0.y & 0xffff0000u, a1.y & 0xffff0000u, a2.y & 0xffff0000u,
+                        xx.y & 0xffff0000u, bb.y & 0xffff0000u, has_bias);
+        *reinterpret_cast<float4 *>(&y_lds[t.lane_ok[q] ? t.e4[q] : NCH]) = y;
+        t.wn0[q] = a1;
+        t.wn1[q] = a2;
+        t.wn2[q] = xx;
+    }
+    lds_barrier();
+
+    // ---- L2 norms of q and k (every wave computes the same sums)
+    float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int i = lane; i < DK; i += 64) {
+        const float qv = y_lds[i], kv = y_lds[DK + i];
+        sq = fmaf(qv, qv, sq);
+        sk = fmaf(kv, kv, sk);
+        sqk = fmaf(qv, kv, sqk);
+    }
+    sq = xor_sum<1>(sq);
+    sk = xor_sum<1>(sk);
+    sqk = xor_sum<1>(sqk);
+    const float rq = 1.0f / sqrtf(sq + p.l2_eps);
+    const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+    const float qs = rq * p.q_scale;
+    const float kq = sqk * rk * qs; // k^ . q^
+
+    // ---- projections of the state onto k^ and q^
+    const float alpha = expf(t.g);
+    const float bt = t.beta;
+    float4 pa = f4_zero(), pb = f4_zero();
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const float kh = y_lds[DK + i] * rk;
+        const float qh = y_lds[i] * qs;
+        pa.x = fmaf(t.s[m].x, kh, pa.x);
+        pa.y = fmaf(t.s[m].y, kh, pa.y);
+        pa.z = fmaf(t.s[m].z, kh, pa.z);
+        pa.w = fmaf(t.s[m].w, kh, pa.w);
+        pb.x = fmaf(t.s[m].x, qh, pb.x);
+        pb.y = fmaf(t.s[m].y, qh, pb.y);
+        pb.z = fmaf(t.s[m].z, qh, pb.z);
+        pb.w = fmaf(t.s[m].w, qh, pb.w);
+    }
+    pa.x = xor_sum<CG>(pa.x);
+    pa.y = xor_sum<CG>(pa.y);
+    pa.z = xor_sum<CG>(pa.z);
+    pa.w = xor_sum<CG>(pa.w);
+    pb.x = xor_sum<CG>(pb.x);
+    pb.y = xor_sum<CG>(pb.y);
+    pb.z = xor_sum<CG>(pb.z);
+    pb.w = xor_sum<CG>(pb.w);
+    if (lane < CG) {
+        red_lds[wv][0][cg] = pa;
+        red_lds[wv][1][cg] = pb;
+    }
+    lds_barrier();
+    // the higher row-group bits live in the wave index: the same pairwise tree
+    float4 av[NWH], bv[NWH];
+#pragma unroll
+    for (int w = 0; w < NWH; ++w) {
+        av[w] = red_lds[w][0][cg];
+        bv[w] = red_lds[w][1][cg];
+    }
+#pragma unroll
+    for (int st = 1; st < NWH; st *= 2) {
+#pragma unroll
+        for (int w = 0; w + st < NWH; w += 2 * st) {
+            av[w].x += av[w + st].x; av[w].y += av[w + st].y; av[w].z += av[w + st].z; av[w].w += av[w + st].w;
+            bv[w].x += bv[w + st].x; bv[w].y += bv[w + st].y; bv[w].z += bv[w + st].z; bv[w].w += bv[w + st].w;
+        }
+    }
+    const float4 a = av[0], b = bv[0];
+
+    // ---- delta update in registers, and the read-out
+    const float *vv = &y_lds[2 * DK + 4 * cg];
+    float4 u;
+    u.x = bt * (vv[0] - alpha * a.x);
+    u.y = bt * (vv[1] - alpha * a.y);
+    u.z = bt * (vv[2] - alpha * a.z);
+    u.w = bt * (vv[3] - alpha * a.w);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const float kh = y_lds[DK + rg + RG * m] * rk;
+        t.s[m].x = fmaf(kh, u.x, alpha * t.s[m].x);
+        t.s[m].y = fmaf(kh, u.y, alpha * t.s[m].y);
+        t.s[m].z = fmaf(kh, u.z, alpha * t.s[m].z);
+        t.s[m].w = fmaf(kh, u.w, alpha * t.s[m].w);
+    }
+    const float o0 = fmaf(u.x, kq, alpha * b.x);
+    const float o1 = fmaf(u.y, kq, alpha * b.y);
+    const float o2 = fmaf(u.z, kq, alpha * b.z);
+    const float o3 = fmaf(u.w, kq, alpha * b.w);
+    const uint32_t f2 = (uint32_t)t.fill * 0x10001u;
+    const u32x2 pk = {t.real ? ((uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16)) : f2,
+                      t.real ? ((uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16)) : f2};
+    // o: row group 0 of every column group; padding and unusable rows get their fill
+    const __amdgpu_buffer_rsrc_t orow =
+        bf16_rsrc(p.out + ((size_t)t.r * p.H_v + t.hv) * DV, t.valid ? (uint32_t)DV * 2u : 0u);
+    if (wv == 0) // row group 0 lives in wave 0; the stores of the other waves would all be dropped
+        __builtin_amdgcn_raw_buffer_store_b64(pk, orow, rg == 0 ? (uint32_t)(t.col0 + 4 * cg) * 2u : kOOB, 0, 0);
+
+    // ---- advanced conv windows of the channels this tile owns: a shift of
+    // bf16 values, stored as the bits they were read as
+    const uint32_t cbytes = (uint32_t)p.C * 2u;
+    const __amdgpu_buffer_rsrc_t wwin = bf16_rsrc(p.conv_state + (size_t)(t.real ? t.ws : 0) * 3 * p.C,
+                                                  t.real ? 3u * cbytes : 0u);
+#pragma unroll
+    for (int q = 0; q < TT::NCQ; ++q) {
+        if (((int)(threadIdx.x + q * Cfg::NT) >> 6) >= NCW) // waves with no conv lane own nothing
+            continue;
+        const uint32_t o2w = t.own[q] ? (uint32_t)t.c[q] * 2u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{t.wn0[q].x, t.wn0[q].y}, wwin, o2w, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{t.wn1[q].x, t.wn1[q].y}, wwin, o2w + cbytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{t.wn2[q].x, t.wn2[q].y}, wwin, o2w + 2u * cbytes, 0, 0);
+    }
+
+    // ---- new state -> write slot
+    constexpr uint32_t TILE = (uint32_t)DK * DV;
+    const __amdgpu_buffer_rsrc_t wr =
+        tile_rsrc(p.state + ((size_t)(t.real ? t.ws : 0) * p.H_v + t.hv) * TILE, t.real ? TILE * 4u : 0u);
+    const uint32_t vo = voff + (uint32_t)(t.col0 * 4);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t.s[m]), wr, vo, m * RG * DV * 4,
+                                               kStorePolicyTwin);
+}
+
+template <int DK, int DV, int DVS>
+__global__ __launch_bounds__(2 * DVS) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void gdn_step_twin_kernel(StepParams p)
+{
+    using TT = TwinTile<DK, DVS>;
+    using Cfg = typename TT::Cfg;
+    constexpr int CG = Cfg::CG, NWH = Cfg::NWH, NCH = Cfg::NCH;
+    static_assert(Cfg::NT == 2 * DVS, "launch bound must match the layout");
+
+    __shared__ float y_lds[NCH + 4]; // + a padding slot for spare conv lanes
+    __shared__ float4 red_lds[NWH][2][CG];
+
+    const int tid = threadIdx.x;
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    const int wv = tid >> 6;
+    const int lane = tid & 63;
+    const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
+
+    TT t;
+    twin_locate(t, blockIdx.x, p);
+    twin_issue_small<DK, DV, DVS>(t, p);
+    __builtin_amdgcn_sched_barrier(0); // the small loads stay ahead of the tile loads
+    twin_issue_state<DK, DV, DVS>(t, p, voff);
+    // every load is in flight; keep the scheduler from sinking any below the first wait
+    __builtin_amdgcn_sched_barrier(0);
+    twin_process<DK, DV, DVS>(t, p, cg, rg, wv, lane, voff, y_lds, red_lds);
+
+    // fused commit: the workgroup of a row's first tile writes the swapped
+    // pair into the next step's slot arrays (distinct from the ones this step
+    // reads, so there is no race)
+    if (p.next_read_slot && tid == 0 && t.valid && t.hv == 0 && t.col0 == 0) {
+        p.next_read_slot[t.r] = t.ws;
+        p.next_write_slot[t.r] = t.rs;
+    }
+}
+
+template <int DK, int DV, int DVS>
+static hipError_t launch_twin(const StepParams &p, hipStream_t stream)
+{
+    StepParams q = p;
+    q.n_slices = DV / DVS;
+    const long long tiles = (long long)p.B * p.H_v * q.n_slices;
+    if (tiles <= 0)
+        return hipSuccess;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_step_twin_kernel<DK, DV, DVS>), dim3((unsigned)tiles),
+                           dim3(2 * DVS), args, 0, stream);
+}
+
+// Column slices per head: split d_v only when the rows give very few
+// workgroups (with the state cold in HBM, whole tiles win from 16 rows of 16
+// heads up; slices stay >= 32 columns).
+template <int DK, int DV>
+static hipError_t dispatch_twin(const StepParams &p, hipStream_t stream)
+{
+    const long long heads = (long long)p.B * p.H_v;
+    if (heads >= 128)
+        return launch_twin<DK, DV, DV>(p, stream);
+    if (heads >= 32 || DV < 128)
+        return launch_twin<DK, DV, DV / 2>(p, stream);
+    return launch_twin<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>(p, stream);
+}
+
+hipError_t launch_gdn_step_twin(const StepParams &p, int d_k, int d_v, hipStream_t stream)
+{
+    if (d_k == 128 && d_v == 128) return dispatch_twin<128, 128>(p, stream);
+    if (d_k == 64 && d_v == 64) return dispatch_twin<64, 64>(p, stream);
+    if (d_k == 128 && d_v == 64) return dispatch_twin<128, 64>(p, stream);
+    if (d_k == 64 && d_v == 128) return dispatch_twin<64, 128>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+} // namespace gdn

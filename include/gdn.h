@@ -203,9 +203,15 @@ const char *gdn_status_string(gdn_status status);
  *   mode 1  write only: writes every real row's write-slot tiles
  *   mode 2  copy: reads the read slot, writes the write slot (twin traffic)
  *   mode 3  in place: reads the read slot and writes it back
- * state is [N][H][d_k][d_v] fp32; rows with read slot 0 are skipped.
- * sink [1] fp32 receives nothing in practice; it only keeps the read-only
- * mode's loads alive.  d_k, d_v in {64, 128}.
+ *   mode 4  the bytes of mode 2 as one contiguous copy: the B slots from
+ *           read_slot[0] on to the B slots from write_slot[0] on (the
+ *           plain-copy ceiling).  A range outside [1, N) makes it a no-op;
+ *           B slots must be under 2 GiB (else GDN_ERR_SHAPE); overlapping
+ *           ranges race.
+ * Loads stream (nt); stores use the step's policy (write-through for a twin
+ * write, streaming in place).  state is [N][H][d_k][d_v] fp32; rows with
+ * read slot 0 are skipped.  sink [1] fp32 receives nothing in practice; it
+ * only keeps the read-only mode's loads alive.  d_k, d_v in {64, 128}.
  */
 gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
                              float *state, const int32_t *read_slot, const int32_t *write_slot,

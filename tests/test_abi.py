@@ -135,6 +135,8 @@ def test_slot_commit_and_probe_validation():
     assert L.slot_commit(FAKE, FAKE, -1, None) == SHAPE
     assert L.gdn_traffic_probe(2, 4, 4, 64, 64, 9, FAKE, FAKE, None, FAKE, None) == NULL
     assert L.gdn_traffic_probe(7, 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(4, 4, 4, 64, 64, 9, FAKE, FAKE, None, FAKE, None) == NULL
+    assert L.gdn_traffic_probe(4, 40000, 4, 128, 128, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE  # over 2 GiB
     assert L.gdn_traffic_probe(0, 4, 4, 96, 64, 9, FAKE, FAKE, None, FAKE, None) == UNSUPPORTED
 
 

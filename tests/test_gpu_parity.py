@@ -478,3 +478,11 @@ def test_traffic_probe_moves_the_tiles(gdn, torch):
     t.cuda.synchronize()
     assert t.equal(before, dp.state)
     assert float(sink[0]) == 0.0
+    base = t.tensor([2, 6], dtype=t.int32, device="cuda")
+    gdn.traffic_probe(4, dp.state, base[0:1], base[1:2], sink, rows=3)   # slots 2..4 -> 6..8, contiguous
+    t.cuda.synchronize()
+    assert t.equal(dp.state[6:9], before[2:5])
+    assert t.equal(dp.state[:6], before[:6]) and t.equal(dp.state[9:], before[9:])
+    gdn.traffic_probe(4, dp.state, base[1:2], base[0:1], sink, rows=6)   # 6..11 runs past N = 11: no-op
+    t.cuda.synchronize()
+    assert t.equal(dp.state[:6], before[:6])
