@@ -62,19 +62,22 @@ def kernel_sources_sha256() -> str:
 
 
 def algorithmic_bytes(B_real: int, B_pad: int, T: int, H_v: int, d_k: int, d_v: int, C: int, W: int,
-                      twin: bool) -> int:
-    """Bytes one decode launch must move.  Per real row: the state tile read and
-    written (fp32), the conv window read and written (bf16), T tokens of x (bf16),
-    the read-out (bf16), g and beta (fp32) and the slot indices (two, and two
-    more written by a fused commit).  Per padding row: its slot indices and its
-    zero read-out.  Once per launch: the conv weights."""
-    state = 2 * H_v * d_k * d_v * 4
-    conv = 2 * (W - 1) * C * 2
+                      mode: str) -> int:
+    """Bytes one decode launch must move.  Per real row: the state tile read (fp32)
+    and written -- once (twin, in place) or once per kept token (tokens mode) --, the
+    conv window read and written likewise (bf16), T tokens of x (bf16), of read-out
+    (bf16) and of g and beta (fp32), and the slot indices (read and write slot, and
+    two more written by a fused commit; the read slot in place; the read slot and
+    T token slots in tokens mode).  Per padding row: its slot indices and its zero
+    read-out.  Once per launch: the conv weights."""
+    tile = H_v * d_k * d_v * 4
+    win = (W - 1) * C * 2
+    writes = T if mode == "tokens" else 1
     x = T * C * 2
     out = T * H_v * d_v * 2
     gates = 2 * T * H_v * 4
-    slots = 16 if twin else 4
-    per_real = state + conv + x + out + gates + slots
+    slots = {"twin": 16, "inplace": 4, "tokens": 4 + 4 * T}[mode]
+    per_real = (1 + writes) * (tile + win) + x + out + gates + slots
     per_pad = slots + out
     return B_real * per_real + B_pad * per_pad + C * W * 2
 
@@ -131,31 +134,69 @@ def _bf(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def cpu_baseline(seconds: float = 10.0) -> dict:
-    """The fp64 oracle, as it stands, on 8-row slices of the same workload until
-    about `seconds` of CPU time have passed (single thread)."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(seconds: float = 10.0, threads: int | None = None) -> dict:
+    """The fp64 oracle, as it stands, on the 64-row workload: first one host
+    thread over 8-row calls, then `threads` host threads (default: the host's
+    CPUs, at most 16), each calling the oracle on its own slice of the rows
+    (the oracle's ctypes calls release the GIL, so the slices run in
+    parallel).  Each leg runs for about `seconds` / 2 of wall time."""
+    import threading
+
     import gdn_inputs as gi
     import oracle
 
     case = gi.qwen08b(B=64)
     s, pool, step = case.shape, case.pools[0], case.steps[0][0]
     st, cs = pool.state.copy(), pool.conv_state.copy()
-    rows = 0
-    t0 = time.perf_counter()
-    i = 0
-    while time.perf_counter() - t0 < seconds:
-        sl = slice((8 * i) % 64, (8 * i) % 64 + 8)
+
+    def rows_call(lo, hi):
+        sl = slice(lo, hi)
         oracle.gdn_decode_step(np.ascontiguousarray(step.x[sl]), pool.conv_w, None, cs, st,
                                np.ascontiguousarray(step.g[sl]), np.ascontiguousarray(step.beta[sl]),
                                np.ascontiguousarray(pool.read_slot[sl]), np.ascontiguousarray(pool.write_slot[sl]),
                                H_k=s.H_k)
-        rows += 8
-        i += 1
-    dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} rows of the 64-row workload in 8-row calls (one decode step each), "
-                      f"fp64 C loops on one host thread, {dt:.1f} s",
-            "us_per_64_row_step": 64 / (rows / dt) * 1e6}
+
+    def leg(n_threads, budget):
+        per = 64 // n_threads
+        done = [0] * n_threads
+        t0 = time.perf_counter()
+
+        def work(k):
+            # each thread owns rows [k*per, (k+1)*per): disjoint slots, so the
+            # shared pool arrays are written at disjoint places
+            while time.perf_counter() - t0 < budget:
+                rows_call(k * per, (k + 1) * per)
+                done[k] += per
+
+        ths = [threading.Thread(target=work, args=(k,)) for k in range(n_threads)]
+        for th in ths:
+            th.start()
+        for th in ths:
+            th.join()
+        dt = time.perf_counter() - t0
+        return sum(done) / dt, sum(done), dt
+
+    n = threads or max(1, min(16, os.cpu_count() or 1))
+    while 64 % n:
+        n -= 1
+    one, rows1, dt1 = leg(1, seconds / 2)
+    many, rowsn, dtn = leg(n, seconds / 2)
+    return {"value": many, "unit": "rows/s", "cores": n, "kind": "oracle",
+            "sample": f"the 64-row workload's decode step, fp64 C loops: {rowsn} rows in {dtn:.1f} s on {n} host "
+                      f"threads ({64 // n} rows a call per thread); one thread: {rows1} rows in {dt1:.1f} s",
+            "single_thread_rows_per_s": one, "us_per_64_row_step": 64 / many * 1e6,
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 class Bench:
@@ -170,10 +211,12 @@ class Bench:
         torch.cuda.set_device(0)
         self.args = args
         self.twin = args.mode == "twin"
+        self.tokens_mode = args.mode == "tokens"
         self.fused = self.twin and args.commit == "fused"
         B = self.B = args.rows
+        T = self.T = args.tokens
         # the pool (257 slot pairs) and inputs for all 256 pair-rows
-        case = gi.qwen08b(B=256)
+        case = gi.qwen08b(B=256, T=T)
         s, pool, step = case.shape, case.pools[0], case.steps[0][0]
         self.shape = s
         self.state = torch.from_numpy(pool.state).cuda()
@@ -182,6 +225,13 @@ class Bench:
         if self.twin:
             nsets = 1 if args.hot else max(1, min(4, 256 // B))
             slot_rows = [(pool.read_slot[k * B:(k + 1) * B], pool.write_slot[k * B:(k + 1) * B]) for k in range(nsets)]
+        elif self.tokens_mode:
+            # each set: B read slots and B*T token slots, all distinct
+            per = B * (T + 1)
+            nsets = 1 if args.hot else max(1, min(8, 512 // per))
+            perm = np.random.Generator(np.random.PCG64(1)).permutation(512).astype(np.int32) + 1
+            slot_rows = [(perm[k * per:k * per + B], perm[k * per + B:(k + 1) * per].reshape(B, T))
+                         for k in range(nsets)]
         else:
             nsets = 1 if args.hot else max(1, min(8, 512 // B))
             perm = np.random.Generator(np.random.PCG64(1)).permutation(512).astype(np.int32) + 1
@@ -194,7 +244,7 @@ class Bench:
                       beta=torch.from_numpy(np.ascontiguousarray(step.beta[rows])).cuda(),
                       rd=torch.from_numpy(np.ascontiguousarray(rd)).cuda(),
                       wr=None if wr is None else torch.from_numpy(np.ascontiguousarray(wr)).cuda(),
-                      out=torch.empty((B, 1, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda"))
+                      out=torch.empty((B, T, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda"))
             # the second pair of slot arrays the fused commit alternates with
             st["pairs"] = [(st["rd"], st["wr"]), (torch.empty_like(st["rd"]), None if wr is None else
                                                   torch.empty_like(st["wr"]))]
@@ -203,7 +253,7 @@ class Bench:
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
         self.timer = HipTimer()
-        self.bytes = algorithmic_bytes(B, 0, 1, s.H_v, s.d_k, s.d_v, s.C, s.W, self.twin)
+        self.bytes = algorithmic_bytes(B, 0, T, s.H_v, s.d_k, s.d_v, s.C, s.W, args.mode)
         self.cycles_per_ms = None
 
     def launch(self, st):
@@ -213,6 +263,9 @@ class Bench:
             g.gdn_decode_step_commit(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
                                      rd, wr, nrd, nwr, st["out"], H_k=s.H_k)
             st["parity"] ^= 1
+        elif self.tokens_mode:
+            g.gdn_decode_step_tokens(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
+                                     st["rd"], st["wr"], st["out"], H_k=s.H_k)
         else:
             g.gdn_decode_step(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
                               st["rd"], st["wr"] if self.twin else None, st["out"], H_k=s.H_k)
@@ -348,7 +401,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", type=int, default=64)
-    ap.add_argument("--mode", choices=("twin", "inplace"), default="twin")
+    ap.add_argument("--mode", choices=("twin", "inplace", "tokens"), default="twin",
+                    help="twin-slot write, in-place write, or a kept state per token (speculative verify)")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens a row (in place and tokens mode)")
     ap.add_argument("--commit", choices=("fused", "separate"), default="fused")
     ap.add_argument("--hot", action="store_true", help="same rows every step (cache-warm)")
     ap.add_argument("--graph", action="store_true", help="time steps replayed from a captured HIP graph")
@@ -361,6 +416,10 @@ def main() -> int:
         print(f"bench.py: the decode step runs on one GPU (asked for --gpus {args.gpus}); it "
               "shards by rows or by heads with no exchange inside the step, and no multi-GPU path is built.",
               file=sys.stderr)
+        return 2
+
+    if args.tokens < 1 or (args.mode == "twin" and args.tokens != 1):
+        print("bench.py: --tokens must be >= 1, and twin-slot writes take one token a row", file=sys.stderr)
         return 2
 
     b = Bench(args)
@@ -383,7 +442,8 @@ def main() -> int:
     rows_per_s = b.B / (ms_per_step * 1e-3)
     twin = b.twin
     commit = ("folded into the step kernel (next slot pair written by the step)" if b.fused else
-              "separate slot_commit kernel" if twin else "none (in place)")
+              "separate slot_commit kernel" if twin else
+              "none (states kept per token)" if b.tokens_mode else "none (in place)")
     result = {
         "metric": METRIC,
         "value": rows_per_s,
@@ -400,12 +460,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"0.8B-like GDN layer decode step: {b.B} rows x 16+16 heads x 128x128 fp32 state, "
                                f"conv width 4 over 6144 channels, bf16 conv windows and activations, "
-                               f"257 slot pairs, {'twin-slot write' if twin else 'in-place write'}, commit "
+                               f"257 slot pairs, {b.T} token{'s' if b.T > 1 else ''} a row, "
+                               f"{ {'twin': 'twin-slot write', 'inplace': 'in-place write', 'tokens': 'state kept per token (speculative verify)'}[args.mode]}, commit "
                                f"{commit}, "
                                + ("same rows every step (cache-warm)" if args.hot else
                                   f"{b.nsets} disjoint row sets rotated (cold cache)")
                                + (", HIP graph replay" if graph is not None else ", stream launches"),
-                   "B": b.B, "T": 1, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": s.N,
+                   "B": b.B, "T": b.T, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": s.N,
                    "write": args.mode, "commit": "fused" if b.fused else ("separate" if twin else "none"),
                    "row_sets": b.nsets, "graph": graph is not None},
         "step_GBps": b.bytes / (ms_per_step * 1e-3) / 1e9,
@@ -426,7 +487,7 @@ def main() -> int:
                           "kernel_us_p50": float(np.percentile(kus, 50)),
                           "kernel_us_p90": float(np.percentile(kus, 90)),
                           "bytes_per_launch": b.bytes}
-    if not args.no_calib:
+    if not args.no_calib and not b.tokens_mode:
         result["calibration"] = b.calibration()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

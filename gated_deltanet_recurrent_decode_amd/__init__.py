@@ -13,12 +13,14 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit",
+__all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "conv_decode",
+           "slot_commit",
            "slot_reset", "slot_copy", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "conv_decode", "slot_commit", "gdn_slot_reset",
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "conv_decode", "slot_commit",
+           "gdn_slot_reset",
            "gdn_slot_copy", "gdn_status_string", "gdn_traffic_probe")
 
 GDN_OK = 0
@@ -58,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.gdn_decode_step_commit.restype = i32
     L.gdn_decode_step_commit.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, P, P, f32, f32, P]
+    L.gdn_decode_step_tokens.restype = i32
+    L.gdn_decode_step_tokens.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.conv_decode.restype = i32
     L.conv_decode.argtypes = [i32, i32, i32, i32, P, i64, P, P, P, P, P, P, i64, i32, P]
     L.slot_commit.restype = i32
@@ -182,6 +186,22 @@ def gdn_decode_step_commit(x, conv_w, conv_b, conv_state, state, g, beta, read_s
         ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
         _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(next_read_slot), _ptr(next_write_slot),
         _ptr(out), float(q_scale), float(l2_eps), _stream(stream)))
+
+
+def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, token_slots, out, *,
+                           H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """T tokens a row from the read slot, the state after token t kept in slot
+    token_slots[r][t] (0: not kept); the read slot is not written (see
+    ``gdn_decode_step_tokens`` in include/gdn.h).  token_slots is [B][T] int32."""
+    torch = _torch()
+    _contig(_dev(token_slots, "token_slots", torch.int32), "token_slots")
+    if token_slots.shape != x.shape[:2]:
+        raise ValueError("token_slots must be [B][T]")
+    d, xs = _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, None, out, H_k)
+    _check("gdn_decode_step_tokens", lib().gdn_decode_step_tokens(
+        ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+        _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(token_slots), _ptr(out), float(q_scale), float(l2_eps),
+        _stream(stream)))
 
 
 def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,

@@ -37,7 +37,8 @@ namespace {
 gdn_status step_impl(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const gdn_bf16 *conv_w,
                      const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
                      const int32_t *read_slot, const int32_t *write_slot, int32_t *next_read_slot,
-                     int32_t *next_write_slot, gdn_bf16 *out, float q_scale, float l2_eps, hipStream_t stream)
+                     int32_t *next_write_slot, const int32_t *token_slots, gdn_bf16 *out, float q_scale,
+                     float l2_eps, hipStream_t stream)
 {
     if (!dims)
         return GDN_ERR_NULL;
@@ -91,6 +92,7 @@ gdn_status step_impl(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stri
     p.C = (int)C;
     p.G = G;
     p.twin = write_slot ? 1 : 0;
+    p.token_slots = token_slots;
     return from_hip(p.twin ? gdn::launch_gdn_step_twin(p, d.d_k, d.d_v, stream)
                            : gdn::launch_gdn_step(p, d.d_k, d.d_v, stream));
 }
@@ -106,7 +108,19 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_ro
                            float q_scale, float l2_eps, hipStream_t stream)
 {
     return step_impl(dims, x, x_row_stride, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot,
-                     nullptr, nullptr, out, q_scale, l2_eps, stream);
+                     nullptr, nullptr, nullptr, out, q_scale, l2_eps, stream);
+}
+
+gdn_status gdn_decode_step_tokens(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                  const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                                  float *state, const float *g, const float *beta, const int32_t *read_slot,
+                                  const int32_t *token_slots, gdn_bf16 *out, float q_scale, float l2_eps,
+                                  hipStream_t stream)
+{
+    if (dims && dims->B != 0 && !token_slots)
+        return GDN_ERR_NULL;
+    return step_impl(dims, x, x_row_stride, conv_w, conv_b, conv_state, state, g, beta, read_slot, nullptr,
+                     nullptr, nullptr, token_slots, out, q_scale, l2_eps, stream);
 }
 
 gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
@@ -128,7 +142,7 @@ gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64
                     return GDN_ERR_SHAPE;
     }
     return step_impl(dims, x, x_row_stride, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot,
-                     next_read_slot, next_write_slot, out, q_scale, l2_eps, stream);
+                     next_read_slot, next_write_slot, nullptr, out, q_scale, l2_eps, stream);
 }
 
 gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,

@@ -64,7 +64,14 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     const int T = p.T;
 
     const int rs = p.read_slot[r];
-    const bool bad = rs < 0 || rs >= p.N;
+    bool bad = rs < 0 || rs >= p.N;
+    if (p.token_slots && rs != 0) {
+        // per-token states: every kept slot must be a usable slot other than the read slot
+        for (int t = 0; t < T; ++t) {
+            const int ts = p.token_slots[(size_t)r * T + t];
+            bad = bad || ts < 0 || ts >= p.N || ts == rs;
+        }
+    }
     if (rs == 0 || bad) {
         // padding row (or a row with an unusable slot): touch no slot; out gets
         // +0.0 for padding and NaN for the unusable slot.
@@ -146,15 +153,25 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     __builtin_amdgcn_sched_barrier(0);
 
     const bool has_bias = p.conv_b != nullptr;
+    uint2 xn[NCQ];     // the next token's x, loaded one token ahead
+    float g_n = 0.f, b_n = 0.f;
     for (int t = 0; t < T; ++t) {
         if (t > 0) {
             lds_barrier(); // the previous token's readers of y_lds / red_lds are done
 #pragma unroll
             for (int k = 0; k < NCQ; ++k)
-                if (conv_wave[k])
-                    xq[k] = *reinterpret_cast<const uint2 *>(xrow + (size_t)t * C + c[k]);
-            g_t = p.g[((size_t)r * T + t) * p.H_v + hv];
-            b_t = p.beta[((size_t)r * T + t) * p.H_v + hv];
+                xq[k] = xn[k];
+            g_t = g_n;
+            b_t = b_n;
+        }
+        if (t + 1 < T) {
+            // loads of token t+1's inputs go out now and land while token t computes
+#pragma unroll
+            for (int k = 0; k < NCQ; ++k)
+                xn[k] = conv_wave[k] ? *reinterpret_cast<const uint2 *>(xrow + (size_t)(t + 1) * C + c[k])
+                                     : make_uint2(0, 0);
+            g_n = p.g[((size_t)r * T + t + 1) * p.H_v + hv];
+            b_n = p.beta[((size_t)r * T + t + 1) * p.H_v + hv];
         }
 
         // ---- conv decode + SiLU of this workgroup's channels -> LDS; the
@@ -270,7 +287,32 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
                               (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16)};
             __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(p.out + (gi * DV + col0 + 4 * cg)));
         }
+        if (p.token_slots) {
+            // speculative verify: the state and window after this token go to
+            // the token's own slot (0: not kept); the read slot stays as it was
+            const int ts = p.token_slots[(size_t)r * T + t];
+            if (ts != 0) {
+                uint16_t *cs_tok = p.conv_state + (size_t)ts * 3 * C;
+#pragma unroll
+                for (int k = 0; k < NCQ; ++k) {
+                    if (own[k]) {
+                        uint16_t *dst = cs_tok + c[k];
+                        *reinterpret_cast<u32x2 *>(dst) = u32x2{wn0[k].x, wn0[k].y};
+                        *reinterpret_cast<u32x2 *>(dst + C) = u32x2{wn1[k].x, wn1[k].y};
+                        *reinterpret_cast<u32x2 *>(dst + 2 * C) = u32x2{wn2[k].x, wn2[k].y};
+                    }
+                }
+                const __amdgpu_buffer_rsrc_t tok_tile =
+                    tile_rsrc(p.state + ((size_t)ts * p.H_v + hv) * TILE, TILE * 4u);
+#pragma unroll
+                for (int m = 0; m < RPT; ++m)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), tok_tile, voff,
+                                                           m * RG * DV * 4, kStorePolicyTwin);
+            }
+        }
     }
+    if (p.token_slots)
+        return;
 
     // ---- advanced conv windows of the channels this workgroup owns: a shift
     // of bf16 values, stored as the bits they were read as
@@ -284,7 +326,7 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
         }
     }
 
-    // ---- new state -> write slot (the read slot in place)
+    // ---- new state -> the read slot
     const __amdgpu_buffer_rsrc_t wr_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u);
 #pragma unroll
     for (int m = 0; m < RPT; ++m)

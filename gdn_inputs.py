@@ -163,9 +163,9 @@ def tiny(seed: int = 0) -> Case:
     return make_case("tiny", SHAPE_TINY, steps=8, seed=seed)
 
 
-def qwen08b(seed: int = 0, B: int = 64, twin: bool = True, steps: int = 1) -> Case:
+def qwen08b(seed: int = 0, B: int = 64, twin: bool = True, steps: int = 1, T: int = 1) -> Case:
     """One 0.8B-like GDN layer: 16+16 heads of 128, 6144 conv channels, 257 slot pairs."""
-    s = Shape(B=B, T=1, H_k=16, H_v=16, d_k=128, d_v=128, W=4, N=513)
+    s = Shape(B=B, T=T, H_k=16, H_v=16, d_k=128, d_v=128, W=4, N=513)
     return make_case("0.8b" if B == 64 else f"sweep-B{B}", s, steps=steps, twin=twin, seed=seed)
 
 

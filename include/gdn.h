@@ -135,6 +135,33 @@ gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64
                                   gdn_bf16 *out, float q_scale, float l2_eps, hipStream_t stream);
 
 /*
+ * gdn_decode_step_tokens -- T tokens a row from the read slot, keeping the
+ * state after every token in a slot of its own, for speculative decoding's
+ * verify pass (PR #1139, "What changed": speculative decoding's slots already
+ * hold a state per token, which is why the pool refuses twin slots with it).
+ *
+ * For each row r with rs = read_slot[r]: the state S and conv window start
+ * from slot rs; tokens t = 0..T-1 run in order exactly as in
+ * gdn_decode_step; after token t, when ts = token_slots[r*T + t] is not 0,
+ * the state and the advanced window at that point are stored to slot ts
+ * (state[ts], conv_state[ts]).  out [B][T][H_v][d_v] gets every token's
+ * read-out.  Slot rs itself is never written, so rejecting draft tokens costs
+ * nothing: the caller keeps the slot of the last accepted token.
+ * A row with rs == 0 is padding (out +0.0, no slot touched).  A row whose
+ * read slot or any token slot lies outside [0, N), or has a token slot equal
+ * to its read slot, touches no slot and gets NaN in out.
+ * Layouts, sizes, alignment and errors as gdn_decode_step in place (write
+ * slot NULL, H_v/H_k in {1, 2, 4}); token_slots is [B][T] int32 on the
+ * device (NULL with B > 0: GDN_ERR_NULL).  Preconditions, not checked: the
+ * non-zero token slots are distinct and are not any row's read slot.
+ */
+gdn_status gdn_decode_step_tokens(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                  const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,
+                                  float *state, const float *g, const float *beta, const int32_t *read_slot,
+                                  const int32_t *token_slots, gdn_bf16 *out, float q_scale, float l2_eps,
+                                  hipStream_t stream);
+
+/*
  * conv_decode -- the pooled conv update for one token a row, standalone
  * (PR #1139, "What changed": causal_conv1d_decode, with null slots, strided
  * rows, optional bias and activation, and a write slot that leaves the read

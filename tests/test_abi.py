@@ -105,6 +105,22 @@ def test_step_commit_validation():
              1e-6, None) == OK
 
 
+def test_step_tokens_validation():
+    f = gdn.lib().gdn_decode_step_tokens
+
+    def call(d, tok=FAKE, x=FAKE):
+        C = 2 * d.H_k * d.d_k + d.H_v * d.d_v
+        return f(ctypes.byref(d), x, d.T * C, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, tok, FAKE, 1.0, 1e-6, None)
+    assert call(_dims(T=3), tok=None) == NULL
+    assert call(_dims(T=3), x=None) == NULL
+    assert call(_dims(T=0)) == SHAPE
+    assert call(_dims(T=3, H_k=1, H_v=8)) == UNSUPPORTED       # in-place kernel: H_v / H_k in {1, 2, 4}
+    assert call(_dims(T=3, d_k=96)) == UNSUPPORTED
+    empty = gdn.Dims(0, 3, 4, 4, 64, 64, 4, 9)
+    assert f(ctypes.byref(empty), None, 0, None, None, None, None, None, None, None, None, None, 1.0, 1e-6,
+             None) == OK
+
+
 def test_slot_ops_validation():
     L = gdn.lib()
     d = _dims()

@@ -177,11 +177,16 @@ def test_9b_24_layers_back_to_back_sampled_rows(gdn, torch):
 
 # ------------------------------------------------------------------ workload: padded bucket
 
-def test_padded_bucket_twin_real_rows_identical_to_unpadded(gdn, torch):
+@pytest.mark.parametrize("twin", [True, False], ids=["twin", "inplace"])
+def test_padded_bucket_real_rows_identical_to_unpadded(gdn, torch, twin):
+    """The 128-row bucket with 46 real rows first and 82 on the null slot.  In
+    place it is the mixed step's decode half (PR #965, "What changed": a run of
+    one-token rows, width sized to the bucket, padding on slot 0; PR #1139,
+    "What changed": that half updates in place)."""
     t = torch
-    case = gi.padded()
+    case = gi.padded(twin=twin)
     s, pool, step = case.shape, case.pools[0], case.steps[0][0]
-    dp, out = _check_step(gdn, case)
+    dp, out = _check_step(gdn, case, twin=twin)
     assert t.count_nonzero(out[gi.PADDED_REAL:].view(t.int16)) == 0, "padding rows must read out +0.0"
     assert t.count_nonzero(dp.state[0].view(t.int32)) == 0 and t.count_nonzero(dp.conv_state[0].view(t.int16)) == 0
     # the same 46 rows without the padding: bit-identical outputs and state
@@ -190,7 +195,7 @@ def test_padded_bucket_twin_real_rows_identical_to_unpadded(gdn, torch):
     dp2.rd, dp2.wr = dp2.rd[:n].contiguous(), dp2.wr[:n].contiguous()
     sub = gi.StepInputs(np.ascontiguousarray(step.x[:n]), np.ascontiguousarray(step.g[:n]),
                         np.ascontiguousarray(step.beta[:n]))
-    out2 = H.gpu_step(gdn, dp2, sub, s)
+    out2 = H.gpu_step(gdn, dp2, sub, s, twin=twin)
     t.cuda.synchronize()
     assert t.equal(out[:n].view(t.int16), out2.view(t.int16))
     wr = t.from_numpy(pool.write_slot[:n].astype(np.int64)).cuda()
@@ -212,6 +217,89 @@ def test_padded_bucket_in_place_four_tokens(gdn, torch):
         assert t.equal(o[:, 0].view(t.int16), out4[:, k].view(t.int16)), f"token {k}"
     assert t.equal(dp1.state.view(t.int32), dp.state.view(t.int32))
     assert t.equal(dp1.conv_state.view(t.int16), dp.conv_state.view(t.int16))
+
+
+# ------------------------------------------------------------------ a state per token (speculative verify)
+
+def _token_slots(pool, B, T, keep, rng_seed):
+    """Distinct slots, none a read slot, for the kept tokens (keep[r][t]); 0 elsewhere."""
+    used = set(int(x) for x in pool.read_slot)
+    free = [sl for sl in range(1, pool.state.shape[0]) if sl not in used]
+    rng = np.random.Generator(np.random.PCG64(rng_seed))
+    rng.shuffle(free)
+    tok = np.zeros((B, T), np.int32)
+    k = 0
+    for r in range(B):
+        for t in range(T):
+            if keep[r][t]:
+                tok[r, t] = free[k]
+                k += 1
+    return tok
+
+
+@pytest.mark.parametrize("B,T,hk,hv,d,real", [(5, 3, 2, 4, 128, 4), (6, 4, 2, 2, 64, None), (3, 2, 1, 4, 64, None)],
+                         ids=["B5-T3-G2-pad", "B6-T4-d64", "B3-T2-G4"])
+def test_per_token_states_match_oracle(gdn, torch, B, T, hk, hv, d, real):
+    t = torch
+    case = gi.small(B=B, T=T, H_k=hk, H_v=hv, d=d, N=1 + 2 * B + 2 * B * T, twin=False, real_rows=real, seed=B + T)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    keep = [[(r + tt) % 3 != 2 for tt in range(T)] for r in range(B)]   # some tokens not kept
+    tok = _token_slots(pool, B, T, keep, 7)
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    before_state, before_conv = dp.state.clone(), dp.conv_state.clone()
+    out = t.empty((B, T, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    gdn.gdn_decode_step_tokens(H.bf16_dev(step.x), dp.conv_w, None, dp.conv_state, dp.state,
+                               t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda(), dp.rd,
+                               t.from_numpy(tok).cuda(), out, H_k=s.H_k)
+    ref = oracle.gdn_decode_step_tokens(step.x, hp.conv_w, None, hp.conv_state, hp.state, step.g, step.beta, hp.rd,
+                                        tok, H_k=s.H_k)
+    t.cuda.synchronize()
+    H.assert_out_close(out, ref)
+    real_rows = pool.read_slot != 0
+    kept = sorted(int(x) for x in tok[real_rows].ravel() if x != 0)
+    idx = t.tensor(kept, dtype=t.int64, device="cuda")
+    H.assert_state_close(dp.state[idx].cpu().numpy(), hp.state[kept], "kept states")
+    np.testing.assert_array_equal(H.bf16_host(dp.conv_state[idx]), hp.conv_state[kept])
+    mask = t.ones(s.N, dtype=t.bool, device="cuda")
+    mask[idx] = False   # every other slot, the read slots included, is untouched
+    assert t.equal(dp.state[mask].view(t.int32), before_state[mask].view(t.int32))
+    assert t.equal(dp.conv_state[mask].view(t.int16), before_conv[mask].view(t.int16))
+    # the state kept after token k is, bit for bit, an in-place call over the first k+1 tokens
+    for k in range(T):
+        dpk = H.DevPool(pool)
+        sub = gi.StepInputs(np.ascontiguousarray(step.x[:, :k + 1]), np.ascontiguousarray(step.g[:, :k + 1]),
+                            np.ascontiguousarray(step.beta[:, :k + 1]))
+        ok = H.gpu_step(gdn, dpk, sub, s, twin=False)
+        t.cuda.synchronize()
+        assert t.equal(ok.view(t.int16), out[:, :k + 1].view(t.int16)), f"outputs through token {k}"
+        for r in range(B):
+            if real_rows[r] and tok[r, k]:
+                rs = int(pool.read_slot[r])
+                assert t.equal(dp.state[int(tok[r, k])].view(t.int32), dpk.state[rs].view(t.int32)), (r, k)
+                assert t.equal(dp.conv_state[int(tok[r, k])].view(t.int16), dpk.conv_state[rs].view(t.int16))
+
+
+def test_per_token_states_unusable_slot(gdn, torch):
+    """A token slot outside the pool, or equal to the row's read slot, makes the
+    row NaN and touches nothing; the other rows are unaffected."""
+    t = torch
+    B, T = 3, 2
+    case = gi.small(B=B, T=T, H_k=2, H_v=2, d=64, N=1 + 2 * B + 2 * B * T, twin=False, seed=3)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    tok = _token_slots(pool, B, T, [[True] * T] * B, 5)
+    tok[1, 1] = s.N            # outside the pool
+    tok[2, 0] = pool.read_slot[2]  # the row's own read slot
+    dp = H.DevPool(pool)
+    before = dp.state.clone()
+    out = t.empty((B, T, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    gdn.gdn_decode_step_tokens(H.bf16_dev(step.x), dp.conv_w, None, dp.conv_state, dp.state,
+                               t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda(), dp.rd,
+                               t.from_numpy(tok).cuda(), out, H_k=s.H_k)
+    t.cuda.synchronize()
+    assert bool(t.isnan(out[1:].float()).all()) and not bool(t.isnan(out[0].float()).any())
+    for r in (1, 2):
+        for sl in [int(x) for x in tok[r] if 0 < x < s.N]:
+            assert t.equal(dp.state[sl].view(t.int32), before[sl].view(t.int32))
 
 
 # ------------------------------------------------------------------ fused commit
