@@ -395,14 +395,99 @@ class Bench:
         return cal
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PREFILL_METRIC = "GDN chunked prefill tokens/s and achieved fp32 matrix TFLOP/s (% of peak)"
+
+
+def prefill_flops_per_token(H_v: int, d_k: int, d_v: int, chunk: int = 32) -> float:
+    """Matrix-core flops the chunked prefill executes per token: per chunk and value
+    head K S0 and Q S0 (2 * chunk * d_k * d_v each), K K^T and Q K^T (2 * chunk^2 * d_k
+    each), P U (2 * chunk^2 * d_v) and K^T U (2 * d_k * chunk * d_v)."""
+    per_chunk = 3 * 2 * chunk * d_k * d_v + 2 * 2 * chunk * chunk * d_k + 2 * chunk * chunk * d_v
+    return H_v * per_chunk / chunk
+
+
+def run_prefill(args) -> dict:
+    """Packed prompts of --prefill-len tokens, --rows of them per call, at the 0.8B-like
+    layer's shapes, in place; two sets of slots alternate.  Times the prefill kernel with
+    fence-free HIP events around every launch."""
+    import torch
+
+    import gated_deltanet_recurrent_decode_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.lib()
+    torch.cuda.set_device(0)
+    nseq, L = args.rows, args.prefill_len
+    case = gi.prefill([L] * (2 * nseq), H_k=16, H_v=16, d=128, N=513, seed=0)
+    s = case.shape
+    state = torch.from_numpy(case.pool.state).cuda()
+    conv_state = _bf(torch, case.pool.conv_state)
+    conv_w = _bf(torch, case.pool.conv_w)
+    sets = []
+    for k in range(2):
+        rows = slice(k * nseq * L, (k + 1) * nseq * L)
+        sets.append(dict(x=_bf(torch, case.x[rows]), g=torch.from_numpy(np.ascontiguousarray(case.g[rows])).cuda(),
+                         beta=torch.from_numpy(np.ascontiguousarray(case.beta[rows])).cuda(),
+                         cu=torch.arange(0, (nseq + 1) * L, L, dtype=torch.int32, device="cuda"),
+                         slot=torch.from_numpy(np.ascontiguousarray(case.pool.read_slot[k * nseq:(k + 1) * nseq])).cuda(),
+                         out=torch.empty((nseq * L, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda")))
+
+    def launch(i):
+        st = sets[i % 2]
+        gdn.gdn_prefill(st["x"], conv_w, None, conv_state, state, st["g"], st["beta"], st["cu"], st["slot"],
+                        st["out"], H_k=s.H_k)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    timer = HipTimer()
+    sh = torch.cuda.current_stream().cuda_stream
+    K = args.steps
+    evs = [(timer.event(), timer.event()) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        timer.record(evs[i][0], sh)
+        launch(i)
+        timer.record(evs[i][1], sh)
+    end.record()
+    torch.cuda.synchronize()
+    us = np.array([timer.elapsed_ms(a, b) for a, b in evs]) * 1e3
+    for a, b in evs:
+        timer.destroy(a)
+        timer.destroy(b)
+    ms_per_call = start.elapsed_time(end) / K
+    tokens = nseq * L
+    flops = prefill_flops_per_token(s.H_v, s.d_k, s.d_v) * tokens
+    k_us = float(us.mean())
+    achieved = flops / (k_us * 1e-6) / 1e12
+    hbm = tokens * (s.C * 2 + s.H_v * s.d_v * 2 + 2 * s.H_v * 4) + nseq * 2 * (s.H_v * s.d_k * s.d_v * 4 + 3 * s.C * 2)
+    return {
+        "metric": PREFILL_METRIC, "value": tokens / (k_us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_call, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"chunked prefill, {nseq} prompts of {L} tokens a call, 0.8B-like layer (16+16 heads "
+                               f"of 128, 6144 conv channels, fp32 state), in place, two slot sets alternating",
+                   "prompts": nseq, "prompt_len": L, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None, "kernel": "gdn_prefill_kernel",
+                     "kernel_us_mean": k_us, "kernel_us_p50": float(np.percentile(us, 50)),
+                     "flops_per_launch": flops, "hbm_bytes_per_launch": hbm,
+                     "hbm_GBps": hbm / (k_us * 1e-6) / 1e9},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", type=int, default=64)
-    ap.add_argument("--mode", choices=("twin", "inplace", "tokens"), default="twin",
-                    help="twin-slot write, in-place write, or a kept state per token (speculative verify)")
+    ap.add_argument("--mode", choices=("twin", "inplace", "tokens", "prefill"), default="twin",
+                    help="twin-slot write, in-place write, a kept state per token (speculative verify), or the "
+                         "chunked prefill of --rows prompts of --prefill-len tokens")
+    ap.add_argument("--prefill-len", type=int, default=512)
     ap.add_argument("--tokens", type=int, default=1, help="tokens a row (in place and tokens mode)")
     ap.add_argument("--commit", choices=("fused", "separate"), default="fused")
     ap.add_argument("--hot", action="store_true", help="same rows every step (cache-warm)")
@@ -418,6 +503,12 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.mode == "prefill":
+        if args.rows < 1 or args.prefill_len < 1 or 4 * args.rows > 512:
+            print("bench.py: prefill needs 1 <= --rows <= 128 and --prefill-len >= 1", file=sys.stderr)
+            return 2
+        print(json.dumps(run_prefill(args)), flush=True)
+        return 0
     if args.tokens < 1 or (args.mode == "twin" and args.tokens != 1):
         print("bench.py: --tokens must be >= 1, and twin-slot writes take one token a row", file=sys.stderr)
         return 2

@@ -13,13 +13,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "conv_decode",
+__all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill",
+           "conv_decode",
            "slot_commit",
            "slot_reset", "slot_copy", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "conv_decode", "slot_commit",
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill", "conv_decode",
+           "slot_commit",
            "gdn_slot_reset",
            "gdn_slot_copy", "gdn_status_string", "gdn_traffic_probe")
 
@@ -62,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_decode_step_commit.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.gdn_decode_step_tokens.restype = i32
     L.gdn_decode_step_tokens.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
+    L.gdn_prefill.restype = i32
+    L.gdn_prefill.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.conv_decode.restype = i32
     L.conv_decode.argtypes = [i32, i32, i32, i32, P, i64, P, P, P, P, P, P, i64, i32, P]
     L.slot_commit.restype = i32
@@ -202,6 +206,37 @@ def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_s
         ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
         _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(token_slots), _ptr(out), float(q_scale), float(l2_eps),
         _stream(stream)))
+
+
+def gdn_prefill(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, *, H_k: int,
+                q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """Chunked prefill of packed sequences, in place (see ``gdn_prefill`` in include/gdn.h).
+
+    x [T][C] bf16 (rows may be strided), g/beta [T][H_v] fp32, cu_seqlens [B+1] int32,
+    slot [B] int32, out [T][H_v][d_v] bf16; the pool tensors as for gdn_decode_step."""
+    torch = _torch()
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _dev(x, "x", bf)
+    for t, n, dt in ((conv_w, "conv_w", bf), (conv_state, "conv_state", bf), (state, "state", f32),
+                     (g, "g", f32), (beta, "beta", f32), (cu_seqlens, "cu_seqlens", i32), (slot, "slot", i32),
+                     (out, "out", bf)):
+        _contig(_dev(t, n, dt), n)
+    _contig(_dev(conv_b, "conv_b", bf, allow_none=True), "conv_b")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x: expected [T][C] with contiguous channels")
+    T, C = x.shape
+    N, H_v, d_k, d_v = state.shape
+    W = conv_w.shape[1]
+    B = slot.shape[0]
+    if cu_seqlens.shape != (B + 1,) or g.shape != (T, H_v) or beta.shape != (T, H_v) or out.shape != (T, H_v, d_v):
+        raise ValueError("cu_seqlens [B+1], g/beta [T][H_v], out [T][H_v][d_v] expected")
+    if conv_state.shape != (N, W - 1, C) or conv_w.shape[0] != C:
+        raise ValueError("conv_state / conv_w do not match x and state")
+    d = Dims(B, T, H_k, H_v, d_k, d_v, W, N)
+    xs = x.stride(0) if T > 0 else C
+    _check("gdn_prefill", lib().gdn_prefill(
+        ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+        _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _stream(stream)))
 
 
 def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,

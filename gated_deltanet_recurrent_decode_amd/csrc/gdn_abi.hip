@@ -145,6 +145,57 @@ gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64
                      next_read_slot, next_write_slot, nullptr, out, q_scale, l2_eps, stream);
 }
 
+gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const int32_t *cu_seqlens,
+                       const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state,
+                       const float *g, const float *beta, const int32_t *slot, gdn_bf16 *out, float q_scale,
+                       float l2_eps, hipStream_t stream)
+{
+    if (!dims)
+        return GDN_ERR_NULL;
+    const gdn_dims d = *dims;
+    if (d.B == 0) // no sequences; the arrays may be NULL
+        return GDN_OK;
+    if (!x || !cu_seqlens || !conv_w || !conv_state || !state || !g || !beta || !slot || !out)
+        return GDN_ERR_NULL;
+    if (d.B < 0 || d.T < 0 || d.H_k < 1 || d.H_v < 1 || d.N < 1 || d.H_v % d.H_k != 0)
+        return GDN_ERR_SHAPE;
+    if (!head_dim_ok(d.d_k) || !head_dim_ok(d.d_v) || d.W != 4)
+        return GDN_ERR_UNSUPPORTED;
+    const int64_t C = 2LL * d.H_k * d.d_k + (int64_t)d.H_v * d.d_v;
+    if (C > INT32_MAX || x_row_stride < C || (int64_t)d.B * d.H_k > INT32_MAX)
+        return GDN_ERR_SHAPE;
+    if (!(l2_eps >= 0.0f) || !isfinite(l2_eps) || !isfinite(q_scale))
+        return GDN_ERR_SHAPE;
+    // channel pairs are read and written 4 bytes at a time, the state 16
+    if (!aligned(x, 4) || x_row_stride % 2 != 0 || !aligned(conv_state, 4) || !aligned(state, 16) ||
+        !aligned(out, 2) || !aligned(conv_w, 2) || (conv_b && !aligned(conv_b, 2)))
+        return GDN_ERR_UNSUPPORTED;
+    if (d.T == 0) // every sequence is empty
+        return GDN_OK;
+    gdn::PrefillParams p{};
+    p.x = x;
+    p.x_row_stride = x_row_stride;
+    p.cu_seqlens = cu_seqlens;
+    p.conv_w = conv_w;
+    p.conv_b = conv_b;
+    p.conv_state = conv_state;
+    p.state = state;
+    p.g = g;
+    p.beta = beta;
+    p.slot = slot;
+    p.out = out;
+    p.q_scale = q_scale;
+    p.l2_eps = l2_eps;
+    p.B = d.B;
+    p.total = d.T;
+    p.H_k = d.H_k;
+    p.H_v = d.H_v;
+    p.G = d.H_v / d.H_k;
+    p.N = d.N;
+    p.C = (int)C;
+    return from_hip(gdn::launch_gdn_prefill(p, d.d_k, d.d_v, stream));
+}
+
 gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,
                        int64_t x_row_stride, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
                        gdn_bf16 *conv_state, const int32_t *read_slot, const int32_t *write_slot,

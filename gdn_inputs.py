@@ -188,3 +188,38 @@ def small(B: int, T: int, H_k: int, H_v: int, d: int, N: int | None = None, *, t
     n = N if N is not None else 2 * max(rr, 1) + 1
     s = Shape(B=B, T=T, H_k=H_k, H_v=H_v, d_k=d, d_v=dv, W=4, N=n)
     return make_case(f"small-B{B}-T{T}-{H_k}x{H_v}-d{d}", s, steps=steps, real_rows=rr, twin=twin, seed=seed)
+
+
+# ------------------------------------------------------------------ packed prompts (prefill)
+
+@dataclass
+class PrefillCase:
+    shape: Shape             # B = sequences, T = total tokens
+    pool: Pool               # read_slot holds each sequence's slot (0: padding)
+    x: np.ndarray            # [T][C] bf16 bits
+    g: np.ndarray            # [T][H_v] fp32
+    beta: np.ndarray         # [T][H_v] fp32
+    cu_seqlens: np.ndarray   # [B+1] int32
+
+
+def prefill(lengths, *, H_k: int, H_v: int, d: int, d_v: int | None = None, pad: tuple = (), seed: int = 0,
+            N: int | None = None) -> PrefillCase:
+    """Packed prompts of the given lengths (one slot each, a random permutation of
+    slot pairs' first slots); sequences whose index is in `pad` sit on slot 0.
+    Values drawn as for a decode step, per token."""
+    dv = d if d_v is None else d_v
+    B = len(lengths)
+    n = N if N is not None else 2 * B + 1
+    total = int(sum(lengths))
+    s = Shape(B=B, T=total, H_k=H_k, H_v=H_v, d_k=d, d_v=dv, W=4, N=n)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pool = draw_pool(rng, s, B)
+    for b in pad:
+        pool.read_slot[b] = 0
+        pool.write_slot[b] = 0
+    x = bf16_bits(rng.standard_normal((total, s.C), dtype=np.float32))
+    g = (-_softplus(rng.standard_normal((total, H_v)))).astype(np.float32)
+    beta = _sigmoid(rng.standard_normal((total, H_v))).astype(np.float32)
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return PrefillCase(s, pool, x, g, beta, cu)

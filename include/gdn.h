@@ -162,6 +162,36 @@ gdn_status gdn_decode_step_tokens(const gdn_dims *dims, const gdn_bf16 *x, int64
                                   hipStream_t stream);
 
 /*
+ * gdn_prefill -- chunked prefill of packed prompts, each updating its slot in
+ * place (PR #1139, "What changed": prefill keeps the state in place; PR #965
+ * names the chunked GDN path that the mixed step's prompt rows take).
+ *
+ * dims: B = sequences, T = total tokens in x, g, beta and out (the packed
+ * length); H_k, H_v, d_k, d_v, W, N as for gdn_decode_step.  Sequence b owns
+ * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of the packed arrays and slot
+ * s = slot[b].  The result is what gdn_decode_step in place computes over
+ * those tokens one after the other (conv decode + SiLU from the slot's
+ * window, L2 norms, the gated delta rule from the slot's state, a read-out per
+ * token), and the final state and window go back to slot s; the arithmetic is
+ * the chunked form of that recurrence in fp32 (32-token chunks, matrix-core
+ * products), so results match the token-by-token path within rounding, not
+ * bit for bit.  s == 0 is a padding sequence: its read-out is +0.0 and no slot
+ * is touched.  A sequence whose token range is not inside [0, T] or whose
+ * slot is outside [0, N) touches nothing (its read-out is left as it was).
+ *
+ * Layouts: x [T][C] bf16, rows x_row_stride elements apart (>= C, even);
+ * cu_seqlens [B+1] int32 and slot [B] int32 on the device; g, beta [T][H_v]
+ * fp32; out [T][H_v][d_v] bf16; conv_w, conv_b, conv_state, state as for
+ * gdn_decode_step.  Alignment (GDN_ERR_UNSUPPORTED otherwise): x and
+ * conv_state 4 bytes, state 16.  Preconditions, not checked: no two
+ * sequences share a slot; cu_seqlens is non-decreasing.
+ */
+gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const int32_t *cu_seqlens,
+                       const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state,
+                       const float *g, const float *beta, const int32_t *slot, gdn_bf16 *out, float q_scale,
+                       float l2_eps, hipStream_t stream);
+
+/*
  * conv_decode -- the pooled conv update for one token a row, standalone
  * (PR #1139, "What changed": causal_conv1d_decode, with null slots, strided
  * rows, optional bias and activation, and a write slot that leaves the read

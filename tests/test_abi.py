@@ -121,6 +121,31 @@ def test_step_tokens_validation():
              None) == OK
 
 
+def test_prefill_validation():
+    f = gdn.lib().gdn_prefill
+
+    def call(d, stride=None, x=FAKE, cu=FAKE, state=FAKE, cs=FAKE, eps=1e-6):
+        C = 2 * d.H_k * d.d_k + d.H_v * d.d_v
+        return f(ctypes.byref(d), x, C if stride is None else stride, cu, FAKE, None, cs, state, FAKE, FAKE, FAKE,
+                 FAKE, 1.0, eps, None)
+    assert f(None, FAKE, 0, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1e-6, None) == NULL
+    assert call(_dims(T=40), cu=None) == NULL
+    assert call(_dims(T=40), x=None) == NULL
+    assert call(_dims(T=-1)) == SHAPE
+    assert call(_dims(T=40, H_k=3, H_v=4)) == SHAPE
+    assert call(_dims(T=40), stride=10) == SHAPE
+    assert call(_dims(T=40), eps=-1.0) == SHAPE
+    assert call(_dims(T=40, d_k=96)) == UNSUPPORTED
+    assert call(_dims(T=40, W=3)) == UNSUPPORTED
+    assert call(_dims(T=40), state=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert call(_dims(T=40), cs=ctypes.c_void_p(0x10002)) == UNSUPPORTED
+    assert call(_dims(T=40), stride=2 * 4 * 64 + 4 * 64 + 1) == UNSUPPORTED
+    assert call(_dims(T=0)) == OK      # every sequence empty: nothing enqueued
+    empty = gdn.Dims(0, 0, 4, 4, 64, 64, 4, 9)
+    assert f(ctypes.byref(empty), None, 0, None, None, None, None, None, None, None, None, None, 1.0, 1e-6,
+             None) == OK
+
+
 def test_slot_ops_validation():
     L = gdn.lib()
     d = _dims()
