@@ -48,7 +48,7 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # kernel source the counters were taken on: reported as null otherwise.
 MEASURED_TRAFFIC = {"kernel_sources_sha256": "514c5dd48bcb5d87efd6a66585f3fbbbec9a852182e8d6ef28d1f0356654f255",
                     "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_273_349}
-KERNEL_SOURCES = ("gdn_step_twin.hip", "step_common.h", "device_common.h", "gdn_internal.h")
+KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 
 def kernel_sources_sha256() -> str:
@@ -573,7 +573,8 @@ def main() -> int:
     result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                           "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                           "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                          "kernel": "gdn_step_twin_kernel" if twin else "gdn_step_kernel", "kernel_us_mean": k_us,
+                          "kernel": ("gdn_step_tile_kernel" if (twin or (b.T == 1 and not b.tokens_mode)) else
+                                     "gdn_step_kernel"), "kernel_us_mean": k_us,
                           "kernel_us_p10": float(np.percentile(kus, 10)),
                           "kernel_us_p50": float(np.percentile(kus, 50)),
                           "kernel_us_p90": float(np.percentile(kus, 90)),

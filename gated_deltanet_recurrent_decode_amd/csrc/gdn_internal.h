@@ -84,7 +84,7 @@ struct PrefillParams {
 
 hipError_t launch_gdn_step(const StepParams &p, int d_k, int d_v, hipStream_t stream);
 hipError_t launch_gdn_prefill(const PrefillParams &p, int d_k, int d_v, hipStream_t stream);
-hipError_t launch_gdn_step_twin(const StepParams &p, int d_k, int d_v, hipStream_t stream);
+hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream);
 hipError_t launch_conv_decode(const ConvParams &p, hipStream_t stream);
 hipError_t launch_slot_commit(int32_t *read_slot, int32_t *write_slot, int B, hipStream_t stream);
 hipError_t launch_slot_ops(const SlotOpsParams &p, int n, hipStream_t stream);

@@ -21,8 +21,11 @@
 // The delta rule is Gated DeltaNet's (decay, predict with the decayed state,
 // correct, read out); the slot handling follows mstar PR #1139, "What
 // changed" (keep_in_place for prefill, split walks and the mixed step's decode
-// half) and "Tests" (padding on slot 0).  Twin-slot steps run in
-// gdn_step_twin.hip with the same thread layout and summation order.
+// half) and "Tests" (padding on slot 0).  Single-token steps that allow one
+// head tile per workgroup (every twin step, and in place with one value head
+// per key head) run in gdn_step_tile.hip instead, with the same thread layout
+// and summation order; this kernel takes token walks, per-token states and
+// in-place GQA.
 //
 // No MFMA: per state element the step does a handful of FMAs against 8 bytes
 // of HBM traffic, far under the fp32 ridge point, so the kernel is written for

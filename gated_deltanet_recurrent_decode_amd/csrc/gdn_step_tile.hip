@@ -1,18 +1,22 @@
-// gdn_step_twin.hip -- the twin-slot, single-token decode step for gfx950.
+// gdn_step_tile.hip -- the single-token decode step, one head tile per
+// workgroup, for gfx950: every twin-slot step, and in-place steps whose key
+// heads each have one value head.
 //
-// The same computation as the in-place step kernel (conv decode + SiLU, L2
-// norms, gated delta rule, read-out), with the same thread layout and the
-// same fixed summation order, so twin and in-place writes give identical
-// bits; it reads one slot of the request's pair and writes the other (mstar
-// PR #1139, "What changed").  One workgroup per head tile (row, value head,
-// column slice).  The code is straight-line: a padding row (read slot 0) or
-// a row with an unusable slot gets buffer resources of size 0, so its loads
-// return zeros without touching memory and its stores are dropped, and only
-// its read-out is written (zeros, or NaN for an unusable slot).  Without a
-// branch between the slot lookup and the loads, every load is issued after
-// a short chain of scalar waits, and each later wait covers exactly the loads
-// it needs (measured on MI355X: 0.5-1 us faster at 64 rows than the same
-// arithmetic with an early exit and pointer-based loads).
+// The same computation as the key-head-group kernel in gdn_step.hip (conv
+// decode + SiLU, L2 norms, gated delta rule, read-out), with the same thread
+// layout and the same fixed summation order, so both give identical bits.  A
+// twin step reads one slot of the request's pair and writes the other (mstar
+// PR #1139, "What changed"); in place it writes back to the slot it read,
+// which is only safe here when no other workgroup reads the tile's q/k conv
+// windows, i.e. with one value head per key head.  One workgroup per head
+// tile (row, value head, column slice).  The code is straight-line: a padding
+// row (read slot 0) or a row with an unusable slot gets buffer resources of
+// size 0, so its loads return zeros without touching memory and its stores are
+// dropped, and only its read-out is written (zeros, or NaN for an unusable
+// slot).  Without a branch between the slot lookup and the loads, every load is
+// issued after a short chain of scalar waits, and each later wait covers
+// exactly the loads it needs (measured on MI355X: 0.5-1 us faster at 64 rows
+// than the same arithmetic with an early exit and pointer-based loads).
 
 #include "gdn_internal.h"
 #include "step_common.h"
@@ -42,7 +46,7 @@ __device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // Everything one head tile carries from its loads to its stores.
 template <int DK, int DVS>
-struct TwinTile {
+struct TileState {
     using Cfg = StepCfg<DK, DVS, 1>;
     static constexpr int NCL = Cfg::NCH / 4;                  // conv lanes (channel quads)
     static constexpr int NCQ = (NCL + Cfg::NT - 1) / Cfg::NT; // quads per thread
@@ -60,7 +64,7 @@ struct TwinTile {
 // Tile index -> (row, value head, column slice), its slots and gates.  Tiles
 // are ordered row-major, then value head, then column slice.
 template <int DK, int DVS>
-__device__ __forceinline__ void twin_locate(TwinTile<DK, DVS> &t, int tile, const StepParams &p)
+__device__ __forceinline__ void tile_locate(TileState<DK, DVS> &t, int tile, const StepParams &p)
 {
     const int ntiles = p.B * p.H_v * p.n_slices;
     t.valid = tile < ntiles;
@@ -73,8 +77,8 @@ __device__ __forceinline__ void twin_locate(TwinTile<DK, DVS> &t, int tile, cons
     t.col0 = cs * DVS;
     t.own_qk = (t.hv % p.G == 0) && cs == 0; // the tile that writes back the key head's q/k windows
     t.rs = p.read_slot[t.r];
-    t.ws = p.write_slot[t.r];
-    const bool bad = t.rs < 0 || t.rs >= p.N || t.ws < 0 || t.ws >= p.N || t.ws == t.rs;
+    t.ws = p.twin ? p.write_slot[t.r] : t.rs;
+    const bool bad = t.rs < 0 || t.rs >= p.N || t.ws < 0 || t.ws >= p.N || (p.twin && t.ws == t.rs);
     t.real = t.valid && t.rs != 0 && !bad;
     t.fill = t.rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
     t.g = p.g[(size_t)t.r * p.H_v + t.hv];
@@ -85,9 +89,9 @@ __device__ __forceinline__ void twin_locate(TwinTile<DK, DVS> &t, int tile, cons
 // columns): each conv lane takes four consecutive channels -- 16-byte weight
 // loads, 8-byte window, x and bias loads, raw bf16 bits.
 template <int DK, int DV, int DVS>
-__device__ __forceinline__ void twin_issue_small(TwinTile<DK, DVS> &t, const StepParams &p)
+__device__ __forceinline__ void tile_issue_small(TileState<DK, DVS> &t, const StepParams &p)
 {
-    using TT = TwinTile<DK, DVS>;
+    using TT = TileState<DK, DVS>;
     constexpr int NT = TT::Cfg::NT;
     const int C = p.C;
     const uint32_t cbytes = (uint32_t)C * 2u;
@@ -123,9 +127,9 @@ __device__ __forceinline__ void twin_issue_small(TwinTile<DK, DVS> &t, const Ste
 // The tile's fp32 state slice -> registers (16-byte streaming loads; each wave
 // instruction covers whole 128-byte lines).
 template <int DK, int DV, int DVS>
-__device__ __forceinline__ void twin_issue_state(TwinTile<DK, DVS> &t, const StepParams &p, uint32_t voff)
+__device__ __forceinline__ void tile_issue_state(TileState<DK, DVS> &t, const StepParams &p, uint32_t voff)
 {
-    using Cfg = typename TwinTile<DK, DVS>::Cfg;
+    using Cfg = typename TileState<DK, DVS>::Cfg;
     constexpr uint32_t TILE = (uint32_t)DK * DV;
     const __amdgpu_buffer_rsrc_t rd =
         tile_rsrc(p.state + ((size_t)(t.real ? t.rs : 0) * p.H_v + t.hv) * TILE, t.real ? TILE * 4u : 0u);
@@ -139,11 +143,11 @@ __device__ __forceinline__ void twin_issue_state(TwinTile<DK, DVS> &t, const Ste
 // Conv + SiLU -> LDS, L2 norms, projections, the fixed-order reduction, the
 // delta update, the read-out, and the stores of o, the advanced conv windows
 // and the new state.
-template <int DK, int DV, int DVS>
-__device__ __forceinline__ void twin_process(TwinTile<DK, DVS> &t, const StepParams &p, int cg, int rg, int wv,
+template <int DK, int DV, int DVS, bool INPLACE>
+__device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepParams &p, int cg, int rg, int wv,
                                              int lane, uint32_t voff, float *y_lds, float4 (*red_lds)[2][DVS / 4])
 {
-    using TT = TwinTile<DK, DVS>;
+    using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
     constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH, NCH = Cfg::NCH;
     constexpr int NCW = (TT::NCL + 63) / 64; // waves' worth of conv lanes
@@ -286,14 +290,14 @@ __device__ __forceinline__ void twin_process(TwinTile<DK, DVS> &t, const StepPar
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t.s[m]), wr, vo, m * RG * DV * 4,
-                                               kStorePolicyTwin);
+                                               INPLACE ? kStorePolicyInPlace : kStorePolicyTwin);
 }
 
-template <int DK, int DV, int DVS>
+template <int DK, int DV, int DVS, bool INPLACE>
 __global__ __launch_bounds__(2 * DVS) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
-void gdn_step_twin_kernel(StepParams p)
+void gdn_step_tile_kernel(StepParams p)
 {
-    using TT = TwinTile<DK, DVS>;
+    using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
     constexpr int CG = Cfg::CG, NWH = Cfg::NWH, NCH = Cfg::NCH;
     static_assert(Cfg::NT == 2 * DVS, "launch bound must match the layout");
@@ -309,13 +313,13 @@ void gdn_step_twin_kernel(StepParams p)
     const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
 
     TT t;
-    twin_locate(t, blockIdx.x, p);
-    twin_issue_small<DK, DV, DVS>(t, p);
+    tile_locate(t, blockIdx.x, p);
+    tile_issue_small<DK, DV, DVS>(t, p);
     __builtin_amdgcn_sched_barrier(0); // the small loads stay ahead of the tile loads
-    twin_issue_state<DK, DV, DVS>(t, p, voff);
+    tile_issue_state<DK, DV, DVS>(t, p, voff);
     // every load is in flight; keep the scheduler from sinking any below the first wait
     __builtin_amdgcn_sched_barrier(0);
-    twin_process<DK, DV, DVS>(t, p, cg, rg, wv, lane, voff, y_lds, red_lds);
+    tile_process<DK, DV, DVS, INPLACE>(t, p, cg, rg, wv, lane, voff, y_lds, red_lds);
 
     // fused commit: the workgroup of a row's first tile writes the swapped
     // pair into the next step's slot arrays (distinct from the ones this step
@@ -327,7 +331,7 @@ void gdn_step_twin_kernel(StepParams p)
 }
 
 template <int DK, int DV, int DVS>
-static hipError_t launch_twin(const StepParams &p, hipStream_t stream)
+static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
 {
     StepParams q = p;
     q.n_slices = DV / DVS;
@@ -335,30 +339,31 @@ static hipError_t launch_twin(const StepParams &p, hipStream_t stream)
     if (tiles <= 0)
         return hipSuccess;
     void *args[] = {&q};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_step_twin_kernel<DK, DV, DVS>), dim3((unsigned)tiles),
-                           dim3(2 * DVS), args, 0, stream);
+    const void *k = p.twin ? reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, false>)
+                           : reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, true>);
+    return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(2 * DVS), args, 0, stream);
 }
 
 // Column slices per head: split d_v only when the rows give very few
 // workgroups (with the state cold in HBM, whole tiles win from 16 rows of 16
 // heads up; slices stay >= 32 columns).
 template <int DK, int DV>
-static hipError_t dispatch_twin(const StepParams &p, hipStream_t stream)
+static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
 {
     const long long heads = (long long)p.B * p.H_v;
     if (heads >= 128)
-        return launch_twin<DK, DV, DV>(p, stream);
+        return launch_tile<DK, DV, DV>(p, stream);
     if (heads >= 32 || DV < 128)
-        return launch_twin<DK, DV, DV / 2>(p, stream);
-    return launch_twin<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>(p, stream);
+        return launch_tile<DK, DV, DV / 2>(p, stream);
+    return launch_tile<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>(p, stream);
 }
 
-hipError_t launch_gdn_step_twin(const StepParams &p, int d_k, int d_v, hipStream_t stream)
+hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream)
 {
-    if (d_k == 128 && d_v == 128) return dispatch_twin<128, 128>(p, stream);
-    if (d_k == 64 && d_v == 64) return dispatch_twin<64, 64>(p, stream);
-    if (d_k == 128 && d_v == 64) return dispatch_twin<128, 64>(p, stream);
-    if (d_k == 64 && d_v == 128) return dispatch_twin<64, 128>(p, stream);
+    if (d_k == 128 && d_v == 128) return dispatch_tile<128, 128>(p, stream);
+    if (d_k == 64 && d_v == 64) return dispatch_tile<64, 64>(p, stream);
+    if (d_k == 128 && d_v == 64) return dispatch_tile<128, 64>(p, stream);
+    if (d_k == 64 && d_v == 128) return dispatch_tile<64, 128>(p, stream);
     return hipErrorInvalidValue;
 }
 
