@@ -46,8 +46,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "514c5dd48bcb5d87efd6a66585f3fbbbec9a852182e8d6ef28d1f0356654f255",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_273_349}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "5d37fdfbdae49c34ad552cd74bb50c3525e1456b5ad925e067ce2c98d4aa388e",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_270_918}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 

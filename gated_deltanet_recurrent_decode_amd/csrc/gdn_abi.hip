@@ -8,6 +8,7 @@
 
 #include "gdn.h"
 #include "gdn_internal.h"
+#include "prefill_internal.h"
 
 namespace {
 

@@ -31,6 +31,7 @@
 // conv's SiLU uses the hardware exp and reciprocal (about an ulp each).
 
 #include "gdn_internal.h"
+#include "prefill_internal.h"
 #include "step_common.h"
 
 namespace gdn {
