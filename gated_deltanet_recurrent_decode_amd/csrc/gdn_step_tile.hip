@@ -346,12 +346,15 @@ static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
 
 // Column slices per head: split d_v only when the rows give very few
 // workgroups (with the state cold in HBM, whole tiles win from 16 rows of 16
-// heads up; slices stay >= 32 columns).
+// heads up; slices stay >= 32 columns).  Never in place: every slice reads the
+// head's q/k conv windows and one of them writes them back, so in place a
+// slice that starts late could read an advanced window; with whole tiles and
+// one value head per key head, no other workgroup reads them.
 template <int DK, int DV>
 static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
 {
     const long long heads = (long long)p.B * p.H_v;
-    if (heads >= 128)
+    if (heads >= 128 || !p.twin)
         return launch_tile<DK, DV, DV>(p, stream);
     if (heads >= 32 || DV < 128)
         return launch_tile<DK, DV, DV / 2>(p, stream);
