@@ -1,22 +1,26 @@
 """Benchmark of the pooled GDN decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows B] [--mode twin|inplace]
-                    [--commit fused|separate] [--hot] [--graph] [--no-cpu] [--no-calib]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows B]
+                    [--mode twin|inplace|tokens|prefill|stack] [--tokens T] [--prefill-len L]
+                    [--layers L] [--commit fused|separate] [--hot] [--graph] [--no-cpu] [--no-calib]
 
 Workload: one 0.8B-like GDN layer -- B = 64 rows, 16 key and 16 value heads,
 d_k = d_v = 128 fp32 state (1 MiB a row), conv width 4 over 6144 channels with
-bf16 conv windows and activations, a pool of 257 slot pairs (N = 513),
-twin-slot writes.  A step is the whole path: conv + SiLU, L2 norm, gates,
-delta rule, read-out, the twin write, and the slot commit.  With --commit fused
+bf16 conv windows and activations, twin-slot writes.  A step is the whole path:
+conv + SiLU, L2 norm, gates, delta rule, read-out, the twin write, and the slot
+commit.  With --commit fused
 (default) the commit is folded into the step kernel, which writes the swapped
 slot pair into a second pair of slot arrays (the two pairs alternate); with
 --commit separate it is its own kernel after the step.  Inputs are synthetic,
 seeded, and resident in HBM before the timed region.
 
-Cold cache: MI355X's 256 MB Infinity Cache could hold one 64-row working set
-(128 MiB), so consecutive steps rotate over disjoint row sets: four 64-row sets
-over all 256 slot pairs for twin writes (512 MiB touched), eight over 512 slots
-in place.  --hot runs the same rows every step (reported as such).
+Cold cache: MI355X's 256 MB Infinity Cache takes in the lines a step writes
+(streamed reads do not allocate there), so a slot read back within ~256 MB of
+writes comes partly from that cache.  Consecutive steps rotate over enough
+disjoint row sets that at least 768 MiB of state is written between two visits
+of a set: 13 sets of 64 rows for twin writes, over a pool of 2049 slots (the
+drawn 513-slot pool, its 512 non-null slots replicated four times on the
+device).  --hot runs the same rows every step (reported as such).
 
 Timing: each timed loop is queued behind a GPU sleep long enough for the host
 to enqueue the whole loop, so the GPU runs the steps back to back and the
@@ -46,8 +50,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "5d37fdfbdae49c34ad552cd74bb50c3525e1456b5ad925e067ce2c98d4aa388e",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_270_918}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "eab1c379515bed3c072c803611e1092c6abeb1b9d8f5f051a9d455218e1a412f",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_280_982}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 
@@ -80,6 +84,27 @@ def algorithmic_bytes(B_real: int, B_pad: int, T: int, H_v: int, d_k: int, d_v: 
     per_real = (1 + writes) * (tile + win) + x + out + gates + slots
     per_pad = slots + out
     return B_real * per_real + B_pad * per_pad + C * W * 2
+
+
+DRAWN_SLOTS = 512          # non-null slots of the drawn pool: 256 slot pairs
+COLD_BYTES = 768 << 20     # state written between two visits of a row set
+
+
+def row_sets(mode: str, B: int, T: int, slot_bytes: int, hot: bool) -> tuple[int, int]:
+    """(row sets rotated, slots one set takes).  MI355X's 256 MB Infinity Cache
+    takes in the lines a step writes (streamed reads do not allocate there), so
+    a slot written and read back within ~256 MB of other writes is read partly
+    from that cache.  Enough disjoint sets rotate that at least COLD_BYTES of
+    state is written between two visits of one set: a twin set's write slots
+    are its read slots the next time round, in place the same slots, in tokens
+    mode the token slots."""
+    per = {"twin": 2 * B, "inplace": B, "tokens": B * (T + 1)}[mode]
+    if per > DRAWN_SLOTS:
+        raise ValueError(f"a row set takes {per} slots; at most {DRAWN_SLOTS}")
+    if hot:
+        return 1, per
+    written = B * slot_bytes * (T if mode == "tokens" else 1)
+    return max(4, 1 + -(-COLD_BYTES // written)), per
 
 
 class HipTimer:
@@ -215,27 +240,36 @@ class Bench:
         self.fused = self.twin and args.commit == "fused"
         B = self.B = args.rows
         T = self.T = args.tokens
-        # the pool (257 slot pairs) and inputs for all 256 pair-rows
+        # the drawn pool (the null slot and 256 slot pairs) and inputs for 256 rows
         case = gi.qwen08b(B=256, T=T)
         s, pool, step = case.shape, case.pools[0], case.steps[0][0]
         self.shape = s
-        self.state = torch.from_numpy(pool.state).cuda()
-        self.conv_state = _bf(torch, pool.conv_state)
+        nsets, per = row_sets(args.mode, B, T, s.H_v * s.d_k * s.d_v * 4, args.hot)
+        spc = DRAWN_SLOTS // per                  # disjoint row sets one copy of the drawn pool holds
+        copies = -(-nsets // spc)
+        self.N = 1 + DRAWN_SLOTS * copies
+        # the drawn pool's 512 slots replicated `copies` times on the device after the null slot
+        state0 = torch.from_numpy(pool.state).cuda()
+        cs0 = _bf(torch, pool.conv_state)
+        self.state = torch.empty((self.N,) + tuple(state0.shape[1:]), dtype=state0.dtype, device="cuda")
+        self.conv_state = torch.empty((self.N,) + tuple(cs0.shape[1:]), dtype=cs0.dtype, device="cuda")
+        self.state[0], self.conv_state[0] = state0[0], cs0[0]
+        for c in range(copies):
+            self.state[1 + DRAWN_SLOTS * c:1 + DRAWN_SLOTS * (c + 1)] = state0[1:]
+            self.conv_state[1 + DRAWN_SLOTS * c:1 + DRAWN_SLOTS * (c + 1)] = cs0[1:]
+        del state0, cs0
         self.conv_w = _bf(torch, pool.conv_w)
-        if self.twin:
-            nsets = 1 if args.hot else max(1, min(4, 256 // B))
-            slot_rows = [(pool.read_slot[k * B:(k + 1) * B], pool.write_slot[k * B:(k + 1) * B]) for k in range(nsets)]
-        elif self.tokens_mode:
-            # each set: B read slots and B*T token slots, all distinct
-            per = B * (T + 1)
-            nsets = 1 if args.hot else max(1, min(8, 512 // per))
-            perm = np.random.Generator(np.random.PCG64(1)).permutation(512).astype(np.int32) + 1
-            slot_rows = [(perm[k * per:k * per + B], perm[k * per + B:(k + 1) * per].reshape(B, T))
-                         for k in range(nsets)]
-        else:
-            nsets = 1 if args.hot else max(1, min(8, 512 // B))
-            perm = np.random.Generator(np.random.PCG64(1)).permutation(512).astype(np.int32) + 1
-            slot_rows = [(perm[k * B:(k + 1) * B], None) for k in range(nsets)]
+        perm = np.random.Generator(np.random.PCG64(1)).permutation(DRAWN_SLOTS).astype(np.int32) + 1
+        slot_rows = []
+        for k in range(nsets):
+            j, off = k % spc, DRAWN_SLOTS * (k // spc)
+            if self.twin:
+                slot_rows.append((pool.read_slot[j * B:(j + 1) * B] + off, pool.write_slot[j * B:(j + 1) * B] + off))
+            elif self.tokens_mode:
+                # B read slots and B*T token slots, all distinct
+                slot_rows.append((perm[j * per:j * per + B] + off, (perm[j * per + B:(j + 1) * per] + off).reshape(B, T)))
+            else:
+                slot_rows.append((perm[j * B:(j + 1) * B] + off, None))
         self.nsets = nsets
         self.sets = []
         for k, (rd, wr) in enumerate(slot_rows):
@@ -395,6 +429,86 @@ class Bench:
         return cal
 
 
+STACK_METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak), 24-layer 9B-like stack"
+
+
+def run_stack(args) -> dict:
+    """The 9B-like decode: B rows, 16 key heads shared by 32 value heads (d = 128),
+    8192 conv channels, one pool of 1 + 2B slots per layer, --layers layers stepped
+    back to back (twin slots, fused commit) -- one step is every layer's launch.
+    Layers share one drawn pool (copied per layer) and one set of inputs; the
+    layer pools together (6.3 GB at 24 layers) keep every layer's state cold."""
+    import torch
+
+    import gated_deltanet_recurrent_decode_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.lib()
+    torch.cuda.set_device(0)
+    B, layers = args.rows, args.layers
+    shape = gi.Shape(B=B, T=1, H_k=16, H_v=32, d_k=128, d_v=128, W=4, N=1 + 2 * B)
+    case = gi.make_case("9b-bench", shape, seed=0)
+    pool, step = case.pools[0], case.steps[0][0]
+    s = case.shape
+    state0 = torch.from_numpy(pool.state).cuda()
+    cs0 = _bf(torch, pool.conv_state)
+    L = []
+    for _ in range(layers):
+        rd = torch.from_numpy(pool.read_slot.copy()).cuda()
+        wr = torch.from_numpy(pool.write_slot.copy()).cuda()
+        L.append(dict(state=state0.clone(), cs=cs0.clone(), pairs=[(rd, wr), (torch.empty_like(rd), torch.empty_like(wr))],
+                      parity=0))
+    del state0, cs0
+    conv_w = _bf(torch, pool.conv_w)
+    x, g, beta = _bf(torch, step.x), torch.from_numpy(step.g).cuda(), torch.from_numpy(step.beta).cuda()
+    out = torch.empty((B, 1, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+
+    def one_step():
+        for lay in L:
+            (rd, wr), (nrd, nwr) = lay["pairs"][lay["parity"]], lay["pairs"][1 - lay["parity"]]
+            gdn.gdn_decode_step_commit(x, conv_w, None, lay["cs"], lay["state"], g, beta, rd, wr, nrd, nwr, out,
+                                       H_k=s.H_k)
+            lay["parity"] ^= 1
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    K = args.steps
+    # queue the timed loop behind a GPU spin long enough for the host to enqueue
+    # all of it (the launches are issued from Python), so the layers run back to
+    # back and host launch cost never shows as GPU idle time
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(2_000_000)
+    c1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 2_000_000 / max(c0.elapsed_time(c1), 1e-3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int((5.0 + K * layers * 0.04) * cycles_per_ms))
+    a.record()
+    for _ in range(K):
+        one_step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    per_layer = algorithmic_bytes(B, 0, 1, s.H_v, s.d_k, s.d_v, s.C, s.W, "twin")
+    total = per_layer * layers
+    achieved = total / (ms * 1e-3) / 1e9
+    return {
+        "metric": STACK_METRIC, "value": B / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"9B-like GDN decode: {B} rows x 16 key / 32 value heads x 128x128 fp32 state, conv "
+                               f"width 4 over 8192 channels, {layers} layers back to back on separate {s.N}-slot "
+                               f"pools, twin-slot write with the commit folded in, stream launches",
+                   "B": B, "layers": layers, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "N": s.N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": "gdn_step_tile_kernel",
+                     "note": "whole-step time: every layer's launch queued back to back on one stream",
+                     "bytes_per_step": total, "us_per_layer": ms * 1e3 / layers},
+    }
+
+
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PREFILL_METRIC = "GDN chunked prefill tokens/s and achieved fp32 matrix TFLOP/s (% of peak)"
 
@@ -484,9 +598,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", type=int, default=64)
-    ap.add_argument("--mode", choices=("twin", "inplace", "tokens", "prefill"), default="twin",
+    ap.add_argument("--mode", choices=("twin", "inplace", "tokens", "prefill", "stack"), default="twin",
                     help="twin-slot write, in-place write, a kept state per token (speculative verify), or the "
-                         "chunked prefill of --rows prompts of --prefill-len tokens")
+                         "chunked prefill of --rows prompts of --prefill-len tokens, or the 9B-like stack of "
+                         "--layers layers (twin)")
+    ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--prefill-len", type=int, default=512)
     ap.add_argument("--tokens", type=int, default=1, help="tokens a row (in place and tokens mode)")
     ap.add_argument("--commit", choices=("fused", "separate"), default="fused")
@@ -503,6 +619,12 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.mode == "stack":
+        if args.rows < 1 or args.layers < 1:
+            print("bench.py: the stack needs --rows >= 1 and --layers >= 1", file=sys.stderr)
+            return 2
+        print(json.dumps(run_stack(args)), flush=True)
+        return 0
     if args.mode == "prefill":
         if args.rows < 1 or args.prefill_len < 1 or 4 * args.rows > 512:
             print("bench.py: prefill needs 1 <= --rows <= 128 and --prefill-len >= 1", file=sys.stderr)
@@ -513,7 +635,11 @@ def main() -> int:
         print("bench.py: --tokens must be >= 1, and twin-slot writes take one token a row", file=sys.stderr)
         return 2
 
-    b = Bench(args)
+    try:
+        b = Bench(args)
+    except ValueError as e:
+        print(f"bench.py: {e}", file=sys.stderr)
+        return 2
     s = b.shape
     for i in range(args.warmup):
         b.step(i)
@@ -551,13 +677,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"0.8B-like GDN layer decode step: {b.B} rows x 16+16 heads x 128x128 fp32 state, "
                                f"conv width 4 over 6144 channels, bf16 conv windows and activations, "
-                               f"257 slot pairs, {b.T} token{'s' if b.T > 1 else ''} a row, "
+                               f"{b.N}-slot pool, {b.T} token{'s' if b.T > 1 else ''} a row, "
                                f"{ {'twin': 'twin-slot write', 'inplace': 'in-place write', 'tokens': 'state kept per token (speculative verify)'}[args.mode]}, commit "
                                f"{commit}, "
                                + ("same rows every step (cache-warm)" if args.hot else
                                   f"{b.nsets} disjoint row sets rotated (cold cache)")
                                + (", HIP graph replay" if graph is not None else ", stream launches"),
-                   "B": b.B, "T": b.T, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": s.N,
+                   "B": b.B, "T": b.T, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": b.N,
                    "write": args.mode, "commit": "fused" if b.fused else ("separate" if twin else "none"),
                    "row_sets": b.nsets, "graph": graph is not None},
         "step_GBps": b.bytes / (ms_per_step * 1e-3) / 1e9,

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
 #pragma unroll
                 for (int m = 0; m < RPT; ++m)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), tok_tile, voff,
-                                                           m * RG * DV * 4, kStorePolicyTwin);
+                                                           m * RG * DV * 4, kStorePolicy);
             }
         }
     }
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), wr_tile, voff, m * RG * DV * 4,
-                                               kStorePolicyInPlace);
+                                               kStorePolicy);
 }
 
 template <int DK, int DV, int HPW>

@@ -290,7 +290,7 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t.s[m]), wr, vo, m * RG * DV * 4,
-                                               INPLACE ? kStorePolicyInPlace : kStorePolicyTwin);
+                                               kStorePolicy);
 }
 
 template <int DK, int DV, int DVS, bool INPLACE>

@@ -61,16 +61,15 @@ __device__ __forceinline__ float conv_tap4(uint32_t w01, uint32_t w23, uint32_t 
 // A state tile is read once and written once per step and is not touched
 // again until the next step of the layer, long after the caches have turned
 // over.  Loads stream (nt): measured on MI355X, streaming reads run at ~7.1
-// TB/s against ~6.3 for plain ones and leave the Infinity Cache to the small
-// per-row inputs.  Twin-slot stores go out system-scope (sc0 sc1: written
-// through to memory rather than held dirty in L2): with the read and write
-// streams mixed, that beats both plain and streaming stores at every batch
-// from 16 rows up (64 rows: 26.7 us against 28.4 with nt stores, cold slots).
-// In place the store hits the lines just read, and streaming stores measured
-// faster there.
+// TB/s against ~6.3 for plain ones.  Stores stream too, twin or in place.
+// Measured with at least 768 MiB of state written between two visits of a
+// slot (so nothing is left of it in the 256 MB Infinity Cache, which takes in
+// written lines but not streamed reads): 64 rows 28.3 us with streaming
+// stores against 30.5 written through (sc0 sc1) and 30.7 plain; 128 rows 54.2
+// against 58.3 and 59.2.  Written-through stores only look faster when the
+// next read of the slot comes soon enough to hit the Infinity Cache.
 constexpr int kLoadPolicy = 2;
-constexpr int kStorePolicyTwin = 17;
-constexpr int kStorePolicyInPlace = 2;
+constexpr int kStorePolicy = 2;
 // Four waves per SIMD for the twin single-token kernel: a 64-row step (1024
 // head tiles of 256 threads) is then resident on the 256 compute units all at
 // once.  The in-place kernel carries all G value heads of a key head and T

@@ -16,11 +16,9 @@ namespace gdn {
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-// Cache-policy bits as the step uses them: streaming loads; write-through
-// (sc0 sc1) stores for a twin write, streaming stores in place.
+// Cache-policy bits as the step uses them: streaming loads and stores.
 constexpr int kProbeLoad = 2;
-constexpr int kProbeStoreTwin = 17;
-constexpr int kProbeStoreInPlace = 2;
+constexpr int kProbeStore = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(float *base, uint32_t bytes)
 {
@@ -65,12 +63,8 @@ __global__ __launch_bounds__(NTH) void traffic_probe_kernel(ProbeParams p)
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const float4 v = make_float4(s[m].x * p.one, s[m].y * p.one, s[m].z * p.one, s[m].w * p.one);
-        if (p.mode == 3)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wr, voff, m * RG * DV * 4,
-                                                   kProbeStoreInPlace);
-        else
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wr, voff, m * RG * DV * 4,
-                                                   kProbeStoreTwin);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wr, voff, m * RG * DV * 4,
+                                               kProbeStore);
     }
 }
 
@@ -98,7 +92,7 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(ProbeParams p, uint32_
         for (int u = 0; u < 4; ++u) {
             const float4 w = make_float4(v[u].x * p.one, v[u].y * p.one, v[u].z * p.one, v[u].w * p.one);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), D, (i + 256u * u) * 16u, 0,
-                                                   kProbeStoreTwin);
+                                                   kProbeStore);
         }
     }
 }
