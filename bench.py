@@ -50,8 +50,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "eab1c379515bed3c072c803611e1092c6abeb1b9d8f5f051a9d455218e1a412f",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_280_982}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "85fecd8614450f43d92ae0523c1ea97165c64bd30b9e44ebbd1daec033031fb4",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 141_827_698}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 
@@ -240,11 +240,13 @@ class Bench:
         self.fused = self.twin and args.commit == "fused"
         B = self.B = args.rows
         T = self.T = args.tokens
+        # the first R rows are real; the rest of the bucket points at the null slot
+        R = self.R = B if args.real is None else args.real
         # the drawn pool (the null slot and 256 slot pairs) and inputs for 256 rows
         case = gi.qwen08b(B=256, T=T)
         s, pool, step = case.shape, case.pools[0], case.steps[0][0]
         self.shape = s
-        nsets, per = row_sets(args.mode, B, T, s.H_v * s.d_k * s.d_v * 4, args.hot)
+        nsets, per = row_sets(args.mode, R, T, s.H_v * s.d_k * s.d_v * 4, args.hot)
         spc = DRAWN_SLOTS // per                  # disjoint row sets one copy of the drawn pool holds
         copies = -(-nsets // spc)
         self.N = 1 + DRAWN_SLOTS * copies
@@ -261,15 +263,17 @@ class Bench:
         self.conv_w = _bf(torch, pool.conv_w)
         perm = np.random.Generator(np.random.PCG64(1)).permutation(DRAWN_SLOTS).astype(np.int32) + 1
         slot_rows = []
+        pad = np.zeros(B - R, np.int32)
         for k in range(nsets):
             j, off = k % spc, DRAWN_SLOTS * (k // spc)
             if self.twin:
-                slot_rows.append((pool.read_slot[j * B:(j + 1) * B] + off, pool.write_slot[j * B:(j + 1) * B] + off))
+                slot_rows.append((np.concatenate([pool.read_slot[j * R:(j + 1) * R] + off, pad]),
+                                  np.concatenate([pool.write_slot[j * R:(j + 1) * R] + off, pad])))
             elif self.tokens_mode:
                 # B read slots and B*T token slots, all distinct
                 slot_rows.append((perm[j * per:j * per + B] + off, (perm[j * per + B:(j + 1) * per] + off).reshape(B, T)))
             else:
-                slot_rows.append((perm[j * B:(j + 1) * B] + off, None))
+                slot_rows.append((np.concatenate([perm[j * R:(j + 1) * R] + off, pad]), None))
         self.nsets = nsets
         self.sets = []
         for k, (rd, wr) in enumerate(slot_rows):
@@ -287,7 +291,7 @@ class Bench:
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
         self.timer = HipTimer()
-        self.bytes = algorithmic_bytes(B, 0, T, s.H_v, s.d_k, s.d_v, s.C, s.W, args.mode)
+        self.bytes = algorithmic_bytes(R, B - R, T, s.H_v, s.d_k, s.d_v, s.C, s.W, args.mode)
         self.cycles_per_ms = None
 
     def launch(self, st):
@@ -394,8 +398,8 @@ class Bench:
                  (4, "contiguous_copy"))
 
         # the contiguous copy rotates over disjoint ranges of 2B slots as well
-        ranges = [(torch.tensor([1 + 2 * self.B * k], dtype=torch.int32, device="cuda"),
-                   torch.tensor([1 + 2 * self.B * k + self.B], dtype=torch.int32, device="cuda"))
+        ranges = [(torch.tensor([1 + 2 * self.R * k], dtype=torch.int32, device="cuda"),
+                   torch.tensor([1 + 2 * self.R * k + self.R], dtype=torch.int32, device="cuda"))
                   for k in range(self.nsets)]
 
         def slots(mode, i):
@@ -411,20 +415,20 @@ class Bench:
             if mode == 3 and self.twin:
                 continue
             for i in range(8):
-                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.B)
+                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.R if mode == 4 else self.B)
             torch.cuda.synchronize()
             evs = [(timer.event(), timer.event()) for _ in range(reps)]
             self._sleep_for(5.0 + reps * 0.12)
             for i in range(reps):
                 timer.record(evs[i][0], sh)
-                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.B)
+                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.R if mode == 4 else self.B)
                 timer.record(evs[i][1], sh)
             torch.cuda.synchronize()
             us = np.array([timer.elapsed_ms(a, b) for a, b in evs]) * 1e3
             for a, b in evs:
                 timer.destroy(a)
                 timer.destroy(b)
-            nbytes = (1 if mode in (0, 1) else 2) * self.B * s.H_v * s.d_k * s.d_v * 4
+            nbytes = (1 if mode in (0, 1) else 2) * self.R * s.H_v * s.d_k * s.d_v * 4
             cal[name] = {"us_mean": float(us.mean()), "GBps": nbytes / (us.mean() * 1e-6) / 1e9}
         return cal
 
@@ -506,6 +510,98 @@ def run_stack(args) -> dict:
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": "gdn_step_tile_kernel",
                      "note": "whole-step time: every layer's launch queued back to back on one stream",
                      "bytes_per_step": total, "us_per_layer": ms * 1e3 / layers},
+    }
+
+
+SLOTOPS_METRIC = "GDN slot copy slots/s and achieved HBM GB/s (% of peak)"
+
+
+def run_slotops(args) -> dict:
+    """Slot lifecycle ops at the 0.8B-like layer's shapes: gdn_slot_copy of --rows
+    slots (state and conv window, e.g. forking requests) and gdn_slot_reset of
+    --rows slots (releasing them), each timed with fence-free HIP events around
+    every launch.  Calls rotate over disjoint slot sets so that at least 768 MiB
+    is written between two visits of a set (cold cache, as for the step)."""
+    import torch
+
+    import gated_deltanet_recurrent_decode_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.lib()
+    torch.cuda.set_device(0)
+    B = args.rows
+    case = gi.qwen08b(B=256)
+    s, pool = case.shape, case.pools[0]
+    slot_bytes = s.H_v * s.d_k * s.d_v * 4 + (s.W - 1) * s.C * 2
+    nsets, per = row_sets("twin", B, 1, slot_bytes, args.hot)   # a copy set: B sources and B destinations
+    spc = DRAWN_SLOTS // per
+    copies = -(-nsets // spc)
+    N = 1 + DRAWN_SLOTS * copies
+    state0 = torch.from_numpy(pool.state).cuda()
+    cs0 = _bf(torch, pool.conv_state)
+    state = torch.zeros((N,) + tuple(state0.shape[1:]), dtype=state0.dtype, device="cuda")
+    conv_state = torch.zeros((N,) + tuple(cs0.shape[1:]), dtype=cs0.dtype, device="cuda")
+    for c in range(copies):
+        state[1 + DRAWN_SLOTS * c:1 + DRAWN_SLOTS * (c + 1)] = state0[1:]
+        conv_state[1 + DRAWN_SLOTS * c:1 + DRAWN_SLOTS * (c + 1)] = cs0[1:]
+    del state0, cs0
+    perm = np.random.Generator(np.random.PCG64(2)).permutation(DRAWN_SLOTS).astype(np.int32) + 1
+    sets = []
+    for k in range(nsets):
+        j, off = k % spc, DRAWN_SLOTS * (k // spc)
+        sets.append((torch.from_numpy(perm[j * per:j * per + B] + off).cuda(),
+                     torch.from_numpy(perm[j * per + B:(j + 1) * per] + off).cuda()))
+    timer = HipTimer()
+    sh = torch.cuda.current_stream().cuda_stream
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(2_000_000)
+    c1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 2_000_000 / max(c0.elapsed_time(c1), 1e-3)
+
+    def timed(op):
+        for i in range(args.warmup):
+            op(sets[i % nsets])
+        torch.cuda.synchronize()
+        K = args.steps
+        evs = [(timer.event(), timer.event()) for _ in range(K)]
+        torch.cuda._sleep(int((5.0 + K * 0.12) * cycles_per_ms))
+        for i in range(K):
+            timer.record(evs[i][0], sh)
+            op(sets[i % nsets])
+            timer.record(evs[i][1], sh)
+        torch.cuda.synchronize()
+        us = np.array([timer.elapsed_ms(a, b) for a, b in evs]) * 1e3
+        for a, b in evs:
+            timer.destroy(a)
+            timer.destroy(b)
+        return us
+
+    # a copy reads the source slot and writes the destination; a reset writes zeros
+    copy_us = timed(lambda st: gdn.slot_copy(state, conv_state, st[0], st[1], H_k=s.H_k))
+    reset_us = timed(lambda st: gdn.slot_reset(state, conv_state, st[1], H_k=s.H_k))
+    copy_bytes = B * (2 * slot_bytes + 8)
+    reset_bytes = B * (slot_bytes + 4)
+    k_us = float(copy_us.mean())
+    achieved = copy_bytes / (k_us * 1e-6) / 1e9
+    r_us = float(reset_us.mean())
+    return {
+        "metric": SLOTOPS_METRIC, "value": B / (k_us * 1e-6), "unit": "slots/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": k_us * 1e-3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"slot copy and slot reset of {B} slots a call (0.8B-like layer: 16 heads x 128x128 "
+                               f"fp32 state and a bf16 conv window of 3 x 6144 a slot), {nsets} disjoint slot sets "
+                               f"rotated over a {N}-slot pool (cold cache)",
+                   "slots": B, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "C": s.C, "N": N, "row_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": "slot_ops_kernel (copy)",
+                     "kernel_us_mean": k_us, "kernel_us_p10": float(np.percentile(copy_us, 10)),
+                     "kernel_us_p50": float(np.percentile(copy_us, 50)),
+                     "kernel_us_p90": float(np.percentile(copy_us, 90)), "bytes_per_launch": copy_bytes},
+        "reset": {"kernel_us_mean": r_us, "kernel_us_p50": float(np.percentile(reset_us, 50)),
+                  "bytes_per_launch": reset_bytes, "GBps": reset_bytes / (r_us * 1e-6) / 1e9,
+                  "frac": reset_bytes / (r_us * 1e-6) / 1e9 / PEAK_HBM_GBPS},
     }
 
 
@@ -598,13 +694,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", type=int, default=64)
-    ap.add_argument("--mode", choices=("twin", "inplace", "tokens", "prefill", "stack"), default="twin",
-                    help="twin-slot write, in-place write, a kept state per token (speculative verify), or the "
-                         "chunked prefill of --rows prompts of --prefill-len tokens, or the 9B-like stack of "
-                         "--layers layers (twin)")
+    ap.add_argument("--mode", choices=("twin", "inplace", "tokens", "prefill", "stack", "slotops"), default="twin",
+                    help="twin-slot write, in-place write, a kept state per token (speculative verify), the "
+                         "chunked prefill of --rows prompts of --prefill-len tokens, the 9B-like stack of "
+                         "--layers layers (twin), or slot copy and reset of --rows slots a call")
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--prefill-len", type=int, default=512)
     ap.add_argument("--tokens", type=int, default=1, help="tokens a row (in place and tokens mode)")
+    ap.add_argument("--real", type=int, default=None,
+                    help="a padded bucket: only the first REAL of the --rows rows are real, the rest point at the "
+                         "null slot (twin and in place)")
     ap.add_argument("--commit", choices=("fused", "separate"), default="fused")
     ap.add_argument("--hot", action="store_true", help="same rows every step (cache-warm)")
     ap.add_argument("--graph", action="store_true", help="time steps replayed from a captured HIP graph")
@@ -631,6 +730,15 @@ def main() -> int:
             return 2
         print(json.dumps(run_prefill(args)), flush=True)
         return 0
+    if args.mode == "slotops":
+        if not 1 <= args.rows <= 256:
+            print("bench.py: slot ops take 1 <= --rows <= 256", file=sys.stderr)
+            return 2
+        print(json.dumps(run_slotops(args)), flush=True)
+        return 0
+    if args.real is not None and (args.mode == "tokens" or not 1 <= args.real <= args.rows):
+        print("bench.py: --real takes 1 <= REAL <= --rows, twin or in place", file=sys.stderr)
+        return 2
     if args.tokens < 1 or (args.mode == "twin" and args.tokens != 1):
         print("bench.py: --tokens must be >= 1, and twin-slot writes take one token a row", file=sys.stderr)
         return 2
@@ -656,7 +764,7 @@ def main() -> int:
     ms_per_step, _, host_ms = b.timed(K, per_kernel_events=False, graph=graph)
     _, kus, _ = b.timed(K, per_kernel_events=True)
 
-    rows_per_s = b.B / (ms_per_step * 1e-3)
+    rows_per_s = b.R / (ms_per_step * 1e-3)
     twin = b.twin
     commit = ("folded into the step kernel (next slot pair written by the step)" if b.fused else
               "separate slot_commit kernel" if twin else
@@ -675,7 +783,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"0.8B-like GDN layer decode step: {b.B} rows x 16+16 heads x 128x128 fp32 state, "
+        "config": {"workload": f"0.8B-like GDN layer decode step: {b.B} rows"
+                               + (f" ({b.R} real, {b.B - b.R} on the null slot)" if b.R < b.B else "")
+                               + " x 16+16 heads x 128x128 fp32 state, "
                                f"conv width 4 over 6144 channels, bf16 conv windows and activations, "
                                f"{b.N}-slot pool, {b.T} token{'s' if b.T > 1 else ''} a row, "
                                f"{ {'twin': 'twin-slot write', 'inplace': 'in-place write', 'tokens': 'state kept per token (speculative verify)'}[args.mode]}, commit "
@@ -683,7 +793,7 @@ def main() -> int:
                                + ("same rows every step (cache-warm)" if args.hot else
                                   f"{b.nsets} disjoint row sets rotated (cold cache)")
                                + (", HIP graph replay" if graph is not None else ", stream launches"),
-                   "B": b.B, "T": b.T, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": b.N,
+                   "B": b.B, "real_rows": b.R, "T": b.T, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v, "W": s.W, "N": b.N,
                    "write": args.mode, "commit": "fused" if b.fused else ("separate" if twin else "none"),
                    "row_sets": b.nsets, "graph": graph is not None},
         "step_GBps": b.bytes / (ms_per_step * 1e-3) / 1e9,

@@ -265,10 +265,10 @@ const char *gdn_status_string(gdn_status status);
  *           plain-copy ceiling).  A range outside [1, N) makes it a no-op;
  *           B slots must be under 2 GiB (else GDN_ERR_SHAPE); overlapping
  *           ranges race.
- * Loads stream (nt); stores use the step's policy (write-through for a twin
- * write, streaming in place).  state is [N][H][d_k][d_v] fp32; rows with
- * read slot 0 are skipped.  sink [1] fp32 receives nothing in practice; it
- * only keeps the read-only mode's loads alive.  d_k, d_v in {64, 128}.
+ * Loads and stores stream (nt), as the step's state accesses do.  state is
+ * [N][H][d_k][d_v] fp32; rows with read slot 0 are skipped.  sink [1] fp32
+ * receives nothing in practice; it only keeps the read-only mode's loads
+ * alive.  d_k, d_v in {64, 128}.
  */
 gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
                              float *state, const int32_t *read_slot, const int32_t *write_slot,
