@@ -14,13 +14,14 @@ import ctypes
 import os
 
 __all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill",
-           "conv_decode",
+           "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "conv_decode",
            "slot_commit",
            "slot_reset", "slot_copy", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill", "conv_decode",
+EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill",
+           "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "conv_decode",
            "slot_commit",
            "gdn_slot_reset",
            "gdn_slot_copy", "gdn_status_string", "gdn_traffic_probe")
@@ -66,6 +67,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_decode_step_tokens.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.gdn_prefill.restype = i32
     L.gdn_prefill.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
+    L.gdn_prefill_two_pass.restype = i32
+    L.gdn_prefill_two_pass.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P,
+                                       ctypes.c_size_t, P]
+    L.gdn_prefill_two_pass_workspace_bytes.restype = ctypes.c_size_t
+    L.gdn_prefill_two_pass_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.conv_decode.restype = i32
     L.conv_decode.argtypes = [i32, i32, i32, i32, P, i64, P, P, P, P, P, P, i64, i32, P]
     L.slot_commit.restype = i32
@@ -208,12 +214,7 @@ def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_s
         _stream(stream)))
 
 
-def gdn_prefill(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, *, H_k: int,
-                q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
-    """Chunked prefill of packed sequences, in place (see ``gdn_prefill`` in include/gdn.h).
-
-    x [T][C] bf16 (rows may be strided), g/beta [T][H_v] fp32, cu_seqlens [B+1] int32,
-    slot [B] int32, out [T][H_v][d_v] bf16; the pool tensors as for gdn_decode_step."""
+def _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k):
     torch = _torch()
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     _dev(x, "x", bf)
@@ -232,11 +233,38 @@ def gdn_prefill(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot,
         raise ValueError("cu_seqlens [B+1], g/beta [T][H_v], out [T][H_v][d_v] expected")
     if conv_state.shape != (N, W - 1, C) or conv_w.shape[0] != C:
         raise ValueError("conv_state / conv_w do not match x and state")
-    d = Dims(B, T, H_k, H_v, d_k, d_v, W, N)
-    xs = x.stride(0) if T > 0 else C
+    return Dims(B, T, H_k, H_v, d_k, d_v, W, N), (x.stride(0) if T > 0 else C)
+
+
+def gdn_prefill(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, *, H_k: int,
+                q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """Chunked prefill of packed sequences, in place (see ``gdn_prefill`` in include/gdn.h).
+
+    x [T][C] bf16 (rows may be strided), g/beta [T][H_v] fp32, cu_seqlens [B+1] int32,
+    slot [B] int32, out [T][H_v][d_v] bf16; the pool tensors as for gdn_decode_step."""
+    d, xs = _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k)
     _check("gdn_prefill", lib().gdn_prefill(
         ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
         _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _stream(stream)))
+
+
+def gdn_prefill_two_pass_workspace_bytes(B: int, T: int, H_k: int, H_v: int, d_k: int, d_v: int) -> int:
+    """Workspace bytes gdn_prefill_two_pass needs (see include/gdn.h); 0 for unusable sizes."""
+    d = Dims(B, T, H_k, H_v, d_k, d_v, 4, 1)
+    return int(lib().gdn_prefill_two_pass_workspace_bytes(ctypes.byref(d)))
+
+
+def gdn_prefill_two_pass(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, workspace, *,
+                         H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """gdn_prefill in two passes with a caller-owned workspace (a device uint8 tensor of at
+    least gdn_prefill_two_pass_workspace_bytes bytes); see include/gdn.h."""
+    torch = _torch()
+    d, xs = _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k)
+    _contig(_dev(workspace, "workspace", torch.uint8), "workspace")
+    _check("gdn_prefill_two_pass", lib().gdn_prefill_two_pass(
+        ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+        _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
 
 
 def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_abi.hip", "gdn_step.hip", "gdn_step_tile.hip", "gdn_prefill.hip", "conv_decode.hip", "slot_commit.hip", "slot_ops.hip",
-           "traffic_probe.hip"]
+           "traffic_probe.hip", "gdn_prefill_two_pass.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

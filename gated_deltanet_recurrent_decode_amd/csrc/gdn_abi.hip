@@ -150,11 +150,17 @@ gdn_status gdn_decode_step_commit(const gdn_dims *dims, const gdn_bf16 *x, int64
                      next_read_slot, next_write_slot, nullptr, out, q_scale, l2_eps, stream);
 }
 
-gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const int32_t *cu_seqlens,
-                       const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state,
-                       const float *g, const float *beta, const int32_t *slot, gdn_bf16 *out, float q_scale,
-                       float l2_eps, hipStream_t stream)
+namespace {
+
+// The checks gdn_prefill and gdn_prefill_two_pass share; on GDN_OK with
+// *run set, p holds the launch parameters (*run is false when there is
+// nothing to do).
+gdn_status prefill_setup(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const int32_t *cu_seqlens,
+                         const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state,
+                         const float *g, const float *beta, const int32_t *slot, gdn_bf16 *out, float q_scale,
+                         float l2_eps, gdn::PrefillParams &p, bool *run)
 {
+    *run = false;
     if (!dims)
         return GDN_ERR_NULL;
     const gdn_dims d = *dims;
@@ -167,7 +173,7 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
     if (!head_dim_ok(d.d_k) || !head_dim_ok(d.d_v) || d.W != 4)
         return GDN_ERR_UNSUPPORTED;
     const int64_t C = 2LL * d.H_k * d.d_k + (int64_t)d.H_v * d.d_v;
-    if (C > INT32_MAX || x_row_stride < C || (int64_t)d.B * d.H_k > INT32_MAX)
+    if (C > INT32_MAX || x_row_stride < C || (int64_t)d.B * d.H_v * 4 > INT32_MAX || d.H_v > 65535)
         return GDN_ERR_SHAPE;
     if (!(l2_eps >= 0.0f) || !isfinite(l2_eps) || !isfinite(q_scale))
         return GDN_ERR_SHAPE;
@@ -177,7 +183,7 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
         return GDN_ERR_UNSUPPORTED;
     if (d.T == 0) // every sequence is empty
         return GDN_OK;
-    gdn::PrefillParams p{};
+    p = gdn::PrefillParams{};
     p.x = x;
     p.x_row_stride = x_row_stride;
     p.cu_seqlens = cu_seqlens;
@@ -198,7 +204,59 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
     p.G = d.H_v / d.H_k;
     p.N = d.N;
     p.C = (int)C;
-    return from_hip(gdn::launch_gdn_prefill(p, d.d_k, d.d_v, stream));
+    *run = true;
+    return GDN_OK;
+}
+
+} // namespace
+
+gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride, const int32_t *cu_seqlens,
+                       const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state,
+                       const float *g, const float *beta, const int32_t *slot, gdn_bf16 *out, float q_scale,
+                       float l2_eps, hipStream_t stream)
+{
+    gdn::PrefillParams p;
+    bool run;
+    const gdn_status st = prefill_setup(dims, x, x_row_stride, cu_seqlens, conv_w, conv_b, conv_state, state, g,
+                                        beta, slot, out, q_scale, l2_eps, p, &run);
+    if (st != GDN_OK || !run)
+        return st;
+    return from_hip(gdn::launch_gdn_prefill(p, dims->d_k, dims->d_v, stream));
+}
+
+size_t gdn_prefill_two_pass_workspace_bytes(const gdn_dims *dims)
+{
+    if (!dims)
+        return 0;
+    const gdn_dims d = *dims;
+    if (d.B < 0 || d.T < 0 || d.H_v < 1 || !head_dim_ok(d.d_k) || !head_dim_ok(d.d_v))
+        return 0;
+    return gdn::two_pass_layout(d.B, d.T, d.H_v, d.d_k, d.d_v, nullptr, nullptr);
+}
+
+gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                const int32_t *cu_seqlens, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
+                                gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
+                                const int32_t *slot, gdn_bf16 *out, float q_scale, float l2_eps, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    gdn::PrefillParams p;
+    bool run;
+    const gdn_status st = prefill_setup(dims, x, x_row_stride, cu_seqlens, conv_w, conv_b, conv_state, state, g,
+                                        beta, slot, out, q_scale, l2_eps, p, &run);
+    if (st != GDN_OK || !run)
+        return st;
+    if (!workspace)
+        return GDN_ERR_NULL;
+    if (!aligned(workspace, 256))
+        return GDN_ERR_UNSUPPORTED;
+    if ((long long)p.total / 32 + p.B + 1 > INT32_MAX)
+        return GDN_ERR_SHAPE;
+    gdn::TwoPassParams tp{};
+    tp.p = p;
+    if (workspace_bytes < gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, workspace, &tp.ws))
+        return GDN_ERR_SHAPE;
+    return from_hip(gdn::launch_gdn_prefill_two_pass(tp, dims->d_k, dims->d_v, stream));
 }
 
 gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf16 *x,

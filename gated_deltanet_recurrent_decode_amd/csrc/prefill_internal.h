@@ -26,4 +26,25 @@ struct PrefillParams {
 
 hipError_t launch_gdn_prefill(const PrefillParams &p, int d_k, int d_v, hipStream_t stream);
 
+// The two-pass prefill: its workspace, carved by two_pass_layout from one
+// caller buffer.  Per value head hv and packed token t (row hv * total + t):
+// q~ = e^gamma q^ [d_k], k~ = e^(gamma_last - gamma) k^ [d_k],
+// w = ((I + A)^-1 diag(beta e^gamma) K)[t] [d_k], u~ = ((I + A)^-1 diag(beta) V)[t]
+// [d_v], p = P[t] [32], and el = e^gamma_last at the chunk's first token.
+struct TwoPassWorkspace {
+    int32_t *chunk_start; // [B+1]: exclusive scan of each sequence's chunk count
+    float *qt, *kt, *ww, *ut, *pp, *el;
+};
+
+struct TwoPassParams {
+    PrefillParams p;
+    TwoPassWorkspace ws;
+};
+
+// Bytes of the workspace for B sequences, total tokens, H_v heads, d_k, d_v;
+// with a base pointer, also the regions (each 256-byte aligned).
+size_t two_pass_layout(int B, int total, int H_v, int d_k, int d_v, void *base, TwoPassWorkspace *ws);
+
+hipError_t launch_gdn_prefill_two_pass(const TwoPassParams &p, int d_k, int d_v, hipStream_t stream);
+
 } // namespace gdn

@@ -40,6 +40,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -190,6 +191,37 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
                        const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state, float *state,
                        const float *g, const float *beta, const int32_t *slot, gdn_bf16 *out, float q_scale,
                        float l2_eps, hipStream_t stream);
+
+/*
+ * gdn_prefill_two_pass -- the same computation and contract as gdn_prefill,
+ * for calls with few prompts: it runs in two passes with a caller-provided
+ * workspace.  The first pass works on every 32-token chunk of every prompt at
+ * once (conv decode + SiLU, L2 norms, the chunk's decay and the triangular
+ * solve of the chunked delta rule, PR #1139 "What changed": prefill in place),
+ * the second walks each prompt's chunks in order with the d_v columns of each
+ * head split over several workgroups.  Results match gdn_prefill within
+ * rounding, not bit for bit.
+ *
+ * workspace: device memory of at least
+ * gdn_prefill_two_pass_workspace_bytes(dims) bytes, 256-byte aligned, owned
+ * by the caller; its contents on entry do not matter and on return are
+ * scratch.  Calls that share a workspace must be stream-ordered.  Beyond
+ * gdn_prefill's statuses: GDN_ERR_NULL without a workspace,
+ * GDN_ERR_UNSUPPORTED if it is misaligned, GDN_ERR_SHAPE if it is too small.
+ */
+gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                const int32_t *cu_seqlens, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
+                                gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
+                                const int32_t *slot, gdn_bf16 *out, float q_scale, float l2_eps, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_prefill_two_pass_workspace_bytes -- the workspace gdn_prefill_two_pass
+ * needs for dims (B sequences, T packed tokens, H_v, d_k, d_v): per token and
+ * value head (3 d_k + d_v + 33) fp32 values, plus B + 1 int32, each region
+ * rounded up to 256 bytes.  0 when dims is NULL or its sizes are unusable.
+ */
+size_t gdn_prefill_two_pass_workspace_bytes(const gdn_dims *dims);
 
 /*
  * conv_decode -- the pooled conv update for one token a row, standalone

@@ -146,6 +146,36 @@ def test_prefill_validation():
              None) == OK
 
 
+def test_prefill_two_pass_validation():
+    L = gdn.lib()
+    f = L.gdn_prefill_two_pass
+    d = _dims(T=40)
+    need = L.gdn_prefill_two_pass_workspace_bytes(ctypes.byref(d))
+    # per token and value head 3 d_k + d_v + 33 floats, plus B + 1 ints, each region rounded to 256 bytes
+    rows = d.H_v * d.T
+    parts = [4 * (d.B + 1), 4 * rows * d.d_k, 4 * rows * d.d_k, 4 * rows * d.d_k, 4 * rows * d.d_v, 4 * rows * 32,
+             4 * rows]
+    assert need == sum((x + 255) // 256 * 256 for x in parts)
+    assert L.gdn_prefill_two_pass_workspace_bytes(None) == 0
+    assert L.gdn_prefill_two_pass_workspace_bytes(ctypes.byref(_dims(T=40, d_k=96))) == 0
+    ws = ctypes.c_void_p(0x100000)
+
+    def call(dd, workspace=ws, nbytes=need, cu=FAKE):
+        C = 2 * dd.H_k * dd.d_k + dd.H_v * dd.d_v
+        return f(ctypes.byref(dd), FAKE, C, cu, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1e-6,
+                 workspace, nbytes, None)
+    assert call(d, workspace=None) == NULL
+    assert call(d, cu=None) == NULL
+    assert call(d, workspace=ctypes.c_void_p(0x100080)) == UNSUPPORTED   # not 256-byte aligned
+    assert call(d, nbytes=need - 1) == SHAPE
+    assert call(_dims(T=40, H_k=3, H_v=4)) == SHAPE
+    assert call(_dims(T=40, d_k=96)) == UNSUPPORTED
+    assert call(_dims(T=0), workspace=None) == OK                        # nothing to do, no workspace needed
+    empty = gdn.Dims(0, 0, 4, 4, 64, 64, 4, 9)
+    assert f(ctypes.byref(empty), None, 0, None, None, None, None, None, None, None, None, None, 1.0, 1e-6, None, 0,
+             None) == OK
+
+
 def test_slot_ops_validation():
     L = gdn.lib()
     d = _dims()

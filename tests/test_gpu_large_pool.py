@@ -140,16 +140,22 @@ def test_per_token_states_past_4gib(gdn, torch, big):
     bp.check(hp.state, hp.conv_state, tok.ravel())
 
 
-def test_prefill_past_4gib(gdn, torch, big):
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one-kernel", "two-pass"])
+def test_prefill_past_4gib(gdn, torch, big, two_pass):
     t = torch
     case = gi.prefill([45, 3, 70], H_k=H_K, H_v=H_V, d=D, seed=64)
     s, pool = case.shape, case.pool
     bp = BigPool(t, big, pool)
     hp = H.HostPool(pool)
     out = t.full((s.T, H_V, D), 7.0, dtype=t.bfloat16, device="cuda")
-    gdn.gdn_prefill(H.bf16_dev(case.x), bp.conv_w, None, bp.conv, bp.state, t.from_numpy(case.g).cuda(),
-                    t.from_numpy(case.beta).cuda(), t.from_numpy(case.cu_seqlens).cuda(),
-                    bp.dev_slots(pool.read_slot), out, H_k=H_K)
+    args = (H.bf16_dev(case.x), bp.conv_w, None, bp.conv, bp.state, t.from_numpy(case.g).cuda(),
+            t.from_numpy(case.beta).cuda(), t.from_numpy(case.cu_seqlens).cuda(), bp.dev_slots(pool.read_slot), out)
+    if two_pass:
+        ws = t.empty((gdn.gdn_prefill_two_pass_workspace_bytes(s.B, s.T, H_K, H_V, D, D),), dtype=t.uint8,
+                     device="cuda")
+        gdn.gdn_prefill_two_pass(*args, ws, H_k=H_K)
+    else:
+        gdn.gdn_prefill(*args, H_k=H_K)
     ref = _oracle_prefill(case, hp)
     t.cuda.synchronize()
     H.assert_out_close(out, ref)

@@ -1,5 +1,5 @@
-"""GPU parity of the chunked prefill (gdn_prefill, through the C ABI) against the
-fp64 oracle.  A prompt's prefill is, by definition, the in-place decode step run
+"""GPU parity of the chunked prefill (gdn_prefill and gdn_prefill_two_pass,
+through the C ABI) against the fp64 oracle.  A prompt's prefill is, by definition, the in-place decode step run
 over its tokens in order, so the oracle for each sequence is
 oracle.gdn_decode_step in place with T = that sequence's length.  The kernel's
 chunked arithmetic differs from the token-by-token order only by rounding, so
@@ -44,21 +44,28 @@ def _oracle_prefill(case, hp, conv_b=None, q_scale=1.0):
     return out
 
 
-def _run(gdn, t, case, dp, conv_b=None, q_scale=1.0, cu=None):
+def _run(gdn, t, case, dp, conv_b=None, q_scale=1.0, cu=None, two_pass=False):
     s = case.shape
     out = t.full((s.T, s.H_v, s.d_v), 7.0, dtype=t.bfloat16, device="cuda")  # any unwritten row shows
     cu_dev = t.from_numpy(case.cu_seqlens if cu is None else cu).cuda()
-    gdn.gdn_prefill(H.bf16_dev(case.x), dp.conv_w, conv_b, dp.conv_state, dp.state, t.from_numpy(case.g).cuda(),
-                    t.from_numpy(case.beta).cuda(), cu_dev, dp.rd, out, H_k=s.H_k, q_scale=q_scale)
+    args = (H.bf16_dev(case.x), dp.conv_w, conv_b, dp.conv_state, dp.state, t.from_numpy(case.g).cuda(),
+            t.from_numpy(case.beta).cuda(), cu_dev, dp.rd, out)
+    if two_pass:
+        nbytes = gdn.gdn_prefill_two_pass_workspace_bytes(s.B, s.T, s.H_k, s.H_v, s.d_k, s.d_v)
+        # stale contents must not matter: fill the workspace with NaN bits
+        ws = t.full((nbytes,), 0xFF, dtype=t.uint8, device="cuda")
+        gdn.gdn_prefill_two_pass(*args, ws, H_k=s.H_k, q_scale=q_scale)
+    else:
+        gdn.gdn_prefill(*args, H_k=s.H_k, q_scale=q_scale)
     return out
 
 
-def _check(gdn, t, case, conv_b=None, q_scale=1.0):
+def _check(gdn, t, case, conv_b=None, q_scale=1.0, two_pass=False):
     s, pool = case.shape, case.pool
     dp, hp = H.DevPool(pool), H.HostPool(pool)
     before_state, before_conv = dp.state.clone(), dp.conv_state.clone()
     bias_dev = None if conv_b is None else H.bf16_dev(conv_b)
-    out = _run(gdn, t, case, dp, conv_b=bias_dev, q_scale=q_scale)
+    out = _run(gdn, t, case, dp, conv_b=bias_dev, q_scale=q_scale, two_pass=two_pass)
     ref = _oracle_prefill(case, hp, conv_b=conv_b, q_scale=q_scale)
     t.cuda.synchronize()
     H.assert_out_close(out, ref)
@@ -85,54 +92,83 @@ CASES = [
 ]
 
 
+PATHS = pytest.mark.parametrize("two_pass", [False, True], ids=["one-kernel", "two-pass"])
+
+
+@PATHS
 @pytest.mark.parametrize("lengths,hk,hv,d,dv,pad", CASES,
                          ids=[f"{len(c[0])}seq-{c[1]}x{c[2]}-d{c[3]}x{c[4]}" for c in CASES])
-def test_prefill_matches_oracle(gdn, torch, lengths, hk, hv, d, dv, pad):
+def test_prefill_matches_oracle(gdn, torch, lengths, hk, hv, d, dv, pad, two_pass):
     case = gi.prefill(list(lengths), H_k=hk, H_v=hv, d=d, d_v=dv, pad=pad, seed=len(lengths) + d)
-    _, out = _check(gdn, torch, case)
+    _, out = _check(gdn, torch, case, two_pass=two_pass)
     for b in pad:
         a, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
         assert torch.count_nonzero(out[a:e].view(torch.int16)) == 0, "padding sequences read out +0.0"
 
 
-def test_prefill_bias_and_q_scale(gdn, torch):
+@PATHS
+def test_prefill_bias_and_q_scale(gdn, torch, two_pass):
     case = gi.prefill([45, 12], H_k=2, H_v=2, d=128, seed=11)
     bias = gi.bf16_bits(np.random.Generator(np.random.PCG64(4)).standard_normal(case.shape.C).astype(np.float32))
-    _check(gdn, torch, case, conv_b=bias, q_scale=128 ** -0.5)
+    _check(gdn, torch, case, conv_b=bias, q_scale=128 ** -0.5, two_pass=two_pass)
 
 
-def test_prefill_08b_shapes(gdn, torch):
+@PATHS
+def test_prefill_08b_shapes(gdn, torch, two_pass):
     """The 0.8B-like layer's shapes: 16+16 heads of 128, 6144 channels."""
     case = gi.prefill([300, 45, 1], H_k=16, H_v=16, d=128, seed=2)
-    _check(gdn, torch, case)
+    _check(gdn, torch, case, two_pass=two_pass)
 
 
-def test_prefill_in_two_calls_equals_one(gdn, torch):
+def test_two_pass_long_prompt_and_slices(gdn, torch):
+    """One long prompt (the column-sliced walk, every chunk in flight in pass 1),
+    then many short ones (whole-tile walk), at the 0.8B shapes."""
+    _check(gdn, torch, gi.prefill([1000], H_k=16, H_v=16, d=128, seed=21), two_pass=True)
+    _check(gdn, torch, gi.prefill([3, 40, 1, 33] * 4 + [2] * 8, H_k=16, H_v=16, d=128, N=97, seed=22),
+           two_pass=True)
+
+
+def test_two_pass_agrees_with_one_kernel(gdn, torch):
+    """The two paths on the same inputs: within the state bar of each other."""
+    t = torch
+    case = gi.prefill([200, 7, 64], H_k=2, H_v=4, d=128, seed=23)
+    dp1, dp2 = H.DevPool(case.pool), H.DevPool(case.pool)
+    o1 = _run(gdn, t, case, dp1)
+    o2 = _run(gdn, t, case, dp2, two_pass=True)
+    t.cuda.synchronize()
+    H.assert_state_close(dp2.state.cpu().numpy(), dp1.state.cpu().numpy().astype(np.float64), "two-pass vs one-kernel")
+    assert t.equal(dp1.conv_state.view(t.int16), dp2.conv_state.view(t.int16))
+    H.assert_out_close(o2, H.bf16_host_f64(o1), "two-pass vs one-kernel out")
+
+
+@PATHS
+def test_prefill_in_two_calls_equals_one(gdn, torch, two_pass):
     """A prompt prefilled in two calls (the first 40 tokens, then the other 30)
     leaves the slot where one 70-token prefill does, within rounding, and the
     windows bit for bit (the conv window carries exactly the last inputs)."""
     t = torch
     case = gi.prefill([70], H_k=2, H_v=2, d=64, seed=5)
     dp1, dp2 = H.DevPool(case.pool), H.DevPool(case.pool)
-    _run(gdn, t, case, dp1)
-    for a, e in ((0, 40), (40, 70)):
+    _run(gdn, t, case, dp1, two_pass=two_pass)
+    for a, e in ((0, 40), (40, 41), (41, 70)):   # a one-token call in the middle: the window shifts by one
         sub = gi.PrefillCase(gi.Shape(B=1, T=e - a, H_k=2, H_v=2, d_k=64, d_v=64, W=4, N=case.shape.N), case.pool,
                              np.ascontiguousarray(case.x[a:e]), np.ascontiguousarray(case.g[a:e]),
                              np.ascontiguousarray(case.beta[a:e]), np.array([0, e - a], np.int32))
-        _run(gdn, t, sub, dp2)
+        _run(gdn, t, sub, dp2, two_pass=two_pass)
     t.cuda.synchronize()
     sl = int(case.pool.read_slot[0])
     H.assert_state_close(dp2.state[sl].cpu().numpy(), dp1.state[sl].cpu().numpy().astype(np.float64), "split prefill")
     assert t.equal(dp1.conv_state[sl].view(t.int16), dp2.conv_state[sl].view(t.int16))
 
 
-def test_prefill_unusable_ranges_touch_nothing(gdn, torch):
+@PATHS
+def test_prefill_unusable_ranges_touch_nothing(gdn, torch, two_pass):
     t = torch
     case = gi.prefill([10, 20, 5], H_k=1, H_v=1, d=64, seed=8)
     dp = H.DevPool(case.pool)
     before = dp.state.clone()
     bad = np.array([0, 10, 5, 99], np.int32)   # sequence 1 runs backwards, sequence 2 past T
-    out = _run(gdn, t, case, dp, cu=bad)
+    out = _run(gdn, t, case, dp, cu=bad, two_pass=two_pass)
     t.cuda.synchronize()
     for b in (1, 2):
         sl = int(case.pool.read_slot[b])
