@@ -643,10 +643,18 @@ def run_prefill(args) -> dict:
                          slot=torch.from_numpy(np.ascontiguousarray(case.pool.read_slot[k * nseq:(k + 1) * nseq])).cuda(),
                          out=torch.empty((nseq * L, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda")))
 
+    ws = None
+    if args.two_pass:
+        ws = torch.empty((gdn.gdn_prefill_two_pass_workspace_bytes(nseq, nseq * L, s.H_k, s.H_v, s.d_k, s.d_v),),
+                         dtype=torch.uint8, device="cuda")
+
     def launch(i):
         st = sets[i % 2]
-        gdn.gdn_prefill(st["x"], conv_w, None, conv_state, state, st["g"], st["beta"], st["cu"], st["slot"],
-                        st["out"], H_k=s.H_k)
+        a = (st["x"], conv_w, None, conv_state, state, st["g"], st["beta"], st["cu"], st["slot"], st["out"])
+        if ws is not None:
+            gdn.gdn_prefill_two_pass(*a, ws, H_k=s.H_k)
+        else:
+            gdn.gdn_prefill(*a, H_k=s.H_k)
 
     for i in range(args.warmup):
         launch(i)
@@ -678,10 +686,16 @@ def run_prefill(args) -> dict:
         "warmup": args.warmup, "ms_per_step": ms_per_call, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"chunked prefill, {nseq} prompts of {L} tokens a call, 0.8B-like layer (16+16 heads "
-                               f"of 128, 6144 conv channels, fp32 state), in place, two slot sets alternating",
-                   "prompts": nseq, "prompt_len": L, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v},
+                               f"of 128, 6144 conv channels, fp32 state), in place, two slot sets alternating, "
+                               + ("two passes (chunk-parallel, then a column-sliced walk)" if ws is not None else
+                                  "one kernel (a workgroup per prompt and key head)"),
+                   "prompts": nseq, "prompt_len": L, "H_k": s.H_k, "H_v": s.H_v, "d_k": s.d_k, "d_v": s.d_v,
+                   "path": "two-pass" if ws is not None else "one-kernel",
+                   "workspace_bytes": 0 if ws is None else int(ws.numel())},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None, "kernel": "gdn_prefill_kernel",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "kernel": ("tp_chunk_map + tp_intra + tp_inter (one call)" if ws is not None else
+                                "gdn_prefill_kernel"),
                      "kernel_us_mean": k_us, "kernel_us_p50": float(np.percentile(us, 50)),
                      "flops_per_launch": flops, "hbm_bytes_per_launch": hbm,
                      "hbm_GBps": hbm / (k_us * 1e-6) / 1e9},
@@ -700,6 +714,7 @@ def main() -> int:
                          "--layers layers (twin), or slot copy and reset of --rows slots a call")
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--prefill-len", type=int, default=512)
+    ap.add_argument("--two-pass", action="store_true", help="prefill through gdn_prefill_two_pass")
     ap.add_argument("--tokens", type=int, default=1, help="tokens a row (in place and tokens mode)")
     ap.add_argument("--real", type=int, default=None,
                     help="a padded bucket: only the first REAL of the --rows rows are real, the rest point at the "

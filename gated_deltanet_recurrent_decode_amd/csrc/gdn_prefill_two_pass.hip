@@ -46,6 +46,30 @@ __device__ __forceinline__ v4f mma16(float a, float b, v4f c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// A byte offset past the end of every buffer resource used here: a load there
+// returns 0 and a store there is dropped, with no memory access.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Base and size are the same for the whole workgroup: they are moved to scalar
+// registers here, or a value the compiler happened to compute on the vector
+// unit (a clamp, a 64-bit multiply-add) makes it wrap every access in a loop
+// over the lanes' distinct resources.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes)
+{
+    // readfirstlane works on int: each half goes back through uint32_t so that
+    // the low word is not sign-extended into the high one
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(hi << 32 | lo), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ v4f buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ bool sequence_usable(const PrefillParams &p, int b, int &t_begin, int &t_end, int &s)
 {
     t_begin = p.cu_seqlens[b];
@@ -388,12 +412,16 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     constexpr int SP = DVS + ((DVS + 16) % 32 == 16 ? 16 : 32); // S and U: B operands, read down a column
     constexpr int PPI = BT + 4;                                 // P: A operand read along a row
     constexpr int CBS = DVS / 16;                               // column blocks of the slice
-    constexpr int TPW = 2 * CBS / 4;                            // output tiles (row block, column block) a wave
+    // output tiles (row block, column block) of W S0, Q~ S0 and O a wave takes;
+    // a 16-column slice has two, so waves 0-1 take W S0 and waves 2-3 Q~ S0 and O
+    constexpr bool SPLIT = CBS == 1;
+    constexpr int TPW = SPLIT ? 1 : 2 * CBS / 4;
     constexpr int RBW = DK / 16 / 4;                            // row blocks of S a wave updates
     constexpr int NW4 = BT * DK / 4 / NT;                       // float4 a thread stages of W, Q~, K~
-    constexpr int NU4 = BT * DVS / 4 / NT;                      // ... of U~
+    constexpr int NU4E = BT * DVS / 4;                          // float4 of U~ a chunk
+    constexpr int NU4 = (NU4E + NT - 1) / NT;                   // ... a thread
     constexpr int NP4 = BT * BT / 4 / NT;                       // ... of P
-    static_assert(TPW >= 1 && NU4 >= 1 && NW4 >= 1 && NP4 == 1, "slices of 32 columns or more");
+    static_assert(NW4 >= 1 && NP4 == 1 && DVS >= 16, "slices of 16 columns or more");
 
     __shared__ __align__(16) float S[DK * SP];
     __shared__ __align__(16) float Wm[BT * KP];
@@ -412,6 +440,11 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     int t_begin, t_end, s;
     if (!sequence_usable(p, b, t_begin, t_end, s))
         return; // an unusable range or slot touches nothing
+    // one value for the whole workgroup: the buffer resources built from these
+    // must sit in scalar registers
+    t_begin = __builtin_amdgcn_readfirstlane(t_begin);
+    t_end = __builtin_amdgcn_readfirstlane(t_end);
+    s = __builtin_amdgcn_readfirstlane(s);
     if (s == 0) {
         // padding sequence on the null slot: its read-out is +0.0
         for (int e = tid; e < (t_end - t_begin) * DVS; e += NT)
@@ -430,33 +463,43 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
         *reinterpret_cast<v4f *>(&S[i * SP + 4 * j4]) = v;
     }
 
-    // ---- a chunk's pass-1 results, staged in registers one chunk ahead
+    // ---- a chunk's pass-1 results, staged in registers one chunk ahead.  The
+    // loads are buffer loads over the chunk's real rows only (rows past the
+    // prompt's end, or a chunk past it, read zeros without touching memory),
+    // so the walk has no branch around a memory access and every wait in it
+    // covers exactly the loads it needs, not the read-out stores in flight.
     v4f rw[NW4], rq[NW4], rk[NW4], ru[NU4], rp[NP4];
     float rel = 0.f;
     auto prefetch = [&](int c0) {
-        const int nn = t_end - c0 < BT ? t_end - c0 : BT;
+        c0 = __builtin_amdgcn_readfirstlane(c0);
+        int nn = t_end - c0;
+        nn = nn < 0 ? 0 : (nn > BT ? BT : nn);
+        const size_t row0 = (size_t)hv * T + (size_t)c0;
+        const __amdgpu_buffer_rsrc_t rW = buf_rsrc(tp.ws.ww + row0 * DK, (uint32_t)(nn * DK * 4));
+        const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(tp.ws.qt + row0 * DK, (uint32_t)(nn * DK * 4));
+        const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.kt + row0 * DK, (uint32_t)(nn * DK * 4));
+        const __amdgpu_buffer_rsrc_t rU =
+            buf_rsrc(tp.ws.ut + row0 * DV + col0, nn > 0 ? (uint32_t)(((nn - 1) * DV + DVS) * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pp + row0 * BT, (uint32_t)(nn * BT * 4));
 #pragma unroll
         for (int m = 0; m < NW4; ++m) {
             const int e4 = tid + NT * m, tt = e4 / (DK / 4), i4 = e4 % (DK / 4);
-            const size_t off = ((size_t)hv * T + c0 + tt) * DK + 4 * i4;
-            const bool ok = tt < nn;
-            rw[m] = ok ? *reinterpret_cast<const v4f *>(tp.ws.ww + off) : v4f{0.f, 0.f, 0.f, 0.f};
-            rq[m] = ok ? *reinterpret_cast<const v4f *>(tp.ws.qt + off) : v4f{0.f, 0.f, 0.f, 0.f};
-            rk[m] = ok ? *reinterpret_cast<const v4f *>(tp.ws.kt + off) : v4f{0.f, 0.f, 0.f, 0.f};
+            const uint32_t off = (uint32_t)(tt * DK + 4 * i4) * 4u;
+            rw[m] = buf_load4(rW, off);
+            rq[m] = buf_load4(rQ, off);
+            rk[m] = buf_load4(rK, off);
         }
 #pragma unroll
         for (int m = 0; m < NU4; ++m) {
             const int e4 = tid + NT * m, tt = e4 / (DVS / 4), j4 = e4 % (DVS / 4);
-            ru[m] = tt < nn ? *reinterpret_cast<const v4f *>(tp.ws.ut + ((size_t)hv * T + c0 + tt) * DV + col0 + 4 * j4)
-                            : v4f{0.f, 0.f, 0.f, 0.f};
+            ru[m] = buf_load4(rU, e4 < NU4E ? (uint32_t)(tt * DV + 4 * j4) * 4u : kOOB);
         }
 #pragma unroll
         for (int m = 0; m < NP4; ++m) {
             const int e4 = tid + NT * m, tt = e4 / (BT / 4), s4 = e4 % (BT / 4);
-            rp[m] = tt < nn ? *reinterpret_cast<const v4f *>(tp.ws.pp + ((size_t)hv * T + c0 + tt) * BT + 4 * s4)
-                            : v4f{0.f, 0.f, 0.f, 0.f};
+            rp[m] = buf_load4(rP, (uint32_t)(tt * BT + 4 * s4) * 4u);
         }
-        rel = tp.ws.el[(size_t)hv * T + c0];
+        rel = tp.ws.el[(size_t)hv * T + (size_t)__builtin_amdgcn_readfirstlane(c0 < t_end ? c0 : t_end - 1)];
     };
     prefetch(t_begin);
 
@@ -473,7 +516,8 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
 #pragma unroll
         for (int m = 0; m < NU4; ++m) {
             const int e4 = tid + NT * m, tt = e4 / (DVS / 4), j4 = e4 % (DVS / 4);
-            *reinterpret_cast<v4f *>(&Um[tt * SP + 4 * j4]) = ru[m];
+            if (e4 < NU4E)
+                *reinterpret_cast<v4f *>(&Um[tt * SP + 4 * j4]) = ru[m];
         }
 #pragma unroll
         for (int m = 0; m < NP4; ++m) {
@@ -481,51 +525,83 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
             *reinterpret_cast<v4f *>(&Pm[tt * PPI + 4 * s4]) = rp[m];
         }
         __syncthreads(); // the chunk is staged (and the previous chunk's S update is in)
-        if (t0 + BT < t_end)
-            prefetch(t0 + BT);
+        prefetch(t0 + BT);
+        // the read-out rows of the chunk's real tokens; later rows fall outside
+        const int t0u = __builtin_amdgcn_readfirstlane(t0), nu = __builtin_amdgcn_readfirstlane(n);
+        const __amdgpu_buffer_rsrc_t rO = buf_rsrc(p.out + ((size_t)t0u * p.H_v + hv) * DV + col0,
+                                                   (uint32_t)(((nu - 1) * p.H_v * DV + DVS) * 2));
 
-        // ---- W S0 and Q~ S0 on this wave's output tiles
-        v4f aw[TPW], aq[TPW];
+        if constexpr (SPLIT) {
+            // ---- waves 0-1: W S0 and U = U~ - W S0 on row block wv; waves 2-3:
+            // Q~ S0 on row block wv - 2, then O = Q~ S0 + P U -> out
+            const int rb = wv & 1;
+            const bool is_w = wv < 2;
+            const float *Asrc = is_w ? Wm : Qm;
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int k0 = 0; k0 < DK; k0 += 4)
+                acc = mma16(Asrc[(rb * 16 + li) * KP + k0 + lk], S[(k0 + lk) * SP + li], acc);
+            if (is_w) {
 #pragma unroll
-        for (int k = 0; k < TPW; ++k)
-            aw[k] = aq[k] = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < 4; ++r)
+                    Um[(rb * 16 + 4 * lk + r) * SP + li] -= acc[r];
+            }
+            __syncthreads(); // U complete; every read of S0 for this chunk is done
+            if (!is_w) {
+#pragma unroll
+                for (int k0 = 0; k0 < BT; k0 += 4)
+                    acc = mma16(Pm[(rb * 16 + li) * PPI + k0 + lk], Um[(k0 + lk) * SP + li], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tt = rb * 16 + 4 * lk + r;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[r]), rO,
+                                                          (uint32_t)(tt * p.H_v * DV + li) * 2u, 0, 0);
+                }
+            }
+        } else {
+            // ---- W S0 and Q~ S0 on this wave's output tiles
+            v4f aw[TPW], aq[TPW];
+#pragma unroll
+            for (int k = 0; k < TPW; ++k)
+                aw[k] = aq[k] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-        for (int k0 = 0; k0 < DK; k0 += 4) {
+            for (int k0 = 0; k0 < DK; k0 += 4) {
+#pragma unroll
+                for (int k = 0; k < TPW; ++k) {
+                    const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
+                    const float bs = S[(k0 + lk) * SP + cb * 16 + li];
+                    aw[k] = mma16(Wm[(rb * 16 + li) * KP + k0 + lk], bs, aw[k]);
+                    aq[k] = mma16(Qm[(rb * 16 + li) * KP + k0 + lk], bs, aq[k]);
+                }
+            }
+            // U = U~ - W S0 over the same tiles (a wave reads and writes only its own)
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
-                const float bs = S[(k0 + lk) * SP + cb * 16 + li];
-                aw[k] = mma16(Wm[(rb * 16 + li) * KP + k0 + lk], bs, aw[k]);
-                aq[k] = mma16(Qm[(rb * 16 + li) * KP + k0 + lk], bs, aq[k]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Um[(rb * 16 + 4 * lk + r) * SP + cb * 16 + li] -= aw[k][r];
             }
-        }
-        // U = U~ - W S0 over the same tiles (a wave reads and writes only its own)
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Um[(rb * 16 + 4 * lk + r) * SP + cb * 16 + li] -= aw[k][r];
-        }
-        __syncthreads(); // U complete; every read of S0 for this chunk is done
+            __syncthreads(); // U complete; every read of S0 for this chunk is done
 
-        // ---- O = Q~ S0 + P U -> out (rows of real tokens)
+            // ---- O = Q~ S0 + P U -> out (rows of real tokens)
 #pragma unroll
-        for (int k0 = 0; k0 < BT; k0 += 4) {
+            for (int k0 = 0; k0 < BT; k0 += 4) {
+#pragma unroll
+                for (int k = 0; k < TPW; ++k) {
+                    const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
+                    aq[k] = mma16(Pm[(rb * 16 + li) * PPI + k0 + lk], Um[(k0 + lk) * SP + cb * 16 + li], aq[k]);
+                }
+            }
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
-                aq[k] = mma16(Pm[(rb * 16 + li) * PPI + k0 + lk], Um[(k0 + lk) * SP + cb * 16 + li], aq[k]);
-            }
-        }
 #pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = rb * 16 + 4 * lk + r;
-                if (tt < n)
-                    p.out[((size_t)(t0 + tt) * p.H_v + hv) * DV + col0 + cb * 16 + li] = f32_to_bf16_rne(aq[k][r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int tt = rb * 16 + 4 * lk + r;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(aq[k][r]), rO,
+                                                          (uint32_t)(tt * p.H_v * DV + cb * 16 + li) * 2u, 0, 0);
+                }
             }
         }
 
@@ -599,6 +675,15 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     }
 }
 
+template <int DK, int DV, int DVS>
+hipError_t launch_inter(const TwoPassParams &tp, long long heads, hipStream_t stream)
+{
+    TwoPassParams q = tp;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&tp_inter_kernel<DK, DV, DVS>),
+                           dim3((unsigned)(heads * (DV / DVS))), dim3(NT), args, 0, stream);
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
 {
@@ -615,21 +700,18 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
                         dim3(NT), args, 0, stream);
     if (e != hipSuccess)
         return e;
-    // column slices: enough workgroups for the compute units, slices of 32 columns or more
+    // column slices: double them until the walk has 256 workgroups or the
+    // slices are 16 columns wide
     const long long heads = (long long)p.B * p.H_v;
-    const void *k2;
-    long long nsl;
-    if (heads >= 256 || DV / 2 < 32) {
-        k2 = reinterpret_cast<const void *>(&tp_inter_kernel<DK, DV, DV>);
-        nsl = 1;
-    } else if (heads * 2 >= 256 || DV / 4 < 32) {
-        k2 = reinterpret_cast<const void *>(&tp_inter_kernel<DK, DV, (DV / 2 >= 32 ? DV / 2 : 32)>);
-        nsl = 2;
-    } else {
-        k2 = reinterpret_cast<const void *>(&tp_inter_kernel<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>);
-        nsl = 4;
+    int nsl = 1;
+    while (nsl < DV / 16 && heads * nsl < 256)
+        nsl *= 2;
+    switch (nsl) {
+    case 1: return launch_inter<DK, DV, DV>(tp, heads, stream);
+    case 2: return launch_inter<DK, DV, DV / 2>(tp, heads, stream);
+    case 4: return launch_inter<DK, DV, DV / 4>(tp, heads, stream);
+    default: return launch_inter<DK, DV, (DV / 8 >= 16 ? DV / 8 : 16)>(tp, heads, stream);
     }
-    return hipLaunchKernel(k2, dim3((unsigned)(heads * nsl)), dim3(NT), args, 0, stream);
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
