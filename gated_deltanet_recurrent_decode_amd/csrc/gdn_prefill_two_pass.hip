@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
 
     __shared__ __align__(16) float Qs[BT * KP];
     __shared__ __align__(16) float Ks[BT * KP];
-    __shared__ __align__(16) float Vs[BT * VP];
+    __shared__ __align__(16) float Vs[BT * (VP > KP ? VP : KP)]; // V, then W
     __shared__ float Am[BT * AP];
     __shared__ float Pm[BT * AP];
     __shared__ float Tm[BT * AP];
@@ -136,7 +136,9 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
     const int hv = blockIdx.y;
     const int hk = hv / p.G;
     const int32_t *cs = tp.ws.chunk_start;
-    if (gidx >= cs[p.B])
+    // chunks past the workspace's capacity exist only when ranges overlap,
+    // which the contract excludes; they are skipped rather than written out of bounds
+    if (gidx >= cs[p.B] || gidx >= tp.ws.nchunk)
         return;
     // the sequence owning chunk gidx: the last b with chunk_start[b] <= gidx
     // (sequences with no chunks share their start with the next one)
@@ -156,7 +158,6 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
     const int t0 = t_begin + c * BT;
     const int n = L - c * BT < BT ? L - c * BT : BT;
     const int C = p.C;
-    const size_t T = (size_t)p.total;
 
     // ---- conv lanes: channel pair (e, e+1) of the q | k | v channels of (hk, hv)
     const bool conv_lane = tid < NPAIR;
@@ -334,8 +335,9 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
     __syncthreads();
 
     // ---- W = T diag(beta e^gamma) K and U~ = T diag(beta) V on the matrix
-    // cores: this wave's column blocks of each, both row blocks; rows of real
-    // tokens go to the workspace (the others are zero by construction)
+    // cores: this wave's column blocks of each, both row blocks.  Rows of
+    // padding tokens come out zero (their rows of A, and beta, are zero).
+    const size_t blk = (size_t)hv * tp.ws.nchunk + gidx;
     {
         constexpr int WCB = DK / 64, UCB = DV / 64;
         v4f wacc[2][WCB], uacc[2][UCB];
@@ -366,38 +368,60 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
                 uacc[1][q] = mma16(at1, bv, uacc[1][q]);
             }
         }
+        // U~ leaves in the accumulator layout it was computed in
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = rb * 16 + 4 * lk + r;
-                if (tt < n) {
-                    const size_t row = (size_t)hv * T + t0 + tt;
+            for (int q = 0; q < UCB; ++q)
+                *reinterpret_cast<v4f *>(tp.ws.ud + ((blk * 2 + rb) * (DV / 16) + wv * UCB + q) * 256 + lane * 4) =
+                    uacc[rb][q];
+        __syncthreads(); // every read of V is done: W goes over it
 #pragma unroll
-                    for (int q = 0; q < WCB; ++q)
-                        tp.ws.ww[row * DK + (wv * WCB + q) * 16 + li] = wacc[rb][q][r];
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                    for (int q = 0; q < UCB; ++q)
-                        tp.ws.ut[row * DV + (wv * UCB + q) * 16 + li] = uacc[rb][q][r];
-                }
-            }
+            for (int q = 0; q < WCB; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Vs[(rb * 16 + 4 * lk + r) * KP + (wv * WCB + q) * 16 + li] = wacc[rb][q][r];
     }
+    __syncthreads();
 
-    // ---- Q~, K~, the rows of P and e^gamma_last
-    for (int e2 = tid; e2 < n * (DK / 4); e2 += NT) {
-        const int tt = e2 / (DK / 4), i4 = e2 % (DK / 4);
-        const size_t row = (size_t)hv * T + t0 + tt;
-        const v4f qv = *reinterpret_cast<const v4f *>(&Qs[tt * KP + 4 * i4]);
-        const v4f kv = *reinterpret_cast<const v4f *>(&Ks[tt * KP + 4 * i4]);
-        *reinterpret_cast<v4f *>(tp.ws.qt + row * DK + 4 * i4) = qv * eg[tt];
-        *reinterpret_cast<v4f *>(tp.ws.kt + row * DK + 4 * i4) = kv * egl[tt];
+    // ---- Q~, W, K~ and P in the order the second pass feeds them to the
+    // matrix cores (one float4 per lane and four k-slices)
+    const float *Ws = Vs;
+    for (int idx = tid; idx < 2 * (DK / 16) * 64; idx += NT) {
+        const int l = idx & 63, m4 = (idx >> 6) % (DK / 16), rb = idx / (64 * (DK / 16));
+        const int row = rb * 16 + (l & 15);
+        v4f qv, wv4;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int col = 4 * (4 * m4 + e4) + (l >> 4);
+            qv[e4] = Qs[row * KP + col] * eg[row];
+            wv4[e4] = Ws[row * KP + col];
+        }
+        *reinterpret_cast<v4f *>(tp.ws.qa + blk * (BT * DK) + (size_t)idx * 4) = qv;
+        *reinterpret_cast<v4f *>(tp.ws.wa + blk * (BT * DK) + (size_t)idx * 4) = wv4;
     }
-    for (int e2 = tid; e2 < n * BT; e2 += NT) {
-        const int tt = e2 / BT, ss = e2 % BT;
-        tp.ws.pp[((size_t)hv * T + t0 + tt) * BT + ss] = Pm[tt * AP + ss];
+    for (int idx = tid; idx < (DK / 16) * 2 * 64; idx += NT) {
+        const int l = idx & 63, m4 = (idx >> 6) & 1, ib = idx >> 7;
+        v4f kv;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int tt = 4 * (4 * m4 + e4) + (l >> 4);
+            kv[e4] = Ks[tt * KP + ib * 16 + (l & 15)] * egl[tt];
+        }
+        *reinterpret_cast<v4f *>(tp.ws.ka + blk * (BT * DK) + (size_t)idx * 4) = kv;
+    }
+    {
+        const int idx = tid, l = idx & 63, m4 = (idx >> 6) & 1, rb = idx >> 7; // 256 float4: one a thread
+        v4f pv;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+            pv[e4] = Pm[(rb * 16 + (l & 15)) * AP + 4 * (4 * m4 + e4) + (l >> 4)];
+        *reinterpret_cast<v4f *>(tp.ws.pa + blk * (BT * BT) + (size_t)idx * 4) = pv;
     }
     if (tid == 0)
-        tp.ws.el[(size_t)hv * T + t0] = eg[BT - 1]; // padding tokens carry g = 0
+        tp.ws.el[blk] = eg[BT - 1]; // padding tokens carry g = 0
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -407,28 +431,19 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
 {
     const PrefillParams &p = tp.p;
     constexpr int NSL = DV / DVS;
-    constexpr int KP = DK + 4;                                  // W, Q~: A operands read along a row
-    constexpr int K2P = DK + 16;                                // K~: the S update's A operand, read down a column
     constexpr int SP = DVS + ((DVS + 16) % 32 == 16 ? 16 : 32); // S and U: B operands, read down a column
-    constexpr int PPI = BT + 4;                                 // P: A operand read along a row
     constexpr int CBS = DVS / 16;                               // column blocks of the slice
-    // output tiles (row block, column block) of W S0, Q~ S0 and O a wave takes;
-    // a 16-column slice has two, so waves 0-1 take W S0 and waves 2-3 Q~ S0 and O
+    // Output tiles of W S0, Q~ S0 and O: wave w takes row block w & 1 and, of
+    // a slice of two or more column blocks, half of them; a 16-column slice
+    // has one column block, so there waves 0-1 take W S0 and waves 2-3 Q~ S0.
     constexpr bool SPLIT = CBS == 1;
-    constexpr int TPW = SPLIT ? 1 : 2 * CBS / 4;
-    constexpr int RBW = DK / 16 / 4;                            // row blocks of S a wave updates
-    constexpr int NW4 = BT * DK / 4 / NT;                       // float4 a thread stages of W, Q~, K~
-    constexpr int NU4E = BT * DVS / 4;                          // float4 of U~ a chunk
-    constexpr int NU4 = (NU4E + NT - 1) / NT;                   // ... a thread
-    constexpr int NP4 = BT * BT / 4 / NT;                       // ... of P
-    static_assert(NW4 >= 1 && NP4 == 1 && DVS >= 16, "slices of 16 columns or more");
+    constexpr int CBW = SPLIT ? 1 : CBS / 2;
+    constexpr int NA4 = DK / 16;  // float4 a lane holds of one A-operand tile over k = d_k
+    constexpr int RBW = DK / 64;  // row blocks of S a wave updates
+    constexpr int CHUNK_QK = BT * DK, CHUNK_P = BT * BT, CHUNK_U = BT * DV;
 
     __shared__ __align__(16) float S[DK * SP];
-    __shared__ __align__(16) float Wm[BT * KP];
-    __shared__ __align__(16) float Qm[BT * KP];
-    __shared__ __align__(16) float Km[BT * K2P];
     __shared__ __align__(16) float Um[BT * SP];
-    __shared__ __align__(16) float Pm[BT * PPI];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
@@ -453,8 +468,17 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     }
     if (t_end == t_begin)
         return;
-    const size_t T = (size_t)p.total;
+    const int nchunks = (t_end - t_begin + BT - 1) / BT;
+    const int cs_b = __builtin_amdgcn_readfirstlane(tp.ws.chunk_start[b]);
+    if (cs_b < 0 || (long long)cs_b + nchunks > tp.ws.nchunk)
+        return; // only with overlapping ranges (excluded by the contract): touch nothing
+    const size_t blk0 = (size_t)hv * tp.ws.nchunk + (size_t)cs_b;
     float *tile = p.state + ((size_t)s * p.H_v + hv) * (size_t)(DK * DV);
+
+    const int rb = wv & 1;
+    const int cb0 = SPLIT ? 0 : (wv >> 1) * CBW;
+    const bool takes_w = !SPLIT || wv < 2;
+    const bool takes_q = !SPLIT || wv >= 2;
 
     // ---- the state's column slice -> LDS (16-byte streaming loads)
     for (int e = tid; e < DK * DVS / 4; e += NT) {
@@ -463,146 +487,123 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
         *reinterpret_cast<v4f *>(&S[i * SP + 4 * j4]) = v;
     }
 
-    // ---- a chunk's pass-1 results, staged in registers one chunk ahead.  The
-    // loads are buffer loads over the chunk's real rows only (rows past the
-    // prompt's end, or a chunk past it, read zeros without touching memory),
-    // so the walk has no branch around a memory access and every wait in it
-    // covers exactly the loads it needs, not the read-out stores in flight.
-    v4f rw[NW4], rq[NW4], rk[NW4], ru[NU4], rp[NP4];
-    float rel = 0.f;
-    auto prefetch = [&](int c0) {
-        c0 = __builtin_amdgcn_readfirstlane(c0);
-        int nn = t_end - c0;
-        nn = nn < 0 ? 0 : (nn > BT ? BT : nn);
-        const size_t row0 = (size_t)hv * T + (size_t)c0;
-        const __amdgpu_buffer_rsrc_t rW = buf_rsrc(tp.ws.ww + row0 * DK, (uint32_t)(nn * DK * 4));
-        const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(tp.ws.qt + row0 * DK, (uint32_t)(nn * DK * 4));
-        const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.kt + row0 * DK, (uint32_t)(nn * DK * 4));
+    // ---- this wave's operands of a chunk, loaded one chunk ahead straight
+    // into registers (pass 1 wrote them in operand order).  Buffer loads over
+    // resources sized to what the wave needs, zero-sized past the last chunk,
+    // so the walk has no branch around a memory access.
+    v4f xw[NA4], xq[NA4], xk[RBW][2], xp[2], xu[CBW];
+    float xel = 0.f;
+    auto prefetch = [&](int c) {
+        const bool real = c < nchunks;
+        const size_t blk = blk0 + (size_t)(real ? c : 0);
+        const __amdgpu_buffer_rsrc_t rW =
+            buf_rsrc(tp.ws.wa + blk * CHUNK_QK + rb * NA4 * 256, (real && takes_w) ? NA4 * 1024u : 0u);
+        const __amdgpu_buffer_rsrc_t rQ =
+            buf_rsrc(tp.ws.qa + blk * CHUNK_QK + rb * NA4 * 256, (real && takes_q) ? NA4 * 1024u : 0u);
+        const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.ka + blk * CHUNK_QK + wv * RBW * 512, real ? RBW * 2048u : 0u);
+        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P + rb * 512, (real && takes_q) ? 2048u : 0u);
         const __amdgpu_buffer_rsrc_t rU =
-            buf_rsrc(tp.ws.ut + row0 * DV + col0, nn > 0 ? (uint32_t)(((nn - 1) * DV + DVS) * 4) : 0u);
-        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pp + row0 * BT, (uint32_t)(nn * BT * 4));
+            buf_rsrc(tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16 + cb0) * 256,
+                     (real && takes_w) ? CBW * 1024u : 0u);
 #pragma unroll
-        for (int m = 0; m < NW4; ++m) {
-            const int e4 = tid + NT * m, tt = e4 / (DK / 4), i4 = e4 % (DK / 4);
-            const uint32_t off = (uint32_t)(tt * DK + 4 * i4) * 4u;
-            rw[m] = buf_load4(rW, off);
-            rq[m] = buf_load4(rQ, off);
-            rk[m] = buf_load4(rK, off);
+        for (int m4 = 0; m4 < NA4; ++m4) {
+            xw[m4] = buf_load4(rW, (uint32_t)(m4 * 64 + lane) * 16u);
+            xq[m4] = buf_load4(rQ, (uint32_t)(m4 * 64 + lane) * 16u);
         }
 #pragma unroll
-        for (int m = 0; m < NU4; ++m) {
-            const int e4 = tid + NT * m, tt = e4 / (DVS / 4), j4 = e4 % (DVS / 4);
-            ru[m] = buf_load4(rU, e4 < NU4E ? (uint32_t)(tt * DV + 4 * j4) * 4u : kOOB);
-        }
+        for (int q = 0; q < RBW; ++q)
 #pragma unroll
-        for (int m = 0; m < NP4; ++m) {
-            const int e4 = tid + NT * m, tt = e4 / (BT / 4), s4 = e4 % (BT / 4);
-            rp[m] = buf_load4(rP, (uint32_t)(tt * BT + 4 * s4) * 4u);
-        }
-        rel = tp.ws.el[(size_t)hv * T + (size_t)__builtin_amdgcn_readfirstlane(c0 < t_end ? c0 : t_end - 1)];
+            for (int m4 = 0; m4 < 2; ++m4)
+                xk[q][m4] = buf_load4(rK, (uint32_t)((q * 2 + m4) * 64 + lane) * 16u);
+#pragma unroll
+        for (int m4 = 0; m4 < 2; ++m4)
+            xp[m4] = buf_load4(rP, (uint32_t)(m4 * 64 + lane) * 16u);
+#pragma unroll
+        for (int q = 0; q < CBW; ++q)
+            xu[q] = buf_load4(rU, (uint32_t)(q * 64 + lane) * 16u);
+        xel = tp.ws.el[blk];
     };
-    prefetch(t_begin);
+    prefetch(0);
+    __syncthreads(); // the state is in LDS
 
-    for (int t0 = t_begin; t0 < t_end; t0 += BT) {
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = t_begin + c * BT;
         const int n = t_end - t0 < BT ? t_end - t0 : BT;
-        const float el = rel;
+        v4f aw_op[NA4], aq_op[NA4], ak_op[RBW][2], ap_op[2], au[CBW];
 #pragma unroll
-        for (int m = 0; m < NW4; ++m) {
-            const int e4 = tid + NT * m, tt = e4 / (DK / 4), i4 = e4 % (DK / 4);
-            *reinterpret_cast<v4f *>(&Wm[tt * KP + 4 * i4]) = rw[m];
-            *reinterpret_cast<v4f *>(&Qm[tt * KP + 4 * i4]) = rq[m];
-            *reinterpret_cast<v4f *>(&Km[tt * K2P + 4 * i4]) = rk[m];
+        for (int m4 = 0; m4 < NA4; ++m4) {
+            aw_op[m4] = xw[m4];
+            aq_op[m4] = xq[m4];
         }
 #pragma unroll
-        for (int m = 0; m < NU4; ++m) {
-            const int e4 = tid + NT * m, tt = e4 / (DVS / 4), j4 = e4 % (DVS / 4);
-            if (e4 < NU4E)
-                *reinterpret_cast<v4f *>(&Um[tt * SP + 4 * j4]) = ru[m];
+        for (int q = 0; q < RBW; ++q) {
+            ak_op[q][0] = xk[q][0];
+            ak_op[q][1] = xk[q][1];
         }
+        ap_op[0] = xp[0];
+        ap_op[1] = xp[1];
 #pragma unroll
-        for (int m = 0; m < NP4; ++m) {
-            const int e4 = tid + NT * m, tt = e4 / (BT / 4), s4 = e4 % (BT / 4);
-            *reinterpret_cast<v4f *>(&Pm[tt * PPI + 4 * s4]) = rp[m];
-        }
-        __syncthreads(); // the chunk is staged (and the previous chunk's S update is in)
-        prefetch(t0 + BT);
+        for (int q = 0; q < CBW; ++q)
+            au[q] = xu[q];
+        const float el = xel;
+        prefetch(c + 1);
         // the read-out rows of the chunk's real tokens; later rows fall outside
         const int t0u = __builtin_amdgcn_readfirstlane(t0), nu = __builtin_amdgcn_readfirstlane(n);
         const __amdgpu_buffer_rsrc_t rO = buf_rsrc(p.out + ((size_t)t0u * p.H_v + hv) * DV + col0,
                                                    (uint32_t)(((nu - 1) * p.H_v * DV + DVS) * 2));
 
-        if constexpr (SPLIT) {
-            // ---- waves 0-1: W S0 and U = U~ - W S0 on row block wv; waves 2-3:
-            // Q~ S0 on row block wv - 2, then O = Q~ S0 + P U -> out
-            const int rb = wv & 1;
-            const bool is_w = wv < 2;
-            const float *Asrc = is_w ? Wm : Qm;
-            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int k0 = 0; k0 < DK; k0 += 4)
-                acc = mma16(Asrc[(rb * 16 + li) * KP + k0 + lk], S[(k0 + lk) * SP + li], acc);
-            if (is_w) {
+        // ---- W S0 and Q~ S0 on this wave's tiles (row block rb)
+        v4f aw[CBW], aq[CBW];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Um[(rb * 16 + 4 * lk + r) * SP + li] -= acc[r];
-            }
-            __syncthreads(); // U complete; every read of S0 for this chunk is done
-            if (!is_w) {
+        for (int q = 0; q < CBW; ++q)
+            aw[q] = aq[q] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k0 = 0; k0 < BT; k0 += 4)
-                    acc = mma16(Pm[(rb * 16 + li) * PPI + k0 + lk], Um[(k0 + lk) * SP + li], acc);
+        for (int m4 = 0; m4 < NA4; ++m4)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tt = rb * 16 + 4 * lk + r;
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[r]), rO,
-                                                          (uint32_t)(tt * p.H_v * DV + li) * 2u, 0, 0);
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int k0 = 4 * (4 * m4 + e4);
+#pragma unroll
+                for (int q = 0; q < CBW; ++q) {
+                    const float bs = S[(k0 + lk) * SP + (cb0 + q) * 16 + li];
+                    if constexpr (SPLIT) {
+                        // one accumulator: W S0 on waves 0-1, Q~ S0 on waves 2-3
+                        aw[q] = mma16(takes_w ? aw_op[m4][e4] : aq_op[m4][e4], bs, aw[q]);
+                    } else {
+                        aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
+                        aq[q] = mma16(aq_op[m4][e4], bs, aq[q]);
+                    }
                 }
             }
-        } else {
-            // ---- W S0 and Q~ S0 on this wave's output tiles
-            v4f aw[TPW], aq[TPW];
+        if constexpr (SPLIT)
+            aq[0] = aw[0];
+        // U = U~ - W S0 on the same tiles -> LDS
+        if (takes_w) {
 #pragma unroll
-            for (int k = 0; k < TPW; ++k)
-                aw[k] = aq[k] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int k0 = 0; k0 < DK; k0 += 4) {
-#pragma unroll
-                for (int k = 0; k < TPW; ++k) {
-                    const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
-                    const float bs = S[(k0 + lk) * SP + cb * 16 + li];
-                    aw[k] = mma16(Wm[(rb * 16 + li) * KP + k0 + lk], bs, aw[k]);
-                    aq[k] = mma16(Qm[(rb * 16 + li) * KP + k0 + lk], bs, aq[k]);
-                }
-            }
-            // U = U~ - W S0 over the same tiles (a wave reads and writes only its own)
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
+            for (int q = 0; q < CBW; ++q)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Um[(rb * 16 + 4 * lk + r) * SP + cb * 16 + li] -= aw[k][r];
-            }
-            __syncthreads(); // U complete; every read of S0 for this chunk is done
+                    Um[(rb * 16 + 4 * lk + r) * SP + (cb0 + q) * 16 + li] = au[q][r] - aw[q][r];
+        }
+        __syncthreads(); // U complete; every read of S0 for this chunk is done
 
-            // ---- O = Q~ S0 + P U -> out (rows of real tokens)
+        // ---- O = Q~ S0 + P U -> out
+        if (takes_q) {
 #pragma unroll
-            for (int k0 = 0; k0 < BT; k0 += 4) {
+            for (int m4 = 0; m4 < 2; ++m4)
 #pragma unroll
-                for (int k = 0; k < TPW; ++k) {
-                    const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
-                    aq[k] = mma16(Pm[(rb * 16 + li) * PPI + k0 + lk], Um[(k0 + lk) * SP + cb * 16 + li], aq[k]);
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int k0 = 4 * (4 * m4 + e4);
+#pragma unroll
+                    for (int q = 0; q < CBW; ++q)
+                        aq[q] = mma16(ap_op[m4][e4], Um[(k0 + lk) * SP + (cb0 + q) * 16 + li], aq[q]);
                 }
-            }
 #pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int ti = wv * TPW + k, rb = ti & 1, cb = ti >> 1;
+            for (int q = 0; q < CBW; ++q)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tt = rb * 16 + 4 * lk + r;
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(aq[k][r]), rO,
-                                                          (uint32_t)(tt * p.H_v * DV + cb * 16 + li) * 2u, 0, 0);
-                }
-            }
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        f32_to_bf16_rne(aq[q][r]), rO,
+                        (uint32_t)((rb * 16 + 4 * lk + r) * p.H_v * DV + (cb0 + q) * 16 + li) * 2u, 0, 0);
         }
 
         // ---- S1 = e^gamma_last S0 + K~^T U: this wave's row blocks, the slice's column blocks
@@ -616,15 +617,16 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
                     for (int r = 0; r < 4; ++r)
                         sacc[q][jb][r] = el * S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li];
 #pragma unroll
-            for (int k0 = 0; k0 < BT; k0 += 4) {
+            for (int m4 = 0; m4 < 2; ++m4)
 #pragma unroll
-                for (int q = 0; q < RBW; ++q) {
-                    const float a = Km[(k0 + lk) * K2P + (wv * RBW + q) * 16 + li];
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int k0 = 4 * (4 * m4 + e4);
 #pragma unroll
-                    for (int jb = 0; jb < CBS; ++jb)
-                        sacc[q][jb] = mma16(a, Um[(k0 + lk) * SP + jb * 16 + li], sacc[q][jb]);
+                    for (int q = 0; q < RBW; ++q)
+#pragma unroll
+                        for (int jb = 0; jb < CBS; ++jb)
+                            sacc[q][jb] = mma16(ak_op[q][m4][e4], Um[(k0 + lk) * SP + jb * 16 + li], sacc[q][jb]);
                 }
-            }
 #pragma unroll
             for (int q = 0; q < RBW; ++q)
 #pragma unroll
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
                     for (int r = 0; r < 4; ++r)
                         S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li] = sacc[q][jb][r];
         }
-        __syncthreads(); // S, U and the staging buffers are free for the next chunk
+        __syncthreads(); // S and U are free for the next chunk
     }
 
     // ---- the state's slice back to the slot
@@ -720,31 +722,35 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t two_pass_layout(int B, int total, int H_v, int d_k, int d_v, void *base, TwoPassWorkspace *ws)
 {
-    const size_t rows = (size_t)H_v * (size_t)total;
+    // chunk blocks per head: an upper bound on the call's chunk count (each
+    // sequence adds at most one partial chunk)
+    const size_t nchunk = ((size_t)total + BT - 1) / BT + (size_t)B;
+    const size_t blocks = (size_t)H_v * nchunk;
     size_t off = 0;
     const size_t o_cs = off;
     off = round_up(off + (size_t)(B + 1) * sizeof(int32_t));
-    const size_t o_qt = off;
-    off = round_up(off + rows * d_k * sizeof(float));
-    const size_t o_kt = off;
-    off = round_up(off + rows * d_k * sizeof(float));
-    const size_t o_ww = off;
-    off = round_up(off + rows * d_k * sizeof(float));
-    const size_t o_ut = off;
-    off = round_up(off + rows * d_v * sizeof(float));
-    const size_t o_pp = off;
-    off = round_up(off + rows * BT * sizeof(float));
+    const size_t o_qa = off;
+    off = round_up(off + blocks * BT * d_k * sizeof(float));
+    const size_t o_wa = off;
+    off = round_up(off + blocks * BT * d_k * sizeof(float));
+    const size_t o_ka = off;
+    off = round_up(off + blocks * BT * d_k * sizeof(float));
+    const size_t o_pa = off;
+    off = round_up(off + blocks * BT * BT * sizeof(float));
+    const size_t o_ud = off;
+    off = round_up(off + blocks * BT * d_v * sizeof(float));
     const size_t o_el = off;
-    off = round_up(off + rows * sizeof(float));
+    off = round_up(off + blocks * sizeof(float));
     if (base && ws) {
         char *c = static_cast<char *>(base);
         ws->chunk_start = reinterpret_cast<int32_t *>(c + o_cs);
-        ws->qt = reinterpret_cast<float *>(c + o_qt);
-        ws->kt = reinterpret_cast<float *>(c + o_kt);
-        ws->ww = reinterpret_cast<float *>(c + o_ww);
-        ws->ut = reinterpret_cast<float *>(c + o_ut);
-        ws->pp = reinterpret_cast<float *>(c + o_pp);
+        ws->qa = reinterpret_cast<float *>(c + o_qa);
+        ws->wa = reinterpret_cast<float *>(c + o_wa);
+        ws->ka = reinterpret_cast<float *>(c + o_ka);
+        ws->pa = reinterpret_cast<float *>(c + o_pa);
+        ws->ud = reinterpret_cast<float *>(c + o_ud);
         ws->el = reinterpret_cast<float *>(c + o_el);
+        ws->nchunk = (int)nchunk;
     }
     return off;
 }

@@ -27,13 +27,26 @@ struct PrefillParams {
 hipError_t launch_gdn_prefill(const PrefillParams &p, int d_k, int d_v, hipStream_t stream);
 
 // The two-pass prefill: its workspace, carved by two_pass_layout from one
-// caller buffer.  Per value head hv and packed token t (row hv * total + t):
-// q~ = e^gamma q^ [d_k], k~ = e^(gamma_last - gamma) k^ [d_k],
-// w = ((I + A)^-1 diag(beta e^gamma) K)[t] [d_k], u~ = ((I + A)^-1 diag(beta) V)[t]
-// [d_v], p = P[t] [32], and el = e^gamma_last at the chunk's first token.
+// caller buffer.  Chunks are numbered across the call (sequence b's chunks
+// start at chunk_start[b]); the workspace holds nchunk = ceil(total / 32) + B
+// chunk blocks per value head, block (hv, g) at hv * nchunk + g, each laid out
+// as the second pass's matrix-core operands, so it loads them straight into
+// registers:
+//   qa, wa  [2 row blocks][d_k / 16][64 lanes][4]: q~ = e^gamma q^ and
+//           w = ((I + A)^-1 diag(beta e^gamma) K), element (rb, m, lane) the
+//           A operand of k-slice m: row rb * 16 + lane % 16, column 4 m + lane / 16
+//   ka      [d_k / 16 row blocks][2][64][4]: k~ = e^(gamma_last - gamma) k^ as
+//           the A operand of the state update, element (ib, m, lane) =
+//           k~[4 m + lane / 16][ib * 16 + lane % 16]
+//   pa      [2][2][64][4]: P as an A operand, like qa
+//   ud      [2 row blocks][d_v / 16 column blocks][64][4]: u~ = ((I + A)^-1
+//           diag(beta) V) in the accumulator layout, lane j + 16 g holding rows
+//           4 g .. 4 g + 3 of column j
+//   el      e^gamma_last of the chunk
 struct TwoPassWorkspace {
     int32_t *chunk_start; // [B+1]: exclusive scan of each sequence's chunk count
-    float *qt, *kt, *ww, *ut, *pp, *el;
+    float *qa, *wa, *ka, *pa, *ud, *el;
+    int nchunk;
 };
 
 struct TwoPassParams {
