@@ -619,8 +619,9 @@ def prefill_flops_per_token(H_v: int, d_k: int, d_v: int, chunk: int = 32) -> fl
 
 def run_prefill(args) -> dict:
     """Packed prompts of --prefill-len tokens, --rows of them per call, at the 0.8B-like
-    layer's shapes, in place; two sets of slots alternate.  Times the prefill kernel with
-    fence-free HIP events around every launch."""
+    layer's shapes, in place; two sets of slots alternate.  Times each call (the two-pass
+    form's three launches, or with --one-kernel the single prefill kernel) with fence-free
+    HIP events around it; the workspace is allocated before the timed region."""
     import torch
 
     import gated_deltanet_recurrent_decode_amd as gdn
@@ -644,7 +645,7 @@ def run_prefill(args) -> dict:
                          out=torch.empty((nseq * L, s.H_v, s.d_v), dtype=torch.bfloat16, device="cuda")))
 
     ws = None
-    if args.two_pass:
+    if not args.one_kernel:
         ws = torch.empty((gdn.gdn_prefill_two_pass_workspace_bytes(nseq, nseq * L, s.H_k, s.H_v, s.d_k, s.d_v),),
                          dtype=torch.uint8, device="cuda")
 
@@ -714,7 +715,8 @@ def main() -> int:
                          "--layers layers (twin), or slot copy and reset of --rows slots a call")
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--prefill-len", type=int, default=512)
-    ap.add_argument("--two-pass", action="store_true", help="prefill through gdn_prefill_two_pass")
+    ap.add_argument("--one-kernel", action="store_true",
+                    help="prefill through gdn_prefill (one kernel, no workspace) instead of gdn_prefill_two_pass")
     ap.add_argument("--tokens", type=int, default=1, help="tokens a row (in place and tokens mode)")
     ap.add_argument("--real", type=int, default=None,
                     help="a padded bucket: only the first REAL of the --rows rows are real, the rest point at the "
