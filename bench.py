@@ -50,8 +50,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "85fecd8614450f43d92ae0523c1ea97165c64bd30b9e44ebbd1daec033031fb4",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 141_827_698}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "acc6ab4fc9a51c7da1642106e6d5f9dd1478c1b47f1f6023b6afc9adff41709b",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 141_828_160}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 
