@@ -489,38 +489,57 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
 
     // ---- this wave's operands of a chunk, loaded one chunk ahead straight
     // into registers (pass 1 wrote them in operand order).  Buffer loads over
-    // resources sized to what the wave needs, zero-sized past the last chunk,
-    // so the walk has no branch around a memory access.
+    // resources sized to the real rows, zero-sized past the last chunk, so the
+    // walk has no branch around a memory access.  A wave loads only what it
+    // uses: every load, even an empty one, takes the compute unit's address
+    // path (about 16 cycles for a 1 KiB wave load, shared by the four waves),
+    // so with 16-column slices a wave fetches one A tile (W on waves 0-1, Q~ on
+    // waves 2-3) and one of P or U~.
+    constexpr int NLOAD = SPLIT ? NA4 + 2 * RBW + 2 : 2 * NA4 + 2 * RBW + 2 + CBW; // loads a wave issues a chunk
     v4f xw[NA4], xq[NA4], xk[RBW][2], xp[2], xu[CBW];
     float xel = 0.f;
     auto prefetch = [&](int c) {
         const bool real = c < nchunks;
         const size_t blk = blk0 + (size_t)(real ? c : 0);
-        const __amdgpu_buffer_rsrc_t rW =
-            buf_rsrc(tp.ws.wa + blk * CHUNK_QK + rb * NA4 * 256, (real && takes_w) ? NA4 * 1024u : 0u);
-        const __amdgpu_buffer_rsrc_t rQ =
-            buf_rsrc(tp.ws.qa + blk * CHUNK_QK + rb * NA4 * 256, (real && takes_q) ? NA4 * 1024u : 0u);
         const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.ka + blk * CHUNK_QK + wv * RBW * 512, real ? RBW * 2048u : 0u);
-        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P + rb * 512, (real && takes_q) ? 2048u : 0u);
-        const __amdgpu_buffer_rsrc_t rU =
-            buf_rsrc(tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16 + cb0) * 256,
-                     (real && takes_w) ? CBW * 1024u : 0u);
+        if constexpr (SPLIT) {
+            const __amdgpu_buffer_rsrc_t rA =
+                buf_rsrc((takes_w ? tp.ws.wa : tp.ws.qa) + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
+            const __amdgpu_buffer_rsrc_t rX =
+                buf_rsrc(takes_q ? tp.ws.pa + blk * CHUNK_P + rb * 512
+                                 : tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16) * 256,
+                         real ? (takes_q ? 2048u : 1024u) : 0u);
 #pragma unroll
-        for (int m4 = 0; m4 < NA4; ++m4) {
-            xw[m4] = buf_load4(rW, (uint32_t)(m4 * 64 + lane) * 16u);
-            xq[m4] = buf_load4(rQ, (uint32_t)(m4 * 64 + lane) * 16u);
+            for (int m4 = 0; m4 < NA4; ++m4)
+                xw[m4] = buf_load4(rA, (uint32_t)(m4 * 64 + lane) * 16u);
+#pragma unroll
+            for (int m4 = 0; m4 < 2; ++m4)
+                xp[m4] = buf_load4(rX, (uint32_t)(m4 * 64 + lane) * 16u); // P, or U~ in the first
+        } else {
+            const __amdgpu_buffer_rsrc_t rW =
+                buf_rsrc(tp.ws.wa + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
+            const __amdgpu_buffer_rsrc_t rQ =
+                buf_rsrc(tp.ws.qa + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
+            const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P + rb * 512, real ? 2048u : 0u);
+            const __amdgpu_buffer_rsrc_t rU =
+                buf_rsrc(tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16 + cb0) * 256, real ? CBW * 1024u : 0u);
+#pragma unroll
+            for (int m4 = 0; m4 < NA4; ++m4) {
+                xw[m4] = buf_load4(rW, (uint32_t)(m4 * 64 + lane) * 16u);
+                xq[m4] = buf_load4(rQ, (uint32_t)(m4 * 64 + lane) * 16u);
+            }
+#pragma unroll
+            for (int m4 = 0; m4 < 2; ++m4)
+                xp[m4] = buf_load4(rP, (uint32_t)(m4 * 64 + lane) * 16u);
+#pragma unroll
+            for (int q = 0; q < CBW; ++q)
+                xu[q] = buf_load4(rU, (uint32_t)(q * 64 + lane) * 16u);
         }
 #pragma unroll
         for (int q = 0; q < RBW; ++q)
 #pragma unroll
             for (int m4 = 0; m4 < 2; ++m4)
                 xk[q][m4] = buf_load4(rK, (uint32_t)((q * 2 + m4) * 64 + lane) * 16u);
-#pragma unroll
-        for (int m4 = 0; m4 < 2; ++m4)
-            xp[m4] = buf_load4(rP, (uint32_t)(m4 * 64 + lane) * 16u);
-#pragma unroll
-        for (int q = 0; q < CBW; ++q)
-            xu[q] = buf_load4(rU, (uint32_t)(q * 64 + lane) * 16u);
         xel = tp.ws.el[blk];
     };
     prefetch(0);
@@ -533,7 +552,7 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
 #pragma unroll
         for (int m4 = 0; m4 < NA4; ++m4) {
             aw_op[m4] = xw[m4];
-            aq_op[m4] = xq[m4];
+            aq_op[m4] = SPLIT ? xw[m4] : xq[m4];
         }
 #pragma unroll
         for (int q = 0; q < RBW; ++q) {
@@ -544,7 +563,7 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
         ap_op[1] = xp[1];
 #pragma unroll
         for (int q = 0; q < CBW; ++q)
-            au[q] = xu[q];
+            au[q] = SPLIT ? xp[0] : xu[q];
         const float el = xel;
         prefetch(c + 1);
         // the read-out rows of the chunk's real tokens; later rows fall outside
@@ -567,13 +586,21 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
                     const float bs = S[(k0 + lk) * SP + (cb0 + q) * 16 + li];
                     if constexpr (SPLIT) {
                         // one accumulator: W S0 on waves 0-1, Q~ S0 on waves 2-3
-                        aw[q] = mma16(takes_w ? aw_op[m4][e4] : aq_op[m4][e4], bs, aw[q]);
+                        // (the A tile the wave loaded)
+                        aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
                     } else {
                         aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
                         aq[q] = mma16(aq_op[m4][e4], bs, aq[q]);
                     }
                 }
             }
+        // interleave the next chunk's loads with these products, so their
+        // address processing runs under the matrix cores instead of in front
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // one vector-memory read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMA
+        }
         if constexpr (SPLIT)
             aq[0] = aw[0];
         // U = U~ - W S0 on the same tiles -> LDS
