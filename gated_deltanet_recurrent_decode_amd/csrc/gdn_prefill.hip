@@ -236,11 +236,14 @@ __global__ __launch_bounds__(256) void gdn_prefill_kernel(PrefillParams p)
                 sq = fmaf(qv, qv, sq);
                 sk = fmaf(kv, kv, sk);
             }
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1) {
-                sq += __shfl_xor(sq, o, 64);
-                sk += __shfl_xor(sk, o, 64);
-            }
+            // the sums over each token's eight lanes: DPP butterflies (same pairs as an
+            // xor shuffle, no LDS round trip)
+            sq += dpp_xor<1>(sq);
+            sk += dpp_xor<1>(sk);
+            sq += dpp_xor<2>(sq);
+            sk += dpp_xor<2>(sk);
+            sq += dpp_xor<4>(sq);
+            sk += dpp_xor<4>(sk);
             if (tt < n) {
                 const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
                 const float rk = 1.0f / sqrtf(sk + p.l2_eps);

@@ -128,6 +128,23 @@ def test_two_pass_long_prompt_and_slices(gdn, torch):
            two_pass=True)
 
 
+@PATHS
+def test_prefill_many_ragged_sequences(gdn, torch, two_pass):
+    """300 sequences (more than one 256-wide tile of the two-pass chunk map,
+    whose scan carries across tiles): lengths 0-70 drawn at random, some on the
+    null slot."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    lengths = [int(v) for v in rng.integers(0, 71, size=300)]
+    lengths[5] = lengths[256] = 0          # empty sequences on each side of the tile edge
+    lengths[255], lengths[257] = 33, 64     # chunk edges next to it
+    pad = tuple(int(b) for b in rng.choice(300, size=12, replace=False))
+    case = gi.prefill(lengths, H_k=1, H_v=2, d=64, pad=pad, seed=78)
+    _, out = _check(gdn, torch, case, two_pass=two_pass)
+    for b in pad:
+        a, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        assert torch.count_nonzero(out[a:e].view(torch.int16)) == 0, "padding sequences read out +0.0"
+
+
 def test_two_pass_agrees_with_one_kernel(gdn, torch):
     """The two paths on the same inputs: within the state bar of each other."""
     t = torch
