@@ -191,3 +191,45 @@ def test_prefill_unusable_ranges_touch_nothing(gdn, torch, two_pass):
         sl = int(case.pool.read_slot[b])
         assert t.equal(dp.state[sl].view(t.int32), before[sl].view(t.int32))
     assert bool((out[10:].float() == 7.0).all()), "rows of unusable sequences stay as they were"
+
+
+def test_two_pass_graph_replay_matches_eager(gdn, torch):
+    """The two-pass prefill (three launches, a caller workspace, no allocation)
+    captured once and replayed several times, with eager work between replays,
+    gives the bits of the same calls run eagerly (each replay continues the
+    prompts from where the previous one left the slots)."""
+    t = torch
+    case = gi.prefill([70, 5, 33], H_k=2, H_v=4, d=128, seed=31)
+    s = case.shape
+    dp_e, dp_g = H.DevPool(case.pool), H.DevPool(case.pool)
+    x, g, beta = H.bf16_dev(case.x), t.from_numpy(case.g).cuda(), t.from_numpy(case.beta).cuda()
+    cu = t.from_numpy(case.cu_seqlens).cuda()
+    nbytes = gdn.gdn_prefill_two_pass_workspace_bytes(s.B, s.T, s.H_k, s.H_v, s.d_k, s.d_v)
+    ws_e = t.empty((nbytes,), dtype=t.uint8, device="cuda")
+    ws_g = t.empty_like(ws_e)
+    out_e = t.empty((s.T, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    out_g = t.empty_like(out_e)
+
+    def run(dp, out, ws):
+        gdn.gdn_prefill_two_pass(x, dp.conv_w, None, dp.conv_state, dp.state, g, beta, cu, dp.rd, out, ws, H_k=s.H_k)
+
+    stream = t.cuda.Stream()
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.stream(stream):
+        run(dp_g, out_g, ws_g)  # warm-up outside capture
+    t.cuda.synchronize()
+    dp_g.state.copy_(t.from_numpy(case.pool.state).cuda())
+    dp_g.conv_state.copy_(H.bf16_dev(case.pool.conv_state))
+    t.cuda.synchronize()
+    with t.cuda.graph(graph, stream=stream):
+        run(dp_g, out_g, ws_g)
+    t.cuda.synchronize()
+    assert t.equal(dp_g.state, t.from_numpy(case.pool.state).cuda()), "capture must not execute"
+    for k in range(4):
+        run(dp_e, out_e, ws_e)
+        graph.replay()
+        t.cuda.synchronize()
+        _ = (dp_e.state.sum() + 1).item()  # eager work between replays
+        assert t.equal(out_g.view(t.int16), out_e.view(t.int16)), f"replay {k}"
+        assert t.equal(dp_g.state.view(t.int32), dp_e.state.view(t.int32)), f"replay {k}"
+        assert t.equal(dp_g.conv_state.view(t.int16), dp_e.conv_state.view(t.int16)), f"replay {k}"
