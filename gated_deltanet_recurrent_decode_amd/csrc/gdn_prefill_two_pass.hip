@@ -111,8 +111,10 @@ __global__ __launch_bounds__(NT) void tp_chunk_map_kernel(TwoPassParams tp)
 
 // ---------------------------------------------------------------- pass 1
 
+// two workgroups a CU (LDS allows two): at most 256 registers a lane, which
+// the compiler meets by recomputing LDS addresses inside the chunk loop
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void tp_intra_kernel(TwoPassParams tp)
 {
     const PrefillParams &p = tp.p;
     constexpr int NPAIR = (2 * DK + DV) / 2; // conv lanes, two channels each
@@ -120,6 +122,7 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
     // row want 4 mod 32, B-style reads down a column 16 mod 32
     constexpr int KP = DK + 4, VP = DV + 16, AP = BT + 1;
     static_assert(NPAIR <= NT, "one conv lane per channel pair");
+    static_assert((2 * (DK / 16) * 64) % NT == 0, "whole store rounds");
 
     __shared__ __align__(16) float Qs[BT * KP];
     __shared__ __align__(16) float Ks[BT * KP];
@@ -132,39 +135,22 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
-    const int gidx = blockIdx.x;
     const int hv = blockIdx.y;
     const int hk = hv / p.G;
+    const int C = p.C;
     const int32_t *cs = tp.ws.chunk_start;
     // chunks past the workspace's capacity exist only when ranges overlap,
     // which the contract excludes; they are skipped rather than written out of bounds
-    if (gidx >= cs[p.B] || gidx >= tp.ws.nchunk)
+    const int nch = __builtin_amdgcn_readfirstlane(cs[p.B] < tp.ws.nchunk ? cs[p.B] : tp.ws.nchunk);
+    if (nch <= 0 || (int)blockIdx.x >= nch)
         return;
-    // the sequence owning chunk gidx: the last b with chunk_start[b] <= gidx
-    // (sequences with no chunks share their start with the next one)
-    int lo = 0, hi = p.B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cs[mid] <= gidx)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const int b = lo;
-    const int c = gidx - cs[b];
-    const int t_begin = p.cu_seqlens[b];
-    const int L = p.cu_seqlens[b + 1] - t_begin;
-    const int s = p.slot[b];
-    const int t0 = t_begin + c * BT;
-    const int n = L - c * BT < BT ? L - c * BT : BT;
-    const int C = p.C;
 
     // ---- conv lanes: channel pair (e, e+1) of the q | k | v channels of (hk, hv)
     const bool conv_lane = tid < NPAIR;
     const int e = conv_lane ? 2 * tid : 0;
     const bool isq = e < DK, isk = !isq && e < 2 * DK;
     const int ch = isq ? hk * DK + e : isk ? p.H_k * DK + hk * DK + (e - DK) : 2 * p.H_k * DK + hv * DV + (e - 2 * DK);
-    float w0[2], w1[2], w2[2], w3[2], bias[2], h0[2], h1[2], h2[2];
+    float w0[2], w1[2], w2[2], w3[2], bias[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint16_t *wc = p.conv_w + (size_t)(ch + h) * 4;
@@ -174,257 +160,308 @@ __global__ __launch_bounds__(NT) void tp_intra_kernel(TwoPassParams tp)
         w3[h] = bf16_to_f32(wc[3]);
         bias[h] = p.conv_b ? bf16_to_f32(p.conv_b[ch + h]) : 0.f;
     }
-    // the three inputs before the chunk (oldest first)
-    uint32_t hist[3];
-    if (c == 0) {
-        const uint16_t *win = p.conv_state + (size_t)s * 3 * C + ch;
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            hist[k] = *reinterpret_cast<const uint32_t *>(win + (size_t)k * C);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            hist[k] = *reinterpret_cast<const uint32_t *>(p.x + (size_t)(t0 - 3 + k) * p.x_row_stride + ch);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        h0[h] = __uint_as_float(h ? hist[0] & 0xffff0000u : hist[0] << 16);
-        h1[h] = __uint_as_float(h ? hist[1] & 0xffff0000u : hist[1] << 16);
-        h2[h] = __uint_as_float(h ? hist[2] & 0xffff0000u : hist[2] << 16);
-    }
-    uint32_t xb[BT];
-#pragma unroll
-    for (int tt = 0; tt < BT; ++tt)
-        xb[tt] = (conv_lane && tt < n) ? *reinterpret_cast<const uint32_t *>(p.x + (size_t)(t0 + tt) * p.x_row_stride + ch)
-                                       : 0u;
-    const float g_in = tid < n ? p.g[(size_t)(t0 + tid) * p.H_v + hv] : 0.f;
-    const float b_in = tid < n ? p.beta[(size_t)(t0 + tid) * p.H_v + hv] : 0.f;
 
-    // ---- conv + SiLU; rows past the chunk's last token stay zero
-    if (conv_lane) {
-        float *ydst = isq ? &Qs[e] : isk ? &Ks[e - DK] : &Vs[e - 2 * DK];
-        const int ypitch = (isq || isk) ? KP : VP;
-        const bool has_bias = p.conv_b != nullptr;
+    // ---- a chunk's inputs: its place, the three inputs before it (from the
+    // slot's window for a prompt's first chunk, else from x), its x rows and
+    // gates.  The workgroup walks chunks blockIdx.x, + gridDim.x, ... and
+    // loads the next one's inputs while it computes the current one; x and the
+    // gates come through buffer resources over the chunk's real rows (later
+    // rows read zeros), so no branch surrounds those loads.
+    struct ChunkIn {
+        uint32_t xb[BT];
+        uint32_t hist[3];
+        float g_in, b_in;
+        int t0, n;
+    };
+    auto load = [&](int gi, ChunkIn &in) {
+        const int gq = __builtin_amdgcn_readfirstlane(gi < nch ? gi : nch - 1); // past the end: a real chunk, unused
+        // the sequence owning chunk gq: the last b with chunk_start[b] <= gq
+        // (sequences with no chunks share their start with the next one)
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cs[mid] <= gq)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int b = lo;
+        const int c = gq - cs[b];
+        const int t_begin = p.cu_seqlens[b];
+        const int L = p.cu_seqlens[b + 1] - t_begin;
+        const int sl = p.slot[b];
+        const int t0 = __builtin_amdgcn_readfirstlane(t_begin + c * BT);
+        const int n = __builtin_amdgcn_readfirstlane(L - c * BT < BT ? L - c * BT : BT);
+        const uint16_t *hb = c == 0 ? p.conv_state + (size_t)sl * 3 * C + ch
+                                    : p.x + (size_t)(t0 - 3) * p.x_row_stride + ch;
+        const size_t hs = c == 0 ? (size_t)C : (size_t)p.x_row_stride;
 #pragma unroll
-        for (int tt = 0; tt < BT; ++tt) {
-            float y0 = 0.f, y1 = 0.f;
-            if (tt < n) {
-                const float x0 = __uint_as_float(xb[tt] << 16), x1 = __uint_as_float(xb[tt] & 0xffff0000u);
-                float acc0 = w0[0] * h0[0];
-                acc0 = fmaf(w1[0], h1[0], acc0);
-                acc0 = fmaf(w2[0], h2[0], acc0);
-                acc0 = fmaf(w3[0], x0, acc0);
-                float acc1 = w0[1] * h0[1];
-                acc1 = fmaf(w1[1], h1[1], acc1);
-                acc1 = fmaf(w2[1], h2[1], acc1);
-                acc1 = fmaf(w3[1], x1, acc1);
-                if (has_bias) {
-                    acc0 += bias[0];
-                    acc1 += bias[1];
+        for (int k = 0; k < 3; ++k)
+            in.hist[k] = *reinterpret_cast<const uint32_t *>(hb + k * hs);
+        const __amdgpu_buffer_rsrc_t rx =
+            buf_rsrc(p.x + (size_t)t0 * p.x_row_stride, (uint32_t)(((n - 1) * p.x_row_stride + C) * 2));
+        // (lanes without a channel pair load the first pair's inputs, unused)
+#pragma unroll
+        for (int tt = 0; tt < BT; ++tt)
+            in.xb[tt] = __builtin_amdgcn_raw_buffer_load_b32(rx, (uint32_t)(tt * p.x_row_stride + ch) * 2u, 0, 0);
+        const __amdgpu_buffer_rsrc_t rg = buf_rsrc(p.g + (size_t)t0 * p.H_v, (uint32_t)(n * p.H_v * 4));
+        const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(p.beta + (size_t)t0 * p.H_v, (uint32_t)(n * p.H_v * 4));
+        const uint32_t goff = (uint32_t)((tid & (BT - 1)) * p.H_v + hv) * 4u; // lanes past BT: unused copies
+        in.g_in = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
+        in.b_in = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_, goff, 0, 0));
+        in.t0 = t0;
+        in.n = n;
+    };
+
+    ChunkIn cur, nxt;
+    load(blockIdx.x, cur);
+    for (int g = blockIdx.x; g < nch; g += gridDim.x) {
+        const int t0 = cur.t0, n = cur.n;
+        float h0[2], h1[2], h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            h0[h] = __uint_as_float(h ? cur.hist[0] & 0xffff0000u : cur.hist[0] << 16);
+            h1[h] = __uint_as_float(h ? cur.hist[1] & 0xffff0000u : cur.hist[1] << 16);
+            h2[h] = __uint_as_float(h ? cur.hist[2] & 0xffff0000u : cur.hist[2] << 16);
+        }
+
+        // ---- conv + SiLU; rows past the chunk's last token stay zero
+        if (conv_lane) {
+            float *ydst = isq ? &Qs[e] : isk ? &Ks[e - DK] : &Vs[e - 2 * DK];
+            const int ypitch = (isq || isk) ? KP : VP;
+            const bool has_bias = p.conv_b != nullptr;
+#pragma unroll
+            for (int tt = 0; tt < BT; ++tt) {
+                float y0 = 0.f, y1 = 0.f;
+                if (tt < n) {
+                    const float x0 = __uint_as_float(cur.xb[tt] << 16), x1 = __uint_as_float(cur.xb[tt] & 0xffff0000u);
+                    float acc0 = w0[0] * h0[0];
+                    acc0 = fmaf(w1[0], h1[0], acc0);
+                    acc0 = fmaf(w2[0], h2[0], acc0);
+                    acc0 = fmaf(w3[0], x0, acc0);
+                    float acc1 = w0[1] * h0[1];
+                    acc1 = fmaf(w1[1], h1[1], acc1);
+                    acc1 = fmaf(w2[1], h2[1], acc1);
+                    acc1 = fmaf(w3[1], x1, acc1);
+                    if (has_bias) {
+                        acc0 += bias[0];
+                        acc1 += bias[1];
+                    }
+                    y0 = acc0 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc0));
+                    y1 = acc1 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc1));
+                    h0[0] = h1[0]; h1[0] = h2[0]; h2[0] = x0;
+                    h0[1] = h1[1]; h1[1] = h2[1]; h2[1] = x1;
                 }
-                y0 = acc0 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc0));
-                y1 = acc1 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc1));
-                h0[0] = h1[0]; h1[0] = h2[0]; h2[0] = x0;
-                h0[1] = h1[1]; h1[1] = h2[1]; h2[1] = x1;
+                ydst[tt * ypitch] = y0;
+                ydst[tt * ypitch + 1] = y1;
             }
-            ydst[tt * ypitch] = y0;
-            ydst[tt * ypitch + 1] = y1;
         }
-    }
-    if (tid < BT) {
-        // the running log decay inside the chunk and the factors derived from it
-        float gsum = g_in;
+        // the next chunk's inputs load while this one computes; issued after
+        // the conv, so only one chunk's x rows are live in registers at a time
+        load(g + gridDim.x, nxt);
+        if (tid < BT) {
+            // the running log decay inside the chunk and the factors derived from it
+            float gsum = cur.g_in;
 #pragma unroll
-        for (int o = 1; o < BT; o <<= 1) {
-            const float up = __shfl_up(gsum, o, 64);
-            if (tid >= o)
-                gsum += up;
+            for (int o = 1; o < BT; o <<= 1) {
+                const float up = __shfl_up(gsum, o, 64);
+                if (tid >= o)
+                    gsum += up;
+            }
+            const float glast = __shfl(gsum, BT - 1, 64);
+            gam[tid] = gsum;
+            bet[tid] = cur.b_in;
+            eg[tid] = expf(gsum);
+            egl[tid] = expf(glast - gsum);
         }
-        const float glast = __shfl(gsum, BT - 1, 64);
-        gam[tid] = gsum;
-        bet[tid] = b_in;
-        eg[tid] = expf(gsum);
-        egl[tid] = expf(glast - gsum);
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- L2 norms of q and k: eight lanes a token
-    {
-        const int tt = tid >> 3, sub = tid & 7;
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int i = sub; i < DK; i += 8) {
-            const float qv = Qs[tt * KP + i], kv = Ks[tt * KP + i];
-            sq = fmaf(qv, qv, sq);
-            sk = fmaf(kv, kv, sk);
-        }
-        // the sums over each token's eight lanes: DPP butterflies (same pairs as an
-        // xor shuffle, no LDS round trip)
-        sq += dpp_xor<1>(sq);
-        sk += dpp_xor<1>(sk);
-        sq += dpp_xor<2>(sq);
-        sk += dpp_xor<2>(sk);
-        sq += dpp_xor<4>(sq);
-        sk += dpp_xor<4>(sk);
-        if (tt < n) {
-            const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
-            const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+        // ---- L2 norms of q and k: eight lanes a token
+        {
+            const int tt = tid >> 3, sub = tid & 7;
+            float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int i = sub; i < DK; i += 8) {
-                Qs[tt * KP + i] *= qs;
-                Ks[tt * KP + i] *= rk;
+                const float qv = Qs[tt * KP + i], kv = Ks[tt * KP + i];
+                sq = fmaf(qv, qv, sq);
+                sk = fmaf(kv, kv, sk);
+            }
+            // the sums over each token's eight lanes: DPP butterflies (same pairs as an
+            // xor shuffle, no LDS round trip)
+            sq += dpp_xor<1>(sq);
+            sk += dpp_xor<1>(sk);
+            sq += dpp_xor<2>(sq);
+            sk += dpp_xor<2>(sk);
+            sq += dpp_xor<4>(sq);
+            sk += dpp_xor<4>(sk);
+            if (tt < n) {
+                const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
+                const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+#pragma unroll
+                for (int i = sub; i < DK; i += 8) {
+                    Qs[tt * KP + i] *= qs;
+                    Ks[tt * KP + i] *= rk;
+                }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- K K^T (waves 0, 1) and Q K^T (waves 2, 3) -> the masked, decay-weighted A and P
-    {
-        const float *Asrc = wv < 2 ? Ks : Qs;
-        const int rb = wv & 1;
-        v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+        // ---- K K^T (waves 0, 1) and Q K^T (waves 2, 3) -> the masked, decay-weighted A and P
+        {
+            const float *Asrc = wv < 2 ? Ks : Qs;
+            const int rb = wv & 1;
+            v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 8
-        for (int k0 = 0; k0 < DK; k0 += 4) {
-            const float a = Asrc[(rb * 16 + li) * KP + k0 + lk];
+            for (int k0 = 0; k0 < DK; k0 += 4) {
+                const float a = Asrc[(rb * 16 + li) * KP + k0 + lk];
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    acc[cb] = mma16(a, Ks[(cb * 16 + li) * KP + k0 + lk], acc[cb]);
+            }
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
-                acc[cb] = mma16(a, Ks[(cb * 16 + li) * KP + k0 + lk], acc[cb]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tt = rb * 16 + 4 * lk + r, ss = cb * 16 + li;
+                    const float d = expf(gam[tt] - gam[ss]);
+                    if (wv < 2)
+                        Am[tt * AP + ss] = ss < tt ? bet[tt] * d * acc[cb][r] : 0.f;
+                    else
+                        Pm[tt * AP + ss] = ss <= tt ? d * acc[cb][r] : 0.f;
+                }
         }
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = rb * 16 + 4 * lk + r, ss = cb * 16 + li;
-                const float d = expf(gam[tt] - gam[ss]);
-                if (wv < 2)
-                    Am[tt * AP + ss] = ss < tt ? bet[tt] * d * acc[cb][r] : 0.f;
-                else
-                    Pm[tt * AP + ss] = ss <= tt ? d * acc[cb][r] : 0.f;
-            }
-    }
-    __syncthreads();
-
-    // ---- (I + A)^-1: the two 16x16 diagonal blocks by forward substitution
-    // (thread j of a block solves column j), then T21 = -T22 (A21 T11)
-    if (tid < BT) {
-        const int b0 = tid & 16, j = tid & 15;
-        float xcol[16];
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-            float acc = tt == j ? 1.f : 0.f;
-#pragma unroll
-            for (int ss = 0; ss < tt; ++ss)
-                acc = fmaf(-Am[(b0 + tt) * AP + b0 + ss], xcol[ss], acc);
-            xcol[tt] = tt < j ? 0.f : acc;
-            Tm[(b0 + tt) * AP + b0 + j] = xcol[tt];
-            Tm[(b0 + tt) * AP + (b0 ^ 16) + j] = 0.f;
-        }
-    }
-    __syncthreads();
-    {
-        const int r = tid >> 4, cc = tid & 15;
-        float acc = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-            acc = fmaf(Am[(16 + r) * AP + u], Tm[u * AP + cc], acc);
-        Mm[r * 17 + cc] = acc;
         __syncthreads();
-        float t21 = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-            t21 = fmaf(Tm[(16 + r) * AP + 16 + u], Mm[u * 17 + cc], t21);
-        Tm[(16 + r) * AP + cc] = -t21;
-    }
-    __syncthreads();
 
-    // ---- W = T diag(beta e^gamma) K and U~ = T diag(beta) V on the matrix
-    // cores: this wave's column blocks of each, both row blocks.  Rows of
-    // padding tokens come out zero (their rows of A, and beta, are zero).
-    const size_t blk = (size_t)hv * tp.ws.nchunk + gidx;
-    {
-        constexpr int WCB = DK / 64, UCB = DV / 64;
-        v4f wacc[2][WCB], uacc[2][UCB];
+        // ---- (I + A)^-1: the two 16x16 diagonal blocks by forward substitution
+        // (thread j of a block solves column j), then T21 = -T22 (A21 T11)
+        if (tid < BT) {
+            const int b0 = tid & 16, j = tid & 15;
+            float xcol[16];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+            for (int tt = 0; tt < 16; ++tt) {
+                float acc = tt == j ? 1.f : 0.f;
 #pragma unroll
-            for (int q = 0; q < WCB; ++q)
-                wacc[rb][q] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < UCB; ++q)
-                uacc[rb][q] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int k0 = 0; k0 < BT; k0 += 4) {
-            const float at0 = Tm[li * AP + k0 + lk], at1 = Tm[(16 + li) * AP + k0 + lk];
-            const float bs = bet[k0 + lk];
-            const float bse = bs * eg[k0 + lk];
-#pragma unroll
-            for (int q = 0; q < WCB; ++q) {
-                const float bk = bse * Ks[(k0 + lk) * KP + (wv * WCB + q) * 16 + li];
-                wacc[0][q] = mma16(at0, bk, wacc[0][q]);
-                wacc[1][q] = mma16(at1, bk, wacc[1][q]);
-            }
-#pragma unroll
-            for (int q = 0; q < UCB; ++q) {
-                const float bv = bs * Vs[(k0 + lk) * VP + (wv * UCB + q) * 16 + li];
-                uacc[0][q] = mma16(at0, bv, uacc[0][q]);
-                uacc[1][q] = mma16(at1, bv, uacc[1][q]);
+                for (int ss = 0; ss < tt; ++ss)
+                    acc = fmaf(-Am[(b0 + tt) * AP + b0 + ss], xcol[ss], acc);
+                xcol[tt] = tt < j ? 0.f : acc;
+                Tm[(b0 + tt) * AP + b0 + j] = xcol[tt];
+                Tm[(b0 + tt) * AP + (b0 ^ 16) + j] = 0.f;
             }
         }
-        // U~ leaves in the accumulator layout it was computed in
+        __syncthreads();
+        {
+            const int r = tid >> 4, cc = tid & 15;
+            float acc = 0.f;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+            for (int u = 0; u < 16; ++u)
+                acc = fmaf(Am[(16 + r) * AP + u], Tm[u * AP + cc], acc);
+            Mm[r * 17 + cc] = acc;
+            __syncthreads();
+            float t21 = 0.f;
 #pragma unroll
-            for (int q = 0; q < UCB; ++q)
-                *reinterpret_cast<v4f *>(tp.ws.ud + ((blk * 2 + rb) * (DV / 16) + wv * UCB + q) * 256 + lane * 4) =
-                    uacc[rb][q];
-        __syncthreads(); // every read of V is done: W goes over it
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int q = 0; q < WCB; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Vs[(rb * 16 + 4 * lk + r) * KP + (wv * WCB + q) * 16 + li] = wacc[rb][q][r];
-    }
-    __syncthreads();
+            for (int u = 0; u < 16; ++u)
+                t21 = fmaf(Tm[(16 + r) * AP + 16 + u], Mm[u * 17 + cc], t21);
+            Tm[(16 + r) * AP + cc] = -t21;
+        }
+        __syncthreads();
 
-    // ---- Q~, W, K~ and P in the order the second pass feeds them to the
-    // matrix cores (one float4 per lane and four k-slices)
-    const float *Ws = Vs;
-    for (int idx = tid; idx < 2 * (DK / 16) * 64; idx += NT) {
-        const int l = idx & 63, m4 = (idx >> 6) % (DK / 16), rb = idx / (64 * (DK / 16));
-        const int row = rb * 16 + (l & 15);
-        v4f qv, wv4;
+        // ---- W = T diag(beta e^gamma) K and U~ = T diag(beta) V on the matrix
+        // cores: this wave's column blocks of each, both row blocks.  Rows of
+        // padding tokens come out zero (their rows of A, and beta, are zero).
+        const size_t blk = (size_t)hv * tp.ws.nchunk + g;
+        {
+            constexpr int WCB = DK / 64, UCB = DV / 64;
+            v4f wacc[2][WCB], uacc[2][UCB];
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const int col = 4 * (4 * m4 + e4) + (l >> 4);
-            qv[e4] = Qs[row * KP + col] * eg[row];
-            wv4[e4] = Ws[row * KP + col];
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int q = 0; q < WCB; ++q)
+                    wacc[rb][q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < UCB; ++q)
+                    uacc[rb][q] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < BT; k0 += 4) {
+                const float at0 = Tm[li * AP + k0 + lk], at1 = Tm[(16 + li) * AP + k0 + lk];
+                const float bs = bet[k0 + lk];
+                const float bse = bs * eg[k0 + lk];
+#pragma unroll
+                for (int q = 0; q < WCB; ++q) {
+                    const float bk = bse * Ks[(k0 + lk) * KP + (wv * WCB + q) * 16 + li];
+                    wacc[0][q] = mma16(at0, bk, wacc[0][q]);
+                    wacc[1][q] = mma16(at1, bk, wacc[1][q]);
+                }
+#pragma unroll
+                for (int q = 0; q < UCB; ++q) {
+                    const float bv = bs * Vs[(k0 + lk) * VP + (wv * UCB + q) * 16 + li];
+                    uacc[0][q] = mma16(at0, bv, uacc[0][q]);
+                    uacc[1][q] = mma16(at1, bv, uacc[1][q]);
+                }
+            }
+            // U~ leaves in the accumulator layout it was computed in
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int q = 0; q < UCB; ++q)
+                    *reinterpret_cast<v4f *>(tp.ws.ud + ((blk * 2 + rb) * (DV / 16) + wv * UCB + q) * 256 + lane * 4) =
+                        uacc[rb][q];
+            __syncthreads(); // every read of V is done: W goes over it
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int q = 0; q < WCB; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Vs[(rb * 16 + 4 * lk + r) * KP + (wv * WCB + q) * 16 + li] = wacc[rb][q][r];
         }
-        *reinterpret_cast<v4f *>(tp.ws.qa + blk * (BT * DK) + (size_t)idx * 4) = qv;
-        *reinterpret_cast<v4f *>(tp.ws.wa + blk * (BT * DK) + (size_t)idx * 4) = wv4;
-    }
-    for (int idx = tid; idx < (DK / 16) * 2 * 64; idx += NT) {
-        const int l = idx & 63, m4 = (idx >> 6) & 1, ib = idx >> 7;
-        v4f kv;
+        __syncthreads();
+
+        // ---- Q~, W, K~ and P in the order the second pass feeds them to the
+        // matrix cores (one float4 per lane and four k-slices)
+        const float *Ws = Vs;
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const int tt = 4 * (4 * m4 + e4) + (l >> 4);
-            kv[e4] = Ks[tt * KP + ib * 16 + (l & 15)] * egl[tt];
+        for (int it = 0; it < 2 * (DK / 16) * 64 / NT; ++it) {
+            const int idx = tid + it * NT;
+            const int l = idx & 63, m4 = (idx >> 6) % (DK / 16), rb = idx / (64 * (DK / 16));
+            const int row = rb * 16 + (l & 15);
+            v4f qv, wv4;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int col = 4 * (4 * m4 + e4) + (l >> 4);
+                qv[e4] = Qs[row * KP + col] * eg[row];
+                wv4[e4] = Ws[row * KP + col];
+            }
+            *reinterpret_cast<v4f *>(tp.ws.qa + blk * (BT * DK) + (size_t)idx * 4) = qv;
+            *reinterpret_cast<v4f *>(tp.ws.wa + blk * (BT * DK) + (size_t)idx * 4) = wv4;
         }
-        *reinterpret_cast<v4f *>(tp.ws.ka + blk * (BT * DK) + (size_t)idx * 4) = kv;
-    }
-    {
-        const int idx = tid, l = idx & 63, m4 = (idx >> 6) & 1, rb = idx >> 7; // 256 float4: one a thread
-        v4f pv;
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4)
-            pv[e4] = Pm[(rb * 16 + (l & 15)) * AP + 4 * (4 * m4 + e4) + (l >> 4)];
-        *reinterpret_cast<v4f *>(tp.ws.pa + blk * (BT * BT) + (size_t)idx * 4) = pv;
+        for (int it = 0; it < (DK / 16) * 2 * 64 / NT; ++it) {
+            const int idx = tid + it * NT;
+            const int l = idx & 63, m4 = (idx >> 6) & 1, ib = idx >> 7;
+            v4f kv;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int tt = 4 * (4 * m4 + e4) + (l >> 4);
+                kv[e4] = Ks[tt * KP + ib * 16 + (l & 15)] * egl[tt];
+            }
+            *reinterpret_cast<v4f *>(tp.ws.ka + blk * (BT * DK) + (size_t)idx * 4) = kv;
+        }
+        {
+            const int idx = tid, l = idx & 63, m4 = (idx >> 6) & 1, rb = idx >> 7; // 256 float4: one a thread
+            v4f pv;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                pv[e4] = Pm[(rb * 16 + (l & 15)) * AP + 4 * (4 * m4 + e4) + (l >> 4)];
+            *reinterpret_cast<v4f *>(tp.ws.pa + blk * (BT * BT) + (size_t)idx * 4) = pv;
+        }
+        // e^gamma_last (padding tokens carry g = 0): every lane stores the same
+        // value to the same place, which needs no branch
+        tp.ws.el[blk] = eg[BT - 1];
+
+        cur = nxt;
+        __syncthreads(); // LDS is read to the end of the chunk; the next one rewrites it
     }
-    if (tid == 0)
-        tp.ws.el[blk] = eg[BT - 1]; // padding tokens carry g = 0
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -726,8 +763,11 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
                                    stream);
     if (e != hipSuccess)
         return e;
-    // an upper bound on the chunk count: each sequence adds at most one partial chunk
-    const long long gx = ((long long)p.total + BT - 1) / BT + p.B;
+    // pass 1 walks the chunks with about two resident workgroups a compute
+    // unit (its LDS allows two), each taking every gx-th chunk of a head
+    const long long nchunk_max = ((long long)p.total + BT - 1) / BT + p.B;
+    long long gx = 512 / p.H_v;
+    gx = gx < 1 ? 1 : (gx > nchunk_max ? nchunk_max : gx);
     e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV>), dim3((unsigned)gx, (unsigned)p.H_v),
                         dim3(NT), args, 0, stream);
     if (e != hipSuccess)
