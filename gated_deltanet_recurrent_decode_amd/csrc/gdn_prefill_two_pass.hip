@@ -13,16 +13,18 @@
 //     O  = Q~ S0 + P U,       Q~ = diag(e^gamma) Q
 //     S1 = e^gamma_last S0 + K~^T U,   K~ = diag(e^(gamma_last - gamma)) K
 //
-// Pass 1 (one workgroup per chunk and value head): conv + SiLU (the three
-// inputs before the chunk come from the slot's window for a prompt's first
-// chunk, else from x), L2 norms, the running log decay, K K^T and Q K^T -> A
-// and P, (I + A)^-1 by blocked forward substitution, then W and U~ on the
-// matrix cores; Q~, K~, W, U~, P and e^gamma_last go to the workspace.
+// Pass 1 (workgroups per value head, each walking every gx-th chunk of the
+// call): conv + SiLU (the three inputs before the chunk come from the slot's
+// window for a prompt's first chunk, else from x), L2 norms, the running log
+// decay, K K^T and Q K^T -> A and P, (I + A)^-1 by blocked forward
+// substitution, then W and U~ on the matrix cores; Q~, K~, W, U~, P and
+// e^gamma_last go to the workspace.
 // Pass 2 (one workgroup per sequence, value head and slice of d_v columns):
-// the slice of the state in LDS, the chunks in order, each three matrix-core
-// products and the read-out; then the state and the advanced conv window go
-// back to the slot.  Pass 1 reads the old windows and pass 2 writes the new
-// ones, so no workgroup can read a window another has already advanced.
+// the chunks in order, each three matrix-core products and the read-out, with
+// a 16-column slice of the state in registers and a wider one in LDS; then the
+// state and the advanced conv window go back to the slot.  Pass 1 reads the old
+// windows and pass 2 writes the new ones, so no workgroup can read a window
+// another has already advanced.
 // A map kernel first turns each sequence's length into its run of chunk
 // indices (an exclusive scan), which pass 1 searches.
 
@@ -63,6 +65,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
     return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(hi << 32 | lo), (short)0,
                                              (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// fp32 -> bf16 bits, round to nearest even, a NaN kept quiet: the same bits as
+// f32_to_bf16_rne, as selects instead of a branch around each store
+__device__ __forceinline__ uint16_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x0040u;
+    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 __device__ __forceinline__ v4f buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
@@ -418,20 +430,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         __syncthreads();
 
         // ---- Q~, W, K~ and P in the order the second pass feeds them to the
-        // matrix cores (one float4 per lane and four k-slices)
+        // matrix cores: 1 KiB blocks of one float4 a lane, lane j + 16 g of
+        // block (row block rb, k block m4) holding X[16 rb + j][16 m4 + 4 g + r]
+        // for r = 0..3 -- the k-steps of a 16-wide k block taken in the order
+        // the accumulator layout holds rows (4 g + r), so that a state slice
+        // kept in that layout is a B operand as it stands
         const float *Ws = Vs;
 #pragma unroll
         for (int it = 0; it < 2 * (DK / 16) * 64 / NT; ++it) {
             const int idx = tid + it * NT;
             const int l = idx & 63, m4 = (idx >> 6) % (DK / 16), rb = idx / (64 * (DK / 16));
             const int row = rb * 16 + (l & 15);
-            v4f qv, wv4;
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int col = 4 * (4 * m4 + e4) + (l >> 4);
-                qv[e4] = Qs[row * KP + col] * eg[row];
-                wv4[e4] = Ws[row * KP + col];
-            }
+            const int col = 16 * m4 + 4 * (l >> 4);
+            const float er = eg[row];
+            const v4f q4 = *reinterpret_cast<const v4f *>(&Qs[row * KP + col]);
+            const v4f qv = {q4[0] * er, q4[1] * er, q4[2] * er, q4[3] * er};
+            const v4f wv4 = *reinterpret_cast<const v4f *>(&Ws[row * KP + col]);
             *reinterpret_cast<v4f *>(tp.ws.qa + blk * (BT * DK) + (size_t)idx * 4) = qv;
             *reinterpret_cast<v4f *>(tp.ws.wa + blk * (BT * DK) + (size_t)idx * 4) = wv4;
         }
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             v4f kv;
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
-                const int tt = 4 * (4 * m4 + e4) + (l >> 4);
+                const int tt = 16 * m4 + 4 * (l >> 4) + e4;
                 kv[e4] = Ks[tt * KP + ib * 16 + (l & 15)] * egl[tt];
             }
             *reinterpret_cast<v4f *>(tp.ws.ka + blk * (BT * DK) + (size_t)idx * 4) = kv;
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             v4f pv;
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
-                pv[e4] = Pm[(rb * 16 + (l & 15)) * AP + 4 * (4 * m4 + e4) + (l >> 4)];
+                pv[e4] = Pm[(rb * 16 + (l & 15)) * AP + 16 * m4 + 4 * (l >> 4) + e4];
             *reinterpret_cast<v4f *>(tp.ws.pa + blk * (BT * BT) + (size_t)idx * 4) = pv;
         }
         // e^gamma_last (padding tokens carry g = 0): every lane stores the same
@@ -466,259 +480,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 // ---------------------------------------------------------------- pass 2
 
+// The advanced conv windows of a prompt: the last three inputs of [window,
+// prompt] for the slice's v channels, and for the key head's q and k channels
+// from its first value head's first slice.  Nothing else reads or writes these
+// channels of this slot now: pass 1 is over.
 template <int DK, int DV, int DVS>
-__global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
+__device__ __forceinline__ void advance_windows(const PrefillParams &p, int hv, int sl, int t_begin, int t_end, int s)
 {
-    const PrefillParams &p = tp.p;
-    constexpr int NSL = DV / DVS;
-    constexpr int SP = DVS + ((DVS + 16) % 32 == 16 ? 16 : 32); // S and U: B operands, read down a column
-    constexpr int CBS = DVS / 16;                               // column blocks of the slice
-    // Output tiles of W S0, Q~ S0 and O: wave w takes row block w & 1 and, of
-    // a slice of two or more column blocks, half of them; a 16-column slice
-    // has one column block, so there waves 0-1 take W S0 and waves 2-3 Q~ S0.
-    constexpr bool SPLIT = CBS == 1;
-    constexpr int CBW = SPLIT ? 1 : CBS / 2;
-    constexpr int NA4 = DK / 16;  // float4 a lane holds of one A-operand tile over k = d_k
-    constexpr int RBW = DK / 64;  // row blocks of S a wave updates
-    constexpr int CHUNK_QK = BT * DK, CHUNK_P = BT * BT, CHUNK_U = BT * DV;
-
-    __shared__ __align__(16) float S[DK * SP];
-    __shared__ __align__(16) float Um[BT * SP];
-
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
-    const int sl = blockIdx.x % NSL;
-    const int bh = blockIdx.x / NSL;
-    const int hv = bh % p.H_v;
-    const int b = bh / p.H_v;
-    const int col0 = sl * DVS;
-    int t_begin, t_end, s;
-    if (!sequence_usable(p, b, t_begin, t_end, s))
-        return; // an unusable range or slot touches nothing
-    // one value for the whole workgroup: the buffer resources built from these
-    // must sit in scalar registers
-    t_begin = __builtin_amdgcn_readfirstlane(t_begin);
-    t_end = __builtin_amdgcn_readfirstlane(t_end);
-    s = __builtin_amdgcn_readfirstlane(s);
-    if (s == 0) {
-        // padding sequence on the null slot: its read-out is +0.0
-        for (int e = tid; e < (t_end - t_begin) * DVS; e += NT)
-            p.out[((size_t)(t_begin + e / DVS) * p.H_v + hv) * DV + col0 + e % DVS] = 0;
-        return;
-    }
-    if (t_end == t_begin)
-        return;
-    const int nchunks = (t_end - t_begin + BT - 1) / BT;
-    const int cs_b = __builtin_amdgcn_readfirstlane(tp.ws.chunk_start[b]);
-    if (cs_b < 0 || (long long)cs_b + nchunks > tp.ws.nchunk)
-        return; // only with overlapping ranges (excluded by the contract): touch nothing
-    const size_t blk0 = (size_t)hv * tp.ws.nchunk + (size_t)cs_b;
-    float *tile = p.state + ((size_t)s * p.H_v + hv) * (size_t)(DK * DV);
-
-    const int rb = wv & 1;
-    const int cb0 = SPLIT ? 0 : (wv >> 1) * CBW;
-    const bool takes_w = !SPLIT || wv < 2;
-    const bool takes_q = !SPLIT || wv >= 2;
-
-    // ---- the state's column slice -> LDS (16-byte streaming loads)
-    for (int e = tid; e < DK * DVS / 4; e += NT) {
-        const int i = e / (DVS / 4), j4 = e % (DVS / 4);
-        const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(tile + (size_t)i * DV + col0) + j4);
-        *reinterpret_cast<v4f *>(&S[i * SP + 4 * j4]) = v;
-    }
-
-    // ---- this wave's operands of a chunk, loaded one chunk ahead straight
-    // into registers (pass 1 wrote them in operand order).  Buffer loads over
-    // resources sized to the real rows, zero-sized past the last chunk, so the
-    // walk has no branch around a memory access.  A wave loads only what it
-    // uses: every load, even an empty one, takes the compute unit's address
-    // path (about 16 cycles for a 1 KiB wave load, shared by the four waves),
-    // so with 16-column slices a wave fetches one A tile (W on waves 0-1, Q~ on
-    // waves 2-3) and one of P or U~.
-    constexpr int NLOAD = SPLIT ? NA4 + 2 * RBW + 2 : 2 * NA4 + 2 * RBW + 2 + CBW; // loads a wave issues a chunk
-    v4f xw[NA4], xq[NA4], xk[RBW][2], xp[2], xu[CBW];
-    float xel = 0.f;
-    auto prefetch = [&](int c) {
-        const bool real = c < nchunks;
-        const size_t blk = blk0 + (size_t)(real ? c : 0);
-        const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.ka + blk * CHUNK_QK + wv * RBW * 512, real ? RBW * 2048u : 0u);
-        if constexpr (SPLIT) {
-            const __amdgpu_buffer_rsrc_t rA =
-                buf_rsrc((takes_w ? tp.ws.wa : tp.ws.qa) + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
-            const __amdgpu_buffer_rsrc_t rX =
-                buf_rsrc(takes_q ? tp.ws.pa + blk * CHUNK_P + rb * 512
-                                 : tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16) * 256,
-                         real ? (takes_q ? 2048u : 1024u) : 0u);
-#pragma unroll
-            for (int m4 = 0; m4 < NA4; ++m4)
-                xw[m4] = buf_load4(rA, (uint32_t)(m4 * 64 + lane) * 16u);
-#pragma unroll
-            for (int m4 = 0; m4 < 2; ++m4)
-                xp[m4] = buf_load4(rX, (uint32_t)(m4 * 64 + lane) * 16u); // P, or U~ in the first
-        } else {
-            const __amdgpu_buffer_rsrc_t rW =
-                buf_rsrc(tp.ws.wa + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
-            const __amdgpu_buffer_rsrc_t rQ =
-                buf_rsrc(tp.ws.qa + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
-            const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P + rb * 512, real ? 2048u : 0u);
-            const __amdgpu_buffer_rsrc_t rU =
-                buf_rsrc(tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16 + cb0) * 256, real ? CBW * 1024u : 0u);
-#pragma unroll
-            for (int m4 = 0; m4 < NA4; ++m4) {
-                xw[m4] = buf_load4(rW, (uint32_t)(m4 * 64 + lane) * 16u);
-                xq[m4] = buf_load4(rQ, (uint32_t)(m4 * 64 + lane) * 16u);
-            }
-#pragma unroll
-            for (int m4 = 0; m4 < 2; ++m4)
-                xp[m4] = buf_load4(rP, (uint32_t)(m4 * 64 + lane) * 16u);
-#pragma unroll
-            for (int q = 0; q < CBW; ++q)
-                xu[q] = buf_load4(rU, (uint32_t)(q * 64 + lane) * 16u);
-        }
-#pragma unroll
-        for (int q = 0; q < RBW; ++q)
-#pragma unroll
-            for (int m4 = 0; m4 < 2; ++m4)
-                xk[q][m4] = buf_load4(rK, (uint32_t)((q * 2 + m4) * 64 + lane) * 16u);
-        xel = tp.ws.el[blk];
-    };
-    prefetch(0);
-    __syncthreads(); // the state is in LDS
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = t_begin + c * BT;
-        const int n = t_end - t0 < BT ? t_end - t0 : BT;
-        v4f aw_op[NA4], aq_op[NA4], ak_op[RBW][2], ap_op[2], au[CBW];
-#pragma unroll
-        for (int m4 = 0; m4 < NA4; ++m4) {
-            aw_op[m4] = xw[m4];
-            aq_op[m4] = SPLIT ? xw[m4] : xq[m4];
-        }
-#pragma unroll
-        for (int q = 0; q < RBW; ++q) {
-            ak_op[q][0] = xk[q][0];
-            ak_op[q][1] = xk[q][1];
-        }
-        ap_op[0] = xp[0];
-        ap_op[1] = xp[1];
-#pragma unroll
-        for (int q = 0; q < CBW; ++q)
-            au[q] = SPLIT ? xp[0] : xu[q];
-        const float el = xel;
-        prefetch(c + 1);
-        // the read-out rows of the chunk's real tokens; later rows fall outside
-        const int t0u = __builtin_amdgcn_readfirstlane(t0), nu = __builtin_amdgcn_readfirstlane(n);
-        const __amdgpu_buffer_rsrc_t rO = buf_rsrc(p.out + ((size_t)t0u * p.H_v + hv) * DV + col0,
-                                                   (uint32_t)(((nu - 1) * p.H_v * DV + DVS) * 2));
-
-        // ---- W S0 and Q~ S0 on this wave's tiles (row block rb)
-        v4f aw[CBW], aq[CBW];
-#pragma unroll
-        for (int q = 0; q < CBW; ++q)
-            aw[q] = aq[q] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m4 = 0; m4 < NA4; ++m4)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int k0 = 4 * (4 * m4 + e4);
-#pragma unroll
-                for (int q = 0; q < CBW; ++q) {
-                    const float bs = S[(k0 + lk) * SP + (cb0 + q) * 16 + li];
-                    if constexpr (SPLIT) {
-                        // one accumulator: W S0 on waves 0-1, Q~ S0 on waves 2-3
-                        // (the A tile the wave loaded)
-                        aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
-                    } else {
-                        aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
-                        aq[q] = mma16(aq_op[m4][e4], bs, aq[q]);
-                    }
-                }
-            }
-        // interleave the next chunk's loads with these products, so their
-        // address processing runs under the matrix cores instead of in front
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // one vector-memory read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMA
-        }
-        if constexpr (SPLIT)
-            aq[0] = aw[0];
-        // U = U~ - W S0 on the same tiles -> LDS
-        if (takes_w) {
-#pragma unroll
-            for (int q = 0; q < CBW; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Um[(rb * 16 + 4 * lk + r) * SP + (cb0 + q) * 16 + li] = au[q][r] - aw[q][r];
-        }
-        __syncthreads(); // U complete; every read of S0 for this chunk is done
-
-        // ---- O = Q~ S0 + P U -> out
-        if (takes_q) {
-#pragma unroll
-            for (int m4 = 0; m4 < 2; ++m4)
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int k0 = 4 * (4 * m4 + e4);
-#pragma unroll
-                    for (int q = 0; q < CBW; ++q)
-                        aq[q] = mma16(ap_op[m4][e4], Um[(k0 + lk) * SP + (cb0 + q) * 16 + li], aq[q]);
-                }
-#pragma unroll
-            for (int q = 0; q < CBW; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    __builtin_amdgcn_raw_buffer_store_b16(
-                        f32_to_bf16_rne(aq[q][r]), rO,
-                        (uint32_t)((rb * 16 + 4 * lk + r) * p.H_v * DV + (cb0 + q) * 16 + li) * 2u, 0, 0);
-        }
-
-        // ---- S1 = e^gamma_last S0 + K~^T U: this wave's row blocks, the slice's column blocks
-        {
-            v4f sacc[RBW][CBS];
-#pragma unroll
-            for (int q = 0; q < RBW; ++q)
-#pragma unroll
-                for (int jb = 0; jb < CBS; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sacc[q][jb][r] = el * S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li];
-#pragma unroll
-            for (int m4 = 0; m4 < 2; ++m4)
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int k0 = 4 * (4 * m4 + e4);
-#pragma unroll
-                    for (int q = 0; q < RBW; ++q)
-#pragma unroll
-                        for (int jb = 0; jb < CBS; ++jb)
-                            sacc[q][jb] = mma16(ak_op[q][m4][e4], Um[(k0 + lk) * SP + jb * 16 + li], sacc[q][jb]);
-                }
-#pragma unroll
-            for (int q = 0; q < RBW; ++q)
-#pragma unroll
-                for (int jb = 0; jb < CBS; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li] = sacc[q][jb][r];
-        }
-        __syncthreads(); // S and U are free for the next chunk
-    }
-
-    // ---- the state's slice back to the slot
-    for (int e = tid; e < DK * DVS / 4; e += NT) {
-        const int i = e / (DVS / 4), j4 = e % (DVS / 4);
-        const v4f v = *reinterpret_cast<const v4f *>(&S[i * SP + 4 * j4]);
-        __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(tile + (size_t)i * DV + col0) + j4);
-    }
-
-    // ---- the advanced conv windows: the last three inputs of [window, prompt]
-    // for this slice's v channels, and for the key head's q and k channels from
-    // its first value head's first slice.  Nothing else reads or writes these
-    // channels of this slot now: pass 1 is over.
     const int L = t_end - t_begin;
     const int C = p.C;
     const int hk = hv / p.G;
+    const int col0 = sl * DVS;
     const bool qk_owner = (hv % p.G == 0) && sl == 0;
     const int npair = DVS / 2 + (qk_owner ? DK : 0);
     uint16_t *win = p.conv_state + (size_t)s * 3 * C;
@@ -742,6 +515,484 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
         for (int k = 0; k < 3; ++k)
             *reinterpret_cast<uint32_t *>(win + (size_t)k * C + ch) = nw[k];
     }
+}
+
+// The (prompt, value head) pair and the column slice of pass-2 workgroup j, of
+// nsl slices a head.  Workgroups go to the eight XCDs in turn, so the slices
+// of a head are placed eight workgroups apart: they share one XCD, whose L2
+// then fetches the head's operands once for all of them.  Pairs past the last
+// whole group of eight are placed in order.
+__device__ __forceinline__ void walk_place(int j, int heads, int nsl, int &bh, int &sl)
+{
+    const int h8 = heads & ~7;
+    if (j < h8 * nsl) {
+        const int k = j >> 3;
+        bh = (k / nsl) * 8 + (j & 7);
+        sl = k % nsl;
+    } else {
+        const int r = j - h8 * nsl;
+        bh = h8 + r / nsl;
+        sl = r % nsl;
+    }
+}
+
+// Where a pass-2 workgroup's prompt stands: false when it has nothing to do
+// (an unusable range or slot touches nothing; a padding prompt on the null
+// slot gets its read-out of +0.0 here; an empty prompt does nothing).
+template <int DV, int DVS>
+__device__ __forceinline__ bool walk_setup(const TwoPassParams &tp, int b, int hv, int col0, int &t_begin, int &t_end,
+                                           int &s, int &nchunks, size_t &blk0)
+{
+    const PrefillParams &p = tp.p;
+    if (!sequence_usable(p, b, t_begin, t_end, s))
+        return false;
+    // one value for the whole workgroup: the buffer resources built from these
+    // must sit in scalar registers
+    t_begin = __builtin_amdgcn_readfirstlane(t_begin);
+    t_end = __builtin_amdgcn_readfirstlane(t_end);
+    s = __builtin_amdgcn_readfirstlane(s);
+    if (s == 0) {
+        for (int e = threadIdx.x; e < (t_end - t_begin) * DVS; e += NT)
+            p.out[((size_t)(t_begin + e / DVS) * p.H_v + hv) * DV + col0 + e % DVS] = 0;
+        return false;
+    }
+    if (t_end == t_begin)
+        return false;
+    nchunks = (t_end - t_begin + BT - 1) / BT;
+    const int cs_b = __builtin_amdgcn_readfirstlane(tp.ws.chunk_start[b]);
+    if (cs_b < 0 || (long long)cs_b + nchunks > tp.ws.nchunk)
+        return false; // only with overlapping ranges (excluded by the contract): touch nothing
+    blk0 = (size_t)hv * tp.ws.nchunk + (size_t)cs_b;
+    return true;
+}
+
+// Slices of 32 columns or more: the slice of the state and U in LDS.  Wave w
+// takes row block w & 1 of W S0, Q~ S0 and O and half the slice's column
+// blocks, and row blocks w * DK / 64 .. of the state update.  The k-steps of
+// every product run in pass 1's operand order (k = 16 m4 + 4 g + e4 at lane
+// group g), so the B operands are read from LDS at those rows.
+template <int DK, int DV, int DVS>
+__global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
+{
+    const PrefillParams &p = tp.p;
+    constexpr int NSL = DV / DVS;
+    // S and U are B operands read down a column, four rows apart across lane
+    // groups: a pitch of DVS + 4 puts the four groups 16 banks apart
+    constexpr int SP = DVS + 4;
+    constexpr int CBS = DVS / 16; // column blocks of the slice
+    static_assert(CBS >= 2, "16-column slices take tp_inter16_kernel");
+    constexpr int CBW = CBS / 2;  // column blocks of W S0, Q~ S0 and O a wave takes
+    constexpr int NA4 = DK / 16;  // float4 a lane holds of one A-operand tile over k = d_k
+    constexpr int RBW = DK / 64;  // row blocks of S a wave updates
+    constexpr int CHUNK_QK = BT * DK, CHUNK_P = BT * BT, CHUNK_U = BT * DV;
+
+    __shared__ __align__(16) float S[DK * SP];
+    __shared__ __align__(16) float Um[BT * SP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
+    int bh, sl;
+    walk_place(blockIdx.x, p.B * p.H_v, NSL, bh, sl);
+    const int hv = bh % p.H_v;
+    const int b = bh / p.H_v;
+    const int col0 = sl * DVS;
+    int t_begin, t_end, s, nchunks;
+    size_t blk0;
+    if (!walk_setup<DV, DVS>(tp, b, hv, col0, t_begin, t_end, s, nchunks, blk0))
+        return;
+    float *tile = p.state + ((size_t)s * p.H_v + hv) * (size_t)(DK * DV);
+
+    const int rb = wv & 1;
+    const int cb0 = (wv >> 1) * CBW;
+
+    // ---- the state's column slice -> LDS (16-byte streaming loads)
+    for (int e = tid; e < DK * DVS / 4; e += NT) {
+        const int i = e / (DVS / 4), j4 = e % (DVS / 4);
+        const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(tile + (size_t)i * DV + col0) + j4);
+        *reinterpret_cast<v4f *>(&S[i * SP + 4 * j4]) = v;
+    }
+
+    // ---- this wave's operands of a chunk, loaded one chunk ahead straight
+    // into registers.  Buffer loads over resources zero-sized past the last
+    // chunk, so the walk has no branch around a memory access.  Every load,
+    // even an empty one, takes the compute unit's address path (about 16
+    // cycles for a 1 KiB wave load, shared by the four waves), so they are
+    // interleaved with the matrix-core products below.
+    constexpr int NLOAD = 2 * NA4 + 2 * RBW + 2 + CBW; // loads a wave issues a chunk
+    v4f xw[NA4], xq[NA4], xk[RBW][2], xp[2], xu[CBW];
+    float xel = 0.f;
+    auto prefetch = [&](int c) {
+        const bool real = c < nchunks;
+        const size_t blk = blk0 + (size_t)(real ? c : 0);
+        const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.ka + blk * CHUNK_QK + wv * RBW * 512, real ? RBW * 2048u : 0u);
+        const __amdgpu_buffer_rsrc_t rW = buf_rsrc(tp.ws.wa + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
+        const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(tp.ws.qa + blk * CHUNK_QK + rb * NA4 * 256, real ? NA4 * 1024u : 0u);
+        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P + rb * 512, real ? 2048u : 0u);
+        const __amdgpu_buffer_rsrc_t rU =
+            buf_rsrc(tp.ws.ud + blk * CHUNK_U + (rb * (DV / 16) + col0 / 16 + cb0) * 256, real ? CBW * 1024u : 0u);
+#pragma unroll
+        for (int m4 = 0; m4 < NA4; ++m4) {
+            xw[m4] = buf_load4(rW, (uint32_t)(m4 * 64 + lane) * 16u);
+            xq[m4] = buf_load4(rQ, (uint32_t)(m4 * 64 + lane) * 16u);
+        }
+#pragma unroll
+        for (int m4 = 0; m4 < 2; ++m4)
+            xp[m4] = buf_load4(rP, (uint32_t)(m4 * 64 + lane) * 16u);
+#pragma unroll
+        for (int q = 0; q < CBW; ++q)
+            xu[q] = buf_load4(rU, (uint32_t)(q * 64 + lane) * 16u);
+#pragma unroll
+        for (int q = 0; q < RBW; ++q)
+#pragma unroll
+            for (int m4 = 0; m4 < 2; ++m4)
+                xk[q][m4] = buf_load4(rK, (uint32_t)((q * 2 + m4) * 64 + lane) * 16u);
+        xel = tp.ws.el[blk];
+    };
+    prefetch(0);
+    __syncthreads(); // the state is in LDS
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = t_begin + c * BT;
+        const int n = t_end - t0 < BT ? t_end - t0 : BT;
+        v4f aw_op[NA4], aq_op[NA4], ak_op[RBW][2], ap_op[2], au[CBW];
+#pragma unroll
+        for (int m4 = 0; m4 < NA4; ++m4) {
+            aw_op[m4] = xw[m4];
+            aq_op[m4] = xq[m4];
+        }
+#pragma unroll
+        for (int q = 0; q < RBW; ++q) {
+            ak_op[q][0] = xk[q][0];
+            ak_op[q][1] = xk[q][1];
+        }
+        ap_op[0] = xp[0];
+        ap_op[1] = xp[1];
+#pragma unroll
+        for (int q = 0; q < CBW; ++q)
+            au[q] = xu[q];
+        const float el = xel;
+        prefetch(c + 1);
+        // the read-out rows of the chunk's real tokens; later rows fall outside
+        const int t0u = __builtin_amdgcn_readfirstlane(t0), nu = __builtin_amdgcn_readfirstlane(n);
+        const __amdgpu_buffer_rsrc_t rO = buf_rsrc(p.out + ((size_t)t0u * p.H_v + hv) * DV + col0,
+                                                   (uint32_t)(((nu - 1) * p.H_v * DV + DVS) * 2));
+
+        // ---- W S0 and Q~ S0 on this wave's tiles (row block rb)
+        v4f aw[CBW], aq[CBW];
+#pragma unroll
+        for (int q = 0; q < CBW; ++q)
+            aw[q] = aq[q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m4 = 0; m4 < NA4; ++m4)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int k = 16 * m4 + 4 * lk + e4;
+#pragma unroll
+                for (int q = 0; q < CBW; ++q) {
+                    const float bs = S[k * SP + (cb0 + q) * 16 + li];
+                    aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
+                    aq[q] = mma16(aq_op[m4][e4], bs, aq[q]);
+                }
+            }
+        // interleave the next chunk's loads with these products, so their
+        // address processing runs under the matrix cores instead of in front
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // one vector-memory read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMA
+        }
+        // U = U~ - W S0 on the same tiles -> LDS
+#pragma unroll
+        for (int q = 0; q < CBW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Um[(rb * 16 + 4 * lk + r) * SP + (cb0 + q) * 16 + li] = au[q][r] - aw[q][r];
+        __syncthreads(); // U complete; every read of S0 for this chunk is done
+
+        // ---- O = Q~ S0 + P U -> out
+#pragma unroll
+        for (int m4 = 0; m4 < 2; ++m4)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int k = 16 * m4 + 4 * lk + e4;
+#pragma unroll
+                for (int q = 0; q < CBW; ++q)
+                    aq[q] = mma16(ap_op[m4][e4], Um[k * SP + (cb0 + q) * 16 + li], aq[q]);
+            }
+#pragma unroll
+        for (int q = 0; q < CBW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    f32_to_bf16_rne(aq[q][r]), rO,
+                    (uint32_t)((rb * 16 + 4 * lk + r) * p.H_v * DV + (cb0 + q) * 16 + li) * 2u, 0, 0);
+
+        // ---- S1 = e^gamma_last S0 + K~^T U: this wave's row blocks, the slice's column blocks
+        {
+            v4f sacc[RBW][CBS];
+#pragma unroll
+            for (int q = 0; q < RBW; ++q)
+#pragma unroll
+                for (int jb = 0; jb < CBS; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sacc[q][jb][r] = el * S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li];
+#pragma unroll
+            for (int m4 = 0; m4 < 2; ++m4)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int k = 16 * m4 + 4 * lk + e4;
+#pragma unroll
+                    for (int q = 0; q < RBW; ++q)
+#pragma unroll
+                        for (int jb = 0; jb < CBS; ++jb)
+                            sacc[q][jb] = mma16(ak_op[q][m4][e4], Um[k * SP + jb * 16 + li], sacc[q][jb]);
+                }
+#pragma unroll
+            for (int q = 0; q < RBW; ++q)
+#pragma unroll
+                for (int jb = 0; jb < CBS; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li] = sacc[q][jb][r];
+        }
+        __syncthreads(); // S and U are free for the next chunk
+    }
+
+    // ---- the state's slice back to the slot
+    for (int e = tid; e < DK * DVS / 4; e += NT) {
+        const int i = e / (DVS / 4), j4 = e % (DVS / 4);
+        const v4f v = *reinterpret_cast<const v4f *>(&S[i * SP + 4 * j4]);
+        __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(tile + (size_t)i * DV + col0) + j4);
+    }
+    advance_windows<DK, DV, DVS>(p, hv, sl, t_begin, t_end, s);
+}
+
+// 16-column slices: the slice of the state stays in registers.  Wave w holds
+// row blocks w * RBW .. of the slice in the accumulator layout (lane j + 16 g,
+// element r: row 4 g + r of the block, column j), which with pass 1's operand
+// order is the B operand of a product over the state's rows as it stands:
+// step (row block R, r) takes row 16 R + 4 g + r at lane group g.  Each wave
+// forms W S0 and Q~ S0 over its own rows; one barrier a chunk sums the four
+// partial products (in LDS, double-buffered by chunk parity, so the next
+// chunk's writes cannot meet this chunk's reads) in a fixed order into
+// U = U~ - W S0, which every wave then holds in the accumulator layout: the B
+// operand, again as it stands, of its own rows' K~^T U and of a quarter of
+// P U.  The read-out is spread over the four waves a chunk late: wave w takes
+// P U for read-out row block w & 1 over tokens 16 (w >> 1) ..; waves 2-3 add
+// the summed Q~ S0 partials and leave that in LDS, and waves 0-1 add it to
+// theirs after the next chunk's barrier (one more barrier after the last
+// chunk) and store the rows.
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
+{
+    const PrefillParams &p = tp.p;
+    constexpr int NSL = DV / 16;
+    constexpr int NRB = DK / 16; // row blocks of the state
+    constexpr int RBW = NRB / 4; // row blocks a wave holds
+    static_assert(NRB % 4 == 0, "whole row blocks a wave");
+    constexpr int CHUNK_QK = BT * DK, CHUNK_P = BT * BT, CHUNK_U = BT * DV;
+
+    // partial products: [chunk parity][wave][W S0, Q~ S0][row block][lane]
+    __shared__ v4f part[2][4][2][2][64];
+    // Q~ S0 + P U over tokens 16 .. 31 from waves 2-3: [chunk parity][row block][lane]
+    __shared__ v4f osum[2][2][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, li = lane & 15, lk = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bh, sl;
+    walk_place(blockIdx.x, p.B * p.H_v, NSL, bh, sl);
+    const int hv = bh % p.H_v;
+    const int b = bh / p.H_v;
+    const int col0 = sl * 16;
+    int t_begin, t_end, s, nchunks;
+    size_t blk0;
+    if (!walk_setup<DV, 16>(tp, b, hv, col0, t_begin, t_end, s, nchunks, blk0))
+        return;
+    float *tile = p.state + ((size_t)s * p.H_v + hv) * (size_t)(DK * DV) + col0 + li;
+
+    // ---- this wave's rows of the slice -> registers (a lane group's 16 lanes
+    // read 64 contiguous bytes of a row)
+    v4f st[RBW];
+#pragma unroll
+    for (int q = 0; q < RBW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            st[q][r] = __builtin_nontemporal_load(tile + (size_t)((wv * RBW + q) * 16 + 4 * lk + r) * DV);
+
+    // ---- this wave's operands of a chunk: W and Q~ over its own rows (k
+    // blocks wv * RBW ..), K~^T for its own rows, U~ of the slice, and its
+    // quarter of P (row block wv & 1, k block wv >> 1), loaded one chunk ahead
+    // (two chunks ahead, in two sets, measured no faster).
+    constexpr int NLOAD = 6 * RBW + 3; // loads a wave issues a chunk
+    struct Ops {
+        v4f w[2][RBW], q[2][RBW], k[RBW][2], p, u[2];
+        float el;
+    };
+    auto prefetch = [&](int c, Ops &x) {
+        const bool real = c < nchunks;
+        const size_t blk = blk0 + (size_t)(real ? c : 0);
+        const __amdgpu_buffer_rsrc_t rW = buf_rsrc(tp.ws.wa + blk * CHUNK_QK, real ? CHUNK_QK * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(tp.ws.qa + blk * CHUNK_QK, real ? CHUNK_QK * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rK = buf_rsrc(tp.ws.ka + blk * CHUNK_QK + wv * RBW * 512, real ? RBW * 2048u : 0u);
+        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P, real ? CHUNK_P * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rU = buf_rsrc(tp.ws.ud + blk * CHUNK_U, real ? CHUNK_U * 4u : 0u);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int q = 0; q < RBW; ++q) {
+                const uint32_t o = (uint32_t)((mb * NRB + wv * RBW + q) * 64 + lane) * 16u;
+                x.w[mb][q] = buf_load4(rW, o);
+                x.q[mb][q] = buf_load4(rQ, o);
+            }
+#pragma unroll
+        for (int q = 0; q < RBW; ++q)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+                x.k[q][tb] = buf_load4(rK, (uint32_t)((q * 2 + tb) * 64 + lane) * 16u);
+        x.p = buf_load4(rP, (uint32_t)((((wv & 1) * 2 + (wv >> 1)) * 64 + lane) * 16u));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+            x.u[tb] = buf_load4(rU, (uint32_t)((tb * NSL + sl) * 64 + lane) * 16u);
+        x.el = tp.ws.el[blk];
+    };
+    // read-out row block wv (waves 0-1) of the chunk starting at token t0s,
+    // ns real tokens; later rows fall outside the resource.  (Only waves 0-1
+    // issue these: dropped stores on waves 2-3, which would make every
+    // wave's count of memory operations the same, measured slower.)
+    auto store_o = [&](const v4f o, int t0s, int ns) {
+        const int t0u = __builtin_amdgcn_readfirstlane(t0s), nu = __builtin_amdgcn_readfirstlane(ns);
+        const __amdgpu_buffer_rsrc_t rO =
+            buf_rsrc(p.out + ((size_t)t0u * p.H_v + hv) * DV + col0, (uint32_t)(((nu - 1) * p.H_v * DV + 16) * 2));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(o[r]), rO,
+                                                  (uint32_t)((wv * 16 + 4 * lk + r) * p.H_v * DV + li) * 2u, 0, 0);
+    };
+
+    v4f o_lo = {0.f, 0.f, 0.f, 0.f}; // waves 0-1: the last chunk's P U over tokens 0 .. 15
+    // chunk c with its operands in cur; chunk c + 1's loads go to nx, issued
+    // among its first products
+    auto walk_chunk = [&](int c, const Ops &cur, Ops &nx) {
+        const int t0 = t_begin + c * BT;
+        prefetch(c + 1, nx);
+
+        // ---- partial W S0 and Q~ S0 over this wave's rows
+        v4f pw[2], pq[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+            pw[mb] = pq[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < RBW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    pw[mb] = mma16(cur.w[mb][q][r], st[q][r], pw[mb]);
+                    pq[mb] = mma16(cur.q[mb][q][r], st[q][r], pq[mb]);
+                }
+        // the loads interleaved with these products, so their address
+        // processing runs under the matrix cores
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // one vector-memory read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // two MFMA
+        }
+        v4f(*pc)[2][2][64] = part[c & 1];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            pc[wv][0][mb][lane] = pw[mb];
+            pc[wv][1][mb][lane] = pq[mb];
+        }
+        __syncthreads();
+
+        // ---- U = U~ - (W S0), the partials summed in wave order (the same
+        // operands in the same order on every wave, so all four hold the same U)
+        v4f u[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            v4f ws = pc[0][0][tb][lane];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                const v4f x = pc[w][0][tb][lane];
+                ws = v4f{ws[0] + x[0], ws[1] + x[1], ws[2] + x[2], ws[3] + x[3]};
+            }
+            u[tb] = v4f{cur.u[tb][0] - ws[0], cur.u[tb][1] - ws[1], cur.u[tb][2] - ws[2], cur.u[tb][3] - ws[3]};
+        }
+
+        // ---- the previous chunk's read-out rows (a whole chunk: only the last
+        // can be partial), ahead of the state update, which then covers the
+        // stores' latency
+        if (wv < 2 && c > 0) {
+            const v4f x = osum[(c - 1) & 1][wv][lane];
+            store_o(v4f{x[0] + o_lo[0], x[1] + o_lo[1], x[2] + o_lo[2], x[3] + o_lo[3]}, t0 - BT, BT);
+        }
+        // ---- this wave's quarter of P U: read-out row block wv & 1, tokens 16 (wv >> 1) ..
+        {
+            const v4f ut = wv >= 2 ? u[1] : u[0];
+            v4f op = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                op = mma16(cur.p[r], ut[r], op);
+            if (wv >= 2) {
+                // + Q~ S0, its partials summed in wave order
+                v4f o = pc[0][1][wv & 1][lane];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) {
+                    const v4f x = pc[w][1][wv & 1][lane];
+                    o = v4f{o[0] + x[0], o[1] + x[1], o[2] + x[2], o[3] + x[3]};
+                }
+                osum[c & 1][wv & 1][lane] = v4f{o[0] + op[0], o[1] + op[1], o[2] + op[2], o[3] + op[3]};
+            } else {
+                o_lo = op;
+            }
+        }
+
+        // ---- S1 = e^gamma_last S0 + K~^T U on this wave's rows: each row
+        // block's product over the two token blocks in separate accumulators,
+        // interleaved, so no product waits on the one before it
+        {
+            v4f a0[RBW], a1[RBW];
+#pragma unroll
+            for (int q = 0; q < RBW; ++q) {
+                a0[q] = v4f{cur.el * st[q][0], cur.el * st[q][1], cur.el * st[q][2], cur.el * st[q][3]};
+                a1[q] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q = 0; q < RBW; ++q) {
+                    a0[q] = mma16(cur.k[q][0][r], u[0][r], a0[q]);
+                    a1[q] = mma16(cur.k[q][1][r], u[1][r], a1[q]);
+                }
+#pragma unroll
+            for (int q = 0; q < RBW; ++q)
+                st[q] = v4f{a0[q][0] + a1[q][0], a0[q][1] + a1[q][1], a0[q][2] + a1[q][2], a0[q][3] + a1[q][3]};
+        }
+    };
+
+    Ops ops;
+    prefetch(0, ops);
+    for (int c = 0; c < nchunks; ++c) {
+        const Ops cur = ops;
+        walk_chunk(c, cur, ops);
+    }
+    // ---- the last chunk's read-out rows
+    __syncthreads();
+    if (wv < 2) {
+        const int c = nchunks - 1, t0 = t_begin + c * BT;
+        const v4f x = osum[c & 1][wv][lane];
+        store_o(v4f{x[0] + o_lo[0], x[1] + o_lo[1], x[2] + o_lo[2], x[3] + o_lo[3]}, t0, t_end - t0);
+    }
+
+    // ---- the slice back to the slot
+#pragma unroll
+    for (int q = 0; q < RBW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __builtin_nontemporal_store(st[q][r], tile + (size_t)((wv * RBW + q) * 16 + 4 * lk + r) * DV);
+    advance_windows<DK, DV, 16>(p, hv, sl, t_begin, t_end, s);
 }
 
 template <int DK, int DV, int DVS>
@@ -778,11 +1029,13 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
     int nsl = 1;
     while (nsl < DV / 16 && heads * nsl < 256)
         nsl *= 2;
+    if (DV / nsl == 16)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&tp_inter16_kernel<DK, DV>),
+                               dim3((unsigned)(heads * (DV / 16))), dim3(NT), args, 0, stream);
     switch (nsl) {
     case 1: return launch_inter<DK, DV, DV>(tp, heads, stream);
     case 2: return launch_inter<DK, DV, DV / 2>(tp, heads, stream);
-    case 4: return launch_inter<DK, DV, DV / 4>(tp, heads, stream);
-    default: return launch_inter<DK, DV, (DV / 8 >= 16 ? DV / 8 : 16)>(tp, heads, stream);
+    default: return launch_inter<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>(tp, heads, stream);
     }
 }
 
