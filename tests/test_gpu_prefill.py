@@ -128,6 +128,17 @@ def test_two_pass_long_prompt_and_slices(gdn, torch):
            two_pass=True)
 
 
+@pytest.mark.parametrize("lengths,hk,hv", [
+    ([100, 33, 64, 5], 16, 16),                                     # 64 heads: 32-column slices
+    ([40, 1, 70, 32, 31, 65, 2, 50], 16, 16),                       # 128 heads: 64-column slices
+    ([9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20, 6], 2, 4),  # 68 heads: 8 past the last group of 8
+], ids=["4seq-slices32", "8seq-slices64", "17seq-slices32-tail"])
+def test_two_pass_wide_slices(gdn, torch, lengths, hk, hv):
+    """The walk over column slices 32 and 64 wide (state and U in LDS), and
+    prompt-head pairs past the last whole group of eight placed in order."""
+    _check(gdn, torch, gi.prefill(lengths, H_k=hk, H_v=hv, d=128, seed=len(lengths) + 90), two_pass=True)
+
+
 @PATHS
 def test_prefill_many_ragged_sequences(gdn, torch, two_pass):
     """300 sequences (more than one 256-wide tile of the two-pass chunk map,
