@@ -128,6 +128,13 @@ def test_two_pass_long_prompt_and_slices(gdn, torch):
            two_pass=True)
 
 
+def test_two_pass_bench_workload_one_long_prompt(gdn, torch):
+    """The prefill bench's single-prompt workload as it times it: one prompt of
+    4096 tokens at the 0.8B-like shapes (128 chunks, 16-column slices), every
+    output row and the final state against the oracle."""
+    _check(gdn, torch, gi.prefill([4096], H_k=16, H_v=16, d=128, seed=31), two_pass=True)
+
+
 @pytest.mark.parametrize("lengths,hk,hv", [
     ([100, 33, 64, 5], 16, 16),                                     # 64 heads: 32-column slices
     ([40, 1, 70, 32, 31, 65, 2, 50], 16, 16),                       # 128 heads: 64-column slices
