@@ -275,8 +275,6 @@ gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf1
         return GDN_ERR_SHAPE;
     if (W != 4)
         return GDN_ERR_UNSUPPORTED;
-    if (B == 0)
-        return GDN_OK;
     gdn::ConvParams p{};
     p.x = x;
     p.x_row_stride = x_row_stride;
