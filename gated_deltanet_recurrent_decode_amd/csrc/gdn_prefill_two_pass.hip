@@ -323,12 +323,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const float *Asrc = wv < 2 ? Ks : Qs;
             const int rb = wv & 1;
             v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-            for (int k0 = 0; k0 < DK; k0 += 4) {
-                const float a = Asrc[(rb * 16 + li) * KP + k0 + lk];
+            // a dot product over k, so its k-steps may run in any order: step
+            // (m, r) takes k = 16 m + 4 lk + r, and a lane's four values of a k
+            // block are one 16-byte read
+#pragma unroll 4
+            for (int m = 0; m < DK / 16; ++m) {
+                const v4f a4 = *reinterpret_cast<const v4f *>(&Asrc[(rb * 16 + li) * KP + 16 * m + 4 * lk]);
+                v4f b4[2];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    acc[cb] = mma16(a, Ks[(cb * 16 + li) * KP + k0 + lk], acc[cb]);
+                    b4[cb] = *reinterpret_cast<const v4f *>(&Ks[(cb * 16 + li) * KP + 16 * m + 4 * lk]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[cb] = mma16(a4[r], b4[cb][r], acc[cb]);
             }
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
