@@ -579,15 +579,17 @@ __device__ __forceinline__ bool walk_setup(const TwoPassParams &tp, int b, int h
 // takes row block w & 1 of W S0, Q~ S0 and O and half the slice's column
 // blocks, and row blocks w * DK / 64 .. of the state update.  The k-steps of
 // every product run in pass 1's operand order (k = 16 m4 + 4 g + e4 at lane
-// group g), so the B operands are read from LDS at those rows.
+// group g), and LDS holds S and U transposed (column-major), so a lane's four
+// k-steps of a k block are four consecutive words: one 16-byte read, and the
+// accumulator layout's four rows one 16-byte write.
 template <int DK, int DV, int DVS>
 __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
 {
     const PrefillParams &p = tp.p;
     constexpr int NSL = DV / DVS;
-    // S and U are B operands read down a column, four rows apart across lane
-    // groups: a pitch of DVS + 4 puts the four groups 16 banks apart
-    constexpr int SP = DVS + 4;
+    // St[col][k] and Ut[col][token]: pitches of 4 mod 32 words put the 16
+    // columns a lane group reads 4 banks apart (16-byte accesses, conflict-free)
+    constexpr int SPT = DK + 4, UPT = BT + 4;
     constexpr int CBS = DVS / 16; // column blocks of the slice
     static_assert(CBS >= 2, "16-column slices take tp_inter16_kernel");
     constexpr int CBW = CBS / 2;  // column blocks of W S0, Q~ S0 and O a wave takes
@@ -595,8 +597,8 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     constexpr int RBW = DK / 64;  // row blocks of S a wave updates
     constexpr int CHUNK_QK = BT * DK, CHUNK_P = BT * BT, CHUNK_U = BT * DV;
 
-    __shared__ __align__(16) float S[DK * SP];
-    __shared__ __align__(16) float Um[BT * SP];
+    __shared__ __align__(16) float St[DVS * SPT];
+    __shared__ __align__(16) float Ut[DVS * UPT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
@@ -614,11 +616,16 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     const int rb = wv & 1;
     const int cb0 = (wv >> 1) * CBW;
 
-    // ---- the state's column slice -> LDS (16-byte streaming loads)
+    // ---- the state's column slice -> LDS, transposed: a lane takes four rows
+    // of one column (streaming loads, consecutive lanes on consecutive columns,
+    // so each wave load covers whole rows) and writes them as one 16-byte run
     for (int e = tid; e < DK * DVS / 4; e += NT) {
-        const int i = e / (DVS / 4), j4 = e % (DVS / 4);
-        const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(tile + (size_t)i * DV + col0) + j4);
-        *reinterpret_cast<v4f *>(&S[i * SP + 4 * j4]) = v;
+        const int j = e % DVS, i4 = e / DVS;
+        v4f v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            v[r] = __builtin_nontemporal_load(tile + (size_t)(4 * i4 + r) * DV + col0 + j);
+        *reinterpret_cast<v4f *>(&St[j * SPT + 4 * i4]) = v;
     }
 
     // ---- this wave's operands of a chunk, loaded one chunk ahead straight
@@ -692,17 +699,19 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
         for (int q = 0; q < CBW; ++q)
             aw[q] = aq[q] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m4 = 0; m4 < NA4; ++m4)
+        for (int m4 = 0; m4 < NA4; ++m4) {
+            v4f bs[CBW];
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int k = 16 * m4 + 4 * lk + e4;
+            for (int q = 0; q < CBW; ++q)
+                bs[q] = *reinterpret_cast<const v4f *>(&St[((cb0 + q) * 16 + li) * SPT + 16 * m4 + 4 * lk]);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
                 for (int q = 0; q < CBW; ++q) {
-                    const float bs = S[k * SP + (cb0 + q) * 16 + li];
-                    aw[q] = mma16(aw_op[m4][e4], bs, aw[q]);
-                    aq[q] = mma16(aq_op[m4][e4], bs, aq[q]);
+                    aw[q] = mma16(aw_op[m4][e4], bs[q][e4], aw[q]);
+                    aq[q] = mma16(aq_op[m4][e4], bs[q][e4], aq[q]);
                 }
-            }
+        }
         // interleave the next chunk's loads with these products, so their
         // address processing runs under the matrix cores instead of in front
 #pragma unroll
@@ -713,21 +722,23 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
         // U = U~ - W S0 on the same tiles -> LDS
 #pragma unroll
         for (int q = 0; q < CBW; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Um[(rb * 16 + 4 * lk + r) * SP + (cb0 + q) * 16 + li] = au[q][r] - aw[q][r];
+            *reinterpret_cast<v4f *>(&Ut[((cb0 + q) * 16 + li) * UPT + rb * 16 + 4 * lk]) =
+                v4f{au[q][0] - aw[q][0], au[q][1] - aw[q][1], au[q][2] - aw[q][2], au[q][3] - aw[q][3]};
         __syncthreads(); // U complete; every read of S0 for this chunk is done
 
         // ---- O = Q~ S0 + P U -> out
 #pragma unroll
-        for (int m4 = 0; m4 < 2; ++m4)
+        for (int m4 = 0; m4 < 2; ++m4) {
+            v4f ub[CBW];
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int k = 16 * m4 + 4 * lk + e4;
+            for (int q = 0; q < CBW; ++q)
+                ub[q] = *reinterpret_cast<const v4f *>(&Ut[((cb0 + q) * 16 + li) * UPT + 16 * m4 + 4 * lk]);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
                 for (int q = 0; q < CBW; ++q)
-                    aq[q] = mma16(ap_op[m4][e4], Um[k * SP + (cb0 + q) * 16 + li], aq[q]);
-            }
+                    aq[q] = mma16(ap_op[m4][e4], ub[q][e4], aq[q]);
+        }
 #pragma unroll
         for (int q = 0; q < CBW; ++q)
 #pragma unroll
@@ -742,37 +753,37 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
 #pragma unroll
             for (int q = 0; q < RBW; ++q)
 #pragma unroll
-                for (int jb = 0; jb < CBS; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sacc[q][jb][r] = el * S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li];
+                for (int jb = 0; jb < CBS; ++jb) {
+                    const v4f s4 = *reinterpret_cast<const v4f *>(&St[(jb * 16 + li) * SPT + (wv * RBW + q) * 16 + 4 * lk]);
+                    sacc[q][jb] = v4f{el * s4[0], el * s4[1], el * s4[2], el * s4[3]};
+                }
 #pragma unroll
             for (int m4 = 0; m4 < 2; ++m4)
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int k = 16 * m4 + 4 * lk + e4;
+                for (int jb = 0; jb < CBS; ++jb) {
+                    const v4f ub = *reinterpret_cast<const v4f *>(&Ut[(jb * 16 + li) * UPT + 16 * m4 + 4 * lk]);
 #pragma unroll
-                    for (int q = 0; q < RBW; ++q)
+                    for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
-                        for (int jb = 0; jb < CBS; ++jb)
-                            sacc[q][jb] = mma16(ak_op[q][m4][e4], Um[k * SP + jb * 16 + li], sacc[q][jb]);
+                        for (int q = 0; q < RBW; ++q)
+                            sacc[q][jb] = mma16(ak_op[q][m4][e4], ub[e4], sacc[q][jb]);
                 }
 #pragma unroll
             for (int q = 0; q < RBW; ++q)
 #pragma unroll
                 for (int jb = 0; jb < CBS; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        S[((wv * RBW + q) * 16 + 4 * lk + r) * SP + jb * 16 + li] = sacc[q][jb][r];
+                    *reinterpret_cast<v4f *>(&St[(jb * 16 + li) * SPT + (wv * RBW + q) * 16 + 4 * lk]) = sacc[q][jb];
         }
         __syncthreads(); // S and U are free for the next chunk
     }
 
-    // ---- the state's slice back to the slot
+    // ---- the state's slice back to the slot (the same mapping)
     for (int e = tid; e < DK * DVS / 4; e += NT) {
-        const int i = e / (DVS / 4), j4 = e % (DVS / 4);
-        const v4f v = *reinterpret_cast<const v4f *>(&S[i * SP + 4 * j4]);
-        __builtin_nontemporal_store(v, reinterpret_cast<v4f *>(tile + (size_t)i * DV + col0) + j4);
+        const int j = e % DVS, i4 = e / DVS;
+        const v4f v = *reinterpret_cast<const v4f *>(&St[j * SPT + 4 * i4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __builtin_nontemporal_store(v[r], tile + (size_t)(4 * i4 + r) * DV + col0 + j);
     }
     advance_windows<DK, DV, DVS>(p, hv, sl, t_begin, t_end, s);
 }
