@@ -38,18 +38,24 @@ MUTATIONS = {
 }
 
 
-def _run_mutant(name, tmp):
+# the mistakes in the delta rule, the conv and the L2 norm, which the property
+# tests (tests/test_oracle_properties.py) must catch on their own as well
+PROPERTY_MUTATIONS = ("delta_sign", "no_decay", "pred_transposed", "readout_with_key", "beta_dropped",
+                      "conv_taps_reversed", "l2_no_sqrt")
+
+
+def _run_mutant(name, tmp, tests="test_oracle_pins.py"):
     old, new = MUTATIONS[name]
     src = open(SRC).read()
     assert src.count(old) == 1, f"{name}: pattern not found exactly once"
-    path = os.path.join(tmp, f"{name}.c")
-    lib = os.path.join(tmp, f"lib_{name}.so")
+    path = os.path.join(tmp, f"{name}-{tests}.c")
+    lib = os.path.join(tmp, f"lib_{name}-{tests}.so")
     open(path, "w").write(src.replace(old, new))
     subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC", "-o", lib, path, "-lm"],
                    check=True)
     env = dict(os.environ, GDN_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", tests)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return r.returncode
 
@@ -60,3 +66,12 @@ def test_every_planted_mistake_fails_a_pin():
             rcs = dict(zip(MUTATIONS, ex.map(lambda n: _run_mutant(n, tmp), MUTATIONS)))
     survivors = [n for n, rc in rcs.items() if rc == 0]
     assert not survivors, f"planted mistakes not caught by any pin: {survivors}"
+
+
+def test_property_tests_alone_catch_the_delta_rule_conv_and_norm_mistakes():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            rcs = dict(zip(PROPERTY_MUTATIONS,
+                           ex.map(lambda n: _run_mutant(n, tmp, "test_oracle_properties.py"), PROPERTY_MUTATIONS)))
+    survivors = [n for n, rc in rcs.items() if rc == 0]
+    assert not survivors, f"planted mistakes the property tests let through: {survivors}"
