@@ -575,15 +575,16 @@ __device__ __forceinline__ bool walk_setup(const TwoPassParams &tp, int b, int h
     return true;
 }
 
-// Slices of 32 columns or more: the slice of the state and U in LDS.  Wave w
+// Slices of 32 or 64 columns: the slice of the state and U in LDS.  Wave w
 // takes row block w & 1 of W S0, Q~ S0 and O and half the slice's column
 // blocks, and row blocks w * DK / 64 .. of the state update.  The k-steps of
 // every product run in pass 1's operand order (k = 16 m4 + 4 g + e4 at lane
 // group g), and LDS holds S and U transposed (column-major), so a lane's four
 // k-steps of a k block are four consecutive words: one 16-byte read, and the
 // accumulator layout's four rows one 16-byte write.
+// at most 256 registers a lane: two workgroups a CU (LDS allows two at 64 columns)
 template <int DK, int DV, int DVS>
-__global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void tp_inter_kernel(TwoPassParams tp)
 {
     const PrefillParams &p = tp.p;
     constexpr int NSL = DV / DVS;
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(NT) void tp_inter_kernel(TwoPassParams tp)
     // columns a lane group reads 4 banks apart (16-byte accesses, conflict-free)
     constexpr int SPT = DK + 4, UPT = BT + 4;
     constexpr int CBS = DVS / 16; // column blocks of the slice
-    static_assert(CBS >= 2, "16-column slices take tp_inter16_kernel");
+    static_assert(CBS == 2 || CBS == 4, "16-column slices take tp_inter16_kernel");
     constexpr int CBW = CBS / 2;  // column blocks of W S0, Q~ S0 and O a wave takes
     constexpr int NA4 = DK / 16;  // float4 a lane holds of one A-operand tile over k = d_k
     constexpr int RBW = DK / 64;  // row blocks of S a wave updates
@@ -1044,18 +1045,21 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     // column slices: double them until the walk has 256 workgroups or the
-    // slices are 16 columns wide
+    // slices are 16 columns wide, and keep them at most 64 columns wide (two
+    // workgroups a CU then fit; with whole 128-column slices, one a CU, 16 x
+    // 512 took 10 us and 128 x 64 71 us longer)
     const long long heads = (long long)p.B * p.H_v;
     int nsl = 1;
     while (nsl < DV / 16 && heads * nsl < 256)
         nsl *= 2;
-    if (DV / nsl == 16)
+    if (DV / nsl > 64)
+        nsl = DV / 64;
+    switch (DV / nsl) {
+    case 16:
         return hipLaunchKernel(reinterpret_cast<const void *>(&tp_inter16_kernel<DK, DV>),
                                dim3((unsigned)(heads * (DV / 16))), dim3(NT), args, 0, stream);
-    switch (nsl) {
-    case 1: return launch_inter<DK, DV, DV>(tp, heads, stream);
-    case 2: return launch_inter<DK, DV, DV / 2>(tp, heads, stream);
-    default: return launch_inter<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>(tp, heads, stream);
+    case 32: return launch_inter<DK, DV, 32>(tp, heads, stream);
+    default: return launch_inter<DK, DV, 64>(tp, heads, stream);
     }
 }
 
