@@ -121,8 +121,9 @@ def test_prefill_08b_shapes(gdn, torch, two_pass):
 
 
 def test_two_pass_long_prompt_and_slices(gdn, torch):
-    """One long prompt (the column-sliced walk, every chunk in flight in pass 1),
-    then many short ones (whole-tile walk), at the 0.8B shapes."""
+    """One long prompt (16-column slices, the state in registers; every chunk in
+    flight in pass 1), then many short ones (64-column slices, the state in LDS),
+    at the 0.8B shapes."""
     _check(gdn, torch, gi.prefill([1000], H_k=16, H_v=16, d=128, seed=21), two_pass=True)
     _check(gdn, torch, gi.prefill([3, 40, 1, 33] * 4 + [2] * 8, H_k=16, H_v=16, d=128, N=97, seed=22),
            two_pass=True)
