@@ -893,10 +893,9 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
     };
 
     v4f o_lo = {0.f, 0.f, 0.f, 0.f}; // waves 0-1: the last chunk's P U over tokens 0 .. 15
-    // chunk c with its operands in cur; chunk c + 1's loads go to nx, issued
-    // among its first products
-    auto walk_chunk = [&](int c, const Ops &cur, Ops &nx) {
-        const int t0 = t_begin + c * BT;
+    // chunk c's first products, from its operands in cur and the state entering
+    // it, into LDS; chunk c + 1's loads go to nx, issued among the products
+    auto first_products = [&](int c, const Ops &cur, Ops &nx) {
         prefetch(c + 1, nx);
 
         // ---- partial W S0 and Q~ S0 over this wave's rows
@@ -926,7 +925,11 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
             pc[wv][0][mb][lane] = pw[mb];
             pc[wv][1][mb][lane] = pq[mb];
         }
-        __syncthreads();
+    };
+    // the rest of chunk c, after the barrier that follows its first products
+    auto after_barrier = [&](int c, const Ops &cur) {
+        const int t0 = t_begin + c * BT;
+        v4f(*pc)[2][2][64] = part[c & 1];
 
         // ---- U = U~ - (W S0), the partials summed in wave order (the same
         // operands in the same order on every wave, so all four hold the same U)
@@ -993,11 +996,31 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
         }
     };
 
-    Ops ops;
-    prefetch(0, ops);
-    for (int c = 0; c < nchunks; ++c) {
-        const Ops cur = ops;
-        walk_chunk(c, cur, ops);
+    // The walk turned so that one pass of the loop holds chunk c's state update
+    // and chunk c + 1's first products: the products that need the new state
+    // then follow its computation with no loop edge between (after the last
+    // chunk they run on zero operands and their results are not read).
+    // Two operand sets used in turn (chunk c in one, c + 1 in the other), so
+    // no set is copied: a copy would wait for loads just issued.
+    // The loop takes whole pairs and an odd last chunk follows it, so the loop
+    // body has no branch: a path that skipped its second half would make every
+    // wait at the top of the loop take all memory operations in flight.
+    Ops opa, opb;
+    prefetch(0, opa);
+    first_products(0, opa, opb);
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        __syncthreads();
+        after_barrier(c, opa);
+        first_products(c + 1, opb, opa);
+        __syncthreads();
+        after_barrier(c + 1, opb);
+        first_products(c + 2, opa, opb);
+    }
+    if (c < nchunks) {
+        __syncthreads();
+        after_barrier(c, opa);
+        first_products(c + 1, opb, opa);
     }
     // ---- the last chunk's read-out rows
     __syncthreads();
