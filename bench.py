@@ -1,7 +1,7 @@
 """Benchmark of the pooled GDN decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows B]
-                    [--mode twin|inplace|tokens|prefill|stack] [--tokens T] [--prefill-len L]
+                    [--mode twin|inplace|tokens|prefill|stack|slotops] [--tokens T] [--prefill-len L]
                     [--layers L] [--commit fused|separate] [--hot] [--graph] [--no-cpu] [--no-calib]
 
 Workload: one 0.8B-like GDN layer -- B = 64 rows, 16 key and 16 value heads,
@@ -27,7 +27,9 @@ to enqueue the whole loop, so the GPU runs the steps back to back and the
 Python launch cost never shows up as GPU idle time.  value = rows/s from the
 loop without per-kernel events; roofline = the step kernel's algorithmic bytes
 over its mean duration, from fence-free HIP events around every launch of a
-second identical loop.  Prints ONE JSON line on stdout.
+second identical loop.  Every mode adds cpu_baseline: the fp64 oracle timed
+on the host on a bounded sample of the same workload (--no-cpu skips it).
+Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -170,41 +172,22 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(seconds: float = 10.0, threads: int | None = None) -> dict:
-    """The fp64 oracle, as it stands, on the 64-row workload: first one host
-    thread over 8-row calls, then `threads` host threads (default: the host's
-    CPUs, at most 16), each calling the oracle on its own slice of the rows
-    (the oracle's ctypes calls release the GIL, so the slices run in
-    parallel).  Each leg runs for about `seconds` / 2 of wall time."""
+def _oracle_legs(call, seconds: float, threads: int):
+    """Time `call(k, n)` -- thread k of n doing one piece of its own share of the
+    sample and returning the units it did -- first on one host thread, then on
+    `threads` threads (the oracle's ctypes calls release the GIL, so the threads
+    run in parallel), each leg for about `seconds` / 2 of wall time."""
     import threading
 
-    import gdn_inputs as gi
-    import oracle
-
-    case = gi.qwen08b(B=64)
-    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
-    st, cs = pool.state.copy(), pool.conv_state.copy()
-
-    def rows_call(lo, hi):
-        sl = slice(lo, hi)
-        oracle.gdn_decode_step(np.ascontiguousarray(step.x[sl]), pool.conv_w, None, cs, st,
-                               np.ascontiguousarray(step.g[sl]), np.ascontiguousarray(step.beta[sl]),
-                               np.ascontiguousarray(pool.read_slot[sl]), np.ascontiguousarray(pool.write_slot[sl]),
-                               H_k=s.H_k)
-
-    def leg(n_threads, budget):
-        per = 64 // n_threads
-        done = [0] * n_threads
+    def leg(n, budget):
+        done = [0] * n
         t0 = time.perf_counter()
 
         def work(k):
-            # each thread owns rows [k*per, (k+1)*per): disjoint slots, so the
-            # shared pool arrays are written at disjoint places
             while time.perf_counter() - t0 < budget:
-                rows_call(k * per, (k + 1) * per)
-                done[k] += per
+                done[k] += call(k, n)
 
-        ths = [threading.Thread(target=work, args=(k,)) for k in range(n_threads)]
+        ths = [threading.Thread(target=work, args=(k,)) for k in range(n)]
         for th in ths:
             th.start()
         for th in ths:
@@ -212,16 +195,109 @@ def cpu_baseline(seconds: float = 10.0, threads: int | None = None) -> dict:
         dt = time.perf_counter() - t0
         return sum(done) / dt, sum(done), dt
 
-    n = threads or max(1, min(16, os.cpu_count() or 1))
-    while 64 % n:
+    return leg(1, seconds / 2), leg(threads, seconds / 2)
+
+
+def _host_threads(divides: int | None = None) -> int:
+    n = max(1, min(16, os.cpu_count() or 1))
+    while divides and divides % n:
         n -= 1
-    one, rows1, dt1 = leg(1, seconds / 2)
-    many, rowsn, dtn = leg(n, seconds / 2)
-    return {"value": many, "unit": "rows/s", "cores": n, "kind": "oracle",
-            "sample": f"the 64-row workload's decode step, fp64 C loops: {rowsn} rows in {dtn:.1f} s on {n} host "
-                      f"threads ({64 // n} rows a call per thread); one thread: {rows1} rows in {dt1:.1f} s",
-            "single_thread_rows_per_s": one, "us_per_64_row_step": 64 / many * 1e6,
-            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
+    return n
+
+
+def cpu_baseline(args, seconds: float = 10.0) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the workload the
+    bench line times (the same shapes, tokens a row and write mode), on one host
+    thread and then on all of them (at most 16), each thread on its own rows,
+    prompts or slots so that the shared pool arrays are written at disjoint
+    places.  `value` is the all-threads rate in the bench line's unit."""
+    import gdn_inputs as gi
+    import oracle
+
+    mode = args.mode
+    if mode in ("twin", "inplace", "tokens", "stack"):
+        if mode == "stack":
+            shape = gi.Shape(B=64, T=1, H_k=16, H_v=32, d_k=128, d_v=128, W=4, N=129)
+            case = gi.make_case("9b-oracle", shape, seed=0)
+        else:
+            T = args.tokens
+            rows = 64 if mode != "tokens" else min(64, 512 // (1 + T))
+            case = gi.qwen08b(B=rows, T=T, twin=mode == "twin")
+        s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+        st, cs = pool.state.copy(), pool.conv_state.copy()
+        n = _host_threads(s.B)
+        if mode == "tokens":
+            perm = np.random.Generator(np.random.PCG64(1)).permutation(DRAWN_SLOTS).astype(np.int32) + 1
+            rd_all = perm[:s.B]
+            tok_all = perm[s.B:s.B * (1 + s.T)].reshape(s.B, s.T)
+
+        def call(k, nthreads):
+            per = s.B // nthreads
+            sl = slice(k * per, (k + 1) * per)
+            a = (np.ascontiguousarray(step.x[sl]), pool.conv_w, None, cs, st, np.ascontiguousarray(step.g[sl]),
+                 np.ascontiguousarray(step.beta[sl]))
+            if mode == "tokens":
+                oracle.gdn_decode_step_tokens(*a, np.ascontiguousarray(rd_all[sl]), np.ascontiguousarray(tok_all[sl]),
+                                              H_k=s.H_k)
+            else:
+                oracle.gdn_decode_step(*a, np.ascontiguousarray(pool.read_slot[sl]),
+                                       np.ascontiguousarray(pool.write_slot[sl]) if mode in ("twin", "stack") else None,
+                                       H_k=s.H_k)
+            return per
+
+        (one, u1, dt1), (many, un, dtn) = _oracle_legs(call, seconds, n)
+        if mode == "stack":
+            # a row of the stack is a row through every layer; each layer is the same work
+            one, many = one / args.layers, many / args.layers
+            what = (f"one 9B-like layer's decode step (16 key / 32 value heads of 128, 8192 channels, twin): {un} "
+                    f"row-layers in {dtn:.1f} s on {n} host threads, rates divided by the {args.layers} layers")
+        else:
+            what = (f"the 0.8B-like layer's decode step, {s.T} token{'s' if s.T > 1 else ''} a row, "
+                    f"{ {'twin': 'twin-slot write', 'inplace': 'in place', 'tokens': 'a state kept per token'}[mode]}: "
+                    f"{un} rows in {dtn:.1f} s on {n} host threads ({s.B // n} rows a call per thread)")
+        unit = "rows/s"
+    elif mode == "prefill":
+        L = args.prefill_len
+        piece = min(L, 128)
+        n = _host_threads()
+        case = gi.prefill([piece] * n, H_k=16, H_v=16, d=128, seed=0)
+        s, pool = case.shape, case.pool
+        st, cs = pool.state.copy(), pool.conv_state.copy()
+
+        def call(k, nthreads):
+            a, e = int(case.cu_seqlens[k]), int(case.cu_seqlens[k + 1])
+            # prompt k continues on its own slot: each call is the next `piece` tokens of a prompt
+            oracle.gdn_decode_step(np.ascontiguousarray(case.x[None, a:e]), pool.conv_w, None, cs, st,
+                                   np.ascontiguousarray(case.g[None, a:e]), np.ascontiguousarray(case.beta[None, a:e]),
+                                   np.ascontiguousarray(pool.read_slot[k:k + 1]), None, H_k=s.H_k)
+            return e - a
+
+        (one, u1, dt1), (many, un, dtn) = _oracle_legs(call, seconds, n)
+        what = (f"prefill as its definition, the in-place recurrence token by token (0.8B-like heads), each host "
+                f"thread on its own prompt in pieces of {piece} tokens: {un} tokens in {dtn:.1f} s on {n} threads")
+        unit = "tokens/s"
+    else:  # slot ops: the copy the bench line reports
+        case = gi.qwen08b(B=256)
+        pool = case.pools[0]
+        st, cs = pool.state.copy(), pool.conv_state.copy()
+        n = _host_threads(256)
+        per_call = 8
+        perm = np.random.Generator(np.random.PCG64(2)).permutation(DRAWN_SLOTS).astype(np.int32) + 1
+
+        def call(k, nthreads):
+            # thread k copies among its own 512/n slots: sources from its first half to its second
+            own = perm[k * (DRAWN_SLOTS // nthreads):(k + 1) * (DRAWN_SLOTS // nthreads)]
+            h = min(per_call, own.size // 2)
+            oracle.slot_copy(st, cs, np.ascontiguousarray(own[:h]), np.ascontiguousarray(own[h:2 * h]))
+            return h
+
+        (one, u1, dt1), (many, un, dtn) = _oracle_legs(call, seconds, n)
+        what = (f"slot copy (state and conv window of the 0.8B-like layer, 1 MiB + 36 KiB a slot), {per_call} slots a "
+                f"call per thread: {un} slots in {dtn:.1f} s on {n} host threads")
+        unit = "slots/s"
+    return {"value": many, "unit": unit, "cores": n, "kind": "oracle",
+            "sample": f"{what}; one thread: {u1} in {dt1:.1f} s",
+            "single_thread_rate": one, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 class Bench:
@@ -739,19 +815,28 @@ def main() -> int:
         if args.rows < 1 or args.layers < 1:
             print("bench.py: the stack needs --rows >= 1 and --layers >= 1", file=sys.stderr)
             return 2
-        print(json.dumps(run_stack(args)), flush=True)
+        result = run_stack(args)
+        if not args.no_cpu:
+            result["cpu_baseline"] = cpu_baseline(args, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
         return 0
     if args.mode == "prefill":
         if args.rows < 1 or args.prefill_len < 1 or 4 * args.rows > 512:
             print("bench.py: prefill needs 1 <= --rows <= 128 and --prefill-len >= 1", file=sys.stderr)
             return 2
-        print(json.dumps(run_prefill(args)), flush=True)
+        result = run_prefill(args)
+        if not args.no_cpu:
+            result["cpu_baseline"] = cpu_baseline(args, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
         return 0
     if args.mode == "slotops":
         if not 1 <= args.rows <= 256:
             print("bench.py: slot ops take 1 <= --rows <= 256", file=sys.stderr)
             return 2
-        print(json.dumps(run_slotops(args)), flush=True)
+        result = run_slotops(args)
+        if not args.no_cpu:
+            result["cpu_baseline"] = cpu_baseline(args, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
         return 0
     if args.real is not None and (args.mode == "tokens" or not 1 <= args.real <= args.rows):
         print("bench.py: --real takes 1 <= REAL <= --rows, twin or in place", file=sys.stderr)
@@ -835,7 +920,7 @@ def main() -> int:
     if not args.no_calib and not b.tokens_mode:
         result["calibration"] = b.calibration()
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 
