@@ -1,0 +1,66 @@
+"""The bench's accounting, on the CPU: the algorithmic bytes behind
+roofline.achieved, the prefill's matrix-core flops, and the cold-cache rotation.
+Each expected figure is counted here item by item from the data the step must
+move (or the products the chunked form executes), not through the bench's own
+formula."""
+import bench
+
+MiB = 1 << 20
+
+
+def _row_bytes_08b(tokens=1):
+    """One real row of the 0.8B-like layer (16 value heads of 128 x 128 fp32,
+    6144 bf16 channels, conv width 4), counted item by item."""
+    state = 16 * 128 * 128 * 4            # one slot's state, read once and written once
+    window = 3 * 6144 * 2                 # one slot's conv window, read once and written once
+    x = tokens * 6144 * 2                 # the row's pre-conv activations
+    out = tokens * 16 * 128 * 2           # bf16 read-out
+    gates = tokens * 16 * 4 * 2           # g and beta
+    return 2 * state + 2 * window + x + out + gates
+
+
+def test_decode_bytes_at_64_rows_twin():
+    # 2,097,152 state + 73,728 window + 12,288 x + 4,096 out + 128 gates = 2,187,392 a row, plus slot indices:
+    # the read and write slot, and the swapped pair the fused commit writes (4 x 4 B)
+    assert _row_bytes_08b() == 2_187_392
+    weights = 6144 * 4 * 2
+    want = 64 * (2_187_392 + 16) + weights
+    assert want == 140_043_264
+    assert bench.algorithmic_bytes(64, 0, 1, 16, 128, 128, 6144, 4, "twin") == want
+
+
+def test_decode_bytes_in_place_with_tokens_and_padding():
+    # 46 real rows of 4 tokens in place (one read slot each), 82 padding rows that
+    # read their slot index and write a zero read-out of 4 tokens
+    real = _row_bytes_08b(tokens=4) + 4
+    pad = 4 + 4 * 16 * 128 * 2
+    want = 46 * real + 82 * pad + 6144 * 4 * 2
+    assert bench.algorithmic_bytes(46, 82, 4, 16, 128, 128, 6144, 4, "inplace") == want
+
+
+def test_decode_bytes_with_a_state_per_token():
+    # 3 tokens: one read of the read slot's state and window, a write of both per
+    # token; the read slot and three token slots are read
+    state, window = 16 * 128 * 128 * 4, 3 * 6144 * 2
+    row = 4 * (state + window) + 3 * (6144 * 2 + 16 * 128 * 2 + 16 * 4 * 2) + 4 * 4
+    assert bench.algorithmic_bytes(64, 0, 3, 16, 128, 128, 6144, 4, "tokens") == 64 * row + 6144 * 4 * 2
+
+
+def test_prefill_flops_per_token_at_the_08b_shapes():
+    # per chunk of 32 tokens and value head: W S0, Q~ S0 and K~^T U (32 x 128 x 128
+    # each), K K^T and Q K^T (32 x 32 x 128 each), P U (32 x 32 x 128); 2 flops a
+    # multiply-add; 16 value heads
+    per_chunk = 3 * (2 * 32 * 128 * 128) + 2 * (2 * 32 * 32 * 128) + 2 * 32 * 32 * 128
+    assert per_chunk == 3_932_160
+    assert bench.prefill_flops_per_token(16, 128, 128) == 16 * per_chunk / 32 == 1_966_080
+
+
+def test_cold_rotation_row_sets():
+    # 64 twin rows write 64 MiB a step: 12 more sets must pass before a set comes
+    # back for 768 MiB to be written in between, and a set takes 128 slots
+    assert bench.row_sets("twin", 64, 1, MiB, hot=False) == (13, 128)
+    assert bench.row_sets("inplace", 64, 1, MiB, hot=False) == (13, 64)
+    # at least four sets even when a step writes more than 768 MiB
+    assert bench.row_sets("twin", 256, 1, 4 * MiB, hot=False) == (4, 512)
+    assert bench.row_sets("tokens", 16, 4, MiB, hot=False) == (13, 80)
+    assert bench.row_sets("twin", 64, 1, MiB, hot=True) == (1, 128)
