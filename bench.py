@@ -56,12 +56,20 @@ MEASURED_TRAFFIC = {"kernel_sources_sha256": "acc6ab4fc9a51c7da1642106e6d5f9dd14
                     "workload": (64, "twin", "fused", False), "bytes_per_launch": 141_828_160}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
+# The same counters over one call of the two-pass prefill (chunk map, pass 1 and
+# pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
+# summary with its commands is in profiles/.  Valid only for these sources.
+MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "27a185d90d7dfb6a36a28a726de88cdfa09b111a3f371c7a481752c3f72beab3",
+                            "bytes_per_call": {(16, 512): 754_782_553, (1, 4096): 364_300_837}}
+PREFILL_SOURCES = ("gdn_prefill_two_pass.hip", "prefill_internal.h", "step_common.h", "device_common.h",
+                   "gdn_internal.h")
 
-def kernel_sources_sha256() -> str:
+
+def kernel_sources_sha256(files=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
     base = os.path.join(ROOT, "gated_deltanet_recurrent_decode_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(base, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -758,6 +766,9 @@ def run_prefill(args) -> dict:
     k_us = float(us.mean())
     achieved = flops / (k_us * 1e-6) / 1e12
     hbm = tokens * (s.C * 2 + s.H_v * s.d_v * 2 + 2 * s.H_v * 4) + nseq * 2 * (s.H_v * s.d_k * s.d_v * 4 + 3 * s.C * 2)
+    traffic = None
+    if ws is not None and kernel_sources_sha256(PREFILL_SOURCES) == MEASURED_PREFILL_TRAFFIC["kernel_sources_sha256"]:
+        traffic = MEASURED_PREFILL_TRAFFIC["bytes_per_call"].get((nseq, L))
     return {
         "metric": PREFILL_METRIC, "value": tokens / (k_us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_call, "higher_is_better": True, "scaling": "weak",
@@ -770,7 +781,9 @@ def run_prefill(args) -> dict:
                    "path": "two-pass" if ws is not None else "one-kernel",
                    "workspace_bytes": 0 if ws is None else int(ws.numel())},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per call, its three kernels (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
                      "kernel": ("tp_chunk_map + tp_intra + tp_inter (one call)" if ws is not None else
                                 "gdn_prefill_kernel"),
                      "kernel_us_mean": k_us, "kernel_us_p50": float(np.percentile(us, 50)),
