@@ -127,10 +127,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _device(*tensors):
+    """The one GPU every given tensor lives on (None entries skipped)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+    return devs.pop()
+
+
+def _stream(stream, device):
+    """The stream to launch on: the given one, which must belong to the tensors'
+    GPU, or that GPU's current torch stream."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if s.device != device:
+        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
     return ctypes.c_void_p(s.cuda_stream)
+
+
+class _on:
+    """Make the tensors' GPU the current HIP device for the call (a no-op when it already is)."""
+
+    def __init__(self, device):
+        self.device, self.prev = device, None
+
+    def __enter__(self):
+        torch = _torch()
+        cur = torch.cuda.current_device()
+        if cur != self.device.index:
+            self.prev = cur
+            torch.cuda.set_device(self.device)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            _torch().cuda.set_device(self.prev)
+        return False
 
 
 # ------------------------------------------------------------------ entry points
@@ -173,10 +205,12 @@ def gdn_decode_step(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, wr
     state [N][H_v][d_k][d_v] fp32, g/beta [B][T][H_v] fp32, read_slot/write_slot
     [B] int32 (write_slot None => in place), out [B][T][H_v][d_v] bf16."""
     d, xs = _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k)
-    _check("gdn_decode_step", lib().gdn_decode_step(
-        ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
-        _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(out), float(q_scale), float(l2_eps),
-        _stream(stream)))
+    dev = _device(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out)
+    with _on(dev):
+        _check("gdn_decode_step", lib().gdn_decode_step(
+            ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+            _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(out), float(q_scale), float(l2_eps),
+            _stream(stream, dev)))
 
 
 def gdn_decode_step_commit(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, next_read_slot,
@@ -192,10 +226,13 @@ def gdn_decode_step_commit(x, conv_w, conv_b, conv_state, state, g, beta, read_s
         if t.shape != read_slot.shape:
             raise ValueError(f"{n} must be [B]")
     d, xs = _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k)
-    _check("gdn_decode_step_commit", lib().gdn_decode_step_commit(
-        ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
-        _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(next_read_slot), _ptr(next_write_slot),
-        _ptr(out), float(q_scale), float(l2_eps), _stream(stream)))
+    dev = _device(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, next_read_slot,
+                  next_write_slot, out)
+    with _on(dev):
+        _check("gdn_decode_step_commit", lib().gdn_decode_step_commit(
+            ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+            _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(write_slot), _ptr(next_read_slot), _ptr(next_write_slot),
+            _ptr(out), float(q_scale), float(l2_eps), _stream(stream, dev)))
 
 
 def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, token_slots, out, *,
@@ -208,10 +245,12 @@ def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_s
     if token_slots.shape != x.shape[:2]:
         raise ValueError("token_slots must be [B][T]")
     d, xs = _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, None, out, H_k)
-    _check("gdn_decode_step_tokens", lib().gdn_decode_step_tokens(
-        ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
-        _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(token_slots), _ptr(out), float(q_scale), float(l2_eps),
-        _stream(stream)))
+    dev = _device(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, token_slots, out)
+    with _on(dev):
+        _check("gdn_decode_step_tokens", lib().gdn_decode_step_tokens(
+            ctypes.byref(d), _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
+            _ptr(g), _ptr(beta), _ptr(read_slot), _ptr(token_slots), _ptr(out), float(q_scale), float(l2_eps),
+            _stream(stream, dev)))
 
 
 def _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k):
@@ -228,6 +267,8 @@ def _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slo
     T, C = x.shape
     N, H_v, d_k, d_v = state.shape
     W = conv_w.shape[1]
+    if slot.dim() != 1:
+        raise ValueError("slot must be [B]")
     B = slot.shape[0]
     if cu_seqlens.shape != (B + 1,) or g.shape != (T, H_v) or beta.shape != (T, H_v) or out.shape != (T, H_v, d_v):
         raise ValueError("cu_seqlens [B+1], g/beta [T][H_v], out [T][H_v][d_v] expected")
@@ -243,9 +284,12 @@ def gdn_prefill(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot,
     x [T][C] bf16 (rows may be strided), g/beta [T][H_v] fp32, cu_seqlens [B+1] int32,
     slot [B] int32, out [T][H_v][d_v] bf16; the pool tensors as for gdn_decode_step."""
     d, xs = _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k)
-    _check("gdn_prefill", lib().gdn_prefill(
-        ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
-        _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _stream(stream)))
+    dev = _device(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out)
+    with _on(dev):
+        _check("gdn_prefill", lib().gdn_prefill(
+            ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+            _ptr(state), _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps),
+            _stream(stream, dev)))
 
 
 def gdn_prefill_two_pass_workspace_bytes(B: int, T: int, H_k: int, H_v: int, d_k: int, d_v: int) -> int:
@@ -261,10 +305,12 @@ def gdn_prefill_two_pass(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqle
     torch = _torch()
     d, xs = _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k)
     _contig(_dev(workspace, "workspace", torch.uint8), "workspace")
-    _check("gdn_prefill_two_pass", lib().gdn_prefill_two_pass(
-        ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(state),
-        _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+    dev = _device(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, workspace)
+    with _on(dev):
+        _check("gdn_prefill_two_pass", lib().gdn_prefill_two_pass(
+            ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+            _ptr(state), _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _ptr(workspace),
+            workspace.numel(), _stream(stream, dev)))
 
 
 def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,
@@ -287,10 +333,12 @@ def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, ac
         raise ValueError("x and out must be [B][C] with contiguous channels")
     if x.shape[0] != B or out.shape[0] != B or x.shape[1] < C or out.shape[1] < C:
         raise ValueError("x / out do not match [B][C]")
-    _check("conv_decode", lib().conv_decode(
-        B, C, Wm1 + 1, N, _ptr(x), x.stride(0) if B > 0 else C, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
-        _ptr(read_slot), _ptr(write_slot), _ptr(out), out.stride(0) if B > 0 else C, int(bool(activation)),
-        _stream(stream)))
+    dev = _device(x, conv_w, conv_b, conv_state, read_slot, write_slot, out)
+    with _on(dev):
+        _check("conv_decode", lib().conv_decode(
+            B, C, Wm1 + 1, N, _ptr(x), x.stride(0) if B > 0 else C, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+            _ptr(read_slot), _ptr(write_slot), _ptr(out), out.stride(0) if B > 0 else C, int(bool(activation)),
+            _stream(stream, dev)))
 
 
 def slot_commit(read_slot, write_slot, *, stream=None) -> None:
@@ -300,8 +348,10 @@ def slot_commit(read_slot, write_slot, *, stream=None) -> None:
     _contig(_dev(write_slot, "write_slot", torch.int32), "write_slot")
     if read_slot.shape != write_slot.shape or read_slot.dim() != 1:
         raise ValueError("slot arrays must both be [B]")
-    _check("slot_commit", lib().slot_commit(_ptr(read_slot), _ptr(write_slot), read_slot.shape[0],
-                                            _stream(stream)))
+    dev = _device(read_slot, write_slot)
+    with _on(dev):
+        _check("slot_commit", lib().slot_commit(_ptr(read_slot), _ptr(write_slot), read_slot.shape[0],
+                                                _stream(stream, dev)))
 
 
 def _pool_dims(state, conv_state, H_k):
@@ -319,8 +369,10 @@ def slot_reset(state, conv_state, slots, *, H_k: int, stream=None) -> None:
     torch = _torch()
     _contig(_dev(slots, "slots", torch.int32), "slots")
     d = _pool_dims(state, conv_state, H_k)
-    _check("gdn_slot_reset", lib().gdn_slot_reset(ctypes.byref(d), _ptr(state), _ptr(conv_state), _ptr(slots),
-                                                  slots.numel(), _stream(stream)))
+    dev = _device(state, conv_state, slots)
+    with _on(dev):
+        _check("gdn_slot_reset", lib().gdn_slot_reset(ctypes.byref(d), _ptr(state), _ptr(conv_state), _ptr(slots),
+                                                      slots.numel(), _stream(stream, dev)))
 
 
 def slot_copy(state, conv_state, src_slots, dst_slots, *, H_k: int, stream=None) -> None:
@@ -331,8 +383,10 @@ def slot_copy(state, conv_state, src_slots, dst_slots, *, H_k: int, stream=None)
     if src_slots.shape != dst_slots.shape or src_slots.dim() != 1:
         raise ValueError("src_slots and dst_slots must both be [n]")
     d = _pool_dims(state, conv_state, H_k)
-    _check("gdn_slot_copy", lib().gdn_slot_copy(ctypes.byref(d), _ptr(state), _ptr(conv_state), _ptr(src_slots),
-                                                _ptr(dst_slots), src_slots.numel(), _stream(stream)))
+    dev = _device(state, conv_state, src_slots, dst_slots)
+    with _on(dev):
+        _check("gdn_slot_copy", lib().gdn_slot_copy(ctypes.byref(d), _ptr(state), _ptr(conv_state), _ptr(src_slots),
+                                                    _ptr(dst_slots), src_slots.numel(), _stream(stream, dev)))
 
 
 def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, rows: int | None = None, stream=None) -> None:
@@ -347,7 +401,8 @@ def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, rows: int | 
     _contig(_dev(write_slot, "write_slot", torch.int32, allow_none=True), "write_slot")
     _contig(_dev(sink, "sink", torch.float32), "sink")
     N, H, d_k, d_v = state.shape
-    _check("gdn_traffic_probe", lib().gdn_traffic_probe(
-        int(mode), read_slot.shape[0] if rows is None else int(rows), H, d_k, d_v, N, _ptr(state), _ptr(read_slot),
-        _ptr(write_slot),
-        _ptr(sink), _stream(stream)))
+    dev = _device(state, read_slot, write_slot, sink)
+    with _on(dev):
+        _check("gdn_traffic_probe", lib().gdn_traffic_probe(
+            int(mode), read_slot.shape[0] if rows is None else int(rows), H, d_k, d_v, N, _ptr(state),
+            _ptr(read_slot), _ptr(write_slot), _ptr(sink), _stream(stream, dev)))
