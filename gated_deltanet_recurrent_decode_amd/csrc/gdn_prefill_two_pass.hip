@@ -26,7 +26,9 @@
 // windows and pass 2 writes the new ones, so no workgroup can read a window
 // another has already advanced.
 // A map kernel first turns each sequence's length into its run of chunk
-// indices (an exclusive scan), which pass 1 searches.
+// indices (an exclusive scan) and writes each chunk's record (first token,
+// tokens, slot, first chunk of its sequence or not), which pass 1 reads with
+// one load instead of searching the scan.
 
 #include "gdn_internal.h"
 #include "prefill_internal.h"
@@ -119,6 +121,27 @@ __global__ __launch_bounds__(NT) void tp_chunk_map_kernel(TwoPassParams tp)
         carry += scan[NT - 1];
         __syncthreads(); // scan[] is rewritten by the next tile
     }
+    // every chunk's record: a thread a chunk finds its sequence in the scan just
+    // written (the barrier above made this workgroup's stores visible to it)
+    const int32_t *cs = tp.ws.chunk_start;
+    const int nch = carry < tp.ws.nchunk ? carry : tp.ws.nchunk;
+    for (int g = tid; g < nch; g += NT) {
+        // the last b with chunk_start[b] <= g (sequences with no chunks share
+        // their start with the next one)
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cs[mid] <= g)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int c = g - cs[lo];
+        const int t_begin = p.cu_seqlens[lo];
+        const int L = p.cu_seqlens[lo + 1] - t_begin;
+        *reinterpret_cast<int4 *>(tp.ws.chunk_rec + 4 * (size_t)g) =
+            make_int4(t_begin + c * BT, L - c * BT < BT ? L - c * BT : BT, p.slot[lo], c == 0 ? 1 : 0);
+    }
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -173,7 +196,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         bias[h] = p.conv_b ? bf16_to_f32(p.conv_b[ch + h]) : 0.f;
     }
 
-    // ---- a chunk's inputs: its place, the three inputs before it (from the
+    // ---- a chunk's inputs: its record, the three inputs before it (from the
     // slot's window for a prompt's first chunk, else from x), its x rows and
     // gates.  The workgroup walks chunks blockIdx.x, + gridDim.x, ... and
     // loads the next one's inputs while it computes the current one; x and the
@@ -187,26 +210,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     };
     auto load = [&](int gi, ChunkIn &in) {
         const int gq = __builtin_amdgcn_readfirstlane(gi < nch ? gi : nch - 1); // past the end: a real chunk, unused
-        // the sequence owning chunk gq: the last b with chunk_start[b] <= gq
-        // (sequences with no chunks share their start with the next one)
-        int lo = 0, hi = p.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cs[mid] <= gq)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int b = lo;
-        const int c = gq - cs[b];
-        const int t_begin = p.cu_seqlens[b];
-        const int L = p.cu_seqlens[b + 1] - t_begin;
-        const int sl = p.slot[b];
-        const int t0 = __builtin_amdgcn_readfirstlane(t_begin + c * BT);
-        const int n = __builtin_amdgcn_readfirstlane(L - c * BT < BT ? L - c * BT : BT);
-        const uint16_t *hb = c == 0 ? p.conv_state + (size_t)sl * 3 * C + ch
-                                    : p.x + (size_t)(t0 - 3) * p.x_row_stride + ch;
-        const size_t hs = c == 0 ? (size_t)C : (size_t)p.x_row_stride;
+        const int4 rec = *reinterpret_cast<const int4 *>(tp.ws.chunk_rec + 4 * (size_t)gq);
+        const int t0 = __builtin_amdgcn_readfirstlane(rec.x);
+        const int n = __builtin_amdgcn_readfirstlane(rec.y);
+        const int sl = __builtin_amdgcn_readfirstlane(rec.z);
+        const bool first = __builtin_amdgcn_readfirstlane(rec.w) != 0;
+        const uint16_t *hb = first ? p.conv_state + (size_t)sl * 3 * C + ch
+                                   : p.x + (size_t)(t0 - 3) * p.x_row_stride + ch;
+        const size_t hs = first ? (size_t)C : (size_t)p.x_row_stride;
 #pragma unroll
         for (int k = 0; k < 3; ++k)
             in.hist[k] = *reinterpret_cast<const uint32_t *>(hb + k * hs);
@@ -242,30 +253,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             float *ydst = isq ? &Qs[e] : isk ? &Ks[e - DK] : &Vs[e - 2 * DK];
             const int ypitch = (isq || isk) ? KP : VP;
             const bool has_bias = p.conv_b != nullptr;
+            // the pair's two outputs of a token are adjacent: one 8-byte store.
+            // Tokens past the chunk's end are computed on the zeros their loads
+            // returned and stored as zero, with no branch per token.
 #pragma unroll
             for (int tt = 0; tt < BT; ++tt) {
-                float y0 = 0.f, y1 = 0.f;
-                if (tt < n) {
-                    const float x0 = __uint_as_float(cur.xb[tt] << 16), x1 = __uint_as_float(cur.xb[tt] & 0xffff0000u);
-                    float acc0 = w0[0] * h0[0];
-                    acc0 = fmaf(w1[0], h1[0], acc0);
-                    acc0 = fmaf(w2[0], h2[0], acc0);
-                    acc0 = fmaf(w3[0], x0, acc0);
-                    float acc1 = w0[1] * h0[1];
-                    acc1 = fmaf(w1[1], h1[1], acc1);
-                    acc1 = fmaf(w2[1], h2[1], acc1);
-                    acc1 = fmaf(w3[1], x1, acc1);
-                    if (has_bias) {
-                        acc0 += bias[0];
-                        acc1 += bias[1];
-                    }
-                    y0 = acc0 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc0));
-                    y1 = acc1 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc1));
-                    h0[0] = h1[0]; h1[0] = h2[0]; h2[0] = x0;
-                    h0[1] = h1[1]; h1[1] = h2[1]; h2[1] = x1;
+                const float x0 = __uint_as_float(cur.xb[tt] << 16), x1 = __uint_as_float(cur.xb[tt] & 0xffff0000u);
+                float acc0 = w0[0] * h0[0];
+                acc0 = fmaf(w1[0], h1[0], acc0);
+                acc0 = fmaf(w2[0], h2[0], acc0);
+                acc0 = fmaf(w3[0], x0, acc0);
+                float acc1 = w0[1] * h0[1];
+                acc1 = fmaf(w1[1], h1[1], acc1);
+                acc1 = fmaf(w2[1], h2[1], acc1);
+                acc1 = fmaf(w3[1], x1, acc1);
+                if (has_bias) {
+                    acc0 += bias[0];
+                    acc1 += bias[1];
                 }
-                ydst[tt * ypitch] = y0;
-                ydst[tt * ypitch + 1] = y1;
+                const bool live = tt < n;
+                const float y0 = live ? acc0 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc0)) : 0.f;
+                const float y1 = live ? acc1 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc1)) : 0.f;
+                h0[0] = h1[0]; h1[0] = h2[0]; h2[0] = x0;
+                h0[1] = h1[1]; h1[1] = h2[1]; h2[1] = x1;
+                *reinterpret_cast<float2 *>(&ydst[tt * ypitch]) = make_float2(y0, y1);
             }
         }
         // the next chunk's inputs load while this one computes; issued after
@@ -288,15 +299,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
         __syncthreads();
 
-        // ---- L2 norms of q and k: eight lanes a token
+        // ---- L2 norms of q and k: eight lanes a token, each lane four runs of
+        // four values (16-byte accesses), held in registers until scaled
         {
             const int tt = tid >> 3, sub = tid & 7;
+            constexpr int NR = DK / 32; // runs of four a lane
+            v4f qr[NR], kr[NR];
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int i = sub; i < DK; i += 8) {
-                const float qv = Qs[tt * KP + i], kv = Ks[tt * KP + i];
-                sq = fmaf(qv, qv, sq);
-                sk = fmaf(kv, kv, sk);
+            for (int j = 0; j < NR; ++j) {
+                qr[j] = *reinterpret_cast<const v4f *>(&Qs[tt * KP + 4 * sub + 32 * j]);
+                kr[j] = *reinterpret_cast<const v4f *>(&Ks[tt * KP + 4 * sub + 32 * j]);
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    sq = fmaf(qr[j][e4], qr[j][e4], sq);
+                    sk = fmaf(kr[j][e4], kr[j][e4], sk);
+                }
             }
             // the sums over each token's eight lanes: DPP butterflies (same pairs as an
             // xor shuffle, no LDS round trip)
@@ -310,9 +328,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
                 const float rk = 1.0f / sqrtf(sk + p.l2_eps);
 #pragma unroll
-                for (int i = sub; i < DK; i += 8) {
-                    Qs[tt * KP + i] *= qs;
-                    Ks[tt * KP + i] *= rk;
+                for (int j = 0; j < NR; ++j) {
+                    *reinterpret_cast<v4f *>(&Qs[tt * KP + 4 * sub + 32 * j]) =
+                        v4f{qr[j][0] * qs, qr[j][1] * qs, qr[j][2] * qs, qr[j][3] * qs};
+                    *reinterpret_cast<v4f *>(&Ks[tt * KP + 4 * sub + 32 * j]) =
+                        v4f{kr[j][0] * rk, kr[j][1] * rk, kr[j][2] * rk, kr[j][3] * rk};
                 }
             }
         }
@@ -1099,6 +1119,8 @@ size_t two_pass_layout(int B, int total, int H_v, int d_k, int d_v, void *base, 
     size_t off = 0;
     const size_t o_cs = off;
     off = round_up(off + (size_t)(B + 1) * sizeof(int32_t));
+    const size_t o_rec = off;
+    off = round_up(off + nchunk * 4 * sizeof(int32_t));
     const size_t o_qa = off;
     off = round_up(off + blocks * BT * d_k * sizeof(float));
     const size_t o_wa = off;
@@ -1114,6 +1136,7 @@ size_t two_pass_layout(int B, int total, int H_v, int d_k, int d_v, void *base, 
     if (base && ws) {
         char *c = static_cast<char *>(base);
         ws->chunk_start = reinterpret_cast<int32_t *>(c + o_cs);
+        ws->chunk_rec = reinterpret_cast<int32_t *>(c + o_rec);
         ws->qa = reinterpret_cast<float *>(c + o_qa);
         ws->wa = reinterpret_cast<float *>(c + o_wa);
         ws->ka = reinterpret_cast<float *>(c + o_ka);

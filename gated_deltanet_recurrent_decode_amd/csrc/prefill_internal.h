@@ -43,8 +43,12 @@ hipError_t launch_gdn_prefill(const PrefillParams &p, int d_k, int d_v, hipStrea
 //           diag(beta) V) in the accumulator layout, lane j + 16 g holding rows
 //           4 g .. 4 g + 3 of column j
 //   el      e^gamma_last of the chunk
+// and, per chunk of the call, its record [nchunk][4]: first token, tokens
+// (at most 32), slot, and 1 for a sequence's first chunk (whose three earlier
+// inputs come from the slot's window) else 0.
 struct TwoPassWorkspace {
     int32_t *chunk_start; // [B+1]: exclusive scan of each sequence's chunk count
+    int32_t *chunk_rec;   // [nchunk][4]
     float *qa, *wa, *ka, *pa, *ud, *el;
     int nchunk;
 };

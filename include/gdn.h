@@ -220,8 +220,8 @@ gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t
  * needs for dims (B sequences, T packed tokens, H_v, d_k, d_v): room for
  * K = ceil(T / 32) + B chunks (every sequence adds at most one partial chunk)
  * per value head, each chunk (3 d_k + d_v + 32) * 32 + 1 fp32 values, plus
- * B + 1 int32; each region rounded up to 256 bytes.  0 when dims is NULL or
- * its sizes are unusable.
+ * B + 1 int32 and 4 int32 per chunk; each region rounded up to 256 bytes.  0
+ * when dims is NULL or its sizes are unusable.
  */
 size_t gdn_prefill_two_pass_workspace_bytes(const gdn_dims *dims);
 

@@ -152,9 +152,10 @@ def test_prefill_two_pass_validation():
     d = _dims(T=40)
     need = L.gdn_prefill_two_pass_workspace_bytes(ctypes.byref(d))
     # per value head room for ceil(T / 32) + B chunks of (3 d_k + d_v + 32) * 32 + 1 floats, plus B + 1
-    # ints, each region rounded to 256 bytes
-    blocks = d.H_v * ((d.T + 31) // 32 + d.B)
-    parts = [4 * (d.B + 1), 4 * blocks * 32 * d.d_k, 4 * blocks * 32 * d.d_k, 4 * blocks * 32 * d.d_k,
+    # ints and a 4-int record per chunk, each region rounded to 256 bytes
+    nchunk = (d.T + 31) // 32 + d.B
+    blocks = d.H_v * nchunk
+    parts = [4 * (d.B + 1), 16 * nchunk, 4 * blocks * 32 * d.d_k, 4 * blocks * 32 * d.d_k, 4 * blocks * 32 * d.d_k,
              4 * blocks * 32 * 32, 4 * blocks * 32 * d.d_v, 4 * blocks]
     assert need == sum((x + 255) // 256 * 256 for x in parts)
     assert L.gdn_prefill_two_pass_workspace_bytes(None) == 0
