@@ -76,9 +76,9 @@ __global__ __launch_bounds__(256) void gdn_prefill_kernel(PrefillParams p)
     constexpr int BT = kChunk;
 
     __shared__ float S[DK * SP];  // the state, S[i][j], i over keys
-    __shared__ float Qs[BT * KP]; // q^ of the chunk's tokens (scaled by q_scale)
-    __shared__ float Ks[BT * KP]; // k^
-    __shared__ float Vs[BT * VP]; // v, then R = V - e^gamma K S0, then U
+    __shared__ __align__(16) float Qs[BT * KP]; // q^ of the chunk's tokens (scaled by q_scale)
+    __shared__ __align__(16) float Ks[BT * KP]; // k^
+    __shared__ __align__(16) float Vs[BT * VP]; // v, then R = V - e^gamma K S0, then U
     __shared__ float Am[BT * AP]; // the strictly lower A
     __shared__ float Pm[BT * AP]; // P
     __shared__ float Tm[BT * AP]; // (I + A)^-1
@@ -176,6 +176,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_kernel(PrefillParams p)
         // ---- conv decode + SiLU of the chunk's tokens (x already in registers);
         // zero rows past the end
         if (conv_lane) {
+            // the pair's two outputs of a token are adjacent: one 8-byte store
 #pragma unroll
             for (int tt = 0; tt < BT; ++tt) {
                 float y0 = 0.f, y1 = 0.f;
@@ -198,8 +199,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_kernel(PrefillParams p)
                     a0[0] = a1[0]; a1[0] = a2[0]; a2[0] = x0;
                     a0[1] = a1[1]; a1[1] = a2[1]; a2[1] = x1;
                 }
-                ydst[tt * ypitch] = y0;
-                ydst[tt * ypitch + 1] = y1;
+                *reinterpret_cast<float2 *>(&ydst[tt * ypitch]) = make_float2(y0, y1);
             }
         }
         if (tid < BT) {
@@ -225,16 +225,23 @@ __global__ __launch_bounds__(256) void gdn_prefill_kernel(PrefillParams p)
         __syncthreads();
 
         // ---- L2 norms of q and k: eight lanes a token, each summing DK/8
-        // elements, then three butterfly steps inside the eight; rows past the
+        // elements in runs of four (16-byte accesses, held in registers until
+        // scaled), then three butterfly steps inside the eight; rows past the
         // end stay zero.
         {
             const int tt = tid >> 3, sub = tid & 7;
+            constexpr int NR = DK / 32; // runs of four a lane
+            v4f qr[NR], kr[NR];
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int i = sub; i < DK; i += 8) {
-                const float qv = Qs[tt * KP + i], kv = Ks[tt * KP + i];
-                sq = fmaf(qv, qv, sq);
-                sk = fmaf(kv, kv, sk);
+            for (int j = 0; j < NR; ++j) {
+                qr[j] = *reinterpret_cast<const v4f *>(&Qs[tt * KP + 4 * sub + 32 * j]);
+                kr[j] = *reinterpret_cast<const v4f *>(&Ks[tt * KP + 4 * sub + 32 * j]);
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    sq = fmaf(qr[j][e4], qr[j][e4], sq);
+                    sk = fmaf(kr[j][e4], kr[j][e4], sk);
+                }
             }
             // the sums over each token's eight lanes: DPP butterflies (same pairs as an
             // xor shuffle, no LDS round trip)
@@ -248,9 +255,11 @@ __global__ __launch_bounds__(256) void gdn_prefill_kernel(PrefillParams p)
                 const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
                 const float rk = 1.0f / sqrtf(sk + p.l2_eps);
 #pragma unroll
-                for (int i = sub; i < DK; i += 8) {
-                    Qs[tt * KP + i] *= qs;
-                    Ks[tt * KP + i] *= rk;
+                for (int j = 0; j < NR; ++j) {
+                    *reinterpret_cast<v4f *>(&Qs[tt * KP + 4 * sub + 32 * j]) =
+                        v4f{qr[j][0] * qs, qr[j][1] * qs, qr[j][2] * qs, qr[j][3] * qs};
+                    *reinterpret_cast<v4f *>(&Ks[tt * KP + 4 * sub + 32 * j]) =
+                        v4f{kr[j][0] * rk, kr[j][1] * rk, kr[j][2] * rk, kr[j][3] * rk};
                 }
             }
         }
