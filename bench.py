@@ -59,8 +59,8 @@ KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
 # summary with its commands is in profiles/.  Valid only for these sources.
-MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "27a185d90d7dfb6a36a28a726de88cdfa09b111a3f371c7a481752c3f72beab3",
-                            "bytes_per_call": {(16, 512): 754_782_553, (1, 4096): 364_300_837}}
+MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "a70a43f676c6bfc05c8647f3201b7af3fb29d9f5b8645b04fd005b94297acc5e",
+                            "bytes_per_call": {(16, 512): 754_985_225, (1, 4096): 364_492_547}}
 PREFILL_SOURCES = ("gdn_prefill_two_pass.hip", "prefill_internal.h", "step_common.h", "device_common.h",
                    "gdn_internal.h")
 
