@@ -129,6 +129,18 @@ def test_two_pass_long_prompt_and_slices(gdn, torch):
            two_pass=True)
 
 
+@PATHS
+@pytest.mark.parametrize("g_scale", [0.01, 0.0], ids=["weak-decay", "no-decay"])
+def test_prefill_long_prompt_with_weak_or_no_decay(gdn, torch, two_pass, g_scale):
+    """2048 tokens at the 0.8B shapes with the log decay scaled by 0.01 (a state
+    that remembers for hundreds of tokens), and with g = 0 exactly (every decay
+    factor 1): errors of the chunked form would accumulate here if anywhere,
+    yet the bars are the decode step's."""
+    case = gi.prefill([2048], H_k=16, H_v=16, d=128, seed=33)
+    case.g[:] = (case.g * np.float32(g_scale)).astype(np.float32)
+    _check(gdn, torch, case, two_pass=two_pass)
+
+
 def test_two_pass_bench_workload_one_long_prompt(gdn, torch):
     """The prefill bench's single-prompt workload as it times it: one prompt of
     4096 tokens at the 0.8B-like shapes (128 chunks, 16-column slices), every
