@@ -131,6 +131,30 @@ def test_tiny_eight_chained_steps_with_commit(gdn, torch):
         np.testing.assert_array_equal(dp.wr.cpu().numpy(), hp.wr)
 
 
+@pytest.mark.parametrize("twin", [True, False], ids=["twin", "inplace"])
+def test_256_chained_steps_without_decay(gdn, torch, twin):
+    """256 steps of 4 rows (2 + 2 heads of 128) with g = 0: nothing decays, so the
+    state remembers every step and rounding differences would pile up; each
+    side chains through its own fp32 slots, twin slots committed between steps.
+    The last step's output and the whole pool against the oracle."""
+    t = torch
+    case = gi.small(4, 1, 2, 2, 128, twin=twin, steps=256, seed=7)
+    s, pool = case.shape, case.pools[0]
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    for k in range(256):
+        step = case.steps[k][0]
+        step.g[:] = 0.0
+        out = H.gpu_step(gdn, dp, step, s, twin=twin)
+        ref = H.oracle_step(oracle, hp, step, s, twin=twin)
+        if twin:
+            gdn.slot_commit(dp.rd, dp.wr)
+            oracle.slot_commit(hp.rd, hp.wr)
+    t.cuda.synchronize()
+    H.assert_out_close(out, ref, "out of the last step")
+    H.assert_state_close(dp.state.cpu().numpy(), hp.state, "pool after 256 steps")
+    np.testing.assert_array_equal(H.bf16_host(dp.conv_state), hp.conv_state)
+
+
 # ------------------------------------------------------------------ workload: 0.8B layer, 64 rows
 
 def test_08b_layer_64_rows_twin(gdn, torch):
