@@ -303,6 +303,41 @@ def test_per_token_states_match_oracle(gdn, torch, B, T, hk, hv, d, real):
                 assert t.equal(dp.conv_state[int(tok[r, k])].view(t.int16), dpk.conv_state[rs].view(t.int16))
 
 
+@pytest.mark.parametrize("path", ["twin", "inplace-tokens", "inplace-G2", "per-token-states"])
+def test_conv_bias_and_q_scale_on_every_step_kernel(gdn, torch, path):
+    """A conv bias and q_scale = d_k^-1/2 through each step kernel: the single-token
+    tile (twin), the in-place token walk (3 tokens; G = 1, and G = 2 with its
+    key-head groups), and the per-token-state walk."""
+    t = torch
+    T = 1 if path == "twin" else 3
+    hv = 4 if path == "inplace-G2" else 2
+    B = 4
+    case = gi.small(B=B, T=T, H_k=2, H_v=hv, d=128, N=1 + 2 * B + 2 * B * T, twin=path == "twin", seed=17)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    bias = gi.bf16_bits(np.random.Generator(np.random.PCG64(18)).standard_normal(s.C).astype(np.float32))
+    qs = 128 ** -0.5
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    a = (H.bf16_dev(step.x), dp.conv_w, H.bf16_dev(bias), dp.conv_state, dp.state, t.from_numpy(step.g).cuda(),
+         t.from_numpy(step.beta).cuda(), dp.rd)
+    out = t.empty((B, T, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+    if path == "per-token-states":
+        tok = _token_slots(pool, B, T, [[True] * T] * B, 19)
+        gdn.gdn_decode_step_tokens(*a, t.from_numpy(tok).cuda(), out, H_k=s.H_k, q_scale=qs)
+        ref = oracle.gdn_decode_step_tokens(step.x, hp.conv_w, bias, hp.conv_state, hp.state, step.g, step.beta,
+                                            hp.rd, tok, H_k=s.H_k, q_scale=qs)
+        written = sorted(int(x) for x in tok.ravel())
+    else:
+        twin = path == "twin"
+        gdn.gdn_decode_step(*a, dp.wr if twin else None, out, H_k=s.H_k, q_scale=qs)
+        ref = oracle.gdn_decode_step(step.x, hp.conv_w, bias, hp.conv_state, hp.state, step.g, step.beta, hp.rd,
+                                     hp.wr if twin else None, H_k=s.H_k, q_scale=qs)
+        written = sorted(int(x) for x in (pool.write_slot if twin else pool.read_slot))
+    t.cuda.synchronize()
+    H.assert_out_close(out, ref)
+    H.assert_state_close(dp.state[written].cpu().numpy(), hp.state[written])
+    np.testing.assert_array_equal(H.bf16_host(dp.conv_state[written]), hp.conv_state[written])
+
+
 def test_per_token_states_unusable_slot(gdn, torch):
     """A token slot outside the pool, or equal to the row's read slot, makes the
     row NaN and touches nothing; the other rows are unaffected."""
