@@ -45,8 +45,12 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     constexpr int NT = Cfg::NT, NTH = Cfg::NTH, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH;
     constexpr int NCH = Cfg::NCH;
 
-    __shared__ float y_lds[NCH + 4]; // + a padding slot for spare conv lanes
-    __shared__ float4 red_lds[HPW][NWH][2][CG];
+    // conv outputs (+ a padding slot for spare conv lanes) and the cross-wave
+    // partial sums, one of each for even and one for odd tokens: token t
+    // writes the set that token t - 2 read, and every wave has passed token
+    // t - 1's barriers, so it is done with token t - 2, before it gets there
+    __shared__ float y_buf[2][NCH + 4];
+    __shared__ float4 red_buf[2][HPW][NWH][2][CG];
 
     const int tid = threadIdx.x;
     // head of the group this thread updates; NTH is a multiple of the wave size,
@@ -159,8 +163,9 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     uint2 xn[NCQ];     // the next token's x, loaded one token ahead
     float g_n = 0.f, b_n = 0.f;
     for (int t = 0; t < T; ++t) {
+        float *y_lds = y_buf[t & 1];
+        float4(*red_lds)[NWH][2][CG] = red_buf[t & 1];
         if (t > 0) {
-            lds_barrier(); // the previous token's readers of y_lds / red_lds are done
 #pragma unroll
             for (int k = 0; k < NCQ; ++k)
                 xq[k] = xn[k];
