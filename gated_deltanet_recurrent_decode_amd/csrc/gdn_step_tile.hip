@@ -20,12 +20,12 @@
 // an unusable slot) and leave: a 128-row bucket with 46 real rows then takes
 // 22.3 us against 25.9 when they ran the arithmetic on zeros.
 //
-// At d_k = d_v = 128 the whole-tile kernel sits at 128 VGPRs (four waves per
-// SIMD) and the compiler spills one register (a conv lane's channel offset,
-// 4 bytes a lane: about 1 MiB written and 0.5 MiB read back per 64-row launch,
-// 1% of its traffic).  Measured on MI355X, every spill-free form tried --
-// recomputing the offset at the window stores, with or without an explicit
-// wait or a pause before the stores -- ran 0.2-0.7 us slower at 1-64 rows.
+// Each wave holds all eight row groups of 32 columns, so the projections'
+// sums over d_k end inside the wave (lane butterflies) with no LDS round trip
+// and no barrier; the only barrier publishes the conv outputs.  At d_k = d_v
+// = 128 the whole-tile kernel takes 121 VGPRs, four waves per SIMD, with no
+// spill (measured on MI355X against the layout that summed the row groups
+// across waves in LDS: 64 rows 28.4 -> 27.6 us a step).
 
 #include "gdn_internal.h"
 #include "step_common.h"
@@ -153,12 +153,12 @@ __device__ __forceinline__ void tile_issue_state(TileState<DK, DVS> &t, const St
 // delta update, the read-out, and the stores of o, the advanced conv windows
 // and the new state.
 template <int DK, int DV, int DVS, bool INPLACE>
-__device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepParams &p, int cg, int rg, int wv,
-                                             int lane, uint32_t voff, float *y_lds, float4 (*red_lds)[2][DVS / 4])
+__device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepParams &p, int cg, int rg, int lane,
+                                             uint32_t voff, float *y_lds)
 {
     using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
-    constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH, NCH = Cfg::NCH;
+    constexpr int RG = Cfg::RG, RPT = Cfg::RPT, NCH = Cfg::NCH;
     constexpr int NCW = (TT::NCL + 63) / 64; // waves' worth of conv lanes
     const bool has_bias = p.conv_b != nullptr;
 
@@ -218,35 +218,18 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
         pb.z = fmaf(t.s[m].z, qh, pb.z);
         pb.w = fmaf(t.s[m].w, qh, pb.w);
     }
-    pa.x = xor_sum<CG>(pa.x);
-    pa.y = xor_sum<CG>(pa.y);
-    pa.z = xor_sum<CG>(pa.z);
-    pa.w = xor_sum<CG>(pa.w);
-    pb.x = xor_sum<CG>(pb.x);
-    pb.y = xor_sum<CG>(pb.y);
-    pb.z = xor_sum<CG>(pb.z);
-    pb.w = xor_sum<CG>(pb.w);
-    if (lane < CG) {
-        red_lds[wv][0][cg] = pa;
-        red_lds[wv][1][cg] = pb;
-    }
-    lds_barrier();
-    // the higher row-group bits live in the wave index: the same pairwise tree
-    float4 av[NWH], bv[NWH];
-#pragma unroll
-    for (int w = 0; w < NWH; ++w) {
-        av[w] = red_lds[w][0][cg];
-        bv[w] = red_lds[w][1][cg];
-    }
-#pragma unroll
-    for (int st = 1; st < NWH; st *= 2) {
-#pragma unroll
-        for (int w = 0; w + st < NWH; w += 2 * st) {
-            av[w].x += av[w + st].x; av[w].y += av[w + st].y; av[w].z += av[w + st].z; av[w].w += av[w + st].w;
-            bv[w].x += bv[w + st].x; bv[w].y += bv[w + st].y; bv[w].z += bv[w + st].z; bv[w].w += bv[w + st].w;
-        }
-    }
-    const float4 a = av[0], b = bv[0];
+    // the eight row groups are lane bits 3-5 of one wave: butterflies over
+    // bits 3, 4, 5 form the pairwise tree ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7))
+    // in every lane, with no LDS round trip and no barrier
+    pa.x = xor_sum<8>(pa.x);
+    pa.y = xor_sum<8>(pa.y);
+    pa.z = xor_sum<8>(pa.z);
+    pa.w = xor_sum<8>(pa.w);
+    pb.x = xor_sum<8>(pb.x);
+    pb.y = xor_sum<8>(pb.y);
+    pb.z = xor_sum<8>(pb.z);
+    pb.w = xor_sum<8>(pb.w);
+    const float4 a = pa, b = pb;
 
     // ---- delta update in registers, and the read-out
     const float *vv = &y_lds[2 * DK + 4 * cg];
@@ -270,11 +253,10 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
     const uint32_t f2 = (uint32_t)t.fill * 0x10001u;
     const u32x2 pk = {t.real ? ((uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16)) : f2,
                       t.real ? ((uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16)) : f2};
-    // o: row group 0 of every column group; padding and unusable rows get their fill
+    // o: row group 0 of every column group (lanes 0-7 of each wave)
     const __amdgpu_buffer_rsrc_t orow =
         bf16_rsrc(p.out + ((size_t)t.r * p.H_v + t.hv) * DV, t.valid ? (uint32_t)DV * 2u : 0u);
-    if (wv == 0) // row group 0 lives in wave 0; the stores of the other waves would all be dropped
-        __builtin_amdgcn_raw_buffer_store_b64(pk, orow, rg == 0 ? (uint32_t)(t.col0 + 4 * cg) * 2u : kOOB, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(pk, orow, rg == 0 ? (uint32_t)(t.col0 + 4 * cg) * 2u : kOOB, 0, 0);
 
     // ---- advanced conv windows of the channels this tile owns: a shift of
     // bf16 values, stored as the bits they were read as
@@ -308,17 +290,19 @@ void gdn_step_tile_kernel(StepParams p)
 {
     using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
-    constexpr int CG = Cfg::CG, NWH = Cfg::NWH, NCH = Cfg::NCH;
+    constexpr int CG = Cfg::CG, NCH = Cfg::NCH;
     static_assert(Cfg::NT == 2 * DVS, "launch bound must match the layout");
+    static_assert(Cfg::RG == 8 && DVS % 32 == 0, "a wave holds the eight row groups of 32 columns");
 
     __shared__ float y_lds[NCH + 4]; // + a padding slot for spare conv lanes
-    __shared__ float4 red_lds[NWH][2][CG];
 
+    // thread layout: wave w holds columns 32 w .. 32 w + 31 of the slice, lane
+    // l column group 8 w + l % 8 (four columns) and row group l / 8, i.e. rows
+    // l / 8, l / 8 + 8, ..., so a row's projection is a sum inside one wave
     const int tid = threadIdx.x;
-    const int cg = tid % CG;
-    const int rg = tid / CG;
-    const int wv = tid >> 6;
     const int lane = tid & 63;
+    const int rg = lane >> 3;
+    const int cg = (tid >> 6) * 8 + (lane & 7);
     const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
 
     TT t;
@@ -342,7 +326,7 @@ void gdn_step_tile_kernel(StepParams p)
         }
         return;
     }
-    tile_process<DK, DV, DVS, INPLACE>(t, p, cg, rg, wv, lane, voff, y_lds, red_lds);
+    tile_process<DK, DV, DVS, INPLACE>(t, p, cg, rg, lane, voff, y_lds);
 
     // fused commit: the workgroup of a row's first tile writes the swapped
     // pair into the next step's slot arrays (distinct from the ones this step
