@@ -52,8 +52,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "acc6ab4fc9a51c7da1642106e6d5f9dd1478c1b47f1f6023b6afc9adff41709b",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 141_828_160}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "fd4109d5f030c7ae3cdbc9cf35389446e875073147fa94dfa0da5ad60b3920b2",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_272_814}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
