@@ -351,17 +351,25 @@ static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
     return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(2 * DVS), args, 0, stream);
 }
 
-// Column slices per head: split d_v only when the rows give very few
-// workgroups (with the state cold in HBM, whole tiles win from 16 rows of 16
-// heads up; slices stay >= 32 columns).  Never in place: every slice reads the
-// head's q/k conv windows and one of them writes them back, so in place a
-// slice that starts late could read an advanced window; with whole tiles and
-// one value head per key head, no other workgroup reads them.
+// Column slices per head.  Up to 2047 head tiles a step is one round of
+// workgroups on the 256 CUs, and its time follows the CUs that get the most
+// tiles.  Halving the tiles evens that out when heads mod 256 is between 1
+// and 128 (two half tiles where one CU had a whole one more than another);
+// otherwise whole tiles win, as slicing adds the q/k conv a slice more.
+// Measured on MI355X with the state cold, 16 heads a row, us a step whole
+// against sliced: 8 rows 6.66 / 5.78, 12 rows 7.20 / 7.26, 16 rows 8.13 /
+// 8.46, 24 rows 12.61 / 11.06, 40 rows 19.18 / 18.41, 48 rows 21.69 / 21.73,
+// 56 rows 25.56 / 24.98, 64 rows 27.8 / 28.4.  Under 128 tiles slices keep
+// going down to 32 columns.  Never in place: every slice reads the head's q/k
+// conv windows and one of them writes them back, so in place a slice that
+// starts late could read an advanced window; with whole tiles and one value
+// head per key head, no other workgroup reads them.
 template <int DK, int DV>
 static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
 {
     const long long heads = (long long)p.B * p.H_v;
-    if (heads >= 128 || !p.twin)
+    const long long rem = heads % 256;
+    if (!p.twin || heads >= 2048 || (heads >= 128 && (rem == 0 || rem > 128)))
         return launch_tile<DK, DV, DV>(p, stream);
     if (heads >= 32 || DV < 128)
         return launch_tile<DK, DV, DV / 2>(p, stream);

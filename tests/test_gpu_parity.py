@@ -73,7 +73,7 @@ SMALL = [
     (2, 1, 1, 4, 64, 64, True, None),      # GQA, G = 4
     (7, 1, 2, 2, 128, 64, True, None),     # d_k != d_v
     (6, 1, 2, 2, 64, 128, True, 4),        # padding rows on slot 0
-    (40, 1, 4, 4, 128, 128, True, None),   # 160 heads: 2 slices
+    (32, 1, 4, 4, 128, 128, True, None),   # 128 heads: 2 slices (128 mod 256 is in 1..128)
     (150, 1, 2, 4, 64, 64, True, None),    # 600 heads: whole tiles
     (5, 1, 2, 2, 128, 128, False, None),   # in place
     (3, 3, 2, 4, 128, 128, False, None),   # in place, 3 tokens, G = 2
