@@ -52,15 +52,15 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "fd4109d5f030c7ae3cdbc9cf35389446e875073147fa94dfa0da5ad60b3920b2",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_272_814}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "4a5ce59cab0faa6746880429be8799045c30b2ca9c67b2aada01eb9681a0cd73",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_267_615}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
 # summary with its commands is in profiles/.  Valid only for these sources.
-MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "a70a43f676c6bfc05c8647f3201b7af3fb29d9f5b8645b04fd005b94297acc5e",
-                            "bytes_per_call": {(16, 512): 754_985_225, (1, 4096): 364_492_547}}
+MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "bea985d15d7d091f9f95ac8285055f69bc547fe684f90fe9fd53e12223aac699",
+                            "bytes_per_call": {(16, 512): 754_958_786, (1, 4096): 364_492_810}}
 PREFILL_SOURCES = ("gdn_prefill_two_pass.hip", "prefill_internal.h", "step_common.h", "device_common.h",
                    "gdn_internal.h")
 
