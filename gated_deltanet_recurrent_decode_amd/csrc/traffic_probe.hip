@@ -28,10 +28,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(float *base, uint32
 template <int DK, int DV, int NTH>
 __global__ __launch_bounds__(NTH) void traffic_probe_kernel(ProbeParams p)
 {
-    constexpr int CG = DV / 4, RG = NTH / CG, RPT = DK / RG;
+    // the step's whole-tile layout: eight row groups, wave w holding columns
+    // 32 w .. 32 w + 31, lane l column group 8 w + l % 8 and row group l / 8
+    constexpr int RG = 8, RPT = DK / RG;
+    static_assert(NTH == 2 * DV && DV % 32 == 0, "two threads a column, as in the step");
     constexpr uint32_t TILE = (uint32_t)DK * DV;
     const int tid = threadIdx.x;
-    const int cg = tid % CG, rg = tid / CG;
+    const int lane = tid & 63;
+    const int rg = lane >> 3;
+    const int cg = (tid >> 6) * 8 + (lane & 7);
     const int h = blockIdx.x % p.H;
     const int r = blockIdx.x / p.H;
     const int rs = p.read_slot[r];
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(ProbeParams p, uint32_
 template <int DK, int DV>
 static hipError_t launch_probe(const ProbeParams &p, hipStream_t stream)
 {
-    constexpr int NTH = (DK * DV >= 128 * 128) ? 256 : 128;
+    constexpr int NTH = 2 * DV;
     const long long tiles = (long long)p.B * p.H;
     if (tiles <= 0)
         return hipSuccess;
