@@ -1089,16 +1089,23 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
                         dim3(NT), args, 0, stream);
     if (e != hipSuccess)
         return e;
-    // column slices: double them until the walk has 256 workgroups or the
-    // slices are 16 columns wide, and keep them at most 64 columns wide (two
-    // workgroups a CU then fit; with whole 128-column slices, one a CU, 16 x
-    // 512 took 10 us and 128 x 64 71 us longer)
+    // column slices 64, 32 or 16 wide (two workgroups a CU fit; with whole
+    // 128-column slices, one a CU, 16 x 512 took 10 us and 128 x 64 71 us
+    // longer).  The walk's time follows the CUs that get the most workgroups,
+    // each worth 1 / nsl of a head's work: take the nsl that makes
+    // ceil(heads nsl / 256) / nsl least, the fewer slices on a tie (measured
+    // on MI355X against doubling until 256 workgroups: 6 x 1024 221 -> 215 us,
+    // 12 x 768 306 -> 296; the power-of-two batches keep their choice)
     const long long heads = (long long)p.B * p.H_v;
-    int nsl = 1;
-    while (nsl < DV / 16 && heads * nsl < 256)
-        nsl *= 2;
-    if (DV / nsl > 64)
-        nsl = DV / 64;
+    int nsl = DV / 64 > 1 ? DV / 64 : 1;
+    long long best = (heads * nsl + 255) / 256; // per-CU share, in units of 1 / nsl
+    for (int n = 2 * nsl; n <= DV / 16; n *= 2) {
+        const long long share = (heads * n + 255) / 256;
+        if (share * nsl < best * n) { // share / n < best / nsl
+            nsl = n;
+            best = share;
+        }
+    }
     switch (DV / nsl) {
     case 16:
         return hipLaunchKernel(reinterpret_cast<const void *>(&tp_inter16_kernel<DK, DV>),

@@ -151,10 +151,15 @@ def test_two_pass_bench_workload_one_long_prompt(gdn, torch):
 @pytest.mark.parametrize("lengths,hk,hv", [
     ([100, 33, 64, 5], 16, 16),                                     # 64 heads: 32-column slices
     ([40, 1, 70, 32, 31, 65, 2, 50], 16, 16),                       # 128 heads: 64-column slices
-    ([9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20, 6], 2, 4),  # 68 heads: 8 past the last group of 8
-], ids=["4seq-slices32", "8seq-slices64", "17seq-slices32-tail"])
+    ([9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20, 6], 2, 4),  # 68 heads: 16-column, 4 past the last group of 8
+    ([9, 40, 1, 33, 64, 2, 17, 30, 5], 2, 4),                       # 36 heads: 32-column, 4 past the last group of 8
+    ([30, 7, 61, 2, 33, 12, 40, 1, 64, 25, 3, 50], 16, 16),         # 192 heads: 32-column slices
+    ([40, 3, 65, 32, 1, 70], 16, 16),                               # 96 heads: 16-column slices
+], ids=["4seq-slices32", "8seq-slices64", "17seq-slices16-tail", "9seq-slices32-tail", "12seq-slices32",
+        "6seq-slices16"])
 def test_two_pass_wide_slices(gdn, torch, lengths, hk, hv):
-    """The walk over column slices 32 and 64 wide (state and U in LDS), and
+    """The walk over column slices of each width the call's head count picks
+    (16 wide: the state in registers; 32 and 64: state and U in LDS), and
     prompt-head pairs past the last whole group of eight placed in order."""
     _check(gdn, torch, gi.prefill(lengths, H_k=hk, H_v=hv, d=128, seed=len(lengths) + 90), two_pass=True)
 
