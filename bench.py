@@ -59,8 +59,8 @@ KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
 # summary with its commands is in profiles/.  Valid only for these sources.
-MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "bea985d15d7d091f9f95ac8285055f69bc547fe684f90fe9fd53e12223aac699",
-                            "bytes_per_call": {(16, 512): 754_958_786, (1, 4096): 364_492_810}}
+MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "af22cc7cd053d4de4d03c0a7962cc3bef17720b62ec37a87ec34db05457a8c8d",
+                            "bytes_per_call": {(16, 512): 754_928_363, (1, 4096): 364_499_998}}
 PREFILL_SOURCES = ("gdn_prefill_two_pass.hip", "prefill_internal.h", "step_common.h", "device_common.h",
                    "gdn_internal.h")
 
