@@ -52,8 +52,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "4a5ce59cab0faa6746880429be8799045c30b2ca9c67b2aada01eb9681a0cd73",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_267_615}
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "aa8c3b834f71e511101c4bf3eb2a47729ab6e2b91ce665b7c0aedd81cb7bd67f",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_273_436}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
