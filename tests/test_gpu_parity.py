@@ -179,6 +179,24 @@ def test_sweep_twin_and_in_place(gdn, torch, B):
     assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
 
 
+@pytest.mark.parametrize("B", [8, 24, 40])
+def test_sliced_twin_step_equals_whole_tile_in_place(gdn, torch, B):
+    """Row counts whose head tiles leave a remainder of 1..128 over the 256 CUs
+    (8, 24, 40 rows of 16 heads): the twin step splits each head into two column
+    slices while the in-place step keeps whole tiles.  Both match the oracle and
+    each other bit for bit (every slice sums over d_k in the same order)."""
+    t = torch
+    case = gi.qwen08b(B=B, seed=B)
+    dp_t, out_t = _check_step(gdn, case, twin=True, poison=True)
+    dp_i, out_i = _check_step(gdn, case, twin=False)
+    assert t.equal(out_t.view(t.int16), out_i.view(t.int16))
+    pool = case.pools[0]
+    wr = t.from_numpy(pool.write_slot.astype(np.int64)).cuda()
+    rd = t.from_numpy(pool.read_slot.astype(np.int64)).cuda()
+    assert t.equal(dp_t.state[wr].view(t.int32), dp_i.state[rd].view(t.int32))
+    assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
+
+
 # ------------------------------------------------------------------ workload: 9B-like, 24 layers
 
 def test_9b_24_layers_back_to_back_sampled_rows(gdn, torch):
