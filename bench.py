@@ -52,14 +52,14 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
 # kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "aa8c3b834f71e511101c4bf3eb2a47729ab6e2b91ce665b7c0aedd81cb7bd67f",
+MEASURED_TRAFFIC = {"kernel_sources_sha256": "4863858c8d7ca2b7e1d24014f6a9a5fad8c1b7fed79cde630f4c85f422a2a03c",
                     "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_273_436}
 KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
 # summary with its commands is in profiles/.  Valid only for these sources.
-MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "af22cc7cd053d4de4d03c0a7962cc3bef17720b62ec37a87ec34db05457a8c8d",
+MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "622f3182d49fa21c025fdb89cbe4482853d89abcbc62bdc50e3394953b4d9495",
                             "bytes_per_call": {(16, 512): 754_928_363, (1, 4096): 364_499_998}}
 PREFILL_SOURCES = ("gdn_prefill_two_pass.hip", "prefill_internal.h", "step_common.h", "device_common.h",
                    "gdn_internal.h")

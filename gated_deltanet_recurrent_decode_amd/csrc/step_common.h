@@ -14,6 +14,9 @@ namespace gdn {
 // column split and head grouping: in-thread over m, then the pairwise tree
 // ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over row groups -- so twin and
 // in-place launches, and padded and unpadded buckets, give identical bits.
+// The single-token tile kernel keeps the row groups in lane bits 3-5 (a wave
+// holds 32 columns and the tree ends inside it); the token walk keeps them in
+// lane bit 5 and the wave index (the tree ends in LDS).  Both form this tree.
 template <int DK, int DVS, int HPW>
 struct StepCfg {
     static constexpr int RG = 8;                   // row groups
@@ -67,7 +70,9 @@ __device__ __forceinline__ float conv_tap4(uint32_t w01, uint32_t w23, uint32_t 
 // written lines but not streamed reads): 64 rows 28.3 us with streaming
 // stores against 30.5 written through (sc0 sc1) and 30.7 plain; 128 rows 54.2
 // against 58.3 and 59.2.  Written-through stores only look faster when the
-// next read of the slot comes soon enough to hit the Infinity Cache.
+// next read of the slot comes soon enough to hit the Infinity Cache.  On the
+// current tile kernel at 64 rows: 27.7 us a step streaming, 29.5 written
+// through, 30.2 plain.
 constexpr int kLoadPolicy = 2;
 constexpr int kStorePolicy = 2;
 // Four waves per SIMD for the twin single-token kernel: a 64-row step (1024
