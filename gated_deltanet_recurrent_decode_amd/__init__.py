@@ -167,6 +167,39 @@ class _on:
 
 # ------------------------------------------------------------------ entry points
 
+def _channels(H_k, H_v, d_k, d_v):
+    """The conv's channel count for these heads (q and k of every key head, v of
+    every value head); the library derives every conv offset from it."""
+    if H_k < 1 or H_v < 1 or H_v % H_k != 0:
+        raise ValueError(f"H_v ({H_v}) must be a positive multiple of H_k ({H_k})")
+    return 2 * H_k * d_k + H_v * d_v
+
+
+def _step_layout(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k):
+    """Shape and stride checks of a decode step (any device, meta tensors too);
+    returns the Dims and x's row stride."""
+    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError("x: expected [B][T][C] with contiguous tokens and channels")
+    if state.dim() != 4 or conv_state.dim() != 3 or conv_w.dim() != 2:
+        raise ValueError("state must be [N][H_v][d_k][d_v], conv_state [N][W-1][C], conv_w [C][W]")
+    B, T, C = x.shape
+    N, H_v, d_k, d_v = state.shape
+    W = conv_w.shape[1]
+    if C != _channels(H_k, H_v, d_k, d_v):
+        raise ValueError(f"x has {C} channels; H_k={H_k}, H_v={H_v}, d_k={d_k}, d_v={d_v} need 2*H_k*d_k + H_v*d_v")
+    if tuple(conv_state.shape) != (N, W - 1, C) or conv_w.shape[0] != C:
+        raise ValueError("conv_state / conv_w do not match x and state")
+    if tuple(g.shape) != (B, T, H_v) or tuple(beta.shape) != (B, T, H_v) or tuple(out.shape) != (B, T, H_v, d_v):
+        raise ValueError("g, beta, out do not match [B][T][H_v](, d_v)")
+    if tuple(read_slot.shape) != (B,) or (write_slot is not None and tuple(write_slot.shape) != (B,)):
+        raise ValueError("slot arrays must be [B]")
+    if conv_b is not None and tuple(conv_b.shape) != (C,):
+        raise ValueError("conv_b must be [C]")
+    d = Dims(B, T, H_k, H_v, d_k, d_v, W, N)
+    x_row_stride = x.stride(0) if B > 0 else T * C
+    return d, x_row_stride
+
+
 def _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k):
     torch = _torch()
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
@@ -176,24 +209,7 @@ def _step_args(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_s
         _contig(_dev(t, n, dt), n)
     _contig(_dev(conv_b, "conv_b", bf, allow_none=True), "conv_b")
     _contig(_dev(write_slot, "write_slot", i32, allow_none=True), "write_slot")
-    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
-        raise ValueError("x: expected [B][T][C] with contiguous tokens and channels")
-    if state.dim() != 4 or conv_state.dim() != 3 or conv_w.dim() != 2:
-        raise ValueError("state must be [N][H_v][d_k][d_v], conv_state [N][W-1][C], conv_w [C][W]")
-    B, T, C = x.shape
-    N, H_v, d_k, d_v = state.shape
-    W = conv_w.shape[1]
-    if conv_state.shape != (N, W - 1, C) or conv_w.shape[0] != C:
-        raise ValueError("conv_state / conv_w do not match x and state")
-    if g.shape != (B, T, H_v) or beta.shape != (B, T, H_v) or out.shape != (B, T, H_v, d_v):
-        raise ValueError("g, beta, out do not match [B][T][H_v](, d_v)")
-    if read_slot.shape != (B,) or (write_slot is not None and write_slot.shape != (B,)):
-        raise ValueError("slot arrays must be [B]")
-    if conv_b is not None and conv_b.shape != (C,):
-        raise ValueError("conv_b must be [C]")
-    d = Dims(B, T, H_k, H_v, d_k, d_v, W, N)
-    x_row_stride = x.stride(0) if B > 0 else T * C
-    return d, x_row_stride
+    return _step_layout(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, H_k)
 
 
 def gdn_decode_step(x, conv_w, conv_b, conv_state, state, g, beta, read_slot, write_slot, out, *,
@@ -253,6 +269,31 @@ def gdn_decode_step_tokens(x, conv_w, conv_b, conv_state, state, g, beta, read_s
             _stream(stream, dev)))
 
 
+def _prefill_layout(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k):
+    """Shape and stride checks of a prefill call (any device, meta tensors too);
+    returns the Dims and x's row stride."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x: expected [T][C] with contiguous channels")
+    if state.dim() != 4 or conv_state.dim() != 3 or conv_w.dim() != 2:
+        raise ValueError("state must be [N][H_v][d_k][d_v], conv_state [N][W-1][C], conv_w [C][W]")
+    T, C = x.shape
+    N, H_v, d_k, d_v = state.shape
+    W = conv_w.shape[1]
+    if C != _channels(H_k, H_v, d_k, d_v):
+        raise ValueError(f"x has {C} channels; H_k={H_k}, H_v={H_v}, d_k={d_k}, d_v={d_v} need 2*H_k*d_k + H_v*d_v")
+    if slot.dim() != 1:
+        raise ValueError("slot must be [B]")
+    B = slot.shape[0]
+    if (tuple(cu_seqlens.shape) != (B + 1,) or tuple(g.shape) != (T, H_v) or tuple(beta.shape) != (T, H_v)
+            or tuple(out.shape) != (T, H_v, d_v)):
+        raise ValueError("cu_seqlens [B+1], g/beta [T][H_v], out [T][H_v][d_v] expected")
+    if tuple(conv_state.shape) != (N, W - 1, C) or conv_w.shape[0] != C:
+        raise ValueError("conv_state / conv_w do not match x and state")
+    if conv_b is not None and tuple(conv_b.shape) != (C,):
+        raise ValueError("conv_b must be [C]")
+    return Dims(B, T, H_k, H_v, d_k, d_v, W, N), (x.stride(0) if T > 0 else C)
+
+
 def _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k):
     torch = _torch()
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
@@ -262,19 +303,7 @@ def _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slo
                      (out, "out", bf)):
         _contig(_dev(t, n, dt), n)
     _contig(_dev(conv_b, "conv_b", bf, allow_none=True), "conv_b")
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x: expected [T][C] with contiguous channels")
-    T, C = x.shape
-    N, H_v, d_k, d_v = state.shape
-    W = conv_w.shape[1]
-    if slot.dim() != 1:
-        raise ValueError("slot must be [B]")
-    B = slot.shape[0]
-    if cu_seqlens.shape != (B + 1,) or g.shape != (T, H_v) or beta.shape != (T, H_v) or out.shape != (T, H_v, d_v):
-        raise ValueError("cu_seqlens [B+1], g/beta [T][H_v], out [T][H_v][d_v] expected")
-    if conv_state.shape != (N, W - 1, C) or conv_w.shape[0] != C:
-        raise ValueError("conv_state / conv_w do not match x and state")
-    return Dims(B, T, H_k, H_v, d_k, d_v, W, N), (x.stride(0) if T > 0 else C)
+    return _prefill_layout(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k)
 
 
 def gdn_prefill(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, *, H_k: int,
@@ -313,6 +342,27 @@ def gdn_prefill_two_pass(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqle
             workspace.numel(), _stream(stream, dev)))
 
 
+def _conv_layout(x, conv_w, conv_b, conv_state, read_slot, write_slot, out):
+    """Shape and stride checks of conv_decode (any device, meta tensors too);
+    returns B, C, W, N."""
+    if conv_state.dim() != 3 or conv_w.dim() != 2 or read_slot.dim() != 1:
+        raise ValueError("conv_state must be [N][W-1][C], conv_w [C][W], read_slot [B]")
+    N, Wm1, C = conv_state.shape
+    W = Wm1 + 1
+    B = read_slot.shape[0]
+    if tuple(conv_w.shape) != (C, W):
+        raise ValueError(f"conv_w must be [C][W] = [{C}][{W}] to match conv_state")
+    if conv_b is not None and tuple(conv_b.shape) != (C,):
+        raise ValueError("conv_b must be [C]")
+    if write_slot is not None and tuple(write_slot.shape) != (B,):
+        raise ValueError("write_slot must be [B] like read_slot")
+    if x.dim() != 2 or out.dim() != 2 or x.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("x and out must be [B][C] with contiguous channels")
+    if x.shape[0] != B or out.shape[0] != B or x.shape[1] < C or out.shape[1] < C:
+        raise ValueError("x / out do not match [B][C]")
+    return B, C, W, N
+
+
 def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, activation: bool = True,
                 stream=None) -> None:
     """Pooled conv decode for one token a row (see ``conv_decode`` in include/gdn.h).
@@ -327,16 +377,11 @@ def conv_decode(x, conv_w, conv_b, conv_state, read_slot, write_slot, out, *, ac
         _contig(_dev(t, n, dt), n)
     _contig(_dev(conv_b, "conv_b", bf, allow_none=True), "conv_b")
     _contig(_dev(write_slot, "write_slot", i32, allow_none=True), "write_slot")
-    N, Wm1, C = conv_state.shape
-    B = read_slot.shape[0]
-    if x.dim() != 2 or out.dim() != 2 or x.stride(1) != 1 or out.stride(1) != 1:
-        raise ValueError("x and out must be [B][C] with contiguous channels")
-    if x.shape[0] != B or out.shape[0] != B or x.shape[1] < C or out.shape[1] < C:
-        raise ValueError("x / out do not match [B][C]")
+    B, C, W, N = _conv_layout(x, conv_w, conv_b, conv_state, read_slot, write_slot, out)
     dev = _device(x, conv_w, conv_b, conv_state, read_slot, write_slot, out)
     with _on(dev):
         _check("conv_decode", lib().conv_decode(
-            B, C, Wm1 + 1, N, _ptr(x), x.stride(0) if B > 0 else C, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+            B, C, W, N, _ptr(x), x.stride(0) if B > 0 else C, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
             _ptr(read_slot), _ptr(write_slot), _ptr(out), out.stride(0) if B > 0 else C, int(bool(activation)),
             _stream(stream, dev)))
 
@@ -354,14 +399,22 @@ def slot_commit(read_slot, write_slot, *, stream=None) -> None:
                                                 _stream(stream, dev)))
 
 
+def _pool_layout(state, conv_state, H_k):
+    """Shape checks of a slot operation (any device, meta tensors too); returns the Dims."""
+    if state.dim() != 4 or conv_state.dim() != 3 or state.shape[0] != conv_state.shape[0]:
+        raise ValueError("state must be [N][H_v][d_k][d_v] and conv_state [N][W-1][C] over the same slots")
+    N, H_v, d_k, d_v = state.shape
+    if conv_state.shape[2] != _channels(H_k, H_v, d_k, d_v):
+        raise ValueError(f"conv_state has {conv_state.shape[2]} channels; H_k={H_k}, H_v={H_v}, d_k={d_k}, "
+                         f"d_v={d_v} need 2*H_k*d_k + H_v*d_v")
+    return Dims(0, 1, H_k, H_v, d_k, d_v, conv_state.shape[1] + 1, N)
+
+
 def _pool_dims(state, conv_state, H_k):
     torch = _torch()
     _contig(_dev(state, "state", torch.float32), "state")
     _contig(_dev(conv_state, "conv_state", torch.bfloat16), "conv_state")
-    if state.dim() != 4 or conv_state.dim() != 3 or state.shape[0] != conv_state.shape[0]:
-        raise ValueError("state must be [N][H_v][d_k][d_v] and conv_state [N][W-1][C] over the same slots")
-    N, H_v, d_k, d_v = state.shape
-    return Dims(0, 1, H_k, H_v, d_k, d_v, conv_state.shape[1] + 1, N)
+    return _pool_layout(state, conv_state, H_k)
 
 
 def slot_reset(state, conv_state, slots, *, H_k: int, stream=None) -> None:
@@ -400,9 +453,16 @@ def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, rows: int | 
     _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
     _contig(_dev(write_slot, "write_slot", torch.int32, allow_none=True), "write_slot")
     _contig(_dev(sink, "sink", torch.float32), "sink")
+    if state.dim() != 4 or read_slot.dim() != 1:
+        raise ValueError("state must be [N][H][d_k][d_v] and read_slot [B]")
     N, H, d_k, d_v = state.shape
+    n = read_slot.shape[0] if rows is None else int(rows)
+    if mode in (0, 1, 2, 3) and (n > read_slot.shape[0] or (write_slot is not None and write_slot.shape[0] < n)):
+        raise ValueError("the slot arrays must hold an entry for every row")
+    if mode == 4 and (read_slot.shape[0] < 1 or write_slot is None or write_slot.shape[0] < 1):
+        raise ValueError("the contiguous copy takes its first slots from read_slot[0] and write_slot[0]")
     dev = _device(state, read_slot, write_slot, sink)
     with _on(dev):
         _check("gdn_traffic_probe", lib().gdn_traffic_probe(
-            int(mode), read_slot.shape[0] if rows is None else int(rows), H, d_k, d_v, N, _ptr(state),
+            int(mode), n, H, d_k, d_v, N, _ptr(state),
             _ptr(read_slot), _ptr(write_slot), _ptr(sink), _stream(stream, dev)))
