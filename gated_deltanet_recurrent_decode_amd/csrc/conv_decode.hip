@@ -25,7 +25,9 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(ConvParams p)
         *o = 0;
         return;
     }
-    if (rs < 0 || rs >= p.N || ws < 0 || ws >= p.N) { // unusable slot: NaN, no slot touched
+    // unusable: a slot out of range, or a write into the null slot (which must
+    // stay zero): NaN, no slot touched
+    if (rs < 0 || rs >= p.N || ws < 0 || ws >= p.N || ws == 0) {
         *o = 0x7fc0;
         return;
     }

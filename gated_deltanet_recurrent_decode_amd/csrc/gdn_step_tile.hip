@@ -1,6 +1,6 @@
-// gdn_step_tile.hip -- the single-token decode step, one head tile per
-// workgroup, for gfx950: every twin-slot step, and in-place steps whose key
-// heads each have one value head.
+// gdn_step_tile.hip -- the single-token decode step, by head tiles, for
+// gfx950: every twin-slot step, and in-place steps whose key heads each have
+// one value head.
 //
 // The same computation as the key-head-group kernel in gdn_step.hip (conv
 // decode + SiLU, L2 norms, gated delta rule, read-out), with the same thread
@@ -8,8 +8,10 @@
 // twin step reads one slot of the request's pair and writes the other (mstar
 // PR #1139, "What changed"); in place it writes back to the slot it read,
 // which is only safe here when no other workgroup reads the tile's q/k conv
-// windows, i.e. with one value head per key head.  One workgroup per head
-// tile (row, value head, column slice).  The loads are straight-line: a
+// windows, i.e. with one value head per key head.  A workgroup takes one head
+// tile (row, value head, column slice), or two or three whole tiles when that
+// keeps each compute unit's reads ahead of its writes (see dispatch_tile).
+// The loads are straight-line: a
 // padding row (read slot 0) or a row with an unusable slot gets buffer
 // resources of size 0, so its loads return zeros without touching memory.
 // Without a branch between the slot lookup and the loads, every load is issued
@@ -22,13 +24,17 @@
 //
 // Each wave holds all eight row groups of 32 columns, so the projections'
 // sums over d_k end inside the wave (lane butterflies) with no LDS round trip
-// and no barrier; the only barrier publishes the conv outputs.  At d_k = d_v
-// = 128 the whole-tile kernel takes 121 VGPRs, four waves per SIMD, with no
-// spill (measured on MI355X against the layout that summed the row groups
-// across waves in LDS: 64 rows 28.4 -> 27.6 us a step).
+// and no barrier; one barrier publishes the conv outputs, and a multi-tile
+// workgroup meets a second one between its last load and its first store.  At
+// d_k = d_v = 128 the kernel takes 122 VGPRs (107 with several tiles a
+// workgroup), four waves per SIMD, with no spill (measured on MI355X against
+// the layout that summed the row groups across waves in LDS: 64 rows 28.4 ->
+// 27.6 us a step).
 
 #include "gdn_internal.h"
 #include "step_common.h"
+
+#include <atomic>
 
 namespace gdn {
 
@@ -87,7 +93,9 @@ __device__ __forceinline__ void tile_locate(TileState<DK, DVS> &t, int tile, con
     t.own_qk = (t.hv % p.G == 0) && cs == 0; // the tile that writes back the key head's q/k windows
     t.rs = p.read_slot[t.r];
     t.ws = p.twin ? p.write_slot[t.r] : t.rs;
-    const bool bad = t.rs < 0 || t.rs >= p.N || t.ws < 0 || t.ws >= p.N || (p.twin && t.ws == t.rs);
+    // unusable: a slot out of range, or a twin row writing over its own read
+    // slot or into the null slot (which must stay zero: it never holds a row)
+    const bool bad = t.rs < 0 || t.rs >= p.N || t.ws < 0 || t.ws >= p.N || (p.twin && (t.ws == t.rs || t.ws == 0));
     t.real = t.valid && t.rs != 0 && !bad;
     t.fill = t.rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
     t.g = p.g[(size_t)t.r * p.H_v + t.hv];
@@ -98,7 +106,7 @@ __device__ __forceinline__ void tile_locate(TileState<DK, DVS> &t, int tile, con
 // columns): each conv lane takes four consecutive channels -- 16-byte weight
 // loads, 8-byte window, x and bias loads, raw bf16 bits.
 template <int DK, int DV, int DVS>
-__device__ __forceinline__ void tile_issue_small(TileState<DK, DVS> &t, const StepParams &p)
+__device__ __forceinline__ void tile_issue_small(TileState<DK, DVS> &t, const StepParams &p, int ht)
 {
     using TT = TileState<DK, DVS>;
     constexpr int NT = TT::Cfg::NT;
@@ -111,7 +119,7 @@ __device__ __forceinline__ void tile_issue_small(TileState<DK, DVS> &t, const St
     const __amdgpu_buffer_rsrc_t br = bf16_rsrc(p.conv_b ? p.conv_b : p.conv_w, p.conv_b ? cbytes : 0u);
 #pragma unroll
     for (int q = 0; q < TT::NCQ; ++q) {
-        const int li = threadIdx.x + q * NT;
+        const int li = ht + q * NT;
         t.lane_ok[q] = li < TT::NCL;
         const int e = t.lane_ok[q] ? 4 * li : 0;
         t.e4[q] = e;
@@ -152,9 +160,9 @@ __device__ __forceinline__ void tile_issue_state(TileState<DK, DVS> &t, const St
 // Conv + SiLU -> LDS, L2 norms, projections, the fixed-order reduction, the
 // delta update, the read-out, and the stores of o, the advanced conv windows
 // and the new state.
-template <int DK, int DV, int DVS, bool INPLACE>
+template <int DK, int DV, int DVS, bool INPLACE, int TPW>
 __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepParams &p, int cg, int rg, int lane,
-                                             uint32_t voff, float *y_lds)
+                                             int ht, uint32_t voff, float *y_lds)
 {
     using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
@@ -165,7 +173,7 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
     // ---- conv decode + SiLU -> LDS; the window advances in registers
 #pragma unroll
     for (int q = 0; q < TT::NCQ; ++q) {
-        if (((int)(threadIdx.x + q * Cfg::NT) >> 6) >= NCW) // wave-uniform; no memory access inside
+        if (!t.real || ((ht + q * Cfg::NT) >> 6) >= NCW) // wave-uniform; no memory access inside
             continue;
         const uint4 wl = t.wlo[q], wh = t.whi[q];
         const uint2 a0 = t.wn0[q], a1 = t.wn1[q], a2 = t.wn2[q], xx = t.xq[q], bb = t.bq[q];
@@ -185,6 +193,11 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
 
     // ---- L2 norms of q and k (every wave computes the same sums)
     float sq = 0.f, sk = 0.f, sqk = 0.f;
+    float4 a = f4_zero(), b = f4_zero();
+    float rk = 0.f, kq = 0.f;
+    const float alpha = expf(t.g);
+    const float bt = t.beta;
+    if (t.real) {
 #pragma unroll
     for (int i = lane; i < DK; i += 64) {
         const float qv = y_lds[i], kv = y_lds[DK + i];
@@ -196,13 +209,11 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
     sk = xor_sum<1>(sk);
     sqk = xor_sum<1>(sqk);
     const float rq = 1.0f / sqrtf(sq + p.l2_eps);
-    const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+    rk = 1.0f / sqrtf(sk + p.l2_eps);
     const float qs = rq * p.q_scale;
-    const float kq = sqk * rk * qs; // k^ . q^
+    kq = sqk * rk * qs; // k^ . q^
 
     // ---- projections of the state onto k^ and q^
-    const float alpha = expf(t.g);
-    const float bt = t.beta;
     float4 pa = f4_zero(), pb = f4_zero();
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
@@ -229,7 +240,22 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
     pb.y = xor_sum<8>(pb.y);
     pb.z = xor_sum<8>(pb.z);
     pb.w = xor_sum<8>(pb.w);
-    const float4 a = pa, b = pb;
+    a = pa;
+    b = pb;
+    }
+    if constexpr (TPW > 1) {
+        // every wave of the workgroup has its tile in registers before any
+        // wave stores: the compute unit's reads all come before its writes.
+        // A real tile has consumed every load by now; waiting for all of them
+        // on every path also keeps the compiler from guarding the stores below
+        // with waits for loads a padding tile never consumed
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!t.real)
+        return;
 
     // ---- delta update in registers, and the read-out
     const float *vv = &y_lds[2 * DK + 4 * cg];
@@ -267,7 +293,7 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
                                                   t.real ? 3u * cbytes : 0u);
 #pragma unroll
     for (int q = 0; q < TT::NCQ; ++q) {
-        if (((int)(threadIdx.x + q * Cfg::NT) >> 6) >= NCW) // waves with no conv lane own nothing
+        if (((ht + q * Cfg::NT) >> 6) >= NCW) // waves with no conv lane own nothing
             continue;
         const uint32_t o2w = t.own[q] ? (uint32_t)t.c[q] * 2u : kOOB;
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{t.wn0[q].x, t.wn0[q].y}, wwin, o2w, 0, kStorePolicy);
@@ -286,30 +312,42 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
                                                kStorePolicy);
 }
 
-template <int DK, int DV, int DVS, bool INPLACE>
-__global__ __launch_bounds__(2 * DVS) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+template <int DK, int DV, int DVS, bool INPLACE, int TPW>
+__global__ __launch_bounds__(2 * DVS * TPW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void gdn_step_tile_kernel(StepParams p)
 {
     using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
-    constexpr int CG = Cfg::CG, NCH = Cfg::NCH;
-    static_assert(Cfg::NT == 2 * DVS, "launch bound must match the layout");
+    constexpr int CG = Cfg::CG, NCH = Cfg::NCH, NTS = Cfg::NT;
+    static_assert(NTS == 2 * DVS, "launch bound must match the layout");
     static_assert(Cfg::RG == 8 && DVS % 32 == 0, "a wave holds the eight row groups of 32 columns");
 
-    __shared__ float y_lds[NCH + 4]; // + a padding slot for spare conv lanes
+    __shared__ float y_all[TPW][NCH + 4]; // + a padding slot for spare conv lanes
 
-    // thread layout: wave w holds columns 32 w .. 32 w + 31 of the slice, lane
-    // l column group 8 w + l % 8 (four columns) and row group l / 8, i.e. rows
-    // l / 8, l / 8 + 8, ..., so a row's projection is a sum inside one wave
+    // TPW head tiles a workgroup, 2 DVS threads each.  Thread layout inside a
+    // tile: wave w holds columns 32 w .. 32 w + 31 of the slice, lane l column
+    // group 8 w + l % 8 (four columns) and row group l / 8, i.e. rows l / 8,
+    // l / 8 + 8, ..., so a row's projection is a sum inside one wave
     const int tid = threadIdx.x;
+    const int sub = __builtin_amdgcn_readfirstlane(tid / NTS); // wave-uniform
+    const int ht = tid - sub * NTS;
     const int lane = tid & 63;
     const int rg = lane >> 3;
-    const int cg = (tid >> 6) * 8 + (lane & 7);
+    const int cg = (ht >> 6) * 8 + (lane & 7);
     const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
+    float *y_lds = y_all[sub];
 
+    // workgroup -> tile group; with p.xcd_order, workgroups (which the
+    // hardware deals to the eight XCDs in turn) are renumbered so that each
+    // XCD gets a contiguous run of tile groups
+    int grp = blockIdx.x;
+    if (p.xcd_order) {
+        const int n = gridDim.x, x = blockIdx.x % 8, q = n / 8, rr = n % 8;
+        grp = x * q + min(x, rr) + (int)blockIdx.x / 8;
+    }
     TT t;
-    tile_locate(t, blockIdx.x, p);
-    tile_issue_small<DK, DV, DVS>(t, p);
+    tile_locate(t, grp * TPW + sub, p);
+    tile_issue_small<DK, DV, DVS>(t, p, ht);
     __builtin_amdgcn_sched_barrier(0); // the small loads stay ahead of the tile loads
     tile_issue_state<DK, DV, DVS>(t, p, voff);
     // every load is in flight; keep the scheduler from sinking any below the first wait
@@ -320,26 +358,28 @@ void gdn_step_tile_kernel(StepParams p)
         const uint32_t f2 = (uint32_t)t.fill * 0x10001u;
         const __amdgpu_buffer_rsrc_t orow =
             bf16_rsrc(p.out + ((size_t)t.r * p.H_v + t.hv) * DV, t.valid ? (uint32_t)DV * 2u : 0u);
-        if (tid < CG)
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{f2, f2}, orow, (uint32_t)(t.col0 + 4 * tid) * 2u, 0, 0);
-        if (p.next_read_slot && tid == 0 && t.valid && t.hv == 0 && t.col0 == 0) {
+        if (ht < CG)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{f2, f2}, orow, (uint32_t)(t.col0 + 4 * ht) * 2u, 0, 0);
+        if (p.next_read_slot && ht == 0 && t.valid && t.hv == 0 && t.col0 == 0) {
             p.next_read_slot[t.r] = t.ws;
             p.next_write_slot[t.r] = t.rs;
         }
-        return;
+        if constexpr (TPW == 1)
+            return;
     }
-    tile_process<DK, DV, DVS, INPLACE>(t, p, cg, rg, lane, voff, y_lds);
+    // the tiles of real rows do the work; the others only meet the barriers
+    tile_process<DK, DV, DVS, INPLACE, TPW>(t, p, cg, rg, lane, ht, voff, y_lds);
 
     // fused commit: the workgroup of a row's first tile writes the swapped
     // pair into the next step's slot arrays (distinct from the ones this step
     // reads, so there is no race)
-    if (p.next_read_slot && tid == 0 && t.valid && t.hv == 0 && t.col0 == 0) {
+    if (t.real && p.next_read_slot && ht == 0 && t.hv == 0 && t.col0 == 0) {
         p.next_read_slot[t.r] = t.ws;
         p.next_write_slot[t.r] = t.rs;
     }
 }
 
-template <int DK, int DV, int DVS>
+template <int DK, int DV, int DVS, int TPW>
 static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
 {
     StepParams q = p;
@@ -348,34 +388,75 @@ static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
     if (tiles <= 0)
         return hipSuccess;
     void *args[] = {&q};
-    const void *k = p.twin ? reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, false>)
-                           : reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, true>);
-    return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(2 * DVS), args, 0, stream);
+    const void *k = p.twin ? reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, false, TPW>)
+                           : reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, true, TPW>);
+    return hipLaunchKernel(k, dim3((unsigned)((tiles + TPW - 1) / TPW)), dim3(2 * DVS * TPW), args, 0, stream);
 }
 
-// Column slices per head.  Up to 2047 head tiles a step is one round of
-// workgroups on the 256 CUs, and its time follows the CUs that get the most
-// tiles.  Halving the tiles evens that out when heads mod 256 is between 1
-// and 128 (two half tiles where one CU had a whole one more than another);
-// otherwise whole tiles win, as slicing adds the q/k conv a slice more.
-// Measured on MI355X with the state cold, 16 heads a row, us a step whole
-// against sliced: 8 rows 6.66 / 5.78, 12 rows 7.20 / 7.26, 16 rows 8.13 /
-// 8.46, 24 rows 12.61 / 11.06, 40 rows 19.18 / 18.41, 48 rows 21.69 / 21.73,
-// 56 rows 25.56 / 24.98, 64 rows 27.8 / 28.4.  Under 128 tiles slices keep
-// going down to 32 columns.  Never in place: every slice reads the head's q/k
-// conv windows and one of them writes them back, so in place a slice that
-// starts late could read an advanced window; with whole tiles and one value
-// head per key head, no other workgroup reads them.
+// Compute units of the current device (cached per device; 256 on MI355X).
+static int device_cus()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Launch shape.  Up to 2047 head tiles a step is one round of workgroups on
+// the 256 CUs, and its time follows the CUs that get the most tiles.
+//
+// Tiles a workgroup (twin writes of 128 x 128 tiles).  With one tile a
+// workgroup, the four workgroups on a CU get their tiles at different times
+// (measured with clock stamps: the last load of a workgroup arrives anywhere
+// from 3 to 20 us into a 64-row step), and each writes as soon as its tile is
+// in, so reads and writes share HBM for most of the step -- which it serves
+// far worse than either alone (a probe with half the workgroups only reading
+// and half only writing took 34.7 us against 11.8 + 12.4 for the two apart).
+// A workgroup of two or three tiles waits until all of them are in before any
+// wave writes, so a CU's reads come before its writes.  It pays when a round
+// puts three or four tiles on every CU; measured, us a step: 64 rows 27.9 ->
+// 26.6 (two tiles a workgroup), 56 rows 24.8 -> 23.4 (two), 48 rows 21.7 ->
+// 20.8 (three); no gain at 32, 40, 96 or 128 rows, four tiles at 64 rows 27.2,
+// and none in place.
+//
+// Column slices per head otherwise.  Halving the tiles evens out the CUs' share
+// when heads mod 256 is between 1 and 128 (two half tiles where one CU had a
+// whole one more than another); otherwise whole tiles win, as slicing adds the
+// q/k conv a slice more.  Measured on MI355X with the state cold, 16 heads a
+// row, us a step whole against sliced: 8 rows 6.66 / 5.78, 12 rows 7.20 / 7.26,
+// 16 rows 8.13 / 8.46, 24 rows 12.61 / 11.06, 40 rows 19.18 / 18.41.  Under 128
+// tiles slices keep going down to 32 columns.  Never in place: every slice
+// reads the head's q/k conv windows and one of them writes them back, so in
+// place a slice that starts late could read an advanced window; with whole
+// tiles and one value head per key head, no other workgroup reads them.
+//
+// In place, workgroups are handed to the XCDs in contiguous runs of tiles
+// (64 rows 28.5 -> 28.1 us, 128 rows 53.7 -> 52.7); for twin writes that
+// order measured equal or slower and is not used.
 template <int DK, int DV>
 static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
 {
+    StepParams q = p;
+    q.xcd_order = p.twin ? 0 : 1;
     const long long heads = (long long)p.B * p.H_v;
     const long long rem = heads % 256;
+    if constexpr (DK == 128 && DV == 128) {
+        const long long cus = device_cus();
+        if (p.twin && heads * 2 > 5 * cus && heads <= 4 * cus)
+            return heads <= 3 * cus ? launch_tile<DK, DV, DV, 3>(q, stream) : launch_tile<DK, DV, DV, 2>(q, stream);
+    }
     if (!p.twin || heads >= 2048 || (heads >= 128 && (rem == 0 || rem > 128)))
-        return launch_tile<DK, DV, DV>(p, stream);
+        return launch_tile<DK, DV, DV, 1>(q, stream);
     if (heads >= 32 || DV < 128)
-        return launch_tile<DK, DV, DV / 2>(p, stream);
-    return launch_tile<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32)>(p, stream);
+        return launch_tile<DK, DV, DV / 2, 1>(q, stream);
+    return launch_tile<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32), 1>(q, stream);
 }
 
 hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream)

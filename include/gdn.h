@@ -31,9 +31,10 @@
  *     slot values lie in [0, N); no two real rows share a slot; for a twin
  *     write a real row's write slot differs from its read slot and from every
  *     other row's slots.  The kernels bounds-check every slot they read: a
- *     row with a slot outside [0, N), or a twin row whose write slot equals
- *     its read slot, touches no pool memory and gets NaN in every output
- *     element instead.
+ *     row with a slot outside [0, N), or a real row (read slot not 0) of a
+ *     twin write whose write slot equals its read slot or is the null slot
+ *     0, touches no pool memory and gets NaN in every output element
+ *     instead.  Slot 0 is never written by any entry point.
  *   - Calls that overlap on the same pool slots race (as any two kernels
  *     writing the same memory would).
  */
@@ -237,7 +238,9 @@ size_t gdn_prefill_two_pass_workspace_bytes(const gdn_dims *dims);
  *   y   = sum_w conv_w[c][w] * win[w] (+ conv_b[c]), in fp32
  *   out[r][c] = bf16(activation ? silu(y) : y)
  *   conv_state[ws][..][c] = win[1..W-1]   (a bit-exact shift of bf16 values)
- * A row with rs == 0 gets +0.0 outputs and touches no slot.
+ * A row with rs == 0 gets +0.0 outputs and touches no slot.  A row with
+ * rs != 0 and a slot outside [0, N), or with ws == 0 (the null slot never
+ * holds a window), gets NaN outputs and touches no slot.
  *   x   [B][C] bf16, rows x_row_stride elements apart (>= C)
  *   out [B][C] bf16, rows out_row_stride elements apart (>= C)
  *   activation: 0 none, 1 SiLU.  W must be 4.  B = 0 returns GDN_OK at once.

@@ -39,7 +39,8 @@
  *     hv / (H_v / H_k);
  *   - g (log decay) and beta arrive precomputed per (row, token, value head);
  *   - a row whose read slot is 0 is padding: its output is +0.0 and it reads
- *     and writes no slot;
+ *     and writes no slot; slot 0 is the null slot and never holds a row's
+ *     state or window, so a real row that would write it is refused;
  *   - the state is held in fp64 during a call and rounded to fp32 (round to
  *     nearest even) only where it is stored back to the pool; conv-window
  *     values are bf16 inputs and are stored back exactly.
@@ -125,7 +126,8 @@ void oracle_conv_token(int C, int W, const uint16_t *conv_w, const uint16_t *con
  * shifted window to conv_state[write_slot[r]] (read slot when write_slot is
  * NULL), y to out[r][c] in fp64.  Padding rows (read slot 0) give y = 0 and
  * touch no slot.  conv_state is [N][W-1][C] bf16 bits.  Returns 0, or -1 if a
- * slot is out of range or a window value is not bf16. */
+ * slot is out of range, a real row's write slot is the null slot 0, or a
+ * window value is not bf16. */
 int oracle_conv_decode(int B, int C, int W, int N, const uint16_t *x, int64_t x_row_stride,
                        const uint16_t *conv_w, const uint16_t *conv_b, uint16_t *conv_state,
                        const int32_t *read_slot, const int32_t *write_slot, int act,
@@ -137,6 +139,8 @@ int oracle_conv_decode(int B, int C, int W, int N, const uint16_t *x, int64_t x_
         int rs = read_slot[r];
         int ws = write_slot ? write_slot[r] : rs;
         if (rs < 0 || rs >= N || ws < 0 || ws >= N) { ok = 0; break; }
+        /* a real row never writes the null slot: slot 0 holds no row's window */
+        if (rs != 0 && ws == 0) { ok = 0; break; }
         if (rs == 0) {
             for (int c = 0; c < C; ++c)
                 out[(size_t)r * C + c] = 0.0;
@@ -231,8 +235,9 @@ static void oracle_row_token(int H_k, int H_v, int d_k, int d_v, int W, const ui
  *   read_slot, write_slot [B] int32 (write_slot NULL => in place)
  *   out        [B][T][H_v][d_v] fp64 (unrounded read-out)
  * Rows are processed in order; a row's new state and window are stored to
- * its write slot after its last token.  Returns 0, or -1 on an invalid slot,
- * shape or a non-bf16 window value.
+ * its write slot after its last token.  Returns 0, or -1 on an invalid slot
+ * (out of range, or a real twin row whose write slot is its read slot or the
+ * null slot 0), shape or a non-bf16 window value.
  */
 int oracle_gdn_decode_step(int B, int T, int H_k, int H_v, int d_k, int d_v, int W, int N,
                            const uint16_t *x, int64_t x_row_stride, const uint16_t *conv_w,
@@ -258,6 +263,9 @@ int oracle_gdn_decode_step(int B, int T, int H_k, int H_v, int d_k, int d_v, int
         int rs = read_slot[r];
         int ws = write_slot ? write_slot[r] : rs;
         if (rs < 0 || rs >= N || ws < 0 || ws >= N) { ok = 0; break; }
+        /* a real twin row writes a slot of its own other than the one it reads,
+         * and never the null slot, which holds no row's state */
+        if (write_slot && rs != 0 && (ws == 0 || ws == rs)) { ok = 0; break; }
         double *out_r = out + (size_t)r * T * H_v * d_v;
         if (rs == 0) {
             for (size_t e = 0; e < (size_t)T * H_v * d_v; ++e)

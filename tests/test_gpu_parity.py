@@ -179,12 +179,15 @@ def test_sweep_twin_and_in_place(gdn, torch, B):
     assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
 
 
-@pytest.mark.parametrize("B", [8, 24, 40])
-def test_sliced_twin_step_equals_whole_tile_in_place(gdn, torch, B):
-    """Row counts whose head tiles leave a remainder of 1..128 over the 256 CUs
-    (8, 24, 40 rows of 16 heads): the twin step splits each head into two column
-    slices while the in-place step keeps whole tiles.  Both match the oracle and
-    each other bit for bit (every slice sums over d_k in the same order)."""
+@pytest.mark.parametrize("B", [8, 24, 40, 44, 48, 56])
+def test_twin_launch_shapes_equal_whole_tile_in_place(gdn, torch, B):
+    """Row counts at which the twin step changes its launch shape while the
+    in-place step keeps one whole tile a workgroup: 8, 24 and 40 rows of 16
+    heads leave a remainder of 1..128 tiles over the 256 CUs, so the twin step
+    splits each head into two column slices; 44 and 48 rows put three whole
+    tiles in a workgroup (44: the last workgroup holds two tiles and an empty
+    one), 56 rows two.  Both match the oracle and each other bit for bit
+    (every tile sums over d_k in the same order whatever the launch shape)."""
     t = torch
     case = gi.qwen08b(B=B, seed=B)
     dp_t, out_t = _check_step(gdn, case, twin=True, poison=True)
@@ -197,24 +200,72 @@ def test_sliced_twin_step_equals_whole_tile_in_place(gdn, torch, B):
     assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
 
 
+@pytest.mark.parametrize("B,pad_rows", [(48, (5, 17, 30, 47)), (64, (0, 3, 31, 32, 63))], ids=["48rows", "64rows"])
+def test_multi_tile_workgroups_with_padding_rows(gdn, torch, B, pad_rows):
+    """Twin steps whose workgroups hold several head tiles (three at 48 rows,
+    two at 64), with padding rows scattered among the real ones so that some
+    workgroups hold tiles of a real and of a padding row.  Real rows match the
+    oracle, padding rows read out +0.0, slot 0 stays zero, nothing else in the
+    pool changes, and every real row's bits equal those of the same rows
+    stepped without the padding (a launch of another shape)."""
+    t = torch
+    case = gi.qwen08b(B=B, seed=100 + B)
+    pool, step, s = case.pools[0], case.steps[0][0], case.shape
+    for r in pad_rows:
+        pool.read_slot[r] = 0
+        pool.write_slot[r] = 0
+    dp, out = _check_step(gdn, case, twin=True)
+    pad = list(pad_rows)
+    assert t.count_nonzero(out[pad].view(t.int16)) == 0, "padding rows must read out +0.0"
+    assert t.count_nonzero(dp.state[0].view(t.int32)) == 0 and t.count_nonzero(dp.conv_state[0].view(t.int16)) == 0
+    real = [r for r in range(B) if r not in pad_rows]
+    dp2 = H.DevPool(pool)
+    idx = t.tensor(real, dtype=t.int64, device="cuda")
+    dp2.rd, dp2.wr = dp2.rd[idx].contiguous(), dp2.wr[idx].contiguous()
+    sub = gi.StepInputs(np.ascontiguousarray(step.x[real]), np.ascontiguousarray(step.g[real]),
+                        np.ascontiguousarray(step.beta[real]))
+    out2 = H.gpu_step(gdn, dp2, sub, s, twin=True)
+    t.cuda.synchronize()
+    assert t.equal(out[idx].view(t.int16), out2.view(t.int16))
+    wr = t.from_numpy(pool.write_slot[real].astype(np.int64)).cuda()
+    assert t.equal(dp.state[wr].view(t.int32), dp2.state[wr].view(t.int32))
+    assert t.equal(dp.conv_state[wr].view(t.int16), dp2.conv_state[wr].view(t.int16))
+
+
 # ------------------------------------------------------------------ workload: 9B-like, 24 layers
 
-def test_9b_24_layers_back_to_back_sampled_rows(gdn, torch):
+def test_9b_24_layers_back_to_back_every_row(gdn, torch):
+    """The 9B-like stack: 24 layers (16 key heads shared by 32 value heads, so
+    only the first value head of a key head writes back its q/k windows) run
+    back to back on their own pools, then every row of every layer is compared
+    with the oracle (outputs, written states and windows), with the write slots
+    NaN-poisoned beforehand and every other slot of each pool unchanged."""
     t = torch
     case = gi.qwen9b()
     s = case.shape
-    dps = [H.DevPool(p) for p in case.pools]
-    outs = [H.gpu_step(gdn, dps[L], case.steps[0][L], s) for L in range(24)]
-    t.cuda.synchronize()
-    rows = [0, 17, 40, 63]
+    dps, befores = [], []
     for L in range(24):
         pool = case.pools[L]
+        dp = H.DevPool(pool)
+        dp.state[t.from_numpy(pool.write_slot.astype(np.int64)).cuda()] = float("nan")
+        dps.append(dp)
+        befores.append((dp.state.clone(), dp.conv_state.clone()))
+    outs = [H.gpu_step(gdn, dps[L], case.steps[0][L], s) for L in range(24)]
+    t.cuda.synchronize()
+    for L in range(24):
+        pool, dp = case.pools[L], dps[L]
         hp = H.HostPool(pool)
-        ref = H.oracle_step(oracle, hp, case.steps[0][L], s, rows=rows)
-        H.assert_out_close(outs[L][rows], ref, f"layer {L} out")
-        wr = [int(pool.write_slot[r]) for r in rows]
-        H.assert_state_close(dps[L].state[wr].cpu().numpy(), hp.state[wr], f"layer {L} state")
-        np.testing.assert_array_equal(H.bf16_host(dps[L].conv_state[wr]), hp.conv_state[wr])
+        ref = H.oracle_step(oracle, hp, case.steps[0][L], s)
+        H.assert_out_close(outs[L], ref, f"layer {L} out")
+        wr = [int(x) for x in pool.write_slot]
+        idx = t.tensor(wr, dtype=t.int64, device="cuda")
+        H.assert_state_close(dp.state[idx].cpu().numpy(), hp.state[wr], f"layer {L} state")
+        np.testing.assert_array_equal(H.bf16_host(dp.conv_state[idx]), hp.conv_state[wr])
+        mask = t.ones(s.N, dtype=t.bool, device="cuda")
+        mask[idx] = False
+        bs, bc = befores[L]
+        assert t.equal(dp.state[mask].view(t.int32), bs[mask].view(t.int32)), f"layer {L}: a slot outside the write set changed"
+        assert t.equal(dp.conv_state[mask].view(t.int16), bc[mask].view(t.int16))
 
 
 # ------------------------------------------------------------------ workload: padded bucket
@@ -548,24 +599,58 @@ def test_empty_step_is_a_no_op(gdn, torch):
 
 
 def test_unusable_slots_give_nan_and_touch_nothing(gdn, torch):
+    """Rows with an unusable slot read out NaN and touch no pool memory: a read
+    slot out of range, a twin row writing over its own read slot, and a real
+    twin row whose write slot is the null slot (slot 0 holds no row)."""
     t = torch
-    case = gi.small(B=3, T=1, H_k=2, H_v=2, d=64, N=9)
+    case = gi.small(B=4, T=1, H_k=2, H_v=2, d=64, N=11)
     s, pool, step = case.shape, case.pools[0], case.steps[0][0]
     dp = H.DevPool(pool)
     rd = pool.read_slot.copy()
     wr = pool.write_slot.copy()
     rd[1] = s.N + 5      # out of range
     wr[2] = rd[2]        # twin row writing over its own read slot
+    wr[3] = 0            # real twin row writing into the null slot
     dp.rd, dp.wr = t.from_numpy(rd).cuda(), t.from_numpy(wr).cuda()
     before_s, before_c = dp.state.clone(), dp.conv_state.clone()
     out = H.gpu_step(gdn, dp, step, s)
     t.cuda.synchronize()
     o = H.bf16_host_f64(out)
-    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and not np.isnan(o[0]).any()
+    assert np.isnan(o[1:]).all() and not np.isnan(o[0]).any()
     mask = t.ones(s.N, dtype=t.bool, device="cuda")
     mask[int(wr[0])] = False
     assert t.equal(dp.state[mask], before_s[mask])
     assert t.equal(dp.conv_state[mask].view(t.int16), before_c[mask].view(t.int16))
+    assert t.count_nonzero(dp.state[0].view(t.int32)) == 0 and t.count_nonzero(dp.conv_state[0].view(t.int16)) == 0
+
+
+def test_conv_decode_never_writes_the_null_slot(gdn, torch):
+    """conv_decode with a real row whose write slot is 0: NaN outputs, no slot
+    touched; the other rows match the oracle and slot 0 stays zero."""
+    t = torch
+    case = gi.small(B=3, T=1, H_k=2, H_v=2, d=64, N=9, seed=4)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    rd = pool.read_slot.copy()
+    wr = pool.write_slot.copy()
+    wr[1] = 0
+    cs = H.bf16_dev(pool.conv_state)
+    before = cs.clone()
+    x = H.bf16_dev(np.ascontiguousarray(step.x[:, 0]))
+    out = t.empty((s.B, s.C), dtype=t.bfloat16, device="cuda")
+    gdn.conv_decode(x, H.bf16_dev(pool.conv_w), None, cs, t.from_numpy(rd).cuda(), t.from_numpy(wr).cuda(), out)
+    t.cuda.synchronize()
+    o = H.bf16_host_f64(out)
+    assert np.isnan(o[1]).all() and not np.isnan(o[[0, 2]]).any()
+    keep = [0, 2]
+    hcs = pool.conv_state.copy()
+    ref = oracle.conv_decode(np.ascontiguousarray(step.x[keep, 0]), pool.conv_w, None, hcs,
+                             np.ascontiguousarray(rd[keep]), np.ascontiguousarray(wr[keep]), act=True)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(o[keep] - ref) <= ulp + 1e-30)
+    mask = t.ones(s.N, dtype=t.bool, device="cuda")
+    mask[[int(wr[0]), int(wr[2])]] = False
+    assert t.equal(cs[mask].view(t.int16), before[mask].view(t.int16))
+    np.testing.assert_array_equal(H.bf16_host(cs[[int(wr[0]), int(wr[2])]]), hcs[[int(wr[0]), int(wr[2])]])
 
 
 def test_refusals_through_the_binding(gdn, torch):

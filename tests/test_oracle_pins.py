@@ -344,6 +344,32 @@ def test_step_padding_rows_sit_on_the_null_slot():
     np.testing.assert_array_equal(cs, cs2)
 
 
+def test_real_rows_never_write_the_null_slot():
+    """Slot 0 holds no row: the oracle refuses a real twin row whose write slot
+    is 0 (or its own read slot), and a standalone conv decode whose real row
+    would write slot 0, rather than putting a row's data into the null slot."""
+    case = gi.small(B=2, T=1, H_k=2, H_v=2, d=64, N=9)
+    pool, step = case.pools[0], case.steps[0][0]
+    for bad in (0, int(pool.read_slot[1])):
+        wr = pool.write_slot.copy()
+        wr[1] = bad
+        st, cs = pool.state.copy(), pool.conv_state.copy()
+        with pytest.raises(ValueError):
+            oracle.gdn_decode_step(step.x, pool.conv_w, None, cs, st, step.g, step.beta, pool.read_slot, wr, H_k=2)
+    # padding rows may name slot 0 as their write slot: that is how they sit on it
+    rd = pool.read_slot.copy()
+    wr = pool.write_slot.copy()
+    rd[1], wr[1] = 0, 0
+    st, cs = pool.state.copy(), pool.conv_state.copy()
+    oracle.gdn_decode_step(step.x, pool.conv_w, None, cs, st, step.g, step.beta, rd, wr, H_k=2)
+    np.testing.assert_array_equal(st[0], 0.0)
+    x2 = np.ascontiguousarray(step.x[:, 0])
+    wr = pool.write_slot.copy()
+    wr[0] = 0
+    with pytest.raises(ValueError):
+        oracle.conv_decode(x2, pool.conv_w, None, pool.conv_state.copy(), pool.read_slot, wr, act=True)
+
+
 def test_step_multi_token_in_place_equals_chained_single_tokens():
     """T tokens in one in-place call equal T single-token in-place calls; the state
     only differs by the fp32 rounding the chained calls take between tokens."""
