@@ -3,16 +3,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows B]
                     [--mode twin|inplace|tokens|prefill|stack|slotops] [--tokens T] [--prefill-len L]
                     [--layers L] [--commit fused|separate] [--hot] [--graph] [--no-cpu] [--no-calib]
+                    [--no-sweep]
 
 Workload: one 0.8B-like GDN layer -- B = 64 rows, 16 key and 16 value heads,
 d_k = d_v = 128 fp32 state (1 MiB a row), conv width 4 over 6144 channels with
 bf16 conv windows and activations, twin-slot writes.  A step is the whole path:
 conv + SiLU, L2 norm, gates, delta rule, read-out, the twin write, and the slot
-commit.  With --commit fused
-(default) the commit is folded into the step kernel, which writes the swapped
-slot pair into a second pair of slot arrays (the two pairs alternate); with
---commit separate it is its own kernel after the step.  Inputs are synthetic,
-seeded, and resident in HBM before the timed region.
+commit.  With --commit fused (default) the commit is folded into the step
+kernel, which writes the swapped slot pair into a second pair of slot arrays
+(the two pairs alternate); with --commit separate it is its own kernel after
+the step.  Inputs are synthetic, seeded, and resident in HBM before the timed
+region.
 
 Cold cache: MI355X's 256 MB Infinity Cache takes in the lines a step writes
 (streamed reads do not allocate there), so a slot read back within ~256 MB of
@@ -20,15 +21,33 @@ writes comes partly from that cache.  Consecutive steps rotate over enough
 disjoint row sets that at least 768 MiB of state is written between two visits
 of a set: 13 sets of 64 rows for twin writes, over a pool of 2049 slots (the
 drawn 513-slot pool, its 512 non-null slots replicated four times on the
-device).  --hot runs the same rows every step (reported as such).
+device), shared by every configuration the bench times.  --hot runs the same
+rows every step (reported as such).
 
 Timing: each timed loop is queued behind a GPU sleep long enough for the host
 to enqueue the whole loop, so the GPU runs the steps back to back and the
 Python launch cost never shows up as GPU idle time.  value = rows/s from the
 loop without per-kernel events; roofline = the step kernel's algorithmic bytes
 over its mean duration, from fence-free HIP events around every launch of a
-second identical loop.  Every mode adds cpu_baseline: the fp64 oracle timed
-on the host on a bounded sample of the same workload (--no-cpu skips it).
+second identical loop.
+
+Beside the headline the default run adds (each labelled in the JSON line):
+  calibration  the step's state traffic with no arithmetic in several workgroup
+               designs over the same row sets (gdn_traffic_probe): read only,
+               write only, copies in the step's own tile layout with one, two
+               or four tiles a workgroup, plain chunk copies, copies whose
+               stores are held until about the end of the read phase, and the
+               same bytes between consecutive slots;
+  roofline.ceiling  the best of those designs (GB/s), the step's time at that
+               rate, and the step's fraction of it -- the practical ceiling of
+               this traffic on this part, beside the 8 TB/s spec;
+  sweep        twin and in place at 1, 4, 16, 64 and 128 rows (cold), and the
+               64-row twin step hot;
+  floor        an empty kernel, a kernel doing one slot-index load then one tile
+               load, and the 1-row step: back to back, bracketed by events, and
+               replayed from a captured HIP graph;
+  cpu_baseline the fp64 oracle timed on the host on a bounded sample of the same
+               workload (--no-cpu skips it).
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
@@ -51,27 +70,96 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # HBM bytes per launch of the step kernel on the default workload, from the two
 # rocprofv3 counter passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE,
 # each scaled by what it reads for a copy of known size).  Only valid for the
-# kernel source the counters were taken on: reported as null otherwise.
-MEASURED_TRAFFIC = {"kernel_sources_sha256": "4863858c8d7ca2b7e1d24014f6a9a5fad8c1b7fed79cde630f4c85f422a2a03c",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_273_436}
-KERNEL_SOURCES = ("gdn_step_tile.hip", "step_common.h", "device_common.h", "gdn_internal.h")
+# machine code the counters were taken on: the gfx950 code of the kernels the
+# launch runs is hashed from the built library, and traffic is reported as null
+# when it differs.
+STEP_KERNELS_64_TWIN = ("_ZN3gdn20gdn_step_tile_kernelILi128ELi128ELi128ELb0ELi2EEEvNS_10StepParamsE",)
+MEASURED_TRAFFIC = {"kernel_code_sha256": "e488a944e461377fb1eff67610dc2a6da2ba88f440ae832bb592cf54e2b8c6f6",
+                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_336_568}
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
-# summary with its commands is in profiles/.  Valid only for these sources.
-MEASURED_PREFILL_TRAFFIC = {"kernel_sources_sha256": "622f3182d49fa21c025fdb89cbe4482853d89abcbc62bdc50e3394953b4d9495",
+# summary with its commands is in profiles/.  Valid only for this machine code.
+PREFILL_KERNELS = ("_ZN3gdn12_GLOBAL__N_119tp_chunk_map_kernelENS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_115tp_inter_kernelILi128ELi128ELi64EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_117tp_inter16_kernelILi128ELi128EEEvNS_13TwoPassParamsE")
+MEASURED_PREFILL_TRAFFIC = {"kernel_code_sha256": "f0947739f8a69197219350d1fd3a40ba7bda42d672fe28b610ab0dbf4e11cb59",
                             "bytes_per_call": {(16, 512): 754_928_363, (1, 4096): 364_499_998}}
-PREFILL_SOURCES = ("gdn_prefill_two_pass.hip", "prefill_internal.h", "step_common.h", "device_common.h",
-                   "gdn_internal.h")
 
 
-def kernel_sources_sha256(files=KERNEL_SOURCES) -> str:
+def _elf_sections(elf: bytes):
+    """(name, type, addr, offset, size, link) of every section of a 64-bit ELF."""
+    import struct
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+    raw = [struct.unpack_from("<IIQQQQIIQQ", elf, shoff + i * shentsize) for i in range(shnum)]
+    strtab_off = raw[shstrndx][4]
+    out = []
+    for (name, typ, _flags, addr, off, size, link, _info, _align, _entsize) in raw:
+        end = elf.index(b"\0", strtab_off + name)
+        out.append((elf[strtab_off + name:end].decode(), typ, addr, off, size, link))
+    return out
+
+
+def device_code_objects(lib_path: str, arch: str = "gfx950") -> list:
+    """The device code objects for `arch` in a HIP shared library's .hip_fatbin
+    section (one offload bundle per translation unit, each 4 KiB aligned)."""
+    import struct
+    data = open(lib_path, "rb").read()
+    sec = [x for x in _elf_sections(data) if x[0] == ".hip_fatbin"]
+    if not sec:
+        raise ValueError("no .hip_fatbin section")
+    fat = data[sec[0][3]:sec[0][3] + sec[0][4]]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out = []
+    start = fat.find(magic)
+    while start >= 0:
+        n, = struct.unpack_from("<Q", fat, start + 24)
+        pos = start + 32
+        for _ in range(n):
+            off, size, tlen = struct.unpack_from("<QQQ", fat, pos)
+            triple = fat[pos + 24:pos + 24 + tlen]
+            pos += 24 + tlen
+            if arch.encode() in triple and size > 0:
+                out.append(fat[start + off:start + off + size])
+        start = fat.find(magic, pos)
+    if not out:
+        raise ValueError(f"no {arch} code object in the library")
+    return out
+
+
+def kernel_code_sha256(symbols=STEP_KERNELS_64_TWIN, lib_path: str | None = None) -> str | None:
+    """SHA-256 over the machine code of the named kernels in the built library's
+    gfx950 code object (None if the library or a kernel is missing)."""
     import hashlib
+    import struct
+    if lib_path is None:
+        lib_path = os.path.join(ROOT, "gated_deltanet_recurrent_decode_amd", "libgdn.so")
+    try:
+        objs = device_code_objects(lib_path)
+    except (OSError, ValueError):
+        return None
+    found = {}
+    for co in objs:
+        secs = _elf_sections(co)
+        symtab = [x for x in secs if x[0] == ".symtab"]
+        if not symtab:
+            continue
+        _, _, _, st_off, st_size, link = symtab[0]
+        str_off = secs[link][3]
+        for i in range(st_size // 24):
+            name_o, info, other, shndx, value, size = struct.unpack_from("<IBBHQQ", co, st_off + 24 * i)
+            end = co.index(b"\0", str_off + name_o)
+            name = co[str_off + name_o:end].decode()
+            if name in symbols and size > 0 and shndx < len(secs):
+                _, _, addr, off, _, _ = secs[shndx]
+                found[name] = co[off + (value - addr):off + (value - addr) + size]
+    if set(found) != set(symbols):
+        return None
     h = hashlib.sha256()
-    base = os.path.join(ROOT, "gated_deltanet_recurrent_decode_amd", "csrc")
-    for f in files:
-        with open(os.path.join(base, f), "rb") as fh:
-            h.update(fh.read())
+    for name in symbols:
+        h.update(found[name])
     return h.hexdigest()
 
 
@@ -308,33 +396,29 @@ def cpu_baseline(args, seconds: float = 10.0) -> dict:
             "single_thread_rate": one, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
-class Bench:
-    def __init__(self, args):
+POOL_SLOTS = 1 + 4 * DRAWN_SLOTS   # the drawn pool's 512 slots, four times over, after the null slot
+
+
+class DevicePool:
+    """The drawn pool of the 0.8B-like layer (the null slot and 256 slot pairs)
+    with its 512 non-null slots replicated on the device to POOL_SLOTS slots
+    (2 GiB of state), shared by every decode configuration the bench times, so
+    each can rotate over disjoint row sets that are cold when visited."""
+
+    def __init__(self):
         import torch
 
         import gated_deltanet_recurrent_decode_amd as gdn
         import gdn_inputs as gi
 
-        self.torch, self.gdn = torch, gdn
+        self.torch, self.gdn, self.gi = torch, gdn, gi
         gdn.lib()
         torch.cuda.set_device(0)
-        self.args = args
-        self.twin = args.mode == "twin"
-        self.tokens_mode = args.mode == "tokens"
-        self.fused = self.twin and args.commit == "fused"
-        B = self.B = args.rows
-        T = self.T = args.tokens
-        # the first R rows are real; the rest of the bucket points at the null slot
-        R = self.R = B if args.real is None else args.real
-        # the drawn pool (the null slot and 256 slot pairs) and inputs for 256 rows
-        case = gi.qwen08b(B=256, T=T)
-        s, pool, step = case.shape, case.pools[0], case.steps[0][0]
-        self.shape = s
-        nsets, per = row_sets(args.mode, R, T, s.H_v * s.d_k * s.d_v * 4, args.hot)
-        spc = DRAWN_SLOTS // per                  # disjoint row sets one copy of the drawn pool holds
-        copies = -(-nsets // spc)
-        self.N = 1 + DRAWN_SLOTS * copies
-        # the drawn pool's 512 slots replicated `copies` times on the device after the null slot
+        case = gi.qwen08b(B=256, T=1)
+        s, pool = case.shape, case.pools[0]
+        self.shape, self.case = s, case
+        self.N = POOL_SLOTS
+        copies = (POOL_SLOTS - 1) // DRAWN_SLOTS
         state0 = torch.from_numpy(pool.state).cuda()
         cs0 = _bf(torch, pool.conv_state)
         self.state = torch.empty((self.N,) + tuple(state0.shape[1:]), dtype=state0.dtype, device="cuda")
@@ -345,14 +429,96 @@ class Bench:
             self.conv_state[1 + DRAWN_SLOTS * c:1 + DRAWN_SLOTS * (c + 1)] = cs0[1:]
         del state0, cs0
         self.conv_w = _bf(torch, pool.conv_w)
+        self.read_slot, self.write_slot = pool.read_slot, pool.write_slot
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+        self.timer = HipTimer()
+        self.cycles_per_ms = None
+
+    def inputs(self, T: int):
+        """x, g, beta for 256 rows of T tokens: the drawn ones for one token,
+        otherwise a seeded draw of the same distributions."""
+        if T == 1:
+            return self.case.steps[0][0]
+        s = self.shape
+        return self.gi.draw_step(np.random.Generator(np.random.PCG64(1000 + T)),
+                                 self.gi.Shape(B=256, T=T, H_k=s.H_k, H_v=s.H_v, d_k=s.d_k, d_v=s.d_v, W=s.W, N=s.N))
+
+    def sleep_for(self, ms: float):
+        """Queue a GPU spin of about `ms` milliseconds on the current stream."""
+        torch = self.torch
+        if self.cycles_per_ms is None:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            torch.cuda._sleep(2_000_000)
+            b.record()
+            torch.cuda.synchronize()
+            self.cycles_per_ms = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+        torch.cuda._sleep(int(ms * self.cycles_per_ms))
+
+    def time_launches(self, launch, K: int, per_launch_events: bool, host_ms_per_call: float | None = None):
+        """K calls of launch(i) queued behind a GPU spin (so they run back to back);
+        returns (ms per call from one event pair, per-call us from fence-free
+        events around each call or None)."""
+        torch, timer = self.torch, self.timer
+        sh = self.stream.cuda_stream
+        kev = [(timer.event(), timer.event()) for _ in range(K)] if per_launch_events else None
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # enough spin for the host to queue the whole loop (about 60 us a call from Python)
+        if host_ms_per_call is None:
+            host_ms_per_call = 0.12 if per_launch_events else 0.08
+        self.sleep_for(max(5.0, K * host_ms_per_call))
+        start.record()
+        for i in range(K):
+            if kev is not None:
+                timer.record(kev[i][0], sh)
+            launch(i)
+            if kev is not None:
+                timer.record(kev[i][1], sh)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / K
+        us = None
+        if kev is not None:
+            us = np.array([timer.elapsed_ms(a, b) for a, b in kev]) * 1e3
+            for a, b in kev:
+                timer.destroy(a)
+                timer.destroy(b)
+        return ms, us
+
+
+class Bench:
+    """One decode configuration over the shared pool: B rows (the first R real,
+    the rest on the null slot), T tokens a row, a write mode, rotating over
+    enough disjoint row sets to be cold (or the same rows every step when hot)."""
+
+    def __init__(self, dp: DevicePool, mode: str = "twin", B: int = 64, T: int = 1, real=None, hot: bool = False,
+                 commit: str = "fused"):
+        torch = dp.torch
+        self.dp, self.torch, self.gdn = dp, torch, dp.gdn
+        self.mode, self.hot = mode, hot
+        self.twin = mode == "twin"
+        self.tokens_mode = mode == "tokens"
+        self.fused = self.twin and commit == "fused"
+        self.B, self.T = B, T
+        R = self.R = B if real is None else real
+        s = self.shape = dp.shape
+        nsets, per = row_sets(mode, R, T, s.H_v * s.d_k * s.d_v * 4, hot)
+        spc = DRAWN_SLOTS // per                  # disjoint row sets one copy of the drawn pool holds
+        copies = -(-nsets // spc)
+        if 1 + DRAWN_SLOTS * copies > dp.N:
+            raise ValueError(f"{nsets} row sets of {per} slots do not fit the {dp.N}-slot pool")
+        self.N = dp.N
+        step = dp.inputs(T)
         perm = np.random.Generator(np.random.PCG64(1)).permutation(DRAWN_SLOTS).astype(np.int32) + 1
         slot_rows = []
         pad = np.zeros(B - R, np.int32)
         for k in range(nsets):
             j, off = k % spc, DRAWN_SLOTS * (k // spc)
             if self.twin:
-                slot_rows.append((np.concatenate([pool.read_slot[j * R:(j + 1) * R] + off, pad]),
-                                  np.concatenate([pool.write_slot[j * R:(j + 1) * R] + off, pad])))
+                slot_rows.append((np.concatenate([dp.read_slot[j * R:(j + 1) * R] + off, pad]),
+                                  np.concatenate([dp.write_slot[j * R:(j + 1) * R] + off, pad])))
             elif self.tokens_mode:
                 # B read slots and B*T token slots, all distinct
                 slot_rows.append((perm[j * per:j * per + B] + off, (perm[j * per + B:(j + 1) * per] + off).reshape(B, T)))
@@ -373,23 +539,20 @@ class Bench:
             st["parity"] = 0
             self.sets.append(st)
         torch.cuda.synchronize()
-        self.stream = torch.cuda.current_stream()
-        self.timer = HipTimer()
-        self.bytes = algorithmic_bytes(R, B - R, T, s.H_v, s.d_k, s.d_v, s.C, s.W, args.mode)
-        self.cycles_per_ms = None
+        self.bytes = algorithmic_bytes(R, B - R, T, s.H_v, s.d_k, s.d_v, s.C, s.W, mode)
 
     def launch(self, st):
-        g, s = self.gdn, self.shape
+        g, s, dp = self.gdn, self.shape, self.dp
         if self.fused:
             (rd, wr), (nrd, nwr) = st["pairs"][st["parity"]], st["pairs"][1 - st["parity"]]
-            g.gdn_decode_step_commit(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
+            g.gdn_decode_step_commit(st["x"], dp.conv_w, None, dp.conv_state, dp.state, st["g"], st["beta"],
                                      rd, wr, nrd, nwr, st["out"], H_k=s.H_k)
             st["parity"] ^= 1
         elif self.tokens_mode:
-            g.gdn_decode_step_tokens(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
+            g.gdn_decode_step_tokens(st["x"], dp.conv_w, None, dp.conv_state, dp.state, st["g"], st["beta"],
                                      st["rd"], st["wr"], st["out"], H_k=s.H_k)
         else:
-            g.gdn_decode_step(st["x"], self.conv_w, None, self.conv_state, self.state, st["g"], st["beta"],
+            g.gdn_decode_step(st["x"], dp.conv_w, None, dp.conv_state, dp.state, st["g"], st["beta"],
                               st["rd"], st["wr"] if self.twin else None, st["out"], H_k=s.H_k)
 
     def commit(self, st):
@@ -401,52 +564,38 @@ class Bench:
         self.launch(st)
         self.commit(st)
 
-    def _sleep_for(self, ms: float):
-        """Queue a GPU spin of about `ms` milliseconds on the current stream."""
-        torch = self.torch
-        if self.cycles_per_ms is None:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            torch.cuda._sleep(2_000_000)
-            b.record()
-            torch.cuda.synchronize()
-            self.cycles_per_ms = 2_000_000 / max(a.elapsed_time(b), 1e-3)
-        torch.cuda._sleep(int(ms * self.cycles_per_ms))
+    def warm(self, n: int):
+        for i in range(n):
+            self.step(i)
+        self.torch.cuda.synchronize()
 
     def timed(self, K: int, per_kernel_events: bool, graph=None):
-        """K steps queued behind a sleep; returns (ms per step, kernel durations in us or None)."""
-        torch, timer = self.torch, self.timer
-        sh = self.stream.cuda_stream
-        kev = [(timer.event(), timer.event()) for _ in range(K)] if per_kernel_events else None
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        # enough sleep for the host to queue the whole loop (about 60 us a step from Python)
-        self._sleep_for(max(5.0, K * (0.12 if per_kernel_events else 0.08)))
-        t_host = time.perf_counter()
-        start.record()
+        """K steps queued behind a spin; returns (ms per step, per-kernel us or None).
+        With per-kernel events only the step kernel is bracketed (a separate
+        commit kernel runs outside the events)."""
         if graph is not None:
-            for _ in range(K // graph[1]):
-                graph[0].replay()
-        else:
-            for i in range(K):
-                st = self.sets[i % self.nsets]
-                if kev is not None:
-                    timer.record(kev[i][0], sh)
-                self.launch(st)
-                if kev is not None:
-                    timer.record(kev[i][1], sh)
-                self.commit(st)
-        end.record()
-        host_ms = (time.perf_counter() - t_host) * 1e3
-        torch.cuda.synchronize()
-        total_ms = start.elapsed_time(end)
-        kus = None
-        if kev is not None:
-            kus = np.array([timer.elapsed_ms(a, b) for a, b in kev]) * 1e3
-            for a, b in kev:
-                timer.destroy(a)
-                timer.destroy(b)
-        return total_ms / K, kus, host_ms
+            reps = max(1, K // graph[1])
+            ms, _ = self.dp.time_launches(lambda i: graph[0].replay(), reps, False)
+            return ms / graph[1], None
+        if not per_kernel_events:
+            return self.dp.time_launches(self.step, K, False)
+        torch, timer = self.torch, self.dp.timer
+        sh = self.dp.stream.cuda_stream
+        kev = [(timer.event(), timer.event()) for _ in range(K)]
+
+        def one(i):
+            st = self.sets[i % self.nsets]
+            timer.record(kev[i][0], sh)
+            self.launch(st)
+            timer.record(kev[i][1], sh)
+            self.commit(st)
+
+        ms, _ = self.dp.time_launches(one, K, False, host_ms_per_call=0.14)
+        us = np.array([timer.elapsed_ms(a, b) for a, b in kev]) * 1e3
+        for a, b in kev:
+            timer.destroy(a)
+            timer.destroy(b)
+        return ms, us
 
     def capture(self):
         """One graph holding two steps of every row set (both parities of the
@@ -454,11 +603,11 @@ class Bench:
         torch = self.torch
         n = 2 * self.nsets
         side = torch.cuda.Stream()
-        side.wait_stream(self.stream)
+        side.wait_stream(self.dp.stream)
         with torch.cuda.stream(side):
             for i in range(n):
                 self.step(i)
-        self.stream.wait_stream(side)
+        self.dp.stream.wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -467,54 +616,145 @@ class Bench:
         torch.cuda.synchronize()
         return g, n
 
-    def calibration(self, reps: int = 64) -> dict:
-        """The step's state traffic with no arithmetic, same grid, slots and cache
-        policies (read only, write only, the twin copy, the in-place read and
-        write back), plus the twin copy's bytes as one contiguous copy -- the
-        plain-copy ceiling.  Twin visits swap the read and write slots of a row
-        set every time round, as the commit does, so nothing is re-read warm."""
-        torch, timer, gdn = self.torch, self.timer, self.gdn
-        sh = self.stream.cuda_stream
+    def calibration(self, laps: int = 10) -> dict:
+        """The step's state traffic with no arithmetic, in several workgroup
+        designs, over the same rotating row sets (the method of the PR #1139
+        page, 'Numbers', widened to a sweep of designs; see gdn_traffic_probe).
+        Twin visits swap a set's read and write slots every lap, as the commit
+        does, so nothing is re-read warm.  The contiguous designs move the same
+        bytes between consecutive slots (B read slots, then B write slots, a
+        disjoint range each visit).  The hold designs keep every workgroup's
+        stores until about the read phase's end (a fraction of the read bytes
+        over 6.7 TB/s), which puts the whole launch's reads ahead of its writes.
+        Returns {design: {us_mean, GBps, frac, bytes}}."""
+        torch, gdn, dp = self.torch, self.gdn, self.dp
         sink = torch.zeros(1, device="cuda")
         s = self.shape
-        cal = {}
-        modes = ((0, "read_only"), (1, "write_only"), (2, "copy_twin"), (3, "read_write_in_place"),
-                 (4, "contiguous_copy"))
-
-        # the contiguous copy rotates over disjoint ranges of 2B slots as well
+        tile_bytes = s.d_k * s.d_v * 4
+        read_bytes = self.R * s.H_v * tile_bytes
+        inplace = not self.twin
+        designs = [("read_only", "read", "slots", "tile1", 0.0), ("write_only", "write", "slots", "tile1", 0.0)]
+        traffic = "inplace" if inplace else "copy"
+        for shape in ("tile1", "tile2", "tile4", "chunk256x16", "chunk256x8", "chunk256x1", "chunk1024x1"):
+            designs.append((f"{traffic}_slots_{shape}", traffic, "slots", shape, 0.0))
+        for f in (0.9, 1.0, 1.1):
+            designs.append((f"{traffic}_slots_tile1_hold{f:.1f}", traffic, "slots", "tile1", f))
+        for shape in ("tile1", "chunk256x8", "chunk1024x1"):
+            designs.append((f"{traffic}_contiguous_{shape}", traffic, "contiguous", shape, 0.0))
+        # consecutive-slot ranges, disjoint for every set: [1 + 2Rk, 1 + 2Rk + R) and the next R slots
         ranges = [(torch.tensor([1 + 2 * self.R * k], dtype=torch.int32, device="cuda"),
                    torch.tensor([1 + 2 * self.R * k + self.R], dtype=torch.int32, device="cuda"))
-                  for k in range(self.nsets)]
-
-        def slots(mode, i):
-            st = self.sets[i % self.nsets]
-            rd, wr = (ranges[i % self.nsets] if mode == 4 else (st["rd"], st["wr"]))
-            if self.twin and (i // self.nsets) % 2:
-                return wr, rd
-            return rd, wr
-
-        for mode, name in modes:
-            if mode in (1, 2, 4) and not self.twin:
+                  for k in range(self.nsets) if 1 + 2 * self.R * (k + 1) <= dp.N]
+        out = {}
+        for name, tr, layout, shape, hold in designs:
+            if layout == "contiguous" and len(ranges) < min(self.nsets, 4):
                 continue
-            if mode == 3 and self.twin:
-                continue
-            for i in range(8):
-                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.R if mode == 4 else self.B)
+            nsets = self.nsets if layout == "slots" else len(ranges)
+            hold_ns = int(hold * read_bytes / 6.7e12 * 1e9)
+
+            def launch(i, tr=tr, layout=layout, shape=shape, hold_ns=hold_ns, nsets=nsets):
+                if layout == "slots":
+                    st = self.sets[i % nsets]
+                    rd, wr = st["rd"], st["wr"]
+                else:
+                    rd, wr = ranges[i % nsets]
+                if not inplace and (i // nsets) % 2:
+                    rd, wr = wr, rd
+                gdn.traffic_probe(dp.state, rd, wr, sink, traffic=tr, layout=layout, shape=shape, hold_ns=hold_ns,
+                                  rows=self.R if layout == "contiguous" else self.B)
+
+            reps = laps * nsets if nsets < 64 else 2 * nsets
+            for i in range(min(nsets, 16)):
+                launch(i)
             torch.cuda.synchronize()
-            evs = [(timer.event(), timer.event()) for _ in range(reps)]
-            self._sleep_for(5.0 + reps * 0.12)
-            for i in range(reps):
-                timer.record(evs[i][0], sh)
-                gdn.traffic_probe(mode, self.state, *slots(mode, i), sink, rows=self.R if mode == 4 else self.B)
-                timer.record(evs[i][1], sh)
-            torch.cuda.synchronize()
-            us = np.array([timer.elapsed_ms(a, b) for a, b in evs]) * 1e3
-            for a, b in evs:
-                timer.destroy(a)
-                timer.destroy(b)
-            nbytes = (1 if mode in (0, 1) else 2) * self.R * s.H_v * s.d_k * s.d_v * 4
-            cal[name] = {"us_mean": float(us.mean()), "GBps": nbytes / (us.mean() * 1e-6) / 1e9}
-        return cal
+            _, us = dp.time_launches(launch, reps, True)
+            nbytes = (1 if tr in ("read", "write") else 2) * read_bytes
+            m = float(us.mean())
+            out[name] = {"us_mean": m, "GBps": nbytes / (m * 1e-6) / 1e9,
+                         "frac": nbytes / (m * 1e-6) / 1e9 / PEAK_HBM_GBPS, "bytes": nbytes}
+        return out
+
+
+def ceiling_of(cal: dict, step_bytes: int, achieved_GBps: float) -> dict | None:
+    """The best no-math design of the calibration (the highest GB/s moving
+    the step's traffic: copies for twin writes, read-and-write-back in place),
+    and the best over the step's own slots; with the step's time at each rate."""
+    best = {}
+    for scope in ("any", "slots"):
+        cands = [(v["GBps"], k) for k, v in cal.items()
+                 if not k.startswith(("read_only", "write_only")) and (scope == "any" or "_slots_" in k)]
+        if not cands:
+            return None
+        g, k = max(cands)
+        best[scope] = {"design": k, "us_mean": cal[k]["us_mean"], "GBps": g, "frac": g / PEAK_HBM_GBPS,
+                       "us_at_step_bytes": step_bytes / (g * 1e9) * 1e6, "step_fraction": achieved_GBps / g}
+    out = dict(best["any"])
+    out["on_the_steps_slots"] = best["slots"]
+    out["note"] = ("best no-math copy design at the step's traffic (GB/s, so the step's own bytes can be priced at "
+                   "it); step_fraction = the step's achieved GB/s over the design's")
+    return out
+
+
+SWEEP = [(b, m) for b in (1, 4, 16, 64, 128) for m in ("twin", "inplace")]
+
+
+def run_sweep(dp: DevicePool, K: int = 130) -> dict:
+    """Twin and in-place steps at 1, 4, 16, 64 and 128 rows (cold row sets), plus
+    the 64-row twin step hot (the same rows every step, labelled as such)."""
+    out = {}
+    for B, mode in SWEEP + [(64, "twin-hot")]:
+        hot = mode.endswith("hot")
+        b = Bench(dp, mode="twin" if hot else mode, B=B, hot=hot)
+        b.warm(min(b.nsets, 20) + 4)
+        ms, _ = b.timed(max(K, 2 * min(b.nsets, 13)), False)
+        _, us = b.timed(K, True)
+        k = float(us.mean())
+        out[f"{B}_{mode}"] = {"rows": B, "write": "twin" if hot else mode, "cold": not hot,
+                              "us_per_step": ms * 1e3, "kernel_us_mean": k, "rows_per_s": B / (ms * 1e-3),
+                              "GBps": b.bytes / (k * 1e-6) / 1e9, "frac": b.bytes / (k * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                              "bytes": b.bytes}
+        del b
+    return out
+
+
+def run_floors(dp: DevicePool, K: int = 64) -> dict:
+    """The launch floor of small batches: an empty kernel and a kernel doing one
+    slot-index load then one tile load, back to back from the stream and from
+    a captured graph, beside the 1-row fused twin step the same two ways (the
+    PR #1139 page, 'Numbers', measured ~1.8 us a kernel inside a captured
+    graph on MI325X)."""
+    torch, gdn = dp.torch, dp.gdn
+    sink = torch.zeros(1, device="cuda")
+    rd = torch.tensor([int(dp.read_slot[0])], dtype=torch.int32, device="cuda")
+    out = {}
+    for shape in ("empty", "slot_load"):
+        def launch(i, shape=shape):
+            gdn.traffic_probe(dp.state, rd, None, sink, traffic="read", shape=shape, rows=1)
+        for i in range(8):
+            launch(i)
+        torch.cuda.synchronize()
+        ms, _ = dp.time_launches(launch, K, False)
+        _, us = dp.time_launches(launch, K, True)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                launch(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gms, _ = dp.time_launches(lambda i: g.replay(), 8, False)
+        out[shape] = {"us_back_to_back": ms * 1e3, "us_events_mean": float(us.mean()), "us_graph": gms * 1e3 / K}
+        del g
+    b = Bench(dp, mode="twin", B=1)
+    b.warm(24)
+    ms, _ = b.timed(max(K, 130), False)
+    _, us = b.timed(max(K, 130), True)
+    graph = b.capture()
+    graph[0].replay()
+    torch.cuda.synchronize()
+    gms, _ = b.timed(graph[1] * 2, False, graph=graph)
+    out["step_1_row_twin"] = {"us_back_to_back": ms * 1e3, "us_events_mean": float(us.mean()), "us_graph": gms * 1e3}
+    return out
 
 
 STACK_METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak), 24-layer 9B-like stack"
@@ -767,7 +1007,7 @@ def run_prefill(args) -> dict:
     achieved = flops / (k_us * 1e-6) / 1e12
     hbm = tokens * (s.C * 2 + s.H_v * s.d_v * 2 + 2 * s.H_v * 4) + nseq * 2 * (s.H_v * s.d_k * s.d_v * 4 + 3 * s.C * 2)
     traffic = None
-    if ws is not None and kernel_sources_sha256(PREFILL_SOURCES) == MEASURED_PREFILL_TRAFFIC["kernel_sources_sha256"]:
+    if ws is not None and kernel_code_sha256(PREFILL_KERNELS) == MEASURED_PREFILL_TRAFFIC["kernel_code_sha256"]:
         traffic = MEASURED_PREFILL_TRAFFIC["bytes_per_call"].get((nseq, L))
     return {
         "metric": PREFILL_METRIC, "value": tokens / (k_us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -815,6 +1055,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true", help="time steps replayed from a captured HIP graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-calib", action="store_true", help="skip the traffic calibration probes")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the row sweep (1-128 rows, twin and in place, and a hot 64-row step) and the "
+                         "launch-floor figures")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
 
@@ -858,15 +1101,14 @@ def main() -> int:
         print("bench.py: --tokens must be >= 1, and twin-slot writes take one token a row", file=sys.stderr)
         return 2
 
+    dp = DevicePool()
     try:
-        b = Bench(args)
+        b = Bench(dp, mode=args.mode, B=args.rows, T=args.tokens, real=args.real, hot=args.hot, commit=args.commit)
     except ValueError as e:
         print(f"bench.py: {e}", file=sys.stderr)
         return 2
     s = b.shape
-    for i in range(args.warmup):
-        b.step(i)
-    b.torch.cuda.synchronize()
+    b.warm(args.warmup)
 
     K = args.steps
     graph = None
@@ -876,8 +1118,8 @@ def main() -> int:
         for _ in range(2):
             graph[0].replay()
         b.torch.cuda.synchronize()
-    ms_per_step, _, host_ms = b.timed(K, per_kernel_events=False, graph=graph)
-    _, kus, _ = b.timed(K, per_kernel_events=True)
+    ms_per_step, _ = b.timed(K, per_kernel_events=False, graph=graph)
+    _, kus = b.timed(K, per_kernel_events=True)
 
     rows_per_s = b.R / (ms_per_step * 1e-3)
     twin = b.twin
@@ -912,13 +1154,13 @@ def main() -> int:
                    "write": args.mode, "commit": "fused" if b.fused else ("separate" if twin else "none"),
                    "row_sets": b.nsets, "graph": graph is not None},
         "step_GBps": b.bytes / (ms_per_step * 1e-3) / 1e9,
-        "host_enqueue_ms": host_ms,
     }
     k_us = float(kus.mean())
     achieved = b.bytes / (k_us * 1e-6) / 1e9
     traffic = None
     workload_key = (b.B, args.mode, "fused" if b.fused else "separate", bool(args.hot))
-    if (kernel_sources_sha256() == MEASURED_TRAFFIC["kernel_sources_sha256"]
+    if (MEASURED_TRAFFIC["kernel_code_sha256"] is not None
+            and kernel_code_sha256() == MEASURED_TRAFFIC["kernel_code_sha256"]
             and workload_key == MEASURED_TRAFFIC["workload"]):
         traffic = MEASURED_TRAFFIC["bytes_per_launch"]
     result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -930,8 +1172,16 @@ def main() -> int:
                           "kernel_us_p50": float(np.percentile(kus, 50)),
                           "kernel_us_p90": float(np.percentile(kus, 90)),
                           "bytes_per_launch": b.bytes}
-    if not args.no_calib and not b.tokens_mode:
-        result["calibration"] = b.calibration()
+    if not args.no_calib and not b.tokens_mode and b.T == 1:
+        cal = b.calibration()
+        result["calibration"] = cal
+        ceiling = ceiling_of(cal, b.bytes, achieved)
+        if ceiling is not None:
+            result["roofline"]["ceiling"] = ceiling
+    del b
+    if not args.no_sweep:
+        result["sweep"] = run_sweep(dp)
+        result["floor"] = run_floors(dp)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, args.cpu_seconds)
     print(json.dumps(result), flush=True)

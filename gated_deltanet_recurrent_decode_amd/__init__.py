@@ -41,6 +41,17 @@ class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "H_k", "H_v", "d_k", "d_v", "W", "N")]
 
 
+class Probe(ctypes.Structure):
+    """gdn_probe: a calibration design (see gdn_traffic_probe in include/gdn.h)."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("traffic", "layout", "shape", "hold_ns")]
+
+
+# gdn_probe fields, by name
+PROBE_TRAFFIC = {"read": 0, "write": 1, "copy": 2, "inplace": 3}
+PROBE_SHAPES = {"tile1": 0, "tile2": 1, "tile4": 2, "chunk256x16": 3, "chunk256x8": 4, "chunk256x1": 5,
+                "chunk1024x1": 6, "empty": 7, "slot_load": 8}
+
+
 _lib = None
 
 
@@ -83,7 +94,7 @@ def lib() -> ctypes.CDLL:
     L.gdn_slot_copy.restype = i32
     L.gdn_slot_copy.argtypes = [ctypes.POINTER(Dims), P, P, P, P, i32, P]
     L.gdn_traffic_probe.restype = i32
-    L.gdn_traffic_probe.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+    L.gdn_traffic_probe.argtypes = [ctypes.POINTER(Probe), i32, i32, i32, i32, i32, P, P, P, P, P]
     _lib = L
     return L
 
@@ -442,27 +453,36 @@ def slot_copy(state, conv_state, src_slots, dst_slots, *, H_k: int, stream=None)
                                                     _ptr(dst_slots), src_slots.numel(), _stream(stream, dev)))
 
 
-def traffic_probe(mode: int, state, read_slot, write_slot, sink, *, rows: int | None = None, stream=None) -> None:
-    """The step's state traffic with no arithmetic (see ``gdn_traffic_probe`` in include/gdn.h).
+def traffic_probe(state, read_slot, write_slot, sink, *, traffic: str = "copy", layout: str = "slots",
+                  shape: str = "tile1", hold_ns: int = 0, rows: int | None = None, stream=None) -> None:
+    """The step's state traffic with no arithmetic in one workgroup design (see
+    ``gdn_traffic_probe`` in include/gdn.h).
 
-    mode 0 read only, 1 write only, 2 copy (twin), 3 read + write back (in place),
-    4 the bytes of mode 2 as one contiguous copy of `rows` slots (default: the
-    length of read_slot) from slot read_slot[0] on to slot write_slot[0] on."""
+    traffic: "read", "write", "copy" (read slot -> write slot) or "inplace";
+    layout: "slots" (row r's tiles at read_slot[r] / write_slot[r]) or
+    "contiguous" (`rows` consecutive slots from read_slot[0] to write_slot[0]);
+    shape: one of PROBE_SHAPES; rows defaults to the length of read_slot."""
     torch = _torch()
     _contig(_dev(state, "state", torch.float32), "state")
     _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
     _contig(_dev(write_slot, "write_slot", torch.int32, allow_none=True), "write_slot")
     _contig(_dev(sink, "sink", torch.float32), "sink")
+    if traffic not in PROBE_TRAFFIC or layout not in ("slots", "contiguous") or shape not in PROBE_SHAPES:
+        raise ValueError(f"unknown probe design {traffic!r}, {layout!r}, {shape!r}")
     if state.dim() != 4 or read_slot.dim() != 1:
         raise ValueError("state must be [N][H][d_k][d_v] and read_slot [B]")
     N, H, d_k, d_v = state.shape
     n = read_slot.shape[0] if rows is None else int(rows)
-    if mode in (0, 1, 2, 3) and (n > read_slot.shape[0] or (write_slot is not None and write_slot.shape[0] < n)):
+    writes = traffic in ("write", "copy")
+    if writes and write_slot is None:
+        raise ValueError("write and copy traffic need write_slot")
+    if layout == "slots" and (n > read_slot.shape[0] or (writes and write_slot.shape[0] < n)):
         raise ValueError("the slot arrays must hold an entry for every row")
-    if mode == 4 and (read_slot.shape[0] < 1 or write_slot is None or write_slot.shape[0] < 1):
-        raise ValueError("the contiguous copy takes its first slots from read_slot[0] and write_slot[0]")
+    if layout == "contiguous" and (read_slot.shape[0] < 1 or (writes and write_slot.shape[0] < 1)):
+        raise ValueError("the contiguous layout takes its first slots from read_slot[0] and write_slot[0]")
+    pr = Probe(PROBE_TRAFFIC[traffic], 0 if layout == "slots" else 1, PROBE_SHAPES[shape], int(hold_ns))
     dev = _device(state, read_slot, write_slot, sink)
     with _on(dev):
         _check("gdn_traffic_probe", lib().gdn_traffic_probe(
-            int(mode), n, H, d_k, d_v, N, _ptr(state),
-            _ptr(read_slot), _ptr(write_slot), _ptr(sink), _stream(stream, dev)))
+            ctypes.byref(pr), n, H, d_k, d_v, N, _ptr(state), _ptr(read_slot), _ptr(write_slot), _ptr(sink),
+            _stream(stream, dev)))

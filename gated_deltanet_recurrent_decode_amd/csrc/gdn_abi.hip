@@ -347,33 +347,48 @@ gdn_status gdn_slot_copy(const gdn_dims *dims, float *state, gdn_bf16 *conv_stat
     return slot_ops_impl(dims, state, conv_state, src_slots, dst_slots, n, stream);
 }
 
-gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
-                             float *state, const int32_t *read_slot, const int32_t *write_slot,
-                             float *sink, hipStream_t stream)
+gdn_status gdn_traffic_probe(const gdn_probe *probe, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                             float *state, const int32_t *read_slot, const int32_t *write_slot, float *sink,
+                             hipStream_t stream)
 {
-    if (!state || !read_slot || !sink || ((mode == 1 || mode == 2 || mode == 4) && !write_slot))
+    if (!probe || !state || !read_slot || !sink)
         return GDN_ERR_NULL;
-    if (mode < 0 || mode > 4 || B < 0 || H < 1 || N < 1 || (int64_t)B * H > INT32_MAX)
+    const gdn_probe pr = *probe;
+    if (pr.traffic < 0 || pr.traffic > 3 || pr.layout < 0 || pr.layout > 1 || pr.shape < 0 || pr.shape > 8 ||
+        pr.hold_ns < 0 || pr.hold_ns > 1000000)
         return GDN_ERR_SHAPE;
-    // mode 4 addresses B whole slots with 32-bit byte offsets
-    if (mode == 4 && (int64_t)B * H * d_k * d_v * 4 > INT32_MAX)
+    const bool uses_write = pr.traffic == 1 || pr.traffic == 2;
+    if (uses_write && !write_slot)
+        return GDN_ERR_NULL;
+    if (B < 0 || H < 1 || N < 1 || (int64_t)B * H * 16 > INT32_MAX)
         return GDN_ERR_SHAPE;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v))
         return GDN_ERR_UNSUPPORTED;
+    if ((pr.shape == 1 || pr.shape == 2) && (d_k != 128 || d_v != 128))
+        return GDN_ERR_UNSUPPORTED;
+    const int64_t tile_bytes = (int64_t)d_k * d_v * 4;
+    static const int64_t chunk_bytes[4] = {256 * 16 * 16, 256 * 8 * 16, 256 * 16, 1024 * 16};
+    if (pr.shape >= 3 && pr.shape <= 6 && tile_bytes % chunk_bytes[pr.shape - 3] != 0)
+        return GDN_ERR_UNSUPPORTED;
+    if (pr.layout == 1 && (int64_t)B * H * tile_bytes > INT32_MAX)
+        return GDN_ERR_SHAPE;
     if (!aligned(state, 16))
         return GDN_ERR_UNSUPPORTED;
-    if (B == 0)
+    if (B == 0 && pr.shape != 7)
         return GDN_OK;
     gdn::ProbeParams p{};
     p.state = state;
     p.read_slot = read_slot;
-    p.write_slot = write_slot;
+    p.write_slot = uses_write ? write_slot : nullptr;
     p.sink = sink;
     p.one = 1.0f;
     p.B = B;
     p.H = H;
     p.N = N;
-    p.mode = mode;
+    p.traffic = pr.traffic;
+    p.layout = pr.layout;
+    p.shape = pr.shape;
+    p.hold_ticks = (uint32_t)(pr.hold_ns / 10); // the constant clock ticks at 100 MHz
     return from_hip(gdn::launch_traffic_probe(p, d_k, d_v, stream));
 }
 

@@ -48,10 +48,14 @@ struct ConvParams {
 struct ProbeParams {
     float *state;
     const int32_t *read_slot;
-    const int32_t *write_slot;
+    const int32_t *write_slot; // null for read-only and in-place traffic
     float *sink;
     float one; // 1.0f, opaque to the compiler so stores of loaded values stay
-    int B, H, N, mode;
+    int B, H, N;
+    int traffic;         // 0 read only, 1 write only, 2 copy, 3 read and write back in place
+    int layout;          // 0 the rows' slots, 1 consecutive slots from read_slot[0] / write_slot[0]
+    int shape;           // workgroup design (see gdn_probe in gdn.h)
+    uint32_t hold_ticks; // 0, or: stores wait until this many 100 MHz ticks after the workgroup started
 };
 
 // Zero (src == null) or copy (src[i] -> dst[i]) whole slots of the pool.

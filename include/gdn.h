@@ -290,26 +290,50 @@ const char *gdn_status_string(gdn_status status);
 
 /*
  * gdn_traffic_probe -- calibration: the state traffic of gdn_decode_step at
- * the same shapes, grid and access pattern, with no arithmetic (the method
- * of PR #1139, "Numbers": a kernel with the step's reads and writes and no
- * math, and its read-only and write-only halves).
- *   mode 0  read only: reads every real row's read-slot tiles
- *   mode 1  write only: writes every real row's write-slot tiles
- *   mode 2  copy: reads the read slot, writes the write slot (twin traffic)
- *   mode 3  in place: reads the read slot and writes it back
- *   mode 4  the bytes of mode 2 as one contiguous copy: the B slots from
- *           read_slot[0] on to the B slots from write_slot[0] on (the
- *           plain-copy ceiling).  A range outside [1, N) makes it a no-op;
- *           B slots must be under 2 GiB (else GDN_ERR_SHAPE); overlapping
- *           ranges race.
- * Loads and stores stream (nt), as the step's state accesses do.  state is
- * [N][H][d_k][d_v] fp32; rows with read slot 0 are skipped.  sink [1] fp32
- * receives nothing in practice; it only keeps the read-only mode's loads
- * alive.  d_k, d_v in {64, 128}.
+ * the same shapes and slots, with no arithmetic, in one of several workgroup
+ * designs (the method of PR #1139, "Numbers": a kernel with the step's reads
+ * and writes and no math, and its read-only and write-only halves, gives the
+ * practical ceiling of the step's traffic; several designs make that ceiling
+ * the best of them rather than one kernel's).
+ *
+ * B rows x H heads of d_k x d_v fp32 tiles in state [N][H][d_k][d_v]:
+ *   probe->traffic  0 read only (the read slots), 1 write only (the write
+ *                   slots), 2 copy (read slot -> write slot: twin traffic),
+ *                   3 read and write back (in-place traffic)
+ *   probe->layout   0 the rows' slots: read_slot[r], write_slot[r] (rows with
+ *                   a slot outside [1, N) move nothing);
+ *                   1 consecutive slots: B slots from read_slot[0] on, written
+ *                   to B slots from write_slot[0] on (the launch moves nothing
+ *                   unless both ranges lie in [1, N))
+ *   probe->shape    0, 1, 2: the fused step's thread layout (a wave holds the
+ *                   eight row groups of 32 columns, 2 d_v threads a tile), 1,
+ *                   2 or 4 whole tiles a workgroup (2 and 4: d_k = d_v = 128),
+ *                   stores after all of the workgroup's loads when more than
+ *                   one; 3, 4, 5, 6: plain chunks, one a workgroup, 256
+ *                   threads x 16, 8 or 1 and 1024 threads x 1 16-byte loads a
+ *                   lane (the tile must be a multiple of the chunk);
+ *                   7: an empty kernel (the launch floor);
+ *                   8: one workgroup loads read_slot[0], then 16 bytes a lane
+ *                   of that slot's first tile (the floor of a step's first
+ *                   dependent loads)
+ *   probe->hold_ns  0, or: every workgroup holds its stores until this long
+ *                   after it started (at most 1 ms), which puts the launch's
+ *                   reads ahead of its writes when long enough; for
+ *                   measurement only
+ * Loads and stores stream (nt), as the step's state accesses do.  sink [1]
+ * fp32 receives nothing in practice; it keeps read-only loads alive.
+ * write_slot is required for traffic 1 and 2, ignored otherwise.  Statuses:
+ * GDN_ERR_NULL, GDN_ERR_SHAPE (B < 0, H or N < 1, a value out of range, a
+ * contiguous range over 2 GiB), GDN_ERR_UNSUPPORTED (head dims not 64/128, a
+ * shape not built for them, misaligned state).
  */
-gdn_status gdn_traffic_probe(int32_t mode, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
-                             float *state, const int32_t *read_slot, const int32_t *write_slot,
-                             float *sink, hipStream_t stream);
+typedef struct gdn_probe {
+    int32_t traffic, layout, shape, hold_ns;
+} gdn_probe;
+
+gdn_status gdn_traffic_probe(const gdn_probe *probe, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                             float *state, const int32_t *read_slot, const int32_t *write_slot, float *sink,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

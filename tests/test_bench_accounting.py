@@ -64,3 +64,30 @@ def test_cold_rotation_row_sets():
     assert bench.row_sets("twin", 256, 1, 4 * MiB, hot=False) == (4, 512)
     assert bench.row_sets("tokens", 16, 4, MiB, hot=False) == (13, 80)
     assert bench.row_sets("twin", 64, 1, MiB, hot=True) == (1, 128)
+
+
+def test_kernel_code_hash_reads_the_built_library():
+    """The measured-traffic gate hashes the kernels' gfx950 machine code from the
+    built library: found for the kernels the bench times, different for
+    different kernels, None for a kernel that is not there."""
+    import os
+    if not os.path.exists(os.path.join(bench.ROOT, "gated_deltanet_recurrent_decode_amd", "libgdn.so")):
+        import pytest
+        pytest.skip("libgdn.so is not built")
+    a = bench.kernel_code_sha256(bench.STEP_KERNELS_64_TWIN)
+    b = bench.kernel_code_sha256(bench.PREFILL_KERNELS)
+    assert a is not None and b is not None and a != b
+    assert bench.kernel_code_sha256(("_ZN3gdn_no_such_kernel",)) is None
+    assert bench.kernel_code_sha256(bench.STEP_KERNELS_64_TWIN) == a  # deterministic
+
+
+def test_ceiling_is_the_fastest_copy_design():
+    cal = {"read_only": {"GBps": 7000.0, "us_mean": 9.0},
+           "copy_slots_tile1": {"GBps": 5000.0, "us_mean": 26.8},
+           "copy_slots_tile2": {"GBps": 5300.0, "us_mean": 25.3},
+           "copy_contiguous_chunk256x8": {"GBps": 5700.0, "us_mean": 23.5}}
+    c = bench.ceiling_of(cal, 140_000_000, 5200.0)
+    assert c["design"] == "copy_contiguous_chunk256x8"
+    assert c["on_the_steps_slots"]["design"] == "copy_slots_tile2"
+    assert abs(c["us_at_step_bytes"] - 140_000_000 / 5.7e12 * 1e6) < 1e-9
+    assert abs(c["step_fraction"] - 5200.0 / 5700.0) < 1e-12

@@ -708,31 +708,54 @@ def test_graph_replay_of_step_and_commit_matches_eager(gdn, torch):
 
 # ------------------------------------------------------------------ calibration probe
 
-def test_traffic_probe_moves_the_tiles(gdn, torch):
+@pytest.mark.parametrize("shape", ["tile1", "tile2", "tile4", "chunk256x16", "chunk256x8", "chunk256x1",
+                                   "chunk1024x1"])
+def test_traffic_probe_moves_the_tiles(gdn, torch, shape):
+    """Every calibration design moves exactly the step's tiles: a copy puts each
+    read tile in its write slot, write-only fills the write slots, read-only and
+    in-place traffic leave the pool as it was, and nothing else changes; the
+    contiguous layout copies consecutive slots and is a no-op past the pool."""
     t = torch
-    case = gi.small(B=4, T=1, H_k=2, H_v=2, d=128, N=11)
+    case = gi.small(B=5, T=1, H_k=2, H_v=2, d=128, N=15)
     pool = case.pools[0]
     dp = H.DevPool(pool)
     sink = t.zeros(1, device="cuda")
     rd = [int(x) for x in pool.read_slot]
     wr = [int(x) for x in pool.write_slot]
-    gdn.traffic_probe(2, dp.state, dp.rd, dp.wr, sink)           # copy
+    others = [sl for sl in range(15) if sl not in wr]
+    before = dp.state.clone()
+    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="copy", shape=shape)
     t.cuda.synchronize()
-    assert t.equal(dp.state[wr], dp.state[rd])
-    gdn.traffic_probe(1, dp.state, dp.rd, dp.wr, sink)           # write only
+    assert t.equal(dp.state[wr], before[rd])
+    assert t.equal(dp.state[others], before[others])
+    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="write", shape=shape, hold_ns=2000)
     t.cuda.synchronize()
     assert bool((dp.state[wr] == 1.0).all())
-    before = dp.state.clone()
-    gdn.traffic_probe(3, dp.state, dp.rd, None, sink)            # in place, values unchanged
-    gdn.traffic_probe(0, dp.state, dp.rd, None, sink)            # read only
+    assert t.equal(dp.state[others], before[others])
+    mid = dp.state.clone()
+    gdn.traffic_probe(dp.state, dp.rd, None, sink, traffic="inplace", shape=shape)
+    gdn.traffic_probe(dp.state, dp.rd, None, sink, traffic="read", shape=shape)
     t.cuda.synchronize()
-    assert t.equal(before, dp.state)
+    assert t.equal(mid, dp.state)
     assert float(sink[0]) == 0.0
-    base = t.tensor([2, 6], dtype=t.int32, device="cuda")
-    gdn.traffic_probe(4, dp.state, base[0:1], base[1:2], sink, rows=3)   # slots 2..4 -> 6..8, contiguous
+    base = t.tensor([2, 7], dtype=t.int32, device="cuda")
+    gdn.traffic_probe(dp.state, base[0:1], base[1:2], sink, traffic="copy", layout="contiguous", shape=shape,
+                      rows=3)   # slots 2..4 -> 7..9
     t.cuda.synchronize()
-    assert t.equal(dp.state[6:9], before[2:5])
-    assert t.equal(dp.state[:6], before[:6]) and t.equal(dp.state[9:], before[9:])
-    gdn.traffic_probe(4, dp.state, base[1:2], base[0:1], sink, rows=6)   # 6..11 runs past N = 11: no-op
+    assert t.equal(dp.state[7:10], mid[2:5])
+    assert t.equal(dp.state[:7], mid[:7]) and t.equal(dp.state[10:], mid[10:])
+    gdn.traffic_probe(dp.state, base[1:2], base[0:1], sink, traffic="copy", layout="contiguous", shape=shape,
+                      rows=9)   # 7..15 runs past N = 15: no-op
     t.cuda.synchronize()
-    assert t.equal(dp.state[:6], before[:6])
+    assert t.equal(dp.state[:7], mid[:7])
+
+
+def test_launch_floor_probes_run(gdn, torch):
+    t = torch
+    state = t.zeros((3, 2, 128, 128), device="cuda")
+    rd = t.tensor([1], dtype=t.int32, device="cuda")
+    sink = t.zeros(1, device="cuda")
+    gdn.traffic_probe(state, rd, None, sink, traffic="read", shape="empty")
+    gdn.traffic_probe(state, rd, None, sink, traffic="read", shape="slot_load")
+    t.cuda.synchronize()
+    assert float(sink[0]) == 0.0
