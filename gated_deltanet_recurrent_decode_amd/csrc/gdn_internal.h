@@ -50,7 +50,7 @@ struct ProbeParams {
     const int32_t *read_slot;
     const int32_t *write_slot; // null for read-only and in-place traffic
     float *sink;
-    float one; // 1.0f, opaque to the compiler so stores of loaded values stay
+    float one; // 1.0f, opaque to the compiler (a never-true test on it keeps read-only loads alive)
     int B, H, N;
     int traffic;         // 0 read only, 1 write only, 2 copy, 3 read and write back in place
     int layout;          // 0 the rows' slots, 1 consecutive slots from read_slot[0] / write_slot[0]

@@ -137,12 +137,12 @@ __global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
         __builtin_amdgcn_s_barrier();
     }
     probe_hold(t0, p.hold_ticks);
+    // stores straight from the registers the loads filled: staging the data
+    // through other registers made the compiler write a staging register
+    // right behind a 16-byte store that had not read it yet (seen on MI355X)
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        u32x4 v = s[m];
-        v.x = __float_as_uint(__uint_as_float(v.x) * p.one);
-        __builtin_amdgcn_raw_buffer_store_b128(v, wr, voff, m * RG * DV * 4, kProbeStore);
-    }
+    for (int m = 0; m < RPT; ++m)
+        __builtin_amdgcn_raw_buffer_store_b128(s[m], wr, voff, m * RG * DV * 4, kProbeStore);
 }
 
 // Chunk designs: workgroup c moves chunk c of NTH * L * 16 bytes, thread i
@@ -186,11 +186,8 @@ __global__ __launch_bounds__(NTH) void probe_chunk_kernel(ProbeParams p, uint32_
     }
     probe_hold(t0, p.hold_ticks);
 #pragma unroll
-    for (int m = 0; m < L; ++m) {
-        u32x4 w = v[m];
-        w.x = __float_as_uint(__uint_as_float(w.x) * p.one);
-        __builtin_amdgcn_raw_buffer_store_b128(w, wr, vo, m * NTH * 16, kProbeStore);
-    }
+    for (int m = 0; m < L; ++m)
+        __builtin_amdgcn_raw_buffer_store_b128(v[m], wr, vo, m * NTH * 16, kProbeStore);
 }
 
 // The launch floor: a kernel that does nothing.

@@ -1,0 +1,108 @@
+"""The built library's gfx950 machine code, checked for one hazard: a vector
+instruction that writes a register holding the data of a 16- or 12-byte store
+issued by the instruction right before it.
+
+A store with more than 8 bytes of data reads part of its data registers one
+cycle late, so a vector write to them must wait at least one instruction.  The
+compiler inserts that wait for most stores but not for buffer stores whose
+offset sits in a scalar register, and on MI355X that case is real: a copy
+kernel whose stores were staged through shared registers (a 64-bit register
+move straight behind each buffer store) wrote, now and then, the next row's
+values into half of a 16-byte store.  This test disassembles every kernel of
+libgdn.so (llvm-objdump on the code objects of the offload bundle) and fails
+on any vector write to a wide store's data registers by the next instruction,
+so a recompile cannot bring the pattern back unnoticed.  Loads (LDS included)
+into those registers are not counted: their data arrives long after the store
+has read its registers.
+"""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import bench
+
+LIB = os.path.join(bench.ROOT, "gated_deltanet_recurrent_decode_amd", "libgdn.so")
+OBJDUMP = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "llvm-objdump")
+
+STORE = re.compile(r"^\s*(buffer_store_dwordx[34]|global_store_dwordx[34]|flat_store_dwordx[34]|"
+                   r"scratch_store_dwordx[34])\s+(.*)$")
+VREG = re.compile(r"v\[(\d+):(\d+)\]|v(\d+)")
+
+
+def _regs(tok):
+    m = VREG.fullmatch(tok.strip())
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
+def _store_data(op, args):
+    ops = [a.strip() for a in args.split(",")]
+    # buffer stores: data first; global / flat / scratch stores: address, then data
+    return _regs(ops[0]) if op.startswith("buffer") else (_regs(ops[1]) if len(ops) > 1 else set())
+
+
+def _written(line):
+    m = re.match(r"^\s*([a-z_0-9]+)\s+(.*)$", line)
+    if not m:
+        return "", set()
+    op, args = m.group(1), m.group(2)
+    if op.startswith(("s_", "buffer_store", "global_store", "flat_store", "scratch_store", "ds_", "buffer_load",
+                      "global_load", "flat_load", "scratch_load", "exp")):
+        return op, set()
+    return op, _regs(args.split(",")[0])
+
+
+def _disassembly():
+    if not os.path.exists(LIB):
+        pytest.skip("libgdn.so is not built")
+    if not os.path.exists(OBJDUMP):
+        pytest.skip("llvm-objdump is not available")
+    out = []
+    with tempfile.TemporaryDirectory() as d:
+        for i, co in enumerate(bench.device_code_objects(LIB)):
+            path = os.path.join(d, f"co{i}.elf")
+            with open(path, "wb") as f:
+                f.write(co)
+            r = subprocess.run([OBJDUMP, "-d", "--no-show-raw-insn", path], capture_output=True, text=True,
+                               check=True)
+            out.append(r.stdout)
+    return "\n".join(out)
+
+
+def test_no_write_into_store_data_right_behind_a_wide_store():
+    text = _disassembly()
+    func = None
+    bad = []
+    insts = []
+    for line in text.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+        if m:
+            func = m.group(1)
+            continue
+        s = line.split("//")[0].strip()
+        if not s or s.endswith(":"):
+            continue
+        insts.append((func, s))
+    n = len(insts)
+    stores = 0
+    for i, (f, s) in enumerate(insts):
+        m = STORE.match(s)
+        if not m:
+            continue
+        stores += 1
+        data = _store_data(m.group(1), m.group(2))
+        for j in range(i + 1, min(n, i + 2)):
+            if insts[j][0] != f:
+                break
+            op, w = _written(insts[j][1])
+            if w & data:
+                bad.append(f"{f}: '{s}' then '{insts[j][1]}' ({j - i} later)")
+                break
+    assert stores > 100, "expected the library's wide stores in the disassembly"
+    assert not bad, "store data overwritten right behind the store:\n" + "\n".join(bad[:20])
