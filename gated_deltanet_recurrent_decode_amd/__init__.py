@@ -14,19 +14,22 @@ import ctypes
 import os
 
 __all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill",
-           "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "conv_decode",
+           "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "gdn_prefill_two_pass_noalloc",
+           "NOALLOC_SCRATCH_BYTES", "conv_decode",
            "slot_commit",
            "slot_reset", "slot_copy", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill",
-           "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "conv_decode",
+           "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "gdn_prefill_two_pass_noalloc",
+           "conv_decode",
            "slot_commit",
            "gdn_slot_reset",
            "gdn_slot_copy", "gdn_status_string", "gdn_traffic_probe")
 
 GDN_OK = 0
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES in include/gdn.h
 
 
 class GdnError(RuntimeError):
@@ -81,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_two_pass.restype = i32
     L.gdn_prefill_two_pass.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P,
                                        ctypes.c_size_t, P]
+    L.gdn_prefill_two_pass_noalloc.restype = i32
+    L.gdn_prefill_two_pass_noalloc.argtypes = [ctypes.POINTER(Dims), P, i64, P, P, P, P, P, P, P, P, P, f32, f32, P]
     L.gdn_prefill_two_pass_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_prefill_two_pass_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.conv_decode.restype = i32
@@ -351,6 +356,20 @@ def gdn_prefill_two_pass(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqle
             ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
             _ptr(state), _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps), _ptr(workspace),
             workspace.numel(), _stream(stream, dev)))
+
+
+def gdn_prefill_two_pass_noalloc(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, *,
+                                 H_k: int, q_scale: float = 1.0, l2_eps: float = 1e-6, stream=None) -> None:
+    """gdn_prefill_two_pass with its scratch in the library's static device buffer
+    (NOALLOC_SCRATCH_BYTES a GPU) instead of a caller workspace: nothing is
+    allocated.  Calls that overlap on one GPU race; see include/gdn.h."""
+    d, xs = _prefill_dims(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out, H_k)
+    dev = _device(x, conv_w, conv_b, conv_state, state, g, beta, cu_seqlens, slot, out)
+    with _on(dev):
+        _check("gdn_prefill_two_pass_noalloc", lib().gdn_prefill_two_pass_noalloc(
+            ctypes.byref(d), _ptr(x), xs, _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+            _ptr(state), _ptr(g), _ptr(beta), _ptr(slot), _ptr(out), float(q_scale), float(l2_eps),
+            _stream(stream, dev)))
 
 
 def _conv_layout(x, conv_w, conv_b, conv_state, read_slot, write_slot, out):

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 #include "gdn_internal.h"
 #include "prefill_internal.h"
@@ -29,6 +31,7 @@ extern "C" const char *gdn_status_string(gdn_status status)
     case GDN_ERR_UNSUPPORTED: return "sizes or alignment outside what the kernels are built for";
     case GDN_ERR_REFUSED: return "refused: a twin-slot write takes one token a row (multi-token walks stay in place)";
     case GDN_ERR_HIP: return "the HIP launch failed";
+    case GDN_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
     }
     return "unknown gdn_status";
 }
@@ -256,6 +259,68 @@ gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t
     tp.p = p;
     if (workspace_bytes < gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, workspace, &tp.ws))
         return GDN_ERR_SHAPE;
+    return from_hip(gdn::launch_gdn_prefill_two_pass(tp, dims->d_k, dims->d_v, stream));
+}
+
+} // extern "C"
+
+// Scratch of gdn_prefill_two_pass_noalloc: a file-scope device array, one copy
+// on every GPU the library is loaded on, kept until the process ends.  Host
+// code must not pass the array's name to a kernel (on the host it stands for
+// a host-side stub, not a device address); the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static constexpr size_t kScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (resolved on the first call on each
+// device; a race between two first calls resolves the same address twice).
+gdn_status scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GDN_ERR_HIP;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return GDN_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_two_pass_noalloc(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                        const int32_t *cu_seqlens, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
+                                        gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
+                                        const int32_t *slot, gdn_bf16 *out, float q_scale, float l2_eps,
+                                        hipStream_t stream)
+{
+    gdn::PrefillParams p;
+    bool run;
+    const gdn_status st = prefill_setup(dims, x, x_row_stride, cu_seqlens, conv_w, conv_b, conv_state, state, g,
+                                        beta, slot, out, q_scale, l2_eps, p, &run);
+    if (st != GDN_OK || !run)
+        return st;
+    if ((long long)p.total / 32 + p.B + 1 > INT32_MAX)
+        return GDN_ERR_SHAPE;
+    if (gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, nullptr, nullptr) > kScratchBytes)
+        return GDN_ERR_SCRATCH;
+    void *ws = nullptr;
+    const gdn_status sst = scratch_for_current_device(&ws);
+    if (sst != GDN_OK)
+        return sst;
+    gdn::TwoPassParams tp{};
+    tp.p = p;
+    gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, ws, &tp.ws);
     return from_hip(gdn::launch_gdn_prefill_two_pass(tp, dims->d_k, dims->d_v, stream));
 }
 

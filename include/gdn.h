@@ -57,7 +57,8 @@ typedef enum gdn_status {
     GDN_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes or strides */
     GDN_ERR_UNSUPPORTED = 3, /* sizes outside what the kernels are built for */
     GDN_ERR_REFUSED = 4,     /* a twin-slot write with more than one token a row */
-    GDN_ERR_HIP = 5          /* the HIP launch returned an error */
+    GDN_ERR_HIP = 5,         /* the HIP launch returned an error */
+    GDN_ERR_SCRATCH = 6      /* gdn_prefill_two_pass_noalloc: more scratch than its static buffer */
 } gdn_status;
 
 /* Sizes of one decode step.
@@ -215,6 +216,33 @@ gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t
                                 gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
                                 const int32_t *slot, gdn_bf16 *out, float q_scale, float l2_eps, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_prefill_two_pass_noalloc -- gdn_prefill_two_pass with no workspace
+ * argument and no allocation at all, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same computation, kernels and results as
+ * gdn_prefill_two_pass, bit for bit.
+ *
+ * Its scratch is a static device buffer of GDN_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * inside the library: every GPU the library is loaded on holds one copy until
+ * the process ends, and the address of the current device's copy is looked up
+ * on the first call on that device.  A call whose workspace
+ * (gdn_prefill_two_pass_workspace_bytes of the same dims) exceeds it returns
+ * GDN_ERR_SCRATCH and enqueues nothing: at 16 value heads of 128 x 128 that
+ * is 1,888 tokens for one prompt, 32 fewer for each further prompt.  Every
+ * call on a GPU shares that GPU's buffer, so calls that overlap on one GPU
+ * (on different streams, or from different threads without stream order
+ * between them) race; calls ordered on one stream do not.  The buffer's
+ * contents on entry do not matter.  Other statuses as gdn_prefill_two_pass
+ * (GDN_ERR_HIP also if the buffer's address cannot be had).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_two_pass_noalloc(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
+                                        const int32_t *cu_seqlens, const gdn_bf16 *conv_w, const gdn_bf16 *conv_b,
+                                        gdn_bf16 *conv_state, float *state, const float *g, const float *beta,
+                                        const int32_t *slot, gdn_bf16 *out, float q_scale, float l2_eps,
+                                        hipStream_t stream);
 
 /*
  * gdn_prefill_two_pass_workspace_bytes -- the workspace gdn_prefill_two_pass

@@ -15,7 +15,7 @@ import gated_deltanet_recurrent_decode_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
-OK, NULL, SHAPE, UNSUPPORTED, REFUSED, HIP = range(6)
+OK, NULL, SHAPE, UNSUPPORTED, REFUSED, HIP, SCRATCH = range(7)
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
 
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert gdn.status_string(s)
     assert gdn.status_string(0) == "ok"
     assert "unknown" in gdn.status_string(99)
@@ -228,3 +228,23 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib", None)
     with pytest.raises(ImportError):
         gdn.lib()
+
+
+def test_prefill_noalloc_validation():
+    """The allocation-free prefill refuses, before touching the GPU, a call
+    whose workspace would not fit its static scratch, and validates like the
+    two-pass prefill otherwise."""
+    f = gdn.lib().gdn_prefill_two_pass_noalloc
+
+    def call(d, x=FAKE):
+        C = 2 * d.H_k * d.d_k + d.H_v * d.d_v
+        return f(ctypes.byref(d), x, C, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1e-6, None)
+    big = gdn.Dims(1, 4096, 16, 16, 128, 128, 4, 9)
+    need = gdn.gdn_prefill_two_pass_workspace_bytes(1, 4096, 16, 16, 128, 128)
+    assert need > gdn.NOALLOC_SCRATCH_BYTES
+    assert call(big) == SCRATCH
+    assert call(gdn.Dims(1, 64, 16, 16, 128, 128, 4, 9), x=None) == NULL
+    assert call(gdn.Dims(1, 64, 16, 16, 96, 128, 4, 9)) == UNSUPPORTED
+    empty = gdn.Dims(0, 0, 16, 16, 128, 128, 4, 9)
+    assert f(ctypes.byref(empty), None, 0, None, None, None, None, None, None, None, None, None, 1.0, 1e-6,
+             None) == OK
