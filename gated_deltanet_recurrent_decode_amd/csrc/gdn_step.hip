@@ -12,8 +12,9 @@
 //   3. L2-normalises q and k (wave butterflies over LDS, done redundantly by
 //      every wave so no extra barrier is needed);
 //   4. per head: one pass over the register-resident state gives both
-//      a = S^T k^ and b = S^T q^ (in-thread over its rows, butterfly across
-//      the row groups of a wave, LDS across waves, all in a fixed order);
+//      a = S^T k^ and b = S^T q^ (in-thread over its rows, then butterflies
+//      across the eight row groups, which sit in lane bits 3-5 of one wave, so
+//      the sum ends inside the wave in a fixed order);
 //      u = beta (v - alpha a); S' = alpha S + k^ u^T; o = alpha b + u (k^.q^),
 //      which equals S'^T q^;
 //   5. after the last token, stores the state and the advanced window back to
@@ -42,15 +43,14 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     constexpr int DVS = DV; // whole tiles
     using Cfg = StepCfg<DK, DVS, HPW>;
     static_assert(Cfg::NT == 2 * DVS * HPW, "launch bound must match the layout");
-    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NWH = Cfg::NWH;
+    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, RG = Cfg::RG, RPT = Cfg::RPT;
     constexpr int NCH = Cfg::NCH;
 
-    // conv outputs (+ a padding slot for spare conv lanes) and the cross-wave
-    // partial sums, one of each for even and one for odd tokens: token t
-    // writes the set that token t - 2 read, and every wave has passed token
-    // t - 1's barriers, so it is done with token t - 2, before it gets there
+    // conv outputs (+ a padding slot for spare conv lanes), one set for even
+    // and one for odd tokens: token t writes the set that token t - 2 read,
+    // and a wave gets there only after every wave has passed token t - 1's
+    // barrier, which waits for its LDS reads of token t - 2 to complete
     __shared__ float y_buf[2][NCH + 4];
-    __shared__ float4 red_buf[2][HPW][NWH][2][CG];
 
     const int tid = threadIdx.x;
     // head of the group this thread updates; NTH is a multiple of the wave size,
@@ -58,10 +58,11 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     // it would be compiled as a loop over lanes
     const int hloc = __builtin_amdgcn_readfirstlane(tid / NTH);
     const int ht = tid - hloc * NTH; // thread index inside its head slice
-    const int cg = ht % CG;
-    const int rg = ht / CG;
-    const int wv = ht >> 6;
     const int lane = tid & 63;
+    // each wave holds 32 columns (eight column groups in lane bits 0-2) of
+    // all eight row groups (lane bits 3-5)
+    const int cg = (ht >> 6) * 8 + (lane & 7);
+    const int rg = lane >> 3;
 
     // workgroup -> (row, key head); its value heads are hk*G .. hk*G + G-1
     const int hk = blockIdx.x % p.H_k;
@@ -164,7 +165,6 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     float g_n = 0.f, b_n = 0.f;
     for (int t = 0; t < T; ++t) {
         float *y_lds = y_buf[t & 1];
-        float4(*red_lds)[NWH][2][CG] = red_buf[t & 1];
         if (t > 0) {
 #pragma unroll
             for (int k = 0; k < NCQ; ++k)
@@ -240,36 +240,17 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
             pb.z = fmaf(s[m].z, qh, pb.z);
             pb.w = fmaf(s[m].w, qh, pb.w);
         }
-        pa.x = xor_sum<CG>(pa.x);
-        pa.y = xor_sum<CG>(pa.y);
-        pa.z = xor_sum<CG>(pa.z);
-        pa.w = xor_sum<CG>(pa.w);
-        pb.x = xor_sum<CG>(pb.x);
-        pb.y = xor_sum<CG>(pb.y);
-        pb.z = xor_sum<CG>(pb.z);
-        pb.w = xor_sum<CG>(pb.w);
-        if (lane < CG) {
-            red_lds[hloc][wv][0][cg] = pa;
-            red_lds[hloc][wv][1][cg] = pb;
-        }
-        lds_barrier();
-        // the higher row-group bits live in the wave index: finish the same
-        // pairwise tree across the waves of this head slice
-        float4 av[NWH], bv[NWH];
-#pragma unroll
-        for (int w = 0; w < NWH; ++w) {
-            av[w] = red_lds[hloc][w][0][cg];
-            bv[w] = red_lds[hloc][w][1][cg];
-        }
-#pragma unroll
-        for (int st = 1; st < NWH; st *= 2) {
-#pragma unroll
-            for (int w = 0; w + st < NWH; w += 2 * st) {
-                av[w].x += av[w + st].x; av[w].y += av[w + st].y; av[w].z += av[w + st].z; av[w].w += av[w + st].w;
-                bv[w].x += bv[w + st].x; bv[w].y += bv[w + st].y; bv[w].z += bv[w + st].z; bv[w].w += bv[w + st].w;
-            }
-        }
-        const float4 a = av[0], b = bv[0];
+        // butterflies over lane bits 3, 4, 5 form the pairwise tree
+        // ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over the row groups in every lane
+        pa.x = xor_sum<8>(pa.x);
+        pa.y = xor_sum<8>(pa.y);
+        pa.z = xor_sum<8>(pa.z);
+        pa.w = xor_sum<8>(pa.w);
+        pb.x = xor_sum<8>(pb.x);
+        pb.y = xor_sum<8>(pb.y);
+        pb.z = xor_sum<8>(pb.z);
+        pb.w = xor_sum<8>(pb.w);
+        const float4 a = pa, b = pb;
 
         // ---- delta update in registers, and the read-out
         const float *vv = &y_lds[2 * DK + hloc * DVS + 4 * cg];

@@ -14,21 +14,19 @@ namespace gdn {
 // column split and head grouping: in-thread over m, then the pairwise tree
 // ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over row groups -- so twin and
 // in-place launches, and padded and unpadded buckets, give identical bits.
-// The single-token tile kernel keeps the row groups in lane bits 3-5 (a wave
-// holds 32 columns and the tree ends inside it); the token walk keeps them in
-// lane bit 5 and the wave index (the tree ends in LDS).  Both form this tree.
+// Both step kernels keep the row groups in lane bits 3-5 (a wave holds 32
+// columns of all eight row groups), so the tree ends inside the wave.
 template <int DK, int DVS, int HPW>
 struct StepCfg {
     static constexpr int RG = 8;                   // row groups
     static constexpr int CG = DVS / 4;             // float4 column groups in a head slice
     static constexpr int NTH = RG * CG;            // threads per head slice
     static constexpr int RPT = DK / RG;            // state rows held by each thread
-    static constexpr int NWH = NTH / 64;           // waves per head slice
     static constexpr int NT = NTH * HPW;           // threads per workgroup
     static constexpr int NCH = 2 * DK + HPW * DVS; // conv channels the workgroup needs
     static_assert(CG >= 8 && CG <= 64 && 64 % CG == 0, "a wave must hold whole row groups");
     static_assert(DK % RG == 0, "rows must tile the row groups");
-    static_assert(NWH == 1 || NWH == 2 || NWH == 4, "pairwise tree over at most four waves");
+    static_assert(NTH % 64 == 0, "a head slice is whole waves of eight column groups");
     static_assert(NT <= 1024, "workgroup too large");
 };
 
