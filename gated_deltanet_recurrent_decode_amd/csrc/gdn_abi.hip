@@ -60,6 +60,13 @@ gdn_status step_impl(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stri
         return GDN_ERR_SHAPE;
     if ((int64_t)d.B * d.H_v * 4 > INT32_MAX) // workgroups in the grid
         return GDN_ERR_SHAPE;
+    // the kernels address a row's x (with up to eight tokens of overrun past
+    // the last, which read as zero), its outputs and its gates, and the conv
+    // weights, through 32-bit byte offsets under 2 GiB
+    const int64_t lim = (int64_t)1 << 31;
+    if ((d.T + 8LL) * C * 2 >= lim || 8LL * C >= lim || (int64_t)d.T * d.H_v * d.d_v * 2 >= lim ||
+        (int64_t)d.T * d.H_v * 4 >= lim)
+        return GDN_ERR_SHAPE;
     if (!(l2_eps >= 0.0f) || !isfinite(l2_eps) || !isfinite(q_scale))
         return GDN_ERR_SHAPE;
     const int G = d.H_v / d.H_k;

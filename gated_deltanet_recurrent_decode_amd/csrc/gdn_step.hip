@@ -2,31 +2,37 @@
 // (keep_in_place), T tokens a row.
 //
 // One workgroup owns a key head of a row with all G of its value heads, so no
-// other workgroup reads a conv window it overwrites.  Per workgroup it:
-//   1. issues the loads of its G fp32 state tiles (d_k x d_v each, 16-byte
-//      loads, each wave instruction covering whole 128-byte lines), so HBM
-//      streams while the rest of the prologue runs;
-//   2. per token: runs the conv decode + SiLU of its channels (q and k of the
-//      key head, v of its value heads) into LDS, the window advancing in
-//      registers;
-//   3. L2-normalises q and k (wave butterflies over LDS, done redundantly by
-//      every wave so no extra barrier is needed);
-//   4. per head: one pass over the register-resident state gives both
-//      a = S^T k^ and b = S^T q^ (in-thread over its rows, then butterflies
-//      across the eight row groups, which sit in lane bits 3-5 of one wave, so
-//      the sum ends inside the wave in a fixed order);
+// other workgroup reads a conv window it overwrites.  The tokens go in blocks
+// of up to eight.  Per block the workgroup:
+//   1. issues the loads of the block's conv inputs (weights, bias, the window
+//      before the block, x of its tokens) and gates; before the first block
+//      it then issues the loads of its G fp32 state tiles (d_k x d_v each,
+//      16-byte loads, each wave instruction covering whole 128-byte lines), so
+//      the conv runs while HBM streams the tiles;
+//   2. runs the conv decode + SiLU of its channels (q and k of the key head, v
+//      of its value heads) for every token of the block into LDS, and the
+//      gates exp(g), beta;
+//   3. L2-normalises each token's q and k (one wave a token, the sums in the
+//      same lane order as the single-token kernel) and leaves q^ (times
+//      q_scale) and k^ in LDS;
+//   4. per token and head: one pass over the register-resident state gives
+//      both a = S^T k^ and b = S^T q^ (in-thread over its rows, then
+//      butterflies across the eight row groups, which sit in lane bits 3-5 of
+//      one wave, so the sum ends inside the wave in a fixed order);
 //      u = beta (v - alpha a); S' = alpha S + k^ u^T; o = alpha b + u (k^.q^),
 //      which equals S'^T q^;
 //   5. after the last token, stores the state and the advanced window back to
 //      the read slot; o goes out as bf16 every token.
-// The delta rule is Gated DeltaNet's (decay, predict with the decayed state,
-// correct, read out); the slot handling follows mstar PR #1139, "What
-// changed" (keep_in_place for prefill, split walks and the mixed step's decode
-// half) and "Tests" (padding on slot 0).  Single-token steps that allow one
-// head tile per workgroup (every twin step, and in place with one value head
-// per key head) run in gdn_step_tile.hip instead, with the same thread layout
-// and summation order; this kernel takes token walks, per-token states and
-// in-place GQA.
+// Steps 2-3 leave every register they used free again before the state
+// update, so the kernel fits four waves a SIMD with no spills at any head
+// grouping.  The delta rule is Gated DeltaNet's (decay, predict with the
+// decayed state, correct, read out); the slot handling follows mstar PR #1139,
+// "What changed" (keep_in_place for prefill, split walks and the mixed step's
+// decode half) and "Tests" (padding on slot 0).  Single-token steps that
+// allow one head tile per workgroup (every twin step, and in place with one
+// value head per key head) run in gdn_step_tile.hip instead, with the same
+// thread layout and the same arithmetic in the same order, so both give the
+// same bits; this kernel takes token walks, per-token states and in-place GQA.
 //
 // No MFMA: per state element the step does a handful of FMAs against 8 bytes
 // of HBM traffic, far under the fp32 ridge point, so the kernel is written for
@@ -37,20 +43,47 @@
 
 namespace gdn {
 
-template <int DK, int DV, int HPW>
-__global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
-{
-    constexpr int DVS = DV; // whole tiles
-    using Cfg = StepCfg<DK, DVS, HPW>;
-    static_assert(Cfg::NT == 2 * DVS * HPW, "launch bound must match the layout");
-    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, RG = Cfg::RG, RPT = Cfg::RPT;
-    constexpr int NCH = Cfg::NCH;
+// Tokens whose conv outputs are computed together before their state updates.
+constexpr int kWalkBlock = 8;
 
-    // conv outputs (+ a padding slot for spare conv lanes), one set for even
-    // and one for odd tokens: token t writes the set that token t - 2 read,
-    // and a wave gets there only after every wave has passed token t - 1's
-    // barrier, which waits for its LDS reads of token t - 2 to complete
-    __shared__ float y_buf[2][NCH + 4];
+// Everything a conv lane loads for one block of tokens.
+template <int NCQ, int TB>
+struct ConvIn {
+    uint4 wlo[NCQ], whi[NCQ]; // taps 0-3 of its four channels
+    uint2 a0[NCQ], a1[NCQ], a2[NCQ]; // the window before the block, oldest first
+    uint2 bq[NCQ];
+    uint2 xs[NCQ][TB];        // x of the block's tokens (0 past the last token)
+    float g, beta;            // gate of (token tid / HPW, value head tid % HPW)
+};
+
+// TOKENS: per-token states (p.token_slots set); a separate instantiation, so
+// the plain walk carries none of its registers.
+template <int DK, int DV, int HPW, bool TOKENS>
+__global__ __launch_bounds__(2 * DV * HPW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void gdn_step_kernel(StepParams p)
+{
+    using Cfg = StepCfg<DK, DV, HPW>;
+    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, RG = Cfg::RG, RPT = Cfg::RPT, NCH = Cfg::NCH;
+    constexpr int TB = kWalkBlock;
+    constexpr int NW = NT / 64;                // waves
+    constexpr int NCL = NCH / 4;               // conv lanes (channel quads)
+    constexpr int NCW = (NCL + 63) / 64;       // waves' worth of conv lanes
+    constexpr int NCQ = (NCL + NT - 1) / NT;   // quads per thread
+    static_assert(TB * HPW <= NT, "one gate load a thread");
+    static_assert(TB >= 3, "the window before a later block is the previous block's last three tokens");
+
+    // the block's conv outputs (+ a padding slot for spare conv lanes); after
+    // the norm phase q and k hold q^ q_scale and k^
+    __shared__ float y_blk[TB][NCH + 4];
+    __shared__ float kq_blk[TB];          // k^ . q^ of each token
+    __shared__ float2 gate_blk[TB][HPW];  // exp(g), beta of each token and value head
+    // each conv lane's own inputs, parked here as soon as they arrive so no
+    // register holds them through the conv: rows 0-2 the window before the
+    // block (oldest first), rows 3.. the block's x, then the bias and the
+    // four 8-byte pieces of the weights.  One array indexed [row][lane], so
+    // every access is one per-lane address plus a constant.
+    constexpr int RB = 3 + TB, RW = RB + 1, NROW = RW + 4;
+    __shared__ uint2 conv_st[NROW][NCL];
 
     const int tid = threadIdx.x;
     // head of the group this thread updates; NTH is a multiple of the wave size,
@@ -59,6 +92,7 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     const int hloc = __builtin_amdgcn_readfirstlane(tid / NTH);
     const int ht = tid - hloc * NTH; // thread index inside its head slice
     const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // each wave holds 32 columns (eight column groups in lane bits 0-2) of
     // all eight row groups (lane bits 3-5)
     const int cg = (ht >> 6) * 8 + (lane & 7);
@@ -68,12 +102,11 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
     const int hk = blockIdx.x % p.H_k;
     const int r = blockIdx.x / p.H_k;
     const int hv0 = hk * p.G;
-    constexpr int col0 = 0;
     const int T = p.T;
 
     const int rs = p.read_slot[r];
     bool bad = rs < 0 || rs >= p.N;
-    if (p.token_slots && rs != 0) {
+    if (TOKENS && rs != 0) {
         // per-token states: every kept slot must be a usable slot other than the read slot
         for (int t = 0; t < T; ++t) {
             const int ts = p.token_slots[(size_t)r * T + t];
@@ -84,236 +117,321 @@ __global__ __launch_bounds__(2 * DV * HPW) void gdn_step_kernel(StepParams p)
         // padding row (or a row with an unusable slot): touch no slot; out gets
         // +0.0 for padding and NaN for the unusable slot.
         const uint16_t fill = rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
-        for (int e = tid; e < T * HPW * DVS; e += NT) {
-            const int t = e / (HPW * DVS);
-            const int h = (e / DVS) % HPW;
-            const int j = e % DVS;
-            p.out[(((size_t)r * T + t) * p.H_v + hv0 + h) * DV + col0 + j] = fill;
+        for (int e = tid; e < T * HPW * DV; e += NT) {
+            const int t = e / (HPW * DV);
+            const int h = (e / DV) % HPW;
+            const int j = e % DV;
+            p.out[(((size_t)r * T + t) * p.H_v + hv0 + h) * DV + j] = fill;
         }
         return;
     }
 
-    // ---- conv inputs of token 0 first: they are few and on the critical path,
-    // and loads complete in order, so issuing them before the state tile lets
-    // the conv run while the tile is still streaming in.  Each conv lane takes
-    // four consecutive channels: 8-byte loads of its window rows, x and bias,
-    // 16-byte loads of its weights, all raw bf16 bits.  NCL lanes do the conv,
-    // whole waves except the last, whose spare lanes read lane 0's channels and
-    // write their result to a padding slot of y_lds.
-    constexpr int NCL = NCH / 4;               // conv lanes (channel quads)
-    constexpr int NCW = (NCL + 63) / 64;       // waves' worth of conv lanes
-    constexpr int NCQ = (NCL + NT - 1) / NT;   // quads per thread
+    // ---- conv lanes: each takes four consecutive channels, whole waves except
+    // the last, whose spare lanes read nothing and write their result to the
+    // padding slot of y_blk
     const int C = p.C;
-    const int hv = hv0 + hloc;
-    // gates of token 0, also ahead of the state tile
-    float g_t = p.g[(size_t)r * T * p.H_v + hv];
-    float b_t = p.beta[(size_t)r * T * p.H_v + hv];
-    const uint16_t *xrow = p.x + (size_t)r * p.x_row_stride;
-    const uint16_t *cs_rd = p.conv_state + (size_t)rs * 3 * C;
-    uint16_t *cs_wr = p.conv_state + (size_t)rs * 3 * C;
-    const uint16_t *bias_src = p.conv_b ? p.conv_b : p.conv_w; // conv_w: in-bounds stand-in, unused
-    bool conv_wave[NCQ], conv_lane[NCQ], own[NCQ];
+    const uint32_t cbytes = (uint32_t)C * 2u;
+    // channel of x / conv_w / the window for the first channel e of a quad:
+    // q and k of the key head, then v of its value heads
+    auto channel = [&](int e) {
+        const bool isq = e < DK;
+        const bool isk = !isq && e < 2 * DK;
+        const int ve = e >= 2 * DK ? e - 2 * DK : 0;
+        const int h = ve / DV;
+        return isq ? hk * DK + e
+               : isk ? p.H_k * DK + hk * DK + (e - DK)
+                     : 2 * p.H_k * DK + (hv0 + h) * DV + (ve - h * DV);
+    };
+    bool conv_wave[NCQ], conv_lane[NCQ];
     int c[NCQ], e4[NCQ];
-    uint4 wlo[NCQ], whi[NCQ];
-    uint2 wn0[NCQ], wn1[NCQ], wn2[NCQ], xq[NCQ], bq[NCQ];
 #pragma unroll
     for (int k = 0; k < NCQ; ++k) {
         const int li = tid + k * NT;
         conv_wave[k] = (li >> 6) < NCW; // wave-uniform (NT is a multiple of 64)
         conv_lane[k] = li < NCL;
         e4[k] = conv_lane[k] ? 4 * li : 0; // first channel of the quad
-        const int e = e4[k];
-        const bool isq = e < DK;
-        const bool isk = !isq && e < 2 * DK;
-        const int ve = e >= 2 * DK ? e - 2 * DK : 0;
-        const int h = ve / DVS;
-        c[k] = isq ? hk * DK + e
-               : isk ? p.H_k * DK + hk * DK + (e - DK)
-                     : 2 * p.H_k * DK + (hv0 + h) * DV + col0 + (ve - h * DVS);
-        own[k] = conv_lane[k]; // the workgroup owns every channel it reads
-        wlo[k] = whi[k] = make_uint4(0, 0, 0, 0);
-        wn0[k] = wn1[k] = wn2[k] = xq[k] = bq[k] = make_uint2(0, 0);
-        if (conv_wave[k]) {
-            const int ck = c[k];
-            wlo[k] = *reinterpret_cast<const uint4 *>(p.conv_w + (size_t)ck * 4);
-            whi[k] = *reinterpret_cast<const uint4 *>(p.conv_w + (size_t)ck * 4 + 8);
-            wn0[k] = *reinterpret_cast<const uint2 *>(cs_rd + ck);
-            wn1[k] = *reinterpret_cast<const uint2 *>(cs_rd + C + ck);
-            wn2[k] = *reinterpret_cast<const uint2 *>(cs_rd + 2 * C + ck);
-            xq[k] = *reinterpret_cast<const uint2 *>(xrow + ck);
-            bq[k] = *reinterpret_cast<const uint2 *>(bias_src + ck);
-        }
+        c[k] = channel(e4[k]);
     }
-    // conv inputs stay ahead of the tile loads
+    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x + (size_t)r * p.x_row_stride, (uint32_t)T * cbytes);
+    const __amdgpu_buffer_rsrc_t cw = bf16_rsrc(p.conv_w, cbytes * 4u);
+    const __amdgpu_buffer_rsrc_t br = bf16_rsrc(p.conv_b ? p.conv_b : p.conv_w, p.conv_b ? cbytes : 0u);
+    const __amdgpu_buffer_rsrc_t win = bf16_rsrc(p.conv_state + (size_t)rs * 3 * C, 3u * cbytes);
+    const uint32_t gbytes = (uint32_t)T * (uint32_t)p.H_v * 4u;
+    const __amdgpu_buffer_rsrc_t gr = f32_rsrc(p.g + (size_t)r * T * p.H_v, gbytes);
+    const __amdgpu_buffer_rsrc_t bt_r = f32_rsrc(p.beta + (size_t)r * T * p.H_v, gbytes);
+    const bool has_bias = p.conv_b != nullptr;
+    // o of this row: T tokens x H_v heads x d_v
+    const __amdgpu_buffer_rsrc_t orow =
+        bf16_rsrc(p.out + (size_t)r * T * p.H_v * DV, (uint32_t)T * (uint32_t)p.H_v * DV * 2u);
+
+    // The loads of a block's conv inputs and gates; all offsets of lanes with
+    // nothing to read, and of tokens past the last, fall outside their
+    // resources and read 0, so the block needs no branch around a load.
+    // Both take their lane offsets from a copy of the thread index the
+    // compiler cannot see through, so nothing they compute is kept in a
+    // register across the token blocks.
+    auto issue = [&](ConvIn<NCQ, TB> &in, int t0) {
+        int tt = tid;
+        asm volatile("" : "+v"(tt));
+#pragma unroll
+        for (int k = 0; k < NCQ; ++k) {
+            const int li = tt + k * NT;
+            const bool lane_ok = li < NCL;
+            in.wlo[k] = in.whi[k] = make_uint4(0, 0, 0, 0);
+            in.a0[k] = in.a1[k] = in.a2[k] = in.bq[k] = make_uint2(0, 0);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                in.xs[k][tb] = make_uint2(0, 0);
+            if (!conv_wave[k])
+                continue;
+            // kOOB plus any row offset below 2 GiB stays past the end of every
+            // resource, and so does the offset of a token past the last: no
+            // select per load
+            const int ch = channel(lane_ok ? 4 * li : 0);
+            const uint32_t o2 = lane_ok ? (uint32_t)ch * 2u : kOOB;
+            const uint32_t o8 = lane_ok ? (uint32_t)ch * 8u : kOOB;
+            in.wlo[k] = load_b128(cw, o8);
+            in.whi[k] = load_b128(cw, o8 + 16u);
+            in.bq[k] = load_b64(br, o2);
+            // the window before token t0: the slot's own window for the first
+            // block, the previous block's last three tokens after that
+            const __amdgpu_buffer_rsrc_t wsrc = t0 == 0 ? win : xr;
+            const uint32_t wbase = t0 == 0 ? 0u : (uint32_t)(t0 - 3) * cbytes;
+            in.a0[k] = load_b64(wsrc, o2 + wbase);
+            in.a1[k] = load_b64(wsrc, o2 + wbase + cbytes);
+            in.a2[k] = load_b64(wsrc, o2 + wbase + 2u * cbytes);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                in.xs[k][tb] = load_b64(xr, o2 + (uint32_t)(t0 + tb) * cbytes);
+        }
+        const int gt = tt / HPW, gh = tt % HPW;
+        const uint32_t go = tt < TB * HPW && t0 + gt < T
+                                ? (uint32_t)(((t0 + gt) * p.H_v + hv0 + gh) * 4)
+                                : kOOB;
+        in.g = load_f32(gr, go);
+        in.beta = load_f32(bt_r, go);
+    };
+
+    // Park a block's conv inputs in LDS, each conv lane its own, and its gates
+    // as exp(g), beta.  This waits for the block's conv loads only: they were
+    // issued before anything still in flight.
+    auto stash = [&](const ConvIn<NCQ, TB> &in) {
+        int tt = tid;
+        asm volatile("" : "+v"(tt));
+#pragma unroll
+        for (int k = 0; k < NCQ; ++k) {
+            const int li = tt + k * NT;
+            if (li >= NCL)
+                continue;
+            conv_st[RW][li] = make_uint2(in.wlo[k].x, in.wlo[k].y);
+            conv_st[RW + 1][li] = make_uint2(in.wlo[k].z, in.wlo[k].w);
+            conv_st[RW + 2][li] = make_uint2(in.whi[k].x, in.whi[k].y);
+            conv_st[RW + 3][li] = make_uint2(in.whi[k].z, in.whi[k].w);
+            conv_st[RB][li] = in.bq[k];
+            conv_st[0][li] = in.a0[k];
+            conv_st[1][li] = in.a1[k];
+            conv_st[2][li] = in.a2[k];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                conv_st[3 + tb][li] = in.xs[k][tb];
+        }
+        if (tt < TB * HPW)
+            gate_blk[tt / HPW][tt % HPW] = make_float2(expf(in.g), in.beta);
+    };
+
+    ConvIn<NCQ, TB> in;
+    issue(in, 0);
+    // conv inputs stay ahead of the tile loads: they are few and on the
+    // critical path, and loads complete in order
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- state slice -> registers
+    const int hv = hv0 + hloc;
     constexpr uint32_t TILE = (uint32_t)DK * DV;
     const __amdgpu_buffer_rsrc_t rd_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u);
-    const uint32_t voff = (uint32_t)((rg * DV + col0 + 4 * cg) * 4);
+    const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
     float4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         s[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd_tile, voff, m * RG * DV * 4, kLoadPolicy));
-    // Every load of the step is now in flight.  Keep the scheduler from sinking
-    // any of them below the first wait: under a saturated memory system a load
-    // issued after the flood of tile loads queues behind all of them.
+    // Every load of the first block is now in flight.  Keep the scheduler from
+    // sinking any of them below the first wait: under a saturated memory
+    // system a load issued after the flood of tile loads queues behind all of
+    // them.
     __builtin_amdgcn_sched_barrier(0);
+    stash(in);
 
-    const bool has_bias = p.conv_b != nullptr;
-    uint2 xn[NCQ];     // the next token's x, loaded one token ahead
-    float g_n = 0.f, b_n = 0.f;
-    for (int t = 0; t < T; ++t) {
-        float *y_lds = y_buf[t & 1];
-        if (t > 0) {
-#pragma unroll
-            for (int k = 0; k < NCQ; ++k)
-                xq[k] = xn[k];
-            g_t = g_n;
-            b_t = b_n;
-        }
-        if (t + 1 < T) {
-            // loads of token t+1's inputs go out now and land while token t computes
-#pragma unroll
-            for (int k = 0; k < NCQ; ++k)
-                xn[k] = conv_wave[k] ? *reinterpret_cast<const uint2 *>(xrow + (size_t)(t + 1) * C + c[k])
-                                     : make_uint2(0, 0);
-            g_n = p.g[((size_t)r * T + t + 1) * p.H_v + hv];
-            b_n = p.beta[((size_t)r * T + t + 1) * p.H_v + hv];
-        }
+    for (int t0 = 0;;) {
+        const int nb = T - t0 < TB ? T - t0 : TB;
 
-        // ---- conv decode + SiLU of this workgroup's channels -> LDS; the
-        // window (raw bf16 bits) advances in registers
+        // ---- conv decode + SiLU of the block's tokens -> y_blk.  Token tb
+        // reads rows tb..tb+3 of its lane's parked sequence: the window
+        // before it and its x.  (The compiler barrier keeps the stash from
+        // being forwarded in registers.)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int k = 0; k < NCQ; ++k) {
+            const int li = tid + k * NT;
             if (!conv_wave[k])
                 continue;
-            const uint4 wl = wlo[k], wh = whi[k];
-            const uint2 a0 = wn0[k], a1 = wn1[k], a2 = wn2[k], xx = xq[k], bb = bq[k];
-            float4 y;
-            y.x = conv_tap4(wl.x, wl.y, a0.x << 16, a1.x << 16, a2.x << 16, xx.x << 16, bb.x << 16, has_bias);
-            y.y = conv_tap4(wl.z, wl.w, a0.x & 0xffff0000u, a1.x & 0xffff0000u, a2.x & 0xffff0000u,
-                            xx.x & 0xffff0000u, bb.x & 0xffff0000u, has_bias);
-            y.z = conv_tap4(wh.x, wh.y, a0.y << 16, a1.y << 16, a2.y << 16, xx.y << 16, bb.y << 16, has_bias);
-            y.w = conv_tap4(wh.z, wh.w, a0.y & 0xffff0000u, a1.y & 0xffff0000u, a2.y & 0xffff0000u,
-                            xx.y & 0xffff0000u, bb.y & 0xffff0000u, has_bias);
-            *reinterpret_cast<float4 *>(&y_lds[conv_lane[k] ? e4[k] : NCH]) = y;
-            wn0[k] = a1;
-            wn1[k] = a2;
-            wn2[k] = xx;
+            const int lr = conv_lane[k] ? li : 0; // spare lanes compute lane 0's channels into the padding slot
+            const uint2 w0 = conv_st[RW][lr], w1 = conv_st[RW + 1][lr], w2 = conv_st[RW + 2][lr],
+                        w3 = conv_st[RW + 3][lr];
+            const uint4 wl = make_uint4(w0.x, w0.y, w1.x, w1.y), wh = make_uint4(w2.x, w2.y, w3.x, w3.y);
+            const uint2 bb = conv_st[RB][lr];
+            const int yo = conv_lane[k] ? e4[k] : NCH;
+            for (int tb = 0; tb < nb; ++tb) {
+                const uint2 a0 = conv_st[tb][lr], a1 = conv_st[tb + 1][lr], a2 = conv_st[tb + 2][lr];
+                const uint2 xx = conv_st[tb + 3][lr];
+                float4 y;
+                y.x = conv_tap4(wl.x, wl.y, a0.x << 16, a1.x << 16, a2.x << 16, xx.x << 16, bb.x << 16, has_bias);
+                y.y = conv_tap4(wl.z, wl.w, a0.x & 0xffff0000u, a1.x & 0xffff0000u, a2.x & 0xffff0000u,
+                                xx.x & 0xffff0000u, bb.x & 0xffff0000u, has_bias);
+                y.z = conv_tap4(wh.x, wh.y, a0.y << 16, a1.y << 16, a2.y << 16, xx.y << 16, bb.y << 16, has_bias);
+                y.w = conv_tap4(wh.z, wh.w, a0.y & 0xffff0000u, a1.y & 0xffff0000u, a2.y & 0xffff0000u,
+                                xx.y & 0xffff0000u, bb.y & 0xffff0000u, has_bias);
+                *reinterpret_cast<float4 *>(&y_blk[tb][yo]) = y;
+                if (TOKENS) {
+                    // speculative verify: the window after this token goes to
+                    // the token's own slot (0: not kept)
+                    const int ts = p.token_slots[(size_t)r * T + t0 + tb];
+                    if (ts != 0) {
+                        const __amdgpu_buffer_rsrc_t tw = bf16_rsrc(p.conv_state + (size_t)ts * 3 * C, 3u * cbytes);
+                        const uint32_t o2 = conv_lane[k] ? (uint32_t)c[k] * 2u : kOOB;
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{a1.x, a1.y}, tw, o2, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{a2.x, a2.y}, tw, o2 + cbytes, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{xx.x, xx.y}, tw, o2 + 2u * cbytes, 0, 0);
+                    }
+                }
+            }
+            if (!TOKENS && t0 + nb == T) {
+                // the advanced window of a channel this workgroup owns, back to
+                // the read slot: a shift of bf16 values, stored as the bits
+                // they were read as (no other workgroup reads it)
+                const uint2 n0 = conv_st[nb][lr], n1 = conv_st[nb + 1][lr], n2 = conv_st[nb + 2][lr];
+                const uint32_t o2 = conv_lane[k] ? (uint32_t)c[k] * 2u : kOOB;
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{n0.x, n0.y}, win, o2, 0, kStorePolicy);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{n1.x, n1.y}, win, o2 + cbytes, 0, kStorePolicy);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{n2.x, n2.y}, win, o2 + 2u * cbytes, 0, kStorePolicy);
+            }
         }
         lds_barrier();
 
-        // ---- L2 norms of q and k (every wave computes the same sums)
-        float sq = 0.f, sk = 0.f, sqk = 0.f;
+        // ---- L2 norms of q and k, one wave a token (lane l sums elements l,
+        // l + 64, ...; then a butterfly over the wave), and q, k rescaled in place
+        for (int tb = wave; tb < nb; tb += NW) {
+            float *y = y_blk[tb];
+            float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
-        for (int i = lane; i < DK; i += 64) {
-            const float qv = y_lds[i], kv = y_lds[DK + i];
-            sq = fmaf(qv, qv, sq);
-            sk = fmaf(kv, kv, sk);
-            sqk = fmaf(qv, kv, sqk);
+            for (int i = lane; i < DK; i += 64) {
+                const float qv = y[i], kv = y[DK + i];
+                sq = fmaf(qv, qv, sq);
+                sk = fmaf(kv, kv, sk);
+                sqk = fmaf(qv, kv, sqk);
+            }
+            sq = xor_sum<1>(sq);
+            sk = xor_sum<1>(sk);
+            sqk = xor_sum<1>(sqk);
+            const float rq = 1.0f / sqrtf(sq + p.l2_eps);
+            const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+            const float qs = rq * p.q_scale;
+#pragma unroll
+            for (int i = lane; i < DK; i += 64) {
+                const float qv = y[i], kv = y[DK + i];
+                y[i] = qv * qs;
+                y[DK + i] = kv * rk;
+            }
+            if (lane == 0)
+                kq_blk[tb] = sqk * rk * qs; // k^ . q^
         }
-        sq = xor_sum<1>(sq);
-        sk = xor_sum<1>(sk);
-        sqk = xor_sum<1>(sqk);
-        const float rq = 1.0f / sqrtf(sq + p.l2_eps);
-        const float rk = 1.0f / sqrtf(sk + p.l2_eps);
-        const float qs = rq * p.q_scale;
-        const float kq = sqk * rk * qs; // k^ . q^
+        lds_barrier();
 
-        // ---- projections of the state onto k^ and q^
-        const size_t gi = ((size_t)r * T + t) * p.H_v + hv;
-        const float alpha = expf(g_t);
-        const float bt = b_t;
-        float4 pa = f4_zero(), pb = f4_zero();
+        // ---- per token: projections of the state onto k^ and q^, the delta
+        // update in registers, and the read-out
+        for (int tb = 0; tb < nb; ++tb) {
+            const float *y = y_blk[tb];
+            float4 pa = f4_zero(), pb = f4_zero();
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + RG * m;
-            const float kh = y_lds[DK + i] * rk;
-            const float qh = y_lds[i] * qs;
-            pa.x = fmaf(s[m].x, kh, pa.x);
-            pa.y = fmaf(s[m].y, kh, pa.y);
-            pa.z = fmaf(s[m].z, kh, pa.z);
-            pa.w = fmaf(s[m].w, kh, pa.w);
-            pb.x = fmaf(s[m].x, qh, pb.x);
-            pb.y = fmaf(s[m].y, qh, pb.y);
-            pb.z = fmaf(s[m].z, qh, pb.z);
-            pb.w = fmaf(s[m].w, qh, pb.w);
-        }
-        // butterflies over lane bits 3, 4, 5 form the pairwise tree
-        // ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over the row groups in every lane
-        pa.x = xor_sum<8>(pa.x);
-        pa.y = xor_sum<8>(pa.y);
-        pa.z = xor_sum<8>(pa.z);
-        pa.w = xor_sum<8>(pa.w);
-        pb.x = xor_sum<8>(pb.x);
-        pb.y = xor_sum<8>(pb.y);
-        pb.z = xor_sum<8>(pb.z);
-        pb.w = xor_sum<8>(pb.w);
-        const float4 a = pa, b = pb;
+            for (int m = 0; m < RPT; ++m) {
+                const int i = rg + RG * m;
+                const float kh = y[DK + i];
+                const float qh = y[i];
+                pa.x = fmaf(s[m].x, kh, pa.x);
+                pa.y = fmaf(s[m].y, kh, pa.y);
+                pa.z = fmaf(s[m].z, kh, pa.z);
+                pa.w = fmaf(s[m].w, kh, pa.w);
+                pb.x = fmaf(s[m].x, qh, pb.x);
+                pb.y = fmaf(s[m].y, qh, pb.y);
+                pb.z = fmaf(s[m].z, qh, pb.z);
+                pb.w = fmaf(s[m].w, qh, pb.w);
+            }
+            // k^ is read again for the update below rather than held in
+            // sixteen registers through the butterflies
+            asm volatile("" ::: "memory");
+            // butterflies over lane bits 3, 4, 5 form the pairwise tree
+            // ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) over the row groups in every lane
+            pa.x = xor_sum<8>(pa.x);
+            pa.y = xor_sum<8>(pa.y);
+            pa.z = xor_sum<8>(pa.z);
+            pa.w = xor_sum<8>(pa.w);
+            pb.x = xor_sum<8>(pb.x);
+            pb.y = xor_sum<8>(pb.y);
+            pb.z = xor_sum<8>(pb.z);
+            pb.w = xor_sum<8>(pb.w);
 
-        // ---- delta update in registers, and the read-out
-        const float *vv = &y_lds[2 * DK + hloc * DVS + 4 * cg];
-        float4 u;
-        u.x = bt * (vv[0] - alpha * a.x);
-        u.y = bt * (vv[1] - alpha * a.y);
-        u.z = bt * (vv[2] - alpha * a.z);
-        u.w = bt * (vv[3] - alpha * a.w);
+            const float2 gb = gate_blk[tb][hloc];
+            const float alpha = gb.x, bt = gb.y;
+            const float kq = kq_blk[tb];
+            const float *vv = &y[2 * DK + hloc * DV + 4 * cg];
+            float4 u;
+            u.x = bt * (vv[0] - alpha * pa.x);
+            u.y = bt * (vv[1] - alpha * pa.y);
+            u.z = bt * (vv[2] - alpha * pa.z);
+            u.w = bt * (vv[3] - alpha * pa.w);
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const float kh = y_lds[DK + rg + RG * m] * rk;
-            s[m].x = fmaf(kh, u.x, alpha * s[m].x);
-            s[m].y = fmaf(kh, u.y, alpha * s[m].y);
-            s[m].z = fmaf(kh, u.z, alpha * s[m].z);
-            s[m].w = fmaf(kh, u.w, alpha * s[m].w);
-        }
-        if (rg == 0) {
-            const float o0 = fmaf(u.x, kq, alpha * b.x);
-            const float o1 = fmaf(u.y, kq, alpha * b.y);
-            const float o2 = fmaf(u.z, kq, alpha * b.z);
-            const float o3 = fmaf(u.w, kq, alpha * b.w);
-            const u32x2 pk = {(uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16),
-                              (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16)};
-            __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(p.out + (gi * DV + col0 + 4 * cg)));
-        }
-        if (p.token_slots) {
-            // speculative verify: the state and window after this token go to
-            // the token's own slot (0: not kept); the read slot stays as it was
-            const int ts = p.token_slots[(size_t)r * T + t];
-            if (ts != 0) {
-                uint16_t *cs_tok = p.conv_state + (size_t)ts * 3 * C;
+            for (int m = 0; m < RPT; ++m) {
+                const float kh = y[DK + rg + RG * m];
+                s[m].x = fmaf(kh, u.x, alpha * s[m].x);
+                s[m].y = fmaf(kh, u.y, alpha * s[m].y);
+                s[m].z = fmaf(kh, u.z, alpha * s[m].z);
+                s[m].w = fmaf(kh, u.w, alpha * s[m].w);
+            }
+            {
+                // o: row group 0 of every column group (lanes 0-7 of each wave)
+                const float o0 = fmaf(u.x, kq, alpha * pb.x);
+                const float o1 = fmaf(u.y, kq, alpha * pb.y);
+                const float o2 = fmaf(u.z, kq, alpha * pb.z);
+                const float o3 = fmaf(u.w, kq, alpha * pb.w);
+                const u32x2 pk = {(uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16),
+                                  (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16)};
+                const uint32_t oo = (uint32_t)(((t0 + tb) * p.H_v + hv) * DV + 4 * cg) * 2u;
+                __builtin_amdgcn_raw_buffer_store_b64(pk, orow, rg == 0 ? oo : kOOB, 0, kStorePolicy);
+            }
+            if (TOKENS) {
+                // speculative verify: the state after this token goes to the
+                // token's own slot (0: not kept); the read slot stays as it was
+                const int ts = p.token_slots[(size_t)r * T + t0 + tb];
+                if (ts != 0) {
+                    const __amdgpu_buffer_rsrc_t tok_tile =
+                        tile_rsrc(p.state + ((size_t)ts * p.H_v + hv) * TILE, TILE * 4u);
 #pragma unroll
-                for (int k = 0; k < NCQ; ++k) {
-                    if (own[k]) {
-                        uint16_t *dst = cs_tok + c[k];
-                        *reinterpret_cast<u32x2 *>(dst) = u32x2{wn0[k].x, wn0[k].y};
-                        *reinterpret_cast<u32x2 *>(dst + C) = u32x2{wn1[k].x, wn1[k].y};
-                        *reinterpret_cast<u32x2 *>(dst + 2 * C) = u32x2{wn2[k].x, wn2[k].y};
-                    }
+                    for (int m = 0; m < RPT; ++m)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), tok_tile, voff,
+                                                               m * RG * DV * 4, kStorePolicy);
                 }
-                const __amdgpu_buffer_rsrc_t tok_tile =
-                    tile_rsrc(p.state + ((size_t)ts * p.H_v + hv) * TILE, TILE * 4u);
-#pragma unroll
-                for (int m = 0; m < RPT; ++m)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), tok_tile, voff,
-                                                           m * RG * DV * 4, kStorePolicy);
             }
         }
-    }
-    if (p.token_slots)
-        return;
 
-    // ---- advanced conv windows of the channels this workgroup owns: a shift
-    // of bf16 values, stored as the bits they were read as
-#pragma unroll
-    for (int k = 0; k < NCQ; ++k) {
-        if (own[k]) {
-            uint16_t *dst = cs_wr + c[k];
-            __builtin_nontemporal_store(u32x2{wn0[k].x, wn0[k].y}, reinterpret_cast<u32x2 *>(dst));
-            __builtin_nontemporal_store(u32x2{wn1[k].x, wn1[k].y}, reinterpret_cast<u32x2 *>(dst + C));
-            __builtin_nontemporal_store(u32x2{wn2[k].x, wn2[k].y}, reinterpret_cast<u32x2 *>(dst + 2 * C));
-        }
+        t0 += TB;
+        if (t0 >= T)
+            break;
+        // every wave is done with this block's LDS before the next one writes it
+        lds_barrier();
+        issue(in, t0);
+        stash(in);
     }
+    if (TOKENS)
+        return;
 
     // ---- new state -> the read slot
     const __amdgpu_buffer_rsrc_t wr_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u);
@@ -332,8 +450,9 @@ static hipError_t launch_step(const StepParams &p, hipStream_t stream)
     StepParams q = p;
     q.n_slices = 1;
     void *args[] = {&q};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, HPW>), dim3((unsigned)tiles),
-                           dim3(StepCfg<DK, DV, HPW>::NT), args, 0, stream);
+    const void *k = p.token_slots ? reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, HPW, true>)
+                                  : reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, HPW, false>);
+    return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(StepCfg<DK, DV, HPW>::NT), args, 0, stream);
 }
 
 template <int DK, int DV>

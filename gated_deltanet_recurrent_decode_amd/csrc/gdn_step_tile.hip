@@ -38,27 +38,6 @@
 
 namespace gdn {
 
-// A byte offset past the end of every buffer resource used here: a load there
-// returns 0 and a store there is dropped, with no memory access.
-constexpr uint32_t kOOB = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t bf16_rsrc(const uint16_t *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint2 load_b64(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    return make_uint2(v.x, v.y);
-}
-
-__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // Everything one head tile carries from its loads to its stores.
 template <int DK, int DVS>
 struct TileState {

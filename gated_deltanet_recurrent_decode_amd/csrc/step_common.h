@@ -42,6 +42,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(float *base, uint32_
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
+// A byte offset past the end of every buffer resource used here: a load there
+// returns 0 and a store there is dropped, with no memory access.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Raw buffer resources over bf16 and fp32 arrays of `bytes` bytes (under 2 GiB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bf16_rsrc(const uint16_t *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint2 load_b64(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // One channel of the width-4 conv with SiLU, from bf16 values already moved
 // into the high half of a 32-bit word (so they read as fp32): taps 0-1 in
 // w01, taps 2-3 in w23 (tap 3 multiplies the current token), the three

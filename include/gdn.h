@@ -109,7 +109,9 @@ typedef struct gdn_dims {
  * GDN_ERR_REFUSED (multi-token walks stay in place).  In place needs
  * H_v/H_k in {1, 2, 4}.  Alignment (GDN_ERR_UNSUPPORTED otherwise): state
  * and conv_w 16 bytes; x, conv_b, conv_state and out 8 bytes; x_row_stride a
- * multiple of 4 elements.
+ * multiple of 4 elements.  Size limits (GDN_ERR_SHAPE otherwise): a row's x
+ * with eight more tokens, its out and its gates each under 2 GiB, and conv_w
+ * under 2 GiB.
  */
 gdn_status gdn_decode_step(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
                            const gdn_bf16 *conv_w, const gdn_bf16 *conv_b, gdn_bf16 *conv_state,

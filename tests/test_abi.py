@@ -83,6 +83,13 @@ def test_step_validation():
     assert _step(_dims(), state=ctypes.c_void_p(0x10008)) == UNSUPPORTED
     assert _step(_dims(), out=ctypes.c_void_p(0x10002)) == UNSUPPORTED
     assert _step(_dims(), conv_w=ctypes.c_void_p(0x10004)) == UNSUPPORTED
+    # a row's x (with eight tokens of overrun), out and gates stay under 2 GiB:
+    # C = 2*16*128 + 16*128 = 6144 channels, 2^31 / (2 C) = 174762.67 tokens,
+    # so T + 8 <= 174762.  The largest legal T passes the size checks and is
+    # stopped by the alignment check after them (nothing is launched).
+    big = dict(H_k=16, H_v=16, d_k=128, d_v=128)
+    assert _step(_dims(T=174755, **big), write_slot=None) == SHAPE
+    assert _step(_dims(T=174754, **big), write_slot=None, state=ctypes.c_void_p(0x10008)) == UNSUPPORTED
 
 
 def test_step_commit_validation():

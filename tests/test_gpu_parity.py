@@ -79,6 +79,9 @@ SMALL = [
     (3, 3, 2, 4, 128, 128, False, None),   # in place, 3 tokens, G = 2
     (4, 2, 1, 4, 64, 64, False, 3),        # in place, G = 4, padding
     (9, 4, 2, 2, 64, 128, False, None),    # in place, 4 tokens
+    (3, 11, 2, 2, 128, 128, False, None),  # in place, 11 tokens: a full block of 8, then 3
+    (4, 17, 1, 4, 64, 64, False, 3),       # in place, G = 4, 17 tokens (blocks of 8, 8, 1), padding
+    (2, 9, 2, 4, 128, 64, False, None),    # in place, G = 2, d_k != d_v, 9 tokens
 ]
 
 
