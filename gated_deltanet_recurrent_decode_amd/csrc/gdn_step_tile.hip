@@ -139,7 +139,7 @@ __device__ __forceinline__ void tile_issue_state(TileState<DK, DVS> &t, const St
 // Conv + SiLU -> LDS, L2 norms, projections, the fixed-order reduction, the
 // delta update, the read-out, and the stores of o, the advanced conv windows
 // and the new state.
-template <int DK, int DV, int DVS, bool INPLACE, int TPW>
+template <int DK, int DV, int DVS, bool INPLACE>
 __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepParams &p, int cg, int rg, int lane,
                                              int ht, uint32_t voff, float *y_lds)
 {
@@ -221,17 +221,6 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
     pb.w = xor_sum<8>(pb.w);
     a = pa;
     b = pb;
-    }
-    if constexpr (TPW > 1) {
-        // every wave of the workgroup has its tile in registers before any
-        // wave stores: the compute unit's reads all come before its writes.
-        // A real tile has consumed every load by now; waiting for all of them
-        // on every path also keeps the compiler from guarding the stores below
-        // with waits for loads a padding tile never consumed
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
     }
     if (!t.real)
         return;
@@ -346,8 +335,9 @@ void gdn_step_tile_kernel(StepParams p)
         if constexpr (TPW == 1)
             return;
     }
-    // the tiles of real rows do the work; the others only meet the barriers
-    tile_process<DK, DV, DVS, INPLACE, TPW>(t, p, cg, rg, lane, ht, voff, y_lds);
+    // the tiles of real rows do the work; the others only meet the workgroup
+    // barrier after the conv
+    tile_process<DK, DV, DVS, INPLACE>(t, p, cg, rg, lane, ht, voff, y_lds);
 
     // fused commit: the workgroup of a row's first tile writes the swapped
     // pair into the next step's slot arrays (distinct from the ones this step
@@ -391,19 +381,17 @@ static int device_cus()
 // Launch shape.  Up to 2047 head tiles a step is one round of workgroups on
 // the 256 CUs, and its time follows the CUs that get the most tiles.
 //
-// Tiles a workgroup (twin writes of 128 x 128 tiles).  With one tile a
-// workgroup, the four workgroups on a CU get their tiles at different times
-// (measured with clock stamps: the last load of a workgroup arrives anywhere
-// from 3 to 20 us into a 64-row step), and each writes as soon as its tile is
-// in, so reads and writes share HBM for most of the step -- which it serves
-// far worse than either alone (a probe with half the workgroups only reading
-// and half only writing took 34.7 us against 11.8 + 12.4 for the two apart).
-// A workgroup of two or three tiles waits until all of them are in before any
-// wave writes, so a CU's reads come before its writes.  It pays when a round
-// puts three or four tiles on every CU; measured, us a step: 64 rows 27.9 ->
-// 26.6 (two tiles a workgroup), 56 rows 24.8 -> 23.4 (two), 48 rows 21.7 ->
-// 20.8 (three); no gain at 32, 40, 96 or 128 rows, four tiles at 64 rows 27.2,
-// and none in place.
+// Tiles a workgroup (twin writes of 128 x 128 tiles).  When a round puts
+// three or four tiles on every CU, one workgroup of four tiles a CU (1024
+// threads, a quarter of the workgroups to dispatch and to start) beats four
+// workgroups of one.  Measured on MI355X, 16 heads, slots cold and scattered,
+// us a step, one tile / two tiles with all of a workgroup's loads in before
+// any store / four tiles, each wave storing as soon as its own tile is
+// updated: 48 rows 22.0 / 21.6 / 20.3, 56 rows 25.8 / 23.5 / 22.5, 64 rows
+// 27.7 / 26.3 / 25.65.  The wait for the workgroup's loads helped two tiles
+// and costs four (26.4 at 64 rows), so it is gone; three tiles measured
+// 29.4 at 64 rows.  One tile stays best at 128 rows (53.6 against 54.0) and
+// in place at 64 and 128 rows (27.7 against 27.9 and 28.4).
 //
 // Column slices per head otherwise.  Halving the tiles evens out the CUs' share
 // when heads mod 256 is between 1 and 128 (two half tiles where one CU had a
@@ -429,7 +417,7 @@ static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
     if constexpr (DK == 128 && DV == 128) {
         const long long cus = device_cus();
         if (p.twin && heads * 2 > 5 * cus && heads <= 4 * cus)
-            return heads <= 3 * cus ? launch_tile<DK, DV, DV, 3>(q, stream) : launch_tile<DK, DV, DV, 2>(q, stream);
+            return launch_tile<DK, DV, DV, 4>(q, stream);
     }
     if (!p.twin || heads >= 2048 || (heads >= 128 && (rem == 0 || rem > 128)))
         return launch_tile<DK, DV, DV, 1>(q, stream);

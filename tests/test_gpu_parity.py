@@ -203,6 +203,26 @@ def test_twin_launch_shapes_equal_whole_tile_in_place(gdn, torch, B):
     assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
 
 
+def test_four_tile_workgroups_with_a_partial_last_group(gdn, torch):
+    """45 rows of 15 heads (675 tiles of 128 x 128) take four tiles a
+    workgroup; the last workgroup holds three tiles and one past the end.
+    Twin against the oracle (with padding rows) and bit for bit against the
+    same step in place, which takes one tile a workgroup."""
+    t = torch
+    case = gi.small(B=45, T=1, H_k=15, H_v=15, d=128, twin=True, real_rows=41, seed=45)
+    dp_t, out_t = _check_step(gdn, case, twin=True, poison=True)
+    pool = case.pools[0]
+    ip = gi.Case(case.name, case.shape, [gi.Pool(pool.state, pool.conv_state, pool.conv_w, pool.read_slot,
+                                                 pool.read_slot.copy())], case.steps, case.real_rows, False)
+    dp_i, out_i = _check_step(gdn, ip, twin=False)
+    assert t.equal(out_t.view(t.int16), out_i.view(t.int16))
+    real = pool.read_slot != 0
+    wr = t.from_numpy(pool.write_slot[real].astype(np.int64)).cuda()
+    rd = t.from_numpy(pool.read_slot[real].astype(np.int64)).cuda()
+    assert t.equal(dp_t.state[wr].view(t.int32), dp_i.state[rd].view(t.int32))
+    assert t.equal(dp_t.conv_state[wr].view(t.int16), dp_i.conv_state[rd].view(t.int16))
+
+
 @pytest.mark.parametrize("B,pad_rows", [(48, (5, 17, 30, 47)), (64, (0, 3, 31, 32, 63))], ids=["48rows", "64rows"])
 def test_multi_tile_workgroups_with_padding_rows(gdn, torch, B, pad_rows):
     """Twin steps whose workgroups hold several head tiles (three at 48 rows,
