@@ -1,6 +1,12 @@
-"""The built library's gfx950 machine code, checked for one hazard: a vector
-instruction that writes a register holding the data of a 16- or 12-byte store
-issued by the instruction right before it.
+"""The built library's gfx950 machine code, checked for two things.
+
+No kernel uses scratch memory: each kernel's metadata (llvm-readelf --notes
+on the code objects of the offload bundle) states a private segment of 0
+bytes and no spilled vector register, so no launch shape of any entry point
+spills its registers to memory.
+
+And one hazard: a vector instruction that writes a register holding the data
+of a 16- or 12-byte store issued by the instruction right before it.
 
 A store with more than 8 bytes of data reads part of its data registers one
 cycle late, so a vector write to them must wait at least one instruction.  The
@@ -26,6 +32,7 @@ import bench
 
 LIB = os.path.join(bench.ROOT, "gated_deltanet_recurrent_decode_amd", "libgdn.so")
 OBJDUMP = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "llvm-objdump")
+READELF = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "llvm-readelf")
 
 STORE = re.compile(r"^\s*(buffer_store_dwordx[34]|global_store_dwordx[34]|flat_store_dwordx[34]|"
                    r"scratch_store_dwordx[34])\s+(.*)$")
@@ -106,3 +113,31 @@ def test_no_write_into_store_data_right_behind_a_wide_store():
                 break
     assert stores > 100, "expected the library's wide stores in the disassembly"
     assert not bad, "store data overwritten right behind the store:\n" + "\n".join(bad[:20])
+
+
+def test_no_kernel_uses_scratch():
+    if not os.path.exists(LIB):
+        pytest.skip("libgdn.so is not built")
+    if not os.path.exists(READELF):
+        pytest.skip("llvm-readelf is not available")
+    kernels = {}
+    with tempfile.TemporaryDirectory() as d:
+        for i, co in enumerate(bench.device_code_objects(LIB)):
+            path = os.path.join(d, f"co{i}.elf")
+            with open(path, "wb") as f:
+                f.write(co)
+            notes = subprocess.run([READELF, "--notes", path], capture_output=True, text=True, check=True).stdout
+            name = None
+            for line in notes.splitlines():
+                m = re.match(r"^\s*\.name:\s+(\S+)", line)
+                if m:
+                    name = m.group(1)
+                    kernels.setdefault(name, {})
+                    continue
+                m = re.match(r"^\s*\.(private_segment_fixed_size|vgpr_spill_count|sgpr_spill_count):\s+(\d+)", line)
+                if m and name is not None:
+                    kernels[name][m.group(1)] = int(m.group(2))
+    steps = [k for k in kernels if "gdn_step" in k]
+    assert len(kernels) > 60 and len(steps) >= 40, "expected every kernel's metadata"
+    scratch = {k: v for k, v in kernels.items() if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
+    assert not scratch, f"kernels using scratch: {scratch}"
