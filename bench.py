@@ -88,6 +88,43 @@ MEASURED_PREFILL_TRAFFIC = {"kernel_code_sha256": "f0947739f8a69197219350d1fd3a4
                             "bytes_per_call": {(16, 512): 754_928_363, (1, 4096): 364_499_998}}
 
 
+# The no-math copy designs the calibration sweeps (gdn_traffic_probe): the
+# step's tile layout with one, two or four tiles a workgroup, and plain chunks
+# varied one axis at a time around 256 threads x 8 loads: 16-byte loads in
+# flight a lane, workgroup size, when stores may go (each after its own load,
+# after all of the lane's loads, after all of the workgroup's loads), a
+# persistent grid of k workgroups a CU, and the cache policy.
+PROBE_SWEEP = {
+    "tile1": dict(shape="tile1"),
+    "tile1_wg": dict(shape="tile1", order="workgroup"),
+    "tile2_wg": dict(shape="tile2", order="workgroup"),
+    "tile2": dict(shape="tile2"),
+    "tile4": dict(shape="tile4"),
+    "tile4_wg": dict(shape="tile4", order="workgroup"),
+    "tile4_plain": dict(shape="tile4", policy="plain"),
+    "tile4_sc0sc1": dict(shape="tile4", policy="sc0sc1"),
+    "chunk256x1": dict(shape="chunk", threads=256, loads=1),
+    "chunk256x4": dict(shape="chunk", threads=256, loads=4),
+    "chunk256x8": dict(shape="chunk", threads=256, loads=8),
+    "chunk256x16": dict(shape="chunk", threads=256, loads=16),
+    "chunk512x4": dict(shape="chunk", threads=512, loads=4),
+    "chunk512x8": dict(shape="chunk", threads=512, loads=8),
+    "chunk1024x1": dict(shape="chunk", threads=1024, loads=1),
+    "chunk1024x4": dict(shape="chunk", threads=1024, loads=4),
+    "chunk256x8_lane": dict(shape="chunk", threads=256, loads=8, order="lane"),
+    "chunk256x8_wg": dict(shape="chunk", threads=256, loads=8, order="workgroup"),
+    "chunk1024x4_wg": dict(shape="chunk", threads=1024, loads=4, order="workgroup"),
+    "chunk256x8_persist1": dict(shape="chunk", threads=256, loads=8, persistent=1),
+    "chunk256x8_persist2": dict(shape="chunk", threads=256, loads=8, persistent=2),
+    "chunk256x8_persist4": dict(shape="chunk", threads=256, loads=8, persistent=4),
+    "chunk1024x4_persist1": dict(shape="chunk", threads=1024, loads=4, persistent=1),
+    "chunk256x8_plain": dict(shape="chunk", threads=256, loads=8, policy="plain"),
+    "chunk256x8_sc0sc1": dict(shape="chunk", threads=256, loads=8, policy="sc0sc1"),
+}
+# designs also run over consecutive slots (the plain-copy pattern)
+PROBE_CONTIGUOUS = ("tile1", "tile4", "chunk256x8", "chunk256x16", "chunk1024x4")
+
+
 def _elf_sections(elf: bytes):
     """(name, type, addr, offset, size, link) of every section of a 64-bit ELF."""
     import struct
@@ -616,7 +653,7 @@ class Bench:
         torch.cuda.synchronize()
         return g, n
 
-    def calibration(self, laps: int = 10) -> dict:
+    def calibration(self, laps: int = 10, only: tuple | None = None) -> dict:
         """The step's state traffic with no arithmetic, in several workgroup
         designs, over the same rotating row sets (the method of the PR #1139
         page, 'Numbers', widened to a sweep of designs; see gdn_traffic_probe).
@@ -626,6 +663,7 @@ class Bench:
         disjoint range each visit).  The hold designs keep every workgroup's
         stores until about the read phase's end (a fraction of the read bytes
         over 6.7 TB/s), which puts the whole launch's reads ahead of its writes.
+        `only`: just these PROBE_SWEEP designs over the step's slots.
         Returns {design: {us_mean, GBps, frac, bytes}}."""
         torch, gdn, dp = self.torch, self.gdn, self.dp
         sink = torch.zeros(1, device="cuda")
@@ -633,26 +671,34 @@ class Bench:
         tile_bytes = s.d_k * s.d_v * 4
         read_bytes = self.R * s.H_v * tile_bytes
         inplace = not self.twin
-        designs = [("read_only", "read", "slots", "tile1", 0.0), ("write_only", "write", "slots", "tile1", 0.0)]
         traffic = "inplace" if inplace else "copy"
-        for shape in ("tile1", "tile2", "tile4", "chunk256x16", "chunk256x8", "chunk256x1", "chunk1024x1"):
-            designs.append((f"{traffic}_slots_{shape}", traffic, "slots", shape, 0.0))
+        designs = [("read_only", "read", "slots", PROBE_SWEEP["tile1"], 0.0),
+                   ("write_only", "write", "slots", PROBE_SWEEP["tile1"], 0.0)]
+        for label, kw in PROBE_SWEEP.items():
+            designs.append((f"{traffic}_slots_{label}", traffic, "slots", kw, 0.0))
         for f in (0.9, 1.0, 1.1):
-            designs.append((f"{traffic}_slots_tile1_hold{f:.1f}", traffic, "slots", "tile1", f))
-        for shape in ("tile1", "chunk256x8", "chunk1024x1"):
-            designs.append((f"{traffic}_contiguous_{shape}", traffic, "contiguous", shape, 0.0))
+            designs.append((f"{traffic}_slots_tile1_hold{f:.1f}", traffic, "slots", PROBE_SWEEP["tile1"], f))
+        designs.append((f"{traffic}_slots_tile4_hold0.9", traffic, "slots", PROBE_SWEEP["tile4"], 0.9))
+        for label in PROBE_CONTIGUOUS:
+            designs.append((f"{traffic}_contiguous_{label}", traffic, "contiguous", PROBE_SWEEP[label], 0.0))
+        if only is not None:
+            designs = [(f"{traffic}_slots_{label}", traffic, "slots", PROBE_SWEEP[label], 0.0) for label in only]
         # consecutive-slot ranges, disjoint for every set: [1 + 2Rk, 1 + 2Rk + R) and the next R slots
         ranges = [(torch.tensor([1 + 2 * self.R * k], dtype=torch.int32, device="cuda"),
                    torch.tensor([1 + 2 * self.R * k + self.R], dtype=torch.int32, device="cuda"))
                   for k in range(self.nsets) if 1 + 2 * self.R * (k + 1) <= dp.N]
         out = {}
-        for name, tr, layout, shape, hold in designs:
+        for name, tr, layout, kw, hold in designs:
             if layout == "contiguous" and len(ranges) < min(self.nsets, 4):
+                continue
+            if kw["shape"] in ("tile2", "tile4") and (s.d_k, s.d_v) != (128, 128):
+                continue
+            if kw["shape"] == "chunk" and tile_bytes % (kw["threads"] * kw["loads"] * 16):
                 continue
             nsets = self.nsets if layout == "slots" else len(ranges)
             hold_ns = int(hold * read_bytes / 6.7e12 * 1e9)
 
-            def launch(i, tr=tr, layout=layout, shape=shape, hold_ns=hold_ns, nsets=nsets):
+            def launch(i, tr=tr, layout=layout, kw=kw, hold_ns=hold_ns, nsets=nsets):
                 if layout == "slots":
                     st = self.sets[i % nsets]
                     rd, wr = st["rd"], st["wr"]
@@ -660,8 +706,8 @@ class Bench:
                     rd, wr = ranges[i % nsets]
                 if not inplace and (i // nsets) % 2:
                     rd, wr = wr, rd
-                gdn.traffic_probe(dp.state, rd, wr, sink, traffic=tr, layout=layout, shape=shape, hold_ns=hold_ns,
-                                  rows=self.R if layout == "contiguous" else self.B)
+                gdn.traffic_probe(dp.state, rd, wr, sink, traffic=tr, layout=layout, hold_ns=hold_ns,
+                                  rows=self.R if layout == "contiguous" else self.B, **kw)
 
             reps = laps * nsets if nsets < 64 else 2 * nsets
             for i in range(min(nsets, 16)):
@@ -680,9 +726,10 @@ def ceiling_of(cal: dict, step_bytes: int, achieved_GBps: float) -> dict | None:
     the step's traffic: copies for twin writes, read-and-write-back in place),
     and the best over the step's own slots; with the step's time at each rate."""
     best = {}
-    for scope in ("any", "slots"):
+    for scope in ("any", "slots", "no_hold"):
         cands = [(v["GBps"], k) for k, v in cal.items()
-                 if not k.startswith(("read_only", "write_only")) and (scope == "any" or "_slots_" in k)]
+                 if not k.startswith(("read_only", "write_only")) and (scope != "slots" or "_slots_" in k)
+                 and (scope != "no_hold" or "_hold" not in k)]
         if not cands:
             return None
         g, k = max(cands)
@@ -690,17 +737,27 @@ def ceiling_of(cal: dict, step_bytes: int, achieved_GBps: float) -> dict | None:
                        "us_at_step_bytes": step_bytes / (g * 1e9) * 1e6, "step_fraction": achieved_GBps / g}
     out = dict(best["any"])
     out["on_the_steps_slots"] = best["slots"]
+    out["without_hold"] = best["no_hold"]
     out["note"] = ("best no-math copy design at the step's traffic (GB/s, so the step's own bytes can be priced at "
-                   "it); step_fraction = the step's achieved GB/s over the design's")
+                   "it); step_fraction = the step's achieved GB/s over the design's; without_hold: the best design "
+                   "whose stores are not held for a set time")
     return out
 
 
 SWEEP = [(b, m) for b in (1, 4, 16, 64, 128) for m in ("twin", "inplace")]
 
 
+# the no-math designs each sweep entry is held against (whole tiles for large
+# batches, small chunks that spread a few rows over many CUs for small ones)
+SWEEP_COPY = ("tile1", "tile4_wg", "chunk256x1", "chunk256x4", "chunk256x8")
+
+
 def run_sweep(dp: DevicePool, K: int = 130) -> dict:
     """Twin and in-place steps at 1, 4, 16, 64 and 128 rows (cold row sets), plus
-    the 64-row twin step hot (the same rows every step, labelled as such)."""
+    the 64-row twin step hot (the same rows every step, labelled as such).
+    Every cold entry carries the same run's fastest no-math copy of its state
+    traffic over the same row sets (SWEEP_COPY designs), and the step's time
+    over it."""
     out = {}
     for B, mode in SWEEP + [(64, "twin-hot")]:
         hot = mode.endswith("hot")
@@ -709,27 +766,36 @@ def run_sweep(dp: DevicePool, K: int = 130) -> dict:
         ms, _ = b.timed(max(K, 2 * min(b.nsets, 13)), False)
         _, us = b.timed(K, True)
         k = float(us.mean())
-        out[f"{B}_{mode}"] = {"rows": B, "write": "twin" if hot else mode, "cold": not hot,
-                              "us_per_step": ms * 1e3, "kernel_us_mean": k, "rows_per_s": B / (ms * 1e-3),
-                              "GBps": b.bytes / (k * 1e-6) / 1e9, "frac": b.bytes / (k * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                              "bytes": b.bytes}
+        e = {"rows": B, "write": "twin" if hot else mode, "cold": not hot,
+             "us_per_step": ms * 1e3, "kernel_us_mean": k, "rows_per_s": B / (ms * 1e-3),
+             "GBps": b.bytes / (k * 1e-6) / 1e9, "frac": b.bytes / (k * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+             "bytes": b.bytes}
+        if not hot:
+            cal = b.calibration(laps=6, only=SWEEP_COPY)
+            best = min(cal, key=lambda d: cal[d]["us_mean"])
+            e["copy"] = {"design": best, "us_mean": cal[best]["us_mean"], "bytes": cal[best]["bytes"],
+                         "step_over_copy": k / cal[best]["us_mean"]}
+        out[f"{B}_{mode}"] = e
         del b
     return out
 
 
 def run_floors(dp: DevicePool, K: int = 64) -> dict:
-    """The launch floor of small batches: an empty kernel and a kernel doing one
-    slot-index load then one tile load, back to back from the stream and from
-    a captured graph, beside the 1-row fused twin step the same two ways (the
-    PR #1139 page, 'Numbers', measured ~1.8 us a kernel inside a captured
-    graph on MI325X)."""
+    """The launch floor of small batches: an empty kernel, and a kernel that
+    loads one slot index and then that slot's first tile (a step's first two
+    dependent loads; the index and the tile cold: each launch takes the first
+    row of the next of the 1-row sets the 1-row step rotates over), back to
+    back from the stream and from a captured graph, beside the 1-row fused
+    twin step the same two ways (the PR #1139 page, 'Numbers', measured ~1.8
+    us a kernel inside a captured graph on MI325X)."""
     torch, gdn = dp.torch, dp.gdn
     sink = torch.zeros(1, device="cuda")
-    rd = torch.tensor([int(dp.read_slot[0])], dtype=torch.int32, device="cuda")
+    one = Bench(dp, mode="twin", B=1)
+    rds = [st["rd"] for st in one.sets]
     out = {}
     for shape in ("empty", "slot_load"):
         def launch(i, shape=shape):
-            gdn.traffic_probe(dp.state, rd, None, sink, traffic="read", shape=shape, rows=1)
+            gdn.traffic_probe(dp.state, rds[i % len(rds)], None, sink, traffic="read", shape=shape, rows=1)
         for i in range(8):
             launch(i)
         torch.cuda.synchronize()
@@ -745,6 +811,7 @@ def run_floors(dp: DevicePool, K: int = 64) -> dict:
         gms, _ = dp.time_launches(lambda i: g.replay(), 8, False)
         out[shape] = {"us_back_to_back": ms * 1e3, "us_events_mean": float(us.mean()), "us_graph": gms * 1e3 / K}
         del g
+    del one
     b = Bench(dp, mode="twin", B=1)
     b.warm(24)
     ms, _ = b.timed(max(K, 130), False)

@@ -46,13 +46,15 @@ class Dims(ctypes.Structure):
 
 class Probe(ctypes.Structure):
     """gdn_probe: a calibration design (see gdn_traffic_probe in include/gdn.h)."""
-    _fields_ = [(n, ctypes.c_int32) for n in ("traffic", "layout", "shape", "hold_ns")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("traffic", "layout", "shape", "hold_ns", "order", "threads", "loads",
+                                               "persistent", "policy")]
 
 
 # gdn_probe fields, by name
 PROBE_TRAFFIC = {"read": 0, "write": 1, "copy": 2, "inplace": 3}
-PROBE_SHAPES = {"tile1": 0, "tile2": 1, "tile4": 2, "chunk256x16": 3, "chunk256x8": 4, "chunk256x1": 5,
-                "chunk1024x1": 6, "empty": 7, "slot_load": 8}
+PROBE_SHAPES = {"tile1": 0, "tile2": 1, "tile4": 2, "chunk": 3, "empty": 4, "slot_load": 5}
+PROBE_ORDERS = {"stream": 0, "lane": 1, "workgroup": 2}
+PROBE_POLICIES = {"nt": 0, "plain": 1, "sc0sc1": 2}
 
 
 _lib = None
@@ -473,21 +475,25 @@ def slot_copy(state, conv_state, src_slots, dst_slots, *, H_k: int, stream=None)
 
 
 def traffic_probe(state, read_slot, write_slot, sink, *, traffic: str = "copy", layout: str = "slots",
-                  shape: str = "tile1", hold_ns: int = 0, rows: int | None = None, stream=None) -> None:
+                  shape: str = "tile1", hold_ns: int = 0, order: str = "stream", threads: int = 256, loads: int = 8,
+                  persistent: int = 0, policy: str = "nt", rows: int | None = None, stream=None) -> None:
     """The step's state traffic with no arithmetic in one workgroup design (see
     ``gdn_traffic_probe`` in include/gdn.h).
 
     traffic: "read", "write", "copy" (read slot -> write slot) or "inplace";
     layout: "slots" (row r's tiles at read_slot[r] / write_slot[r]) or
     "contiguous" (`rows` consecutive slots from read_slot[0] to write_slot[0]);
-    shape: one of PROBE_SHAPES; rows defaults to the length of read_slot."""
+    shape: one of PROBE_SHAPES; order: one of PROBE_ORDERS (when stores may
+    go); policy: one of PROBE_POLICIES; threads, loads and persistent set the
+    "chunk" shape; rows defaults to the length of read_slot."""
     torch = _torch()
     _contig(_dev(state, "state", torch.float32), "state")
     _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
     _contig(_dev(write_slot, "write_slot", torch.int32, allow_none=True), "write_slot")
     _contig(_dev(sink, "sink", torch.float32), "sink")
-    if traffic not in PROBE_TRAFFIC or layout not in ("slots", "contiguous") or shape not in PROBE_SHAPES:
-        raise ValueError(f"unknown probe design {traffic!r}, {layout!r}, {shape!r}")
+    if (traffic not in PROBE_TRAFFIC or layout not in ("slots", "contiguous") or shape not in PROBE_SHAPES
+            or order not in PROBE_ORDERS or policy not in PROBE_POLICIES):
+        raise ValueError(f"unknown probe design {traffic!r}, {layout!r}, {shape!r}, {order!r}, {policy!r}")
     if state.dim() != 4 or read_slot.dim() != 1:
         raise ValueError("state must be [N][H][d_k][d_v] and read_slot [B]")
     N, H, d_k, d_v = state.shape
@@ -499,7 +505,8 @@ def traffic_probe(state, read_slot, write_slot, sink, *, traffic: str = "copy", 
         raise ValueError("the slot arrays must hold an entry for every row")
     if layout == "contiguous" and (read_slot.shape[0] < 1 or (writes and write_slot.shape[0] < 1)):
         raise ValueError("the contiguous layout takes its first slots from read_slot[0] and write_slot[0]")
-    pr = Probe(PROBE_TRAFFIC[traffic], 0 if layout == "slots" else 1, PROBE_SHAPES[shape], int(hold_ns))
+    pr = Probe(PROBE_TRAFFIC[traffic], 0 if layout == "slots" else 1, PROBE_SHAPES[shape], int(hold_ns),
+               PROBE_ORDERS[order], int(threads), int(loads), int(persistent), PROBE_POLICIES[policy])
     dev = _device(state, read_slot, write_slot, sink)
     with _on(dev):
         _check("gdn_traffic_probe", lib().gdn_traffic_probe(

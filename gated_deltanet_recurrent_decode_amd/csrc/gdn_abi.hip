@@ -426,8 +426,9 @@ gdn_status gdn_traffic_probe(const gdn_probe *probe, int32_t B, int32_t H, int32
     if (!probe || !state || !read_slot || !sink)
         return GDN_ERR_NULL;
     const gdn_probe pr = *probe;
-    if (pr.traffic < 0 || pr.traffic > 3 || pr.layout < 0 || pr.layout > 1 || pr.shape < 0 || pr.shape > 8 ||
-        pr.hold_ns < 0 || pr.hold_ns > 1000000)
+    if (pr.traffic < 0 || pr.traffic > 3 || pr.layout < 0 || pr.layout > 1 || pr.shape < 0 || pr.shape > 5 ||
+        pr.hold_ns < 0 || pr.hold_ns > 1000000 || pr.order < 0 || pr.order > 2 || pr.policy < 0 ||
+        pr.policy > 2 || pr.persistent < 0 || pr.persistent > 8 || (pr.persistent > 0 && pr.hold_ns > 0))
         return GDN_ERR_SHAPE;
     const bool uses_write = pr.traffic == 1 || pr.traffic == 2;
     if (uses_write && !write_slot)
@@ -439,14 +440,19 @@ gdn_status gdn_traffic_probe(const gdn_probe *probe, int32_t B, int32_t H, int32
     if ((pr.shape == 1 || pr.shape == 2) && (d_k != 128 || d_v != 128))
         return GDN_ERR_UNSUPPORTED;
     const int64_t tile_bytes = (int64_t)d_k * d_v * 4;
-    static const int64_t chunk_bytes[4] = {256 * 16 * 16, 256 * 8 * 16, 256 * 16, 1024 * 16};
-    if (pr.shape >= 3 && pr.shape <= 6 && tile_bytes % chunk_bytes[pr.shape - 3] != 0)
-        return GDN_ERR_UNSUPPORTED;
+    if (pr.shape == 3) {
+        const bool threads_ok = pr.threads == 256 || pr.threads == 512 || pr.threads == 1024;
+        const bool loads_ok = pr.loads == 1 || pr.loads == 4 || pr.loads == 8 || pr.loads == 16;
+        if (!threads_ok || !loads_ok || (int64_t)pr.threads * pr.loads > 4096)
+            return GDN_ERR_SHAPE;
+        if (tile_bytes % ((int64_t)pr.threads * pr.loads * 16) != 0)
+            return GDN_ERR_UNSUPPORTED;
+    }
     if (pr.layout == 1 && (int64_t)B * H * tile_bytes > INT32_MAX)
         return GDN_ERR_SHAPE;
     if (!aligned(state, 16))
         return GDN_ERR_UNSUPPORTED;
-    if (B == 0 && pr.shape != 7)
+    if (B == 0 && pr.shape != 4)
         return GDN_OK;
     gdn::ProbeParams p{};
     p.state = state;
@@ -461,6 +467,11 @@ gdn_status gdn_traffic_probe(const gdn_probe *probe, int32_t B, int32_t H, int32
     p.layout = pr.layout;
     p.shape = pr.shape;
     p.hold_ticks = (uint32_t)(pr.hold_ns / 10); // the constant clock ticks at 100 MHz
+    p.order = pr.order;
+    p.threads = pr.threads;
+    p.loads = pr.loads;
+    p.persistent = pr.persistent;
+    p.policy = pr.policy;
     return from_hip(gdn::launch_traffic_probe(p, d_k, d_v, stream));
 }
 

@@ -56,6 +56,10 @@ struct ProbeParams {
     int layout;          // 0 the rows' slots, 1 consecutive slots from read_slot[0] / write_slot[0]
     int shape;           // workgroup design (see gdn_probe in gdn.h)
     uint32_t hold_ticks; // 0, or: stores wait until this many 100 MHz ticks after the workgroup started
+    int order;           // 0 each store after its own load, 1 a lane's loads first, 2 the workgroup's loads first
+    int threads, loads;  // chunk design: workgroup size, 16-byte loads a lane
+    int persistent;      // chunk design: 0 one chunk a workgroup, k: k workgroups a CU walking the chunks
+    int policy;          // 0 streaming (nt), 1 plain, 2 system scope (sc0 sc1)
 };
 
 // Zero (src == null) or copy (src[i] -> dst[i]) whole slots of the pool.

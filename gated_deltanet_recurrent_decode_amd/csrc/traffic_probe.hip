@@ -1,18 +1,21 @@
 // traffic_probe.hip -- calibration kernels: the decode step's state traffic
-// with no arithmetic, in several workgroup designs (gfx950).
+// with no arithmetic, in many workgroup designs (gfx950).
 //
 // The method of mstar PR #1139, "Numbers": a kernel with the GDN step's reads
 // and writes and no math, plus its read-only and write-only halves, gives the
 // practical bandwidth ceiling of the step's access pattern.  Here the same
-// traffic can be taken by several designs, so that the ceiling is the best of
+// traffic can be taken by many designs, so that the ceiling is the best of
 // them rather than one kernel:
 //   - tile designs: the fused step's thread layout (a wave holds the eight row
 //     groups of 32 columns, 256 threads a 128-wide tile), one, two or four
-//     whole tiles a workgroup; with more than one, every wave waits for the
-//     whole workgroup's loads before any store, as the step does;
-//   - chunk designs: plain one-shot copies, each workgroup moving one
-//     contiguous chunk of a tile (256 threads x 16, 8 or 1 16-byte loads a
-//     lane, or 1024 threads x 1);
+//     whole tiles a workgroup;
+//   - chunk designs: plain copies of chunks of threads x loads x 16 bytes, a
+//     workgroup of 256, 512 or 1024 threads with 1, 4, 8 or 16 16-byte loads
+//     in flight a lane, one chunk a workgroup or a persistent grid of k
+//     workgroups a compute unit walking the chunks;
+//   - for both: stores each as soon as its own load is in, or after all of a
+//     lane's loads, or after all of the workgroup's loads; streaming, plain or
+//     system-scope cache policy;
 //   - either over the step's own slots (tile t of row r at slot read_slot[r])
 //     or over contiguous slots (B consecutive slots from read_slot[0], written
 //     to B consecutive slots from write_slot[0]);
@@ -33,9 +36,22 @@ namespace gdn {
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-// Cache-policy bits as the step uses them: streaming loads and stores.
-constexpr int kProbeLoad = 2;
-constexpr int kProbeStore = 2;
+// Cache-policy bits of policy POL (gfx950 buffer instructions: 1 sc0, 2 nt,
+// 16 sc1): streaming as the step's state accesses, plain, or system scope.
+template <int POL>
+constexpr int probe_aux() { return POL == 0 ? 2 : POL == 1 ? 0 : 17; }
+
+// The stores of a lane (order 1) or of the workgroup (order 2) wait for all
+// of its loads; order 0 lets each store go as soon as its own load is in.
+// `order` is uniform over the workgroup.
+__device__ __forceinline__ void probe_order(int order)
+{
+    if (order >= 1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        if (order == 2)
+            __builtin_amdgcn_s_barrier();
+    }
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(void *base, uint32_t bytes)
 {
@@ -88,9 +104,10 @@ __device__ __forceinline__ void probe_hold(uint64_t t0, uint32_t hold)
 // Tile designs: TPW whole d_k x d_v tiles a workgroup, 2 d_v threads a tile,
 // at the step's occupancy (its registers allow four waves a SIMD; the launch
 // reserves LDS so that no more workgroups share a CU than the step's do).
-template <int DK, int DV, int TPW>
+template <int DK, int DV, int TPW, int POL>
 __global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
 {
+    constexpr int kProbeLoad = probe_aux<POL>(), kProbeStore = probe_aux<POL>();
     constexpr int RG = 8, RPT = DK / RG, NTS = 2 * DV;
     static_assert(DV % 32 == 0, "a wave holds 32 columns");
     constexpr uint32_t TILE = (uint32_t)DK * DV * 4u;
@@ -131,11 +148,7 @@ __global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
             p.sink[0] = (float)acc;
         return;
     }
-    if constexpr (TPW > 1) {
-        // as the step: every wave of the workgroup has its data before any stores
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-    }
+    probe_order(p.order);
     probe_hold(t0, p.hold_ticks);
     // stores straight from the registers the loads filled: staging the data
     // through other registers made the compiler write a staging register
@@ -145,49 +158,55 @@ __global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
         __builtin_amdgcn_raw_buffer_store_b128(s[m], wr, voff, m * RG * DV * 4, kProbeStore);
 }
 
-// Chunk designs: workgroup c moves chunk c of NTH * L * 16 bytes, thread i
-// the 16-byte elements i, i + NTH, ... of it (a wave instruction covers 1 KiB).
-template <int NTH, int L>
+// Chunk designs: chunk c of NTH * L * 16 bytes, thread i the 16-byte elements
+// i, i + NTH, ... of it (a wave instruction covers 1 KiB).  A one-shot grid
+// has a workgroup a chunk; a persistent grid walks the chunks in strides of
+// its size (the chunk index is uniform, so every branch here is too).
+template <int NTH, int L, int POL>
 __global__ __launch_bounds__(NTH) void probe_chunk_kernel(ProbeParams p, uint32_t tile_bytes)
 {
+    constexpr int kProbeLoad = probe_aux<POL>(), kProbeStore = probe_aux<POL>();
     constexpr uint32_t CH = (uint32_t)NTH * L * 16u;
     const int per = (int)(tile_bytes / CH);
-    const int c = blockIdx.x;
-    size_t so = 0, dof = 0;
-    const bool ok = c < p.B * p.H * per && probe_tile(p, c / per, tile_bytes, so, dof);
-    const size_t part = (size_t)(c % per) * CH;
-    char *pool = reinterpret_cast<char *>(p.state);
-    const __amdgpu_buffer_rsrc_t rd = probe_rsrc(pool + so + part, ok ? CH : 0u);
-    const __amdgpu_buffer_rsrc_t wr = probe_rsrc(pool + dof + part, ok ? CH : 0u);
+    const int nch = p.B * p.H * per;
     const uint32_t vo = threadIdx.x * 16u;
-    if (p.traffic == 1) { // write only: ones
+    char *pool = reinterpret_cast<char *>(p.state);
+    for (int c = blockIdx.x; c < nch; c += gridDim.x) {
+        size_t so = 0, dof = 0;
+        const bool ok = probe_tile(p, c / per, tile_bytes, so, dof);
+        const size_t part = (size_t)(c % per) * CH;
+        const __amdgpu_buffer_rsrc_t rd = probe_rsrc(pool + so + part, ok ? CH : 0u);
+        const __amdgpu_buffer_rsrc_t wr = probe_rsrc(pool + dof + part, ok ? CH : 0u);
+        if (p.traffic == 1) { // write only: ones
+            const uint64_t t0 = probe_clock(p.hold_ticks);
+            probe_hold(t0, p.hold_ticks);
+            const unsigned one = __float_as_uint(p.one);
+#pragma unroll
+            for (int m = 0; m < L; ++m)
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{one, one, one, one}, wr, vo, m * NTH * 16, kProbeStore);
+            continue;
+        }
+        u32x4 v[L];
+#pragma unroll
+        for (int m = 0; m < L; ++m)
+            v[m] = __builtin_amdgcn_raw_buffer_load_b128(rd, vo, m * NTH * 16, kProbeLoad);
+        __builtin_amdgcn_sched_barrier(0);
         const uint64_t t0 = probe_clock(p.hold_ticks);
+        if (p.traffic == 0) {
+            unsigned acc = 0;
+#pragma unroll
+            for (int m = 0; m < L; ++m)
+                acc += v[m].x ^ v[m].y ^ v[m].z ^ v[m].w;
+            if (acc == 0x9e3779b9u && p.one == 3.0f)
+                p.sink[0] = (float)acc;
+            continue;
+        }
+        probe_order(p.order);
         probe_hold(t0, p.hold_ticks);
-        const unsigned one = __float_as_uint(p.one);
 #pragma unroll
         for (int m = 0; m < L; ++m)
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{one, one, one, one}, wr, vo, m * NTH * 16, kProbeStore);
-        return;
+            __builtin_amdgcn_raw_buffer_store_b128(v[m], wr, vo, m * NTH * 16, kProbeStore);
     }
-    u32x4 v[L];
-#pragma unroll
-    for (int m = 0; m < L; ++m)
-        v[m] = __builtin_amdgcn_raw_buffer_load_b128(rd, vo, m * NTH * 16, kProbeLoad);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint64_t t0 = probe_clock(p.hold_ticks);
-    if (p.traffic == 0) {
-        unsigned acc = 0;
-#pragma unroll
-        for (int m = 0; m < L; ++m)
-            acc += v[m].x ^ v[m].y ^ v[m].z ^ v[m].w;
-        if (acc == 0x9e3779b9u && p.one == 3.0f)
-            p.sink[0] = (float)acc;
-        return;
-    }
-    probe_hold(t0, p.hold_ticks);
-#pragma unroll
-    for (int m = 0; m < L; ++m)
-        __builtin_amdgcn_raw_buffer_store_b128(v[m], wr, vo, m * NTH * 16, kProbeStore);
 }
 
 // The launch floor: a kernel that does nothing.
@@ -197,32 +216,89 @@ __global__ __launch_bounds__(64) void probe_empty_kernel(ProbeParams p)
         p.sink[0] = 1.0f;
 }
 
-// The small-batch floor: load a slot index, then one 16-byte piece a lane of
-// that slot's first tile (a dependent pair of loads, as every step starts).
-__global__ __launch_bounds__(256) void probe_slot_load_kernel(ProbeParams p, uint32_t tile_bytes)
+// The small-batch floor: load a slot index, then that slot's first head tile
+// (256 threads, 16-byte streaming loads; a dependent pair of loads, as every
+// step starts).
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void probe_slot_load_kernel(ProbeParams p)
 {
+    constexpr uint32_t TILE = (uint32_t)DK * DV * 4u;
+    constexpr int L = (int)(TILE / (256u * 16u)); // 16-byte loads a lane, all in flight at once
     const int rs = p.read_slot[0];
     const bool ok = rs >= 1 && rs < p.N;
     char *pool = reinterpret_cast<char *>(p.state);
-    const __amdgpu_buffer_rsrc_t rd = probe_rsrc(pool + (ok ? (size_t)rs * p.H * tile_bytes : 0), ok ? 4096u : 0u);
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rd, threadIdx.x * 16u, 0, kProbeLoad);
-    if ((v.x ^ v.y ^ v.z ^ v.w) == 0x9e3779b9u && p.one == 3.0f)
+    const __amdgpu_buffer_rsrc_t rd = probe_rsrc(pool + (ok ? (size_t)rs * p.H * TILE : 0), ok ? TILE : 0u);
+    u32x4 v[L];
+#pragma unroll
+    for (int m = 0; m < L; ++m)
+        v[m] = __builtin_amdgcn_raw_buffer_load_b128(rd, threadIdx.x * 16u, m * 4096, probe_aux<0>());
+    unsigned acc = 0;
+#pragma unroll
+    for (int m = 0; m < L; ++m)
+        acc += v[m].x ^ v[m].y ^ v[m].z ^ v[m].w;
+    if (acc == 0x9e3779b9u && p.one == 3.0f) // never true: keeps the loads alive
         p.sink[0] = 1.0f;
 }
 
-template <int NTH, int L>
+// Compute units of the current device (256 on MI355X).
+static int probe_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+template <int NTH, int L, int POL>
 static hipError_t launch_chunk(ProbeParams q, uint32_t tile_bytes, hipStream_t stream)
 {
     constexpr uint32_t CH = (uint32_t)NTH * L * 16u;
     if (tile_bytes % CH != 0)
         return hipErrorInvalidValue;
     const long long chunks = (long long)q.B * q.H * (tile_bytes / CH);
+    long long grid = chunks;
+    if (q.persistent > 0) {
+        const long long g = (long long)probe_cus() * q.persistent;
+        grid = g < chunks ? g : chunks;
+    }
+    if (grid <= 0)
+        return hipSuccess;
     void *args[] = {&q, &tile_bytes};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&probe_chunk_kernel<NTH, L>), dim3((unsigned)chunks),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&probe_chunk_kernel<NTH, L, POL>), dim3((unsigned)grid),
                            dim3(NTH), args, 0, stream);
 }
 
-template <int DK, int DV, int TPW>
+template <int NTH, int POL>
+static hipError_t chunk_loads(const ProbeParams &q, uint32_t tile_bytes, hipStream_t stream)
+{
+    switch (q.loads) {
+    case 1: return launch_chunk<NTH, 1, POL>(q, tile_bytes, stream);
+    case 4: return launch_chunk<NTH, 4, POL>(q, tile_bytes, stream);
+    case 8:
+        if constexpr (NTH <= 512)
+            return launch_chunk<NTH, 8, POL>(q, tile_bytes, stream);
+        break;
+    case 16:
+        if constexpr (NTH <= 256)
+            return launch_chunk<NTH, 16, POL>(q, tile_bytes, stream);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int POL>
+static hipError_t chunk_design(const ProbeParams &q, uint32_t tile_bytes, hipStream_t stream)
+{
+    switch (q.threads) {
+    case 256: return chunk_loads<256, POL>(q, tile_bytes, stream);
+    case 512: return chunk_loads<512, POL>(q, tile_bytes, stream);
+    case 1024: return chunk_loads<1024, POL>(q, tile_bytes, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DK, int DV, int TPW, int POL>
 static hipError_t launch_tiles(ProbeParams q, hipStream_t stream)
 {
     const long long tiles = (long long)q.B * q.H;
@@ -230,34 +306,47 @@ static hipError_t launch_tiles(ProbeParams q, hipStream_t stream)
     // the step's 128 x 128 kernels fit four 256-thread tiles on a CU (registers):
     // reserve a quarter of the 160 KiB LDS per tile so the probe fits no more
     const size_t lds = DK == 128 && DV == 128 && TPW < 4 ? (size_t)TPW * 40 * 1024 : 0;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&probe_tile_kernel<DK, DV, TPW>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&probe_tile_kernel<DK, DV, TPW, POL>),
                            dim3((unsigned)((tiles + TPW - 1) / TPW)), dim3(2 * DV * TPW), args, lds, stream);
+}
+
+template <int DK, int DV, int POL>
+static hipError_t launch_probe_pol(const ProbeParams &p, hipStream_t stream)
+{
+    const uint32_t tile_bytes = (uint32_t)DK * DV * 4u;
+    switch (p.shape) {
+    case 0: return launch_tiles<DK, DV, 1, POL>(p, stream);
+    case 1:
+        if constexpr (DK == 128 && DV == 128)
+            return launch_tiles<DK, DV, 2, POL>(p, stream);
+        break;
+    case 2:
+        if constexpr (DK == 128 && DV == 128)
+            return launch_tiles<DK, DV, 4, POL>(p, stream);
+        break;
+    case 3: return chunk_design<POL>(p, tile_bytes, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int DK, int DV>
 static hipError_t launch_probe(const ProbeParams &p, hipStream_t stream)
 {
-    const uint32_t tile_bytes = (uint32_t)DK * DV * 4u;
     ProbeParams q = p;
-    switch (p.shape) {
-    case 0: return launch_tiles<DK, DV, 1>(q, stream);
-    case 1: return DK == 128 && DV == 128 ? launch_tiles<DK, DV, 2>(q, stream) : hipErrorInvalidValue;
-    case 2: return DK == 128 && DV == 128 ? launch_tiles<DK, DV, 4>(q, stream) : hipErrorInvalidValue;
-    case 3: return launch_chunk<256, 16>(q, tile_bytes, stream);
-    case 4: return launch_chunk<256, 8>(q, tile_bytes, stream);
-    case 5: return launch_chunk<256, 1>(q, tile_bytes, stream);
-    case 6: return launch_chunk<1024, 1>(q, tile_bytes, stream);
-    case 7: {
+    if (p.shape == 4) {
         void *args[] = {&q};
         return hipLaunchKernel(reinterpret_cast<const void *>(&probe_empty_kernel), dim3(1), dim3(64), args, 0,
                                stream);
     }
-    case 8: {
-        uint32_t tb = tile_bytes;
-        void *args[] = {&q, &tb};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&probe_slot_load_kernel), dim3(1), dim3(256), args, 0,
-                               stream);
+    if (p.shape == 5) {
+        void *args[] = {&q};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&probe_slot_load_kernel<DK, DV>), dim3(1), dim3(256),
+                               args, 0, stream);
     }
+    switch (p.policy) {
+    case 0: return launch_probe_pol<DK, DV, 0>(p, stream);
+    case 1: return launch_probe_pol<DK, DV, 1>(p, stream);
+    case 2: return launch_probe_pol<DK, DV, 2>(p, stream);
     }
     return hipErrorInvalidValue;
 }

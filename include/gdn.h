@@ -337,28 +337,37 @@ const char *gdn_status_string(gdn_status status);
  *                   unless both ranges lie in [1, N))
  *   probe->shape    0, 1, 2: the fused step's thread layout (a wave holds the
  *                   eight row groups of 32 columns, 2 d_v threads a tile), 1,
- *                   2 or 4 whole tiles a workgroup (2 and 4: d_k = d_v = 128),
- *                   stores after all of the workgroup's loads when more than
- *                   one; 3, 4, 5, 6: plain chunks, one a workgroup, 256
- *                   threads x 16, 8 or 1 and 1024 threads x 1 16-byte loads a
- *                   lane (the tile must be a multiple of the chunk);
- *                   7: an empty kernel (the launch floor);
- *                   8: one workgroup loads read_slot[0], then 16 bytes a lane
- *                   of that slot's first tile (the floor of a step's first
- *                   dependent loads)
+ *                   2 or 4 whole tiles a workgroup (2 and 4: d_k = d_v = 128);
+ *                   3: plain copy chunks of threads x loads x 16 bytes, as
+ *                   set by the fields below (the tile must be a multiple of
+ *                   the chunk);
+ *                   4: an empty kernel (the launch floor);
+ *                   5: one workgroup loads read_slot[0], then that slot's
+ *                   first tile (the floor of a step's first dependent loads)
  *   probe->hold_ns  0, or: every workgroup holds its stores until this long
  *                   after it started (at most 1 ms), which puts the launch's
  *                   reads ahead of its writes when long enough; for
- *                   measurement only
- * Loads and stores stream (nt), as the step's state accesses do.  sink [1]
- * fp32 receives nothing in practice; it keeps read-only loads alive.
+ *                   measurement only (not with a persistent grid)
+ *   probe->order    0: each store goes as soon as its own load is in;
+ *                   1: a lane's stores wait for all of its loads;
+ *                   2: a workgroup's stores wait for all of its loads
+ *                   (shapes 0-3)
+ *   probe->threads  shape 3: workgroup size, 256, 512 or 1024
+ *   probe->loads    shape 3: 16-byte loads a lane, 1, 4, 8 or 16, with
+ *                   threads x loads at most 4096 (64 KiB a chunk)
+ *   probe->persistent  shape 3: 0, one chunk a workgroup; k in 1..8, k
+ *                   workgroups a compute unit walking the chunks in turn
+ *   probe->policy   shapes 0-3: 0 streaming loads and stores (nt, as the
+ *                   step's state accesses), 1 plain, 2 system scope (sc0 sc1)
+ * sink [1] fp32 receives nothing in practice; it keeps read-only loads alive.
  * write_slot is required for traffic 1 and 2, ignored otherwise.  Statuses:
  * GDN_ERR_NULL, GDN_ERR_SHAPE (B < 0, H or N < 1, a value out of range, a
  * contiguous range over 2 GiB), GDN_ERR_UNSUPPORTED (head dims not 64/128, a
- * shape not built for them, misaligned state).
+ * shape or chunk not built for them, misaligned state).
  */
 typedef struct gdn_probe {
     int32_t traffic, layout, shape, hold_ns;
+    int32_t order, threads, loads, persistent, policy;
 } gdn_probe;
 
 gdn_status gdn_traffic_probe(const gdn_probe *probe, int32_t B, int32_t H, int32_t d_k, int32_t d_v, int32_t N,

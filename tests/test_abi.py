@@ -213,20 +213,30 @@ def test_slot_commit_and_probe_validation():
     L = gdn.lib()
     assert L.slot_commit(None, FAKE, 4, None) == NULL
     assert L.slot_commit(FAKE, FAKE, -1, None) == SHAPE
-    def pr(traffic=2, layout=0, shape=0, hold=0):
-        return ctypes.byref(gdn.Probe(traffic, layout, shape, hold))
+    def pr(traffic=2, layout=0, shape=0, hold=0, order=0, threads=256, loads=8, persistent=0, policy=0):
+        return ctypes.byref(gdn.Probe(traffic, layout, shape, hold, order, threads, loads, persistent, policy))
     assert L.gdn_traffic_probe(None, 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == NULL
     assert L.gdn_traffic_probe(pr(2), 4, 4, 64, 64, 9, FAKE, FAKE, None, FAKE, None) == NULL      # copy needs writes
     assert L.gdn_traffic_probe(pr(1), 4, 4, 64, 64, 9, FAKE, FAKE, None, FAKE, None) == NULL
     assert L.gdn_traffic_probe(pr(4), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE     # no such traffic
     assert L.gdn_traffic_probe(pr(layout=2), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
-    assert L.gdn_traffic_probe(pr(shape=9), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(shape=6), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(order=3), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(policy=3), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(shape=3, persistent=9), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(shape=3, persistent=1, hold=100), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE,
+                               None) == SHAPE  # holds are for one-shot grids
+    assert L.gdn_traffic_probe(pr(shape=3, threads=384), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(shape=3, loads=2), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.gdn_traffic_probe(pr(shape=3, threads=512, loads=16), 4, 4, 128, 128, 9, FAKE, FAKE, FAKE, FAKE,
+                               None) == SHAPE  # 128 KiB chunks: over 64 KiB
     assert L.gdn_traffic_probe(pr(hold=-1), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
     assert L.gdn_traffic_probe(pr(hold=2000000), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
     assert L.gdn_traffic_probe(pr(layout=1), 40000, 4, 128, 128, 9, FAKE, FAKE, FAKE, FAKE, None) == SHAPE  # > 2 GiB
     assert L.gdn_traffic_probe(pr(0), 4, 4, 96, 64, 9, FAKE, FAKE, None, FAKE, None) == UNSUPPORTED
     assert L.gdn_traffic_probe(pr(shape=1), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED  # 128 only
-    assert L.gdn_traffic_probe(pr(shape=3), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED  # chunk > tile
+    assert L.gdn_traffic_probe(pr(shape=3, loads=16), 4, 4, 64, 64, 9, FAKE, FAKE, FAKE, FAKE,
+                               None) == UNSUPPORTED  # a 64 KiB chunk over a 16 KiB tile
     assert L.gdn_traffic_probe(pr(), 4, 4, 64, 64, 9, ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, None) == UNSUPPORTED
 
 

@@ -85,9 +85,17 @@ def test_ceiling_is_the_fastest_copy_design():
     cal = {"read_only": {"GBps": 7000.0, "us_mean": 9.0},
            "copy_slots_tile1": {"GBps": 5000.0, "us_mean": 26.8},
            "copy_slots_tile2": {"GBps": 5300.0, "us_mean": 25.3},
-           "copy_contiguous_chunk256x8": {"GBps": 5700.0, "us_mean": 23.5}}
+           "copy_contiguous_chunk256x8": {"GBps": 5700.0, "us_mean": 23.5},
+           "copy_slots_tile1_hold0.9": {"GBps": 5600.0, "us_mean": 24.0}}
     c = bench.ceiling_of(cal, 140_000_000, 5200.0)
     assert c["design"] == "copy_contiguous_chunk256x8"
-    assert c["on_the_steps_slots"]["design"] == "copy_slots_tile2"
+    assert c["on_the_steps_slots"]["design"] == "copy_slots_tile1_hold0.9"
+    assert c["without_hold"]["design"] == "copy_contiguous_chunk256x8"
+    cal["copy_contiguous_chunk256x8"]["GBps"] = 5500.0
+    c2 = bench.ceiling_of(cal, 140_000_000, 5200.0)
+    assert c2["design"] == "copy_slots_tile1_hold0.9"
+    assert c2["without_hold"]["design"] == "copy_contiguous_chunk256x8"
+    assert abs(c2["without_hold"]["step_fraction"] - 5200.0 / 5500.0) < 1e-12
+    cal["copy_contiguous_chunk256x8"]["GBps"] = 5700.0
     assert abs(c["us_at_step_bytes"] - 140_000_000 / 5.7e12 * 1e6) < 1e-9
     assert abs(c["step_fraction"] - 5200.0 / 5700.0) < 1e-12

@@ -731,14 +731,31 @@ def test_graph_replay_of_step_and_commit_matches_eager(gdn, torch):
 
 # ------------------------------------------------------------------ calibration probe
 
-@pytest.mark.parametrize("shape", ["tile1", "tile2", "tile4", "chunk256x16", "chunk256x8", "chunk256x1",
-                                   "chunk1024x1"])
-def test_traffic_probe_moves_the_tiles(gdn, torch, shape):
+PROBE_DESIGNS = {
+    "tile1": dict(shape="tile1"),
+    "tile1-workgroup-sc0sc1": dict(shape="tile1", order="workgroup", policy="sc0sc1"),
+    "tile2-workgroup": dict(shape="tile2", order="workgroup"),
+    "tile4": dict(shape="tile4"),
+    "tile4-lane-plain": dict(shape="tile4", order="lane", policy="plain"),
+    "chunk256x16": dict(shape="chunk", threads=256, loads=16),
+    "chunk256x4-lane": dict(shape="chunk", threads=256, loads=4, order="lane"),
+    "chunk256x1": dict(shape="chunk", threads=256, loads=1),
+    "chunk512x8-workgroup": dict(shape="chunk", threads=512, loads=8, order="workgroup"),
+    "chunk1024x4-plain": dict(shape="chunk", threads=1024, loads=4, policy="plain"),
+    "chunk1024x1-sc0sc1": dict(shape="chunk", threads=1024, loads=1, policy="sc0sc1"),
+    "chunk256x8-persistent2": dict(shape="chunk", threads=256, loads=8, persistent=2),
+}
+
+
+@pytest.mark.parametrize("design", list(PROBE_DESIGNS))
+def test_traffic_probe_moves_the_tiles(gdn, torch, design):
     """Every calibration design moves exactly the step's tiles: a copy puts each
     read tile in its write slot, write-only fills the write slots, read-only and
     in-place traffic leave the pool as it was, and nothing else changes; the
     contiguous layout copies consecutive slots and is a no-op past the pool."""
     t = torch
+    kw = PROBE_DESIGNS[design]
+    hold = 0 if kw.get("persistent") else 2000
     case = gi.small(B=5, T=1, H_k=2, H_v=2, d=128, N=15)
     pool = case.pools[0]
     dp = H.DevPool(pool)
@@ -747,30 +764,50 @@ def test_traffic_probe_moves_the_tiles(gdn, torch, shape):
     wr = [int(x) for x in pool.write_slot]
     others = [sl for sl in range(15) if sl not in wr]
     before = dp.state.clone()
-    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="copy", shape=shape)
+    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="copy", **kw)
     t.cuda.synchronize()
     assert t.equal(dp.state[wr], before[rd])
     assert t.equal(dp.state[others], before[others])
-    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="write", shape=shape, hold_ns=2000)
+    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="write", hold_ns=hold, **kw)
     t.cuda.synchronize()
     assert bool((dp.state[wr] == 1.0).all())
     assert t.equal(dp.state[others], before[others])
     mid = dp.state.clone()
-    gdn.traffic_probe(dp.state, dp.rd, None, sink, traffic="inplace", shape=shape)
-    gdn.traffic_probe(dp.state, dp.rd, None, sink, traffic="read", shape=shape)
+    gdn.traffic_probe(dp.state, dp.rd, None, sink, traffic="inplace", **kw)
+    gdn.traffic_probe(dp.state, dp.rd, None, sink, traffic="read", **kw)
     t.cuda.synchronize()
     assert t.equal(mid, dp.state)
     assert float(sink[0]) == 0.0
     base = t.tensor([2, 7], dtype=t.int32, device="cuda")
-    gdn.traffic_probe(dp.state, base[0:1], base[1:2], sink, traffic="copy", layout="contiguous", shape=shape,
-                      rows=3)   # slots 2..4 -> 7..9
+    gdn.traffic_probe(dp.state, base[0:1], base[1:2], sink, traffic="copy", layout="contiguous", rows=3,
+                      **kw)   # slots 2..4 -> 7..9
     t.cuda.synchronize()
     assert t.equal(dp.state[7:10], mid[2:5])
     assert t.equal(dp.state[:7], mid[:7]) and t.equal(dp.state[10:], mid[10:])
-    gdn.traffic_probe(dp.state, base[1:2], base[0:1], sink, traffic="copy", layout="contiguous", shape=shape,
-                      rows=9)   # 7..15 runs past N = 15: no-op
+    gdn.traffic_probe(dp.state, base[1:2], base[0:1], sink, traffic="copy", layout="contiguous", rows=9,
+                      **kw)   # 7..15 runs past N = 15: no-op
     t.cuda.synchronize()
     assert t.equal(dp.state[:7], mid[:7])
+
+
+def test_persistent_probe_walks_every_chunk(gdn, torch):
+    """A persistent grid smaller than the chunk count (one 256-thread
+    workgroup a CU over 40 rows x 4 heads in 4 KiB chunks: 2560 chunks) still
+    copies every tile once and touches nothing else."""
+    t = torch
+    case = gi.small(B=40, T=1, H_k=4, H_v=4, d=128)
+    pool = case.pools[0]
+    dp = H.DevPool(pool)
+    sink = t.zeros(1, device="cuda")
+    rd = [int(x) for x in pool.read_slot]
+    wr = [int(x) for x in pool.write_slot]
+    others = [sl for sl in range(pool.state.shape[0]) if sl not in wr]
+    before = dp.state.clone()
+    gdn.traffic_probe(dp.state, dp.rd, dp.wr, sink, traffic="copy", shape="chunk", threads=256, loads=1,
+                      persistent=1)
+    t.cuda.synchronize()
+    assert t.equal(dp.state[wr], before[rd])
+    assert t.equal(dp.state[others], before[others])
 
 
 def test_launch_floor_probes_run(gdn, torch):
