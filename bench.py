@@ -75,7 +75,7 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # when it differs.
 STEP_KERNELS_64_TWIN = ("_ZN3gdn20gdn_step_tile_kernelILi128ELi128ELi128ELb0ELi4EEEvNS_10StepParamsE",)
 MEASURED_TRAFFIC = {"kernel_code_sha256": "9042c0a94dcb327f1511c2c3dcee4574a0ea696c5310ba531ebb300052a095d5",
-                    "workload": (64, "twin", "fused", False), "bytes_per_launch": 140_332_274}
+                    "workload": (64, "twin", "fused", False, 16), "bytes_per_launch": 140_332_274}
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
@@ -440,9 +440,11 @@ class DevicePool:
     """The drawn pool of the 0.8B-like layer (the null slot and 256 slot pairs)
     with its 512 non-null slots replicated on the device to POOL_SLOTS slots
     (2 GiB of state), shared by every decode configuration the bench times, so
-    each can rotate over disjoint row sets that are cold when visited."""
+    each can rotate over disjoint row sets that are cold when visited.  With
+    H_k below 16 the 16 value heads share H_k key heads (same state pool,
+    fewer conv channels)."""
 
-    def __init__(self):
+    def __init__(self, H_k: int = 16):
         import torch
 
         import gated_deltanet_recurrent_decode_amd as gdn
@@ -451,7 +453,10 @@ class DevicePool:
         self.torch, self.gdn, self.gi = torch, gdn, gi
         gdn.lib()
         torch.cuda.set_device(0)
-        case = gi.qwen08b(B=256, T=1)
+        if H_k == 16:
+            case = gi.qwen08b(B=256, T=1)
+        else:
+            case = gi.make_case(f"0.8b-{H_k}x16", gi.Shape(B=256, T=1, H_k=H_k, H_v=16, d_k=128, d_v=128, W=4, N=513))
         s, pool = case.shape, case.pools[0]
         self.shape, self.case = s, case
         self.N = POOL_SLOTS
@@ -706,6 +711,8 @@ class Bench:
                     rd, wr = ranges[i % nsets]
                 if not inplace and (i // nsets) % 2:
                     rd, wr = wr, rd
+                if wr is None:  # in place: the write-only half writes the rows' own slots
+                    wr = rd
                 gdn.traffic_probe(dp.state, rd, wr, sink, traffic=tr, layout=layout, hold_ns=hold_ns,
                                   rows=self.R if layout == "contiguous" else self.B, **kw)
 
@@ -1110,6 +1117,8 @@ def main() -> int:
                          "chunked prefill of --rows prompts of --prefill-len tokens, the 9B-like stack of "
                          "--layers layers (twin), or slot copy and reset of --rows slots a call")
     ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--key-heads", type=int, default=16,
+                    help="decode modes: key heads shared by the 16 value heads (16, 8 or 4; in place G = 16 / H_k)")
     ap.add_argument("--prefill-len", type=int, default=512)
     ap.add_argument("--one-kernel", action="store_true",
                     help="prefill through gdn_prefill (one kernel, no workspace) instead of gdn_prefill_two_pass")
@@ -1168,7 +1177,11 @@ def main() -> int:
         print("bench.py: --tokens must be >= 1, and twin-slot writes take one token a row", file=sys.stderr)
         return 2
 
-    dp = DevicePool()
+    if args.key_heads not in (4, 8, 16):
+        print("bench.py: --key-heads takes 16, 8 or 4 (the in-place kernel groups 1, 2 or 4 value heads)",
+              file=sys.stderr)
+        return 2
+    dp = DevicePool(args.key_heads)
     try:
         b = Bench(dp, mode=args.mode, B=args.rows, T=args.tokens, real=args.real, hot=args.hot, commit=args.commit)
     except ValueError as e:
@@ -1209,8 +1222,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"0.8B-like GDN layer decode step: {b.B} rows"
                                + (f" ({b.R} real, {b.B - b.R} on the null slot)" if b.R < b.B else "")
-                               + " x 16+16 heads x 128x128 fp32 state, "
-                               f"conv width 4 over 6144 channels, bf16 conv windows and activations, "
+                               + f" x {s.H_k}+{s.H_v} heads x 128x128 fp32 state, "
+                               f"conv width 4 over {s.C} channels, bf16 conv windows and activations, "
                                f"{b.N}-slot pool, {b.T} token{'s' if b.T > 1 else ''} a row, "
                                f"{ {'twin': 'twin-slot write', 'inplace': 'in-place write', 'tokens': 'state kept per token (speculative verify)'}[args.mode]}, commit "
                                f"{commit}, "
@@ -1225,7 +1238,7 @@ def main() -> int:
     k_us = float(kus.mean())
     achieved = b.bytes / (k_us * 1e-6) / 1e9
     traffic = None
-    workload_key = (b.B, args.mode, "fused" if b.fused else "separate", bool(args.hot))
+    workload_key = (b.B, args.mode, "fused" if b.fused else "separate", bool(args.hot), s.H_k)
     if (MEASURED_TRAFFIC["kernel_code_sha256"] is not None
             and kernel_code_sha256() == MEASURED_TRAFFIC["kernel_code_sha256"]
             and workload_key == MEASURED_TRAFFIC["workload"]):
