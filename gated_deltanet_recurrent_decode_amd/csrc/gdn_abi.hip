@@ -105,9 +105,12 @@ gdn_status step_impl(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stri
     p.twin = write_slot ? 1 : 0;
     p.token_slots = token_slots;
     // one head tile a workgroup for every single-token step that allows it (a
-    // twin write, or in place with one value head per key head); the key-head-
-    // group kernel for token walks, per-token states and in-place GQA
-    const bool tile = d.T == 1 && !token_slots && (write_slot || G == 1);
+    // twin write, or in place with one value head per key head), except the
+    // in-place sizes that run faster with four value heads a workgroup; the
+    // key-head-group kernel for those, token walks, per-token states and
+    // in-place GQA
+    const bool tile = d.T == 1 && !token_slots && (write_slot || G == 1) &&
+                      !(!write_slot && gdn::walk_key_heads(p, d.d_k, d.d_v) > 1);
     return from_hip(tile ? gdn::launch_gdn_step_tile(p, d.d_k, d.d_v, stream)
                          : gdn::launch_gdn_step(p, d.d_k, d.d_v, stream));
 }

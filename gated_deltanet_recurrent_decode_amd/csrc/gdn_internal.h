@@ -74,6 +74,9 @@ struct SlotOpsParams {
 };
 
 hipError_t launch_gdn_step(const StepParams &p, int d_k, int d_v, hipStream_t stream);
+// key heads a workgroup of the walk kernel for this step (1 unless it groups several)
+int walk_key_heads(const StepParams &p, int d_k, int d_v);
+int device_cus();
 hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream);
 hipError_t launch_conv_decode(const ConvParams &p, hipStream_t stream);
 hipError_t launch_slot_commit(int32_t *read_slot, int32_t *write_slot, int B, hipStream_t stream);

@@ -1,9 +1,11 @@
 // gdn_step.hip -- the fused Gated DeltaNet decode step for gfx950, in place
 // (keep_in_place), T tokens a row.
 //
-// One workgroup owns a key head of a row with all G of its value heads, so no
-// other workgroup reads a conv window it overwrites.  The tokens go in blocks
-// of up to eight.  Per block the workgroup:
+// One workgroup owns one key head of a row (or several: four of one value
+// head each, or two of two, for single-token steps where that is faster) with
+// all of their value heads, so no other workgroup reads a conv window it
+// overwrites.  The tokens go in blocks of up to eight.  Per block the
+// workgroup:
 //   1. issues the loads of the block's conv inputs (weights, bias, the window
 //      before the block, x of its tokens) and gates; before the first block
 //      it then issues the loads of its G fp32 state tiles (d_k x d_v each,
@@ -12,9 +14,9 @@
 //   2. runs the conv decode + SiLU of its channels (q and k of the key head, v
 //      of its value heads) for every token of the block into LDS, and the
 //      gates exp(g), beta;
-//   3. L2-normalises each token's q and k (one wave a token, the sums in the
-//      same lane order as the single-token kernel) and leaves q^ (times
-//      q_scale) and k^ in LDS;
+//   3. L2-normalises each token's q and k (one wave a token and key head, the
+//      sums in the same lane order as the single-token kernel) and leaves q^
+//      (times q_scale) and k^ in LDS;
 //   4. per token and head: one pass over the register-resident state gives
 //      both a = S^T k^ and b = S^T q^ (in-thread over its rows, then
 //      butterflies across the eight row groups, which sit in lane bits 3-5 of
@@ -56,14 +58,18 @@ struct ConvIn {
     float g, beta;            // gate of (token tid / HPW, value head tid % HPW)
 };
 
-// TOKENS: per-token states (p.token_slots set); a separate instantiation, so
-// the plain walk carries none of its registers.
-template <int DK, int DV, int HPW, bool TOKENS>
-__global__ __launch_bounds__(2 * DV * HPW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+// G value heads a key head, KPW key heads a workgroup (HPW = G KPW head
+// slices); TOKENS: per-token states (p.token_slots set), a separate
+// instantiation, so the plain walk carries none of its registers.
+template <int DK, int DV, int G, int KPW, bool TOKENS>
+__global__ __launch_bounds__(2 * DV * G * KPW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void gdn_step_kernel(StepParams p)
 {
+    constexpr int HPW = G * KPW;
     using Cfg = StepCfg<DK, DV, HPW>;
-    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, RG = Cfg::RG, RPT = Cfg::RPT, NCH = Cfg::NCH;
+    constexpr int NT = Cfg::NT, NTH = Cfg::NTH, RG = Cfg::RG, RPT = Cfg::RPT;
+    constexpr int NCHK = 2 * DK + G * DV; // conv channels of one key head: q, k, its value heads' v
+    constexpr int NCH = KPW * NCHK;
     constexpr int TB = kWalkBlock;
     constexpr int NW = NT / 64;                // waves
     constexpr int NCL = NCH / 4;               // conv lanes (channel quads)
@@ -75,7 +81,7 @@ void gdn_step_kernel(StepParams p)
     // the block's conv outputs (+ a padding slot for spare conv lanes); after
     // the norm phase q and k hold q^ q_scale and k^
     __shared__ float y_blk[TB][NCH + 4];
-    __shared__ float kq_blk[TB];          // k^ . q^ of each token
+    __shared__ float kq_blk[TB][KPW];     // k^ . q^ of each token and key head
     __shared__ float2 gate_blk[TB][HPW];  // exp(g), beta of each token and value head
     // each conv lane's own inputs, parked here as soon as they arrive so no
     // register holds them through the conv: rows 0-2 the window before the
@@ -98,10 +104,12 @@ void gdn_step_kernel(StepParams p)
     const int cg = (ht >> 6) * 8 + (lane & 7);
     const int rg = lane >> 3;
 
-    // workgroup -> (row, key head); its value heads are hk*G .. hk*G + G-1
-    const int hk = blockIdx.x % p.H_k;
-    const int r = blockIdx.x / p.H_k;
-    const int hv0 = hk * p.G;
+    // workgroup -> (row, group of KPW key heads); the value heads of key head
+    // hk are hk*G .. hk*G + G-1, so the workgroup's are hv0 .. hv0 + HPW-1
+    const int ngrp = p.H_k / KPW;
+    const int hk0 = (int)(blockIdx.x % ngrp) * KPW;
+    const int r = blockIdx.x / ngrp;
+    const int hv0 = hk0 * G;
     const int T = p.T;
 
     const int rs = p.read_slot[r];
@@ -132,15 +140,18 @@ void gdn_step_kernel(StepParams p)
     const int C = p.C;
     const uint32_t cbytes = (uint32_t)C * 2u;
     // channel of x / conv_w / the window for the first channel e of a quad:
-    // q and k of the key head, then v of its value heads
+    // per key head of the workgroup, its q and k, then v of its value heads
     auto channel = [&](int e) {
-        const bool isq = e < DK;
-        const bool isk = !isq && e < 2 * DK;
-        const int ve = e >= 2 * DK ? e - 2 * DK : 0;
+        const int kl = e / NCHK;
+        const int e2 = e - kl * NCHK;
+        const int hk = hk0 + kl;
+        const bool isq = e2 < DK;
+        const bool isk = !isq && e2 < 2 * DK;
+        const int ve = e2 >= 2 * DK ? e2 - 2 * DK : 0;
         const int h = ve / DV;
-        return isq ? hk * DK + e
-               : isk ? p.H_k * DK + hk * DK + (e - DK)
-                     : 2 * p.H_k * DK + (hv0 + h) * DV + (ve - h * DV);
+        return isq ? hk * DK + e2
+               : isk ? p.H_k * DK + hk * DK + (e2 - DK)
+                     : 2 * p.H_k * DK + (hk * G + h) * DV + (ve - h * DV);
     };
     bool conv_wave[NCQ], conv_lane[NCQ];
     int c[NCQ], e4[NCQ];
@@ -317,10 +328,12 @@ void gdn_step_kernel(StepParams p)
         }
         lds_barrier();
 
-        // ---- L2 norms of q and k, one wave a token (lane l sums elements l,
-        // l + 64, ...; then a butterfly over the wave), and q, k rescaled in place
-        for (int tb = wave; tb < nb; tb += NW) {
-            float *y = y_blk[tb];
+        // ---- L2 norms of q and k, one wave a token and key head (lane l sums
+        // elements l, l + 64, ...; then a butterfly over the wave), and q, k
+        // rescaled in place
+        for (int pr = wave; pr < nb * KPW; pr += NW) {
+            const int tb = pr / KPW, kl = pr - tb * KPW;
+            float *y = &y_blk[tb][kl * NCHK];
             float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
             for (int i = lane; i < DK; i += 64) {
@@ -342,14 +355,15 @@ void gdn_step_kernel(StepParams p)
                 y[DK + i] = kv * rk;
             }
             if (lane == 0)
-                kq_blk[tb] = sqk * rk * qs; // k^ . q^
+                kq_blk[tb][kl] = sqk * rk * qs; // k^ . q^
         }
         lds_barrier();
 
         // ---- per token: projections of the state onto k^ and q^, the delta
         // update in registers, and the read-out
+        const int kl = hloc / G; // the thread's key head in the workgroup (uniform)
         for (int tb = 0; tb < nb; ++tb) {
-            const float *y = y_blk[tb];
+            const float *y = &y_blk[tb][kl * NCHK];
             float4 pa = f4_zero(), pb = f4_zero();
 #pragma unroll
             for (int m = 0; m < RPT; ++m) {
@@ -381,8 +395,8 @@ void gdn_step_kernel(StepParams p)
 
             const float2 gb = gate_blk[tb][hloc];
             const float alpha = gb.x, bt = gb.y;
-            const float kq = kq_blk[tb];
-            const float *vv = &y[2 * DK + hloc * DV + 4 * cg];
+            const float kq = kq_blk[tb][kl];
+            const float *vv = &y[2 * DK + (hloc - kl * G) * DV + 4 * cg];
             float4 u;
             u.x = bt * (vv[0] - alpha * pa.x);
             u.y = bt * (vv[1] - alpha * pa.y);
@@ -441,27 +455,59 @@ void gdn_step_kernel(StepParams p)
                                                kStorePolicy);
 }
 
-template <int DK, int DV, int HPW>
+template <int DK, int DV, int G, int KPW>
 static hipError_t launch_step(const StepParams &p, hipStream_t stream)
 {
-    const long long tiles = (long long)p.B * p.H_k;
-    if (tiles <= 0)
+    if (p.H_k % KPW != 0)
+        return hipErrorInvalidValue;
+    const long long groups = (long long)p.B * (p.H_k / KPW);
+    if (groups <= 0)
         return hipSuccess;
     StepParams q = p;
     q.n_slices = 1;
     void *args[] = {&q};
-    const void *k = p.token_slots ? reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, HPW, true>)
-                                  : reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, HPW, false>);
-    return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(StepCfg<DK, DV, HPW>::NT), args, 0, stream);
+    const void *k = reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, G, KPW, false>);
+    if constexpr (KPW == 1) {
+        if (p.token_slots)
+            k = reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, G, KPW, true>);
+    } else if (p.token_slots) {
+        return hipErrorInvalidValue; // per-token states keep one key head a workgroup
+    }
+    return hipLaunchKernel(k, dim3((unsigned)groups), dim3(2 * DV * G * KPW), args, 0, stream);
+}
+
+// Key heads a workgroup.  Single-token in-place steps of 128 x 128 tiles
+// whose value heads put 2.5 to 4 tiles on every CU (40-64 rows of 16 heads)
+// take four value heads a workgroup -- four key heads of one value head each,
+// or two of two -- in 1024 threads, one workgroup a CU.  Measured on MI355X
+// at 64 rows, cold scattered slots, us a step: one value head a key head 27.6
+// (the one-tile kernel) -> 26.65, two 26.9 -> 26.4.  Token walks keep one key
+// head a workgroup (four tokens at 64 rows: 29.7 against 32.2 grouped), as do
+// 16 and 128 rows (8.2 against 11.8, 52.0 against 54.5), where the grouped
+// workgroups leave CUs idle or hold two to a CU.
+int walk_key_heads(const StepParams &p, int d_k, int d_v)
+{
+    if (p.T != 1 || p.token_slots || p.twin || d_k != 128 || d_v != 128 || (p.G != 1 && p.G != 2))
+        return 1;
+    const long long heads = (long long)p.B * p.H_v, cus = device_cus();
+    const int kpw = 4 / p.G;
+    return heads * 2 > 5 * cus && heads <= 4 * cus && p.H_k % kpw == 0 ? kpw : 1;
 }
 
 template <int DK, int DV>
 static hipError_t dispatch_dims(const StepParams &p, hipStream_t stream)
 {
+    if constexpr (DK == 128 && DV == 128) {
+        const int kpw = walk_key_heads(p, DK, DV);
+        if (kpw == 4)
+            return launch_step<DK, DV, 1, 4>(p, stream);
+        if (kpw == 2)
+            return launch_step<DK, DV, 2, 2>(p, stream);
+    }
     switch (p.G) {
-    case 1: return launch_step<DK, DV, 1>(p, stream);
-    case 2: return launch_step<DK, DV, 2>(p, stream);
-    case 4: return launch_step<DK, DV, 4>(p, stream);
+    case 1: return launch_step<DK, DV, 1, 1>(p, stream);
+    case 2: return launch_step<DK, DV, 2, 1>(p, stream);
+    case 4: return launch_step<DK, DV, 4, 1>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -363,7 +363,7 @@ static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
-static int device_cus()
+int device_cus()
 {
     static std::atomic<int> cached[64];
     int dev = 0;

@@ -75,3 +75,47 @@ def test_grouped_in_place_equals_twin(gdn, G):
     rd = t.from_numpy(pool.read_slot[real].astype(np.int64)).cuda()
     _bits_equal(tw.state[wr], ip.state[rd], "state")
     _bits_equal(tw.conv_state[wr], ip.conv_state[rd], "conv window")
+
+
+@pytest.mark.parametrize("B,G", [(48, 1), (64, 1), (64, 2), (44, 2)], ids=["48rows-G1", "64rows-G1", "64rows-G2",
+                                                                          "44rows-G2"])
+def test_grouped_key_heads_in_place(gdn, B, G):
+    """Single-token in-place steps of 128 x 128 tiles with 2.5-4 tiles a CU run
+    four value heads a workgroup (four key heads of one value head, or two of
+    two).  With padding rows spread over the bucket: the oracle's values, the
+    twin step's bits, zero outputs for padding, and nothing else in the pool
+    touched."""
+    import oracle
+    t = H.torch()
+    H_v = 16
+    case = gi.small(B=B, T=1, H_k=H_v // G, H_v=H_v, d=128, twin=True, seed=B + G)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    pad = np.arange(B) % 7 == 3
+    rd = pool.read_slot.copy()
+    rd[pad] = 0
+    wr = pool.write_slot.copy()
+    wr[pad] = 0
+    p2 = gi.Pool(pool.state, pool.conv_state, pool.conv_w, rd, wr)
+    tw = H.DevPool(p2)
+    out_t = H.gpu_step(gdn, tw, step, s, twin=True)
+    ip = H.DevPool(p2)
+    before = ip.state.clone()
+    before_cs = ip.conv_state.clone()
+    out_i = H.gpu_step(gdn, ip, step, s, twin=False)
+    hp = H.HostPool(gi.Pool(pool.state, pool.conv_state, pool.conv_w, rd, rd.copy()))
+    ref = H.oracle_step(oracle, hp, step, s, twin=False)
+    t.cuda.synchronize()
+    H.assert_out_close(out_i, ref)
+    real = ~pad
+    idx = t.from_numpy(rd[real].astype(np.int64)).cuda()
+    H.assert_state_close(ip.state[idx].cpu().numpy(), hp.state[rd[real]])
+    np.testing.assert_array_equal(H.bf16_host(ip.conv_state[idx]), hp.conv_state[rd[real]])
+    _bits_equal(out_t, out_i, "out")
+    widx = t.from_numpy(wr[real].astype(np.int64)).cuda()
+    _bits_equal(tw.state[widx], ip.state[idx], "state")
+    _bits_equal(tw.conv_state[widx], ip.conv_state[idx], "conv window")
+    assert not bool(out_i[t.from_numpy(np.nonzero(pad)[0]).cuda()].float().abs().sum())
+    mask = t.ones(s.N, dtype=t.bool, device="cuda")
+    mask[idx] = False
+    _bits_equal(ip.state[mask], before[mask], "untouched slots")
+    _bits_equal(ip.conv_state[mask], before_cs[mask], "untouched windows")
