@@ -4,8 +4,8 @@ captured replay.
 The mstar pages require that a graph captured on one layout of the decode
 bucket and replayed on another gives the right rows (PR #965, "Correctness"),
 and test the decode conv as a captured replay against eager steps (PR #1139,
-"Tests").  Here one capture of the 128-row bucket (the mixed step's decode
-half, in place, and the twin-slot step) is replayed after the device slot
+"Tests").  Here one capture of a 128-row and a 64-row bucket (the mixed step's
+decode half, in place, and the twin-slot step) is replayed after the device slot
 arrays and inputs are rewritten to other real/padding splits; every replay is
 compared with the oracle, padding rows must read out +0.0, slot 0 must stay
 zero and no slot outside the real rows' write set may change.  Between replays
@@ -36,30 +36,39 @@ def torch():
     return t
 
 
-ROWS = gi.PADDED_ROWS
-
-
-def _layouts():
-    """(name, real row positions) of the bucket, in replay order: the captured
-    split first, then others, then the captured one again."""
-    first46 = list(range(gi.PADDED_REAL))
+def _layouts(rows, captured):
+    """(name, real row positions) of a bucket of `rows`, in replay order: the
+    captured split first, then others, then the captured one again."""
+    first = list(range(captured))
+    half = rows // 2
     return [
-        ("46 real first (as captured)", first46),
-        ("64 real first", list(range(64))),
+        (f"{captured} real first (as captured)", first),
+        (f"{half} real first", list(range(half))),
         ("10 real first", list(range(10))),
         ("no real row", []),
-        ("64 real, every other row", list(range(0, ROWS, 2))),
-        ("40 real scattered", sorted(np.random.Generator(np.random.PCG64(5)).choice(ROWS, 40, replace=False).tolist())),
-        ("46 real first again", first46),
+        (f"{half} real, every other row", list(range(0, rows, 2))),
+        (f"{rows * 5 // 16} real scattered",
+         sorted(np.random.Generator(np.random.PCG64(5)).choice(rows, rows * 5 // 16, replace=False).tolist())),
+        (f"all {rows} rows real", list(range(rows))),
+        (f"{captured} real first again", first),
     ]
 
 
-@pytest.mark.parametrize("mode", ["inplace-T1", "inplace-T4", "twin-T1"])
+# the 128-row bucket of the mixed step's decode half (46 real), and a 64-row
+# bucket (30 real), whose single-token steps take four head tiles a workgroup
+# (twin) and four value heads a workgroup (in place)
+@pytest.mark.parametrize("mode", ["inplace-T1", "inplace-T4", "twin-T1", "inplace-T1-64rows", "twin-T1-64rows"])
 def test_captured_bucket_replayed_on_other_layouts(gdn, torch, mode):
     t = torch
     twin = mode.startswith("twin")
-    T = 4 if mode.endswith("T4") else 1
-    case = gi.padded(T=T, twin=twin, seed=31)
+    T = 4 if "-T4" in mode else 1
+    if mode.endswith("64rows"):
+        shape = gi.Shape(B=64, T=T, H_k=16, H_v=16, d_k=128, d_v=128, W=4, N=513)
+        case = gi.make_case("bucket-64", shape, real_rows=30, twin=twin, seed=32)
+        captured = 30
+    else:
+        case = gi.padded(T=T, twin=twin, seed=31)
+        captured = gi.PADDED_REAL
     s, pool = case.shape, case.pools[0]
     hp = H.HostPool(pool)
     dp = H.DevPool(pool)
@@ -93,7 +102,7 @@ def test_captured_bucket_replayed_on_other_layouts(gdn, torch, mode):
         gdn.gdn_decode_step(x, dp.conv_w, None, dp.conv_state, dp.state, g, beta, dp.rd, dp.wr if twin else None,
                             out, H_k=s.H_k)
 
-    layouts = _layouts()
+    layouts = _layouts(s.B, captured)
     set_layout(layouts[0][1])
     stream = t.cuda.Stream()
     graph = t.cuda.CUDAGraph()
