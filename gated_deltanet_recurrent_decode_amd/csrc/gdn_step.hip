@@ -8,9 +8,9 @@
 // workgroup:
 //   1. issues the loads of the block's conv inputs (weights, bias, the window
 //      before the block, x of its tokens) and gates; before the first block
-//      it then issues the loads of its G fp32 state tiles (d_k x d_v each,
-//      16-byte loads, each wave instruction covering whole 128-byte lines), so
-//      the conv runs while HBM streams the tiles;
+//      it then issues the loads of its value heads' fp32 state tiles (d_k x
+//      d_v each, 16-byte loads, each wave instruction covering whole 128-byte
+//      lines), so the conv runs while HBM streams the tiles;
 //   2. runs the conv decode + SiLU of its channels (q and k of the key head, v
 //      of its value heads) for every token of the block into LDS, and the
 //      gates exp(g), beta;
@@ -34,7 +34,9 @@
 // allow one head tile per workgroup (every twin step, and in place with one
 // value head per key head) run in gdn_step_tile.hip instead, with the same
 // thread layout and the same arithmetic in the same order, so both give the
-// same bits; this kernel takes token walks, per-token states and in-place GQA.
+// same bits; this kernel takes token walks, per-token states, in-place GQA,
+// and the single-token in-place sizes that run faster grouped (see
+// walk_key_heads).
 //
 // No MFMA: per state element the step does a handful of FMAs against 8 bytes
 // of HBM traffic, far under the fp32 ridge point, so the kernel is written for
