@@ -399,7 +399,9 @@ int device_cus()
 // q/k conv a slice more.  Measured on MI355X with the state cold, 16 heads a
 // row, us a step whole against sliced: 8 rows 6.66 / 5.78, 12 rows 7.20 / 7.26,
 // 16 rows 8.13 / 8.46, 24 rows 12.61 / 11.06, 40 rows 19.18 / 18.41.  Under 128
-// tiles slices keep going down to 32 columns.  Never in place: every slice
+// tiles two slices of 64 columns beat four of 32, whose 64-thread workgroups
+// run the whole q/k conv on one wave (1 row 4.94 against 5.16 us, 2 rows 5.10
+// against 5.30, 4 rows 5.32 against 5.48).  Never in place: every slice
 // reads the head's q/k conv windows and one of them writes them back, so in
 // place a slice that starts late could read an advanced window; with whole
 // tiles and one value head per key head, no other workgroup reads them.
@@ -421,9 +423,7 @@ static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
     }
     if (!p.twin || heads >= 2048 || (heads >= 128 && (rem == 0 || rem > 128)))
         return launch_tile<DK, DV, DV, 1>(q, stream);
-    if (heads >= 32 || DV < 128)
-        return launch_tile<DK, DV, DV / 2, 1>(q, stream);
-    return launch_tile<DK, DV, (DV / 4 >= 32 ? DV / 4 : 32), 1>(q, stream);
+    return launch_tile<DK, DV, DV / 2, 1>(q, stream);
 }
 
 hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream)
