@@ -81,9 +81,11 @@ MEASURED_TRAFFIC = {"kernel_code_sha256": "9042c0a94dcb327f1511c2c3dcee4574a0ea6
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
 # summary with its commands is in profiles/.  Valid only for this machine code.
 PREFILL_KERNELS = ("_ZN3gdn12_GLOBAL__N_119tp_chunk_map_kernelENS_13TwoPassParamsE",
-                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128ELb0EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128ELb1EEEvNS_13TwoPassParamsE",
                    "_ZN3gdn12_GLOBAL__N_115tp_inter_kernelILi128ELi128ELi64EEEvNS_13TwoPassParamsE",
-                   "_ZN3gdn12_GLOBAL__N_117tp_inter16_kernelILi128ELi128EEEvNS_13TwoPassParamsE")
+                   "_ZN3gdn12_GLOBAL__N_117tp_inter16_kernelILi128ELi128EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_114tp_slim_kernelILi128ELi128EEEvNS_13TwoPassParamsE")
 MEASURED_PREFILL_TRAFFIC = {"kernel_code_sha256": "f0947739f8a69197219350d1fd3a40ba7bda42d672fe28b610ab0dbf4e11cb59",
                             "bytes_per_call": {(16, 512): 754_928_363, (1, 4096): 364_499_998}}
 

@@ -244,7 +244,7 @@ size_t gdn_prefill_two_pass_workspace_bytes(const gdn_dims *dims)
     const gdn_dims d = *dims;
     if (d.B < 0 || d.T < 0 || d.H_v < 1 || !head_dim_ok(d.d_k) || !head_dim_ok(d.d_v))
         return 0;
-    return gdn::two_pass_layout(d.B, d.T, d.H_v, d.d_k, d.d_v, nullptr, nullptr);
+    return gdn::two_pass_layout(d.B, d.T, d.H_k, d.H_v, d.d_k, d.d_v, nullptr, nullptr);
 }
 
 gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_stride,
@@ -267,7 +267,7 @@ gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t
         return GDN_ERR_SHAPE;
     gdn::TwoPassParams tp{};
     tp.p = p;
-    if (workspace_bytes < gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, workspace, &tp.ws))
+    if (workspace_bytes < gdn::two_pass_layout(p.B, p.total, p.H_k, p.H_v, dims->d_k, dims->d_v, workspace, &tp.ws))
         return GDN_ERR_SHAPE;
     return from_hip(gdn::launch_gdn_prefill_two_pass(tp, dims->d_k, dims->d_v, stream));
 }
@@ -322,7 +322,7 @@ gdn_status gdn_prefill_two_pass_noalloc(const gdn_dims *dims, const gdn_bf16 *x,
         return st;
     if ((long long)p.total / 32 + p.B + 1 > INT32_MAX)
         return GDN_ERR_SHAPE;
-    if (gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, nullptr, nullptr) > kScratchBytes)
+    if (gdn::two_pass_layout(p.B, p.total, p.H_k, p.H_v, dims->d_k, dims->d_v, nullptr, nullptr) > kScratchBytes)
         return GDN_ERR_SCRATCH;
     void *ws = nullptr;
     const gdn_status sst = scratch_for_current_device(&ws);
@@ -330,7 +330,7 @@ gdn_status gdn_prefill_two_pass_noalloc(const gdn_dims *dims, const gdn_bf16 *x,
         return sst;
     gdn::TwoPassParams tp{};
     tp.p = p;
-    gdn::two_pass_layout(p.B, p.total, p.H_v, dims->d_k, dims->d_v, ws, &tp.ws);
+    gdn::two_pass_layout(p.B, p.total, p.H_k, p.H_v, dims->d_k, dims->d_v, ws, &tp.ws);
     return from_hip(gdn::launch_gdn_prefill_two_pass(tp, dims->d_k, dims->d_v, stream));
 }
 

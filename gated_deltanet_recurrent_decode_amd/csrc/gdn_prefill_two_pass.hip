@@ -140,28 +140,31 @@ __global__ __launch_bounds__(NT) void tp_chunk_map_kernel(TwoPassParams tp)
         const int t_begin = p.cu_seqlens[lo];
         const int L = p.cu_seqlens[lo + 1] - t_begin;
         *reinterpret_cast<int4 *>(tp.ws.chunk_rec + 4 * (size_t)g) =
-            make_int4(t_begin + c * BT, L - c * BT < BT ? L - c * BT : BT, p.slot[lo], c == 0 ? 1 : 0);
+            make_int4(t_begin + c * BT, L - c * BT < BT ? L - c * BT : BT, p.slot[lo], c == 0 ? lo + 1 : 0);
     }
 }
 
 // ---------------------------------------------------------------- pass 1
 
 // two workgroups a CU (LDS allows two): at most 256 registers a lane, which
-// the compiler meets by recomputing LDS addresses inside the chunk loop
-template <int DK, int DV>
+// the compiler meets by recomputing LDS addresses inside the chunk loop.
+// SLIM: the slim layout (T', P and the row factors; no V, W or U~), and each
+// prompt's old window copied to hw at its first chunk.
+template <int DK, int DV, bool SLIM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void tp_intra_kernel(TwoPassParams tp)
 {
     const PrefillParams &p = tp.p;
-    constexpr int NPAIR = (2 * DK + DV) / 2; // conv lanes, two channels each
+    constexpr int NPAIR = SLIM ? DK : (2 * DK + DV) / 2; // conv lanes, two channels each
+    constexpr int VPAIR = SLIM ? DV / 2 : 0;              // slim: lanes that copy the v channels' old window
     // LDS pitches as in the one-kernel prefill: A-style operand reads along a
     // row want 4 mod 32, B-style reads down a column 16 mod 32
     constexpr int KP = DK + 4, VP = DV + 16, AP = BT + 1;
-    static_assert(NPAIR <= NT, "one conv lane per channel pair");
+    static_assert(NPAIR + VPAIR <= NT, "one conv lane per channel pair");
     static_assert((2 * (DK / 16) * 64) % NT == 0, "whole store rounds");
 
     __shared__ __align__(16) float Qs[BT * KP];
     __shared__ __align__(16) float Ks[BT * KP];
-    __shared__ __align__(16) float Vs[BT * (VP > KP ? VP : KP)]; // V, then W
+    __shared__ __align__(16) float Vs[SLIM ? 4 : BT * (VP > KP ? VP : KP)]; // V, then W
     __shared__ float Am[BT * AP];
     __shared__ float Pm[BT * AP];
     __shared__ float Tm[BT * AP];
@@ -181,8 +184,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         return;
 
     // ---- conv lanes: channel pair (e, e+1) of the q | k | v channels of (hk, hv)
+    // (slim: q | k only, and copy lanes for the v channels' window)
     const bool conv_lane = tid < NPAIR;
-    const int e = conv_lane ? 2 * tid : 0;
+    const bool copy_lane = SLIM && !conv_lane && tid < NPAIR + VPAIR;
+    const int e = conv_lane ? 2 * tid : copy_lane ? 2 * DK + 2 * (tid - NPAIR) : 0;
     const bool isq = e < DK, isk = !isq && e < 2 * DK;
     const int ch = isq ? hk * DK + e : isk ? p.H_k * DK + hk * DK + (e - DK) : 2 * p.H_k * DK + hv * DV + (e - 2 * DK);
     float w0[2], w1[2], w2[2], w3[2], bias[2];
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         uint32_t hist[3];
         float g_in, b_in;
         int t0, n;
+        int b1; // the sequence's index + 1 at its first chunk, else 0
     };
     auto load = [&](int gi, ChunkIn &in) {
         const int gq = __builtin_amdgcn_readfirstlane(gi < nch ? gi : nch - 1); // past the end: a real chunk, unused
@@ -214,7 +220,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int t0 = __builtin_amdgcn_readfirstlane(rec.x);
         const int n = __builtin_amdgcn_readfirstlane(rec.y);
         const int sl = __builtin_amdgcn_readfirstlane(rec.z);
-        const bool first = __builtin_amdgcn_readfirstlane(rec.w) != 0;
+        const int b1 = __builtin_amdgcn_readfirstlane(rec.w);
+        const bool first = b1 != 0;
         const uint16_t *hb = first ? p.conv_state + (size_t)sl * 3 * C + ch
                                    : p.x + (size_t)(t0 - 3) * p.x_row_stride + ch;
         const size_t hs = first ? (size_t)C : (size_t)p.x_row_stride;
@@ -223,10 +230,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             in.hist[k] = *reinterpret_cast<const uint32_t *>(hb + k * hs);
         const __amdgpu_buffer_rsrc_t rx =
             buf_rsrc(p.x + (size_t)t0 * p.x_row_stride, (uint32_t)(((n - 1) * p.x_row_stride + C) * 2));
-        // (lanes without a channel pair load the first pair's inputs, unused)
+        // (lanes without a channel pair load nothing: past the resource)
 #pragma unroll
         for (int tt = 0; tt < BT; ++tt)
-            in.xb[tt] = __builtin_amdgcn_raw_buffer_load_b32(rx, (uint32_t)(tt * p.x_row_stride + ch) * 2u, 0, 0);
+            in.xb[tt] = __builtin_amdgcn_raw_buffer_load_b32(
+                rx, conv_lane ? (uint32_t)(tt * p.x_row_stride + ch) * 2u : kOOB, 0, 0);
         const __amdgpu_buffer_rsrc_t rg = buf_rsrc(p.g + (size_t)t0 * p.H_v, (uint32_t)(n * p.H_v * 4));
         const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(p.beta + (size_t)t0 * p.H_v, (uint32_t)(n * p.H_v * 4));
         const uint32_t goff = (uint32_t)((tid & (BT - 1)) * p.H_v + hv) * 4u; // lanes past BT: unused copies
@@ -234,12 +242,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         in.b_in = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_, goff, 0, 0));
         in.t0 = t0;
         in.n = n;
+        in.b1 = b1;
     };
 
     ChunkIn cur, nxt;
     load(blockIdx.x, cur);
     for (int g = blockIdx.x; g < nch; g += gridDim.x) {
-        const int t0 = cur.t0, n = cur.n;
+        const int n = cur.n;
         float h0[2], h1[2], h2[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -248,9 +257,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             h2[h] = __uint_as_float(h ? cur.hist[2] & 0xffff0000u : cur.hist[2] << 16);
         }
 
+        // slim: a prompt's first chunk keeps its old window for the second pass
+        if (SLIM && cur.b1 != 0 && (conv_lane || copy_lane)) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                *reinterpret_cast<uint32_t *>(tp.ws.hw + ((size_t)(cur.b1 - 1) * 3 + k) * C + ch) = cur.hist[k];
+        }
+
         // ---- conv + SiLU; rows past the chunk's last token stay zero
         if (conv_lane) {
-            float *ydst = isq ? &Qs[e] : isk ? &Ks[e - DK] : &Vs[e - 2 * DK];
+            float *ydst = isq ? &Qs[e] : (SLIM || isk) ? &Ks[e - DK] : &Vs[e - 2 * DK];
             const int ypitch = (isq || isk) ? KP : VP;
             const bool has_bias = p.conv_b != nullptr;
             // the pair's two outputs of a token are adjacent: one 8-byte store.
@@ -324,9 +340,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             sk += dpp_xor<2>(sk);
             sq += dpp_xor<4>(sq);
             sk += dpp_xor<4>(sk);
+            const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
+            const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+            if constexpr (SLIM) {
+                // the second pass's row factors (zero for a padding token)
+                if (sub < 3) {
+                    const size_t blk = (size_t)hv * tp.ws.nchunk + g;
+                    const float f = sub == 0 ? rk * eg[tt] : sub == 1 ? qs * eg[tt] : rk * egl[tt];
+                    tp.ws.fac[blk * 128 + sub * BT + tt] = tt < n ? f : 0.f;
+                }
+            }
             if (tt < n) {
-                const float qs = (1.0f / sqrtf(sq + p.l2_eps)) * p.q_scale;
-                const float rk = 1.0f / sqrtf(sk + p.l2_eps);
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
                     *reinterpret_cast<v4f *>(&Qs[tt * KP + 4 * sub + 32 * j]) =
@@ -406,10 +430,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
         __syncthreads();
 
+        const size_t blk = (size_t)hv * tp.ws.nchunk + g;
+        if constexpr (SLIM) {
+            // ---- T' = T diag(beta) as the second pass's A operand (the layout of P below)
+            const int idx = tid, l = idx & 63, m4 = (idx >> 6) & 1, rb = idx >> 7;
+            v4f tv;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int ss = 16 * m4 + 4 * (l >> 4) + e4;
+                tv[e4] = Tm[(rb * 16 + (l & 15)) * AP + ss] * bet[ss];
+            }
+            *reinterpret_cast<v4f *>(tp.ws.ta + blk * (BT * BT) + (size_t)idx * 4) = tv;
+        } else {
         // ---- W = T diag(beta e^gamma) K and U~ = T diag(beta) V on the matrix
         // cores: this wave's column blocks of each, both row blocks.  Rows of
         // padding tokens come out zero (their rows of A, and beta, are zero).
-        const size_t blk = (size_t)hv * tp.ws.nchunk + g;
         {
             constexpr int WCB = DK / 64, UCB = DV / 64;
             v4f wacc[2][WCB], uacc[2][UCB];
@@ -490,6 +525,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             }
             *reinterpret_cast<v4f *>(tp.ws.ka + blk * (BT * DK) + (size_t)idx * 4) = kv;
         }
+        } // full layout
         {
             const int idx = tid, l = idx & 63, m4 = (idx >> 6) & 1, rb = idx >> 7; // 256 float4: one a thread
             v4f pv;
@@ -500,7 +536,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
         // e^gamma_last (padding tokens carry g = 0): every lane stores the same
         // value to the same place, which needs no branch
-        tp.ws.el[blk] = eg[BT - 1];
+        if constexpr (SLIM)
+            tp.ws.fac[blk * 128 + 96] = eg[BT - 1];
+        else
+            tp.ws.el[blk] = eg[BT - 1];
 
         cur = nxt;
         __syncthreads(); // LDS is read to the end of the chunk; the next one rewrites it
@@ -513,7 +552,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // prompt] for the slice's v channels, and for the key head's q and k channels
 // from its first value head's first slice.  Nothing else reads or writes these
 // channels of this slot now: pass 1 is over.
-template <int DK, int DV, int DVS>
+template <int DK, int DV, int DVS, int NTH = NT>
 __device__ __forceinline__ void advance_windows(const PrefillParams &p, int hv, int sl, int t_begin, int t_end, int s)
 {
     const int tid = threadIdx.x;
@@ -524,7 +563,7 @@ __device__ __forceinline__ void advance_windows(const PrefillParams &p, int hv, 
     const bool qk_owner = (hv % p.G == 0) && sl == 0;
     const int npair = DVS / 2 + (qk_owner ? DK : 0);
     uint16_t *win = p.conv_state + (size_t)s * 3 * C;
-    for (int e = tid; e < npair; e += NT) {
+    for (int e = tid; e < npair; e += NTH) {
         const int ch = e < DVS / 2 ? 2 * p.H_k * DK + hv * DV + col0 + 2 * e
                        : e < DVS / 2 + DK / 2 ? hk * DK + 2 * (e - DVS / 2)
                                              : p.H_k * DK + hk * DK + 2 * (e - DVS / 2 - DK / 2);
@@ -568,7 +607,7 @@ __device__ __forceinline__ void walk_place(int j, int heads, int nsl, int &bh, i
 // Where a pass-2 workgroup's prompt stands: false when it has nothing to do
 // (an unusable range or slot touches nothing; a padding prompt on the null
 // slot gets its read-out of +0.0 here; an empty prompt does nothing).
-template <int DV, int DVS>
+template <int DV, int DVS, int NTH = NT>
 __device__ __forceinline__ bool walk_setup(const TwoPassParams &tp, int b, int hv, int col0, int &t_begin, int &t_end,
                                            int &s, int &nchunks, size_t &blk0)
 {
@@ -581,7 +620,7 @@ __device__ __forceinline__ bool walk_setup(const TwoPassParams &tp, int b, int h
     t_end = __builtin_amdgcn_readfirstlane(t_end);
     s = __builtin_amdgcn_readfirstlane(s);
     if (s == 0) {
-        for (int e = threadIdx.x; e < (t_end - t_begin) * DVS; e += NT)
+        for (int e = threadIdx.x; e < (t_end - t_begin) * DVS; e += NTH)
             p.out[((size_t)(t_begin + e / DVS) * p.H_v + hv) * DV + col0 + e % DVS] = 0;
         return false;
     }
@@ -1061,6 +1100,365 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
     advance_windows<DK, DV, 16>(p, hv, sl, t_begin, t_end, s);
 }
 
+// The slim walk: one workgroup a (prompt, value head) over the slim layout,
+// with the chunk's conv run here from x (once for the head), and a wave per
+// 16-column block of the state.  Every wave meets the same barriers, so the
+// head's waves move together (two workgroups sharing a compute unit had run
+// apart: the older one takes the issue slots, the younger finishes alone).
+// With K and Q the chunk's conv + SiLU outputs before normalisation (in LDS)
+// and the state in LDS transposed, per chunk:
+//   Y = K S0 and Z = Q S0, both row blocks of the wave's column block;
+//   R = V - f_a Y, V the lane's own conv outputs at its accumulator-layout
+//   places, f_a = k-norm e^gamma per row;  U = T' R, with R the B operand as
+//   it stands;
+//   O = f_b Z + P U -> out, f_b = q-norm q_scale e^gamma;
+//   U'' = f_c U -> LDS, f_c = k-norm e^(gamma_last - gamma);
+// and after the chunk's second barrier each wave updates its share of the
+// state's 16 x 16 tiles (whole row blocks), S1 = e^gamma_last S0 + K^T U''.  U = T diag(beta) (V - e^gamma K^ S0) is the
+// full layout's U~ - W S0, and K^T U'' its K~^T U.
+// Two barriers a chunk: after the conv (K, Q and the previous update are in
+// LDS) and after U'' (every read of the state, K and Q for the chunk is done,
+// so the update and the next chunk's conv may write them).
+// at most 256 registers a lane: two waves a SIMD (at d_v = 128 one
+// workgroup of eight waves a CU, which its 120 KB of LDS allow)
+template <int DK, int DV>
+__global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2, 2))) void tp_slim_kernel(TwoPassParams tp)
+{
+    const PrefillParams &p = tp.p;
+    constexpr int DVS = DV;
+    constexpr int NW = DV / 16, NTS = 64 * NW;           // a wave per column block
+    constexpr int KP = DK + 4, SPT = DK + 4, UPT = BT + 4; // 4 mod 32 words: 16-byte reads conflict-free
+    constexpr int NA4 = DK / 16, NRB = DK / 16, NCB = DV / 16;
+    // the state update's tiles: RBW row blocks x CBU column blocks a wave
+    constexpr int RBW = NW <= NRB ? NRB / NW : 1;
+    constexpr int CBU = NW <= NRB ? NCB : NCB / (NW / NRB);
+    constexpr int NPQK = DK;                              // q | k channel pairs
+    constexpr int NSPLIT = NTS / NPQK, TPT = BT / NSPLIT; // runs of tokens of the q | k conv
+    static_assert(NTS % NPQK == 0 && BT % NSPLIT == 0 && TPT >= 1, "whole runs of tokens");
+    static_assert(NRB % RBW == 0 && RBW * CBU * NW == NRB * NCB, "the state's tiles split evenly over the waves");
+    constexpr int CHUNK_P = BT * BT;
+
+    __shared__ __align__(16) float St[DVS * SPT];
+    __shared__ __align__(16) float Ut[DVS * UPT];
+    __shared__ __align__(16) float Qs[BT * KP];
+    __shared__ __align__(16) float Ks[BT * KP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, li = lane & 15, lk = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hv = blockIdx.x % p.H_v;
+    const int b = blockIdx.x / p.H_v;
+    const int col0 = 0;
+    // this wave's tiles of the state update: row blocks rb0 .., column blocks cbu0 ..
+    const int rb0 = (wv % (NRB / RBW)) * RBW, cbu0 = (wv / (NRB / RBW)) * CBU;
+    int t_begin, t_end, s, nchunks;
+    size_t blk0;
+    if (!walk_setup<DV, DVS, NTS>(tp, b, hv, col0, t_begin, t_end, s, nchunks, blk0))
+        return;
+    float *tile = p.state + ((size_t)s * p.H_v + hv) * (size_t)(DK * DV);
+    const int C = p.C;
+    const int hk = hv / p.G;
+
+    // ---- conv roles.  q | k: thread tid takes channel pair pp over tokens
+    // sp TPT ..; v: lane (li, lk) of wave w takes column 16 w + li of the
+    // slice at tokens 16 rb + 4 lk + r, its places in the accumulator layout
+    const int pp = tid % NPQK, sp = tid / NPQK; // sp is the same across a wave
+    const int e = 2 * pp;
+    const bool isq = e < DK;
+    const int chqk = isq ? hk * DK + e : p.H_k * DK + hk * DK + (e - DK);
+    float *ydst = isq ? &Qs[e] : &Ks[e - DK];
+    const int chv = 2 * p.H_k * DK + hv * DV + col0 + 16 * wv + li;
+    const bool has_bias = p.conv_b != nullptr;
+    float wq[4][2], bq[2], wvc[4], bvc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            wq[k][h] = bf16_to_f32(p.conv_w[(size_t)(chqk + h) * 4 + k]);
+        bq[h] = has_bias ? bf16_to_f32(p.conv_b[chqk + h]) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        wvc[k] = bf16_to_f32(p.conv_w[(size_t)chv * 4 + k]);
+    bvc = has_bias ? bf16_to_f32(p.conv_b[chv]) : 0.f;
+
+    // ---- a chunk's x inputs, loaded one chunk ahead: the q | k pairs of the
+    // thread's run with the three inputs before it, and the lane's v inputs
+    // (tokens 16 rb + 4 lk - 3 ..).  Inputs before a prompt's first token come
+    // from the window copy in hw (a separate register: an OR here would wait
+    // for the loads).  Buffer resources over the chunk's rows, zero-sized past
+    // the last chunk, so nothing branches around a load.
+    struct XIn {
+        uint32_t qk[TPT + 3], qkh[3]; // bf16 pairs
+        uint32_t v[2][7], vh[3];      // bf16 in the low half
+    };
+    auto load_x = [&](int c, XIn &in) {
+        const bool real = c < nchunks;
+        const int cc = real ? c : 0;
+        const int t0 = t_begin + cc * BT;
+        const int n = t_end - t0 < BT ? t_end - t0 : BT;
+        const int sh = cc == 0 ? 0 : 3; // rows of x before the chunk in the resource
+        const __amdgpu_buffer_rsrc_t rx =
+            buf_rsrc(p.x + (size_t)(t0 - sh) * p.x_row_stride,
+                     real ? (uint32_t)(((size_t)(n - 1 + sh) * p.x_row_stride + C) * 2) : 0u);
+        const __amdgpu_buffer_rsrc_t rh =
+            buf_rsrc(tp.ws.hw + (size_t)b * 3 * C, real && cc == 0 ? (uint32_t)(3 * C * 2) : 0u);
+#pragma unroll
+        for (int i = 0; i < TPT + 3; ++i) {
+            const int t = sp * TPT - 3 + i;
+            in.qk[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                rx, t + sh >= 0 ? (uint32_t)((t + sh) * p.x_row_stride + chqk) * 2u : kOOB, 0, 0);
+            if (i < 3)
+                in.qkh[i] = __builtin_amdgcn_raw_buffer_load_b32(rh, t < 0 ? (uint32_t)((t + 3) * C + chqk) * 2u : kOOB,
+                                                                 0, 0);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 7; ++i) {
+                const int t = 16 * rb + 4 * lk - 3 + i;
+                in.v[rb][i] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rx, t + sh >= 0 ? (uint32_t)((t + sh) * p.x_row_stride + chv) * 2u : kOOB, 0, 0);
+                if (rb == 0 && i < 3)
+                    in.vh[i] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rh, t < 0 ? (uint32_t)((t + 3) * C + chv) * 2u : kOOB, 0, 0);
+            }
+    };
+    // ---- a chunk's operands from the workspace: the nonzero blocks (row
+    // block, token block) (0,0), (1,0), (1,1) of T' and P and the row factors
+    // at the lane's rows (all read before the chunk's second barrier, so the
+    // next chunk's load there reuses their registers), and e^gamma_last (read
+    // at the chunk's end, and loaded there for the next: a value loaded while
+    // the one before is still needed would be copied at the loop's edge,
+    // which waits for every load in flight)
+    struct Ops {
+        v4f t[3], pm[3];
+        v4f fa[2], fb[2], fc[2];
+    };
+    auto fac_rsrc = [&](int c) {
+        const bool real = c < nchunks;
+        return buf_rsrc(tp.ws.fac + (blk0 + (size_t)(real ? c : 0)) * 128, real ? 512u : 0u);
+    };
+    auto load_ops = [&](int c, Ops &o) {
+        const bool real = c < nchunks;
+        const size_t blk = blk0 + (size_t)(real ? c : 0);
+        const __amdgpu_buffer_rsrc_t rT = buf_rsrc(tp.ws.ta + blk * CHUNK_P, real ? CHUNK_P * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rP = buf_rsrc(tp.ws.pa + blk * CHUNK_P, real ? CHUNK_P * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rF = fac_rsrc(c);
+        constexpr int kBlk[3] = {0, 2, 3}; // [row block][token block] of the nonzero blocks
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            o.t[k] = buf_load4(rT, (uint32_t)(kBlk[k] * 64 + lane) * 16u);
+            o.pm[k] = buf_load4(rP, (uint32_t)(kBlk[k] * 64 + lane) * 16u);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            o.fa[rb] = buf_load4(rF, (uint32_t)(0 * BT + 16 * rb + 4 * lk) * 4u);
+            o.fb[rb] = buf_load4(rF, (uint32_t)(1 * BT + 16 * rb + 4 * lk) * 4u);
+            o.fc[rb] = buf_load4(rF, (uint32_t)(2 * BT + 16 * rb + 4 * lk) * 4u);
+        }
+    };
+    auto load_el = [&](int c) { return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(fac_rsrc(c), 96u * 4u, 0, 0)); };
+
+    // ---- the state -> LDS, transposed (as the wide walk)
+    for (int e2 = tid; e2 < DK * DVS / 4; e2 += NTS) {
+        const int j = e2 % DVS, i4 = e2 / DVS;
+        v4f v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            v[r] = __builtin_nontemporal_load(tile + (size_t)(4 * i4 + r) * DV + col0 + j);
+        *reinterpret_cast<v4f *>(&St[j * SPT + 4 * i4]) = v;
+    }
+    XIn xin;
+    Ops ops;
+    load_x(0, xin);
+    // x first, as in the loop: the conv at the loop's top then waits for x alone
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(0, ops);
+    float el = load_el(0);
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = __builtin_amdgcn_readfirstlane(t_begin + c * BT);
+        const int n = __builtin_amdgcn_readfirstlane(t_end - t0 < BT ? t_end - t0 : BT);
+
+        // ---- conv + SiLU of the q | k run -> Qs, Ks (padding tokens: zero),
+        // the same arithmetic as the first pass's
+        {
+            float h0[2], h1[2], h2[2];
+            const uint32_t x0 = xin.qk[0] | xin.qkh[0], x1 = xin.qk[1] | xin.qkh[1], x2 = xin.qk[2] | xin.qkh[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                h0[h] = __uint_as_float(h ? x0 & 0xffff0000u : x0 << 16);
+                h1[h] = __uint_as_float(h ? x1 & 0xffff0000u : x1 << 16);
+                h2[h] = __uint_as_float(h ? x2 & 0xffff0000u : x2 << 16);
+            }
+#pragma unroll
+            for (int tt = 0; tt < TPT; ++tt) {
+                const uint32_t xb = xin.qk[3 + tt];
+                const float xv[2] = {__uint_as_float(xb << 16), __uint_as_float(xb & 0xffff0000u)};
+                float y[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float acc = wq[0][h] * h0[h];
+                    acc = fmaf(wq[1][h], h1[h], acc);
+                    acc = fmaf(wq[2][h], h2[h], acc);
+                    acc = fmaf(wq[3][h], xv[h], acc);
+                    if (has_bias)
+                        acc += bq[h];
+                    y[h] = sp * TPT + tt < n ? acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc)) : 0.f;
+                    h0[h] = h1[h];
+                    h1[h] = h2[h];
+                    h2[h] = xv[h];
+                }
+                *reinterpret_cast<float2 *>(&ydst[(sp * TPT + tt) * KP]) = make_float2(y[0], y[1]);
+            }
+        }
+        // ---- conv + SiLU of v at the lane's places (padding tokens: zero)
+        v4f vv[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float xs[7];
+#pragma unroll
+            for (int i = 0; i < 7; ++i)
+                xs[i] = __uint_as_float((uint32_t)(xin.v[rb][i] | (rb == 0 && i < 3 ? xin.vh[i] : 0u)) << 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float acc = wvc[0] * xs[r];
+                acc = fmaf(wvc[1], xs[r + 1], acc);
+                acc = fmaf(wvc[2], xs[r + 2], acc);
+                acc = fmaf(wvc[3], xs[r + 3], acc);
+                if (has_bias)
+                    acc += bvc;
+                vv[rb][r] = 16 * rb + 4 * lk + r < n ? acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc)) : 0.f;
+            }
+        }
+        load_x(c + 1, xin);
+        __syncthreads(); // Q and K of this chunk; the state after the previous one
+
+        // ---- K^T operands of this wave's state rows (token k-steps in the
+        // accumulator layout's row order), taken now: after the next barrier
+        // the next chunk's conv may rewrite K
+        float kt[RBW][2][4];
+#pragma unroll
+        for (int q = 0; q < RBW; ++q)
+#pragma unroll
+            for (int m4 = 0; m4 < 2; ++m4)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    kt[q][m4][e4] = Ks[(16 * m4 + 4 * lk + e4) * KP + (rb0 + q) * 16 + li];
+
+        // ---- Y = K S0 and Z = Q S0 on column block wv
+        v4f y[2], z[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            y[rb] = z[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m4 = 0; m4 < NA4; ++m4) {
+            const v4f bs = *reinterpret_cast<const v4f *>(&St[(wv * 16 + li) * SPT + 16 * m4 + 4 * lk]);
+            v4f ka[2], qa[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                ka[rb] = *reinterpret_cast<const v4f *>(&Ks[(16 * rb + li) * KP + 16 * m4 + 4 * lk]);
+                qa[rb] = *reinterpret_cast<const v4f *>(&Qs[(16 * rb + li) * KP + 16 * m4 + 4 * lk]);
+            }
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    y[rb] = mma16(ka[rb][e4], bs[e4], y[rb]);
+                    z[rb] = mma16(qa[rb][e4], bs[e4], z[rb]);
+                }
+        }
+
+        // ---- R = V - f_a Y, U = T' R (three independent chains of four)
+        v4f rr[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                rr[rb][r] = fmaf(-ops.fa[rb][r], y[rb][r], vv[rb][r]);
+        v4f u0 = {0.f, 0.f, 0.f, 0.f}, u1a = u0, u1b = u0;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            u0 = mma16(ops.t[0][e4], rr[0][e4], u0);
+            u1a = mma16(ops.t[1][e4], rr[0][e4], u1a);
+            u1b = mma16(ops.t[2][e4], rr[1][e4], u1b);
+        }
+        const v4f u1 = {u1a[0] + u1b[0], u1a[1] + u1b[1], u1a[2] + u1b[2], u1a[3] + u1b[3]};
+
+        // ---- O = f_b Z + P U -> out (rows of real tokens; later rows fall outside)
+        {
+            v4f o0 = {ops.fb[0][0] * z[0][0], ops.fb[0][1] * z[0][1], ops.fb[0][2] * z[0][2], ops.fb[0][3] * z[0][3]};
+            v4f o1a = {ops.fb[1][0] * z[1][0], ops.fb[1][1] * z[1][1], ops.fb[1][2] * z[1][2], ops.fb[1][3] * z[1][3]};
+            v4f o1b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                o0 = mma16(ops.pm[0][e4], u0[e4], o0);
+                o1a = mma16(ops.pm[1][e4], u0[e4], o1a);
+                o1b = mma16(ops.pm[2][e4], u1[e4], o1b);
+            }
+            const v4f o1 = {o1a[0] + o1b[0], o1a[1] + o1b[1], o1a[2] + o1b[2], o1a[3] + o1b[3]};
+            const __amdgpu_buffer_rsrc_t rO =
+                buf_rsrc(p.out + ((size_t)t0 * p.H_v + hv) * DV + col0, (uint32_t)(((n - 1) * p.H_v * DV + DVS) * 2));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(o0[r]), rO,
+                                                      (uint32_t)((4 * lk + r) * p.H_v * DV + 16 * wv + li) * 2u, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    bf16_bits(o1[r]), rO, (uint32_t)((16 + 4 * lk + r) * p.H_v * DV + 16 * wv + li) * 2u, 0, 0);
+            }
+        }
+        // ---- U'' = f_c U -> LDS (transposed, as the wide walk's U)
+        *reinterpret_cast<v4f *>(&Ut[(16 * wv + li) * UPT + 4 * lk]) =
+            v4f{ops.fc[0][0] * u0[0], ops.fc[0][1] * u0[1], ops.fc[0][2] * u0[2], ops.fc[0][3] * u0[3]};
+        *reinterpret_cast<v4f *>(&Ut[(16 * wv + li) * UPT + 16 + 4 * lk]) =
+            v4f{ops.fc[1][0] * u1[0], ops.fc[1][1] * u1[1], ops.fc[1][2] * u1[2], ops.fc[1][3] * u1[3]};
+        load_ops(c + 1, ops);
+        __syncthreads(); // U'' complete; this chunk's reads of the state, K and Q are done
+
+        // ---- S1 = e^gamma_last S0 + K^T U'' on this wave's tiles
+        {
+            v4f sacc[RBW][CBU];
+#pragma unroll
+            for (int q = 0; q < RBW; ++q)
+#pragma unroll
+                for (int jb = 0; jb < CBU; ++jb) {
+                    const v4f s4 =
+                        *reinterpret_cast<const v4f *>(&St[((cbu0 + jb) * 16 + li) * SPT + (rb0 + q) * 16 + 4 * lk]);
+                    sacc[q][jb] = v4f{el * s4[0], el * s4[1], el * s4[2], el * s4[3]};
+                }
+#pragma unroll
+            for (int m4 = 0; m4 < 2; ++m4)
+#pragma unroll
+                for (int jb = 0; jb < CBU; ++jb) {
+                    const v4f ub = *reinterpret_cast<const v4f *>(&Ut[((cbu0 + jb) * 16 + li) * UPT + 16 * m4 + 4 * lk]);
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+                        for (int q = 0; q < RBW; ++q)
+                            sacc[q][jb] = mma16(kt[q][m4][e4], ub[e4], sacc[q][jb]);
+                }
+#pragma unroll
+            for (int q = 0; q < RBW; ++q)
+#pragma unroll
+                for (int jb = 0; jb < CBU; ++jb)
+                    *reinterpret_cast<v4f *>(&St[((cbu0 + jb) * 16 + li) * SPT + (rb0 + q) * 16 + 4 * lk]) = sacc[q][jb];
+        }
+        el = load_el(c + 1);
+    }
+    __syncthreads(); // the last update is in LDS
+
+    // ---- the state's slice back to the slot (the same mapping)
+    for (int e2 = tid; e2 < DK * DVS / 4; e2 += NTS) {
+        const int j = e2 % DVS, i4 = e2 / DVS;
+        const v4f v = *reinterpret_cast<const v4f *>(&St[j * SPT + 4 * i4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __builtin_nontemporal_store(v[r], tile + (size_t)(4 * i4 + r) * DV + col0 + j);
+    }
+    advance_windows<DK, DV, DVS, NTS>(p, hv, 0, t_begin, t_end, s);
+}
+
 template <int DK, int DV, int DVS>
 hipError_t launch_inter(const TwoPassParams &tp, long long heads, hipStream_t stream)
 {
@@ -1085,8 +1483,17 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
     const long long nchunk_max = ((long long)p.total + BT - 1) / BT + p.B;
     long long gx = 512 / p.H_v;
     gx = gx < 1 ? 1 : (gx > nchunk_max ? nchunk_max : gx);
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV>), dim3((unsigned)gx, (unsigned)p.H_v),
-                        dim3(NT), args, 0, stream);
+    const long long heads = (long long)p.B * p.H_v;
+    if (tp.ws.slim) {
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV, true>),
+                            dim3((unsigned)gx, (unsigned)p.H_v), dim3(NT), args, 0, stream);
+        if (e != hipSuccess)
+            return e;
+        return hipLaunchKernel(reinterpret_cast<const void *>(&tp_slim_kernel<DK, DV>), dim3((unsigned)heads),
+                               dim3(4 * DV), args, 0, stream);
+    }
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV, false>),
+                        dim3((unsigned)gx, (unsigned)p.H_v), dim3(NT), args, 0, stream);
     if (e != hipSuccess)
         return e;
     // column slices 64, 32 or 16 wide (two workgroups a CU fit; with whole
@@ -1096,7 +1503,6 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
     // ceil(heads nsl / 256) / nsl least, the fewer slices on a tie (measured
     // on MI355X against doubling until 256 workgroups: 6 x 1024 221 -> 215 us,
     // 12 x 768 306 -> 296; the power-of-two batches keep their choice)
-    const long long heads = (long long)p.B * p.H_v;
     int nsl = DV / 64 > 1 ? DV / 64 : 1;
     long long best = (heads * nsl + 255) / 256; // per-CU share, in units of 1 / nsl
     for (int n = 2 * nsl; n <= DV / 16; n *= 2) {
@@ -1119,40 +1525,61 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 } // namespace
 
-size_t two_pass_layout(int B, int total, int H_v, int d_k, int d_v, void *base, TwoPassWorkspace *ws)
+bool two_pass_slim(int B, int H_v, int d_k, int d_v)
+{
+    // the slim walk's workgroups (one a prompt and value head) fill the 256
+    // compute units at least once
+    return d_k % 64 == 0 && d_v % 64 == 0 && (long long)B * H_v >= 256;
+}
+
+size_t two_pass_layout(int B, int total, int H_k, int H_v, int d_k, int d_v, void *base, TwoPassWorkspace *ws)
 {
     // chunk blocks per head: an upper bound on the call's chunk count (each
     // sequence adds at most one partial chunk)
     const size_t nchunk = ((size_t)total + BT - 1) / BT + (size_t)B;
     const size_t blocks = (size_t)H_v * nchunk;
+    const bool slim = two_pass_slim(B, H_v, d_k, d_v);
     size_t off = 0;
-    const size_t o_cs = off;
-    off = round_up(off + (size_t)(B + 1) * sizeof(int32_t));
-    const size_t o_rec = off;
-    off = round_up(off + nchunk * 4 * sizeof(int32_t));
-    const size_t o_qa = off;
-    off = round_up(off + blocks * BT * d_k * sizeof(float));
-    const size_t o_wa = off;
-    off = round_up(off + blocks * BT * d_k * sizeof(float));
-    const size_t o_ka = off;
-    off = round_up(off + blocks * BT * d_k * sizeof(float));
-    const size_t o_pa = off;
-    off = round_up(off + blocks * BT * BT * sizeof(float));
-    const size_t o_ud = off;
-    off = round_up(off + blocks * BT * d_v * sizeof(float));
-    const size_t o_el = off;
-    off = round_up(off + blocks * sizeof(float));
+    auto region = [&](size_t bytes) {
+        const size_t o = off;
+        off = round_up(off + bytes);
+        return o;
+    };
+    const size_t o_cs = region((size_t)(B + 1) * sizeof(int32_t));
+    const size_t o_rec = region(nchunk * 4 * sizeof(int32_t));
+    size_t o_qa = 0, o_wa = 0, o_ka = 0, o_ud = 0, o_el = 0, o_ta = 0, o_fac = 0, o_hw = 0;
+    if (slim) {
+        o_ta = region(blocks * BT * BT * sizeof(float));
+        o_fac = region(blocks * 128 * sizeof(float));
+        o_hw = region((size_t)B * 3 * ((size_t)2 * H_k * d_k + (size_t)H_v * d_v) * sizeof(uint16_t));
+    } else {
+        o_qa = region(blocks * BT * d_k * sizeof(float));
+        o_wa = region(blocks * BT * d_k * sizeof(float));
+        o_ka = region(blocks * BT * d_k * sizeof(float));
+        o_ud = region(blocks * BT * d_v * sizeof(float));
+        o_el = region(blocks * sizeof(float));
+    }
+    const size_t o_pa = region(blocks * BT * BT * sizeof(float));
     if (base && ws) {
         char *c = static_cast<char *>(base);
+        auto f = [&](size_t o) { return reinterpret_cast<float *>(c + o); };
+        *ws = TwoPassWorkspace{};
         ws->chunk_start = reinterpret_cast<int32_t *>(c + o_cs);
         ws->chunk_rec = reinterpret_cast<int32_t *>(c + o_rec);
-        ws->qa = reinterpret_cast<float *>(c + o_qa);
-        ws->wa = reinterpret_cast<float *>(c + o_wa);
-        ws->ka = reinterpret_cast<float *>(c + o_ka);
-        ws->pa = reinterpret_cast<float *>(c + o_pa);
-        ws->ud = reinterpret_cast<float *>(c + o_ud);
-        ws->el = reinterpret_cast<float *>(c + o_el);
+        ws->pa = f(o_pa);
+        if (slim) {
+            ws->ta = f(o_ta);
+            ws->fac = f(o_fac);
+            ws->hw = reinterpret_cast<uint16_t *>(c + o_hw);
+        } else {
+            ws->qa = f(o_qa);
+            ws->wa = f(o_wa);
+            ws->ka = f(o_ka);
+            ws->ud = f(o_ud);
+            ws->el = f(o_el);
+        }
         ws->nchunk = (int)nchunk;
+        ws->slim = slim ? 1 : 0;
     }
     return off;
 }

@@ -31,7 +31,9 @@ hipError_t launch_gdn_prefill(const PrefillParams &p, int d_k, int d_v, hipStrea
 // start at chunk_start[b]); the workspace holds nchunk = ceil(total / 32) + B
 // chunk blocks per value head, block (hv, g) at hv * nchunk + g, each laid out
 // as the second pass's matrix-core operands, so it loads them straight into
-// registers:
+// registers.  Two layouts, picked by two_pass_slim from the call's shape:
+// full (the second pass reads every product of the chunk that does not depend
+// on the state):
 //   qa, wa  [2 row blocks][d_k / 16][64 lanes][4]: q~ = e^gamma q^ and
 //           w = ((I + A)^-1 diag(beta e^gamma) K), element (rb, m, lane) the
 //           A operand of k-slice m: row rb * 16 + lane % 16, column 4 m + lane / 16
@@ -43,14 +45,27 @@ hipError_t launch_gdn_prefill(const PrefillParams &p, int d_k, int d_v, hipStrea
 //           diag(beta) V) in the accumulator layout, lane j + 16 g holding rows
 //           4 g .. 4 g + 3 of column j
 //   el      e^gamma_last of the chunk
+// slim (the second pass runs the conv itself and forms U from T'):
+//   ta      [2][2][64][4]: T' = (I + A)^-1 diag(beta) as an A operand, like pa
+//   pa      as above
+//   fac     [128] floats: per token t < 32 the row factors k-norm e^gamma
+//           ([0, 32)), q-norm q_scale e^gamma ([32, 64)) and
+//           k-norm e^(gamma_last - gamma) ([64, 96)), each zero for a padding
+//           token; e^gamma_last at [96]
+//   hw      [B][3][C] bf16: each prompt's conv window as the call found it
+//           (the second pass's first chunk takes its three earlier inputs from
+//           here, as another workgroup may already have advanced the slot's)
 // and, per chunk of the call, its record [nchunk][4]: first token, tokens
-// (at most 32), slot, and 1 for a sequence's first chunk (whose three earlier
-// inputs come from the slot's window) else 0.
+// (at most 32), slot, and for a sequence's first chunk (whose three earlier
+// inputs come from the slot's window) the sequence's index + 1, else 0.
 struct TwoPassWorkspace {
     int32_t *chunk_start; // [B+1]: exclusive scan of each sequence's chunk count
     int32_t *chunk_rec;   // [nchunk][4]
-    float *qa, *wa, *ka, *pa, *ud, *el;
+    float *qa, *wa, *ka, *pa, *ud, *el; // full layout (pa in both)
+    float *ta, *fac;                    // slim layout
+    uint16_t *hw;                       // slim layout
     int nchunk;
+    int slim;
 };
 
 struct TwoPassParams {
@@ -58,9 +73,13 @@ struct TwoPassParams {
     TwoPassWorkspace ws;
 };
 
-// Bytes of the workspace for B sequences, total tokens, H_v heads, d_k, d_v;
-// with a base pointer, also the regions (each 256-byte aligned).
-size_t two_pass_layout(int B, int total, int H_v, int d_k, int d_v, void *base, TwoPassWorkspace *ws);
+// Whether a call of B sequences over H_v value heads takes the slim layout and
+// its second pass (64-column slices, at least one workgroup a compute unit).
+bool two_pass_slim(int B, int H_v, int d_k, int d_v);
+
+// Bytes of the workspace for B sequences, total tokens, H_k / H_v heads, d_k,
+// d_v; with a base pointer, also the regions (each 256-byte aligned).
+size_t two_pass_layout(int B, int total, int H_k, int H_v, int d_k, int d_v, void *base, TwoPassWorkspace *ws);
 
 hipError_t launch_gdn_prefill_two_pass(const TwoPassParams &p, int d_k, int d_v, hipStream_t stream);
 

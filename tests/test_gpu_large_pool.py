@@ -140,10 +140,12 @@ def test_per_token_states_past_4gib(gdn, torch, big):
     bp.check(hp.state, hp.conv_state, tok.ravel())
 
 
-@pytest.mark.parametrize("two_pass", [False, True], ids=["one-kernel", "two-pass"])
-def test_prefill_past_4gib(gdn, torch, big, two_pass):
+@pytest.mark.parametrize("two_pass,lengths", [(False, [45, 3, 70]), (True, [45, 3, 70]),
+                                              (True, [45, 3, 70, 12, 33, 1, 64, 20] * 2)],
+                         ids=["one-kernel", "two-pass", "two-pass-slim"])
+def test_prefill_past_4gib(gdn, torch, big, two_pass, lengths):
     t = torch
-    case = gi.prefill([45, 3, 70], H_k=H_K, H_v=H_V, d=D, seed=64)
+    case = gi.prefill(lengths, H_k=H_K, H_v=H_V, d=D, seed=64)
     s, pool = case.shape, case.pool
     bp = BigPool(t, big, pool)
     hp = H.HostPool(pool)

@@ -122,8 +122,8 @@ def test_prefill_08b_shapes(gdn, torch, two_pass):
 
 def test_two_pass_long_prompt_and_slices(gdn, torch):
     """One long prompt (16-column slices, the state in registers; every chunk in
-    flight in pass 1), then many short ones (64-column slices, the state in LDS),
-    at the 0.8B shapes."""
+    flight in pass 1), then many short ones (the slim layout: the conv run again
+    in the walk), at the 0.8B shapes."""
     _check(gdn, torch, gi.prefill([1000], H_k=16, H_v=16, d=128, seed=21), two_pass=True)
     _check(gdn, torch, gi.prefill([3, 40, 1, 33] * 4 + [2] * 8, H_k=16, H_v=16, d=128, N=97, seed=22),
            two_pass=True)
@@ -150,18 +150,70 @@ def test_two_pass_bench_workload_one_long_prompt(gdn, torch):
 
 @pytest.mark.parametrize("lengths,hk,hv", [
     ([100, 33, 64, 5], 16, 16),                                     # 64 heads: 32-column slices
-    ([40, 1, 70, 32, 31, 65, 2, 50], 16, 16),                       # 128 heads: 64-column slices
+    ([40, 1, 70, 32, 31, 65, 2], 16, 16),                           # 112 heads: 64-column slices
     ([9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20, 6], 2, 4),  # 68 heads: 16-column, 4 past the last group of 8
     ([9, 40, 1, 33, 64, 2, 17, 30, 5], 2, 4),                       # 36 heads: 32-column, 4 past the last group of 8
+    ([40, 1, 70, 32, 31, 65, 2, 50], 16, 16),                       # 128 heads: 64-column slices
     ([30, 7, 61, 2, 33, 12, 40, 1, 64, 25, 3, 50], 16, 16),         # 192 heads: 32-column slices
     ([40, 3, 65, 32, 1, 70], 16, 16),                               # 96 heads: 16-column slices
-], ids=["4seq-slices32", "8seq-slices64", "17seq-slices16-tail", "9seq-slices32-tail", "12seq-slices32",
-        "6seq-slices16"])
+], ids=["4seq-slices32", "7seq-slices64", "17seq-slices16-tail", "9seq-slices32-tail", "8seq-slices64",
+        "12seq-slices32", "6seq-slices16"])
 def test_two_pass_wide_slices(gdn, torch, lengths, hk, hv):
     """The walk over column slices of each width the call's head count picks
-    (16 wide: the state in registers; 32 and 64: state and U in LDS), and
-    prompt-head pairs past the last whole group of eight placed in order."""
+    under 256 heads (16 wide: the state in registers; 32 and 64: state and U
+    in LDS), and prompt-head pairs past the last whole group of eight placed in
+    order."""
     _check(gdn, torch, gi.prefill(lengths, H_k=hk, H_v=hv, d=128, seed=len(lengths) + 90), two_pass=True)
+
+
+SLIM_CASES = [
+    # lengths, H_k, H_v, d_k, d_v, padding prompts; B * H_v >= 256
+    ((1, 5, 32, 33, 70, 0, 100, 7, 64, 31, 2, 40, 9, 16, 65, 3), 8, 16, 128, 128, (7,)),  # G = 2, chunk edges, an empty
+                                                                                           # and a padding prompt
+    ((40, 17, 3, 65, 96, 2, 33, 12) * 2, 4, 16, 128, 128, ()),       # G = 4
+    ((64, 3, 200, 1, 31, 9, 9, 9, 9, 9, 9, 9, 9, 9, 9, 9), 16, 16, 64, 64, (2,)),  # d = 64, a long padding prompt
+    ((31, 65, 2, 40) * 4, 16, 16, 128, 64, ()),                      # d_k > d_v
+    ((31, 65, 2, 40, 7, 33, 64, 1) * 2, 16, 16, 64, 128, (1,)),      # d_k < d_v
+    ((9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20, 6), 16, 16, 128, 128, ()),  # 272 heads: a second round
+]
+
+
+@pytest.mark.parametrize("lengths,hk,hv,d,dv,pad", SLIM_CASES,
+                         ids=[f"{len(c[0])}seq-{c[1]}x{c[2]}-d{c[3]}x{c[4]}" for c in SLIM_CASES])
+def test_two_pass_slim_layout(gdn, torch, lengths, hk, hv, d, dv, pad):
+    """The slim layout (calls whose walk, a workgroup a prompt and value head,
+    fills the compute units): pass 1 keeps T', P and the row factors only, and
+    the walk runs the conv again from x, with a prompt's first inputs from the
+    window copy; GQA groups of 2 and 4, d = 64, d_k != d_v, padding and empty
+    prompts, more workgroups than compute units."""
+    case = gi.prefill(list(lengths), H_k=hk, H_v=hv, d=d, d_v=dv, pad=pad, seed=len(lengths) + d + 400)
+    _, out = _check(gdn, torch, case, two_pass=True)
+    for b in pad:
+        a, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        assert torch.count_nonzero(out[a:e].view(torch.int16)) == 0, "padding sequences read out +0.0"
+
+
+def test_two_pass_slim_bias_and_q_scale(gdn, torch):
+    """A conv bias and q_scale through the slim walk's own conv and row factors."""
+    case = gi.prefill([45, 12, 33, 64, 1, 80, 31, 2] * 2, H_k=16, H_v=16, d=128, seed=12)
+    bias = gi.bf16_bits(np.random.Generator(np.random.PCG64(5)).standard_normal(case.shape.C).astype(np.float32))
+    _check(gdn, torch, case, conv_b=bias, q_scale=128 ** -0.5, two_pass=True)
+
+
+@pytest.mark.parametrize("g_scale", [0.01, 0.0], ids=["weak-decay", "no-decay"])
+def test_two_pass_slim_long_prompts_weak_or_no_decay(gdn, torch, g_scale):
+    """Sixteen prompts of 384 tokens (the slim layout) with the log decay scaled
+    by 0.01 and with g = 0: the chunked form's rounding would build up here."""
+    case = gi.prefill([384] * 16, H_k=16, H_v=16, d=128, seed=34)
+    case.g[:] = (case.g * np.float32(g_scale)).astype(np.float32)
+    _check(gdn, torch, case, two_pass=True)
+
+
+def test_two_pass_bench_workload_many_prompts(gdn, torch):
+    """The prefill bench's many-prompt workload as it times it: 16 prompts of 512
+    tokens at the 0.8B-like shapes (the slim layout), every output row and every
+    final state against the oracle."""
+    _check(gdn, torch, gi.prefill([512] * 16, H_k=16, H_v=16, d=128, seed=32), two_pass=True)
 
 
 @PATHS
@@ -229,13 +281,15 @@ def test_prefill_unusable_ranges_touch_nothing(gdn, torch, two_pass):
     assert bool((out[10:].float() == 7.0).all()), "rows of unusable sequences stay as they were"
 
 
-def test_two_pass_graph_replay_matches_eager(gdn, torch):
+@pytest.mark.parametrize("lengths,hk,hv", [([70, 5, 33], 2, 4), ([70, 5, 33, 12, 40, 1, 64, 9] * 2, 16, 16)],
+                         ids=["full-layout", "slim-layout"])
+def test_two_pass_graph_replay_matches_eager(gdn, torch, lengths, hk, hv):
     """The two-pass prefill (three launches, a caller workspace, no allocation)
     captured once and replayed several times, with eager work between replays,
     gives the bits of the same calls run eagerly (each replay continues the
-    prompts from where the previous one left the slots)."""
+    prompts from where the previous one left the slots), in both layouts."""
     t = torch
-    case = gi.prefill([70, 5, 33], H_k=2, H_v=4, d=128, seed=31)
+    case = gi.prefill(lengths, H_k=hk, H_v=hv, d=128, seed=31)
     s = case.shape
     dp_e, dp_g = H.DevPool(case.pool), H.DevPool(case.pool)
     x, g, beta = H.bf16_dev(case.x), t.from_numpy(case.g).cuda(), t.from_numpy(case.beta).cuda()
