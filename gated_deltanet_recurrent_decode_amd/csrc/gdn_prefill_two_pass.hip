@@ -1198,11 +1198,13 @@ __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         const int t0 = t_begin + cc * BT;
         const int n = t_end - t0 < BT ? t_end - t0 : BT;
         const int sh = cc == 0 ? 0 : 3; // rows of x before the chunk in the resource
+        // (sizes times 0 or 1, not a choice: a choice here becomes a branch,
+        // which would keep these loads out of the products they are issued among)
         const __amdgpu_buffer_rsrc_t rx =
             buf_rsrc(p.x + (size_t)(t0 - sh) * p.x_row_stride,
-                     real ? (uint32_t)(((size_t)(n - 1 + sh) * p.x_row_stride + C) * 2) : 0u);
+                     (uint32_t)(((size_t)(n - 1 + sh) * p.x_row_stride + C) * 2) * (uint32_t)real);
         const __amdgpu_buffer_rsrc_t rh =
-            buf_rsrc(tp.ws.hw + (size_t)b * 3 * C, real && cc == 0 ? (uint32_t)(3 * C * 2) : 0u);
+            buf_rsrc(tp.ws.hw + (size_t)b * 3 * C, (uint32_t)(3 * C * 2) * (uint32_t)(real && cc == 0));
 #pragma unroll
         for (int i = 0; i < TPT + 3; ++i) {
             const int t = sp * TPT - 3 + i;
@@ -1332,7 +1334,6 @@ __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 vv[rb][r] = 16 * rb + 4 * lk + r < n ? acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc)) : 0.f;
             }
         }
-        load_x(c + 1, xin);
         __syncthreads(); // Q and K of this chunk; the state after the previous one
 
         // ---- K^T operands of this wave's state rows (token k-steps in the
@@ -1368,6 +1369,14 @@ __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                     y[rb] = mma16(ka[rb][e4], bs[e4], y[rb]);
                     z[rb] = mma16(qa[rb][e4], bs[e4], z[rb]);
                 }
+        }
+        // the next chunk's x loads go out among these products, so their
+        // address processing runs under the matrix cores
+        load_x(c + 1, xin);
+#pragma unroll
+        for (int i = 0; i < (TPT + 3) + 3 + 2 * 7 + 3; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // one vector-memory read
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0); // three MFMA
         }
 
         // ---- R = V - f_a Y, U = T' R (three independent chains of four)
