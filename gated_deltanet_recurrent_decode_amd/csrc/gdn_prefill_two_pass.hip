@@ -146,20 +146,24 @@ __global__ __launch_bounds__(NT) void tp_chunk_map_kernel(TwoPassParams tp)
 
 // ---------------------------------------------------------------- pass 1
 
-// two workgroups a CU (LDS allows two): at most 256 registers a lane, which
-// the compiler meets by recomputing LDS addresses inside the chunk loop.
-// SLIM: the slim layout (T', P and the row factors; no V, W or U~), and each
-// prompt's old window copied to hw at its first chunk.
+// full layout: two workgroups a CU (LDS allows two), at most 256 registers a
+// lane, which the compiler meets by recomputing LDS addresses inside the chunk
+// loop; slim: three (at most 168 registers).
+// SLIM: the slim layout (T', P and the row factors; no V, W or U~), the q | k
+// conv spread over every lane in runs of tokens, and each prompt's old window
+// copied to hw at its first chunk.
 template <int DK, int DV, bool SLIM>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void tp_intra_kernel(TwoPassParams tp)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2, SLIM ? 3 : 2))) void tp_intra_kernel(TwoPassParams tp)
 {
     const PrefillParams &p = tp.p;
-    constexpr int NPAIR = SLIM ? DK : (2 * DK + DV) / 2; // conv lanes, two channels each
-    constexpr int VPAIR = SLIM ? DV / 2 : 0;              // slim: lanes that copy the v channels' old window
+    constexpr int NPAIR = SLIM ? NT : (2 * DK + DV) / 2; // conv lanes, two channels each
+    constexpr int NRUN = SLIM ? NT / DK : 1;             // runs of tokens (slim: DK pairs a run)
+    constexpr int TPT = BT / NRUN;                       // tokens a run
+    static_assert(!SLIM || (NT % DK == 0 && BT % NRUN == 0), "whole runs");
     // LDS pitches as in the one-kernel prefill: A-style operand reads along a
     // row want 4 mod 32, B-style reads down a column 16 mod 32
     constexpr int KP = DK + 4, VP = DV + 16, AP = BT + 1;
-    static_assert(NPAIR + VPAIR <= NT, "one conv lane per channel pair");
+    static_assert(NPAIR <= NT, "one conv lane per channel pair");
     static_assert((2 * (DK / 16) * 64) % NT == 0, "whole store rounds");
 
     __shared__ __align__(16) float Qs[BT * KP];
@@ -184,10 +188,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         return;
 
     // ---- conv lanes: channel pair (e, e+1) of the q | k | v channels of (hk, hv)
-    // (slim: q | k only, and copy lanes for the v channels' window)
+    // (slim: the q | k channels, run `run` of the chunk's tokens)
     const bool conv_lane = tid < NPAIR;
-    const bool copy_lane = SLIM && !conv_lane && tid < NPAIR + VPAIR;
-    const int e = conv_lane ? 2 * tid : copy_lane ? 2 * DK + 2 * (tid - NPAIR) : 0;
+    const int run = SLIM ? __builtin_amdgcn_readfirstlane(tid / DK) : 0; // the same across a wave
+    const int e = SLIM ? 2 * (tid % DK) : conv_lane ? 2 * tid : 0;
     const bool isq = e < DK, isk = !isq && e < 2 * DK;
     const int ch = isq ? hk * DK + e : isk ? p.H_k * DK + hk * DK + (e - DK) : 2 * p.H_k * DK + hv * DV + (e - 2 * DK);
     float w0[2], w1[2], w2[2], w3[2], bias[2];
@@ -208,10 +212,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // gates come through buffer resources over the chunk's real rows (later
     // rows read zeros), so no branch surrounds those loads.
     struct ChunkIn {
-        uint32_t xb[BT];
-        uint32_t hist[3];
+        uint32_t xb[TPT];
+        uint32_t hist[3]; // the three inputs before the run: window or x
         float g_in, b_in;
-        int t0, n;
+        int t0, n, sl;
         int b1; // the sequence's index + 1 at its first chunk, else 0
     };
     auto load = [&](int gi, ChunkIn &in) {
@@ -222,19 +226,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int sl = __builtin_amdgcn_readfirstlane(rec.z);
         const int b1 = __builtin_amdgcn_readfirstlane(rec.w);
         const bool first = b1 != 0;
-        const uint16_t *hb = first ? p.conv_state + (size_t)sl * 3 * C + ch
-                                   : p.x + (size_t)(t0 - 3) * p.x_row_stride + ch;
-        const size_t hs = first ? (size_t)C : (size_t)p.x_row_stride;
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            in.hist[k] = *reinterpret_cast<const uint32_t *>(hb + k * hs);
         const __amdgpu_buffer_rsrc_t rx =
             buf_rsrc(p.x + (size_t)t0 * p.x_row_stride, (uint32_t)(((n - 1) * p.x_row_stride + C) * 2));
+        // the three inputs before the first run: the slot's window for a
+        // prompt's first chunk, else x; before a later run (slim): x rows of
+        // the chunk itself (a resource chosen per wave)
+        const uint16_t *hb = first ? p.conv_state + (size_t)sl * 3 * C : p.x + (size_t)(t0 - 3) * p.x_row_stride;
+        const int hs = first ? C : (int)p.x_row_stride;
+        const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hb, (uint32_t)((2 * (int64_t)hs + C) * 2));
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            in.hist[k] = __builtin_amdgcn_raw_buffer_load_b32(
+                run == 0 ? rh : rx,
+                run == 0 ? (uint32_t)(k * hs + ch) * 2u : (uint32_t)((run * TPT - 3 + k) * p.x_row_stride + ch) * 2u, 0, 0);
         // (lanes without a channel pair load nothing: past the resource)
 #pragma unroll
-        for (int tt = 0; tt < BT; ++tt)
+        for (int tt = 0; tt < TPT; ++tt)
             in.xb[tt] = __builtin_amdgcn_raw_buffer_load_b32(
-                rx, conv_lane ? (uint32_t)(tt * p.x_row_stride + ch) * 2u : kOOB, 0, 0);
+                rx, conv_lane ? (uint32_t)((run * TPT + tt) * p.x_row_stride + ch) * 2u : kOOB, 0, 0);
         const __amdgpu_buffer_rsrc_t rg = buf_rsrc(p.g + (size_t)t0 * p.H_v, (uint32_t)(n * p.H_v * 4));
         const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(p.beta + (size_t)t0 * p.H_v, (uint32_t)(n * p.H_v * 4));
         const uint32_t goff = (uint32_t)((tid & (BT - 1)) * p.H_v + hv) * 4u; // lanes past BT: unused copies
@@ -242,6 +251,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         in.b_in = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_, goff, 0, 0));
         in.t0 = t0;
         in.n = n;
+        in.sl = sl;
         in.b1 = b1;
     };
 
@@ -249,19 +259,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     load(blockIdx.x, cur);
     for (int g = blockIdx.x; g < nch; g += gridDim.x) {
         const int n = cur.n;
+        const uint32_t *hx = cur.hist;
         float h0[2], h1[2], h2[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            h0[h] = __uint_as_float(h ? cur.hist[0] & 0xffff0000u : cur.hist[0] << 16);
-            h1[h] = __uint_as_float(h ? cur.hist[1] & 0xffff0000u : cur.hist[1] << 16);
-            h2[h] = __uint_as_float(h ? cur.hist[2] & 0xffff0000u : cur.hist[2] << 16);
+            h0[h] = __uint_as_float(h ? hx[0] & 0xffff0000u : hx[0] << 16);
+            h1[h] = __uint_as_float(h ? hx[1] & 0xffff0000u : hx[1] << 16);
+            h2[h] = __uint_as_float(h ? hx[2] & 0xffff0000u : hx[2] << 16);
         }
 
         // slim: a prompt's first chunk keeps its old window for the second pass
-        if (SLIM && cur.b1 != 0 && (conv_lane || copy_lane)) {
+        // (q | k from the first run's lanes, the v channels copied here)
+        if (SLIM && cur.b1 != 0) {
+            if (run == 0) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k)
-                *reinterpret_cast<uint32_t *>(tp.ws.hw + ((size_t)(cur.b1 - 1) * 3 + k) * C + ch) = cur.hist[k];
+                for (int k = 0; k < 3; ++k)
+                    *reinterpret_cast<uint32_t *>(tp.ws.hw + ((size_t)(cur.b1 - 1) * 3 + k) * C + ch) = cur.hist[k];
+            }
+            for (int q = tid; q < DV / 2; q += NT) {
+                const int cv = 2 * p.H_k * DK + hv * DV + 2 * q;
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    *reinterpret_cast<uint32_t *>(tp.ws.hw + ((size_t)(cur.b1 - 1) * 3 + k) * C + cv) =
+                        *reinterpret_cast<const uint32_t *>(p.conv_state + ((size_t)cur.sl * 3 + k) * C + cv);
+            }
         }
 
         // ---- conv + SiLU; rows past the chunk's last token stay zero
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             // Tokens past the chunk's end are computed on the zeros their loads
             // returned and stored as zero, with no branch per token.
 #pragma unroll
-            for (int tt = 0; tt < BT; ++tt) {
+            for (int tt = 0; tt < TPT; ++tt) {
                 const float x0 = __uint_as_float(cur.xb[tt] << 16), x1 = __uint_as_float(cur.xb[tt] & 0xffff0000u);
                 float acc0 = w0[0] * h0[0];
                 acc0 = fmaf(w1[0], h1[0], acc0);
@@ -287,12 +308,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                     acc0 += bias[0];
                     acc1 += bias[1];
                 }
-                const bool live = tt < n;
+                const bool live = run * TPT + tt < n;
                 const float y0 = live ? acc0 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc0)) : 0.f;
                 const float y1 = live ? acc1 * __builtin_amdgcn_rcpf(1.0f + __expf(-acc1)) : 0.f;
                 h0[0] = h1[0]; h1[0] = h2[0]; h2[0] = x0;
                 h0[1] = h1[1]; h1[1] = h2[1]; h2[1] = x1;
-                *reinterpret_cast<float2 *>(&ydst[tt * ypitch]) = make_float2(y0, y1);
+                *reinterpret_cast<float2 *>(&ydst[(run * TPT + tt) * ypitch]) = make_float2(y0, y1);
             }
         }
         // the next chunk's inputs load while this one computes; issued after
@@ -1488,9 +1509,9 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     // pass 1 walks the chunks with about two resident workgroups a compute
-    // unit (its LDS allows two), each taking every gx-th chunk of a head
+    // unit (three in the slim layout), each taking every gx-th chunk of a head
     const long long nchunk_max = ((long long)p.total + BT - 1) / BT + p.B;
-    long long gx = 512 / p.H_v;
+    long long gx = (tp.ws.slim ? 768 : 512) / p.H_v;
     gx = gx < 1 ? 1 : (gx > nchunk_max ? nchunk_max : gx);
     const long long heads = (long long)p.B * p.H_v;
     if (tp.ws.slim) {
