@@ -86,8 +86,8 @@ PREFILL_KERNELS = ("_ZN3gdn12_GLOBAL__N_119tp_chunk_map_kernelENS_13TwoPassParam
                    "_ZN3gdn12_GLOBAL__N_115tp_inter_kernelILi128ELi128ELi64EEEvNS_13TwoPassParamsE",
                    "_ZN3gdn12_GLOBAL__N_117tp_inter16_kernelILi128ELi128EEEvNS_13TwoPassParamsE",
                    "_ZN3gdn12_GLOBAL__N_114tp_slim_kernelILi128ELi128EEEvNS_13TwoPassParamsE")
-MEASURED_PREFILL_TRAFFIC = {"kernel_code_sha256": "f0947739f8a69197219350d1fd3a40ba7bda42d672fe28b610ab0dbf4e11cb59",
-                            "bytes_per_call": {(16, 512): 754_928_363, (1, 4096): 364_499_998}}
+MEASURED_PREFILL_TRAFFIC = {"kernel_code_sha256": "bb82c38ed2e6b6a38e062e3976302c160543809cc731db032d7c24d08bcbaff8",
+                            "bytes_per_call": {(16, 512): 309_907_705, (1, 4096): 364_120_357}}
 
 
 # The no-math copy designs the calibration sweeps (gdn_traffic_probe): the

@@ -198,13 +198,17 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
 
 /*
  * gdn_prefill_two_pass -- the same computation and contract as gdn_prefill,
- * for calls with few prompts: it runs in two passes with a caller-provided
- * workspace.  The first pass works on every 32-token chunk of every prompt at
- * once (conv decode + SiLU, L2 norms, the chunk's decay and the triangular
- * solve of the chunked delta rule, PR #1139 "What changed": prefill in place),
- * the second walks each prompt's chunks in order with the d_v columns of each
- * head split over several workgroups.  Results match gdn_prefill within
- * rounding, not bit for bit.
+ * in two passes with a caller-provided workspace.  The first pass works on
+ * every 32-token chunk of every prompt at once (conv decode + SiLU, L2 norms,
+ * the chunk's decay and the triangular solve of the chunked delta rule,
+ * PR #1139 "What changed": prefill in place), the second walks each prompt's
+ * chunks in order.  Under 256 prompt-head pairs (B H_v) the first pass also
+ * forms every product of a chunk that does not depend on the state and the
+ * second splits each head's d_v columns over several workgroups (a single
+ * long prompt fills the chip); from 256 pairs up the first pass keeps only
+ * the chunk's solve and per-token factors and the second, a workgroup per
+ * prompt and head, runs the conv again from x (an eighth of the workspace).
+ * Results match gdn_prefill within rounding, not bit for bit.
  *
  * workspace: device memory of at least
  * gdn_prefill_two_pass_workspace_bytes(dims) bytes, 256-byte aligned, owned
@@ -232,7 +236,9 @@ gdn_status gdn_prefill_two_pass(const gdn_dims *dims, const gdn_bf16 *x, int64_t
  * on the first call on that device.  A call whose workspace
  * (gdn_prefill_two_pass_workspace_bytes of the same dims) exceeds it returns
  * GDN_ERR_SCRATCH and enqueues nothing: at 16 value heads of 128 x 128 that
- * is 1,888 tokens for one prompt, 32 fewer for each further prompt.  Every
+ * is 1,888 tokens for one prompt, 32 fewer for each further prompt, while
+ * a call of 16 such prompts (256 prompt-head pairs: the slim workspace)
+ * holds 14,752 tokens.  Every
  * call on a GPU shares that GPU's buffer, so calls that overlap on one GPU
  * (on different streams, or from different threads without stream order
  * between them) race; calls ordered on one stream do not.  The buffer's
@@ -248,11 +254,13 @@ gdn_status gdn_prefill_two_pass_noalloc(const gdn_dims *dims, const gdn_bf16 *x,
 
 /*
  * gdn_prefill_two_pass_workspace_bytes -- the workspace gdn_prefill_two_pass
- * needs for dims (B sequences, T packed tokens, H_v, d_k, d_v): room for
+ * needs for dims (B sequences, T packed tokens, H_k, H_v, d_k, d_v): room for
  * K = ceil(T / 32) + B chunks (every sequence adds at most one partial chunk)
- * per value head, each chunk (3 d_k + d_v + 32) * 32 + 1 fp32 values, plus
- * B + 1 int32 and 4 int32 per chunk; each region rounded up to 256 bytes.  0
- * when dims is NULL or its sizes are unusable.
+ * per value head, each chunk (3 d_k + d_v + 32) * 32 + 1 fp32 values under
+ * 256 prompt-head pairs (B H_v), else 2 * 32 * 32 + 128 fp32 values, plus in
+ * that case B * 3 * C bf16 (C = 2 H_k d_k + H_v d_v, a copy of each prompt's
+ * window); plus B + 1 int32 and 4 int32 per chunk; each region rounded up to
+ * 256 bytes.  0 when dims is NULL or its sizes are unusable.
  */
 size_t gdn_prefill_two_pass_workspace_bytes(const gdn_dims *dims);
 
