@@ -1,7 +1,8 @@
 """GPU parity over shapes drawn at random (a fixed seed, so the same cases every
 run): key heads, grouping, head dims, rows, tokens, write mode and padding for
 the decode step; heads, head dims and ragged prompt lengths (with empty and
-padding prompts) for both prefill paths.  Each case is checked as the named
+padding prompts) for both prefill paths, and for the two-pass prefill's slim
+layout (256 or more prompt-head pairs).  Each case is checked as the named
 cases are: outputs, every written slot and the untouched rest of the pool
 against the oracle, to the bars in tests/helpers.py.
 """
@@ -44,8 +45,25 @@ def _prefill_cases(n=12, seed=2025):
     return cases
 
 
+def _slim_cases(n=8, seed=2026):
+    """Prompt sets of at least 256 prompt-head pairs (B H_v), where the two-pass
+    prefill takes its slim layout."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(n):
+        hk = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4]))
+        d, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+        B = -(-256 // (hk * G)) + int(rng.integers(0, 9))
+        lengths = [int(v) for v in rng.integers(0, 71, size=B)]
+        pad = tuple(int(b) for b in np.flatnonzero(rng.random(B) < 0.1))
+        cases.append((tuple(lengths), hk, hk * G, d, dv, pad, 300 + i))
+    return cases
+
+
 DECODE = _decode_cases()
 PREFILL = _prefill_cases()
+SLIM = _slim_cases()
 
 
 @pytest.fixture(scope="module")
@@ -76,3 +94,11 @@ def test_decode_random_shape(gdn, torch, B, T, hk, hv, d, dv, twin, real, seed):
 def test_prefill_random_shape(gdn, torch, lengths, hk, hv, d, dv, pad, seed, two_pass):
     case = gi.prefill(list(lengths), H_k=hk, H_v=hv, d=d, d_v=dv, pad=pad, seed=seed)
     _check(gdn, torch, case, two_pass=two_pass)
+
+
+@pytest.mark.parametrize("lengths,hk,hv,d,dv,pad,seed", SLIM,
+                         ids=[f"{len(c[0])}seq-{c[1]}x{c[2]}-d{c[3]}x{c[4]}" for c in SLIM])
+def test_prefill_slim_random_shape(gdn, torch, lengths, hk, hv, d, dv, pad, seed):
+    assert len(lengths) * hv >= 256
+    case = gi.prefill(list(lengths), H_k=hk, H_v=hv, d=d, d_v=dv, pad=pad, seed=seed)
+    _check(gdn, torch, case, two_pass=True)
