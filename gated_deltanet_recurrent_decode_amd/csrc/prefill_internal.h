@@ -74,7 +74,8 @@ struct TwoPassParams {
 };
 
 // Whether a call of B sequences over H_v value heads takes the slim layout and
-// its second pass (64-column slices, at least one workgroup a compute unit).
+// its second pass (a workgroup a sequence and value head; at least 256 of
+// them, the last round of 256 at least three quarters full).
 bool two_pass_slim(int B, int H_v, int d_k, int d_v);
 
 // Bytes of the workspace for B sequences, total tokens, H_k / H_v heads, d_k,

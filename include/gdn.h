@@ -205,9 +205,10 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
  * chunks in order.  Under 256 prompt-head pairs (B H_v) the first pass also
  * forms every product of a chunk that does not depend on the state and the
  * second splits each head's d_v columns over several workgroups (a single
- * long prompt fills the chip); from 256 pairs up the first pass keeps only
- * the chunk's solve and per-token factors and the second, a workgroup per
- * prompt and head, runs the conv again from x (an eighth of the workspace).
+ * long prompt fills the chip); from 256 pairs up (with the last round of 256
+ * at least three quarters full) the first pass keeps only the chunk's solve
+ * and per-token factors and the second, a workgroup per prompt and head, runs
+ * the conv again from x (an eighth of the workspace).
  * Results match gdn_prefill within rounding, not bit for bit.
  *
  * workspace: device memory of at least
@@ -256,9 +257,10 @@ gdn_status gdn_prefill_two_pass_noalloc(const gdn_dims *dims, const gdn_bf16 *x,
  * gdn_prefill_two_pass_workspace_bytes -- the workspace gdn_prefill_two_pass
  * needs for dims (B sequences, T packed tokens, H_k, H_v, d_k, d_v): room for
  * K = ceil(T / 32) + B chunks (every sequence adds at most one partial chunk)
- * per value head, each chunk (3 d_k + d_v + 32) * 32 + 1 fp32 values under
- * 256 prompt-head pairs (B H_v), else 2 * 32 * 32 + 128 fp32 values, plus in
- * that case B * 3 * C bf16 (C = 2 H_k d_k + H_v d_v, a copy of each prompt's
+ * per value head, each chunk (3 d_k + d_v + 32) * 32 + 1 fp32 values in the
+ * full layout, 2 * 32 * 32 + 128 fp32 values in the slim one (B H_v at least
+ * 256, the last round of 256 at least three quarters full), plus in that
+ * case B * 3 * C bf16 (C = 2 H_k d_k + H_v d_v, a copy of each prompt's
  * window); plus B + 1 int32 and 4 int32 per chunk; each region rounded up to
  * 256 bytes.  0 when dims is NULL or its sizes are unusable.
  */

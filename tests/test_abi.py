@@ -165,13 +165,15 @@ def test_prefill_two_pass_validation():
     parts = [4 * (d.B + 1), 16 * nchunk, 4 * blocks * 32 * d.d_k, 4 * blocks * 32 * d.d_k, 4 * blocks * 32 * d.d_k,
              4 * blocks * 32 * 32, 4 * blocks * 32 * d.d_v, 4 * blocks]
     assert need == sum((x + 255) // 256 * 256 for x in parts)
-    # from 256 prompt-head pairs (B H_v) the slim layout: T' and P (32 x 32 floats
-    # each) and 128 floats of row factors a chunk and value head, and each
-    # prompt's [3][C] bf16 window
+    # from 256 prompt-head pairs (B H_v), with the last round of 256 at least three
+    # quarters full, the slim layout: T' and P (32 x 32 floats each) and 128 floats
+    # of row factors a chunk and value head, and each prompt's [3][C] bf16 window
     for B, T, H_k, H_v, dk, dv, slim in ((16, 8192, 16, 16, 128, 128, True), (16, 300, 8, 16, 128, 128, True),
                                          (8, 300, 8, 16, 128, 128, False),
                                          (16, 900, 16, 16, 64, 64, True), (7, 900, 16, 16, 128, 128, False),
-                                         (15, 900, 16, 16, 64, 64, False), (1, 4096, 16, 16, 128, 128, False)):
+                                         (15, 900, 16, 16, 64, 64, False), (1, 4096, 16, 16, 128, 128, False),
+                                         (20, 900, 16, 16, 128, 128, False), (24, 900, 16, 16, 128, 128, True),
+                                         (40, 900, 16, 16, 128, 128, True)):
         dd = gdn.Dims(B, T, H_k, H_v, dk, dv, 4, 9)
         nchunk = (T + 31) // 32 + B
         blocks = H_v * nchunk

@@ -167,14 +167,14 @@ def test_two_pass_wide_slices(gdn, torch, lengths, hk, hv):
 
 
 SLIM_CASES = [
-    # lengths, H_k, H_v, d_k, d_v, padding prompts; B * H_v >= 256
+    # lengths, H_k, H_v, d_k, d_v, padding prompts; B * H_v in 256, 512
     ((1, 5, 32, 33, 70, 0, 100, 7, 64, 31, 2, 40, 9, 16, 65, 3), 8, 16, 128, 128, (7,)),  # G = 2, chunk edges, an empty
                                                                                            # and a padding prompt
     ((40, 17, 3, 65, 96, 2, 33, 12) * 2, 4, 16, 128, 128, ()),       # G = 4
     ((64, 3, 200, 1, 31, 9, 9, 9, 9, 9, 9, 9, 9, 9, 9, 9), 16, 16, 64, 64, (2,)),  # d = 64, a long padding prompt
     ((31, 65, 2, 40) * 4, 16, 16, 128, 64, ()),                      # d_k > d_v
     ((31, 65, 2, 40, 7, 33, 64, 1) * 2, 16, 16, 64, 128, (1,)),      # d_k < d_v
-    ((9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20, 6), 16, 16, 128, 128, ()),  # 272 heads: a second round
+    ((9, 40, 1, 33, 64, 2, 17, 30, 5, 71, 3, 32, 8, 45, 1, 20) * 2, 16, 16, 128, 128, ()),  # 512 pairs: two rounds
 ]
 
 
