@@ -267,6 +267,35 @@ def test_prefill_in_two_calls_equals_one(gdn, torch, two_pass):
 
 
 @PATHS
+@pytest.mark.parametrize("lengths,hk,hv", [([70, 5, 33], 2, 4), ([70, 5, 33, 12, 40, 1, 64, 9] * 2, 16, 16)],
+                         ids=["full-layout", "slim-layout"])
+def test_prefill_strided_x(gdn, torch, lengths, hk, hv, two_pass):
+    """x rows 72 channels apart past C (a column slice of a wider buffer) give
+    the bits of packed x: outputs, states and windows."""
+    t = torch
+    case = gi.prefill(lengths, H_k=hk, H_v=hv, d=128, seed=51)
+    s = case.shape
+    dp1, dp2 = H.DevPool(case.pool), H.DevPool(case.pool)
+    o1 = _run(gdn, t, case, dp1, two_pass=two_pass)
+    wide = t.full((s.T, s.C + 72), 3.0, dtype=t.bfloat16, device="cuda")
+    wide[:, :s.C] = H.bf16_dev(case.x)
+    x = wide[:, :s.C]
+    assert x.stride(0) == s.C + 72
+    o2 = t.full((s.T, s.H_v, s.d_v), 7.0, dtype=t.bfloat16, device="cuda")
+    args = (x, dp2.conv_w, None, dp2.conv_state, dp2.state, t.from_numpy(case.g).cuda(),
+            t.from_numpy(case.beta).cuda(), t.from_numpy(case.cu_seqlens).cuda(), dp2.rd, o2)
+    if two_pass:
+        nbytes = gdn.gdn_prefill_two_pass_workspace_bytes(s.B, s.T, s.H_k, s.H_v, s.d_k, s.d_v)
+        gdn.gdn_prefill_two_pass(*args, t.full((nbytes,), 0xFF, dtype=t.uint8, device="cuda"), H_k=s.H_k)
+    else:
+        gdn.gdn_prefill(*args, H_k=s.H_k)
+    t.cuda.synchronize()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16))
+    assert t.equal(dp1.state.view(t.int32), dp2.state.view(t.int32))
+    assert t.equal(dp1.conv_state.view(t.int16), dp2.conv_state.view(t.int16))
+
+
+@PATHS
 def test_prefill_unusable_ranges_touch_nothing(gdn, torch, two_pass):
     t = torch
     case = gi.prefill([10, 20, 5], H_k=1, H_v=1, d=64, seed=8)
