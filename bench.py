@@ -168,6 +168,28 @@ def device_code_objects(lib_path: str, arch: str = "gfx950") -> list:
     return out
 
 
+def step_kernel_label(twin: bool, B: int, T: int, H_k: int, H_v: int, d_k: int, d_v: int, tokens_mode: bool,
+                      cus: int = 256) -> str:
+    """The kernel the library routes a decode step to (the same rule as its
+    dispatch): twin writes take the tile kernel; in place, single tokens with
+    one value head a key head take it too, unless 40-64 rows' worth of 128 x 128
+    heads (2.5-4 a compute unit) group key heads in the walk kernel; token walks,
+    per-token states and grouped value heads take the walk kernel."""
+    if twin:
+        return "gdn_step_tile_kernel"
+    G = H_v // H_k
+    if T == 1 and not tokens_mode:
+        heads = B * H_v
+        kpw = 4 // G if G in (1, 2) else 1
+        grouped = (d_k == 128 and d_v == 128 and G in (1, 2) and heads * 2 > 5 * cus and heads <= 4 * cus
+                   and H_k % kpw == 0)
+        if grouped:
+            return f"gdn_step_kernel ({kpw} key heads a workgroup)"
+        if G == 1:
+            return "gdn_step_tile_kernel"
+    return "gdn_step_kernel"
+
+
 def kernel_code_sha256(symbols=STEP_KERNELS_64_TWIN, lib_path: str | None = None) -> str | None:
     """SHA-256 over the machine code of the named kernels in the built library's
     gfx950 code object (None if the library or a kernel is missing)."""
@@ -1248,8 +1270,9 @@ def main() -> int:
     result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                           "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                           "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                          "kernel": ("gdn_step_tile_kernel" if (twin or (b.T == 1 and not b.tokens_mode)) else
-                                     "gdn_step_kernel"), "kernel_us_mean": k_us,
+                          "kernel": step_kernel_label(twin, b.B, b.T, s.H_k, s.H_v, s.d_k, s.d_v, b.tokens_mode,
+                                                      torch.cuda.get_device_properties(0).multi_processor_count),
+                          "kernel_us_mean": k_us,
                           "kernel_us_p10": float(np.percentile(kus, 10)),
                           "kernel_us_p50": float(np.percentile(kus, 50)),
                           "kernel_us_p90": float(np.percentile(kus, 90)),

@@ -99,3 +99,16 @@ def test_ceiling_is_the_fastest_copy_design():
     cal["copy_contiguous_chunk256x8"]["GBps"] = 5700.0
     assert abs(c["us_at_step_bytes"] - 140_000_000 / 5.7e12 * 1e6) < 1e-9
     assert abs(c["step_fraction"] - 5200.0 / 5700.0) < 1e-12
+
+
+def test_step_kernel_label_follows_the_routing():
+    lab = bench.step_kernel_label
+    assert lab(True, 64, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel"
+    assert lab(False, 64, 1, 16, 16, 128, 128, False) == "gdn_step_kernel (4 key heads a workgroup)"
+    assert lab(False, 64, 1, 8, 16, 128, 128, False) == "gdn_step_kernel (2 key heads a workgroup)"
+    assert lab(False, 16, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel"     # 256 heads: one a CU
+    assert lab(False, 128, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel"    # 2048 heads: past 4 a CU
+    assert lab(False, 64, 1, 4, 16, 128, 128, False) == "gdn_step_kernel"           # G = 4
+    assert lab(False, 64, 4, 16, 16, 128, 128, False) == "gdn_step_kernel"          # a token walk
+    assert lab(False, 64, 1, 16, 16, 64, 64, False) == "gdn_step_tile_kernel"       # d = 64: no grouping
+    assert lab(False, 16, 4, 16, 16, 128, 128, True) == "gdn_step_kernel"           # per-token states
