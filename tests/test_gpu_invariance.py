@@ -79,11 +79,18 @@ def _reordered(case, order):
                           np.ascontiguousarray(case.beta[take]), new_cu)
 
 
+# ragged prompts over chunk edges, an empty one and a padding one; eight of
+# them (the two-pass prefill's full layout) or sixteen (its slim layout)
+ORDERS = {"8": ([700, 33, 1, 0, 1500, 64, 95, 320], (5,), [4, 7, 0, 3, 6, 2, 5, 1]),
+          "16": ([700, 33, 1, 0, 150, 64, 95, 320, 31, 7, 256, 2, 96, 45, 1, 190], (5, 12),
+                 [4, 15, 7, 0, 11, 3, 9, 6, 13, 2, 5, 10, 1, 14, 8, 12])}
+
+
+@pytest.mark.parametrize("prompts", ["8", "16"], ids=["8prompts", "16prompts"])
 @pytest.mark.parametrize("two_pass", [False, True], ids=["one-kernel", "two-pass"])
-def test_prefill_prompts_in_another_order(gdn, torch, two_pass):
-    # ragged prompts over chunk edges, an empty one and a padding one
-    case = gi.prefill([700, 33, 1, 0, 1500, 64, 95, 320], H_k=16, H_v=16, d=128, pad=(5,), seed=43)
-    order = [4, 7, 0, 3, 6, 2, 5, 1]
+def test_prefill_prompts_in_another_order(gdn, torch, two_pass, prompts):
+    lengths, pad, order = ORDERS[prompts]
+    case = gi.prefill(lengths, H_k=16, H_v=16, d=128, pad=pad, seed=43)
     moved = _reordered(case, order)
     dp_a, dp_b = H.DevPool(case.pool), H.DevPool(moved.pool)
     out_a = _prefill_run(gdn, torch, case, dp_a, two_pass=two_pass)
