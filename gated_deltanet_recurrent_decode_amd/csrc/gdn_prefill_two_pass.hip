@@ -1,5 +1,5 @@
 // gdn_prefill_two_pass.hip -- chunked Gated DeltaNet prefill in two passes
-// (gfx950), for calls with few prompts.
+// (gfx950).
 //
 // The one-kernel prefill (gdn_prefill.hip) walks a prompt's chunks inside one
 // workgroup per (sequence, key head), so a single prompt keeps only H_k
@@ -13,22 +13,33 @@
 //     O  = Q~ S0 + P U,       Q~ = diag(e^gamma) Q
 //     S1 = e^gamma_last S0 + K~^T U,   K~ = diag(e^(gamma_last - gamma)) K
 //
-// Pass 1 (workgroups per value head, each walking every gx-th chunk of the
-// call): conv + SiLU (the three inputs before the chunk come from the slot's
-// window for a prompt's first chunk, else from x), L2 norms, the running log
-// decay, K K^T and Q K^T -> A and P, (I + A)^-1 by blocked forward
+// Two workspace layouts (two_pass_slim picks one from the call's shape):
+//
+// Full (fewer prompt-head pairs than the compute units take, or a ragged last
+// round).  Pass 1 (workgroups per value head, each walking every gx-th chunk
+// of the call): conv + SiLU (the three inputs before the chunk come from the
+// slot's window for a prompt's first chunk, else from x), L2 norms, the
+// running log decay, K K^T and Q K^T -> A and P, (I + A)^-1 by blocked forward
 // substitution, then W and U~ on the matrix cores; Q~, K~, W, U~, P and
-// e^gamma_last go to the workspace.
-// Pass 2 (one workgroup per sequence, value head and slice of d_v columns):
-// the chunks in order, each three matrix-core products and the read-out, with
-// a 16-column slice of the state in registers and a wider one in LDS; then the
-// state and the advanced conv window go back to the slot.  Pass 1 reads the old
-// windows and pass 2 writes the new ones, so no workgroup can read a window
-// another has already advanced.
+// e^gamma_last go to the workspace.  Pass 2 (one workgroup per sequence,
+// value head and slice of d_v columns): the chunks in order, each three
+// matrix-core products and the read-out, with a 16-column slice of the state
+// in registers and a wider one in LDS.
+//
+// Slim (256 or more pairs in nearly whole rounds of 256).  Pass 1 keeps only
+// what needs the chunk's triangular solve, T' = (I + A)^-1 diag(beta), P and
+// per-token row factors (an eighth of the full layout), and copies each
+// prompt's old window; pass 2, a workgroup per sequence and value head, runs
+// the conv again from x and forms U = T' (V - e^gamma K^ S0) on the matrix
+// cores.
+//
+// In both, pass 2 then writes the state and the advanced conv window back to
+// the slot.  Pass 1 reads the old windows and pass 2 writes the new ones, so
+// no workgroup can read a window another has already advanced.
 // A map kernel first turns each sequence's length into its run of chunk
 // indices (an exclusive scan) and writes each chunk's record (first token,
-// tokens, slot, first chunk of its sequence or not), which pass 1 reads with
-// one load instead of searching the scan.
+// tokens, slot, and the sequence's index + 1 at its first chunk), which pass
+// 1 reads with one load instead of searching the scan.
 
 #include "gdn_internal.h"
 #include "prefill_internal.h"
