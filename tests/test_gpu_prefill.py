@@ -310,6 +310,34 @@ def test_prefill_unusable_ranges_touch_nothing(gdn, torch, two_pass):
     assert bool((out[10:].float() == 7.0).all()), "rows of unusable sequences stay as they were"
 
 
+def test_two_pass_slim_unusable_ranges(gdn, torch):
+    """256 prompts (the slim layout), the last two unusable (one running
+    backwards, one past T): their slots and rows stay as they were, and every
+    other prompt matches the oracle."""
+    t = torch
+    case = gi.prefill([10] * 256, H_k=1, H_v=1, d=64, seed=9)
+    dp, hp = H.DevPool(case.pool), H.HostPool(case.pool)
+    before = dp.state.clone()
+    bad = case.cu_seqlens.copy()
+    bad[255] = bad[254] - 5          # prompt 254 runs backwards
+    bad[256] = case.shape.T + 50     # prompt 255 ends past T
+    out = _run(gdn, t, case, dp, cu=bad, two_pass=True)
+    ref = _oracle_prefill(case, hp)
+    t.cuda.synchronize()
+    for b in (254, 255):
+        sl = int(case.pool.read_slot[b])
+        assert t.equal(dp.state[sl].view(t.int32), before[sl].view(t.int32))
+    end = int(case.cu_seqlens[254])
+    assert bool((out[end:].float() == 7.0).all()), "rows of unusable prompts stay as they were"
+    H.assert_out_close(out[:end], ref[:end])
+
+
+def test_two_pass_slim_long_prompts(gdn, torch):
+    """Sixteen prompts of 1024 tokens (the slim layout, 32 chunks a walk), every
+    output row and final state against the oracle."""
+    _check(gdn, torch, gi.prefill([1024] * 16, H_k=16, H_v=16, d=128, seed=35), two_pass=True)
+
+
 @pytest.mark.parametrize("lengths,hk,hv", [([70, 5, 33], 2, 4), ([70, 5, 33, 12, 40, 1, 64, 9] * 2, 16, 16)],
                          ids=["full-layout", "slim-layout"])
 def test_two_pass_graph_replay_matches_eager(gdn, torch, lengths, hk, hv):
