@@ -17,14 +17,14 @@ __all__ = ["GdnError", "lib", "gdn_decode_step", "gdn_decode_step_commit", "gdn_
            "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "gdn_prefill_two_pass_noalloc",
            "NOALLOC_SCRATCH_BYTES", "conv_decode",
            "slot_commit",
-           "slot_reset", "slot_copy", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
+           "slot_reset", "slot_copy", "check_slots", "traffic_probe", "status_string", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 EXPORTS = ("gdn_decode_step", "gdn_decode_step_commit", "gdn_decode_step_tokens", "gdn_prefill",
            "gdn_prefill_two_pass", "gdn_prefill_two_pass_workspace_bytes", "gdn_prefill_two_pass_noalloc",
            "conv_decode",
-           "slot_commit",
+           "slot_commit", "gdn_check_slots",
            "gdn_slot_reset",
            "gdn_slot_copy", "gdn_status_string", "gdn_traffic_probe")
 
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.slot_commit.argtypes = [P, P, i32, P]
     L.gdn_status_string.restype = ctypes.c_char_p
     L.gdn_status_string.argtypes = [i32]
+    L.gdn_check_slots.restype = i32
+    L.gdn_check_slots.argtypes = [ctypes.POINTER(Dims), P, P, P, P]
     L.gdn_slot_reset.restype = i32
     L.gdn_slot_reset.argtypes = [ctypes.POINTER(Dims), P, P, P, i32, P]
     L.gdn_slot_copy.restype = i32
@@ -429,6 +431,28 @@ def slot_commit(read_slot, write_slot, *, stream=None) -> None:
     with _on(dev):
         _check("slot_commit", lib().slot_commit(_ptr(read_slot), _ptr(write_slot), read_slot.shape[0],
                                                 _stream(stream, dev)))
+
+
+def check_slots(read_slot, write_slot=None, *, N: int, stream=None):
+    """The device-side debug check of a step's slot preconditions (see
+    ``gdn_check_slots`` in include/gdn.h): returns a new int32 tensor [2] on the
+    slots' device, filled in stream order with the number of rows that break a
+    precondition and the first of them (-1 if none)."""
+    torch = _torch()
+    _contig(_dev(read_slot, "read_slot", torch.int32), "read_slot")
+    if read_slot.dim() != 1:
+        raise ValueError("read_slot must be [B]")
+    if write_slot is not None:
+        _contig(_dev(write_slot, "write_slot", torch.int32), "write_slot")
+        if write_slot.shape != read_slot.shape:
+            raise ValueError("write_slot must match read_slot")
+    dev = _device(read_slot, write_slot) if write_slot is not None else _device(read_slot)
+    result = torch.full((2,), -2, dtype=torch.int32, device=dev)
+    B = read_slot.shape[0]
+    with _on(dev):
+        _check("gdn_check_slots", lib().gdn_check_slots(ctypes.byref(Dims(B, 1, 1, 1, 64, 64, 4, N)), _ptr(read_slot),
+                                                          _ptr(write_slot), _ptr(result), _stream(stream, dev)))
+    return result
 
 
 def _pool_layout(state, conv_state, H_k):

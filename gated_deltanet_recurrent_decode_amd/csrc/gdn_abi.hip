@@ -378,6 +378,22 @@ gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipSt
     return from_hip(gdn::launch_slot_commit(read_slot, write_slot, B, stream));
 }
 
+gdn_status gdn_check_slots(const gdn_dims *dims, const int32_t *read_slot, const int32_t *write_slot,
+                           int32_t *result, hipStream_t stream)
+{
+    if (!dims)
+        return GDN_ERR_NULL;
+    if (dims->B == 0)
+        return GDN_OK;
+    if (!read_slot || !result)
+        return GDN_ERR_NULL;
+    if (dims->B < 0 || dims->N < 1)
+        return GDN_ERR_SHAPE;
+    if (!aligned(read_slot, 4) || !aligned(result, 4) || (write_slot && !aligned(write_slot, 4)))
+        return GDN_ERR_UNSUPPORTED;
+    return from_hip(gdn::launch_slot_check(read_slot, write_slot, dims->B, dims->N, result, stream));
+}
+
 static gdn_status slot_ops_impl(const gdn_dims *dims, float *state, gdn_bf16 *conv_state, const int32_t *src,
                                 const int32_t *dst, int32_t n, hipStream_t stream)
 {

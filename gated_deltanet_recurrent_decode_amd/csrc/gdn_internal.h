@@ -80,6 +80,8 @@ int device_cus();
 hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream);
 hipError_t launch_conv_decode(const ConvParams &p, hipStream_t stream);
 hipError_t launch_slot_commit(int32_t *read_slot, int32_t *write_slot, int B, hipStream_t stream);
+hipError_t launch_slot_check(const int32_t *read_slot, const int32_t *write_slot, int B, int N, int32_t *result,
+                             hipStream_t stream);
 hipError_t launch_slot_ops(const SlotOpsParams &p, int n, hipStream_t stream);
 hipError_t launch_traffic_probe(const ProbeParams &p, int d_k, int d_v, hipStream_t stream);
 

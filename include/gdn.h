@@ -35,6 +35,8 @@
  *     twin write whose write slot equals its read slot or is the null slot
  *     0, touches no pool memory and gets NaN in every output element
  *     instead.  Slot 0 is never written by any entry point.
+ *     gdn_check_slots verifies the preconditions on the device, for
+ *     debugging.
  *   - Calls that overlap on the same pool slots race (as any two kernels
  *     writing the same memory would).
  */
@@ -299,6 +301,25 @@ gdn_status conv_decode(int32_t B, int32_t C, int32_t W, int32_t N, const gdn_bf1
  *   read_slot, write_slot [B] int32.  B = 0 returns GDN_OK at once.
  */
 gdn_status slot_commit(int32_t *read_slot, int32_t *write_slot, int32_t B, hipStream_t stream);
+
+/*
+ * gdn_check_slots -- a debug check, on the device, of the slot preconditions
+ * every decode step relies on and does not verify (PR #1139, "What changed":
+ * a step reads one slot of a row's pair and writes the other; padding rows sit
+ * on the null slot 0).  A row breaks them when a slot of it lies outside
+ * [0, N); when it is real (read slot not 0) and another real row has the same
+ * read slot; or, for a twin write (write_slot not NULL), when it is real and
+ * its write slot is its own read slot, is 0, or is another row's read or
+ * write slot other than 0.  Enqueues one workgroup on `stream` (comparing
+ * every pair of rows: O(B^2) work, for debugging, not for the hot loop) that
+ * writes result[0] = the number of rows that break a precondition and
+ * result[1] = the first of them, or -1; `result` is a caller-owned device
+ * int32[2].  Stream-ordered, capturable, no allocation.  Uses dims' B and N.
+ * B == 0 returns GDN_OK and enqueues nothing (result untouched);
+ * GDN_ERR_NULL without read_slot or result.
+ */
+gdn_status gdn_check_slots(const gdn_dims *dims, const int32_t *read_slot, const int32_t *write_slot,
+                           int32_t *result, hipStream_t stream);
 
 /*
  * gdn_slot_reset -- zero slots of the pool (PR #1139, "Tests": rollback and

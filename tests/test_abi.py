@@ -285,3 +285,19 @@ def test_prefill_noalloc_validation():
     empty = gdn.Dims(0, 0, 16, 16, 128, 128, 4, 9)
     assert f(ctypes.byref(empty), None, 0, None, None, None, None, None, None, None, None, None, 1.0, 1e-6,
              None) == OK
+
+
+def test_check_slots_validation():
+    L = gdn.lib()
+    f = L.gdn_check_slots
+    d = gdn.Dims(8, 1, 1, 1, 64, 64, 4, 17)
+    assert f(None, FAKE, None, FAKE, None) == NULL
+    assert f(ctypes.byref(gdn.Dims(0, 1, 1, 1, 64, 64, 4, 17)), None, None, None, None) == OK  # nothing to check
+    assert f(ctypes.byref(d), None, None, FAKE, None) == NULL
+    assert f(ctypes.byref(d), FAKE, None, None, None) == NULL
+    assert f(ctypes.byref(gdn.Dims(-1, 1, 1, 1, 64, 64, 4, 17)), FAKE, None, FAKE, None) == SHAPE
+    assert f(ctypes.byref(gdn.Dims(8, 1, 1, 1, 64, 64, 4, 0)), FAKE, None, FAKE, None) == SHAPE
+    odd = ctypes.c_void_p(0x100002)
+    assert f(ctypes.byref(d), odd, None, FAKE, None) == UNSUPPORTED
+    assert f(ctypes.byref(d), FAKE, odd, FAKE, None) == UNSUPPORTED
+    assert f(ctypes.byref(d), FAKE, None, odd, None) == UNSUPPORTED
