@@ -1271,7 +1271,7 @@ def main() -> int:
                           "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                           "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                           "kernel": step_kernel_label(twin, b.B, b.T, s.H_k, s.H_v, s.d_k, s.d_v, b.tokens_mode,
-                                                      torch.cuda.get_device_properties(0).multi_processor_count),
+                                                      b.torch.cuda.get_device_properties(0).multi_processor_count),
                           "kernel_us_mean": k_us,
                           "kernel_us_p10": float(np.percentile(kus, 10)),
                           "kernel_us_p50": float(np.percentile(kus, 50)),
