@@ -10,7 +10,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FILES = ["bench.py", "__graft_entry__.py", "gdn_inputs.py",
          os.path.join("gated_deltanet_recurrent_decode_amd", "__init__.py"),
-         os.path.join("gated_deltanet_recurrent_decode_amd", "build.py")]
+         os.path.join("gated_deltanet_recurrent_decode_amd", "build.py"),
+         os.path.join("oracle", "__init__.py")] + sorted(
+    os.path.join("tests", f) for f in os.listdir(os.path.join(ROOT, "tests")) if f.endswith(".py"))
 
 
 def _unbound(path):
