@@ -26,7 +26,7 @@ struct StepParams {
     int32_t *next_write_slot; // fused commit: receives read_slot[r]
     int n_slices; // d_v column slices per head (set by the launcher)
     int twin;     // 1: write to write_slot; 0: in place
-    int xcd_order; // tile kernel: 1 = give each XCD a contiguous run of tile groups
+    int xcd_groups; // tile kernel: the grid size to give each XCD a contiguous run of tile groups (0: off)
     const int32_t *token_slots; // [B][T]: in-place kernel keeps the state after token t in slot [r][t] (0: not
                                 // kept) and leaves the read slot alone; null: plain in place
 };

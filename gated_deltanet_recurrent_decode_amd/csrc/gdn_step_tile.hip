@@ -70,15 +70,25 @@ __device__ __forceinline__ void tile_locate(TileState<DK, DVS> &t, int tile, con
     t.hk = t.hv / p.G;
     t.col0 = cs * DVS;
     t.own_qk = (t.hv % p.G == 0) && cs == 0; // the tile that writes back the key head's q/k windows
-    t.rs = p.read_slot[t.r];
-    t.ws = p.twin ? p.write_slot[t.r] : t.rs;
-    // unusable: a slot out of range, or a twin row writing over its own read
-    // slot or into the null slot (which must stay zero: it never holds a row)
-    const bool bad = t.rs < 0 || t.rs >= p.N || t.ws < 0 || t.ws >= p.N || (p.twin && (t.ws == t.rs || t.ws == 0));
-    t.real = t.valid && t.rs != 0 && !bad;
-    t.fill = t.rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
+    // the gates and both slots in one round of scalar loads: the write slot
+    // through a pointer that exists in place too, so no branch splits them
     t.g = p.g[(size_t)t.r * p.H_v + t.hv];
     t.beta = p.beta[(size_t)t.r * p.H_v + t.hv];
+    const bool twin = p.twin != 0;
+    const int32_t *wsp = twin ? p.write_slot : p.read_slot;
+    const int32_t rs = p.read_slot[t.r];
+    const int32_t wsl = wsp[t.r];
+    const int32_t ws = twin ? wsl : rs;
+    t.rs = rs;
+    t.ws = ws;
+    // unusable: a slot out of range (a negative one too, as unsigned), or a
+    // twin row writing over its own read slot or into the null slot (which
+    // must stay zero: it never holds a row).  Bitwise, not short-circuit: the
+    // branches of || would hold later loads back behind the slots' wait.
+    const uint32_t n = (uint32_t)p.N;
+    const bool bad = ((uint32_t)rs >= n) | ((uint32_t)ws >= n) | (twin & ((ws == rs) | (ws == 0)));
+    t.real = t.valid & (rs != 0) & !bad;
+    t.fill = rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
 }
 
 // The conv inputs of the tile's channels (q and k of its key head, v of its
@@ -92,9 +102,12 @@ __device__ __forceinline__ void tile_issue_small(TileState<DK, DVS> &t, const St
     const int C = p.C;
     const uint32_t cbytes = (uint32_t)C * 2u;
     const __amdgpu_buffer_rsrc_t cw = bf16_rsrc(p.conv_w, cbytes * 4u);
-    const __amdgpu_buffer_rsrc_t win = bf16_rsrc(p.conv_state + (size_t)(t.real ? t.rs : 0) * 3 * C,
-                                                 t.real ? 3u * cbytes : 0u);
-    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x + (size_t)t.r * p.x_row_stride, t.real ? cbytes : 0u);
+    // unusable rows read through empty resources (multiplied by the flag,
+    // not chosen: a choice here becomes a branch)
+    const uint32_t real = (uint32_t)t.real;
+    const __amdgpu_buffer_rsrc_t win =
+        bf16_rsrc(p.conv_state + (size_t)(t.rs * (int)real) * 3 * C, 3u * cbytes * real);
+    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x + (size_t)t.r * p.x_row_stride, cbytes * real);
     const __amdgpu_buffer_rsrc_t br = bf16_rsrc(p.conv_b ? p.conv_b : p.conv_w, p.conv_b ? cbytes : 0u);
 #pragma unroll
     for (int q = 0; q < TT::NCQ; ++q) {
@@ -128,7 +141,7 @@ __device__ __forceinline__ void tile_issue_state(TileState<DK, DVS> &t, const St
     using Cfg = typename TileState<DK, DVS>::Cfg;
     constexpr uint32_t TILE = (uint32_t)DK * DV;
     const __amdgpu_buffer_rsrc_t rd =
-        tile_rsrc(p.state + ((size_t)(t.real ? t.rs : 0) * p.H_v + t.hv) * TILE, t.real ? TILE * 4u : 0u);
+        tile_rsrc(p.state + ((size_t)(t.rs * (int)t.real) * p.H_v + t.hv) * TILE, TILE * 4u * (uint32_t)t.real);
     const uint32_t vo = voff + (uint32_t)(t.col0 * 4);
 #pragma unroll
     for (int m = 0; m < Cfg::RPT; ++m)
@@ -305,14 +318,13 @@ void gdn_step_tile_kernel(StepParams p)
     const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
     float *y_lds = y_all[sub];
 
-    // workgroup -> tile group; with p.xcd_order, workgroups (which the
-    // hardware deals to the eight XCDs in turn) are renumbered so that each
-    // XCD gets a contiguous run of tile groups
-    int grp = blockIdx.x;
-    if (p.xcd_order) {
-        const int n = gridDim.x, x = blockIdx.x % 8, q = n / 8, rr = n % 8;
-        grp = x * q + min(x, rr) + (int)blockIdx.x / 8;
-    }
+    // workgroup -> tile group; with p.xcd_groups (the grid size, 0: off),
+    // workgroups (which the hardware deals to the eight XCDs in turn) are
+    // renumbered so that each XCD gets a contiguous run of tile groups.  The
+    // grid size comes with the other arguments: read from the dispatch packet
+    // it took a round of scalar loads of its own.
+    const int n = p.xcd_groups, x = blockIdx.x % 8, q = n / 8, rr = n % 8;
+    const int grp = n ? x * q + min(x, rr) + (int)blockIdx.x / 8 : (int)blockIdx.x;
     TT t;
     tile_locate(t, grp * TPW + sub, p);
     tile_issue_small<DK, DV, DVS>(t, p, ht);
@@ -356,10 +368,12 @@ static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
     const long long tiles = (long long)p.B * p.H_v * q.n_slices;
     if (tiles <= 0)
         return hipSuccess;
+    const unsigned groups = (unsigned)((tiles + TPW - 1) / TPW);
+    q.xcd_groups = p.xcd_groups ? (int)groups : 0;
     void *args[] = {&q};
     const void *k = p.twin ? reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, false, TPW>)
                            : reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, true, TPW>);
-    return hipLaunchKernel(k, dim3((unsigned)((tiles + TPW - 1) / TPW)), dim3(2 * DVS * TPW), args, 0, stream);
+    return hipLaunchKernel(k, dim3(groups), dim3(2 * DVS * TPW), args, 0, stream);
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -413,7 +427,7 @@ template <int DK, int DV>
 static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
 {
     StepParams q = p;
-    q.xcd_order = p.twin ? 0 : 1;
+    q.xcd_groups = p.twin ? 0 : 1; // launch_tile sets the grid size
     const long long heads = (long long)p.B * p.H_v;
     const long long rem = heads % 256;
     if constexpr (DK == 128 && DV == 128) {
