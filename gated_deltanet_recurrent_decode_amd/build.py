@@ -18,13 +18,24 @@ SOURCES = ["gdn_abi.hip", "gdn_step.hip", "gdn_step_tile.hip", "gdn_prefill.hip"
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # only the explicit fmaf() calls fuse: the sums have one fixed rounding order
     "-ffp-contract=off",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+
+# Flags of one source only.  The tile step kernel takes what its first round
+# of scalar loads needs (slot arrays, gate arrays, B, H_v, G, the grid size) as
+# eight leading arguments that the hardware preloads into scalar registers
+# (gfx950 kernel argument preloading), so the slots and gates are requested at
+# once instead of after a load of the arguments.  Code objects built with
+# preloading start with a block that loads the same registers, so they run
+# unchanged where the firmware does not preload.
+PER_SOURCE = {
+    "gdn_step_tile.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+}
 
 
 def hipcc() -> str:
@@ -33,9 +44,22 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile each source to an object (in parallel), then link them."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *FLAGS, *PER_SOURCE.get(src, []), *(extra or []), "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((src, obj, subprocess.Popen(cmd)))
+    failed = [src for src, _, pr in jobs if pr.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, "hipcc " + " ".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *[obj for _, obj, _ in jobs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

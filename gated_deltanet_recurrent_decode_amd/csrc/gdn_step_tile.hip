@@ -55,30 +55,38 @@ struct TileState {
     float4 s[Cfg::RPT];
 };
 
+// What the first round of scalar loads needs, passed as separate leading
+// kernel arguments, which the build has the hardware preload into scalar
+// registers (gfx950 kernel argument preloading): the slots and gates are then
+// requested at once, beside the rest of the arguments.
+struct TileArgs {
+    const int32_t *read_slot, *write_slot;
+    const float *g, *beta;
+    int B, H_v, G;
+};
+
 // Tile index -> (row, value head, column slice), its slots and gates.  Tiles
 // are ordered row-major, then value head, then column slice.
-template <int DK, int DVS>
-__device__ __forceinline__ void tile_locate(TileState<DK, DVS> &t, int tile, const StepParams &p)
+template <int DK, int DV, int DVS, bool TWIN>
+__device__ __forceinline__ void tile_locate(TileState<DK, DVS> &t, int tile, const TileArgs &a, const StepParams &p)
 {
-    const int ntiles = p.B * p.H_v * p.n_slices;
+    constexpr int NS = DV / DVS;
+    const int ntiles = a.B * a.H_v * NS;
     t.valid = tile < ntiles;
     const int tt = t.valid ? tile : 0;
-    const int cs = tt % p.n_slices;
-    const int rh = tt / p.n_slices;
-    t.hv = rh % p.H_v;
-    t.r = rh / p.H_v;
-    t.hk = t.hv / p.G;
+    const int cs = tt % NS;
+    const int rh = tt / NS;
+    t.hv = rh % a.H_v;
+    t.r = rh / a.H_v;
+    t.hk = t.hv / a.G;
     t.col0 = cs * DVS;
-    t.own_qk = (t.hv % p.G == 0) && cs == 0; // the tile that writes back the key head's q/k windows
-    // the gates and both slots in one round of scalar loads: the write slot
-    // through a pointer that exists in place too, so no branch splits them
-    t.g = p.g[(size_t)t.r * p.H_v + t.hv];
-    t.beta = p.beta[(size_t)t.r * p.H_v + t.hv];
-    const bool twin = p.twin != 0;
-    const int32_t *wsp = twin ? p.write_slot : p.read_slot;
-    const int32_t rs = p.read_slot[t.r];
-    const int32_t wsl = wsp[t.r];
-    const int32_t ws = twin ? wsl : rs;
+    t.own_qk = (t.hv % a.G == 0) && cs == 0; // the tile that writes back the key head's q/k windows
+    // the gates and both slots in one round of scalar loads
+    t.g = a.g[(size_t)t.r * a.H_v + t.hv];
+    t.beta = a.beta[(size_t)t.r * a.H_v + t.hv];
+    constexpr bool twin = TWIN;
+    const int32_t rs = a.read_slot[t.r];
+    const int32_t ws = twin ? a.write_slot[t.r] : rs;
     t.rs = rs;
     t.ws = ws;
     // unusable: a slot out of range (a negative one too, as unsigned), or a
@@ -295,7 +303,8 @@ __device__ __forceinline__ void tile_process(TileState<DK, DVS> &t, const StepPa
 
 template <int DK, int DV, int DVS, bool INPLACE, int TPW>
 __global__ __launch_bounds__(2 * DVS * TPW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
-void gdn_step_tile_kernel(StepParams p)
+void gdn_step_tile_kernel(const int32_t *read_slot, const int32_t *write_slot, const float *g, const float *beta, int B,
+                          int H_v, int G, int xcd_groups, StepParams p)
 {
     using TT = TileState<DK, DVS>;
     using Cfg = typename TT::Cfg;
@@ -318,15 +327,15 @@ void gdn_step_tile_kernel(StepParams p)
     const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
     float *y_lds = y_all[sub];
 
-    // workgroup -> tile group; with p.xcd_groups (the grid size, 0: off),
+    // workgroup -> tile group; with xcd_groups (the grid size, 0: off),
     // workgroups (which the hardware deals to the eight XCDs in turn) are
     // renumbered so that each XCD gets a contiguous run of tile groups.  The
-    // grid size comes with the other arguments: read from the dispatch packet
-    // it took a round of scalar loads of its own.
-    const int n = p.xcd_groups, x = blockIdx.x % 8, q = n / 8, rr = n % 8;
+    // grid size comes with the arguments: read from the dispatch packet it
+    // took a round of scalar loads of its own.
+    const int n = xcd_groups, x = blockIdx.x % 8, q = n / 8, rr = n % 8;
     const int grp = n ? x * q + min(x, rr) + (int)blockIdx.x / 8 : (int)blockIdx.x;
     TT t;
-    tile_locate(t, grp * TPW + sub, p);
+    tile_locate<DK, DV, DVS, !INPLACE>(t, grp * TPW + sub, TileArgs{read_slot, write_slot, g, beta, B, H_v, G}, p);
     tile_issue_small<DK, DV, DVS>(t, p, ht);
     __builtin_amdgcn_sched_barrier(0); // the small loads stay ahead of the tile loads
     tile_issue_state<DK, DV, DVS>(t, p, voff);
@@ -369,8 +378,11 @@ static hipError_t launch_tile(const StepParams &p, hipStream_t stream)
     if (tiles <= 0)
         return hipSuccess;
     const unsigned groups = (unsigned)((tiles + TPW - 1) / TPW);
-    q.xcd_groups = p.xcd_groups ? (int)groups : 0;
-    void *args[] = {&q};
+    int xcd_groups = p.xcd_groups ? (int)groups : 0;
+    const int32_t *rs = p.read_slot, *ws = p.write_slot;
+    const float *g = p.g, *beta = p.beta;
+    int B = p.B, H_v = p.H_v, G = p.G;
+    void *args[] = {&rs, &ws, &g, &beta, &B, &H_v, &G, &xcd_groups, &q};
     const void *k = p.twin ? reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, false, TPW>)
                            : reinterpret_cast<const void *>(&gdn_step_tile_kernel<DK, DV, DVS, true, TPW>);
     return hipLaunchKernel(k, dim3(groups), dim3(2 * DVS * TPW), args, 0, stream);
