@@ -26,15 +26,17 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-# Flags of one source only.  The tile step kernel takes what its first round
-# of scalar loads needs (slot arrays, gate arrays, B, H_v, G, the grid size) as
-# eight leading arguments that the hardware preloads into scalar registers
-# (gfx950 kernel argument preloading), so the slots and gates are requested at
-# once instead of after a load of the arguments.  Code objects built with
-# preloading start with a block that loads the same registers, so they run
-# unchanged where the firmware does not preload.
+# Flags of single sources.  The step kernels take what their first round of
+# scalar loads needs (the tile kernel: slot arrays, gate arrays, B, H_v, G,
+# the grid size; the walk kernel: the read slots, H_k, N) as leading
+# arguments that the hardware preloads into scalar registers (gfx950 kernel
+# argument preloading), so the slots are requested at once instead of after a
+# load of the arguments.  Code objects built with preloading start with a
+# block that loads the same registers, so they run unchanged where the
+# firmware does not preload.
 PER_SOURCE = {
     "gdn_step_tile.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+    "gdn_step.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"],
 }
 
 

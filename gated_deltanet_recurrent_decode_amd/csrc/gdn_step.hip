@@ -65,7 +65,7 @@ struct ConvIn {
 // instantiation, so the plain walk carries none of its registers.
 template <int DK, int DV, int G, int KPW, bool TOKENS>
 __global__ __launch_bounds__(2 * DV * G * KPW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
-void gdn_step_kernel(StepParams p)
+void gdn_step_kernel(const int32_t *read_slot, int H_k, int N, StepParams p)
 {
     constexpr int HPW = G * KPW;
     using Cfg = StepCfg<DK, DV, HPW>;
@@ -107,34 +107,33 @@ void gdn_step_kernel(StepParams p)
     const int rg = lane >> 3;
 
     // workgroup -> (row, group of KPW key heads); the value heads of key head
-    // hk are hk*G .. hk*G + G-1, so the workgroup's are hv0 .. hv0 + HPW-1
-    const int ngrp = p.H_k / KPW;
+    // hk are hk*G .. hk*G + G-1, so the workgroup's are hv0 .. hv0 + HPW-1.
+    // The read slot's pointer, H_k and N come as leading arguments that the
+    // build has the hardware preload into scalar registers (gfx950 kernel
+    // argument preloading), so the slot load leaves beside the load of the
+    // other arguments.
+    const int ngrp = H_k / KPW;
     const int hk0 = (int)(blockIdx.x % ngrp) * KPW;
     const int r = blockIdx.x / ngrp;
     const int hv0 = hk0 * G;
     const int T = p.T;
 
-    const int rs = p.read_slot[r];
-    bool bad = rs < 0 || rs >= p.N;
-    if (TOKENS && rs != 0) {
+    const int rs_in = read_slot[r];
+    bool bad = (uint32_t)rs_in >= (uint32_t)N; // a negative slot too
+    if (TOKENS && rs_in != 0) {
         // per-token states: every kept slot must be a usable slot other than the read slot
         for (int t = 0; t < T; ++t) {
             const int ts = p.token_slots[(size_t)r * T + t];
-            bad = bad || ts < 0 || ts >= p.N || ts == rs;
+            bad = bad || ts < 0 || ts >= N || ts == rs_in;
         }
     }
-    if (rs == 0 || bad) {
-        // padding row (or a row with an unusable slot): touch no slot; out gets
-        // +0.0 for padding and NaN for the unusable slot.
-        const uint16_t fill = rs == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
-        for (int e = tid; e < T * HPW * DV; e += NT) {
-            const int t = e / (HPW * DV);
-            const int h = (e / DV) % HPW;
-            const int j = e % DV;
-            p.out[(((size_t)r * T + t) * p.H_v + hv0 + h) * DV + j] = fill;
-        }
-        return;
-    }
+    // a padding row (read slot 0) or a row with an unusable slot touches no
+    // slot: its loads below go through empty resources (sizes multiplied by
+    // the flag; a choice would become a branch that holds the loads back
+    // behind the slot's wait), then it writes the read-out fill and leaves
+    const bool real = rs_in != 0 && !bad;
+    const uint32_t realu = (uint32_t)real;
+    const int rs = rs_in * (int)real;
 
     // ---- conv lanes: each takes four consecutive channels, whole waves except
     // the last, whose spare lanes read nothing and write their result to the
@@ -152,8 +151,8 @@ void gdn_step_kernel(StepParams p)
         const int ve = e2 >= 2 * DK ? e2 - 2 * DK : 0;
         const int h = ve / DV;
         return isq ? hk * DK + e2
-               : isk ? p.H_k * DK + hk * DK + (e2 - DK)
-                     : 2 * p.H_k * DK + (hk * G + h) * DV + (ve - h * DV);
+               : isk ? H_k * DK + hk * DK + (e2 - DK)
+                     : 2 * H_k * DK + (hk * G + h) * DV + (ve - h * DV);
     };
     bool conv_wave[NCQ], conv_lane[NCQ];
     int c[NCQ], e4[NCQ];
@@ -165,11 +164,11 @@ void gdn_step_kernel(StepParams p)
         e4[k] = conv_lane[k] ? 4 * li : 0; // first channel of the quad
         c[k] = channel(e4[k]);
     }
-    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x + (size_t)r * p.x_row_stride, (uint32_t)T * cbytes);
+    const __amdgpu_buffer_rsrc_t xr = bf16_rsrc(p.x + (size_t)r * p.x_row_stride, (uint32_t)T * cbytes * realu);
     const __amdgpu_buffer_rsrc_t cw = bf16_rsrc(p.conv_w, cbytes * 4u);
     const __amdgpu_buffer_rsrc_t br = bf16_rsrc(p.conv_b ? p.conv_b : p.conv_w, p.conv_b ? cbytes : 0u);
-    const __amdgpu_buffer_rsrc_t win = bf16_rsrc(p.conv_state + (size_t)rs * 3 * C, 3u * cbytes);
-    const uint32_t gbytes = (uint32_t)T * (uint32_t)p.H_v * 4u;
+    const __amdgpu_buffer_rsrc_t win = bf16_rsrc(p.conv_state + (size_t)rs * 3 * C, 3u * cbytes * realu);
+    const uint32_t gbytes = (uint32_t)T * (uint32_t)p.H_v * 4u * realu;
     const __amdgpu_buffer_rsrc_t gr = f32_rsrc(p.g + (size_t)r * T * p.H_v, gbytes);
     const __amdgpu_buffer_rsrc_t bt_r = f32_rsrc(p.beta + (size_t)r * T * p.H_v, gbytes);
     const bool has_bias = p.conv_b != nullptr;
@@ -261,7 +260,7 @@ void gdn_step_kernel(StepParams p)
     // ---- state slice -> registers
     const int hv = hv0 + hloc;
     constexpr uint32_t TILE = (uint32_t)DK * DV;
-    const __amdgpu_buffer_rsrc_t rd_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u);
+    const __amdgpu_buffer_rsrc_t rd_tile = tile_rsrc(p.state + ((size_t)rs * p.H_v + hv) * TILE, TILE * 4u * realu);
     const uint32_t voff = (uint32_t)((rg * DV + 4 * cg) * 4);
     float4 s[RPT];
 #pragma unroll
@@ -272,6 +271,17 @@ void gdn_step_kernel(StepParams p)
     // system a load issued after the flood of tile loads queues behind all of
     // them.
     __builtin_amdgcn_sched_barrier(0);
+    if (!real) {
+        // out gets +0.0 for padding and NaN for an unusable slot
+        const uint16_t fill = rs_in == 0 ? (uint16_t)0 : (uint16_t)0x7fc0;
+        for (int e = tid; e < T * HPW * DV; e += NT) {
+            const int t = e / (HPW * DV);
+            const int h = (e / DV) % HPW;
+            const int j = e % DV;
+            p.out[(((size_t)r * T + t) * p.H_v + hv0 + h) * DV + j] = fill;
+        }
+        return;
+    }
     stash(in);
 
     for (int t0 = 0;;) {
@@ -467,7 +477,9 @@ static hipError_t launch_step(const StepParams &p, hipStream_t stream)
         return hipSuccess;
     StepParams q = p;
     q.n_slices = 1;
-    void *args[] = {&q};
+    const int32_t *rs = p.read_slot;
+    int H_k = p.H_k, N = p.N;
+    void *args[] = {&rs, &H_k, &N, &q};
     const void *k = reinterpret_cast<const void *>(&gdn_step_kernel<DK, DV, G, KPW, false>);
     if constexpr (KPW == 1) {
         if (p.token_slots)
