@@ -74,8 +74,8 @@ METRIC = "GDN decode rows/s and achieved HBM GB/s (% of peak) at 64 rows"
 # launch runs is hashed from the built library, and traffic is reported as null
 # when it differs.
 STEP_KERNELS_64_TWIN = ("_ZN3gdn20gdn_step_tile_kernelILi128ELi128ELi128ELb0ELi4EEEvPKiS2_PKfS4_iiiiNS_10StepParamsE",)
-MEASURED_TRAFFIC = {"kernel_code_sha256": "9042c0a94dcb327f1511c2c3dcee4574a0ea696c5310ba531ebb300052a095d5",
-                    "workload": (64, "twin", "fused", False, 16), "bytes_per_launch": 140_332_274}
+MEASURED_TRAFFIC = {"kernel_code_sha256": "b4ee9a59f7b7983dca198b44b277973e94b5c1321fba97fde52640a699393df7",
+                    "workload": (64, "twin", "fused", False, 16), "bytes_per_launch": 140_325_912}
 
 # The same counters over one call of the two-pass prefill (chunk map, pass 1 and
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the

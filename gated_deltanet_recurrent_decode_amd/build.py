@@ -37,6 +37,8 @@ FLAGS = [
 PER_SOURCE = {
     "gdn_step_tile.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
     "gdn_step.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"],
+    # the calibration copies, so that their slot loads leave as early as the step's
+    "traffic_probe.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"],
 }
 
 

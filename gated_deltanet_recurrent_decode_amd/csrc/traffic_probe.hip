@@ -27,7 +27,10 @@
 //     piece of that slot's tile: the launch floor of small batches.
 // Every access is a buffer access through a resource sized to its tile or
 // chunk, and every slot is range-checked, so nothing outside the pool can be
-// touched whatever the slot arrays hold.
+// touched whatever the slot arrays hold.  As in the step kernels, the slot
+// arrays and the sizes the first loads depend on come as leading arguments
+// that the build has the hardware preload into scalar registers, so a
+// design's slot loads leave in its first instructions, as the step's do.
 
 #include "device_common.h"
 #include "gdn_internal.h"
@@ -53,6 +56,33 @@ __device__ __forceinline__ void probe_order(int order)
     }
 }
 
+// The leading arguments of every probe kernel (copies of the ProbeParams
+// fields of the same names).
+#define PROBE_LEAD_PARAMS                                                                                              \
+    float *state, const int32_t *read_slot, const int32_t *write_slot, int B, int H, int N, int traffic, int layout
+#define PROBE_LEAD_SET(p)                                                                                                \
+    do {                                                                                                               \
+        (p).state = state;                                                                                             \
+        (p).read_slot = read_slot;                                                                                     \
+        (p).write_slot = write_slot;                                                                                   \
+        (p).B = B;                                                                                                     \
+        (p).H = H;                                                                                                     \
+        (p).N = N;                                                                                                     \
+        (p).traffic = traffic;                                                                                         \
+        (p).layout = layout;                                                                                           \
+    } while (0)
+
+struct ProbeLead {
+    float *state;
+    const int32_t *read_slot, *write_slot;
+    int B, H, N, traffic, layout;
+    explicit ProbeLead(const ProbeParams &q)
+        : state(q.state), read_slot(q.read_slot), write_slot(q.write_slot), B(q.B), H(q.H), N(q.N), traffic(q.traffic),
+          layout(q.layout)
+    {
+    }
+};
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
@@ -64,23 +94,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(void *base, uint32_
 __device__ __forceinline__ bool probe_tile(const ProbeParams &p, int t, size_t tile_bytes, size_t &src, size_t &dst)
 {
     const int r = t / p.H, h = t % p.H;
-    int rs, ws;
-    const bool own = p.traffic == 0 || p.traffic == 3; // read only, or written back in place
-    if (p.layout == 1) {
-        const int r0 = p.read_slot[0], w0 = own ? r0 : p.write_slot[0];
-        if (r0 < 1 || (long long)r0 + p.B > p.N || w0 < 1 || (long long)w0 + p.B > p.N)
-            return false;
-        rs = r0 + r;
-        ws = w0 + r;
-    } else {
-        rs = p.read_slot[r];
-        ws = own ? rs : p.write_slot[r];
-    }
-    if (rs < 1 || rs >= p.N || ws < 1 || ws >= p.N)
-        return false;
+    const bool own = (p.traffic == 0) | (p.traffic == 3); // read only, or written back in place
+    const bool run = p.layout == 1;
+    // both layouts through the same two loads, chosen by value rather than by
+    // branch (a branch would hold the rest of the launch's loads back)
+    const int i = run ? 0 : r;
+    const int32_t *wp = own ? p.read_slot : p.write_slot;
+    const int a = p.read_slot[i], b = wp[i];
+    __builtin_amdgcn_sched_barrier(0); // both loads leave before either value is used
+    const int rs = run ? a + r : a, ws = run ? b + r : b;
+    const int last = p.N - p.B; // the highest first slot of a run of B (N, B > 0: no overflow)
+    const bool run_ok = !run | ((a >= 1) & (a <= last) & (b >= 1) & (b <= last));
     src = ((size_t)rs * p.H + h) * tile_bytes;
     dst = ((size_t)ws * p.H + h) * tile_bytes;
-    return true;
+    return run_ok & (rs >= 1) & (rs < p.N) & (ws >= 1) & (ws < p.N);
 }
 
 // The constant clock (100 MHz), read only when a hold is asked for, and only
@@ -105,8 +132,9 @@ __device__ __forceinline__ void probe_hold(uint64_t t0, uint32_t hold)
 // at the step's occupancy (its registers allow four waves a SIMD; the launch
 // reserves LDS so that no more workgroups share a CU than the step's do).
 template <int DK, int DV, int TPW, int POL>
-__global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
+__global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(PROBE_LEAD_PARAMS, ProbeParams p)
 {
+    PROBE_LEAD_SET(p);
     constexpr int kProbeLoad = probe_aux<POL>(), kProbeStore = probe_aux<POL>();
     constexpr int RG = 8, RPT = DK / RG, NTS = 2 * DV;
     static_assert(DV % 32 == 0, "a wave holds 32 columns");
@@ -119,7 +147,8 @@ __global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
     const int cg = (ht >> 6) * 8 + (lane & 7);
     const int t = blockIdx.x * TPW + sub;
     size_t so = 0, dof = 0;
-    const bool ok = t < p.B * p.H && probe_tile(p, t, TILE, so, dof);
+    const bool in = t < p.B * p.H;
+    const bool ok = probe_tile(p, in ? t : 0, TILE, so, dof) & in;
     char *pool = reinterpret_cast<char *>(p.state);
     const __amdgpu_buffer_rsrc_t rd = probe_rsrc(pool + so, ok ? TILE : 0u);
     const __amdgpu_buffer_rsrc_t wr = probe_rsrc(pool + dof, ok ? TILE : 0u);
@@ -163,8 +192,9 @@ __global__ __launch_bounds__(2 * DV * TPW) void probe_tile_kernel(ProbeParams p)
 // has a workgroup a chunk; a persistent grid walks the chunks in strides of
 // its size (the chunk index is uniform, so every branch here is too).
 template <int NTH, int L, int POL>
-__global__ __launch_bounds__(NTH) void probe_chunk_kernel(ProbeParams p, uint32_t tile_bytes)
+__global__ __launch_bounds__(NTH) void probe_chunk_kernel(PROBE_LEAD_PARAMS, uint32_t tile_bytes, ProbeParams p)
 {
+    PROBE_LEAD_SET(p);
     constexpr int kProbeLoad = probe_aux<POL>(), kProbeStore = probe_aux<POL>();
     constexpr uint32_t CH = (uint32_t)NTH * L * 16u;
     const int per = (int)(tile_bytes / CH);
@@ -210,8 +240,9 @@ __global__ __launch_bounds__(NTH) void probe_chunk_kernel(ProbeParams p, uint32_
 }
 
 // The launch floor: a kernel that does nothing.
-__global__ __launch_bounds__(64) void probe_empty_kernel(ProbeParams p)
+__global__ __launch_bounds__(64) void probe_empty_kernel(PROBE_LEAD_PARAMS, ProbeParams p)
 {
+    PROBE_LEAD_SET(p);
     if (p.one == 3.0f && threadIdx.x == 0) // never true
         p.sink[0] = 1.0f;
 }
@@ -220,8 +251,9 @@ __global__ __launch_bounds__(64) void probe_empty_kernel(ProbeParams p)
 // (256 threads, 16-byte streaming loads; a dependent pair of loads, as every
 // step starts).
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void probe_slot_load_kernel(ProbeParams p)
+__global__ __launch_bounds__(256) void probe_slot_load_kernel(PROBE_LEAD_PARAMS, ProbeParams p)
 {
+    PROBE_LEAD_SET(p);
     constexpr uint32_t TILE = (uint32_t)DK * DV * 4u;
     constexpr int L = (int)(TILE / (256u * 16u)); // 16-byte loads a lane, all in flight at once
     const int rs = p.read_slot[0];
@@ -264,7 +296,8 @@ static hipError_t launch_chunk(ProbeParams q, uint32_t tile_bytes, hipStream_t s
     }
     if (grid <= 0)
         return hipSuccess;
-    void *args[] = {&q, &tile_bytes};
+    ProbeLead l(q);
+    void *args[] = {&l.state, &l.read_slot, &l.write_slot, &l.B, &l.H, &l.N, &l.traffic, &l.layout, &tile_bytes, &q};
     return hipLaunchKernel(reinterpret_cast<const void *>(&probe_chunk_kernel<NTH, L, POL>), dim3((unsigned)grid),
                            dim3(NTH), args, 0, stream);
 }
@@ -302,7 +335,8 @@ template <int DK, int DV, int TPW, int POL>
 static hipError_t launch_tiles(ProbeParams q, hipStream_t stream)
 {
     const long long tiles = (long long)q.B * q.H;
-    void *args[] = {&q};
+    ProbeLead l(q);
+    void *args[] = {&l.state, &l.read_slot, &l.write_slot, &l.B, &l.H, &l.N, &l.traffic, &l.layout, &q};
     // the step's 128 x 128 kernels fit four 256-thread tiles on a CU (registers):
     // reserve a quarter of the 160 KiB LDS per tile so the probe fits no more
     const size_t lds = DK == 128 && DV == 128 && TPW < 4 ? (size_t)TPW * 40 * 1024 : 0;
@@ -333,13 +367,14 @@ template <int DK, int DV>
 static hipError_t launch_probe(const ProbeParams &p, hipStream_t stream)
 {
     ProbeParams q = p;
+    ProbeLead l(q);
     if (p.shape == 4) {
-        void *args[] = {&q};
+        void *args[] = {&l.state, &l.read_slot, &l.write_slot, &l.B, &l.H, &l.N, &l.traffic, &l.layout, &q};
         return hipLaunchKernel(reinterpret_cast<const void *>(&probe_empty_kernel), dim3(1), dim3(64), args, 0,
                                stream);
     }
     if (p.shape == 5) {
-        void *args[] = {&q};
+        void *args[] = {&l.state, &l.read_slot, &l.write_slot, &l.B, &l.H, &l.N, &l.traffic, &l.layout, &q};
         return hipLaunchKernel(reinterpret_cast<const void *>(&probe_slot_load_kernel<DK, DV>), dim3(1), dim3(256),
                                args, 0, stream);
     }
