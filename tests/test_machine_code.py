@@ -1,4 +1,4 @@
-"""The built library's gfx950 machine code, checked for two things.
+"""The built library's gfx950 machine code, checked for three things.
 
 No kernel uses scratch memory: each kernel's metadata (llvm-readelf --notes
 on the code objects of the offload bundle) states a private segment of 0
@@ -20,6 +20,13 @@ on any vector write to a wide store's data registers by the next instruction,
 so a recompile cannot bring the pattern back unnoticed.  Loads (LDS included)
 into those registers are not counted: their data arrives long after the store
 has read its registers.
+
+And the step kernels' argument preloading: the build has the hardware load
+their leading arguments (what the first round of scalar loads needs) into
+scalar registers, which each kernel descriptor states (its 16-bit kernarg
+preload field at byte 58: bits 0-6 the length in dwords, bits 7-15 the offset).
+Losing the build flag would bring back a round trip before every step's first
+load without failing any parity test, so the lengths are checked here.
 """
 import os
 import re
@@ -141,3 +148,44 @@ def test_no_kernel_uses_scratch():
     assert len(kernels) > 60 and len(steps) >= 40, "expected every kernel's metadata"
     scratch = {k: v for k, v in kernels.items() if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
     assert not scratch, f"kernels using scratch: {scratch}"
+
+
+def _kernel_descriptors(co: bytes) -> dict:
+    """name -> the 64-byte kernel descriptor (symbol `name.kd`) of a code object."""
+    import struct
+    secs = bench._elf_sections(co)
+    symtab = [x for x in secs if x[0] == ".symtab"][0]
+    strtab = secs[symtab[5]]
+    out = {}
+    for i in range(symtab[4] // 24):
+        name, _info, _other, shndx, value, _size = struct.unpack_from("<IBBHQQ", co, symtab[3] + i * 24)
+        end = co.index(b"\0", strtab[3] + name)
+        nm = co[strtab[3] + name:end].decode()
+        if nm.endswith(".kd") and 0 < shndx < len(secs):
+            sec = secs[shndx]
+            off = sec[3] + (value - sec[2])
+            out[nm[:-3]] = co[off:off + 64]
+    return out
+
+
+def test_step_kernels_preload_their_leading_arguments():
+    import struct
+    if not os.path.exists(LIB):
+        pytest.skip("libgdn.so is not built")
+    kds = {}
+    for co in bench.device_code_objects(LIB):
+        kds.update(_kernel_descriptors(co))
+    pre = {k: struct.unpack_from("<H", d, 58)[0] for k, d in kds.items()}
+    tile = {k: v for k, v in pre.items() if "gdn_step_tile_kernel" in k}
+    walk = {k: v for k, v in pre.items() if "15gdn_step_kernel" in k}
+    probes = {k: v for k, v in pre.items() if "probe_" in k}
+    assert len(tile) >= 18 and len(walk) >= 26 and len(probes) >= 40, "expected every step and probe kernel"
+    # tile kernel: 4 pointers and 4 ints = 12 dwords from offset 0
+    assert {v & 0x7F for v in tile.values()} == {12} and {v >> 7 for v in tile.values()} == {0}, tile
+    # walk kernel: the read slots' pointer, H_k, N = 4 dwords
+    assert {v & 0x7F for v in walk.values()} == {4} and {v >> 7 for v in walk.values()} == {0}, walk
+    # copy probes: the pool, both slot arrays and five ints (+ the chunk size) = 11 or 12 dwords
+    assert {v & 0x7F for v in probes.values()} <= {11, 12}, probes
+    # kernels whose sources carry no preload flag preload nothing
+    other = {k: v for k, v in pre.items() if k not in tile and k not in walk and k not in probes}
+    assert other and not any(other.values()), {k: v for k, v in other.items() if v}
