@@ -1276,7 +1276,9 @@ def main() -> int:
                           "kernel_us_p10": float(np.percentile(kus, 10)),
                           "kernel_us_p50": float(np.percentile(kus, 50)),
                           "kernel_us_p90": float(np.percentile(kus, 90)),
-                          "bytes_per_launch": b.bytes}
+                          "bytes_per_launch": b.bytes,
+                          # the counted bytes over the same kernel mean (null without counters)
+                          "achieved_counted": traffic / (k_us * 1e-6) / 1e9 if traffic is not None else None}
     if not args.no_calib and not b.tokens_mode and b.T == 1:
         cal = b.calibration()
         result["calibration"] = cal

@@ -558,6 +558,33 @@ def test_slot_reset_and_copy_match_oracle(gdn, torch):
     assert t.count_nonzero(dp.state[0].view(t.int32)) == 0
 
 
+@pytest.mark.parametrize("H_k,H_v,d,d_v,pairs", [
+    (3, 3, 64, 64, 9),      # 48 KiB of state a slot
+    (5, 5, 128, 128, 7),    # 320 KiB
+    (2, 6, 128, 64, 13),    # 192 KiB, two value heads a key head
+    (1, 3, 64, 128, 40),    # 96 KiB, 40 pairs
+])
+def test_slot_copy_shapes_match_oracle(gdn, torch, H_k, H_v, d, d_v, pairs):
+    """Slot copies over several slot sizes and pair counts, with skipped pairs
+    among them: the whole pool bit for bit against the oracle."""
+    t = torch
+    N = 2 * pairs + 3
+    case = gi.small(B=2, T=1, H_k=H_k, H_v=H_v, d=d, d_v=d_v, N=N, seed=97 + pairs)
+    s, pool = case.shape, case.pools[0]
+    dp, hp = H.DevPool(pool), H.HostPool(pool)
+    rng = np.random.default_rng(pairs)
+    perm = rng.permutation(np.arange(1, N)).astype(np.int32)
+    src, dst = perm[:pairs].copy(), perm[pairs:2 * pairs].copy()
+    # a copy from the null slot; skipped: dst 0, src out of range, dst negative
+    src[1], dst[2], src[3], dst[4] = 0, 0, N + 4, -1
+    gdn.slot_copy(dp.state, dp.conv_state, t.from_numpy(src).cuda(), t.from_numpy(dst).cuda(), H_k=s.H_k)
+    oracle.slot_copy(hp.state, hp.conv_state, src, dst)
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(dp.state.cpu().numpy().view(np.uint32), hp.state.view(np.uint32))
+    np.testing.assert_array_equal(H.bf16_host(dp.conv_state), hp.conv_state)
+    assert t.count_nonzero(dp.state[0].view(t.int32)) == 0
+
+
 def test_forked_slot_steps_like_its_source(gdn, torch):
     """A snapshot made with slot_copy steps bit-identically to the slot it was
     copied from (PR #1139 "Tests": forks read the right slot)."""
