@@ -81,10 +81,11 @@ MEASURED_TRAFFIC = {"kernel_code_sha256": "b4ee9a59f7b7983dca198b44b277973e94b5c
 # pass 2 summed), per (prompts, tokens a prompt) workload, scaled as above; the
 # summary with its commands is in profiles/.  Valid only for this machine code.
 PREFILL_KERNELS = ("_ZN3gdn12_GLOBAL__N_119tp_chunk_map_kernelENS_13TwoPassParamsE",
-                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128ELb0EEEvNS_13TwoPassParamsE",
-                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128ELb1EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128ELb0EEEvNS_13TwoPassParamsEii",
+                   "_ZN3gdn12_GLOBAL__N_115tp_intra_kernelILi128ELi128ELb1EEEvNS_13TwoPassParamsEii",
+                   "_ZN3gdn12_GLOBAL__N_114tp_pipe_kernelILi128ELi128EEEvNS_13TwoPassParamsEiiiiii",
                    "_ZN3gdn12_GLOBAL__N_115tp_inter_kernelILi128ELi128ELi64EEEvNS_13TwoPassParamsE",
-                   "_ZN3gdn12_GLOBAL__N_117tp_inter16_kernelILi128ELi128EEEvNS_13TwoPassParamsE",
+                   "_ZN3gdn12_GLOBAL__N_117tp_inter16_kernelILi128ELi128EEEvNS_13TwoPassParamsEii",
                    "_ZN3gdn12_GLOBAL__N_114tp_slim_kernelILi128ELi128EEEvNS_13TwoPassParamsE")
 MEASURED_PREFILL_TRAFFIC = {"kernel_code_sha256": "bb82c38ed2e6b6a38e062e3976302c160543809cc731db032d7c24d08bcbaff8",
                             "bytes_per_call": {(16, 512): 309_907_705, (1, 4096): 364_120_357}}

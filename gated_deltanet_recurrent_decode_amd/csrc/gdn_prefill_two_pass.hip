@@ -45,6 +45,8 @@
 #include "prefill_internal.h"
 #include "step_common.h"
 
+#include <climits>
+
 namespace gdn {
 
 namespace {
@@ -163,8 +165,10 @@ __global__ __launch_bounds__(NT) void tp_chunk_map_kernel(TwoPassParams tp)
 // SLIM: the slim layout (T', P and the row factors; no V, W or U~), the q | k
 // conv spread over every lane in runs of tokens, and each prompt's old window
 // copied to hw at its first chunk.
+// The body of a pass-1 workgroup: (bx, hv) of a gx-wide grid takes the
+// chunks lo + bx, lo + bx + gx, ... below hi (and below the call's count).
 template <int DK, int DV, bool SLIM>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2, SLIM ? 3 : 2))) void tp_intra_kernel(TwoPassParams tp)
+__device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int gx, int hv, int lo, int hi)
 {
     const PrefillParams &p = tp.p;
     constexpr int NPAIR = SLIM ? NT : (2 * DK + DV) / 2; // conv lanes, two channels each
@@ -188,14 +192,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
-    const int hv = blockIdx.y;
     const int hk = hv / p.G;
     const int C = p.C;
     const int32_t *cs = tp.ws.chunk_start;
     // chunks past the workspace's capacity exist only when ranges overlap,
     // which the contract excludes; they are skipped rather than written out of bounds
-    const int nch = __builtin_amdgcn_readfirstlane(cs[p.B] < tp.ws.nchunk ? cs[p.B] : tp.ws.nchunk);
-    if (nch <= 0 || (int)blockIdx.x >= nch)
+    const int nall = __builtin_amdgcn_readfirstlane(cs[p.B] < tp.ws.nchunk ? cs[p.B] : tp.ws.nchunk);
+    const int nch = nall < hi ? nall : hi; // this body's chunks end here
+    if (nch <= 0 || lo + bx >= nch)
         return;
 
     // ---- conv lanes: channel pair (e, e+1) of the q | k | v channels of (hk, hv)
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2
 
     // ---- a chunk's inputs: its record, the three inputs before it (from the
     // slot's window for a prompt's first chunk, else from x), its x rows and
-    // gates.  The workgroup walks chunks blockIdx.x, + gridDim.x, ... and
+    // gates.  The workgroup walks chunks lo + bx, + gx, ... and
     // loads the next one's inputs while it computes the current one; x and the
     // gates come through buffer resources over the chunk's real rows (later
     // rows read zeros), so no branch surrounds those loads.
@@ -267,8 +271,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2
     };
 
     ChunkIn cur, nxt;
-    load(blockIdx.x, cur);
-    for (int g = blockIdx.x; g < nch; g += gridDim.x) {
+    load(lo + bx, cur);
+    for (int g = lo + bx; g < nch; g += gx) {
         const int n = cur.n;
         const uint32_t *hx = cur.hist;
         float h0[2], h1[2], h2[2];
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2
         }
         // the next chunk's inputs load while this one computes; issued after
         // the conv, so only one chunk's x rows are live in registers at a time
-        load(g + gridDim.x, nxt);
+        load(g + gx, nxt);
         if (tid < BT) {
             // the running log decay inside the chunk and the factors derived from it
             float gsum = cur.g_in;
@@ -576,6 +580,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2
         cur = nxt;
         __syncthreads(); // LDS is read to the end of the chunk; the next one rewrites it
     }
+}
+
+// pass 1 over the call's chunks lo .. hi - 1
+template <int DK, int DV, bool SLIM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2, SLIM ? 3 : 2))) void tp_intra_kernel(TwoPassParams tp, int lo, int hi)
+{
+    intra_body<DK, DV, SLIM>(tp, blockIdx.x, gridDim.x, blockIdx.y, lo, hi);
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -897,8 +908,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // the summed Q~ S0 partials and leave that in LDS, and waves 0-1 add it to
 // theirs after the next chunk's barrier (one more barrier after the last
 // chunk) and store the rows.
+//
+// The body of walk workgroup j over the call's chunks lo .. hi - 1 (global
+// chunk indices): a prompt's chunks outside the range are left alone, and the
+// state slice goes from the slot to registers and back around the range, so a
+// prompt can be walked in consecutive ranges by consecutive launches.
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
+__device__ __forceinline__ void inter16_body(const TwoPassParams &tp, int j, int lo, int hi)
 {
     const PrefillParams &p = tp.p;
     constexpr int NSL = DV / 16;
@@ -916,13 +932,19 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
     const int lane = tid & 63, li = lane & 15, lk = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bh, sl;
-    walk_place(blockIdx.x, p.B * p.H_v, NSL, bh, sl);
+    walk_place(j, p.B * p.H_v, NSL, bh, sl);
     const int hv = bh % p.H_v;
     const int b = bh / p.H_v;
     const int col0 = sl * 16;
     int t_begin, t_end, s, nchunks;
     size_t blk0;
     if (!walk_setup<DV, 16>(tp, b, hv, col0, t_begin, t_end, s, nchunks, blk0))
+        return;
+    // this prompt's chunks in the range
+    const int cs_b = (int)(blk0 - (size_t)hv * tp.ws.nchunk);
+    const int c_lo = lo > cs_b ? lo - cs_b : 0;
+    const int c_hi = hi - cs_b < nchunks ? hi - cs_b : nchunks;
+    if (c_lo >= c_hi)
         return;
     float *tile = p.state + ((size_t)s * p.H_v + hv) * (size_t)(DK * DV) + col0 + li;
 
@@ -945,7 +967,7 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
         float el;
     };
     auto prefetch = [&](int c, Ops &x) {
-        const bool real = c < nchunks;
+        const bool real = c < c_hi;
         const size_t blk = blk0 + (size_t)(real ? c : 0);
         const __amdgpu_buffer_rsrc_t rW = buf_rsrc(tp.ws.wa + blk * CHUNK_QK, real ? CHUNK_QK * 4u : 0u);
         const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(tp.ws.qa + blk * CHUNK_QK, real ? CHUNK_QK * 4u : 0u);
@@ -1041,7 +1063,7 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
         // ---- the previous chunk's read-out rows (a whole chunk: only the last
         // can be partial), ahead of the state update, which then covers the
         // stores' latency
-        if (wv < 2 && c > 0) {
+        if (wv < 2 && c > c_lo) {
             const v4f x = osum[(c - 1) & 1][wv][lane];
             store_o(v4f{x[0] + o_lo[0], x[1] + o_lo[1], x[2] + o_lo[2], x[3] + o_lo[3]}, t0 - BT, BT);
         }
@@ -1099,10 +1121,10 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
     // body has no branch: a path that skipped its second half would make every
     // wait at the top of the loop take all memory operations in flight.
     Ops opa, opb;
-    prefetch(0, opa);
-    first_products(0, opa, opb);
-    int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
+    prefetch(c_lo, opa);
+    first_products(c_lo, opa, opb);
+    int c = c_lo;
+    for (; c + 1 < c_hi; c += 2) {
         __syncthreads();
         after_barrier(c, opa);
         first_products(c + 1, opb, opa);
@@ -1110,17 +1132,18 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
         after_barrier(c + 1, opb);
         first_products(c + 2, opa, opb);
     }
-    if (c < nchunks) {
+    if (c < c_hi) {
         __syncthreads();
         after_barrier(c, opa);
         first_products(c + 1, opb, opa);
     }
-    // ---- the last chunk's read-out rows
+    // ---- the range's last chunk's read-out rows
     __syncthreads();
     if (wv < 2) {
-        const int c = nchunks - 1, t0 = t_begin + c * BT;
+        const int c = c_hi - 1, t0 = t_begin + c * BT;
         const v4f x = osum[c & 1][wv][lane];
-        store_o(v4f{x[0] + o_lo[0], x[1] + o_lo[1], x[2] + o_lo[2], x[3] + o_lo[3]}, t0, t_end - t0);
+        store_o(v4f{x[0] + o_lo[0], x[1] + o_lo[1], x[2] + o_lo[2], x[3] + o_lo[3]}, t0,
+                t_end - t0 < BT ? t_end - t0 : BT);
     }
 
     // ---- the slice back to the slot
@@ -1129,7 +1152,37 @@ __global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             __builtin_nontemporal_store(st[q][r], tile + (size_t)((wv * RBW + q) * 16 + 4 * lk + r) * DV);
-    advance_windows<DK, DV, 16>(p, hv, sl, t_begin, t_end, s);
+    if (c_hi == nchunks)
+        advance_windows<DK, DV, 16>(p, hv, sl, t_begin, t_end, s);
+}
+
+// the 16-column walk over the call's chunks lo .. hi - 1
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void tp_inter16_kernel(TwoPassParams tp, int lo, int hi)
+{
+    inter16_body<DK, DV>(tp, blockIdx.x, lo, hi);
+}
+
+// One launch of the pipelined schedule (the full layout, when the 16-column
+// walk leaves compute units idle): workgroups 0 .. n_walk - 1 walk chunks
+// wlo .. whi - 1 while the rest run pass 1 over chunks plo .. phi - 1 (gx
+// workgroups a value head) on the compute units the walk leaves free.  The
+// two bodies' LDS together allow one workgroup a CU, so neither role shares a
+// compute unit with the other; the kernel boundary orders a range's pass 1
+// before its walk, and one range's walk before the next.
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void tp_pipe_kernel(TwoPassParams tp,
+                                                                                                 int n_walk, int wlo,
+                                                                                                 int whi, int gx,
+                                                                                                 int plo, int phi)
+{
+    const int j = blockIdx.x;
+    if (j < n_walk) {
+        inter16_body<DK, DV>(tp, j, wlo, whi);
+        return;
+    }
+    const int v = j - n_walk;
+    intra_body<DK, DV, false>(tp, v % gx, gx, v / gx, plo, phi);
 }
 
 // The slim walk: one workgroup a (prompt, value head) over the slim layout,
@@ -1514,7 +1567,8 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
 {
     const PrefillParams &p = tp.p;
     TwoPassParams q = tp;
-    void *args[] = {&q};
+    int all_lo = 0, all_hi = INT_MAX;
+    void *args[] = {&q, &all_lo, &all_hi};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_chunk_map_kernel), dim3(1), dim3(NT), args, 0,
                                    stream);
     if (e != hipSuccess)
@@ -1533,10 +1587,6 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
         return hipLaunchKernel(reinterpret_cast<const void *>(&tp_slim_kernel<DK, DV>), dim3((unsigned)heads),
                                dim3(4 * DV), args, 0, stream);
     }
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV, false>),
-                        dim3((unsigned)gx, (unsigned)p.H_v), dim3(NT), args, 0, stream);
-    if (e != hipSuccess)
-        return e;
     // column slices 64, 32 or 16 wide (two workgroups a CU fit; with whole
     // 128-column slices, one a CU, 16 x 512 took 10 us and 128 x 64 71 us
     // longer).  The walk's time follows the CUs that get the most workgroups,
@@ -1553,6 +1603,44 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
             best = share;
         }
     }
+    // The pipelined schedule: when the 16-column walk takes at most half the
+    // compute units, the chunks go in consecutive ranges of 32; pass 1 of
+    // range 0 runs alone, a workgroup a chunk, then launch k walks range k on
+    // its workgroups while pass 1 of range k + 1 runs on the compute units
+    // left free, a workgroup each.  At 16 value heads those 128 workgroups take
+    // four chunks each, about as long as the walk takes over 32 chunks.
+    const long long cus = device_cus();
+    const long long n_walk = heads * nsl;
+    // chunks of the call: at most one partial chunk a sequence
+    const long long nchunk_hi = ((long long)p.total + BT - 1) / BT + p.B - 1;
+    constexpr int S = 32;
+    if (DV / nsl == 16 && n_walk * 2 <= cus && nchunk_hi >= 2 * S) {
+        const long long K = (nchunk_hi + S - 1) / S;
+        int lo0 = 0, hi0 = S;
+        void *a0[] = {&q, &lo0, &hi0};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV, false>),
+                            dim3((unsigned)S, (unsigned)p.H_v), dim3(NT), a0, 0, stream);
+        const long long free_cus = cus - n_walk;
+        int nw = (int)n_walk, gxp = (int)(free_cus / p.H_v > 0 ? free_cus / p.H_v : 1);
+        for (long long k = 0; k + 1 < K && e == hipSuccess; ++k) {
+            int wlo = (int)(k * S), whi = (int)((k + 1) * S);
+            int plo = whi, phi = k + 2 < K ? (int)((k + 2) * S) : INT_MAX;
+            void *ak[] = {&q, &nw, &wlo, &whi, &gxp, &plo, &phi};
+            e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_pipe_kernel<DK, DV>),
+                                dim3((unsigned)(n_walk + (long long)gxp * p.H_v)), dim3(NT), ak, 0, stream);
+        }
+        // the last range has no pass 1 beside it: the walk kernel alone
+        int wl = (int)((K - 1) * S), wh = INT_MAX;
+        void *al[] = {&q, &wl, &wh};
+        if (e == hipSuccess)
+            e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_inter16_kernel<DK, DV>), dim3((unsigned)n_walk),
+                                dim3(NT), al, 0, stream);
+        return e;
+    }
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_intra_kernel<DK, DV, false>),
+                        dim3((unsigned)gx, (unsigned)p.H_v), dim3(NT), args, 0, stream);
+    if (e != hipSuccess)
+        return e;
     switch (DV / nsl) {
     case 16:
         return hipLaunchKernel(reinterpret_cast<const void *>(&tp_inter16_kernel<DK, DV>),

@@ -332,14 +332,33 @@ def test_two_pass_slim_unusable_ranges(gdn, torch):
     H.assert_out_close(out[:end], ref[:end])
 
 
+@pytest.mark.parametrize("lengths,hk,hv,d,pad", [
+    ([1200, 37, 0, 900, 1, 333, 50], 1, 2, 128, (6,)),   # G = 2, an empty and a padding prompt, 3 chunk ranges
+    ([2500, 40, 700], 2, 2, 64, ()),                    # d = 64 (four 16-column slices a head), 3 ranges
+    ([3000], 4, 4, 128, ()),                            # one prompt, 4 heads, 3 ranges
+], ids=["ragged-G2", "d64", "one-prompt-4-heads"])
+def test_two_pass_pipelined_ranges(gdn, torch, lengths, hk, hv, d, pad):
+    """Calls whose 16-column walk leaves compute units idle go in chunk ranges
+    of about 32: pass 1 of a range runs beside the walk of the one before.
+    Ranges cut through prompts here (and pass an empty and a padding prompt):
+    every output row, the final states and windows against the oracle, and
+    every other slot untouched."""
+    case = gi.prefill(lengths, H_k=hk, H_v=hv, d=d, pad=pad, seed=sum(lengths) % 97)
+    _, out = _check(gdn, torch, case, two_pass=True)
+    for b in pad:
+        a, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        assert torch.count_nonzero(out[a:e].view(torch.int16)) == 0, "padding prompts read out +0.0"
+
+
 def test_two_pass_slim_long_prompts(gdn, torch):
     """Sixteen prompts of 1024 tokens (the slim layout, 32 chunks a walk), every
     output row and final state against the oracle."""
     _check(gdn, torch, gi.prefill([1024] * 16, H_k=16, H_v=16, d=128, seed=35), two_pass=True)
 
 
-@pytest.mark.parametrize("lengths,hk,hv", [([70, 5, 33], 2, 4), ([70, 5, 33, 12, 40, 1, 64, 9] * 2, 16, 16)],
-                         ids=["full-layout", "slim-layout"])
+@pytest.mark.parametrize("lengths,hk,hv", [([70, 5, 33], 2, 4), ([70, 5, 33, 12, 40, 1, 64, 9] * 2, 16, 16),
+                                            ([1500, 70, 600], 1, 2)],
+                         ids=["full-layout", "slim-layout", "pipelined-ranges"])
 def test_two_pass_graph_replay_matches_eager(gdn, torch, lengths, hk, hv):
     """The two-pass prefill (three launches, a caller workspace, no allocation)
     captured once and replayed several times, with eager work between replays,
