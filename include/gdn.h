@@ -210,7 +210,12 @@ gdn_status gdn_prefill(const gdn_dims *dims, const gdn_bf16 *x, int64_t x_row_st
  * long prompt fills the chip); from 256 pairs up (with the last round of 256
  * at least three quarters full) the first pass keeps only the chunk's solve
  * and per-token factors and the second, a workgroup per prompt and head, runs
- * the conv again from x (an eighth of the workspace).
+ * the conv again from x (an eighth of the workspace).  When the second pass's
+ * workgroups would fill at most half the compute units (one long prompt) and
+ * the call has 64 chunks or more, the chunks go in consecutive ranges of 32
+ * and the first pass of a range runs beside the walk of the one before: more
+ * launches, the same bits (a prompt's state goes through its slot between
+ * ranges unchanged).
  * Results match gdn_prefill within rounding, not bit for bit.
  *
  * workspace: device memory of at least
