@@ -350,6 +350,34 @@ def test_two_pass_pipelined_ranges(gdn, torch, lengths, hk, hv, d, pad):
         assert torch.count_nonzero(out[a:e].view(torch.int16)) == 0, "padding prompts read out +0.0"
 
 
+def test_two_pass_ranges_give_the_bits_of_one_walk(gdn, torch):
+    """One prompt of 2048 tokens at 16 heads runs in two chunk ranges; the same
+    prompt beside an empty padding prompt (32 prompt-head pairs: a walk that
+    fills the chip) runs in one walk.  The prompt's output rows, state and
+    window are the same bits either way."""
+    t = torch
+    case = gi.prefill([2048], H_k=16, H_v=16, d=128, seed=44)
+    s = case.shape
+    x, g, beta = H.bf16_dev(case.x), t.from_numpy(case.g).cuda(), t.from_numpy(case.beta).cuda()
+    res = []
+    for pad in (False, True):
+        dp = H.DevPool(case.pool)
+        cu = t.tensor([0, 2048, 2048] if pad else [0, 2048], dtype=t.int32, device="cuda")
+        slots = t.cat([dp.rd, t.zeros(1, dtype=t.int32, device="cuda")]) if pad else dp.rd
+        B = 2 if pad else 1
+        ws = t.empty((gdn.gdn_prefill_two_pass_workspace_bytes(B, s.T, s.H_k, s.H_v, s.d_k, s.d_v),),
+                     dtype=t.uint8, device="cuda")
+        out = t.empty((s.T, s.H_v, s.d_v), dtype=t.bfloat16, device="cuda")
+        gdn.gdn_prefill_two_pass(x, dp.conv_w, None, dp.conv_state, dp.state, g, beta, cu, slots, out, ws, H_k=s.H_k)
+        t.cuda.synchronize()
+        sl = int(case.pool.read_slot[0])
+        res.append((out, dp.state[sl].clone(), dp.conv_state[sl].clone()))
+    (o1, s1, c1), (o2, s2, c2) = res
+    assert t.equal(o1.view(t.int16), o2.view(t.int16))
+    assert t.equal(s1.view(t.int32), s2.view(t.int32))
+    assert t.equal(c1.view(t.int16), c2.view(t.int16))
+
+
 def test_two_pass_slim_long_prompts(gdn, torch):
     """Sixteen prompts of 1024 tokens (the slim layout, 32 chunks a walk), every
     output row and final state against the oracle."""
