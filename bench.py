@@ -172,11 +172,17 @@ def device_code_objects(lib_path: str, arch: str = "gfx950") -> list:
 def step_kernel_label(twin: bool, B: int, T: int, H_k: int, H_v: int, d_k: int, d_v: int, tokens_mode: bool,
                       cus: int = 256) -> str:
     """The kernel the library routes a decode step to (the same rule as its
-    dispatch): twin writes take the tile kernel; in place, single tokens with
-    one value head a key head take it too, unless 40-64 rows' worth of 128 x 128
-    heads (2.5-4 a compute unit) group key heads in the walk kernel; token walks,
-    per-token states and grouped value heads take the walk kernel."""
+    dispatch): twin writes take the tile kernel, in consecutive row parts when
+    128 x 128 heads need more than one round of four-tile workgroups; in place,
+    single tokens with one value head a key head take it too, unless 40-64
+    rows' worth of 128 x 128 heads (2.5-4 a compute unit) group key heads in the
+    walk kernel; token walks, per-token states and grouped value heads take the
+    walk kernel."""
     if twin:
+        heads = B * H_v
+        parts = -(-heads // (4 * cus))
+        if d_k == 128 and d_v == 128 and 1 < parts <= B and heads * 2 > 5 * cus * parts:
+            return f"gdn_step_tile_kernel ({parts} launches over consecutive rows)"
         return "gdn_step_tile_kernel"
     G = H_v // H_k
     if T == 1 and not tokens_mode:

@@ -452,13 +452,48 @@ static hipError_t dispatch_tile(const StepParams &p, hipStream_t stream)
     return launch_tile<DK, DV, DV / 2, 1>(q, stream);
 }
 
-hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream)
+static hipError_t dispatch_dims(const StepParams &p, int d_k, int d_v, hipStream_t stream)
 {
     if (d_k == 128 && d_v == 128) return dispatch_tile<128, 128>(p, stream);
     if (d_k == 64 && d_v == 64) return dispatch_tile<64, 64>(p, stream);
     if (d_k == 128 && d_v == 64) return dispatch_tile<128, 64>(p, stream);
     if (d_k == 64 && d_v == 128) return dispatch_tile<64, 128>(p, stream);
     return hipErrorInvalidValue;
+}
+
+// Twin steps of 128 x 128 heads that need more than one round of the
+// four-tile workgroups (over 4 heads a CU) go as P launches over consecutive
+// rows, P = ceil(heads / 4 CUs), when each part still puts more than 2.5
+// heads on every CU: each launch is then one round of four-tile workgroups.
+// Rows are independent (a key head's windows belong to one row), so the
+// parts give the bits of one launch.  Measured on MI355X, same session, us a
+// step: 128 rows of 16 heads 52.6 -> 49.9; the 9B-like layer (64 rows of 32
+// value heads) 51.4 -> 48.6.
+hipError_t launch_gdn_step_tile(const StepParams &p, int d_k, int d_v, hipStream_t stream)
+{
+    const long long heads = (long long)p.B * p.H_v, cus = device_cus();
+    const long long parts = (heads + 4 * cus - 1) / (4 * cus);
+    if (p.twin && d_k == 128 && d_v == 128 && parts > 1 && parts <= p.B && heads * 2 > 5 * cus * parts) {
+        hipError_t e = hipSuccess;
+        for (long long k = 0; k < parts && e == hipSuccess; ++k) {
+            const int r0 = (int)(p.B * k / parts), r1 = (int)(p.B * (k + 1) / parts);
+            StepParams q = p;
+            q.B = r1 - r0;
+            q.x = p.x + (size_t)r0 * p.x_row_stride;
+            q.g = p.g + (size_t)r0 * p.T * p.H_v;
+            q.beta = p.beta + (size_t)r0 * p.T * p.H_v;
+            q.read_slot = p.read_slot + r0;
+            q.write_slot = p.write_slot + r0;
+            q.out = p.out + (size_t)r0 * p.T * p.H_v * d_v;
+            if (p.next_read_slot) {
+                q.next_read_slot = p.next_read_slot + r0;
+                q.next_write_slot = p.next_write_slot + r0;
+            }
+            e = dispatch_dims(q, d_k, d_v, stream);
+        }
+        return e;
+    }
+    return dispatch_dims(p, d_k, d_v, stream);
 }
 
 } // namespace gdn

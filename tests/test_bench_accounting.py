@@ -104,6 +104,12 @@ def test_ceiling_is_the_fastest_copy_design():
 def test_step_kernel_label_follows_the_routing():
     lab = bench.step_kernel_label
     assert lab(True, 64, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel"
+    # past one round of four-tile workgroups: consecutive row parts of one round each
+    assert lab(True, 128, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel (2 launches over consecutive rows)"
+    assert lab(True, 64, 1, 16, 32, 128, 128, False) == "gdn_step_tile_kernel (2 launches over consecutive rows)"
+    assert lab(True, 256, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel (4 launches over consecutive rows)"
+    assert lab(True, 80, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel"   # halves of 2.5 heads a CU
+    assert lab(True, 128, 1, 16, 16, 64, 64, False) == "gdn_step_tile_kernel"    # d = 64: no four-tile path
     assert lab(False, 64, 1, 16, 16, 128, 128, False) == "gdn_step_kernel (4 key heads a workgroup)"
     assert lab(False, 64, 1, 8, 16, 128, 128, False) == "gdn_step_kernel (2 key heads a workgroup)"
     assert lab(False, 16, 1, 16, 16, 128, 128, False) == "gdn_step_tile_kernel"     # 256 heads: one a CU

@@ -65,6 +65,32 @@ def test_decode_rows_in_another_order(gdn, torch, twin, T):
     assert _bits_equal(torch, dp_b.conv_state, dp_a.conv_state)
 
 
+@pytest.mark.parametrize("B,H_v", [(192, 16), (64, 32)], ids=["192rows-16heads", "64rows-32heads"])
+def test_twin_step_in_row_parts_equals_one_round_calls(gdn, torch, B, H_v):
+    """A twin step of 128 x 128 heads past one round of four-tile workgroups
+    goes as consecutive row parts (here three of 64 rows, or two of 32 rows of
+    32 value heads); the same rows stepped as separate calls, each one round,
+    give the same bits: every output row and every slot."""
+    t = torch
+    case = gi.make_case(f"parts-B{B}-{H_v}", gi.Shape(B=B, T=1, H_k=16, H_v=H_v, d_k=128, d_v=128, W=4, N=2 * B + 1),
+                        seed=B + H_v)
+    s, pool, step = case.shape, case.pools[0], case.steps[0][0]
+    dp_a = H.DevPool(pool)
+    out_a = H.gpu_step(gdn, dp_a, step, s, twin=True)
+    dp_b = H.DevPool(pool)
+    out_b = t.empty_like(out_a)
+    x, g, beta = H.bf16_dev(step.x), t.from_numpy(step.g).cuda(), t.from_numpy(step.beta).cuda()
+    part = 1024 // H_v  # rows of one round of four-tile workgroups on 256 CUs
+    for r0 in range(0, B, part):
+        r1 = min(B, r0 + part)
+        gdn.gdn_decode_step(x[r0:r1], dp_b.conv_w, None, dp_b.conv_state, dp_b.state, g[r0:r1], beta[r0:r1],
+                            dp_b.rd[r0:r1], dp_b.wr[r0:r1], out_b[r0:r1], H_k=s.H_k)
+    t.cuda.synchronize()
+    assert _bits_equal(t, out_a, out_b), "a row's output depends on how the rows were split into launches"
+    assert _bits_equal(t, dp_a.state, dp_b.state)
+    assert _bits_equal(t, dp_a.conv_state, dp_b.conv_state)
+
+
 def _reordered(case, order):
     """The same prompts packed in `order` (each keeps its slot and its tokens)."""
     cu = case.cu_seqlens
