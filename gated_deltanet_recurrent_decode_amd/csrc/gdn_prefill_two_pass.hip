@@ -167,8 +167,12 @@ __global__ __launch_bounds__(NT) void tp_chunk_map_kernel(TwoPassParams tp)
 // copied to hw at its first chunk.
 // The body of a pass-1 workgroup: (bx, hv) of a gx-wide grid takes the
 // chunks lo + bx, lo + bx + gx, ... below hi (and below the call's count).
+// With at most NT prompts the workgroup builds the chunk map itself (the
+// chunk map kernel's scan, in LDS: kMapInLds) and, with write_map, also
+// stores each prompt's first chunk for the walks.
 template <int DK, int DV, bool SLIM>
-__device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int gx, int hv, int lo, int hi)
+__device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int gx, int hv, int lo, int hi,
+                                           bool write_map)
 {
     const PrefillParams &p = tp.p;
     constexpr int NPAIR = SLIM ? NT : (2 * DK + DV) / 2; // conv lanes, two channels each
@@ -189,15 +193,55 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
     __shared__ float Tm[BT * AP];
     __shared__ float Mm[16 * 17];
     __shared__ float gam[BT], bet[BT], eg[BT], egl[BT];
+    // the chunk map of calls of at most NT prompts: each prompt's first chunk
+    // (cstart[B] = the call's chunk count), its first token and its slot
+    __shared__ int cstart[NT + 1], ctb[NT], cslot[NT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
     const int hk = hv / p.G;
     const int C = p.C;
+    const bool local_map = p.B <= NT;
+    if (local_map) {
+        // the chunk map kernel's scan: chunks of each usable prompt on a slot
+        // other than the null slot, exclusive prefix sums in prompt order
+        int cnt = 0, t_begin = 0, t_end = 0, s = 0;
+        if (tid < p.B && sequence_usable(p, tid, t_begin, t_end, s) && s > 0)
+            cnt = (t_end - t_begin + BT - 1) / BT;
+        if (tid < p.B) {
+            ctb[tid] = t_begin;
+            cslot[tid] = s;
+        }
+        int *scan = reinterpret_cast<int *>(Am); // free until the chunk loop
+        scan[tid] = cnt;
+        __syncthreads();
+        for (int o = 1; o < NT; o <<= 1) {
+            const int v = tid >= o ? scan[tid - o] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        if (tid < p.B) {
+            const int start = tid == 0 ? 0 : scan[tid - 1];
+            cstart[tid] = start;
+            if (write_map)
+                tp.ws.chunk_start[tid] = start;
+        }
+        // the call's chunk count: the last inclusive sum (prompts past B count
+        // 0).  Written apart from the starts above, which cover tid < B only:
+        // with B = NT no thread has tid = B.
+        if (tid == 0) {
+            cstart[p.B] = scan[NT - 1];
+            if (write_map)
+                tp.ws.chunk_start[p.B] = scan[NT - 1];
+        }
+        __syncthreads();
+    }
     const int32_t *cs = tp.ws.chunk_start;
     // chunks past the workspace's capacity exist only when ranges overlap,
     // which the contract excludes; they are skipped rather than written out of bounds
-    const int nall = __builtin_amdgcn_readfirstlane(cs[p.B] < tp.ws.nchunk ? cs[p.B] : tp.ws.nchunk);
+    const int ctotal = local_map ? cstart[p.B] : cs[p.B];
+    const int nall = __builtin_amdgcn_readfirstlane(ctotal < tp.ws.nchunk ? ctotal : tp.ws.nchunk);
     const int nch = nall < hi ? nall : hi; // this body's chunks end here
     if (nch <= 0 || lo + bx >= nch)
         return;
@@ -233,9 +277,27 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
         int t0, n, sl;
         int b1; // the sequence's index + 1 at its first chunk, else 0
     };
+    // chunk g's record: (first token, tokens, slot, prompt + 1 at its first chunk, else 0)
+    auto record = [&](int gq) -> int4 {
+        if (!local_map)
+            return *reinterpret_cast<const int4 *>(tp.ws.chunk_rec + 4 * (size_t)gq);
+        // the last prompt whose first chunk is at or before g (prompts with no
+        // chunks share their start with the next one)
+        int a = 0, z = p.B - 1;
+        while (a < z) {
+            const int mid = (a + z + 1) >> 1;
+            if (cstart[mid] <= gq)
+                a = mid;
+            else
+                z = mid - 1;
+        }
+        const int c = gq - cstart[a];
+        const int L = p.cu_seqlens[a + 1] - ctb[a];
+        return make_int4(ctb[a] + c * BT, L - c * BT < BT ? L - c * BT : BT, cslot[a], c == 0 ? a + 1 : 0);
+    };
     auto load = [&](int gi, ChunkIn &in) {
         const int gq = __builtin_amdgcn_readfirstlane(gi < nch ? gi : nch - 1); // past the end: a real chunk, unused
-        const int4 rec = *reinterpret_cast<const int4 *>(tp.ws.chunk_rec + 4 * (size_t)gq);
+        const int4 rec = record(gq);
         const int t0 = __builtin_amdgcn_readfirstlane(rec.x);
         const int n = __builtin_amdgcn_readfirstlane(rec.y);
         const int sl = __builtin_amdgcn_readfirstlane(rec.z);
@@ -586,7 +648,7 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
 template <int DK, int DV, bool SLIM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SLIM ? 3 : 2, SLIM ? 3 : 2))) void tp_intra_kernel(TwoPassParams tp, int lo, int hi)
 {
-    intra_body<DK, DV, SLIM>(tp, blockIdx.x, gridDim.x, blockIdx.y, lo, hi);
+    intra_body<DK, DV, SLIM>(tp, blockIdx.x, gridDim.x, blockIdx.y, lo, hi, blockIdx.x == 0 && blockIdx.y == 0);
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -1182,7 +1244,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         return;
     }
     const int v = j - n_walk;
-    intra_body<DK, DV, false>(tp, v % gx, gx, v / gx, plo, phi);
+    intra_body<DK, DV, false>(tp, v % gx, gx, v / gx, plo, phi, false);
 }
 
 // The slim walk: one workgroup a (prompt, value head) over the slim layout,
@@ -1569,8 +1631,11 @@ hipError_t launch_dims(const TwoPassParams &tp, hipStream_t stream)
     TwoPassParams q = tp;
     int all_lo = 0, all_hi = INT_MAX;
     void *args[] = {&q, &all_lo, &all_hi};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_chunk_map_kernel), dim3(1), dim3(NT), args, 0,
-                                   stream);
+    hipError_t e = hipSuccess;
+    // up to NT prompts, pass 1 builds the chunk map in LDS (its first
+    // workgroup stores the prompts' first chunks for the walks): no map launch
+    if (p.B > NT)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&tp_chunk_map_kernel), dim3(1), dim3(NT), args, 0, stream);
     if (e != hipSuccess)
         return e;
     // pass 1 walks the chunks with about two resident workgroups a compute
