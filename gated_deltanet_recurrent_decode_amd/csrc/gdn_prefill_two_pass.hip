@@ -194,8 +194,8 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
     __shared__ float Mm[16 * 17];
     __shared__ float gam[BT], bet[BT], eg[BT], egl[BT];
     // the chunk map of calls of at most NT prompts: each prompt's first chunk
-    // (cstart[B] = the call's chunk count), its first token and its slot
-    __shared__ int cstart[NT + 1], ctb[NT], cslot[NT];
+    // (cstart[B] = the call's chunk count), its first token, length and slot
+    __shared__ int cstart[NT + 1], ctb[NT], clen[NT], cslot[NT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
@@ -210,12 +210,15 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
             cnt = (t_end - t_begin + BT - 1) / BT;
         if (tid < p.B) {
             ctb[tid] = t_begin;
+            clen[tid] = t_end - t_begin;
             cslot[tid] = s;
         }
         int *scan = reinterpret_cast<int *>(Am); // free until the chunk loop
         scan[tid] = cnt;
         __syncthreads();
-        for (int o = 1; o < NT; o <<= 1) {
+        // inclusive sums: after the rounds with o < B every entry below B sums
+        // all entries from 0 (the rounds beyond would only add zeros to them)
+        for (int o = 1; o < p.B; o <<= 1) {
             const int v = tid >= o ? scan[tid - o] : 0;
             __syncthreads();
             scan[tid] += v;
@@ -227,13 +230,14 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
             if (write_map)
                 tp.ws.chunk_start[tid] = start;
         }
-        // the call's chunk count: the last inclusive sum (prompts past B count
-        // 0).  Written apart from the starts above, which cover tid < B only:
-        // with B = NT no thread has tid = B.
+        // the call's chunk count, the inclusive sum at B - 1: written apart
+        // from the starts above, which cover tid < B only (with B = NT no
+        // thread has tid = B)
         if (tid == 0) {
-            cstart[p.B] = scan[NT - 1];
+            const int total = p.B > 0 ? scan[p.B - 1] : 0;
+            cstart[p.B] = total;
             if (write_map)
-                tp.ws.chunk_start[p.B] = scan[NT - 1];
+                tp.ws.chunk_start[p.B] = total;
         }
         __syncthreads();
     }
@@ -292,7 +296,7 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
                 z = mid - 1;
         }
         const int c = gq - cstart[a];
-        const int L = p.cu_seqlens[a + 1] - ctb[a];
+        const int L = clen[a];
         return make_int4(ctb[a] + c * BT, L - c * BT < BT ? L - c * BT : BT, cslot[a], c == 0 ? a + 1 : 0);
     };
     auto load = [&](int gi, ChunkIn &in) {
