@@ -46,6 +46,7 @@
 #include "step_common.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace gdn {
 
@@ -467,24 +468,33 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
         // ---- K K^T (waves 0, 1) and Q K^T (waves 2, 3) -> the masked, decay-weighted A and P
         {
             const float *Asrc = wv < 2 ? Ks : Qs;
-            const int rb = wv & 1;
+            const int rb = __builtin_amdgcn_readfirstlane(wv & 1);
             v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
             // a dot product over k, so its k-steps may run in any order: step
             // (m, r) takes k = 16 m + 4 lk + r, and a lane's four values of a k
-            // block are one 16-byte read
+            // block are one 16-byte read.  Row block 0 against column block 1
+            // lies above the diagonal, where both masks below give zero: not
+            // computed.
+            auto products = [&](auto ncb) {
+                constexpr int NCB = decltype(ncb)::value;
 #pragma unroll 4
-            for (int m = 0; m < DK / 16; ++m) {
-                const v4f a4 = *reinterpret_cast<const v4f *>(&Asrc[(rb * 16 + li) * KP + 16 * m + 4 * lk]);
-                v4f b4[2];
+                for (int m = 0; m < DK / 16; ++m) {
+                    const v4f a4 = *reinterpret_cast<const v4f *>(&Asrc[(rb * 16 + li) * KP + 16 * m + 4 * lk]);
+                    v4f b4[NCB];
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    b4[cb] = *reinterpret_cast<const v4f *>(&Ks[(cb * 16 + li) * KP + 16 * m + 4 * lk]);
+                    for (int cb = 0; cb < NCB; ++cb)
+                        b4[cb] = *reinterpret_cast<const v4f *>(&Ks[(cb * 16 + li) * KP + 16 * m + 4 * lk]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                    for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        acc[cb] = mma16(a4[r], b4[cb][r], acc[cb]);
-            }
+                        for (int cb = 0; cb < NCB; ++cb)
+                            acc[cb] = mma16(a4[r], b4[cb][r], acc[cb]);
+                }
+            };
+            if (rb == 0)
+                products(std::integral_constant<int, 1>{});
+            else
+                products(std::integral_constant<int, 2>{});
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -564,16 +574,20 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
                 const float at0 = Tm[li * AP + k0 + lk], at1 = Tm[(16 + li) * AP + k0 + lk];
                 const float bs = bet[k0 + lk];
                 const float bse = bs * eg[k0 + lk];
+                // T is lower triangular: row block 0 has no terms past k = 15 (zero
+                // products, which would leave its sums as they are)
 #pragma unroll
                 for (int q = 0; q < WCB; ++q) {
                     const float bk = bse * Ks[(k0 + lk) * KP + (wv * WCB + q) * 16 + li];
-                    wacc[0][q] = mma16(at0, bk, wacc[0][q]);
+                    if (k0 < 16)
+                        wacc[0][q] = mma16(at0, bk, wacc[0][q]);
                     wacc[1][q] = mma16(at1, bk, wacc[1][q]);
                 }
 #pragma unroll
                 for (int q = 0; q < UCB; ++q) {
                     const float bv = bs * Vs[(k0 + lk) * VP + (wv * UCB + q) * 16 + li];
-                    uacc[0][q] = mma16(at0, bv, uacc[0][q]);
+                    if (k0 < 16)
+                        uacc[0][q] = mma16(at0, bv, uacc[0][q]);
                     uacc[1][q] = mma16(at1, bv, uacc[1][q]);
                 }
             }
