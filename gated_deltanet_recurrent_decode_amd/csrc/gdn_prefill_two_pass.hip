@@ -552,7 +552,10 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
                 const int ss = 16 * m4 + 4 * (l >> 4) + e4;
                 tv[e4] = Tm[(rb * 16 + (l & 15)) * AP + ss] * bet[ss];
             }
-            *reinterpret_cast<v4f *>(tp.ws.ta + blk * (BT * BT) + (size_t)idx * 4) = tv;
+            // block 1 (row block 0, tokens 16 ..: wave 1's) lies above the diagonal,
+            // zero in T' and in P, and the second pass reads neither: not stored
+            if (wv != 1)
+                *reinterpret_cast<v4f *>(tp.ws.ta + blk * (BT * BT) + (size_t)idx * 4) = tv;
         } else {
         // ---- W = T diag(beta e^gamma) K and U~ = T diag(beta) V on the matrix
         // cores: this wave's column blocks of each, both row blocks.  Rows of
@@ -648,7 +651,8 @@ __device__ __forceinline__ void intra_body(const TwoPassParams &tp, int bx, int 
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
                 pv[e4] = Pm[(rb * 16 + (l & 15)) * AP + 16 * m4 + 4 * (l >> 4) + e4];
-            *reinterpret_cast<v4f *>(tp.ws.pa + blk * (BT * BT) + (size_t)idx * 4) = pv;
+            if (!SLIM || wv != 1)
+                *reinterpret_cast<v4f *>(tp.ws.pa + blk * (BT * BT) + (size_t)idx * 4) = pv;
         }
         // e^gamma_last (padding tokens carry g = 0): every lane stores the same
         // value to the same place, which needs no branch
